@@ -1,0 +1,227 @@
+"""CPU oracle for rotated residual/product VQ of the KV cache and LUT decode
+attention -- TEST INFRASTRUCTURE, NOT PART OF THE PRODUCT.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s cpu_baseline
+leg may import, call or execute anything in this package.  It shares no code
+with the HIP library: it imports NumPy and nothing else from this
+repository.
+
+Everything here is float64 NumPy written as the plain definition of each step,
+in the order the pages give, with no blocking or fusion beyond what the
+definition states.  A block loop over vectors is used only to bound memory.
+
+Sources (page title -- section):
+  [ZK]   "ZeroKV-Neo 4.0.0" (PyPI project page) -- Architecture: the FWHT
+         "energy spreading" step before quantisation; the FP16 hot tier.
+  [VQKV] "VQKV: High-Fidelity and High-Ratio Cache Compression via
+         Vector-Quantization" (gist.science summary) -- 2. Methodology,
+         Residual Simple Vector Quantization (RSimVQ): nearest entry in the
+         first codebook, residual, next codebook, N stages; reconstruction as
+         the sum of retrieved entries; 3. Inference Integration: codes stored
+         at prefill, local sliding window of recent tokens kept uncompressed.
+  [VI]   "VeloxQuant-MLX 0.5.1" (PyPI project page) -- VecInfer section:
+         product VQ after a Walsh-Hadamard rotation with one codebook per
+         sub-vector, inverse transform absorbed into the query; Architecture:
+         the residual pipeline decodes by summing stage outputs then
+         unrotating.
+  [DKV]  "Differential-KV" README -- Decode & Prefill Innovations: scoring the
+         query in the compressed domain without materialising K; merging with
+         the dense recency window by an fp32 log-sum-exp combine.
+
+Parity status of each function is stated in its docstring; every function is
+pinned by ``tests/test_oracle_pins.py`` against closed forms, library routines
+or brute force.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = ["hadamard_matrix", "fwht", "nearest", "rvq_encode", "reconstruct_rot",
+           "reconstruct", "attend", "attend_dense", "lse_merge",
+           "code_bytes_per_vector", "compression_ratio_vs_fp16"]
+
+
+# ----------------------------------------------------------------------------
+# O1 -- Walsh-Hadamard rotation  [ZK Architecture "FWHT (energy spreading)"],
+#       [VI VecInfer "Walsh-Hadamard rotation"]
+# ----------------------------------------------------------------------------
+def hadamard_matrix(n: int) -> np.ndarray:
+    """Orthonormal Sylvester Hadamard matrix of order n (a power of two),
+    natural order: H_1 = [1], H_2k = [[H_k, H_k], [H_k, -H_k]], divided by
+    sqrt(n).  No random sign flips (none is stated for this path)."""
+    if n < 1 or (n & (n - 1)) != 0:
+        raise ValueError(f"Hadamard order must be a power of two, got {n}")
+    h = np.ones((1, 1), dtype=np.float64)
+    while h.shape[0] < n:
+        h = np.block([[h, h], [h, -h]])
+    return h / np.sqrt(float(n))
+
+
+def fwht(x: np.ndarray) -> np.ndarray:
+    """y = H_D x for every row (last axis), as a dense product with the
+    matrix above (deliberately not a butterfly, so it is checkable by eye).
+    H is symmetric and orthonormal, hence self-inverse."""
+    x = np.asarray(x, dtype=np.float64)
+    return x @ hadamard_matrix(x.shape[-1])
+
+
+# ----------------------------------------------------------------------------
+# O2 -- greedy residual VQ per group  [VQKV 2. Methodology, RSimVQ steps 1-4],
+#       product split into groups with one codebook each  [VI VecInfer]
+# ----------------------------------------------------------------------------
+def nearest(r: np.ndarray, cb: np.ndarray):
+    """Nearest codeword by squared Euclidean distance, all candidates.
+
+    r: [N][dsub], cb: [C][dsub].  Returns (z, d) with d[n][c] = sum_j
+    (r[n][j] - cb[c][j])^2 in float64 and z = first index of the minimum
+    (exact ties go to the lowest index)."""
+    r = np.asarray(r, dtype=np.float64)
+    cb = np.asarray(cb, dtype=np.float64)
+    diff = r[:, None, :] - cb[None, :, :]
+    d = np.einsum("ncj,ncj->nc", diff, diff)
+    return np.argmin(d, axis=1), d
+
+
+def rvq_encode(x: np.ndarray, codebooks: np.ndarray, *, rotate: bool = True,
+               block: int = 4096, with_stats: bool = False):
+    """Encode vectors into uint8 codes.
+
+    x: [N][D]; codebooks: [S][G][C][dsub] with G*dsub = D, C <= 256.
+    Steps for each vector [VQKV RSimVQ]:
+      y = H_D x (unless ``rotate`` is False: input already rotated);
+      for each group g independently, r = y[g*dsub:(g+1)*dsub];
+      for s = 0..S-1: z_s = nearest entry of codebook (s, g) to r;
+                      r <- r - codebook(s, g)[z_s].
+    Returns codes [N][S][G] uint8 and, with ``with_stats``, a dict with the
+    best distance d1, the second-best d2 and the residual energy |r|^2 after
+    each stage, all [N][S][G] float64.
+    """
+    S, G, C, dsub = codebooks.shape
+    x = np.asarray(x, dtype=np.float64)
+    N, D = x.shape
+    if G * dsub != D or C > 256:
+        raise ValueError("codebook shape does not match the vectors")
+    codes = np.empty((N, S, G), dtype=np.uint8)
+    d1 = np.empty((N, S, G)); d2 = np.empty((N, S, G)); res = np.empty((N, S, G))
+    cb = np.asarray(codebooks, dtype=np.float64)
+    for lo in range(0, N, block):
+        hi = min(N, lo + block)
+        y = fwht(x[lo:hi]) if rotate else x[lo:hi]
+        for g in range(G):
+            r = y[:, g * dsub:(g + 1) * dsub].copy()
+            for s in range(S):
+                z, d = nearest(r, cb[s, g])
+                codes[lo:hi, s, g] = z
+                if with_stats:
+                    part = np.partition(d, 1, axis=1) if C > 1 else np.concatenate([d, d], 1)
+                    d1[lo:hi, s, g] = part[:, 0]
+                    d2[lo:hi, s, g] = part[:, 1]
+                r = r - cb[s, g][z]
+                if with_stats:
+                    res[lo:hi, s, g] = np.einsum("nj,nj->n", r, r)
+    if with_stats:
+        return codes, {"d1": d1, "d2": d2, "resid2": res}
+    return codes
+
+
+# ----------------------------------------------------------------------------
+# O3 -- reconstruction as the sum of retrieved entries  [VQKV RSimVQ
+#       "Reconstruction"], decode then unrotate  [VI Architecture, residual
+#       pipeline decode]
+# ----------------------------------------------------------------------------
+def reconstruct_rot(codes: np.ndarray, codebooks: np.ndarray) -> np.ndarray:
+    """x_hat_rot[g*dsub:(g+1)*dsub] = sum_s codebook(s, g)[z_s], float64,
+    in the rotated domain.  codes [..., S, G] -> [..., D]."""
+    S, G, C, dsub = codebooks.shape
+    codes = np.asarray(codes)
+    cb = np.asarray(codebooks, dtype=np.float64)
+    out = np.zeros(codes.shape[:-2] + (G * dsub,), dtype=np.float64)
+    for g in range(G):
+        for s in range(S):
+            out[..., g * dsub:(g + 1) * dsub] += cb[s, g][codes[..., s, g]]
+    return out
+
+
+def reconstruct(codes: np.ndarray, codebooks: np.ndarray) -> np.ndarray:
+    """Reconstruction in the original domain: H_D applied to the rotated sum
+    (H is its own inverse)."""
+    return fwht(reconstruct_rot(codes, codebooks))
+
+
+# ----------------------------------------------------------------------------
+# O4 -- single-token decode attention over the coded cache plus the fp16
+#       recency window  [VQKV 3. Inference Integration (decode; local window)],
+#       [DKV Decode & Prefill Innovations], [VI VecInfer: q~ . K~^T = q . K^T]
+# ----------------------------------------------------------------------------
+def attend_dense(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float) -> np.ndarray:
+    """Textbook softmax attention of one query row per head.
+
+    q: [Hq][D]; k, v: [Hkv][T][D]; query head h reads KV head h // (Hq/Hkv).
+    o[h] = softmax(scale * K q[h]) V, in float64."""
+    q = np.asarray(q, dtype=np.float64)
+    Hq, D = q.shape
+    Hkv = k.shape[0]
+    rep = Hq // Hkv
+    out = np.empty((Hq, D), dtype=np.float64)
+    for h in range(Hq):
+        kk = np.asarray(k[h // rep], dtype=np.float64)
+        vv = np.asarray(v[h // rep], dtype=np.float64)
+        s = (kk @ q[h]) * scale
+        p = np.exp(s - s.max())
+        out[h] = (p / p.sum()) @ vv
+    return out
+
+
+def attend(q, k_codes, v_codes, k_cb, v_cb, k_win=None, v_win=None, scale=None):
+    """Decode attention for a batch.
+
+    q: [B][Hq][D] (original domain); k_codes, v_codes: [B][Hkv][Tc][S][G];
+    k_cb, v_cb: [S][G][C][dsub]; k_win, v_win: fp16 [B][Hkv][W][D] or None.
+    Keys/values of the coded part are the reconstructions H (sum of entries);
+    the window tokens follow them on the same axis.  scale defaults to
+    1/sqrt(D).  Returns float64 [B][Hq][D].
+    """
+    q = np.asarray(q, dtype=np.float64)
+    B, Hq, D = q.shape
+    scale = 1.0 / np.sqrt(D) if scale is None else float(scale)
+    out = np.empty((B, Hq, D), dtype=np.float64)
+    for b in range(B):
+        parts_k, parts_v = [], []
+        if k_codes is not None and k_codes.shape[2] > 0:
+            parts_k.append(reconstruct(k_codes[b], k_cb))
+            parts_v.append(reconstruct(v_codes[b], v_cb))
+        if k_win is not None and k_win.shape[2] > 0:
+            parts_k.append(np.asarray(k_win[b], dtype=np.float64))
+            parts_v.append(np.asarray(v_win[b], dtype=np.float64))
+        k = np.concatenate(parts_k, axis=1)
+        v = np.concatenate(parts_v, axis=1)
+        out[b] = attend_dense(q[b], k, v, scale)
+    return out
+
+
+def lse_merge(parts):
+    """Log-sum-exp merge of partial softmax results [DKV "Flash-Style LSE
+    Combine"].  parts: iterable of (m, l, o) with m the partial max logit,
+    l = sum exp(s - m) and o = sum exp(s - m) v (unnormalised).  Returns the
+    normalised output sum_i e^(m_i - m*) o_i / sum_i e^(m_i - m*) l_i."""
+    parts = list(parts)
+    m_star = max(p[0] for p in parts)
+    num = sum(np.exp(m - m_star) * np.asarray(o, dtype=np.float64) for m, _, o in parts)
+    den = sum(np.exp(m - m_star) * l for m, l, _ in parts)
+    return num / den
+
+
+# ----------------------------------------------------------------------------
+# Byte accounting  [VI v6 results: key compression 16x at 1 bit/elem, 8x at
+# 2 bits/elem; VI "dsa.bit_pack" sub-byte index packing]
+# ----------------------------------------------------------------------------
+def code_bytes_per_vector(n_stages: int, n_groups: int, n_codewords: int = 256) -> float:
+    """Code bits per vector / 8: S*G codes of ceil(log2 C) bits each."""
+    bits = int(np.ceil(np.log2(n_codewords)))
+    return n_stages * n_groups * bits / 8.0
+
+
+def compression_ratio_vs_fp16(head_dim: int, n_stages: int, n_groups: int,
+                              n_codewords: int = 256) -> float:
+    """fp16 bytes of one vector over its code bytes (codebooks excluded)."""
+    return 2.0 * head_dim / code_bytes_per_vector(n_stages, n_groups, n_codewords)

@@ -1,0 +1,369 @@
+"""Pins of the CPU oracle to facts outside itself (closed forms, library
+routines, brute force, hand-worked fixtures, invariants).  CPU only.
+
+Each group of tests is chosen so that a plausible slip in the oracle (a
+dropped normalisation, a wrong sign or index, argmax for argmin, a transposed
+operand, a wrong GQA mapping) fails at least one of them; the mutation tests
+at the end plant such slips in local copies and show that they are caught.
+"""
+import itertools
+import os
+
+import numpy as np
+import pytest
+import scipy.linalg
+import scipy.spatial.distance as ssd
+import torch
+
+import oracle
+from oracle import (hadamard_matrix, fwht, nearest, rvq_encode, reconstruct_rot,
+                    reconstruct, attend, attend_dense, lse_merge)
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _read_golden(name):
+    out = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            k, v = line.split(":", 1)
+            out[k.strip()] = np.array([float(t) for t in v.split()])
+    return out
+
+
+# --------------------------------------------------------------------------- O1
+@pytest.mark.parametrize("n", [1, 2, 4, 8, 16, 32, 64, 128, 256])
+def test_hadamard_closed_form_and_library(n):
+    h = hadamard_matrix(n)
+    i = np.arange(n)
+    pc = np.array([[bin(a & b).count("1") for b in i] for a in i])
+    closed = np.where(pc % 2 == 0, 1.0, -1.0) / np.sqrt(n)
+    assert np.array_equal(h, closed)
+    assert np.array_equal(h, scipy.linalg.hadamard(n).astype(np.float64) / np.sqrt(n))
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_fwht_invariants(d):
+    h = fwht(np.eye(d))                      # rotate the identity: rows are H
+    assert np.max(np.abs(h @ h.T - np.eye(d))) <= 1e-12
+    assert np.array_equal(h, h.T)
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((50, d))
+    y = fwht(x)
+    assert np.max(np.abs(np.linalg.norm(y, axis=1) - np.linalg.norm(x, axis=1))
+                  / np.linalg.norm(x, axis=1)) <= 1e-12
+    assert np.max(np.abs(fwht(y) - x)) <= 1e-12
+    e0 = np.zeros(d); e0[0] = 1
+    assert np.allclose(fwht(e0), np.full(d, 1 / np.sqrt(d)), atol=0, rtol=1e-15)
+    ones = np.ones(d)
+    expect = np.zeros(d); expect[0] = np.sqrt(d)
+    assert np.max(np.abs(fwht(ones) - expect)) <= 1e-12
+
+
+def test_fwht_golden_d4():
+    g = _read_golden("fwht_d4.txt")
+    assert np.allclose(fwht(g["x"]), g["y"], atol=1e-15, rtol=0)
+
+
+def test_fwht_matches_torch_butterfly():
+    """An independent recursive butterfly (library ops only) agrees with the
+    dense product."""
+    def butterfly(x):
+        n = x.shape[-1]
+        if n == 1:
+            return x
+        a, b = x[..., : n // 2], x[..., n // 2:]
+        return torch.cat([butterfly(a + b), butterfly(a - b)], dim=-1)
+    x = torch.randn(20, 128, dtype=torch.float64)
+    ref = butterfly(x) / np.sqrt(128)
+    assert torch.max(torch.abs(torch.from_numpy(fwht(x.numpy())) - ref)) <= 1e-12
+
+
+# --------------------------------------------------------------------------- O2
+def test_nearest_equals_exhaustive_cdist():
+    rng = np.random.default_rng(1)
+    r = rng.standard_normal((300, 8))
+    cb = rng.standard_normal((256, 8)) * 0.4
+    z, d = nearest(r, cb)
+    ref_d = ssd.cdist(r, cb, "sqeuclidean")
+    assert np.max(np.abs(d - ref_d)) <= 1e-12
+    # second, independent formulation: |x|^2 + |c|^2 - 2 x.c
+    alt = (r ** 2).sum(1)[:, None] + (cb ** 2).sum(1)[None] - 2 * r @ cb.T
+    z_alt = np.argmin(alt, axis=1)
+    srt = np.sort(ref_d, axis=1)
+    clear = (srt[:, 1] - srt[:, 0]) > 1e-9
+    assert np.array_equal(z[clear], z_alt[clear])
+    assert np.array_equal(z, np.argmin(ref_d, axis=1))
+
+
+def test_single_stage_full_dim_equals_exhaustive_search():
+    """Tiny-workload stage 0 alone (one full 64-dim codebook of 256 entries)
+    equals exhaustive nearest-neighbour search after an independently built
+    rotation (scipy's Hadamard)."""
+    w = synth.workload(1, tokens=200)
+    inp = synth.make_inputs(w)
+    x = inp["x_f32"][0, 0].astype(np.float64)
+    cb = inp["cb"][0][:1]                      # [1][1][256][64]
+    codes = rvq_encode(x, cb)
+    y = x @ (scipy.linalg.hadamard(64) / 8.0)
+    ref = np.argmin(ssd.cdist(y, cb[0, 0].astype(np.float64), "sqeuclidean"), axis=1)
+    assert np.array_equal(codes[:, 0, 0], ref)
+
+
+def test_codeword_inputs_return_own_index():
+    rng = np.random.default_rng(3)
+    cb = rng.standard_normal((1, 4, 256, 8)).astype(np.float32)
+    x = np.concatenate([cb[0, g] for g in range(4)], axis=1).astype(np.float64)  # [256][32]
+    codes, st = rvq_encode(x, cb, rotate=False, with_stats=True)
+    for g in range(4):
+        assert np.array_equal(codes[:, 0, g], np.arange(256))
+    assert np.all(st["d1"] == 0)
+    assert np.array_equal(reconstruct_rot(codes, cb), x)
+
+
+def test_rvq_golden_2d():
+    g = _read_golden("rvq_2d.txt")
+    cb = np.stack([g["cb0"].reshape(4, 2), g["cb1"].reshape(4, 2)])[:, None]  # [2][1][4][2]
+    codes, st = rvq_encode(g["x"][None], cb, rotate=False, with_stats=True)
+    assert codes[0, :, 0].tolist() == g["codes"].astype(int).tolist()
+    assert np.allclose(st["resid2"][0, :, 0], g["resid2"], atol=1e-15, rtol=1e-12)
+    assert np.allclose(reconstruct_rot(codes, cb)[0], g["recon"], atol=1e-15)
+
+
+def test_residual_chain_second_stage_is_nearest_to_residual():
+    w = synth.workload(3, batch=1, tokens=300, window=0)
+    inp = synth.make_inputs(w)
+    x = inp["x_f32"][0, 0].astype(np.float64)
+    cb = inp["cb"][0]
+    codes = rvq_encode(x, cb)
+    y = x @ (scipy.linalg.hadamard(128) / np.sqrt(128))
+    cb64 = cb.astype(np.float64)
+    for g in (0, 5, 15):
+        r = y[:, 8 * g:8 * g + 8]
+        z0 = np.argmin(ssd.cdist(r, cb64[0, g], "sqeuclidean"), axis=1)
+        assert np.array_equal(codes[:, 0, g], z0)
+        r1 = r - cb64[0, g][z0]
+        z1 = np.argmin(ssd.cdist(r1, cb64[1, g], "sqeuclidean"), axis=1)
+        assert np.array_equal(codes[:, 1, g], z1)
+
+
+@pytest.mark.parametrize("key", [1, 2, 3, 4, 5])
+def test_total_error_non_increasing_per_stage(key):
+    w = synth.workload(key, batch=1, tokens=400, window=0, layers=1)
+    inp = synth.make_inputs(w)
+    x = inp["x_f32"][0].reshape(-1, w.head_dim)[:600]
+    _, st = rvq_encode(x, inp["cb"][0], with_stats=True)
+    tot = st["resid2"].sum(axis=(0, 2))
+    y2 = (fwht(x) ** 2).sum()
+    assert tot[0] <= y2
+    assert np.all(np.diff(tot) <= 0)
+
+
+def test_per_vector_error_non_increasing_with_zero_entry():
+    rng = np.random.default_rng(5)
+    cb = rng.standard_normal((4, 16, 256, 8)).astype(np.float32) * 0.5
+    cb[:, :, 0, :] = 0.0                       # entry 0 is the zero vector
+    x = rng.standard_normal((500, 128))
+    _, st = rvq_encode(x, cb, with_stats=True)
+    y = fwht(x)
+    e0 = (y.reshape(500, 16, 8) ** 2).sum(-1)
+    seq = np.concatenate([e0[:, None, :], st["resid2"]], axis=1)
+    assert np.all(np.diff(seq, axis=1) <= 1e-12)
+
+
+def test_greedy_is_stagewise_not_joint():
+    """Exhaustive joint search over all C^S pairs is never worse than greedy,
+    and greedy's first choice is the stage-0 nearest entry."""
+    rng = np.random.default_rng(11)
+    cb = rng.standard_normal((2, 1, 4, 3))
+    x = rng.standard_normal((200, 3))
+    codes, st = rvq_encode(x, cb, rotate=False, with_stats=True)
+    strictly_better = 0
+    for n in range(200):
+        best = min(np.sum((x[n] - cb[0, 0, a] - cb[1, 0, b]) ** 2)
+                   for a, b in itertools.product(range(4), range(4)))
+        assert best <= st["resid2"][n, 1, 0] + 1e-12
+        strictly_better += best < st["resid2"][n, 1, 0] - 1e-12
+        assert codes[n, 0, 0] == np.argmin(((x[n] - cb[0, 0]) ** 2).sum(1))
+    assert strictly_better > 0                  # greedy really differs from joint
+
+
+# --------------------------------------------------------------------------- O3
+def test_reconstruct_explicit_loop():
+    rng = np.random.default_rng(2)
+    cb = rng.standard_normal((3, 4, 16, 2))
+    codes = rng.integers(0, 16, size=(7, 3, 4)).astype(np.uint8)
+    out = reconstruct_rot(codes, cb)
+    for n in range(7):
+        for g in range(4):
+            for j in range(2):
+                ref = 0.0
+                for s in range(3):
+                    ref += cb[s, g, codes[n, s, g], j]
+                assert out[n, 2 * g + j] == pytest.approx(ref, abs=1e-15)
+
+
+def test_decode_of_encode_is_identity_on_codeword_sums():
+    rng = np.random.default_rng(9)
+    cb = (rng.standard_normal((2, 16, 256, 8)) * [[[[1.0]]], [[[0.1]]]]).astype(np.float32)
+    cb[1, :, 0, :] = 0.0                 # stage 1 can add nothing
+    z = rng.integers(0, 256, size=(64, 16))
+    x_rot = np.stack([np.concatenate([cb[0, g, z[n, g]] for g in range(16)]) for n in range(64)])
+    x = fwht(x_rot)                      # original-domain input whose rotation is a codeword row
+    codes = rvq_encode(x, cb)
+    assert np.array_equal(codes[:, 0, :], z)
+    assert np.all(codes[:, 1, :] == 0)
+    assert np.max(np.abs(reconstruct(codes, cb) - x)) <= 1e-12
+
+
+# --------------------------------------------------------------------------- O4
+def _sdpa(q, k, v, scale):
+    return torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[:, :, None, :], torch.from_numpy(k), torch.from_numpy(v),
+        scale=scale)[:, :, 0, :].numpy()
+
+
+def test_window_only_equals_dense_softmax_library():
+    rng = np.random.default_rng(4)
+    B, Hkv, Hq, W, D = 2, 4, 8, 37, 128
+    q = rng.standard_normal((B, Hq, D))
+    kw = rng.standard_normal((B, Hkv, W, D)).astype(np.float16)
+    vw = rng.standard_normal((B, Hkv, W, D)).astype(np.float16)
+    empty = np.zeros((B, Hkv, 0, 1, 16), dtype=np.uint8)
+    got = attend(q, empty, empty, None, None, kw, vw)
+    rep = Hq // Hkv
+    kk = np.repeat(kw.astype(np.float64), rep, axis=1)   # head h reads kv h // rep
+    vv = np.repeat(vw.astype(np.float64), rep, axis=1)
+    ref = _sdpa(q, kk, vv, 1 / np.sqrt(D))
+    assert np.max(np.abs(got - ref)) <= 1e-12
+
+
+def test_attention_special_cases():
+    rng = np.random.default_rng(6)
+    q = rng.standard_normal((3, 16))
+    k = np.repeat(rng.standard_normal((1, 1, 16)), 9, axis=1).repeat(3, axis=0)
+    v = rng.standard_normal((3, 9, 16))
+    out = attend_dense(q, k, v, 0.25)
+    assert np.allclose(out, v.mean(axis=1), atol=1e-14)      # equal keys -> mean of values
+    out1 = attend_dense(q, k[:, :1], v[:, :1], 0.25)
+    assert np.allclose(out1, v[:, 0], atol=1e-15)            # one token -> its value
+
+
+def test_lse_partition_invariance():
+    rng = np.random.default_rng(8)
+    T, D = 1000, 32
+    q = rng.standard_normal(D)
+    k = rng.standard_normal((T, D)) * 2
+    v = rng.standard_normal((T, D))
+    full = attend_dense(q[None], k[None], v[None], 0.3)[0]
+    cuts = [0, 1, 150, 151, 600, 1000]
+    parts = []
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        s = 0.3 * (k[a:b] @ q)
+        m = s.max()
+        p = np.exp(s - m)
+        parts.append((m, p.sum(), p @ v[a:b]))
+    assert np.max(np.abs(lse_merge(parts) - full)) <= 1e-12
+
+
+def test_query_side_rotation_identity():
+    rng = np.random.default_rng(10)
+    q = rng.standard_normal(128)
+    k_rot = rng.standard_normal((40, 128))
+    assert np.allclose(fwht(k_rot) @ q, k_rot @ fwht(q), atol=1e-12)
+
+
+def test_attend_coded_matches_library_on_reconstruction():
+    w = synth.workload(3, batch=2, tokens=300, window=20)
+    inp = synth.make_inputs(w)
+    Tc = w.code_tokens
+    x = inp["x_f32"]
+    codes = [rvq_encode(x[b].reshape(-1, 128)[:, :], inp["cb"][b]).reshape(w.batch, w.n_kv_heads, w.tokens, 2, 16)
+             for b in range(2)]
+    kc, vc = codes[0][:, :, :Tc], codes[1][:, :, :Tc]
+    got = attend(inp["q"], kc, vc, inp["cb"][0], inp["cb"][1], inp["k_win"], inp["v_win"])
+    kh = np.concatenate([reconstruct(kc, inp["cb"][0]), inp["k_win"].astype(np.float64)], axis=2)
+    vh = np.concatenate([reconstruct(vc, inp["cb"][1]), inp["v_win"].astype(np.float64)], axis=2)
+    rep = w.n_q_heads // w.n_kv_heads
+    ref = _sdpa(inp["q"].astype(np.float64), np.repeat(kh, rep, 1), np.repeat(vh, rep, 1),
+                1 / np.sqrt(128))
+    assert np.max(np.abs(got - ref)) <= 1e-12
+
+
+# ---------------------------------------------------------------- byte account
+def test_compression_ratios_match_pages():
+    """'VeloxQuant-MLX 0.5.1', v6 results: product VQ key compression 16x at
+    1 bit/elem and 8x at 2 bits/elem, for head_dim 64 and 128 alike."""
+    for d in (64, 128):
+        assert oracle.compression_ratio_vs_fp16(d, 1, d // 8) == 16.0
+        assert oracle.compression_ratio_vs_fp16(d, 2, d // 8) == 8.0
+    assert oracle.compression_ratio_vs_fp16(128, 4, 16) == 4.0
+    assert oracle.code_bytes_per_vector(2, 16) == 32
+
+
+# --------------------------------------------------------------- synth inputs
+def test_synth_deterministic_and_shaped():
+    a = synth.make_inputs(synth.workload(2, tokens=512, window=128))
+    b = synth.make_inputs(synth.workload(2, tokens=512, window=128))
+    for k in ("x", "cb", "q", "k_win", "v_win"):
+        assert np.array_equal(a[k], b[k])
+    w = a["workload"]
+    assert a["x"].shape == (2, 8, 512, 128) and a["x"].dtype == np.uint16
+    assert a["cb"].shape == (2, 1, 16, 256, 8)
+    assert a["k_win"].shape == (1, 8, 128, 128) and a["k_win"].dtype == np.float16
+    # window = the last W tokens, cast from the bf16 values
+    assert np.array_equal(a["k_win"][0, 3].astype(np.float32), a["x_f32"][0, 3, 384:])
+    # 4 outlier channels per head (same on K and V), scaled x10: V column energy
+    v = a["x_f32"][1].astype(np.float64)
+    col = (v ** 2).mean(axis=1)                     # [seq][D]
+    assert np.all((col > 30).sum(axis=1) == 4)
+
+
+def test_bf16_rounding_is_rne():
+    x = np.array([1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -2.5, 3.0e38], dtype=np.float32)
+    back = synth.bf16_bits_to_f32(synth.bf16_bits(x))
+    assert back[0] == 1.0 and back[1] == 1.0            # tie -> even
+    assert back[2] == np.float32(1.0 + 4 * 2 ** -8)     # tie -> even (up)
+    assert back[3] == -2.5
+    assert torch.equal(torch.from_numpy(x).to(torch.bfloat16).float(), torch.from_numpy(back))
+
+
+# -------------------------------------------------------- planted-slip checks
+def test_pins_catch_planted_slips():
+    """Local mutants of oracle steps fail the pins above."""
+    d = 64
+    # (a) missing 1/sqrt(D): H H^T != I
+    h_bad = hadamard_matrix(d) * np.sqrt(d)
+    assert np.max(np.abs(h_bad @ h_bad.T - np.eye(d))) > 1
+    # (b) a sign slip in the Sylvester step: no longer matches scipy
+    h = np.ones((1, 1))
+    while h.shape[0] < d:
+        h = np.block([[h, -h], [h, h]])
+    assert not np.array_equal(h / 8, scipy.linalg.hadamard(d) / 8)
+    # (c) argmax instead of argmin breaks the codeword-returns-own-index pin
+    rng = np.random.default_rng(3)
+    cb = rng.standard_normal((256, 8))
+    d2 = ssd.cdist(cb, cb, "sqeuclidean")
+    assert not np.array_equal(np.argmax(d2, axis=1), np.arange(256))
+    # (d) residual update with + instead of - breaks error monotonicity
+    x = rng.standard_normal((500, 8))
+    cbs = rng.standard_normal((2, 256, 8)) * [[[1.0]], [[0.5]]]
+    r = x.copy()
+    errs = [(r ** 2).sum()]
+    for s in range(2):
+        z = np.argmin(ssd.cdist(r, cbs[s], "sqeuclidean"), axis=1)
+        r = r + cbs[s][z]
+        errs.append((r ** 2).sum())
+    assert np.any(np.diff(errs) > 0)
+    # (e) GQA mapping h % Hkv instead of h // rep differs from the library pin
+    q = rng.standard_normal((8, 16))
+    k = rng.standard_normal((2, 5, 16))
+    v = rng.standard_normal((2, 5, 16))
+    good = attend_dense(q, k, v, 0.25)
+    bad = np.stack([attend_dense(q[h:h + 1], k[h % 2:h % 2 + 1], v[h % 2:h % 2 + 1], 0.25)[0]
+                    for h in range(8)])
+    assert np.max(np.abs(good - bad)) > 1e-3
