@@ -1,0 +1,237 @@
+"""kvq -- rotated residual/product VQ of the KV cache and LUT decode attention
+on AMD Instinct MI355X (gfx950).
+
+A thin ctypes binding over ``libkvq.so`` (C ABI in ``include/kvq.h``).  Every
+step of the path runs in the library's HIP kernels; this module only turns
+torch device tensors into pointers, sizes and the current HIP stream, and
+raises :class:`KvqError` when the library reports a non-OK status.  The
+library is loaded on first use (``lib``); if it has not been built that use
+raises ImportError: there is no fallback path.
+
+Calls (same names as the C ABI):
+  rotate(x)                                  y = H_D x            [..., D] -> f32
+  encode(x, codebooks, n_rows=...)           codes uint8 [books][seq][rows][S][G]
+  decode_reconstruct(codes, codebooks)       sum of codewords     -> f32 [..., D]
+  attend_decode(q, k_codes, v_codes, k_cb, v_cb, k_win, v_win) -> f32 [B][Hq][D]
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["KvqError", "LIB_PATH", "lib", "rotate", "encode", "encode_workspace_size",
+           "decode_reconstruct", "attend_decode", "attend_workspace_size", "EXPORTS",
+           "KVQ_INPUT_PRE_ROTATED", "KVQ_UNROTATE", "KVQ_ENCODE_GENERIC", "VqDesc", "AttnDesc",
+           "status_string"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvq.so")
+
+KVQ_INPUT_PRE_ROTATED = 0x1
+KVQ_UNROTATE = 0x2
+KVQ_ENCODE_GENERIC = 0x4
+F32, BF16, F16 = 0, 1, 2
+
+EXPORTS = ("kvq_rotate", "kvq_encode_workspace_size", "kvq_encode", "kvq_decode_reconstruct",
+           "kvq_attend_workspace_size", "kvq_attend_decode", "kvq_status_string",
+           "kvq_last_hip_error")
+
+
+class VqDesc(ctypes.Structure):
+    _fields_ = [("head_dim", ctypes.c_int32), ("n_groups", ctypes.c_int32),
+                ("n_stages", ctypes.c_int32), ("n_codewords", ctypes.c_int32)]
+
+
+class AttnDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("n_code_tokens", ctypes.c_int32),
+                ("n_window", ctypes.c_int32), ("vq", VqDesc), ("softmax_scale", ctypes.c_float)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m compressed_attention_fwht_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, U32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32, ctypes.c_size_t
+    L.kvq_rotate.argtypes = [P, I32, P, I64, I32, P]
+    L.kvq_encode_workspace_size.argtypes = [ctypes.POINTER(VqDesc), I64, ctypes.POINTER(SZ)]
+    L.kvq_encode.argtypes = [P, I32, ctypes.POINTER(VqDesc), I64, I64, I64, I64, P, P, U32, P, SZ, P]
+    L.kvq_decode_reconstruct.argtypes = [P, ctypes.POINTER(VqDesc), I64, I64, P, P, U32, P]
+    L.kvq_attend_workspace_size.argtypes = [ctypes.POINTER(AttnDesc), ctypes.POINTER(SZ)]
+    L.kvq_attend_decode.argtypes = [ctypes.POINTER(AttnDesc), P, P, P, P, P, P, P, P, P, SZ, P]
+    L.kvq_status_string.argtypes = [I32]
+    L.kvq_status_string.restype = ctypes.c_char_p
+    L.kvq_last_hip_error.argtypes = []
+    for name in EXPORTS:
+        if name not in ("kvq_status_string",):
+            getattr(L, name).restype = ctypes.c_int32 if name != "kvq_last_hip_error" else ctypes.c_int
+    return L
+
+
+_LIB = None
+
+
+def _lib():
+    global _LIB
+    if _LIB is None:
+        _LIB = _load()
+    return _LIB
+
+
+def __getattr__(name):          # module attribute ``lib`` loads the library
+    if name == "lib":
+        return _lib()
+    raise AttributeError(name)
+
+
+class KvqError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        msg = _lib().kvq_status_string(status).decode()
+        if status == 7:
+            msg += f" (hipError {_lib().kvq_last_hip_error()})"
+        super().__init__(f"{where}: {msg}")
+        self.status = status
+
+
+def status_string(status: int) -> str:
+    return _lib().kvq_status_string(status).decode()
+
+
+def _check(st: int, where: str):
+    if st != 0:
+        raise KvqError(st, where)
+
+
+# --------------------------------------------------------------- torch glue
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(t):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    m = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
+    if t.dtype not in m:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return m[t.dtype]
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr() if t is not None and t.numel() > 0 else 0)
+
+
+def _need_contig(*ts):
+    for t in ts:
+        if t is not None and not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def rotate(x, out=None):
+    """y = H_D x over the last axis.  x: cuda tensor f32/bf16/f16 [..., D]."""
+    torch = _torch()
+    _need_contig(x)
+    D = x.shape[-1]
+    n = x.numel() // D if D else 0
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.float32, device=x.device)
+    _need_contig(out)
+    _check(_lib().kvq_rotate(_ptr(x), _dtype_code(x), _ptr(out), n, D, _stream(x)), "kvq_rotate")
+    return out
+
+
+def encode_workspace_size(head_dim, n_groups, n_stages, n_codewords, n_books) -> int:
+    vq = VqDesc(head_dim, n_groups, n_stages, n_codewords)
+    sz = ctypes.c_size_t(0)
+    _check(_lib().kvq_encode_workspace_size(ctypes.byref(vq), n_books, ctypes.byref(sz)),
+           "kvq_encode_workspace_size")
+    return sz.value
+
+
+def encode(x, codebooks, *, n_rows=None, pre_rotated=False, generic=False, codes=None,
+           workspace=None):
+    """Encode rows [0, n_rows) of every sequence.
+
+    x: [n_books][n_seq][seq_stride][D] (f32/bf16/f16); codebooks:
+    [n_books][S][G][C][dsub] f32.  Returns codes [n_books][n_seq][n_rows][S][G] u8."""
+    torch = _torch()
+    _need_contig(x, codebooks)
+    nb, ns, stride, D = x.shape
+    _, S, G, C, dsub = codebooks.shape
+    n_rows = stride if n_rows is None else n_rows
+    vq = VqDesc(D, G, S, C)
+    if codes is None:
+        codes = torch.empty((nb, ns, n_rows, S, G), dtype=torch.uint8, device=x.device)
+    _need_contig(codes)
+    need = encode_workspace_size(D, G, S, C, nb)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    flags = (KVQ_INPUT_PRE_ROTATED if pre_rotated else 0) | (KVQ_ENCODE_GENERIC if generic else 0)
+    ws_bytes = workspace.numel() if workspace is not None else 0
+    _check(_lib().kvq_encode(_ptr(x), _dtype_code(x), ctypes.byref(vq), nb, ns, stride, n_rows,
+                          _ptr(codebooks), _ptr(codes), flags, _ptr(workspace), ws_bytes,
+                          _stream(x)), "kvq_encode")
+    return codes
+
+
+def decode_reconstruct(codes, codebooks, *, unrotate=False, out=None):
+    """codes [n_books][...][S][G] u8, codebooks [n_books][S][G][C][dsub] f32 ->
+    f32 [n_books][...][D] (rotated domain unless ``unrotate``)."""
+    torch = _torch()
+    _need_contig(codes, codebooks)
+    nb, S, G, C, dsub = codebooks.shape
+    D = G * dsub
+    per_book = codes.numel() // (nb * S * G) if codes.numel() else 0
+    if out is None:
+        out = torch.empty(codes.shape[:-2] + (D,), dtype=torch.float32, device=codes.device)
+    _need_contig(out)
+    vq = VqDesc(D, G, S, C)
+    _check(_lib().kvq_decode_reconstruct(_ptr(codes), ctypes.byref(vq), nb, per_book,
+                                      _ptr(codebooks), _ptr(out),
+                                      KVQ_UNROTATE if unrotate else 0, _stream(codes)),
+           "kvq_decode_reconstruct")
+    return out
+
+
+def _attn_desc(B, Hq, Hkv, D, Tc, W, S, G, C, scale):
+    return AttnDesc(B, Hq, Hkv, Tc, W, VqDesc(D, G, S, C), 0.0 if scale is None else float(scale))
+
+
+def attend_workspace_size(B, Hq, Hkv, D, Tc, W, S, G, C, scale=None) -> int:
+    a = _attn_desc(B, Hq, Hkv, D, Tc, W, S, G, C, scale)
+    sz = ctypes.c_size_t(0)
+    _check(_lib().kvq_attend_workspace_size(ctypes.byref(a), ctypes.byref(sz)),
+           "kvq_attend_workspace_size")
+    return sz.value
+
+
+def attend_decode(q, k_codes, v_codes, k_cb, v_cb, k_win=None, v_win=None, *, scale=None,
+                  out=None, workspace=None):
+    """q [B][Hq][D] f32; k/v_codes [B][Hkv][Tc][S][G] u8; k/v_cb [S][G][C][dsub]
+    f32; k/v_win [B][Hkv][W][D] f16 (or None).  Returns f32 [B][Hq][D]."""
+    torch = _torch()
+    _need_contig(q, k_codes, v_codes, k_cb, v_cb, k_win, v_win)
+    B, Hq, D = q.shape
+    _, Hkv, Tc, S, G = k_codes.shape
+    C = k_cb.shape[2]
+    W = 0 if k_win is None else k_win.shape[2]
+    a = _attn_desc(B, Hq, Hkv, D, Tc, W, S, G, C, scale)
+    sz = ctypes.c_size_t(0)
+    _check(_lib().kvq_attend_workspace_size(ctypes.byref(a), ctypes.byref(sz)),
+           "kvq_attend_workspace_size")
+    if workspace is None:
+        workspace = torch.empty(max(sz.value, 16), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    _need_contig(out)
+    for w in (k_win, v_win):
+        if w is not None and w.dtype != torch.float16:
+            raise TypeError("window tensors must be float16")
+    _check(_lib().kvq_attend_decode(ctypes.byref(a), _ptr(q), _ptr(k_codes), _ptr(v_codes),
+                                 _ptr(k_cb), _ptr(v_cb), _ptr(k_win), _ptr(v_win), _ptr(out),
+                                 _ptr(workspace), workspace.numel(), _stream(q)),
+           "kvq_attend_decode")
+    return out

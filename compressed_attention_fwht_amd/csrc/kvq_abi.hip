@@ -1,0 +1,190 @@
+// C ABI of libkvq: argument validation (before any HIP call), workspace
+// sizing and kernel dispatch.  See include/kvq.h for the contract.
+#include <math.h>
+
+#include "kvq.h"
+#include "kvq_internal.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline bool pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
+
+kvq_status check_vq(const kvq_vq_desc* vq) {
+  if (!vq) return KVQ_ERR_NULL;
+  const int D = vq->head_dim, G = vq->n_groups, S = vq->n_stages, C = vq->n_codewords;
+  if (D != 64 && D != 128 && D != 256) return KVQ_ERR_SHAPE;
+  if (G < 1 || G > D || D % G != 0) return KVQ_ERR_SHAPE;
+  const int dsub = D / G;
+  if (!pow2(dsub) || dsub < 8 || dsub > 128) return KVQ_ERR_SHAPE;
+  if (S < 1 || S > 8) return KVQ_ERR_SHAPE;
+  if (C < 1 || C > 256) return KVQ_ERR_SHAPE;
+  return KVQ_OK;
+}
+
+inline bool valid_dtype(kvq_dtype t) { return t == KVQ_F32 || t == KVQ_BF16 || t == KVQ_F16; }
+
+kvq_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return KVQ_OK;
+  g_last_hip_error = (int)e;
+  return KVQ_ERR_HIP;
+}
+
+kvq_status check_attn(const kvq_attn_desc* a, kvq::AttnPlan* plan) {
+  if (!a) return KVQ_ERR_NULL;
+  kvq_status st = check_vq(&a->vq);
+  if (st != KVQ_OK) return st;
+  if (a->batch < 1 || a->n_q_heads < 1 || a->n_kv_heads < 1) return KVQ_ERR_SHAPE;
+  if (a->n_q_heads % a->n_kv_heads != 0) return KVQ_ERR_SHAPE;
+  if (a->n_code_tokens < 0 || a->n_window < 0) return KVQ_ERR_SHAPE;
+  if ((int64_t)a->n_code_tokens + a->n_window == 0) return KVQ_ERR_SHAPE;
+  if ((int64_t)a->batch * a->n_q_heads > 0x7fffffff) return KVQ_ERR_SHAPE;
+  if (a->batch > 65535) return KVQ_ERR_UNSUPPORTED;
+  if (!(a->softmax_scale == a->softmax_scale)) return KVQ_ERR_SHAPE;   // NaN
+  const kvq_vq_desc& v = a->vq;
+  *plan = kvq::attn_plan(a->batch, a->n_q_heads, a->n_kv_heads, v.head_dim, v.n_stages,
+                         v.n_groups, v.n_codewords, a->n_code_tokens, a->n_window);
+  if (a->n_code_tokens > 0) {
+    if (plan->rp == 0) return KVQ_ERR_UNSUPPORTED;
+    if ((int64_t)a->n_kv_heads * plan->n_hsplit > 65535) return KVQ_ERR_UNSUPPORTED;
+  }
+  return KVQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kvq_status_string(kvq_status s) {
+  switch (s) {
+    case KVQ_OK: return "ok";
+    case KVQ_ERR_NULL: return "a required pointer is NULL";
+    case KVQ_ERR_SHAPE: return "sizes are inconsistent or out of range";
+    case KVQ_ERR_UNSUPPORTED: return "valid request with no kernel in this build";
+    case KVQ_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case KVQ_ERR_WORKSPACE: return "workspace missing or too small";
+    case KVQ_ERR_DTYPE: return "unknown element type";
+    case KVQ_ERR_HIP: return "a HIP call failed (see kvq_last_hip_error)";
+  }
+  return "unknown status";
+}
+
+int kvq_last_hip_error(void) { return g_last_hip_error; }
+
+kvq_status kvq_rotate(const void* x, kvq_dtype xt, float* y, int64_t n_rows, int32_t dim,
+                      hipStream_t stream) {
+  if (!valid_dtype(xt)) return KVQ_ERR_DTYPE;
+  if (dim != 64 && dim != 128 && dim != 256) return KVQ_ERR_SHAPE;
+  if (n_rows < 0) return KVQ_ERR_SHAPE;
+  if (n_rows == 0) return KVQ_OK;
+  if (!x || !y) return KVQ_ERR_NULL;
+  if (!aligned16(x) || !aligned16(y)) return KVQ_ERR_ALIGN;
+  if (n_rows > ((int64_t)1 << 40) / dim) return KVQ_ERR_SHAPE;
+  if (xt != KVQ_F32) {  // a half-width input may not overlap the float output
+    const uintptr_t xa = (uintptr_t)x, ya = (uintptr_t)y;
+    const uintptr_t xe = xa + (uintptr_t)(n_rows * dim * 2), ye = ya + (uintptr_t)(n_rows * dim * 4);
+    if (xa < ye && ya < xe) return KVQ_ERR_SHAPE;
+  } else if (x != y) {
+    const uintptr_t xa = (uintptr_t)x, ya = (uintptr_t)y, n = (uintptr_t)(n_rows * dim * 4);
+    if (xa < ya + n && ya < xa + n) return KVQ_ERR_SHAPE;   // partial overlap
+  }
+  return hip_status(kvq::launch_rotate(x, (int)xt, y, n_rows, dim, stream));
+}
+
+kvq_status kvq_encode_workspace_size(const kvq_vq_desc* vq, int64_t n_books, size_t* bytes) {
+  if (!bytes) return KVQ_ERR_NULL;
+  kvq_status st = check_vq(vq);
+  if (st != KVQ_OK) return st;
+  if (n_books < 0) return KVQ_ERR_SHAPE;
+  *bytes = kvq::encode_workspace_bytes(vq->head_dim, vq->n_groups, vq->n_stages,
+                                       vq->n_codewords, n_books);
+  return KVQ_OK;
+}
+
+kvq_status kvq_encode(const void* x, kvq_dtype xt, const kvq_vq_desc* vq, int64_t n_books,
+                      int64_t n_seq, int64_t seq_stride, int64_t n_rows, const float* codebooks,
+                      uint8_t* codes, uint32_t flags, void* workspace, size_t ws_bytes,
+                      hipStream_t stream) {
+  if (!valid_dtype(xt)) return KVQ_ERR_DTYPE;
+  kvq_status st = check_vq(vq);
+  if (st != KVQ_OK) return st;
+  if (flags & ~(KVQ_INPUT_PRE_ROTATED | KVQ_ENCODE_GENERIC)) return KVQ_ERR_SHAPE;
+  if (n_books < 0 || n_seq < 0 || seq_stride < 0 || n_rows < 0) return KVQ_ERR_SHAPE;
+  if (n_rows > seq_stride) return KVQ_ERR_SHAPE;
+  if (n_books == 0 || n_seq == 0 || n_rows == 0) return KVQ_OK;
+  if (!x || !codebooks || !codes) return KVQ_ERR_NULL;
+  if (!aligned16(x) || !aligned16(codebooks) || !aligned16(codes)) return KVQ_ERR_ALIGN;
+  const int D = vq->head_dim, G = vq->n_groups, S = vq->n_stages, C = vq->n_codewords;
+  const int64_t n_per_book = n_seq * n_rows;
+  if (n_seq > ((int64_t)1 << 40) / n_rows) return KVQ_ERR_SHAPE;
+  const int64_t tile = 64;   // smallest tile of either kernel
+  if (n_books * ((n_per_book + tile - 1) / tile) > 0x7fffffffLL) return KVQ_ERR_UNSUPPORTED;
+  const bool generic = (flags & KVQ_ENCODE_GENERIC) != 0 ||
+                       !kvq::encode_mfma_eligible(D, G, S, C, (int)xt);
+  if (!generic) {
+    const size_t need = kvq::encode_workspace_bytes(D, G, S, C, n_books);
+    if (ws_bytes < need || (need > 0 && !workspace)) return KVQ_ERR_WORKSPACE;
+    if (need > 0 && !aligned16(workspace)) return KVQ_ERR_ALIGN;
+  }
+  return hip_status(kvq::launch_encode(x, (int)xt, D, G, S, C, n_books, n_seq, seq_stride, n_rows,
+                                       codebooks, codes, (flags & KVQ_INPUT_PRE_ROTATED) ? 1 : 0,
+                                       generic ? 1 : 0, workspace, stream));
+}
+
+kvq_status kvq_decode_reconstruct(const uint8_t* codes, const kvq_vq_desc* vq, int64_t n_books,
+                                  int64_t n_per_book, const float* codebooks, float* out,
+                                  uint32_t flags, hipStream_t stream) {
+  kvq_status st = check_vq(vq);
+  if (st != KVQ_OK) return st;
+  if (flags & ~KVQ_UNROTATE) return KVQ_ERR_SHAPE;
+  if (n_books < 0 || n_per_book < 0) return KVQ_ERR_SHAPE;
+  if (n_books == 0 || n_per_book == 0) return KVQ_OK;
+  if (!codes || !codebooks || !out) return KVQ_ERR_NULL;
+  if (!aligned16(codes) || !aligned16(codebooks) || !aligned16(out)) return KVQ_ERR_ALIGN;
+  if (n_per_book > ((int64_t)1 << 40) / n_books) return KVQ_ERR_SHAPE;
+  return hip_status(kvq::launch_reconstruct(codes, codebooks, out, n_books, n_per_book,
+                                            vq->head_dim, vq->n_groups, vq->n_stages,
+                                            vq->n_codewords, (flags & KVQ_UNROTATE) ? 1 : 0,
+                                            stream));
+}
+
+kvq_status kvq_attend_workspace_size(const kvq_attn_desc* a, size_t* bytes) {
+  if (!bytes) return KVQ_ERR_NULL;
+  kvq::AttnPlan plan;
+  kvq_status st = check_attn(a, &plan);
+  if (st != KVQ_OK) return st;
+  *bytes = plan.ws_bytes;
+  return KVQ_OK;
+}
+
+kvq_status kvq_attend_decode(const kvq_attn_desc* a, const float* q, const uint8_t* k_codes,
+                             const uint8_t* v_codes, const float* k_cb, const float* v_cb,
+                             const uint16_t* k_win, const uint16_t* v_win, float* out,
+                             void* workspace, size_t ws_bytes, hipStream_t stream) {
+  kvq::AttnPlan plan;
+  kvq_status st = check_attn(a, &plan);
+  if (st != KVQ_OK) return st;
+  if (!q || !out || !workspace) return KVQ_ERR_NULL;
+  if (!aligned16(q) || !aligned16(out) || !aligned16(workspace)) return KVQ_ERR_ALIGN;
+  if (a->n_code_tokens > 0) {
+    if (!k_codes || !v_codes || !k_cb || !v_cb) return KVQ_ERR_NULL;
+    if (!aligned16(k_codes) || !aligned16(v_codes) || !aligned16(k_cb) || !aligned16(v_cb))
+      return KVQ_ERR_ALIGN;
+  }
+  if (a->n_window > 0) {
+    if (!k_win || !v_win) return KVQ_ERR_NULL;
+    if (!aligned16(k_win) || !aligned16(v_win)) return KVQ_ERR_ALIGN;
+  }
+  if (ws_bytes < plan.ws_bytes) return KVQ_ERR_WORKSPACE;
+  const kvq_vq_desc& v = a->vq;
+  const float scale = a->softmax_scale > 0.0f ? a->softmax_scale
+                                              : (float)(1.0 / sqrt((double)v.head_dim));
+  return hip_status(kvq::launch_attend(plan, a->batch, a->n_q_heads, a->n_kv_heads, v.head_dim,
+                                       v.n_stages, v.n_groups, v.n_codewords, a->n_code_tokens,
+                                       a->n_window, scale, q, k_codes, v_codes, k_cb, v_cb, k_win,
+                                       v_win, out, workspace, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,139 @@
+// Device helpers shared by the gfx950 kernels of libkvq: element loads,
+// bf16 packing, wavefront exchanges and the Walsh-Hadamard butterfly.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvq {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
+
+// ---------------------------------------------------------------- elements
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
+  return (float)__builtin_bit_cast(_Float16, (unsigned short)(h & 0xffffu));
+}
+
+// Round-to-nearest-even float -> bf16 bits (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// Load 8 consecutive elements of a row of type xt (0 f32, 1 bf16, 2 f16) as
+// float.  p points at the first element; 16-byte aligned for bf16/f16, and
+// 32-byte aligned rows for f32 are read as two 16-byte loads.
+template <int XT>
+__device__ __forceinline__ void load8(const void* p, float (&v)[8]) {
+  if constexpr (XT == 0) {
+    const float4* q = reinterpret_cast<const float4*>(p);
+    float4 a = q[0], b = q[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  } else {
+    uint4 w = *reinterpret_cast<const uint4*>(p);
+    uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (XT == 1) {
+        v[2 * i] = bf16_lo(ws[i]);
+        v[2 * i + 1] = bf16_hi(ws[i]);
+      } else {
+        v[2 * i] = f16_bits_to_f32(ws[i]);
+        v[2 * i + 1] = f16_bits_to_f32(ws[i] >> 16);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------- lane exchanges
+// Value of lane (lane ^ M) within the wavefront, for M in {1,2,4,8,16,32}.
+// DPP where one instruction does it, ds_swizzle (32-lane groups) otherwise.
+template <int M>
+__device__ __forceinline__ float xor_lane(float x) {
+  int v = __float_as_int(x);
+  int r;
+  if constexpr (M == 1) {
+    r = __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, true);      // quad_perm [1,0,3,2]
+  } else if constexpr (M == 2) {
+    r = __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, true);      // quad_perm [2,3,0,1]
+  } else if constexpr (M == 4) {
+    r = __builtin_amdgcn_ds_swizzle(v, 0x101F);                 // xor 4 (bitmask mode)
+  } else if constexpr (M == 8) {
+    r = __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, true);     // row_ror:8 == xor 8 in a row
+  } else if constexpr (M == 16) {
+    r = __builtin_amdgcn_ds_swizzle(v, 0x401F);                 // xor 16 (bitmask mode)
+  } else {
+    static_assert(M == 32, "xor_lane: unsupported mask");
+    r = __shfl_xor(v, 32);
+  }
+  return __int_as_float(r);
+}
+
+// Walsh-Hadamard butterfly over one row of D = E*L elements held by L
+// consecutive lanes (L in {1,2,4,8,16,32}), E consecutive elements per lane:
+// element index = (lane % L) * E + i.  Unnormalised (entries +-1); the caller
+// scales by 1/sqrt(D).  All lanes of the wavefront must execute this.
+template <int E, int L>
+__device__ __forceinline__ void hadamard_row(float (&v)[E], int lane) {
+#pragma unroll
+  for (int h = 1; h < E; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      if ((i & h) == 0) {
+        float a = v[i], b = v[i + h];
+        v[i] = a + b;
+        v[i + h] = a - b;
+      }
+    }
+  }
+#define KVQ_XSTAGE(MASK)                                              \
+  if constexpr (L > (MASK)) {                                         \
+    const float sg = (lane & (MASK)) ? -1.0f : 1.0f;                  \
+    _Pragma("unroll") for (int i = 0; i < E; ++i) {                   \
+      float p = xor_lane<(MASK)>(v[i]);                               \
+      v[i] = __builtin_fmaf(v[i], sg, p);                             \
+    }                                                                 \
+  }
+  KVQ_XSTAGE(1)
+  KVQ_XSTAGE(2)
+  KVQ_XSTAGE(4)
+  KVQ_XSTAGE(8)
+  KVQ_XSTAGE(16)
+#undef KVQ_XSTAGE
+}
+
+// Wavefront reductions (all 64 lanes participate).
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
+  return x;
+}
+
+__device__ __forceinline__ constexpr float rsqrt_pow2(int d) {
+  // 1/sqrt(d) for d in {1,...,256} powers of two, exact to float rounding.
+  return d == 64 ? 0.125f
+       : d == 128 ? 0.08838834764831845f
+       : d == 256 ? 0.0625f
+       : d == 32 ? 0.17677669529663688f
+       : d == 16 ? 0.25f
+       : d == 8 ? 0.3535533905932738f
+       : d == 4 ? 0.5f
+       : d == 2 ? 0.7071067811865476f : 1.0f;
+}
+
+}  // namespace kvq

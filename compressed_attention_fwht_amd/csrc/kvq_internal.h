@@ -1,0 +1,46 @@
+// Internal launch interface between the C ABI (kvq_abi.hip) and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "kvq_device.h"
+
+namespace kvq {
+
+// Decode-attention tables (LUT + V histogram) must fit this many LDS bytes.
+constexpr size_t ATTN_LDS_TABLES = 150 * 1024;
+constexpr int ATTN_MAX_CHUNK = 4096;   // tokens per split-K chunk, upper bound
+constexpr int ATTN_MIN_CHUNK = 1024;   // preferred lower bound on chunk length
+
+struct AttnPlan {
+  int rp;          // query heads per chunk block (0: tables do not fit LDS)
+  int n_hsplit;    // blocks per KV head along the query heads of its group
+  int n_chunks;    // split-K chunks along the coded tokens
+  int chunk;       // tokens per chunk
+  int pstride;     // floats per partial record (m, l, pad, pad, o[D])
+  size_t lut_bytes, part_bytes, ws_bytes;
+};
+
+AttnPlan attn_plan(int B, int Hq, int Hkv, int D, int S, int G, int C, int Tc, int W);
+
+hipError_t launch_rotate(const void* x, int xt, float* y, int64_t n_rows, int dim, hipStream_t s);
+
+size_t encode_workspace_bytes(int D, int G, int S, int C, int64_t n_books);
+bool encode_mfma_eligible(int D, int G, int S, int C, int xt);
+hipError_t launch_encode(const void* x, int xt, int D, int G, int S, int C, int64_t n_books,
+                         int64_t n_seq, int64_t seq_stride, int64_t n_rows, const float* cb,
+                         uint8_t* codes, int pre_rotated, int force_generic, void* ws,
+                         hipStream_t st);
+
+hipError_t launch_reconstruct(const uint8_t* codes, const float* cb, float* out, int64_t n_books,
+                              int64_t n_per_book, int D, int G, int S, int C, int unrotate,
+                              hipStream_t s);
+
+hipError_t launch_attend(const AttnPlan& p, int B, int Hq, int Hkv, int D, int S, int G, int C,
+                         int Tc, int W, float scale, const float* q, const uint8_t* kc,
+                         const uint8_t* vc, const float* kcb, const float* vcb,
+                         const uint16_t* kw, const uint16_t* vw, float* out, void* ws,
+                         hipStream_t st);
+
+}  // namespace kvq

@@ -1,0 +1,104 @@
+// K3 -- reconstruction from codes: x_rot[g*dsub + j] = sum_s C_sg[z_sg][j],
+// optionally followed by the inverse rotation x = H_D x_rot.
+//
+// "VQKV" summary, 2. Methodology (RSimVQ reconstruction as the sum of the
+// retrieved entries); "VeloxQuant-MLX 0.5.1", Architecture (decode by summing
+// stage outputs, then unrotate).
+//
+// The stage sum is accumulated in float64 and rounded once to float32, so the
+// result is the correctly rounded sum whatever the stage order.  Layout as in
+// K1: L = D/8 lanes per row, 8 output dims per lane (coalesced 32-byte
+// stores), which is also the layout the optional unrotation needs.
+// HBM-bound by the 4*D-byte float32 output per vector.
+#include "kvq_internal.h"
+
+namespace kvq {
+
+template <int D>
+__global__ __launch_bounds__(256) void reconstruct_kernel(
+    const uint8_t* __restrict__ codes, const float* __restrict__ cb, float* __restrict__ out,
+    int64_t n_books, int64_t n_per_book, int G, int S, int C, int dsub, int unrotate) {
+  constexpr int L = D / 8;
+  constexpr int ROWS_PER_WAVE = 64 / L;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t n_total = n_books * n_per_book;
+  const int64_t waves_total = (int64_t)gridDim.x * (blockDim.x >> 6);
+  const int sub = lane / L;
+  const int col = lane % L;
+  const int SG = S * G;
+  const int64_t book_stride = (int64_t)S * G * C * dsub;   // floats per book
+  for (int64_t base = ((int64_t)blockIdx.x * (blockDim.x >> 6) + wave) * ROWS_PER_WAVE;
+       base < n_total; base += waves_total * ROWS_PER_WAVE) {
+    const int64_t vec = base + sub;
+    const bool live = vec < n_total;
+    const int64_t v_ld = live ? vec : (n_total - 1);
+    const int64_t book = v_ld / n_per_book;
+    const uint8_t* crow = codes + v_ld * SG;
+    const float* bk = cb + book * book_stride;
+    double acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.0;
+    if (dsub >= 8) {
+      const int d0 = col * 8;
+      const int g = d0 / dsub, j0 = d0 % dsub;
+      for (int s = 0; s < S; ++s) {
+        int z = crow[s * G + g];
+        z = z < C ? z : C - 1;
+        const float4* p = reinterpret_cast<const float4*>(
+            bk + (((int64_t)s * G + g) * C + z) * dsub + j0);
+        float4 a = p[0], b = p[1];
+        acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
+        acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
+      }
+    } else {
+      for (int s = 0; s < S; ++s) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int d = col * 8 + e;
+          const int g = d / dsub, j = d % dsub;
+          int z = crow[s * G + g];
+          z = z < C ? z : C - 1;
+          acc[e] += bk[(((int64_t)s * G + g) * C + z) * dsub + j];
+        }
+      }
+    }
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (float)acc[e];
+    if (unrotate) {                         // uniform branch: all lanes take it
+      hadamard_row<8, L>(v, lane);
+      constexpr float sc = rsqrt_pow2(D);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] *= sc;
+    }
+    if (live) {
+      float4* o = reinterpret_cast<float4*>(out + vec * D + col * 8);
+      o[0] = make_float4(v[0], v[1], v[2], v[3]);
+      o[1] = make_float4(v[4], v[5], v[6], v[7]);
+    }
+  }
+}
+
+hipError_t launch_reconstruct(const uint8_t* codes, const float* cb, float* out, int64_t n_books,
+                              int64_t n_per_book, int D, int G, int S, int C, int unrotate,
+                              hipStream_t s) {
+  const int64_t n = n_books * n_per_book;
+  if (n == 0) return hipSuccess;
+  const int dsub = D / G;
+  const int rows_per_block = 4 * (64 / (D / 8));
+  int64_t blocks = (n + rows_per_block - 1) / rows_per_block;
+  if (blocks > 65536) blocks = 65536;
+  if (D == 64)
+    reconstruct_kernel<64><<<dim3((unsigned)blocks), 256, 0, s>>>(codes, cb, out, n_books, n_per_book,
+                                                                  G, S, C, dsub, unrotate);
+  else if (D == 128)
+    reconstruct_kernel<128><<<dim3((unsigned)blocks), 256, 0, s>>>(codes, cb, out, n_books, n_per_book,
+                                                                   G, S, C, dsub, unrotate);
+  else
+    reconstruct_kernel<256><<<dim3((unsigned)blocks), 256, 0, s>>>(codes, cb, out, n_books, n_per_book,
+                                                                   G, S, C, dsub, unrotate);
+  return hipGetLastError();
+}
+
+}  // namespace kvq

@@ -1,0 +1,173 @@
+/*
+ * kvq.h -- rotated residual/product vector quantisation of a transformer KV
+ * cache, and single-token decode attention that reads the codes directly.
+ * C ABI of libkvq.so (gfx950 / AMD Instinct MI355X).
+ *
+ * The method (sources are the web pages these calls restate):
+ *   - Rotation: every head vector is multiplied by the orthonormal Sylvester
+ *     Walsh-Hadamard matrix H_D (natural order, entries +-1/sqrt(D)) to spread
+ *     its energy before quantisation ("ZeroKV-Neo 4.0.0", Architecture, FWHT
+ *     energy spreading; "VeloxQuant-MLX 0.5.1", VecInfer, Walsh-Hadamard
+ *     rotation).
+ *   - Encode: the rotated vector is split into G groups of dsub = D/G dims;
+ *     each group runs S greedy residual stages, each picking the nearest entry
+ *     (squared Euclidean distance, lowest index on exact ties) of that
+ *     stage's C-entry codebook and subtracting it ("VQKV" summary,
+ *     2. Methodology, Residual Simple Vector Quantization; "VeloxQuant-MLX
+ *     0.5.1", VecInfer product VQ with one codebook per sub-vector).
+ *   - Reconstruct: the sum over stages of the chosen entries, optionally
+ *     unrotated by H_D ("VQKV" summary, RSimVQ reconstruction;
+ *     "VeloxQuant-MLX 0.5.1", Architecture, decode then unrotate).
+ *   - Decode attention: the query is rotated once (the inverse rotation is
+ *     absorbed into the query, "VeloxQuant-MLX 0.5.1", VecInfer), scored
+ *     against the codes through a per-query table LUT[s][g][c] = q_rot_g .
+ *     C_sg[c] without materialising K ("Differential-KV" README, Decode &
+ *     Prefill Innovations, query scoring in the compressed domain), and the
+ *     coded part is merged with a dense fp16 window of the most recent
+ *     tokens by an fp32 log-sum-exp combine (same README, Flash-Style LSE
+ *     Combine; "VQKV" summary, 3. Inference Integration, local sliding
+ *     window).
+ *
+ * Conventions for every call:
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the
+ *     library never allocates device memory and keeps no state beyond a
+ *     thread-local last-error value.  Scratch memory is passed in as a
+ *     caller-owned workspace whose size the matching *_workspace_size call
+ *     reports.
+ *   - Every argument is validated before any HIP call.  On error nothing is
+ *     launched, outputs are untouched and a status other than KVQ_OK is
+ *     returned.
+ *   - Calls are asynchronous: they enqueue kernels on `stream` and return.
+ *     Results are valid once the caller synchronises that stream.
+ *   - Tensors are dense, row-major, and every pointer must be 16-byte
+ *     aligned.
+ *   - Codes are one byte each (C <= 256); a vector's codes are stored
+ *     stage-major: code(s, g) at byte s*G + g of its S*G-byte row.
+ *   - Codebooks are float32 [S][G][C][dsub].
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#ifndef KVQ_API
+#define KVQ_API __attribute__((visibility("default")))
+#endif
+
+typedef enum {
+  KVQ_OK = 0,
+  KVQ_ERR_NULL = 1,        /* a required pointer is NULL                      */
+  KVQ_ERR_SHAPE = 2,       /* sizes inconsistent or out of range              */
+  KVQ_ERR_UNSUPPORTED = 3, /* valid request this build has no kernel for      */
+  KVQ_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                */
+  KVQ_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required         */
+  KVQ_ERR_DTYPE = 6,       /* unknown element type                            */
+  KVQ_ERR_HIP = 7          /* a HIP launch failed; see kvq_last_hip_error()   */
+} kvq_status;
+
+typedef enum { KVQ_F32 = 0, KVQ_BF16 = 1, KVQ_F16 = 2 } kvq_dtype;
+
+/* Quantiser shape.  head_dim D in {64, 128, 256}; n_groups G divides D;
+ * dsub = D/G a power of two in [8, 128]; 1 <= n_stages S <= 8;
+ * 1 <= n_codewords C <= 256. */
+typedef struct {
+  int32_t head_dim;
+  int32_t n_groups;
+  int32_t n_stages;
+  int32_t n_codewords;
+} kvq_vq_desc;
+
+/* Decode attention shape.  One query token per (sequence, query head).
+ * Query head h reads KV head h / (n_q_heads / n_kv_heads).  The cache of a
+ * (sequence, KV head) holds n_code_tokens coded tokens followed by n_window
+ * fp16 tokens on one position axis; either count may be 0, not both.
+ * softmax_scale <= 0 selects 1/sqrt(head_dim). */
+typedef struct {
+  int32_t batch;
+  int32_t n_q_heads;
+  int32_t n_kv_heads;
+  int32_t n_code_tokens;
+  int32_t n_window;
+  kvq_vq_desc vq;          /* vq.head_dim is the attention head_dim */
+  float softmax_scale;
+} kvq_attn_desc;
+
+/* Flags */
+#define KVQ_INPUT_PRE_ROTATED 0x1u /* kvq_encode: x is already H_D x          */
+#define KVQ_UNROTATE          0x2u /* kvq_decode_reconstruct: output H_D x_rot */
+#define KVQ_ENCODE_GENERIC    0x4u /* kvq_encode: force the plain fp32 kernel  */
+
+/* y = H_D x for n_rows rows of length dim (dim in {64, 128, 256}).
+ * x: [n_rows][dim] of type xt; y: [n_rows][dim] float32.  H_D is symmetric
+ * and orthonormal, so applying it twice returns the input.  x == y is
+ * allowed when xt == KVQ_F32 (in place).  n_rows == 0 is a no-op. */
+KVQ_API kvq_status kvq_rotate(const void* x, kvq_dtype xt, float* y, int64_t n_rows,
+                      int32_t dim, hipStream_t stream);
+
+/* Workspace bytes kvq_encode needs for n_books codebooks of shape *vq
+ * (packed bf16 operand copies of the codebooks).  May be 0. */
+KVQ_API kvq_status kvq_encode_workspace_size(const kvq_vq_desc* vq, int64_t n_books,
+                                     size_t* bytes);
+
+/* Encode rows [0, n_rows) of every sequence into codes.
+ * x:         [n_books][n_seq][seq_stride][D] of type xt (original domain,
+ *            or already rotated with KVQ_INPUT_PRE_ROTATED);
+ * codebooks: [n_books][S][G][C][dsub] float32 -- book b codes the vectors of
+ *            x[b];
+ * codes:     [n_books][n_seq][n_rows][S][G] uint8 (output).
+ * Requires n_rows <= seq_stride.  Any of n_books, n_seq, n_rows may be 0
+ * (no-op).  Codes equal the float64 greedy search except where the best two
+ * squared distances of a stage are within a relative 1e-4 of each other,
+ * where either choice may be returned. */
+KVQ_API kvq_status kvq_encode(const void* x, kvq_dtype xt, const kvq_vq_desc* vq,
+                      int64_t n_books, int64_t n_seq, int64_t seq_stride,
+                      int64_t n_rows, const float* codebooks, uint8_t* codes,
+                      uint32_t flags, void* workspace, size_t ws_bytes,
+                      hipStream_t stream);
+
+/* out[b][n] = sum over stages s (ascending) of codebooks[b][s][g][z(s,g)]
+ * placed at dims g*dsub.., accumulated in float64 and rounded once to
+ * float32 (rotated domain); with KVQ_UNROTATE, H_D is applied afterwards.
+ * codes: [n_books][n_per_book][S][G] uint8; out: [n_books][n_per_book][D]
+ * float32.  Codes >= C are out of range: they read entry C-1 (no fault). */
+KVQ_API kvq_status kvq_decode_reconstruct(const uint8_t* codes, const kvq_vq_desc* vq,
+                                  int64_t n_books, int64_t n_per_book,
+                                  const float* codebooks, float* out,
+                                  uint32_t flags, hipStream_t stream);
+
+/* Workspace bytes kvq_attend_decode needs for shape *a. */
+KVQ_API kvq_status kvq_attend_workspace_size(const kvq_attn_desc* a, size_t* bytes);
+
+/* Single-token decode attention.
+ * q:       [B][Hq][D] float32, original domain;
+ * k_codes, v_codes: [B][Hkv][Tc][S][G] uint8 (Tc = n_code_tokens);
+ * k_cb, v_cb: [S][G][C][dsub] float32 (one codebook set for K, one for V);
+ * k_win, v_win: [B][Hkv][W][D] IEEE fp16 bit patterns (W = n_window; may be
+ *          NULL when W == 0);
+ * out:     [B][Hq][D] float32 = softmax(scale * K q) V over the Tc coded
+ *          tokens (K, V = H_D reconstruction) followed by the W window tokens;
+ * workspace: at least kvq_attend_workspace_size bytes.
+ * Codes >= C read entry C-1 (no fault). */
+KVQ_API kvq_status kvq_attend_decode(const kvq_attn_desc* a, const float* q,
+                             const uint8_t* k_codes, const uint8_t* v_codes,
+                             const float* k_cb, const float* v_cb,
+                             const uint16_t* k_win, const uint16_t* v_win,
+                             float* out, void* workspace, size_t ws_bytes,
+                             hipStream_t stream);
+
+/* Static description of a status code. */
+KVQ_API const char* kvq_status_string(kvq_status status);
+
+/* hipError_t value of the last KVQ_ERR_HIP on the calling thread (0 if none). */
+KVQ_API int kvq_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVQ_H */

@@ -1,0 +1,150 @@
+"""The C-ABI library loads, exports every symbol its header declares, and
+rejects bad arguments before touching the GPU.  CPU only: no call here reaches
+a HIP API (every call below fails validation first, or is a pure host size
+query)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import compressed_attention_fwht_amd as kvq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvq.h")
+
+OK, NULL, SHAPE, UNSUP, ALIGN, WS, DTYPE = 0, 1, 2, 3, 4, 5, 6
+FAKE = 0x10000          # 16-byte aligned, never dereferenced (validation fails first)
+
+
+def _declared():
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"KVQ_API\s+[\w\s\*]+?\b(kvq_\w+)\s*\(", txt)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for n in ("kvq_rotate", "kvq_encode", "kvq_decode_reconstruct", "kvq_attend_decode"):
+        assert n in names
+    assert set(names) == set(kvq.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = kvq.lib
+    for n in _declared():
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", kvq.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    for n in _declared():
+        assert n in exported, n
+    # nothing else of ours leaks out of the shared object
+    assert not [s for s in exported if "kvq" in s and not s.startswith("kvq_")]
+
+
+def test_status_strings():
+    for st in range(8):
+        assert kvq.status_string(st)
+    assert kvq.lib.kvq_last_hip_error() == 0
+
+
+def _vq(D=128, G=16, S=2, C=256):
+    return kvq.VqDesc(D, G, S, C)
+
+
+def _enc(x=FAKE, xt=1, vq=None, nb=1, ns=1, stride=64, rows=64, cb=FAKE, codes=FAKE, flags=0,
+         ws=FAKE, wsb=1 << 30):
+    vq = _vq() if vq is None else vq
+    return kvq.lib.kvq_encode(x, xt, ctypes.byref(vq), nb, ns, stride, rows, cb, codes, flags, ws,
+                              wsb, None)
+
+
+def test_encode_argument_errors():
+    assert _enc(xt=9) == DTYPE
+    assert _enc(x=0) == NULL
+    assert _enc(codes=0) == NULL
+    assert _enc(cb=0) == NULL
+    assert _enc(x=FAKE + 4) == ALIGN
+    assert _enc(codes=FAKE + 8) == ALIGN
+    assert _enc(rows=65) == SHAPE                        # rows beyond the sequence stride
+    assert _enc(nb=-1) == SHAPE
+    assert _enc(flags=0x80) == SHAPE
+    assert _enc(vq=_vq(D=96, G=12)) == SHAPE             # head_dim not 64/128/256
+    assert _enc(vq=_vq(G=15)) == SHAPE                   # G does not divide D
+    assert _enc(vq=_vq(G=32)) == SHAPE                   # dsub 4 < 8
+    assert _enc(vq=_vq(S=0)) == SHAPE
+    assert _enc(vq=_vq(S=9)) == SHAPE
+    assert _enc(vq=_vq(C=257)) == SHAPE
+    assert _enc(vq=_vq(C=0)) == SHAPE
+    assert _enc(ws=0, wsb=0) == WS                       # MFMA path needs the packed books
+    assert _enc(wsb=100) == WS
+    assert _enc(ws=FAKE + 4) == ALIGN
+    # zero-size work is a no-op that returns before any HIP call
+    assert _enc(nb=0) == OK and _enc(ns=0) == OK and _enc(rows=0, x=0, cb=0, codes=0) == OK
+    assert kvq.lib.kvq_encode(FAKE, 1, None, 1, 1, 1, 1, FAKE, FAKE, 0, FAKE, 1, None) == NULL
+
+
+def test_encode_workspace_sizes():
+    assert kvq.encode_workspace_size(128, 16, 2, 256, 64) == 64 * 16 * 2 * 20480
+    assert kvq.encode_workspace_size(128, 16, 1, 256, 2) == 2 * 16 * 20480
+    assert kvq.encode_workspace_size(64, 1, 2, 256, 2) == 0      # generic path, no workspace
+    with pytest.raises(kvq.KvqError):
+        kvq.encode_workspace_size(100, 4, 2, 256, 1)
+
+
+def test_rotate_argument_errors():
+    L = kvq.lib
+    assert L.kvq_rotate(FAKE, 5, FAKE, 10, 128, None) == DTYPE
+    assert L.kvq_rotate(FAKE, 1, FAKE, 10, 100, None) == SHAPE
+    assert L.kvq_rotate(FAKE, 1, FAKE, -1, 128, None) == SHAPE
+    assert L.kvq_rotate(0, 1, FAKE, 10, 128, None) == NULL
+    assert L.kvq_rotate(FAKE, 1, FAKE + 2, 10, 128, None) == ALIGN
+    assert L.kvq_rotate(FAKE, 1, FAKE, 10, 128, None) == SHAPE   # bf16 in place: overlap
+    assert L.kvq_rotate(FAKE, 0, FAKE + 16, 10, 128, None) == SHAPE  # partial f32 overlap
+    assert L.kvq_rotate(0, 1, 0, 0, 128, None) == OK               # no rows: no-op
+
+
+def test_reconstruct_argument_errors():
+    L = kvq.lib
+    vq = _vq()
+    assert L.kvq_decode_reconstruct(0, ctypes.byref(vq), 1, 10, FAKE, FAKE, 0, None) == NULL
+    assert L.kvq_decode_reconstruct(FAKE, ctypes.byref(vq), 1, 10, FAKE, FAKE, 8, None) == SHAPE
+    assert L.kvq_decode_reconstruct(FAKE + 1, ctypes.byref(vq), 1, 10, FAKE, FAKE, 0, None) == ALIGN
+    assert L.kvq_decode_reconstruct(FAKE, ctypes.byref(_vq(S=0)), 1, 10, FAKE, FAKE, 0, None) == SHAPE
+    assert L.kvq_decode_reconstruct(0, ctypes.byref(vq), 1, 0, 0, 0, 0, None) == OK
+
+
+def _attn(B=1, Hq=32, Hkv=8, Tc=1000, W=16, S=1, G=16, C=256, D=128, scale=0.0):
+    return kvq.AttnDesc(B, Hq, Hkv, Tc, W, kvq.VqDesc(D, G, S, C), scale)
+
+
+def _att(a, q=FAKE, kc=FAKE, vc=FAKE, kcb=FAKE, vcb=FAKE, kw=FAKE, vw=FAKE, out=FAKE, ws=FAKE,
+         wsb=1 << 34):
+    return kvq.lib.kvq_attend_decode(ctypes.byref(a), q, kc, vc, kcb, vcb, kw, vw, out, ws, wsb, None)
+
+
+def test_attend_argument_errors():
+    assert _att(_attn(Hq=30)) == SHAPE                 # Hq not a multiple of Hkv
+    assert _att(_attn(Tc=0, W=0)) == SHAPE
+    assert _att(_attn(Tc=-1)) == SHAPE
+    assert _att(_attn(B=0)) == SHAPE
+    assert _att(_attn(scale=float("nan"))) == SHAPE
+    assert _att(_attn(), q=0) == NULL
+    assert _att(_attn(), kc=0) == NULL
+    assert _att(_attn(), kw=0) == NULL
+    assert _att(_attn(W=0), kw=0, vw=0, ws=0) == NULL
+    assert _att(_attn(), out=FAKE + 4) == ALIGN
+    assert _att(_attn(), wsb=10) == WS
+    assert _att(_attn(S=8, G=16)) == UNSUP              # tables exceed LDS
+    assert kvq.lib.kvq_attend_decode(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1,
+                                     None) == NULL
+
+
+def test_attend_workspace_sizes():
+    # LUT B*Hq*S*G*C floats, then per (b, h) (chunks + window) records of D + 4 floats
+    sz = kvq.attend_workspace_size(1, 32, 8, 128, 32640, 128, 1, 16, 256)
+    lut = 32 * 16 * 256 * 4
+    assert sz > lut and (sz - lut) % (32 * 132 * 4) == 0
+    sz_w = kvq.attend_workspace_size(2, 4, 2, 64, 0, 50, 2, 1, 256)   # window only
+    assert sz_w == 2 * 4 * 2 * 256 * 4 + 2 * 4 * 1 * 68 * 4

@@ -1,0 +1,294 @@
+"""Parity of the HIP library (through its C ABI) with the float64 oracle.
+
+Tolerances (see oracle/check.py): codes exact except accepted near ties
+(relative 1e-4), reconstruction 1e-6 absolute (and bit-exact to the rounded
+float64 sum), attention 2e-3 max-abs and 1e-3 relative L2.  Inputs come from
+the seeded workload generator; the reduced sizes keep the distributions of
+the named workloads and span several tiles plus a ragged tail.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import compressed_attention_fwht_amd as kvq
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    torch.cuda.set_device(0)
+    yield
+    torch.cuda.synchronize()
+
+
+def to_dev(inp_x, w):
+    if w.x_dtype == "bf16":
+        return torch.from_numpy(inp_x.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(inp_x).cuda()
+
+
+def cuda(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+# ------------------------------------------------------------------ rotate
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_rotate_identity_is_orthonormal(D):
+    say(f"rotate identity D={D}")
+    y = kvq.rotate(torch.eye(D, dtype=torch.float32, device="cuda")).double().cpu().numpy()
+    assert np.max(np.abs(y @ y.T - np.eye(D))) <= 1e-6
+    assert np.max(np.abs(y - oracle.hadamard_matrix(D))) <= 1e-7
+
+
+@pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("D,n", [(64, 1), (64, 1001), (128, 63), (128, 4097), (256, 333)])
+def test_rotate_parity(dt, D, n):
+    say(f"rotate parity dtype={dt} D={D} rows={n}")
+    g = torch.Generator().manual_seed(D * 7 + n)
+    x = (torch.randn(n, D, generator=g) * 3).to(dt)
+    y = kvq.rotate(x.cuda()).cpu().double().numpy()
+    xd = x.double().numpy()
+    ref = oracle.fwht(xd)
+    nrm = np.linalg.norm(xd, axis=1)
+    assert np.max(np.abs(y - ref).max(axis=1) / nrm) <= 1e-6
+    assert np.max(np.abs(np.linalg.norm(y, axis=1) - nrm) / nrm) <= 1e-6
+
+
+def test_rotate_in_place_f32():
+    say("rotate in place")
+    x = torch.randn(777, 128, dtype=torch.float32)
+    xd = x.cuda()
+    kvq.rotate(xd, out=xd)
+    assert np.max(np.abs(xd.cpu().double().numpy() - oracle.fwht(x.double().numpy()))) <= 1e-5
+
+
+# ------------------------------------------------------------- reconstruct
+@pytest.mark.parametrize("key", [1, 2, 3, 4])
+def test_reconstruct_parity(key):
+    say(f"reconstruct parity workload {key}")
+    w = synth.workload(key)
+    cb = synth.make_codebooks(w)[:2]                        # K and V books
+    rng = np.random.default_rng(key)
+    n = 2000 + 17
+    codes = rng.integers(0, w.n_codewords, size=(2, n, w.n_stages, w.n_groups), dtype=np.uint8)
+    got = kvq.decode_reconstruct(cuda(codes), cuda(cb)).cpu().numpy()
+    for b in range(2):
+        ref = oracle.reconstruct_rot(codes[b], cb[b])
+        assert np.array_equal(got[b], ref.astype(np.float32))     # correctly rounded sum
+        assert oracle.check_recon(got[b], ref)["ok"]
+    got_u = kvq.decode_reconstruct(cuda(codes), cuda(cb), unrotate=True).cpu().numpy()
+    for b in range(2):
+        ref = oracle.reconstruct(codes[b], cb[b])
+        nrm = np.linalg.norm(ref, axis=1, keepdims=True)
+        assert np.max(np.abs(got_u[b] - ref) / nrm) <= 1e-6
+
+
+def test_reconstruct_out_of_range_codes_clamp():
+    say("reconstruct clamp")
+    rng = np.random.default_rng(0)
+    cb = rng.standard_normal((1, 2, 16, 100, 8)).astype(np.float32)
+    codes = rng.integers(0, 256, size=(1, 300, 2, 16), dtype=np.uint8)
+    got = kvq.decode_reconstruct(cuda(codes), cuda(cb)).cpu().numpy()
+    ref = oracle.reconstruct_rot(np.minimum(codes[0], 99), cb[0]).astype(np.float32)
+    assert np.array_equal(got[0], ref)
+
+
+# ------------------------------------------------------------------ encode
+SMALL_ENCODE = [
+    (1, dict()),                                              # tiny, full size
+    (2, dict(tokens=1300, window=128)),                       # n_rows 1172 < stride
+    (3, dict(batch=2, tokens=700, window=64)),
+    (4, dict(tokens=900, window=256)),
+    (5, dict(layers=2, tokens=333)),
+]
+
+
+def _encode_case(key, over, generic=False, pre_rotated=False, f16=False):
+    w = synth.workload(key, **over)
+    inp = synth.make_inputs(w)
+    x = to_dev(inp["x"], w)
+    xf = inp["x_f32"].astype(np.float64)
+    if f16:
+        x = x.float().half()
+        xf = x.float().cpu().numpy().astype(np.float64)
+    if pre_rotated:
+        xr = oracle.fwht(xf)
+        x = torch.from_numpy(xr.astype(np.float32)).cuda()
+        if w.x_dtype == "bf16":
+            x = x.bfloat16()
+        xf = x.double().cpu().numpy()
+    n_rows = w.tokens - w.window
+    codes = kvq.encode(x, cuda(inp["cb"]), n_rows=n_rows, generic=generic,
+                       pre_rotated=pre_rotated).cpu().numpy()
+    tot = {"total": 0, "exact": 0, "near_tie": 0, "hard": 0}
+    for b in range(x.shape[0]):
+        xb = xf[b][:, :n_rows].reshape(-1, w.head_dim)
+        res = oracle.check_codes(xb, inp["cb"][b], codes[b].reshape(-1, w.n_stages, w.n_groups),
+                                 rotate=not pre_rotated)
+        for k in tot:
+            tot[k] += res[k]
+        assert res["hard"] == 0, (key, b, res)
+    return tot
+
+
+@pytest.mark.parametrize("key,over", SMALL_ENCODE)
+@pytest.mark.parametrize("generic", [False, True])
+def test_encode_parity(key, over, generic):
+    say(f"encode parity workload {key} {over} generic={generic}")
+    tot = _encode_case(key, over, generic=generic)
+    say("   ", tot)
+    assert tot["exact"] >= 0.999 * tot["total"]
+
+
+def test_encode_pre_rotated_and_f16():
+    say("encode pre-rotated bf16 / f16 input")
+    for pre, f16 in ((True, False), (False, True)):
+        tot = _encode_case(3, dict(batch=1, tokens=1100, window=64), pre_rotated=pre, f16=f16)
+        assert tot["hard"] == 0 and tot["exact"] >= 0.999 * tot["total"]
+
+
+def test_encode_deterministic():
+    say("encode determinism")
+    w = synth.workload(2, tokens=2000, window=0)
+    inp = synth.make_inputs(w)
+    x, cb = to_dev(inp["x"], w), cuda(inp["cb"])
+    a = kvq.encode(x, cb)
+    b = kvq.encode(x, cb)
+    assert torch.equal(a, b)
+
+
+def test_encode_codeword_inputs_return_own_index():
+    """Pre-rotated inputs that are exactly codeword rows come back with their
+    own indices, on both kernels."""
+    say("encode codeword inputs")
+    rng = np.random.default_rng(4)
+    cb = (rng.standard_normal((1, 1, 16, 256, 8)) * 0.5).astype(np.float32)
+    z = rng.integers(0, 256, size=(512, 16))
+    x = np.stack([np.concatenate([cb[0, 0, g, z[n, g]] for g in range(16)]) for n in range(512)])
+    xb = torch.from_numpy(x).cuda().bfloat16()                   # bf16-exact codewords needed
+    xq = xb.double().cpu().numpy()
+    cbq = np.empty_like(cb)
+    for g in range(16):                                            # book holding the bf16 rows
+        cbq[0, 0, g] = cb[0, 0, g]
+        cbq[0, 0, g, z[:, g]] = xq[:, 8 * g:8 * g + 8]
+    for generic in (False, True):
+        codes = kvq.encode(xb.view(1, 1, 512, 128), cuda(cbq), pre_rotated=True,
+                           generic=generic).cpu().numpy()
+        assert np.array_equal(codes[0, 0, :, 0, :], z)
+
+
+# ------------------------------------------------------------------ decode
+SMALL_DECODE = [
+    (1, dict()),
+    (2, dict(tokens=3000, window=128)),
+    (3, dict(batch=3, tokens=2100, window=64)),
+    (4, dict(tokens=5000, window=256)),
+]
+
+
+def _decode_case(w, inp, codes_k, codes_v, **kw):
+    B, Hkv, Tc = w.batch, w.n_kv_heads, w.code_tokens
+    ck = codes_k.reshape(B, Hkv, Tc, w.n_stages, w.n_groups)
+    cv = codes_v.reshape(B, Hkv, Tc, w.n_stages, w.n_groups)
+    kwin = inp.get("k_win")
+    vwin = inp.get("v_win")
+    kw_t = cuda(kwin) if kwin is not None and w.window > 0 else None
+    vw_t = cuda(vwin) if vwin is not None and w.window > 0 else None
+    got = kvq.attend_decode(cuda(inp["q"]), cuda(ck), cuda(cv), cuda(inp["cb"][0]),
+                            cuda(inp["cb"][1]), kw_t, vw_t, **kw).cpu().numpy()
+    ref = oracle.attend(inp["q"], ck, cv, inp["cb"][0], inp["cb"][1],
+                        kwin if w.window > 0 else None, vwin if w.window > 0 else None,
+                        scale=kw.get("scale"))
+    return oracle.check_attn(got, ref)
+
+
+@pytest.mark.parametrize("key,over", SMALL_DECODE)
+def test_decode_parity(key, over):
+    say(f"decode parity workload {key} {over}")
+    w = synth.workload(key, **over)
+    inp = synth.make_inputs(w)
+    Tc = w.code_tokens
+    codes = [oracle.rvq_encode(inp["x_f32"][b][:, :Tc].reshape(-1, w.head_dim), inp["cb"][b])
+             for b in range(2)]
+    res = _decode_case(w, inp, codes[0], codes[1])
+    say("   ", res)
+    assert res["ok"], res
+
+
+def test_decode_random_codes_and_scale():
+    say("decode random codes, explicit scale, GQA 7")
+    w = synth.workload(3, batch=2, tokens=1500, window=33)
+    inp = synth.make_inputs(w)
+    rng = np.random.default_rng(1)
+    shp = (w.batch * w.n_kv_heads * w.code_tokens, w.n_stages, w.n_groups)
+    ck = rng.integers(0, 256, size=shp, dtype=np.uint8)
+    cv = rng.integers(0, 256, size=shp, dtype=np.uint8)
+    res = _decode_case(w, inp, ck, cv, scale=0.05)
+    assert res["ok"], res
+
+
+def test_decode_window_only_equals_dense_softmax():
+    say("decode window only")
+    w = synth.workload(2, tokens=200, window=200)
+    inp = synth.make_inputs(w)
+    empty = np.zeros((0, w.n_stages, w.n_groups), dtype=np.uint8)
+    res = _decode_case(w, inp, empty, empty)
+    assert res["ok"], res
+
+
+def test_decode_codes_only_short():
+    say("decode codes only, short cache")
+    w = synth.workload(4, tokens=37, window=0)
+    inp = synth.make_inputs(w)
+    codes = [oracle.rvq_encode(inp["x_f32"][b].reshape(-1, 128), inp["cb"][b]) for b in range(2)]
+    res = _decode_case(w, inp, codes[0], codes[1])
+    assert res["ok"], res
+
+
+# ------------------------------------------------- full sizes (sampled encode)
+@pytest.mark.parametrize("key", [2, 3, 4])
+def test_full_size_encode_sampled_and_decode(key):
+    say(f"full-size workload {key}: encode (sampled check) + decode")
+    w = synth.workload(key)
+    inp = synth.make_inputs(w)
+    Tc = w.code_tokens
+    x = to_dev(inp["x"], w)
+    codes = kvq.encode(x, cuda(inp["cb"]), n_rows=Tc)
+    torch.cuda.synchronize()
+    codes_np = codes.cpu().numpy()
+    del x
+    for b in range(2):
+        flat = codes_np[b].reshape(-1, w.n_stages, w.n_groups)
+        xs = inp["x_f32"][b][:, :Tc].reshape(-1, w.head_dim)
+        idx = np.arange(0, flat.shape[0], 97)
+        res = oracle.check_codes(xs[idx].astype(np.float64), inp["cb"][b], flat[idx])
+        say("   book", b, {k: res[k] for k in ("total", "exact", "near_tie", "hard")})
+        assert res["hard"] == 0
+    res = _decode_case(w, inp, codes_np[0], codes_np[1])
+    say("   decode", res)
+    assert res["ok"], res
+
+
+def test_full_size_prefill_layers_sampled():
+    say("prefill workload: 2 of 32 layers at full per-layer size, sampled check")
+    w = synth.workload(5)
+    inp = synth.make_inputs(w, layers=[0, 31])
+    x = to_dev(inp["x"], w)
+    codes = kvq.encode(x, cuda(inp["cb"])).cpu().numpy()
+    for b in range(x.shape[0]):
+        flat = codes[b].reshape(-1, 2, 16)
+        xs = inp["x_f32"][b].reshape(-1, 128)
+        idx = np.arange(0, flat.shape[0], 131)
+        res = oracle.check_codes(xs[idx].astype(np.float64), inp["cb"][b], flat[idx])
+        assert res["hard"] == 0, res
