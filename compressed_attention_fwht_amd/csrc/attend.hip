@@ -17,21 +17,42 @@
 //     summary, 3. Inference Integration, local sliding window of recent
 //     tokens kept uncompressed).
 //
-// Kernels: attn_prep (q rotation, LUT, window partial) -> attn_chunk (code
-// streaming, HBM-bound with LDS gathers) -> attn_merge.
+// Kernels: attn_lut (q rotation slices, LUT) -> attn_chunk (code streaming,
+// K scores, V histogram, contraction) -> attn_merge (window, LSE merge,
+// unrotation).
+//
+// The histogram accumulates the weights p = exp(s - m_chunk) in [0, 1] as
+// fixed-point integers round(p * 2^F) with LDS integer atomics (ds_add_u32,
+// or ds_add_u64 carrying two heads' 32-bit fields at once): on gfx950 LDS
+// float atomics retire an order of magnitude slower than integer ones.
+// F = 31 - ceil(log2(chunk)) keeps every bin and every field sum below 2^31,
+// so packed fields never carry into each other.  The chunk's l is the sum of
+// the same integers, so the rounding of the weights cancels in o = sum p v /
+// sum p to first order.
 #include "kvq_internal.h"
 
 namespace kvq {
+
+static int ceil_log2(int64_t v) {
+  int k = 0;
+  while (((int64_t)1 << k) < v) ++k;
+  return k;
+}
 
 // ----------------------------------------------------------- workspace plan
 AttnPlan attn_plan(int B, int Hq, int Hkv, int D, int S, int G, int C, int Tc, int W) {
   AttnPlan p{};
   const int SG = S * G;
   const int R = Hq / Hkv;
+  int P = 512 / (S * D);
+  if (P < 1) P = 1;
+  p.cparts = P;
   p.rp = 0;
   for (int rp = 4; rp >= 1; rp >>= 1) {
     if (rp > R && rp > 1) continue;
-    if ((size_t)2 * SG * C * rp * sizeof(float) <= ATTN_LDS_TABLES) { p.rp = rp; break; }
+    const size_t tab = (size_t)SG * C * rp * 4;
+    const size_t cpart = (size_t)S * P * rp * D * 4;
+    if (tab + cpart <= ATTN_LDS_TABLES) { p.rp = rp; break; }
   }
   p.n_hsplit = p.rp ? (R + p.rp - 1) / p.rp : 0;
   if (Tc > 0 && p.rp) {
@@ -44,170 +65,174 @@ AttnPlan attn_plan(int B, int Hq, int Hkv, int D, int S, int G, int C, int Tc, i
     if (nc < 1) nc = 1;
     p.n_chunks = (int)nc;
     p.chunk = (int)((Tc + nc - 1) / nc);
-  } else {
-    p.n_chunks = 0;
-    p.chunk = 0;
+    p.fbits = 31 - ceil_log2(p.chunk);
   }
   p.pstride = D + 4;                                    // m, l, pad, pad, o[D]
-  p.lut_bytes = (size_t)B * Hq * SG * C * sizeof(float);
+  p.lut_slice = ((size_t)SG * C * (p.rp ? p.rp : 1) * 4 + 255) & ~(size_t)255;
+  p.lut_bytes = (size_t)B * Hkv * p.n_hsplit * p.lut_slice;
   p.part_bytes = (size_t)B * Hq * (p.n_chunks + 1) * p.pstride * sizeof(float);
   p.ws_bytes = ((p.lut_bytes + 255) & ~(size_t)255) + p.part_bytes;
   return p;
 }
 
-// -------------------------------------------------------------- attn_prep
-// grid (B*Hq), block 256.  q_rot via the in-wave butterfly; LUT (pre-scaled
-// by the softmax scale) to the workspace; window partial (m, l, o) in the
-// original domain to the last partial slot.
-template <int D>
-__global__ __launch_bounds__(256) void attn_prep_kernel(
-    const float* __restrict__ q, const float* __restrict__ kcb, const uint16_t* __restrict__ kw,
-    const uint16_t* __restrict__ vw, float* __restrict__ lut, float* __restrict__ part, int Hq,
-    int Hkv, int S, int G, int C, int W, int n_chunks, int pstride, float scale) {
-  constexpr int L = D / 8;
-  __shared__ float qr[D];
-  __shared__ float qo[D];
-  __shared__ float sw[256];
-  __shared__ float red[8];
-  const int bh = blockIdx.x;
-  const int b = bh / Hq, h = bh - b * Hq;
-  const int kv = h / (Hq / Hkv);
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const float* qp = q + (int64_t)bh * D;
-  if (tid < 64) {
-    const int col = lane % L;
-    float v[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = qp[col * 8 + i];
-    hadamard_row<8, L>(v, lane);
-    constexpr float sc = rsqrt_pow2(D);
-    if (lane < L) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) qr[col * 8 + i] = v[i] * sc;
-    }
-  }
-  for (int d = tid; d < D; d += 256) qo[d] = qp[d];
-  __syncthreads();
-
-  // LUT[s][g][c] = scale * sum_j q_rot[g*dsub + j] * C^K_sg[c][j]
-  const int dsub = D / G;
-  const int SG = S * G;
-  float* lp = lut + (int64_t)bh * SG * C;
-  for (int i = tid; i < SG * C; i += 256) {
-    const int sg = i / C, c = i - sg * C;
-    const int g = sg % G;
-    const float* cp = kcb + ((int64_t)sg * C + c) * dsub;
-    const float* qg = qr + g * dsub;
+// --------------------------------------------------------------- attn_lut
+// grid (B*Hkv*n_hsplit, S*G), block 256.  Block (unit, sg) writes the LUT
+// entries of one (s, g) table for the RP query heads of its unit, laid out
+// [unit][sg][c][RP] so a chunk block stages its whole table with contiguous
+// copies.  Heads past the group's last one repeat it (never read back).
+template <int RP>
+__global__ __launch_bounds__(256) void attn_lut_kernel(const float* __restrict__ q,
+                                                       const float* __restrict__ kcb,
+                                                       float* __restrict__ lut, int Hq, int Hkv,
+                                                       int n_hsplit, int D, int G, int C,
+                                                       size_t lut_slice, float scale) {
+  __shared__ float qs[RP][128];
+  const int unit = blockIdx.x, sg = blockIdx.y;
+  const int hs = unit % n_hsplit;
+  const int bkv = unit / n_hsplit;
+  const int kv = bkv % Hkv, b = bkv / Hkv;
+  const int R = Hq / Hkv;
+  const int nh = (R - hs * RP) < RP ? (R - hs * RP) : RP;
+  const int g = sg % G, dsub = D / G;
+  const float rs = scale / sqrtf((float)D);
+  // scale * (H_D q)[g*dsub + j] = scale/sqrt(D) * sum_i (-1)^popc((g*dsub+j) & i) q[i]
+  for (int idx = threadIdx.x; idx < RP * dsub; idx += 256) {
+    const int r = idx / dsub, j = idx - r * dsub;
+    const int h = kv * R + hs * RP + (r < nh ? r : nh - 1);
+    const float* qp = q + ((int64_t)b * Hq + h) * D;
+    const int row = g * dsub + j;
     float acc = 0.0f;
-    for (int j = 0; j < dsub; ++j) acc = __builtin_fmaf(qg[j], cp[j], acc);
-    lp[i] = acc * scale;
+    for (int i = 0; i < D; ++i) acc += (__builtin_popcount(row & i) & 1) ? -qp[i] : qp[i];
+    qs[r][j] = acc * rs;
   }
-
-  // window partial
-  float* pp = part + ((int64_t)bh * (n_chunks + 1) + n_chunks) * pstride;
-  if (W == 0) {
-    if (tid == 0) { pp[0] = -__builtin_inff(); pp[1] = 0.0f; }
-    for (int d = tid; d < D; d += 256) pp[4 + d] = 0.0f;
-    return;
-  }
-  const uint16_t* kwp = kw + ((int64_t)b * Hkv + kv) * W * D;
-  const uint16_t* vwp = vw + ((int64_t)b * Hkv + kv) * W * D;
-  float mloc = -__builtin_inff();
-  for (int w0 = 0; w0 < W; w0 += 256) {
-    const int w = w0 + tid;
-    if (w < W) {
-      float acc = 0.0f;
-      const uint16_t* kr = kwp + (int64_t)w * D;
-      for (int d = 0; d < D; ++d) acc = __builtin_fmaf(qo[d], f16_bits_to_f32(kr[d]), acc);
-      acc *= scale;
-      mloc = fmaxf(mloc, acc);
-    }
-  }
-  // block max
-  float mw = wave_max(mloc);
-  if (lane == 0) red[tid >> 6] = mw;
   __syncthreads();
-  mw = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  __syncthreads();
-  float lsum = 0.0f;
-  float oacc = 0.0f;                         // thread d accumulates output dim d (d < D)
-  for (int w0 = 0; w0 < W; w0 += 256) {
-    const int w = w0 + tid;
-    float p = 0.0f;
-    if (w < W) {
-      float acc = 0.0f;
-      const uint16_t* kr = kwp + (int64_t)w * D;
-      for (int d = 0; d < D; ++d) acc = __builtin_fmaf(qo[d], f16_bits_to_f32(kr[d]), acc);
-      p = __expf(acc * scale - mw);
+  float* dst = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(lut) + unit * lut_slice) +
+               (size_t)sg * C * RP;
+  for (int c = threadIdx.x; c < C; c += 256) {
+    const float* cp = kcb + ((int64_t)sg * C + c) * dsub;
+    float acc[RP];
+#pragma unroll
+    for (int r = 0; r < RP; ++r) acc[r] = 0.0f;
+    for (int j = 0; j < dsub; ++j) {
+      const float cv = cp[j];
+#pragma unroll
+      for (int r = 0; r < RP; ++r) acc[r] = __builtin_fmaf(qs[r][j], cv, acc[r]);
     }
-    lsum += p;
-    sw[tid] = p;
-    __syncthreads();
-    const int nw = (W - w0) < 256 ? (W - w0) : 256;
-    for (int d = tid; d < D; d += 256) {
-      float a = 0.0f;
-      for (int k = 0; k < nw; ++k) a = __builtin_fmaf(sw[k], f16_bits_to_f32(vwp[(int64_t)(w0 + k) * D + d]), a);
-      oacc += a;                              // D <= 256: one dim per thread
-    }
-    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < RP; ++r) dst[c * RP + r] = acc[r];
   }
-  float ls = wave_sum(lsum);
-  if (lane == 0) red[4 + (tid >> 6)] = ls;
-  __syncthreads();
-  if (tid == 0) { pp[0] = mw; pp[1] = red[4] + red[5] + red[6] + red[7]; }
-  if (tid < D) pp[4 + tid] = oacc;
 }
 
 // ------------------------------------------------------------- attn_chunk
-// grid (n_chunks, Hkv * n_hsplit, B), block 512.  LDS: LUT and histogram,
-// each [SG][C][RP] fp32.  Every thread owns up to CH_TPT tokens of the chunk
-// (token = t0 + tid + 512*k), keeps their RP scores in registers across the
-// two passes (K scores, then softmax weights and V histogram).
+// grid (n_chunks, Hkv * n_hsplit, B), block 512.  LDS: one table region of
+// [S*G][C][RP] 4-byte entries that holds the LUT (floats) during pass 1 and
+// the weight histogram (integers) during pass 2, plus the contraction's
+// partial sums.  Each thread owns up to CH_TPT tokens of the chunk
+// (token = t0 + tid + 512*k) and keeps their RP scores in registers across
+// the two passes.
 constexpr int CH_THREADS = 512;
 constexpr int CH_TPT = ATTN_MAX_CHUNK / CH_THREADS;
+
+template <int RP>
+__device__ __forceinline__ void hist_add(uint32_t* tab, int e, const uint32_t (&pw)[RP]) {
+  if constexpr (RP == 1) {
+    atomicAdd(tab + e, pw[0]);
+  } else {
+    unsigned long long* t64 = reinterpret_cast<unsigned long long*>(tab + e);
+#pragma unroll
+    for (int r = 0; r < RP; r += 2)
+      atomicAdd(t64 + r / 2, (unsigned long long)pw[r] | ((unsigned long long)pw[r + 1] << 32));
+  }
+}
+
+template <int RP>
+__device__ __forceinline__ void lut_add(const float* tab, int e, float (&acc)[RP]) {
+  if constexpr (RP == 4) {
+    const float4 v = *reinterpret_cast<const float4*>(tab + e);
+    acc[0] += v.x; acc[1] += v.y; acc[2] += v.z; acc[3] += v.w;
+  } else if constexpr (RP == 2) {
+    const float2 v = *reinterpret_cast<const float2*>(tab + e);
+    acc[0] += v.x; acc[1] += v.y;
+  } else {
+    acc[0] += tab[e];
+  }
+}
+
+// Visit the S*G code bytes of one token row: f(sg, z) with z clamped below C.
+template <int SGC, typename Fn>
+__device__ __forceinline__ void for_codes(const uint8_t* row, int SG, int C, Fn&& f) {
+  if constexpr (SGC != 0) {
+#pragma unroll
+    for (int w4 = 0; w4 < SGC / 16; ++w4) {
+      const uint4 wv = reinterpret_cast<const uint4*>(row)[w4];
+      const uint32_t ws[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) {
+#pragma unroll
+        for (int by = 0; by < 4; ++by) {
+          int z = (ws[qd] >> (8 * by)) & 255;
+          if (C < 256) z = z < C ? z : C - 1;
+          f(w4 * 16 + qd * 4 + by, z);
+        }
+      }
+    }
+  } else {
+    for (int sg = 0; sg < SG; ++sg) {
+      int z = row[sg];
+      z = z < C ? z : C - 1;
+      f(sg, z);
+    }
+  }
+}
 
 template <int RP, int SGC>   // SGC: compile-time S*G (multiple of 16), or 0 = runtime bytes
 __global__ __launch_bounds__(CH_THREADS, 1) void attn_chunk_kernel(
     const uint8_t* __restrict__ kcodes, const uint8_t* __restrict__ vcodes,
     const float* __restrict__ vcb, const float* __restrict__ lut, float* __restrict__ part,
     int Hq, int Hkv, int D, int S, int G, int C, int Tc, int n_chunks, int chunk, int n_hsplit,
-    int pstride) {
-  extern __shared__ __attribute__((aligned(16))) float sm[];
+    int pstride, int fbits, int cparts, size_t lut_slice) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int SG = SGC ? SGC : S * G;
-  const int tabn = SG * C * RP;
-  float* tl = sm;                       // LUT   [SG][C][RP]
-  float* th = sm + tabn;                // hist  [SG][C][RP]
-  __shared__ float red[16][RP];
-  __shared__ float mx[RP], lt[RP];
+  const int tabn = SG * C * RP;                         // entries in the table region
+  float* tabf = reinterpret_cast<float*>(smem);         // LUT during pass 1
+  uint32_t* tabu = reinterpret_cast<uint32_t*>(smem);   // histogram during pass 2
+  float* cpart = reinterpret_cast<float*>(smem + (((size_t)tabn * 4 + 15) & ~(size_t)15));
+  __shared__ float red_f[8][RP];
+  __shared__ uint32_t red_u[8][RP];
+  __shared__ float mx[RP];
+  __shared__ uint32_t lt[RP];
 
   const int ci = blockIdx.x;
-  const int kvs = blockIdx.y;
+  const int unit = blockIdx.y;                          // kv * n_hsplit + hs
   const int b = blockIdx.z;
-  const int kv = kvs / n_hsplit;
-  const int hs = kvs - kv * n_hsplit;
+  const int kv = unit / n_hsplit, hs = unit - kv * n_hsplit;
   const int R = Hq / Hkv;
-  const int h0 = kv * R + hs * RP;                      // first query head of this block
-  const int nh = (R - hs * RP) < RP ? (R - hs * RP) : RP; // real heads in this block
+  const int h0 = kv * R + hs * RP;
+  const int nh = (R - hs * RP) < RP ? (R - hs * RP) : RP;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int t0 = ci * chunk;
   const int t1 = (t0 + chunk) < Tc ? (t0 + chunk) : Tc;
 
-  // ---- tables
-  for (int i = tid; i < SG * C; i += CH_THREADS) {
-#pragma unroll
-    for (int r = 0; r < RP; ++r) {
-      const int hr = h0 + (r < nh ? r : nh - 1);
-      tl[i * RP + r] = lut[((int64_t)b * Hq + hr) * SG * C + i];
-      th[i * RP + r] = 0.0f;
-    }
+  // ---- stage this unit's LUT: whole 1 KiB pieces straight into LDS, tail by hand
+  {
+    const uint8_t* src = reinterpret_cast<const uint8_t*>(lut) +
+                         ((size_t)b * Hkv * n_hsplit + unit) * lut_slice;
+    const int bytes = tabn * 4;
+    const int full = bytes / 1024;
+    for (int piece = wave; piece < full; piece += CH_THREADS / 64)
+      __builtin_amdgcn_global_load_lds(src + piece * 1024 + lane * 16,
+                                       (__attribute__((address_space(3))) void*)(smem + piece * 1024),
+                                       16, 0, 0);
+    for (int i = full * 256 + tid; i < tabn; i += CH_THREADS)
+      tabu[i] = reinterpret_cast<const uint32_t*>(src)[i];
+    __builtin_amdgcn_s_waitcnt(0x0f70);                  // vmcnt(0)
   }
   __syncthreads();
 
   const int64_t rowbase = ((int64_t)b * Hkv + kv) * (int64_t)Tc;
   float sc[CH_TPT][RP];
-  // ---- pass 1: K scores
+  // ---- pass 1: K scores (LUT gathers, RP heads per read)
 #pragma unroll
   for (int k = 0; k < CH_TPT; ++k) {
     const int t = t0 + tid + CH_THREADS * k;
@@ -217,206 +242,270 @@ __global__ __launch_bounds__(CH_THREADS, 1) void attn_chunk_kernel(
       float acc[RP];
 #pragma unroll
       for (int r = 0; r < RP; ++r) acc[r] = 0.0f;
-      const uint8_t* row = kcodes + (rowbase + t) * SG;
-      if constexpr (SGC != 0) {
-#pragma unroll
-        for (int w4 = 0; w4 < SGC / 16; ++w4) {
-          const uint4 wv = reinterpret_cast<const uint4*>(row)[w4];
-          const uint32_t ws[4] = {wv.x, wv.y, wv.z, wv.w};
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-#pragma unroll
-            for (int by = 0; by < 4; ++by) {
-              const int sg = w4 * 16 + q * 4 + by;
-              int z = (ws[q] >> (8 * by)) & 255;
-              z = z < C ? z : C - 1;
-              const float* e = tl + (sg * C + z) * RP;
-              if constexpr (RP == 4) {
-                const float4 v = *reinterpret_cast<const float4*>(e);
-                acc[0] += v.x; acc[1] += v.y; acc[2] += v.z; acc[3] += v.w;
-              } else if constexpr (RP == 2) {
-                const float2 v = *reinterpret_cast<const float2*>(e);
-                acc[0] += v.x; acc[1] += v.y;
-              } else {
-                acc[0] += e[0];
-              }
-            }
-          }
-        }
-      } else {
-        for (int sg = 0; sg < SG; ++sg) {
-          int z = row[sg];
-          z = z < C ? z : C - 1;
-          const float* e = tl + (sg * C + z) * RP;
-#pragma unroll
-          for (int r = 0; r < RP; ++r) acc[r] += e[r];
-        }
-      }
+      for_codes<SGC>(kcodes + (rowbase + t) * SG, SG, C,
+                     [&](int sg, int z) { lut_add<RP>(tabf, (sg * C + z) * RP, acc); });
 #pragma unroll
       for (int r = 0; r < RP; ++r) sc[k][r] = acc[r];
     }
   }
   // ---- chunk max per head
-  float m[RP];
 #pragma unroll
   for (int r = 0; r < RP; ++r) {
     float v = -__builtin_inff();
 #pragma unroll
     for (int k = 0; k < CH_TPT; ++k) v = fmaxf(v, sc[k][r]);
     v = wave_max(v);
-    if (lane == 0) red[wave][r] = v;
+    if (lane == 0) red_f[wave][r] = v;
   }
-  __syncthreads();
+  __syncthreads();                                      // also: every LUT read is done
   if (tid < RP) {
-    float v = red[0][tid];
-    for (int w = 1; w < CH_THREADS / 64; ++w) v = fmaxf(v, red[w][tid]);
+    float v = red_f[0][tid];
+    for (int w = 1; w < CH_THREADS / 64; ++w) v = fmaxf(v, red_f[w][tid]);
     mx[tid] = v;
   }
+  for (int i = tid; i < tabn; i += CH_THREADS) tabu[i] = 0u;
   __syncthreads();
+  float m[RP];
 #pragma unroll
   for (int r = 0; r < RP; ++r) m[r] = mx[r];
 
-  // ---- pass 2: weights, V histogram
-  float ls[RP];
+  // ---- pass 2: fixed-point weights into the V histogram
+  const float fscale = (float)(1u << fbits);
+  uint32_t ls[RP];
 #pragma unroll
-  for (int r = 0; r < RP; ++r) ls[r] = 0.0f;
+  for (int r = 0; r < RP; ++r) ls[r] = 0u;
 #pragma unroll
   for (int k = 0; k < CH_TPT; ++k) {
     const int t = t0 + tid + CH_THREADS * k;
     if (t < t1) {
-      float p[RP];
+      uint32_t pw[RP];
 #pragma unroll
-      for (int r = 0; r < RP; ++r) { p[r] = __expf(sc[k][r] - m[r]); ls[r] += p[r]; }
-      const uint8_t* row = vcodes + (rowbase + t) * SG;
-      if constexpr (SGC != 0) {
-#pragma unroll
-        for (int w4 = 0; w4 < SGC / 16; ++w4) {
-          const uint4 wv = reinterpret_cast<const uint4*>(row)[w4];
-          const uint32_t ws[4] = {wv.x, wv.y, wv.z, wv.w};
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-#pragma unroll
-            for (int by = 0; by < 4; ++by) {
-              const int sg = w4 * 16 + q * 4 + by;
-              int z = (ws[q] >> (8 * by)) & 255;
-              z = z < C ? z : C - 1;
-              float* e = th + (sg * C + z) * RP;
-#pragma unroll
-              for (int r = 0; r < RP; ++r) atomicAdd(e + r, p[r]);
-            }
-          }
-        }
-      } else {
-        for (int sg = 0; sg < SG; ++sg) {
-          int z = row[sg];
-          z = z < C ? z : C - 1;
-          float* e = th + (sg * C + z) * RP;
-#pragma unroll
-          for (int r = 0; r < RP; ++r) atomicAdd(e + r, p[r]);
-        }
+      for (int r = 0; r < RP; ++r) {
+        pw[r] = (uint32_t)__builtin_rintf(__expf(sc[k][r] - m[r]) * fscale);
+        ls[r] += pw[r];
       }
+      for_codes<SGC>(vcodes + (rowbase + t) * SG, SG, C,
+                     [&](int sg, int z) { hist_add<RP>(tabu, (sg * C + z) * RP, pw); });
     }
   }
 #pragma unroll
   for (int r = 0; r < RP; ++r) {
-    const float v = wave_sum(ls[r]);
-    if (lane == 0) red[8 + wave][r] = v;   // rows 8..15 (max rows no longer needed)
+    uint32_t v = ls[r];
+#pragma unroll
+    for (int msk = 32; msk >= 1; msk >>= 1) v += (uint32_t)__shfl_xor((int)v, msk);
+    if (lane == 0) red_u[wave][r] = v;
   }
   __syncthreads();
   if (tid < RP) {
-    float v = 0.0f;
-    for (int w = 0; w < CH_THREADS / 64; ++w) v += red[8 + w][tid];
+    uint32_t v = 0u;
+    for (int w = 0; w < CH_THREADS / 64; ++w) v += red_u[w][tid];
     lt[tid] = v;
   }
-  __syncthreads();
 
-  // ---- o_rot[r][d] = sum_s sum_c W[s][g(d)][c][r] * C^V[s][g][c][j]
+  // ---- o_rot[r][g*dsub + j] = 2^-F sum_s sum_c W[s][g][c][r] * C^V_sg[c][j].
+  // Item (s, codeword part, 4 consecutive dims): float4 codebook loads,
+  // histogram entries broadcast to the lanes sharing a codeword.
   const int dsub = D / G;
+  const int D4 = D / 4;
+  const int P = cparts;
+  const int cper = (C + P - 1) / P;
+  for (int it = tid; it < S * P * D4; it += CH_THREADS) {
+    const int d4 = it % D4;
+    const int rest = it / D4;
+    const int pi = rest % P, s = rest / P;
+    const int d0 = d4 * 4;
+    const int g = d0 / dsub, j0 = d0 - g * dsub;
+    const int sg = s * G + g;
+    const int c0 = pi * cper, c1 = (c0 + cper) < C ? (c0 + cper) : C;
+    float acc[RP][4];
+#pragma unroll
+    for (int r = 0; r < RP; ++r)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[r][e] = 0.0f;
+    const float* cvp = vcb + (int64_t)sg * C * dsub + j0;
+    const uint32_t* hp = tabu + sg * C * RP;
+#pragma unroll 8
+    for (int c = c0; c < c1; ++c) {
+      const float4 cv = *reinterpret_cast<const float4*>(cvp + (int64_t)c * dsub);
+#pragma unroll
+      for (int r = 0; r < RP; ++r) {
+        const float w = (float)hp[c * RP + r];
+        acc[r][0] = __builtin_fmaf(w, cv.x, acc[r][0]);
+        acc[r][1] = __builtin_fmaf(w, cv.y, acc[r][1]);
+        acc[r][2] = __builtin_fmaf(w, cv.z, acc[r][2]);
+        acc[r][3] = __builtin_fmaf(w, cv.w, acc[r][3]);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < RP; ++r)
+      *reinterpret_cast<float4*>(cpart + ((s * P + pi) * RP + r) * D + d0) =
+          make_float4(acc[r][0], acc[r][1], acc[r][2], acc[r][3]);
+  }
+  __syncthreads();
+  const float inv = 1.0f / fscale;
   for (int o = tid; o < RP * D; o += CH_THREADS) {
     const int r = o / D, d = o - r * D;
     if (r >= nh) continue;
-    const int g = d / dsub, j = d - g * dsub;
-    float acc = 0.0f;
-    for (int s = 0; s < S; ++s) {
-      const int sg = s * G + g;
-      const float* cp = vcb + ((int64_t)sg * C) * dsub + j;
-      const float* hp = th + (sg * C) * RP + r;
-#pragma unroll 8
-      for (int c = 0; c < C; ++c) acc = __builtin_fmaf(hp[c * RP], cp[(int64_t)c * dsub], acc);
-    }
+    float v = 0.0f;
+    for (int sp = 0; sp < S * P; ++sp) v += cpart[(sp * RP + r) * D + d];
     float* pp = part + ((int64_t)(b * Hq + h0 + r) * (n_chunks + 1) + ci) * pstride;
-    pp[4 + d] = acc;
-    if (d == 0) { pp[0] = mx[r]; pp[1] = lt[r]; }
+    pp[4 + d] = v * inv;
+    if (d == 0) { pp[0] = mx[r]; pp[1] = (float)lt[r] * inv; }
   }
 }
 
 // ------------------------------------------------------------- attn_merge
-// grid (B*Hq), block 64.  out = (H * sum_i w_i o_rot_i + w_win o_win) /
-// (sum_i w_i l_i + w_win l_win), w = exp(m - m*).
+// grid (B*Hq), block 256.  The fp16 window's partial (L = D/8 lanes per token
+// row), then out = (H * sum_i w_i o_rot_i + w_win o_win) / (sum_i w_i l_i +
+// w_win l_win), w = exp(m - m*).
 template <int D>
-__global__ __launch_bounds__(64) void attn_merge_kernel(const float* __restrict__ part,
-                                                        float* __restrict__ out, int n_chunks,
-                                                        int pstride) {
+__global__ __launch_bounds__(256) void attn_merge_kernel(
+    const float* __restrict__ q, const uint16_t* __restrict__ kw, const uint16_t* __restrict__ vw,
+    const float* __restrict__ part, float* __restrict__ out, int Hq, int Hkv, int W, int n_chunks,
+    int pstride, float scale) {
   constexpr int L = D / 8;
+  constexpr int ROWS = 256 / L;
+  __shared__ float ow[D];
+  __shared__ float orot[D];
+  __shared__ float wts[256];
+  __shared__ float red[16];
   const int bh = blockIdx.x;
-  const int lane = threadIdx.x;
+  const int b = bh / Hq, h = bh - b * Hq;
+  const int kv = h / (Hq / Hkv);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int row = tid / L, col = tid % L;
+
+  // ---- window partial (mw, lw, ow)
+  for (int d = tid; d < D; d += 256) ow[d] = 0.0f;
+  __syncthreads();
+  float mw = -__builtin_inff(), lw = 0.0f;
+  if (W > 0) {
+    const uint16_t* kwp = kw + ((int64_t)b * Hkv + kv) * W * D + col * 8;
+    const uint16_t* vwp = vw + ((int64_t)b * Hkv + kv) * W * D + col * 8;
+    const float* qp = q + (int64_t)bh * D + col * 8;
+    float qv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qv[e] = qp[e] * scale;
+    float mloc = -__builtin_inff();
+    for (int w0 = 0; w0 < W; w0 += ROWS) {              // uniform trip count
+      const int w = w0 + row;
+      const int wl = w < W ? w : W - 1;
+      float kx[8];
+      load8<2>(kwp + (int64_t)wl * D, kx);
+      float dot = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dot = __builtin_fmaf(qv[e], kx[e], dot);
+      dot = row_sum<L>(dot);
+      if (w < W) mloc = fmaxf(mloc, dot);
+    }
+    mloc = wave_max(mloc);
+    if (lane == 0) red[wave] = mloc;
+    __syncthreads();
+    mw = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    float lsum = 0.0f;
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+    for (int w0 = 0; w0 < W; w0 += ROWS) {
+      const int w = w0 + row;
+      const int wl = w < W ? w : W - 1;
+      float kx[8], vx[8];
+      load8<2>(kwp + (int64_t)wl * D, kx);
+      load8<2>(vwp + (int64_t)wl * D, vx);
+      float dot = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dot = __builtin_fmaf(qv[e], kx[e], dot);
+      dot = row_sum<L>(dot);
+      const float pw = w < W ? __expf(dot - mw) : 0.0f;
+      lsum += pw;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(pw, vx[e], acc[e]);
+    }
+    // rows -> dims: each column's 8 dims summed over the ROWS rows
+#pragma unroll
+    for (int e = 0; e < 8; ++e) atomicAdd(&ow[col * 8 + e], acc[e]);
+    const float lsr = wave_sum(col == 0 ? lsum : 0.0f);  // one lane per row counts lsum
+    if (lane == 0) red[4 + wave] = lsr;
+    __syncthreads();
+    lw = red[4] + red[5] + red[6] + red[7];
+  }
+
+  // ---- chunk partials
   const float* pb = part + (int64_t)bh * (n_chunks + 1) * pstride;
   float mloc = -__builtin_inff();
-  for (int i = lane; i <= n_chunks; i += 64) mloc = fmaxf(mloc, pb[(int64_t)i * pstride]);
-  const float ms = wave_max(mloc);
-  const int col = lane % L;
-  float acc[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+  for (int i = tid; i < n_chunks; i += 256) mloc = fmaxf(mloc, pb[(int64_t)i * pstride]);
+  mloc = wave_max(mloc);
+  if (lane == 0) red[8 + wave] = mloc;
+  __syncthreads();
+  float ms = fmaxf(fmaxf(red[8], red[9]), fmaxf(red[10], red[11]));
+  ms = fmaxf(ms, mw);
+  float oacc = 0.0f;                                    // thread d (< D): sum_i w_i o_rot_i[d]
   float den = 0.0f;
-  for (int i = 0; i < n_chunks; ++i) {
-    const float* pi = pb + (int64_t)i * pstride;
-    const float mi = pi[0];
-    if (mi == -__builtin_inff()) continue;
-    const float wgt = __expf(mi - ms);
-    den = __builtin_fmaf(wgt, pi[1], den);
-    const float4* o4 = reinterpret_cast<const float4*>(pi + 4 + col * 8);
-    const float4 a = o4[0], c = o4[1];
-    acc[0] = __builtin_fmaf(wgt, a.x, acc[0]); acc[1] = __builtin_fmaf(wgt, a.y, acc[1]);
-    acc[2] = __builtin_fmaf(wgt, a.z, acc[2]); acc[3] = __builtin_fmaf(wgt, a.w, acc[3]);
-    acc[4] = __builtin_fmaf(wgt, c.x, acc[4]); acc[5] = __builtin_fmaf(wgt, c.y, acc[5]);
-    acc[6] = __builtin_fmaf(wgt, c.z, acc[6]); acc[7] = __builtin_fmaf(wgt, c.w, acc[7]);
+  for (int i0 = 0; i0 < n_chunks; i0 += 256) {
+    const int i = i0 + tid;
+    float wgt = 0.0f, lv = 0.0f;
+    if (i < n_chunks) {
+      const float mi = pb[(int64_t)i * pstride];
+      wgt = mi == -__builtin_inff() ? 0.0f : __expf(mi - ms);
+      lv = pb[(int64_t)i * pstride + 1];
+    }
+    wts[tid] = wgt;
+    den += wgt * lv;
+    __syncthreads();
+    const int n = (n_chunks - i0) < 256 ? (n_chunks - i0) : 256;
+    if (tid < D) {
+#pragma unroll 8
+      for (int k = 0; k < n; ++k)
+        oacc = __builtin_fmaf(wts[k], pb[(int64_t)(i0 + k) * pstride + 4 + tid], oacc);
+    }
+    __syncthreads();
   }
-  hadamard_row<8, L>(acc, lane);
-  constexpr float sc = rsqrt_pow2(D);
-  const float* pw = pb + (int64_t)n_chunks * pstride;
-  const float mw = pw[0];
+  den = wave_sum(den);
+  if (lane == 0) red[12 + wave] = den;
+  if (tid < D) orot[tid] = oacc;
+  __syncthreads();
   const float ww = mw == -__builtin_inff() ? 0.0f : __expf(mw - ms);
-  den = __builtin_fmaf(ww, pw[1], den);
-  const float inv = 1.0f / den;
-  if (lane < L) {
-    const float4* o4 = reinterpret_cast<const float4*>(pw + 4 + col * 8);
-    const float4 a = o4[0], c = o4[1];
-    const float wv[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
-    float r[8];
+  const float total = red[12] + red[13] + red[14] + red[15] + ww * lw;
+  if (tid < 64) {                                        // one wave unrotates the coded part
+    float v[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) r[e] = (acc[e] * sc + ww * wv[e]) * inv;
-    float4* op = reinterpret_cast<float4*>(out + (int64_t)bh * D + col * 8);
-    op[0] = make_float4(r[0], r[1], r[2], r[3]);
-    op[1] = make_float4(r[4], r[5], r[6], r[7]);
+    for (int e = 0; e < 8; ++e) v[e] = orot[col * 8 + e];
+    hadamard_row<8, L>(v, lane);
+    if (lane < L) {
+      constexpr float sc = rsqrt_pow2(D);
+      const float inv = 1.0f / total;
+      float r[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) r[e] = (v[e] * sc + ww * ow[col * 8 + e]) * inv;
+      float4* op = reinterpret_cast<float4*>(out + (int64_t)bh * D + col * 8);
+      op[0] = make_float4(r[0], r[1], r[2], r[3]);
+      op[1] = make_float4(r[4], r[5], r[6], r[7]);
+    }
   }
 }
 
 // --------------------------------------------------------------- launcher
 template <int RP>
-static hipError_t launch_chunk_rp(const AttnPlan& p, int SG, const uint8_t* kc, const uint8_t* vc,
-                                  const float* vcb, const float* lut, float* part, int B, int Hq,
-                                  int Hkv, int D, int S, int G, int C, int Tc, hipStream_t st) {
+static hipError_t launch_rp(const AttnPlan& p, int SG, const float* q, const float* kcb,
+                            const uint8_t* kc, const uint8_t* vc, const float* vcb, float* lut,
+                            float* part, int B, int Hq, int Hkv, int D, int S, int G, int C, int Tc,
+                            float scale, hipStream_t st) {
+  attn_lut_kernel<RP><<<dim3(B * Hkv * p.n_hsplit, SG), 256, 0, st>>>(
+      q, kcb, lut, Hq, Hkv, p.n_hsplit, D, G, C, p.lut_slice, scale);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   dim3 grid(p.n_chunks, Hkv * p.n_hsplit, B);
-  const size_t lds = (size_t)2 * SG * C * RP * sizeof(float);
+  const size_t tab = (((size_t)SG * C * RP * 4) + 15) & ~(size_t)15;
+  const size_t lds = tab + (size_t)S * p.cparts * RP * D * 4;
 #define KVQ_CH(SGV)                                                                            \
   {                                                                                            \
     auto kern = attn_chunk_kernel<RP, SGV>;                                                    \
-    hipError_t e = hipFuncSetAttribute((const void*)kern,                                      \
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);  \
+    e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,     \
+                            (int)lds);                                                         \
     if (e != hipSuccess) return e;                                                             \
     kern<<<grid, CH_THREADS, lds, st>>>(kc, vc, vcb, lut, part, Hq, Hkv, D, S, G, C, Tc,       \
-                                        p.n_chunks, p.chunk, p.n_hsplit, p.pstride);           \
+                                        p.n_chunks, p.chunk, p.n_hsplit, p.pstride, p.fbits,   \
+                                        p.cparts, p.lut_slice);                                \
     return hipGetLastError();                                                                  \
   }
   if (SG == 16) KVQ_CH(16)
@@ -435,22 +524,19 @@ hipError_t launch_attend(const AttnPlan& p, int B, int Hq, int Hkv, int D, int S
   float* part = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) +
                                          ((p.lut_bytes + 255) & ~(size_t)255));
   const int SG = S * G;
-#define KVQ_PREP(DD)                                                                          \
-  attn_prep_kernel<DD><<<dim3(B * Hq), 256, 0, st>>>(q, kcb, kw, vw, lut, part, Hq, Hkv, S, G,  \
-                                                     C, W, p.n_chunks, p.pstride, scale);
-  if (D == 64) { KVQ_PREP(64) } else if (D == 128) { KVQ_PREP(128) } else { KVQ_PREP(256) }
-#undef KVQ_PREP
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  hipError_t e = hipSuccess;
   if (p.n_chunks > 0) {
-    if (p.rp == 4) e = launch_chunk_rp<4>(p, SG, kc, vc, vcb, lut, part, B, Hq, Hkv, D, S, G, C, Tc, st);
-    else if (p.rp == 2) e = launch_chunk_rp<2>(p, SG, kc, vc, vcb, lut, part, B, Hq, Hkv, D, S, G, C, Tc, st);
-    else e = launch_chunk_rp<1>(p, SG, kc, vc, vcb, lut, part, B, Hq, Hkv, D, S, G, C, Tc, st);
+    if (p.rp == 4) e = launch_rp<4>(p, SG, q, kcb, kc, vc, vcb, lut, part, B, Hq, Hkv, D, S, G, C, Tc, scale, st);
+    else if (p.rp == 2) e = launch_rp<2>(p, SG, q, kcb, kc, vc, vcb, lut, part, B, Hq, Hkv, D, S, G, C, Tc, scale, st);
+    else e = launch_rp<1>(p, SG, q, kcb, kc, vc, vcb, lut, part, B, Hq, Hkv, D, S, G, C, Tc, scale, st);
     if (e != hipSuccess) return e;
   }
-  if (D == 64) attn_merge_kernel<64><<<dim3(B * Hq), 64, 0, st>>>(part, out, p.n_chunks, p.pstride);
-  else if (D == 128) attn_merge_kernel<128><<<dim3(B * Hq), 64, 0, st>>>(part, out, p.n_chunks, p.pstride);
-  else attn_merge_kernel<256><<<dim3(B * Hq), 64, 0, st>>>(part, out, p.n_chunks, p.pstride);
+#define KVQ_MG(DD) attn_merge_kernel<DD><<<dim3(B * Hq), 256, 0, st>>>(q, kw, vw, part, out, Hq, Hkv, \
+                                                                       W, p.n_chunks, p.pstride, scale)
+  if (D == 64) KVQ_MG(64);
+  else if (D == 128) KVQ_MG(128);
+  else KVQ_MG(256);
+#undef KVQ_MG
   return hipGetLastError();
 }
 

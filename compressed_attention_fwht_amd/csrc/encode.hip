@@ -86,18 +86,41 @@ __device__ __forceinline__ int64_t row_elem(int64_t book, int64_t n, int64_t n_r
   return ((book * n_seq + seq) * seq_stride + row) * 128;
 }
 
+// Copy one group's S packed stage blocks (S * 20480 contiguous bytes) from
+// global memory straight into LDS with global_load_lds_dwordx4: each
+// instruction moves 64 lanes x 16 bytes into 1 KiB of LDS at a wave-uniform
+// base.  Completion is awaited with wait_vmem().
+template <int S>
+__device__ __forceinline__ void stage_group(const uint8_t* src, uint8_t* dst, int wave, int lane) {
+  constexpr int KIB = S * PACK_BYTES / 1024;             // 1 KiB pieces (20 per stage)
+#pragma unroll
+  for (int k = 0; k < (KIB + MF_WAVES - 1) / MF_WAVES; ++k) {
+    const int piece = k * MF_WAVES + wave;               // wave-uniform
+    if (piece < KIB)
+      __builtin_amdgcn_global_load_lds(src + piece * 1024 + lane * 16,
+                                       (__attribute__((address_space(3))) void*)(dst + piece * 1024),
+                                       16, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void wait_vmem() {
+  __builtin_amdgcn_s_waitcnt(0x0f70);                    // vmcnt(0)
+}
+
 template <int S, int XT>
 __global__ __launch_bounds__(512, 1) void encode_mfma_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ packed, uint8_t* __restrict__ codes,
     int64_t n_seq, int64_t seq_stride, int64_t n_rows, int64_t tiles_per_book, int pre_rotated) {
   constexpr int G = 16;
   constexpr int SG = S * G;
+  // LDS: two buffers of one group's S stage blocks (double buffering); the
+  // per-wave transpose scratch of the tile's input rows aliases them, since
+  // it is dead before the first codebook load is issued.
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  uint8_t* cbs = smem;                                    // S * 20480 bytes: staged group
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int h = lane >> 5;                                // lane half
-  uint8_t* scratch = smem + S * PACK_BYTES + wave * MF_SCRATCH;
+  uint8_t* scratch = smem + wave * MF_SCRATCH;
 
   const int64_t book = blockIdx.x / tiles_per_book;
   const int64_t tile = blockIdx.x - book * tiles_per_book;
@@ -132,6 +155,10 @@ __global__ __launch_bounds__(512, 1) void encode_mfma_kernel(
     __syncthreads();                                    // scratch free for the next round
   }
 
+  const uint8_t* pk_book = packed + book * (int64_t)G * S * PACK_BYTES;
+  // group 0's codebooks load while the rotation runs
+  stage_group<S>(pk_book, smem, wave, lane);
+
   // ---- y = H x (or x itself when pre-rotated), float32 in registers
   float y[128];
 #pragma unroll
@@ -164,20 +191,21 @@ __global__ __launch_bounds__(512, 1) void encode_mfma_kernel(
   uint32_t cw[SG / 4];
 #pragma unroll
   for (int i = 0; i < SG / 4; ++i) cw[i] = 0u;
+  wait_vmem();
+  __syncthreads();                                        // group 0 staged
 
-  const uint8_t* pk_book = packed + book * (int64_t)G * S * PACK_BYTES;
   const int m_lane = lane & 31;
+  // 0xffffff00 held in a vector register (an opaque value, so the compiler
+  // keeps it as the v_and_or_b32 mask operand instead of a literal)
+  uint32_t keep_hi = 0xffffff00u;
+  asm volatile("" : "+v"(keep_hi));
 
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    // ---- stage this group's S codebooks into LDS
-    __syncthreads();
-    {
-      const uint4* src = reinterpret_cast<const uint4*>(pk_book + (int64_t)g * S * PACK_BYTES);
-      uint4* dst = reinterpret_cast<uint4*>(cbs);
-      for (int i = threadIdx.x; i < S * PACK_BYTES / 16; i += 512) dst[i] = src[i];
-    }
-    __syncthreads();
+    const uint8_t* cbs = smem + (g & 1) * (S * PACK_BYTES);
+    // ---- the next group's codebooks stream into the other buffer meanwhile
+    if (g + 1 < G) stage_group<S>(pk_book + (int64_t)(g + 1) * S * PACK_BYTES,
+                                  smem + ((g + 1) & 1) * (S * PACK_BYTES), wave, lane);
 
     float r[8];
 #pragma unroll
@@ -192,10 +220,9 @@ __global__ __launch_bounds__(512, 1) void encode_mfma_kernel(
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const float a = r[2 * k], b = r[2 * k + 1];
-        const uint32_t ha = f32_to_bf16_rne(a), hb = f32_to_bf16_rne(b);
-        hi[k] = ha | (hb << 16);
-        const float la = a - bf16_bits_to_f32(ha), lb = b - bf16_bits_to_f32(hb);
-        lo[k] = f32_to_bf16_rne(la) | (f32_to_bf16_rne(lb) << 16);
+        hi[k] = cvt_pk_bf16(a, b);
+        const float la = a - bf16_lo(hi[k]), lb = b - bf16_hi(hi[k]);
+        lo[k] = cvt_pk_bf16(la, lb);
         nrm = __builtin_fmaf(a, a, nrm);
         nrm = __builtin_fmaf(b, b, nrm);
       }
@@ -218,6 +245,9 @@ __global__ __launch_bounds__(512, 1) void encode_mfma_kernel(
       __builtin_memcpy(&B2T0, b2t0, 16); __builtin_memcpy(&B2T1, b2t1, 16);
 
       int best0 = 0x7fffffff, best1 = 0x7fffffff;
+      // The tile loop stays rolled: the packed index (32t | row) is then a
+      // scalar register and each candidate costs one v_and_or_b32.
+#pragma nounroll
       for (int t = 0; t < 8; ++t) {
         const int m = 32 * t + m_lane;
         const uint4 a1 = *reinterpret_cast<const uint4*>(cbs_s + h * 4096 + m * 16);
@@ -230,13 +260,13 @@ __global__ __launch_bounds__(512, 1) void encode_mfma_kernel(
         acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A1, B1T1, acc1, 0, 0, 0);
         acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A2, B2T0, acc0, 0, 0, 0);
         acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A2, B2T1, acc1, 0, 0, 0);
-        const int tb = t << 5;
+        const uint32_t tb = (uint32_t)__builtin_amdgcn_readfirstlane(t << 5);
         // accumulator register i holds codeword row 8*(i/4) + 4*h + (i%4) of the tile
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int idx = tb | (8 * (i >> 2) + (i & 3));
-          const int k0 = (int)((__float_as_uint(acc0[i]) & 0xffffff00u) | (uint32_t)idx);
-          const int k1 = (int)((__float_as_uint(acc1[i]) & 0xffffff00u) | (uint32_t)idx);
+          const uint32_t idx = tb | (uint32_t)(8 * (i >> 2) + (i & 3));
+          const int k0 = (int)((__float_as_uint(acc0[i]) & keep_hi) | idx);
+          const int k1 = (int)((__float_as_uint(acc1[i]) & keep_hi) | idx);
           best0 = min(best0, k0);
           best1 = min(best1, k1);
         }
@@ -257,6 +287,10 @@ __global__ __launch_bounds__(512, 1) void encode_mfma_kernel(
         r[4] -= c1.x; r[5] -= c1.y; r[6] -= c1.z; r[7] -= c1.w;
       }
     }
+    // own loads of the next group landed; after the barrier every wave's have,
+    // and every wave is done reading this group's buffer
+    wait_vmem();
+    __syncthreads();
   }
 
   if (live) {
@@ -364,7 +398,8 @@ static hipError_t launch_mfma_t(const void* x, const uint8_t* packed, uint8_t* c
                                 int pre_rotated, hipStream_t st) {
   const int64_t n_per_book = n_seq * n_rows;
   const int64_t tiles = (n_per_book + MF_TILE - 1) / MF_TILE;
-  const size_t lds = (size_t)S * PACK_BYTES + MF_WAVES * MF_SCRATCH;
+  size_t lds = (size_t)2 * S * PACK_BYTES;                 // two codebook buffers
+  if (lds < (size_t)MF_WAVES * MF_SCRATCH) lds = (size_t)MF_WAVES * MF_SCRATCH;
   auto kern = encode_mfma_kernel<S, XT>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)lds);

@@ -29,6 +29,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
+// Two floats -> packed bf16 pair (lo in bits 0-15), round to nearest even,
+// by the hardware converter (v_cvt_pk_bf16_f32).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
 // Load 8 consecutive elements of a row of type xt (0 f32, 1 bf16, 2 f16) as
 // float.  p points at the first element; 16-byte aligned for bf16/f16, and
 // 32-byte aligned rows for f32 are read as two 16-byte loads.
@@ -110,6 +119,18 @@ __device__ __forceinline__ void hadamard_row(float (&v)[E], int lane) {
   KVQ_XSTAGE(8)
   KVQ_XSTAGE(16)
 #undef KVQ_XSTAGE
+}
+
+// Sum over the L consecutive lanes of a row (L a power of two <= 32); every
+// lane of the row receives the sum.  All lanes of the wavefront execute this.
+template <int L>
+__device__ __forceinline__ float row_sum(float x) {
+  if constexpr (L > 1) x += xor_lane<1>(x);
+  if constexpr (L > 2) x += xor_lane<2>(x);
+  if constexpr (L > 4) x += xor_lane<4>(x);
+  if constexpr (L > 8) x += xor_lane<8>(x);
+  if constexpr (L > 16) x += xor_lane<16>(x);
+  return x;
 }
 
 // Wavefront reductions (all 64 lanes participate).

@@ -18,7 +18,10 @@ struct AttnPlan {
   int n_hsplit;    // blocks per KV head along the query heads of its group
   int n_chunks;    // split-K chunks along the coded tokens
   int chunk;       // tokens per chunk
+  int fbits;       // fixed-point fraction bits of the softmax-weight histogram
+  int cparts;      // codeword ranges per (stage, dims) item in the V contraction
   int pstride;     // floats per partial record (m, l, pad, pad, o[D])
+  size_t lut_slice;  // bytes of one (sequence, KV head, head split) LUT slice
   size_t lut_bytes, part_bytes, ws_bytes;
 };
 

@@ -136,7 +136,7 @@ def test_attend_argument_errors():
     assert _att(_attn(W=0), kw=0, vw=0, ws=0) == NULL
     assert _att(_attn(), out=FAKE + 4) == ALIGN
     assert _att(_attn(), wsb=10) == WS
-    assert _att(_attn(S=8, G=16)) == UNSUP              # tables exceed LDS
+    assert _att(_attn(D=256, S=8, G=32)) == UNSUP       # tables exceed LDS
     assert kvq.lib.kvq_attend_decode(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1,
                                      None) == NULL
 
