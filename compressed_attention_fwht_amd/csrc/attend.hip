@@ -11,15 +11,16 @@
 //     of softmax weights, W_sg[c] = sum_t p_t [z_tsg == c], and contracted
 //     once per chunk: o_rot = sum_sg sum_c W_sg[c] C^V_sg[c].
 //   * The token axis is split into chunks (split-K); each chunk emits an
-//     fp32 partial (m, l, o_rot) and the merge kernel combines the chunks and
-//     the dense fp16 window by log-sum-exp in fp32, unrotating the coded part
-//     once ("Differential-KV" README, Flash-Style LSE Combine; "VQKV"
+//     fp32 partial (m, l, o_rot).  The dense fp16 window is split the same way
+//     into blocks of the same grid, whose partials stay in the original
+//     domain.  The merge kernel combines all partials by log-sum-exp in fp32,
+//     unrotating the coded part once ("Differential-KV" README, Flash-Style LSE Combine; "VQKV"
 //     summary, 3. Inference Integration, local sliding window of recent
 //     tokens kept uncompressed).
 //
 // Kernels: attn_lut (q rotation slices, LUT) -> attn_chunk (code streaming,
-// K scores, V histogram, contraction) -> attn_merge (window, LSE merge,
-// unrotation).
+// K scores, V histogram, contraction; window blocks) -> attn_merge (LSE
+// merge, unrotation).
 //
 // The histogram accumulates the weights p = exp(s - m_chunk) in [0, 1] as
 // fixed-point integers round(p * 2^F) with LDS integer atomics (ds_add_u32,
@@ -44,15 +45,19 @@ AttnPlan attn_plan(int B, int Hq, int Hkv, int D, int S, int G, int C, int Tc, i
   AttnPlan p{};
   const int SG = S * G;
   const int R = Hq / Hkv;
-  int P = 512 / (S * D);
-  if (P < 1) P = 1;
-  p.cparts = P;
+  // codeword ranges per (stage, 4-dim) item of the V contraction: aim at 512
+  // items (at most 16 ranges), fewer when LDS is short; more heads per block
+  // win over more ranges
+  int P0 = 512 / (S * (D / 4));
+  if (P0 < 1) P0 = 1;
+  if (P0 > 16) P0 = 16;
   p.rp = 0;
-  for (int rp = 4; rp >= 1; rp >>= 1) {
+  for (int rp = 4; rp >= 1 && !p.rp; rp >>= 1) {
     if (rp > R && rp > 1) continue;
     const size_t tab = (size_t)SG * C * rp * 4;
-    const size_t cpart = (size_t)S * P * rp * D * 4;
-    if (tab + cpart <= ATTN_LDS_TABLES) { p.rp = rp; break; }
+    for (int P = P0; P >= 1; P >>= 1) {
+      if (tab + (size_t)S * P * rp * D * 4 <= ATTN_LDS_TABLES) { p.rp = rp; p.cparts = P; break; }
+    }
   }
   p.n_hsplit = p.rp ? (R + p.rp - 1) / p.rp : 0;
   if (Tc > 0 && p.rp) {
@@ -63,14 +68,20 @@ AttnPlan attn_plan(int B, int Hq, int Hkv, int D, int S, int G, int C, int Tc, i
     if (nc > max_nc) nc = max_nc;
     if (nc < min_nc) nc = min_nc;
     if (nc < 1) nc = 1;
-    p.n_chunks = (int)nc;
     p.chunk = (int)((Tc + nc - 1) / nc);
+    p.n_chunks = (int)((Tc + p.chunk - 1) / p.chunk);   // no empty trailing chunk
     p.fbits = 31 - ceil_log2(p.chunk);
   }
+  if (Tc == 0) {                                        // window only: no tables needed
+    p.rp = R >= 4 ? 4 : R >= 2 ? 2 : 1;
+    p.n_hsplit = (R + p.rp - 1) / p.rp;
+    p.cparts = 1;
+  }
+  p.n_wblocks = W > 0 ? (W + ATTN_WIN_BLOCK - 1) / ATTN_WIN_BLOCK : 0;
   p.pstride = D + 4;                                    // m, l, pad, pad, o[D]
   p.lut_slice = ((size_t)SG * C * (p.rp ? p.rp : 1) * 4 + 255) & ~(size_t)255;
-  p.lut_bytes = (size_t)B * Hkv * p.n_hsplit * p.lut_slice;
-  p.part_bytes = (size_t)B * Hq * (p.n_chunks + 1) * p.pstride * sizeof(float);
+  p.lut_bytes = p.n_chunks ? (size_t)B * Hkv * p.n_hsplit * p.lut_slice : 0;
+  p.part_bytes = (size_t)B * Hq * (p.n_chunks + p.n_wblocks) * p.pstride * sizeof(float);
   p.ws_bytes = ((p.lut_bytes + 255) & ~(size_t)255) + p.part_bytes;
   return p;
 }
@@ -80,13 +91,15 @@ AttnPlan attn_plan(int B, int Hq, int Hkv, int D, int S, int G, int C, int Tc, i
 // entries of one (s, g) table for the RP query heads of its unit, laid out
 // [unit][sg][c][RP] so a chunk block stages its whole table with contiguous
 // copies.  Heads past the group's last one repeat it (never read back).
-template <int RP>
+template <int RP, int D>
 __global__ __launch_bounds__(256) void attn_lut_kernel(const float* __restrict__ q,
                                                        const float* __restrict__ kcb,
                                                        float* __restrict__ lut, int Hq, int Hkv,
-                                                       int n_hsplit, int D, int G, int C,
+                                                       int n_hsplit, int G, int C,
                                                        size_t lut_slice, float scale) {
-  __shared__ float qs[RP][128];
+  constexpr int L = D / 8;                 // lanes per query row in the butterfly
+  constexpr int ROWS = 64 / L;             // query rows per wave
+  __shared__ float qs[RP][D];
   const int unit = blockIdx.x, sg = blockIdx.y;
   const int hs = unit % n_hsplit;
   const int bkv = unit / n_hsplit;
@@ -94,21 +107,30 @@ __global__ __launch_bounds__(256) void attn_lut_kernel(const float* __restrict__
   const int R = Hq / Hkv;
   const int nh = (R - hs * RP) < RP ? (R - hs * RP) : RP;
   const int g = sg % G, dsub = D / G;
-  const float rs = scale / sqrtf((float)D);
-  // scale * (H_D q)[g*dsub + j] = scale/sqrt(D) * sum_i (-1)^popc((g*dsub+j) & i) q[i]
-  for (int idx = threadIdx.x; idx < RP * dsub; idx += 256) {
-    const int r = idx / dsub, j = idx - r * dsub;
-    const int h = kv * R + hs * RP + (r < nh ? r : nh - 1);
-    const float* qp = q + ((int64_t)b * Hq + h) * D;
-    const int row = g * dsub + j;
-    float acc = 0.0f;
-    for (int i = 0; i < D; ++i) acc += (__builtin_popcount(row & i) & 1) ? -qp[i] : qp[i];
-    qs[r][j] = acc * rs;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // scale * H_D q for the RP heads: wave 0, L lanes x 8 elements per row
+  if (tid < 64) {
+#pragma unroll
+    for (int r0 = 0; r0 < RP; r0 += ROWS) {
+      const int r = r0 + lane / L;
+      const int rr = r < RP ? r : RP - 1;
+      const int h = kv * R + hs * RP + (rr < nh ? rr : nh - 1);
+      const float* qp = q + ((int64_t)b * Hq + h) * D + (lane % L) * 8;
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = qp[e];
+      hadamard_row<8, L>(v, lane);
+      const float rs = scale * rsqrt_pow2(D);
+      if (r < RP) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qs[r][(lane % L) * 8 + e] = v[e] * rs;
+      }
+    }
   }
   __syncthreads();
   float* dst = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(lut) + unit * lut_slice) +
                (size_t)sg * C * RP;
-  for (int c = threadIdx.x; c < C; c += 256) {
+  for (int c = tid; c < C; c += 256) {
     const float* cp = kcb + ((int64_t)sg * C + c) * dsub;
     float acc[RP];
 #pragma unroll
@@ -116,7 +138,7 @@ __global__ __launch_bounds__(256) void attn_lut_kernel(const float* __restrict__
     for (int j = 0; j < dsub; ++j) {
       const float cv = cp[j];
 #pragma unroll
-      for (int r = 0; r < RP; ++r) acc[r] = __builtin_fmaf(qs[r][j], cv, acc[r]);
+      for (int r = 0; r < RP; ++r) acc[r] = __builtin_fmaf(qs[r][g * dsub + j], cv, acc[r]);
     }
 #pragma unroll
     for (int r = 0; r < RP; ++r) dst[c * RP + r] = acc[r];
@@ -124,7 +146,8 @@ __global__ __launch_bounds__(256) void attn_lut_kernel(const float* __restrict__
 }
 
 // ------------------------------------------------------------- attn_chunk
-// grid (n_chunks, Hkv * n_hsplit, B), block 512.  LDS: one table region of
+// grid (n_chunks + n_wblocks, Hkv * n_hsplit, B), block 512; blocks with
+// x >= n_chunks are window blocks (window_partial).  LDS: one table region of
 // [S*G][C][RP] 4-byte entries that holds the LUT (floats) during pass 1 and
 // the weight histogram (integers) during pass 2, plus the contraction's
 // partial sums.  Each thread owns up to CH_TPT tokens of the chunk
@@ -185,13 +208,157 @@ __device__ __forceinline__ void for_codes(const uint8_t* row, int SG, int C, Fn&
   }
 }
 
+// Window block: softmax partial (m, l, o) of up to ATTN_WIN_BLOCK fp16 window
+// tokens [w0, w1) for the RP query heads of a unit, in the original domain.
+// L = D/8 lanes per token row (8 dims per lane, 16-byte loads); pass A
+// stores the scores in LDS, pass B accumulates p * v per row, rows are summed
+// within each wave by lane exchanges and across waves through LDS.
+template <int RP, int D>
+__device__ __forceinline__ void window_partial(const float* __restrict__ q,
+                                               const uint16_t* __restrict__ kw,
+                                               const uint16_t* __restrict__ vw,
+                                               float* __restrict__ part, uint8_t* smem, int b,
+                                               int kv, int h0, int nh, int Hq, int Hkv, int W,
+                                               int w0, int w1, int slot, int nslots, int pstride,
+                                               float scale) {
+  constexpr int L = D / 8;
+  constexpr int ROWS = 512 / L;
+  float* ssc = reinterpret_cast<float*>(smem);                  // [ATTN_WIN_BLOCK][RP]
+  float* wacc = ssc + ATTN_WIN_BLOCK * RP;                      // [8 waves][RP][D]
+  __shared__ float wred[8][RP];
+  __shared__ float wm[RP];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int row = tid / L, col = tid % L;
+  const uint16_t* kwp = kw + ((int64_t)b * Hkv + kv) * W * D + col * 8;
+  const uint16_t* vwp = vw + ((int64_t)b * Hkv + kv) * W * D + col * 8;
+  float qv[RP][8];
+#pragma unroll
+  for (int r = 0; r < RP; ++r) {
+    const float* qp = q + ((int64_t)b * Hq + h0 + (r < nh ? r : nh - 1)) * D + col * 8;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qv[r][e] = qp[e] * scale;
+  }
+  const int n = w1 - w0;
+  // pass A: scores
+#pragma unroll 4
+  for (int i = 0; i < n; i += ROWS) {                 // uniform trip count
+    const int w = i + row;
+    const int wl = w < n ? w : n - 1;
+    float kx[8];
+    load8<2>(kwp + (int64_t)(w0 + wl) * D, kx);
+#pragma unroll
+    for (int r = 0; r < RP; ++r) {
+      float dot = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dot = __builtin_fmaf(qv[r][e], kx[e], dot);
+      dot = row_sum<L>(dot);
+      if (w < n && col == 0) ssc[w * RP + r] = dot;
+    }
+  }
+  __syncthreads();
+  float m[RP];
+#pragma unroll
+  for (int r = 0; r < RP; ++r) {
+    float v = -__builtin_inff();
+    for (int t = tid; t < n; t += 512) v = fmaxf(v, ssc[t * RP + r]);
+    v = wave_max(v);
+    if (lane == 0) wred[wave][r] = v;
+  }
+  __syncthreads();
+  if (tid < RP) {
+    float v = wred[0][tid];
+    for (int w = 1; w < 8; ++w) v = fmaxf(v, wred[w][tid]);
+    wm[tid] = v;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < RP; ++r) m[r] = wm[r];
+  // pass B: weights and p * v
+  float acc[RP][8], ls[RP];
+#pragma unroll
+  for (int r = 0; r < RP; ++r) {
+    ls[r] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[r][e] = 0.0f;
+  }
+#pragma unroll 4
+  for (int i = 0; i < n; i += ROWS) {
+    const int w = i + row;
+    if (w < n) {
+      float vx[8];
+      load8<2>(vwp + (int64_t)(w0 + w) * D, vx);
+#pragma unroll
+      for (int r = 0; r < RP; ++r) {
+        const float pw = __expf(ssc[w * RP + r] - m[r]);
+        ls[r] += pw;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[r][e] = __builtin_fmaf(pw, vx[e], acc[r][e]);
+      }
+    }
+  }
+  // rows of a wave -> one row (lanes L apart), then waves through LDS
+#pragma unroll
+  for (int r = 0; r < RP; ++r) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {                     // lanes of one column: xor L, 2L, .. 32
+      if constexpr (L <= 8) acc[r][e] += xor_lane<8>(acc[r][e]);
+      if constexpr (L <= 16) acc[r][e] += xor_lane<16>(acc[r][e]);
+      acc[r][e] += xor_lane<32>(acc[r][e]);
+    }
+    ls[r] = wave_sum(col == 0 ? ls[r] : 0.0f);
+  }
+  if (lane < L) {
+#pragma unroll
+    for (int r = 0; r < RP; ++r)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) wacc[(wave * RP + r) * D + col * 8 + e] = acc[r][e];
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int r = 0; r < RP; ++r) wred[wave][r] = ls[r];
+  }
+  __syncthreads();
+  for (int o = tid; o < RP * D; o += 512) {
+    const int r = o / D, d = o - r * D;
+    if (r >= nh) continue;
+    float v = 0.0f;
+    for (int w = 0; w < 8; ++w) v += wacc[(w * RP + r) * D + d];
+    float* pp = part + ((int64_t)(b * Hq + h0 + r) * nslots + slot) * pstride;
+    pp[4 + d] = v;
+    if (d == 0) {
+      float l = 0.0f;
+      for (int w = 0; w < 8; ++w) l += wred[w][r];
+      pp[0] = m[r];
+      pp[1] = l;
+    }
+  }
+}
+
 template <int RP, int SGC>   // SGC: compile-time S*G (multiple of 16), or 0 = runtime bytes
 __global__ __launch_bounds__(CH_THREADS, 1) void attn_chunk_kernel(
     const uint8_t* __restrict__ kcodes, const uint8_t* __restrict__ vcodes,
     const float* __restrict__ vcb, const float* __restrict__ lut, float* __restrict__ part,
     int Hq, int Hkv, int D, int S, int G, int C, int Tc, int n_chunks, int chunk, int n_hsplit,
-    int pstride, int fbits, int cparts, size_t lut_slice) {
+    int pstride, int fbits, int cparts, size_t lut_slice, const float* __restrict__ q,
+    const uint16_t* __restrict__ kw, const uint16_t* __restrict__ vw, int W, int n_wblocks,
+    float scale) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  if ((int)blockIdx.x >= n_chunks) {                    // window block (uniform per block)
+    const int kv = blockIdx.y / n_hsplit, hs = blockIdx.y - kv * n_hsplit;
+    const int R = Hq / Hkv;
+    const int nh = (R - hs * RP) < RP ? (R - hs * RP) : RP;
+    const int wb = blockIdx.x - n_chunks;
+    const int w0 = wb * ATTN_WIN_BLOCK;
+    const int w1 = (w0 + ATTN_WIN_BLOCK) < W ? (w0 + ATTN_WIN_BLOCK) : W;
+    const int h0 = kv * R + hs * RP;
+#define KVQ_WIN(DD) window_partial<RP, DD>(q, kw, vw, part, smem, blockIdx.z, kv, h0, nh, Hq, Hkv, \
+                                          W, w0, w1, n_chunks + wb, n_chunks + n_wblocks, pstride, scale)
+    if (D == 64) KVQ_WIN(64);
+    else if (D == 128) KVQ_WIN(128);
+    else KVQ_WIN(256);
+#undef KVQ_WIN
+    return;
+  }
   const int SG = SGC ? SGC : S * G;
   const int tabn = SG * C * RP;                         // entries in the table region
   float* tabf = reinterpret_cast<float*>(smem);         // LUT during pass 1
@@ -263,7 +430,9 @@ __global__ __launch_bounds__(CH_THREADS, 1) void attn_chunk_kernel(
     for (int w = 1; w < CH_THREADS / 64; ++w) v = fmaxf(v, red_f[w][tid]);
     mx[tid] = v;
   }
-  for (int i = tid; i < tabn; i += CH_THREADS) tabu[i] = 0u;
+  for (int i = tid; i < tabn / 4; i += CH_THREADS)
+    reinterpret_cast<uint4*>(tabu)[i] = make_uint4(0u, 0u, 0u, 0u);
+  for (int i = (tabn / 4) * 4 + tid; i < tabn; i += CH_THREADS) tabu[i] = 0u;
   __syncthreads();
   float m[RP];
 #pragma unroll
@@ -324,7 +493,7 @@ __global__ __launch_bounds__(CH_THREADS, 1) void attn_chunk_kernel(
       for (int e = 0; e < 4; ++e) acc[r][e] = 0.0f;
     const float* cvp = vcb + (int64_t)sg * C * dsub + j0;
     const uint32_t* hp = tabu + sg * C * RP;
-#pragma unroll 8
+#pragma unroll 16
     for (int c = c0; c < c1; ++c) {
       const float4 cv = *reinterpret_cast<const float4*>(cvp + (int64_t)c * dsub);
 #pragma unroll
@@ -348,103 +517,44 @@ __global__ __launch_bounds__(CH_THREADS, 1) void attn_chunk_kernel(
     if (r >= nh) continue;
     float v = 0.0f;
     for (int sp = 0; sp < S * P; ++sp) v += cpart[(sp * RP + r) * D + d];
-    float* pp = part + ((int64_t)(b * Hq + h0 + r) * (n_chunks + 1) + ci) * pstride;
+    float* pp = part + ((int64_t)(b * Hq + h0 + r) * (n_chunks + n_wblocks) + ci) * pstride;
     pp[4 + d] = v * inv;
     if (d == 0) { pp[0] = mx[r]; pp[1] = (float)lt[r] * inv; }
   }
 }
 
 // ------------------------------------------------------------- attn_merge
-// grid (B*Hq), block 256.  The fp16 window's partial (L = D/8 lanes per token
-// row), then out = (H * sum_i w_i o_rot_i + w_win o_win) / (sum_i w_i l_i +
-// w_win l_win), w = exp(m - m*).
+// grid (B*Hq), block 256.  Records [0, n_chunks) are coded-token partials
+// (o in the rotated domain), records [n_chunks, nslots) window partials (o in
+// the original domain).  out = (H * sum_coded w_i o_i + sum_window w_i o_i) /
+// sum_i w_i l_i with w_i = exp(m_i - max_j m_j); the two block halves take
+// alternate records.
 template <int D>
-__global__ __launch_bounds__(256) void attn_merge_kernel(
-    const float* __restrict__ q, const uint16_t* __restrict__ kw, const uint16_t* __restrict__ vw,
-    const float* __restrict__ part, float* __restrict__ out, int Hq, int Hkv, int W, int n_chunks,
-    int pstride, float scale) {
+__global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict__ part,
+                                                         float* __restrict__ out, int n_chunks,
+                                                         int nslots, int pstride) {
   constexpr int L = D / 8;
-  constexpr int ROWS = 256 / L;
-  __shared__ float ow[D];
-  __shared__ float orot[D];
+  __shared__ float crot[2][D];             // coded part, rotated domain
+  __shared__ float corg[2][D];             // window part, original domain
   __shared__ float wts[256];
-  __shared__ float red[16];
+  __shared__ float red[8];
   const int bh = blockIdx.x;
-  const int b = bh / Hq, h = bh - b * Hq;
-  const int kv = h / (Hq / Hkv);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int row = tid / L, col = tid % L;
-
-  // ---- window partial (mw, lw, ow)
-  for (int d = tid; d < D; d += 256) ow[d] = 0.0f;
-  __syncthreads();
-  float mw = -__builtin_inff(), lw = 0.0f;
-  if (W > 0) {
-    const uint16_t* kwp = kw + ((int64_t)b * Hkv + kv) * W * D + col * 8;
-    const uint16_t* vwp = vw + ((int64_t)b * Hkv + kv) * W * D + col * 8;
-    const float* qp = q + (int64_t)bh * D + col * 8;
-    float qv[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) qv[e] = qp[e] * scale;
-    float mloc = -__builtin_inff();
-    for (int w0 = 0; w0 < W; w0 += ROWS) {              // uniform trip count
-      const int w = w0 + row;
-      const int wl = w < W ? w : W - 1;
-      float kx[8];
-      load8<2>(kwp + (int64_t)wl * D, kx);
-      float dot = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) dot = __builtin_fmaf(qv[e], kx[e], dot);
-      dot = row_sum<L>(dot);
-      if (w < W) mloc = fmaxf(mloc, dot);
-    }
-    mloc = wave_max(mloc);
-    if (lane == 0) red[wave] = mloc;
-    __syncthreads();
-    mw = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    float lsum = 0.0f;
-    float acc[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
-    for (int w0 = 0; w0 < W; w0 += ROWS) {
-      const int w = w0 + row;
-      const int wl = w < W ? w : W - 1;
-      float kx[8], vx[8];
-      load8<2>(kwp + (int64_t)wl * D, kx);
-      load8<2>(vwp + (int64_t)wl * D, vx);
-      float dot = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) dot = __builtin_fmaf(qv[e], kx[e], dot);
-      dot = row_sum<L>(dot);
-      const float pw = w < W ? __expf(dot - mw) : 0.0f;
-      lsum += pw;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(pw, vx[e], acc[e]);
-    }
-    // rows -> dims: each column's 8 dims summed over the ROWS rows
-#pragma unroll
-    for (int e = 0; e < 8; ++e) atomicAdd(&ow[col * 8 + e], acc[e]);
-    const float lsr = wave_sum(col == 0 ? lsum : 0.0f);  // one lane per row counts lsum
-    if (lane == 0) red[4 + wave] = lsr;
-    __syncthreads();
-    lw = red[4] + red[5] + red[6] + red[7];
-  }
-
-  // ---- chunk partials
-  const float* pb = part + (int64_t)bh * (n_chunks + 1) * pstride;
+  const int col = lane % L;
+  const float* pb = part + (int64_t)bh * nslots * pstride;
   float mloc = -__builtin_inff();
-  for (int i = tid; i < n_chunks; i += 256) mloc = fmaxf(mloc, pb[(int64_t)i * pstride]);
+  for (int i = tid; i < nslots; i += 256) mloc = fmaxf(mloc, pb[(int64_t)i * pstride]);
   mloc = wave_max(mloc);
-  if (lane == 0) red[8 + wave] = mloc;
+  if (lane == 0) red[wave] = mloc;
   __syncthreads();
-  float ms = fmaxf(fmaxf(red[8], red[9]), fmaxf(red[10], red[11]));
-  ms = fmaxf(ms, mw);
-  float oacc = 0.0f;                                    // thread d (< D): sum_i w_i o_rot_i[d]
+  const float ms = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   float den = 0.0f;
-  for (int i0 = 0; i0 < n_chunks; i0 += 256) {
+  const int half = tid >> 7, d = tid & 127;
+  float oc0 = 0.0f, oc1 = 0.0f, ow0 = 0.0f, ow1 = 0.0f;   // dims d and d + 128
+  for (int i0 = 0; i0 < nslots; i0 += 256) {
     const int i = i0 + tid;
     float wgt = 0.0f, lv = 0.0f;
-    if (i < n_chunks) {
+    if (i < nslots) {
       const float mi = pb[(int64_t)i * pstride];
       wgt = mi == -__builtin_inff() ? 0.0f : __expf(mi - ms);
       lv = pb[(int64_t)i * pstride + 1];
@@ -452,31 +562,42 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(
     wts[tid] = wgt;
     den += wgt * lv;
     __syncthreads();
-    const int n = (n_chunks - i0) < 256 ? (n_chunks - i0) : 256;
-    if (tid < D) {
+    const int n = (nslots - i0) < 256 ? (nslots - i0) : 256;
+    int nc = n_chunks - i0;
+    nc = nc < 0 ? 0 : nc > n ? n : nc;
+    if (d < D) {
 #pragma unroll 8
-      for (int k = 0; k < n; ++k)
-        oacc = __builtin_fmaf(wts[k], pb[(int64_t)(i0 + k) * pstride + 4 + tid], oacc);
+      for (int k = half; k < nc; k += 2) {
+        const float* rec = pb + (int64_t)(i0 + k) * pstride + 4;
+        oc0 = __builtin_fmaf(wts[k], rec[d], oc0);
+        if (D > 128) oc1 = __builtin_fmaf(wts[k], rec[d + 128], oc1);
+      }
+      for (int k = nc + half; k < n; k += 2) {
+        const float* rec = pb + (int64_t)(i0 + k) * pstride + 4;
+        ow0 = __builtin_fmaf(wts[k], rec[d], ow0);
+        if (D > 128) ow1 = __builtin_fmaf(wts[k], rec[d + 128], ow1);
+      }
     }
     __syncthreads();
   }
   den = wave_sum(den);
-  if (lane == 0) red[12 + wave] = den;
-  if (tid < D) orot[tid] = oacc;
+  if (lane == 0) red[4 + wave] = den;
+  if (d < D) { crot[half][d] = oc0; corg[half][d] = ow0; }
+  if (D > 128) { crot[half][d + 128] = oc1; corg[half][d + 128] = ow1; }
   __syncthreads();
-  const float ww = mw == -__builtin_inff() ? 0.0f : __expf(mw - ms);
-  const float total = red[12] + red[13] + red[14] + red[15] + ww * lw;
+  const float total = red[4] + red[5] + red[6] + red[7];
   if (tid < 64) {                                        // one wave unrotates the coded part
     float v[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = orot[col * 8 + e];
+    for (int e = 0; e < 8; ++e) v[e] = crot[0][col * 8 + e] + crot[1][col * 8 + e];
     hadamard_row<8, L>(v, lane);
     if (lane < L) {
       constexpr float sc = rsqrt_pow2(D);
       const float inv = 1.0f / total;
       float r[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) r[e] = (v[e] * sc + ww * ow[col * 8 + e]) * inv;
+      for (int e = 0; e < 8; ++e)
+        r[e] = (v[e] * sc + corg[0][col * 8 + e] + corg[1][col * 8 + e]) * inv;
       float4* op = reinterpret_cast<float4*>(out + (int64_t)bh * D + col * 8);
       op[0] = make_float4(r[0], r[1], r[2], r[3]);
       op[1] = make_float4(r[4], r[5], r[6], r[7]);
@@ -488,15 +609,31 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(
 template <int RP>
 static hipError_t launch_rp(const AttnPlan& p, int SG, const float* q, const float* kcb,
                             const uint8_t* kc, const uint8_t* vc, const float* vcb, float* lut,
-                            float* part, int B, int Hq, int Hkv, int D, int S, int G, int C, int Tc,
-                            float scale, hipStream_t st) {
-  attn_lut_kernel<RP><<<dim3(B * Hkv * p.n_hsplit, SG), 256, 0, st>>>(
-      q, kcb, lut, Hq, Hkv, p.n_hsplit, D, G, C, p.lut_slice, scale);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  dim3 grid(p.n_chunks, Hkv * p.n_hsplit, B);
-  const size_t tab = (((size_t)SG * C * RP * 4) + 15) & ~(size_t)15;
-  const size_t lds = tab + (size_t)S * p.cparts * RP * D * 4;
+                            float* part, const uint16_t* kw, const uint16_t* vw, int B, int Hq,
+                            int Hkv, int D, int S, int G, int C, int Tc, int W, float scale,
+                            hipStream_t st) {
+  hipError_t e = hipSuccess;
+  size_t lds = 0;
+  if (p.n_chunks > 0) {
+    if (D == 64)
+      attn_lut_kernel<RP, 64><<<dim3(B * Hkv * p.n_hsplit, SG), 256, 0, st>>>(
+          q, kcb, lut, Hq, Hkv, p.n_hsplit, G, C, p.lut_slice, scale);
+    else if (D == 128)
+      attn_lut_kernel<RP, 128><<<dim3(B * Hkv * p.n_hsplit, SG), 256, 0, st>>>(
+          q, kcb, lut, Hq, Hkv, p.n_hsplit, G, C, p.lut_slice, scale);
+    else
+      attn_lut_kernel<RP, 256><<<dim3(B * Hkv * p.n_hsplit, SG), 256, 0, st>>>(
+          q, kcb, lut, Hq, Hkv, p.n_hsplit, G, C, p.lut_slice, scale);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const size_t tab = (((size_t)SG * C * RP * 4) + 15) & ~(size_t)15;
+    lds = tab + (size_t)S * p.cparts * RP * D * 4;
+  }
+  if (p.n_wblocks > 0) {
+    const size_t wl = ((size_t)ATTN_WIN_BLOCK * RP + (size_t)8 * RP * D) * 4;
+    if (wl > lds) lds = wl;
+  }
+  dim3 grid(p.n_chunks + p.n_wblocks, Hkv * p.n_hsplit, B);
 #define KVQ_CH(SGV)                                                                            \
   {                                                                                            \
     auto kern = attn_chunk_kernel<RP, SGV>;                                                    \
@@ -505,7 +642,8 @@ static hipError_t launch_rp(const AttnPlan& p, int SG, const float* q, const flo
     if (e != hipSuccess) return e;                                                             \
     kern<<<grid, CH_THREADS, lds, st>>>(kc, vc, vcb, lut, part, Hq, Hkv, D, S, G, C, Tc,       \
                                         p.n_chunks, p.chunk, p.n_hsplit, p.pstride, p.fbits,   \
-                                        p.cparts, p.lut_slice);                                \
+                                        p.cparts, p.lut_slice, q, kw, vw, W, p.n_wblocks,      \
+                                        scale);                                                \
     return hipGetLastError();                                                                  \
   }
   if (SG == 16) KVQ_CH(16)
@@ -524,19 +662,15 @@ hipError_t launch_attend(const AttnPlan& p, int B, int Hq, int Hkv, int D, int S
   float* part = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) +
                                          ((p.lut_bytes + 255) & ~(size_t)255));
   const int SG = S * G;
-  hipError_t e = hipSuccess;
-  if (p.n_chunks > 0) {
-    if (p.rp == 4) e = launch_rp<4>(p, SG, q, kcb, kc, vc, vcb, lut, part, B, Hq, Hkv, D, S, G, C, Tc, scale, st);
-    else if (p.rp == 2) e = launch_rp<2>(p, SG, q, kcb, kc, vc, vcb, lut, part, B, Hq, Hkv, D, S, G, C, Tc, scale, st);
-    else e = launch_rp<1>(p, SG, q, kcb, kc, vc, vcb, lut, part, B, Hq, Hkv, D, S, G, C, Tc, scale, st);
-    if (e != hipSuccess) return e;
-  }
-#define KVQ_MG(DD) attn_merge_kernel<DD><<<dim3(B * Hq), 256, 0, st>>>(q, kw, vw, part, out, Hq, Hkv, \
-                                                                       W, p.n_chunks, p.pstride, scale)
-  if (D == 64) KVQ_MG(64);
-  else if (D == 128) KVQ_MG(128);
-  else KVQ_MG(256);
-#undef KVQ_MG
+  hipError_t e;
+  if (p.rp == 4) e = launch_rp<4>(p, SG, q, kcb, kc, vc, vcb, lut, part, kw, vw, B, Hq, Hkv, D, S, G, C, Tc, W, scale, st);
+  else if (p.rp == 2) e = launch_rp<2>(p, SG, q, kcb, kc, vc, vcb, lut, part, kw, vw, B, Hq, Hkv, D, S, G, C, Tc, W, scale, st);
+  else e = launch_rp<1>(p, SG, q, kcb, kc, vc, vcb, lut, part, kw, vw, B, Hq, Hkv, D, S, G, C, Tc, W, scale, st);
+  if (e != hipSuccess) return e;
+  const int nslots = p.n_chunks + p.n_wblocks;
+  if (D == 64) attn_merge_kernel<64><<<dim3(B * Hq), 256, 0, st>>>(part, out, p.n_chunks, nslots, p.pstride);
+  else if (D == 128) attn_merge_kernel<128><<<dim3(B * Hq), 256, 0, st>>>(part, out, p.n_chunks, nslots, p.pstride);
+  else attn_merge_kernel<256><<<dim3(B * Hq), 256, 0, st>>>(part, out, p.n_chunks, nslots, p.pstride);
   return hipGetLastError();
 }
 

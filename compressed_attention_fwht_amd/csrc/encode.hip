@@ -92,14 +92,19 @@ __device__ __forceinline__ int64_t row_elem(int64_t book, int64_t n, int64_t n_r
 // base.  Completion is awaited with wait_vmem().
 template <int S>
 __device__ __forceinline__ void stage_group(const uint8_t* src, uint8_t* dst, int wave, int lane) {
-  constexpr int KIB = S * PACK_BYTES / 1024;             // 1 KiB pieces (20 per stage)
+  // 20 KiB per stage, except 12 KiB for the last one: no residual update
+  // follows it, so its fp32 copy is never read.
+  constexpr int PIECES = 20 * (S - 1) + 12;
 #pragma unroll
-  for (int k = 0; k < (KIB + MF_WAVES - 1) / MF_WAVES; ++k) {
+  for (int k = 0; k < (PIECES + MF_WAVES - 1) / MF_WAVES; ++k) {
     const int piece = k * MF_WAVES + wave;               // wave-uniform
-    if (piece < KIB)
-      __builtin_amdgcn_global_load_lds(src + piece * 1024 + lane * 16,
-                                       (__attribute__((address_space(3))) void*)(dst + piece * 1024),
+    if (piece < PIECES) {
+      const int st = piece / 20 < S - 1 ? piece / 20 : S - 1;
+      const int off = st * PACK_BYTES + (piece - 20 * st) * 1024;
+      __builtin_amdgcn_global_load_lds(src + off + lane * 16,
+                                       (__attribute__((address_space(3))) void*)(dst + off),
                                        16, 0, 0);
+    }
   }
 }
 
@@ -245,31 +250,39 @@ __global__ __launch_bounds__(512, 1) void encode_mfma_kernel(
       __builtin_memcpy(&B2T0, b2t0, 16); __builtin_memcpy(&B2T1, b2t1, 16);
 
       int best0 = 0x7fffffff, best1 = 0x7fffffff;
-      // The tile loop stays rolled: the packed index (32t | row) is then a
-      // scalar register and each candidate costs one v_and_or_b32.
-#pragma nounroll
-      for (int t = 0; t < 8; ++t) {
+      // One codeword tile of 32 x (2 x 32 vectors): four MFMAs, then the argmin.
+      auto issue = [&](int t, f32x16_t& c0, f32x16_t& c1) {
         const int m = 32 * t + m_lane;
         const uint4 a1 = *reinterpret_cast<const uint4*>(cbs_s + h * 4096 + m * 16);
         const uint4 a2 = *reinterpret_cast<const uint4*>(cbs_s + h * 8192 + m * 16);
         bf16x8_t A1, A2;
         __builtin_memcpy(&A1, &a1, 16);
         __builtin_memcpy(&A2, &a2, 16);
-        f32x16_t acc0 = {0}, acc1 = {0};
-        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A1, B1T0, acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A1, B1T1, acc1, 0, 0, 0);
-        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A2, B2T0, acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A2, B2T1, acc1, 0, 0, 0);
+        const f32x16_t z = {0};
+        c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A1, B1T0, z, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A1, B1T1, z, 0, 0, 0);
+        c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A2, B2T0, c0, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A2, B2T1, c1, 0, 0, 0);
+      };
+      // The packed index (32t | row) comes from a scalar register, so each
+      // candidate costs one v_and_or_b32; accumulator register i holds codeword
+      // row 8*(i/4) + 4*h + (i%4) of the tile (h is or-ed in after the loop).
+      auto reduce = [&](int t, const f32x16_t& c0, const f32x16_t& c1) {
         const uint32_t tb = (uint32_t)__builtin_amdgcn_readfirstlane(t << 5);
-        // accumulator register i holds codeword row 8*(i/4) + 4*h + (i%4) of the tile
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const uint32_t idx = tb | (uint32_t)(8 * (i >> 2) + (i & 3));
-          const int k0 = (int)((__float_as_uint(acc0[i]) & keep_hi) | idx);
-          const int k1 = (int)((__float_as_uint(acc1[i]) & keep_hi) | idx);
+          const int k0 = (int)((__float_as_uint(c0[i]) & keep_hi) | idx);
+          const int k1 = (int)((__float_as_uint(c1[i]) & keep_hi) | idx);
           best0 = min(best0, k0);
           best1 = min(best1, k1);
         }
+      };
+#pragma nounroll
+      for (int t = 0; t < 8; ++t) {
+        f32x16_t acc0, acc1;
+        issue(t, acc0, acc1);
+        reduce(t, acc0, acc1);
       }
       best0 |= h << 2;
       best1 |= h << 2;

@@ -12,6 +12,7 @@ namespace kvq {
 constexpr size_t ATTN_LDS_TABLES = 150 * 1024;
 constexpr int ATTN_MAX_CHUNK = 4096;   // tokens per split-K chunk, upper bound
 constexpr int ATTN_MIN_CHUNK = 1024;   // preferred lower bound on chunk length
+constexpr int ATTN_WIN_BLOCK = 2048;   // fp16 window tokens per window block
 
 struct AttnPlan {
   int rp;          // query heads per chunk block (0: tables do not fit LDS)
@@ -20,6 +21,7 @@ struct AttnPlan {
   int chunk;       // tokens per chunk
   int fbits;       // fixed-point fraction bits of the softmax-weight histogram
   int cparts;      // codeword ranges per (stage, dims) item in the V contraction
+  int n_wblocks;   // window blocks (partial records after the chunks' ones)
   int pstride;     // floats per partial record (m, l, pad, pad, o[D])
   size_t lut_slice;  // bytes of one (sequence, KV head, head split) LUT slice
   size_t lut_bytes, part_bytes, ws_bytes;

@@ -14,12 +14,17 @@
 
 namespace kvq {
 
+// Each lane handles UNR independent vectors per iteration, stage-outer so
+// that the code bytes and codeword rows of all UNR vectors are in flight
+// together (memory-level parallelism).  dsub >= 8: a lane's 8 output dims lie
+// in one group.
 template <int D>
 __global__ __launch_bounds__(256) void reconstruct_kernel(
     const uint8_t* __restrict__ codes, const float* __restrict__ cb, float* __restrict__ out,
     int64_t n_books, int64_t n_per_book, int G, int S, int C, int dsub, int unrotate) {
   constexpr int L = D / 8;
   constexpr int ROWS_PER_WAVE = 64 / L;
+  constexpr int UNR = 4;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int64_t n_total = n_books * n_per_book;
@@ -28,54 +33,57 @@ __global__ __launch_bounds__(256) void reconstruct_kernel(
   const int col = lane % L;
   const int SG = S * G;
   const int64_t book_stride = (int64_t)S * G * C * dsub;   // floats per book
+  const int64_t step = waves_total * ROWS_PER_WAVE;
+  const int d0 = col * 8;
+  const int g = d0 / dsub, j0 = d0 % dsub;
   for (int64_t base = ((int64_t)blockIdx.x * (blockDim.x >> 6) + wave) * ROWS_PER_WAVE;
-       base < n_total; base += waves_total * ROWS_PER_WAVE) {
-    const int64_t vec = base + sub;
-    const bool live = vec < n_total;
-    const int64_t v_ld = live ? vec : (n_total - 1);
-    const int64_t book = v_ld / n_per_book;
-    const uint8_t* crow = codes + v_ld * SG;
-    const float* bk = cb + book * book_stride;
-    double acc[8];
+       base < n_total; base += step * UNR) {
+    const uint8_t* crow[UNR];
+    const float* bk[UNR];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = 0.0;
-    if (dsub >= 8) {
-      const int d0 = col * 8;
-      const int g = d0 / dsub, j0 = d0 % dsub;
-      for (int s = 0; s < S; ++s) {
-        int z = crow[s * G + g];
-        z = z < C ? z : C - 1;
-        const float4* p = reinterpret_cast<const float4*>(
-            bk + (((int64_t)s * G + g) * C + z) * dsub + j0);
-        float4 a = p[0], b = p[1];
-        acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
-        acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
+    for (int u = 0; u < UNR; ++u) {
+      int64_t vec = base + u * step + sub;
+      if (vec >= n_total) vec = n_total - 1;              // keep every lane in the butterfly
+      crow[u] = codes + vec * SG + g;
+      bk[u] = cb + (vec / n_per_book) * book_stride + (int64_t)g * C * dsub + j0;
+    }
+    double acc[UNR][8];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[u][e] = 0.0;
+    for (int s = 0; s < S; ++s) {
+      int z[UNR];
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        z[u] = crow[u][s * G];
+        z[u] = z[u] < C ? z[u] : C - 1;
       }
-    } else {
-      for (int s = 0; s < S; ++s) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int d = col * 8 + e;
-          const int g = d / dsub, j = d % dsub;
-          int z = crow[s * G + g];
-          z = z < C ? z : C - 1;
-          acc[e] += bk[(((int64_t)s * G + g) * C + z) * dsub + j];
-        }
+      for (int u = 0; u < UNR; ++u) {
+        const float4* p = reinterpret_cast<const float4*>(bk[u] + ((int64_t)s * G * C + z[u]) * dsub);
+        const float4 a = p[0], c = p[1];
+        acc[u][0] += a.x; acc[u][1] += a.y; acc[u][2] += a.z; acc[u][3] += a.w;
+        acc[u][4] += c.x; acc[u][5] += c.y; acc[u][6] += c.z; acc[u][7] += c.w;
       }
     }
-    float v[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = (float)acc[e];
-    if (unrotate) {                         // uniform branch: all lanes take it
-      hadamard_row<8, L>(v, lane);
-      constexpr float sc = rsqrt_pow2(D);
+    for (int u = 0; u < UNR; ++u) {
+      const int64_t vec = base + u * step + sub;
+      float v[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] *= sc;
-    }
-    if (live) {
-      float4* o = reinterpret_cast<float4*>(out + vec * D + col * 8);
-      o[0] = make_float4(v[0], v[1], v[2], v[3]);
-      o[1] = make_float4(v[4], v[5], v[6], v[7]);
+      for (int e = 0; e < 8; ++e) v[e] = (float)acc[u][e];
+      if (unrotate) {                       // uniform branch: all lanes take it
+        hadamard_row<8, L>(v, lane);
+        constexpr float sc = rsqrt_pow2(D);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] *= sc;
+      }
+      if (vec < n_total) {
+        float4* o = reinterpret_cast<float4*>(out + vec * D + col * 8);
+        o[0] = make_float4(v[0], v[1], v[2], v[3]);
+        o[1] = make_float4(v[4], v[5], v[6], v[7]);
+      }
     }
   }
 }
@@ -86,9 +94,9 @@ hipError_t launch_reconstruct(const uint8_t* codes, const float* cb, float* out,
   const int64_t n = n_books * n_per_book;
   if (n == 0) return hipSuccess;
   const int dsub = D / G;
-  const int rows_per_block = 4 * (64 / (D / 8));
+  const int rows_per_block = 4 * (64 / (D / 8)) * 4;      // 4 waves, 4 vectors per lane
   int64_t blocks = (n + rows_per_block - 1) / rows_per_block;
-  if (blocks > 65536) blocks = 65536;
+  if (blocks > 16384) blocks = 16384;
   if (D == 64)
     reconstruct_kernel<64><<<dim3((unsigned)blocks), 256, 0, s>>>(codes, cb, out, n_books, n_per_book,
                                                                   G, S, C, dsub, unrotate);

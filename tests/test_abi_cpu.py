@@ -142,9 +142,9 @@ def test_attend_argument_errors():
 
 
 def test_attend_workspace_sizes():
-    # LUT B*Hq*S*G*C floats, then per (b, h) (chunks + window) records of D + 4 floats
+    # LUT B*Hq*S*G*C floats, then per (b, h) (chunks + window blocks) records of D + 4 floats
     sz = kvq.attend_workspace_size(1, 32, 8, 128, 32640, 128, 1, 16, 256)
     lut = 32 * 16 * 256 * 4
     assert sz > lut and (sz - lut) % (32 * 132 * 4) == 0
     sz_w = kvq.attend_workspace_size(2, 4, 2, 64, 0, 50, 2, 1, 256)   # window only
-    assert sz_w == 2 * 4 * 2 * 256 * 4 + 2 * 4 * 1 * 68 * 4
+    assert sz_w == 2 * 4 * 1 * 68 * 4                                  # no LUT, one window block

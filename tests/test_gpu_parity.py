@@ -247,6 +247,26 @@ def test_decode_window_only_equals_dense_softmax():
     assert res["ok"], res
 
 
+@pytest.mark.parametrize("key,over", [
+    (2, dict(tokens=6000, window=4500)),                  # 3 window blocks, ragged last
+    (3, dict(batch=2, tokens=2500, window=2500)),         # window only, 2 blocks, GQA 7
+    (1, dict(tokens=3000, window=2049)),                  # D 64, one-token last block
+])
+def test_decode_long_window(key, over):
+    say(f"decode long window workload {key} {over}")
+    w = synth.workload(key, **over)
+    inp = synth.make_inputs(w)
+    Tc = w.code_tokens
+    if Tc:
+        codes = [oracle.rvq_encode(inp["x_f32"][b][:, :Tc].reshape(-1, w.head_dim), inp["cb"][b])
+                 for b in range(2)]
+    else:
+        codes = [np.zeros((0, w.n_stages, w.n_groups), dtype=np.uint8)] * 2
+    res = _decode_case(w, inp, codes[0], codes[1])
+    say("   ", res)
+    assert res["ok"], res
+
+
 def test_decode_codes_only_short():
     say("decode codes only, short cache")
     w = synth.workload(4, tokens=37, window=0)
