@@ -70,18 +70,32 @@ AttnPlan attn_plan(int B, int Hq, int Hkv, int D, int S, int G, int C, int Tc, i
     if (nc < 1) nc = 1;
     p.chunk = (int)((Tc + nc - 1) / nc);
     p.n_chunks = (int)((Tc + p.chunk - 1) / p.chunk);   // no empty trailing chunk
-    p.fbits = 31 - ceil_log2(p.chunk);
   }
   if (Tc == 0) {                                        // window only: no tables needed
     p.rp = R >= 4 ? 4 : R >= 2 ? 2 : 1;
     p.n_hsplit = (R + p.rp - 1) / p.rp;
     p.cparts = 1;
   }
-  p.n_wblocks = W > 0 ? (W + ATTN_WIN_BLOCK - 1) / ATTN_WIN_BLOCK : 0;
+  // window: a slice of at most 4096/D tokens on each chunk block (one token
+  // per row of D/8 lanes; its row sums need 8*RP*D floats of LDS beside the
+  // LUT), else blocks of its own of ATTN_WIN_BLOCK tokens
+  p.wslice = p.n_wblocks = 0;
+  if (W > 0) {
+    const int per = p.n_chunks > 0 ? (W + p.n_chunks - 1) / p.n_chunks : 0;
+    const int sp = S * p.cparts > 8 ? S * p.cparts : 8;
+    if (p.n_chunks > 0 && per <= 4096 / D &&
+        (size_t)SG * C * p.rp * 4 + (size_t)sp * p.rp * D * 4 <= ATTN_LDS_TABLES)
+      p.wslice = per;
+    else
+      p.n_wblocks = (W + ATTN_WIN_BLOCK - 1) / ATTN_WIN_BLOCK;
+  }
+  // fixed-point weights: every bin and every chunk sum below 2^31
+  if (p.n_chunks > 0) p.fbits = 31 - ceil_log2(p.chunk);
   p.pstride = D + 4;                                    // m, l, pad, pad, o[D]
   p.lut_slice = ((size_t)SG * C * (p.rp ? p.rp : 1) * 4 + 255) & ~(size_t)255;
   p.lut_bytes = p.n_chunks ? (size_t)B * Hkv * p.n_hsplit * p.lut_slice : 0;
-  p.part_bytes = (size_t)B * Hq * (p.n_chunks + p.n_wblocks) * p.pstride * sizeof(float);
+  const int wrec = p.wslice > 0 ? p.n_chunks : p.n_wblocks;   // window records
+  p.part_bytes = (size_t)B * Hq * (p.n_chunks + wrec) * p.pstride * sizeof(float);
   p.ws_bytes = ((p.lut_bytes + 255) & ~(size_t)255) + p.part_bytes;
   return p;
 }
@@ -146,8 +160,9 @@ __global__ __launch_bounds__(256) void attn_lut_kernel(const float* __restrict__
 }
 
 // ------------------------------------------------------------- attn_chunk
-// grid (n_chunks + n_wblocks, Hkv * n_hsplit, B), block 512; blocks with
-// x >= n_chunks are window blocks (window_partial).  LDS: one table region of
+// grid (n_chunks + n_wblocks, Hkv * n_hsplit, B), block 512.  A short
+// window rides on the chunk blocks (a slice each, win_slice_*); a long one gets
+// blocks x >= n_chunks of its own (window_partial).  LDS: one table region of
 // [S*G][C][RP] 4-byte entries that holds the LUT (floats) during pass 1 and
 // the weight histogram (integers) during pass 2, plus the contraction's
 // partial sums.  Each thread owns up to CH_TPT tokens of the chunk
@@ -334,41 +349,78 @@ __device__ __forceinline__ void window_partial(const float* __restrict__ q,
   }
 }
 
-template <int RP, int SGC>   // SGC: compile-time S*G (multiple of 16), or 0 = runtime bytes
+// Window slice riding on a chunk block: up to 4096/D tokens, one per token
+// row of L = D/8 lanes.  The K row, the V row and q are loaded when the block
+// starts (their latency overlaps the LUT staging) and the scores are formed
+// once they have landed.  The slice keeps a softmax partial of its own (own
+// max, float weights, original domain) whose reductions share the chunk's
+// barriers; a common fixed-point scale would round every chunk token against
+// a window maximum that may dwarf it.  Returns whether this row holds a token.
+template <int RP, int D>
+__device__ __forceinline__ bool win_slice_load(uint4& kraw, uint4& vraw, float (&qv)[RP][8],
+                                               const float* __restrict__ q,
+                                               const uint16_t* __restrict__ kw,
+                                               const uint16_t* __restrict__ vw, int b, int kv,
+                                               int h0, int nh, int Hq, int Hkv, int W, int wa,
+                                               int wb, int tid) {
+  constexpr int L = D / 8;
+  const int row = tid / L, col = tid % L;
+  const int t = wa + row;
+  const bool act = t < wb;
+  const int tl = act ? t : (wb > 0 ? wb - 1 : 0);
+  const int64_t off = (((int64_t)b * Hkv + kv) * W + tl) * D + col * 8;
+  kraw = make_uint4(0u, 0u, 0u, 0u);
+  vraw = kraw;
+  if (wb > wa) {
+    kraw = *reinterpret_cast<const uint4*>(kw + off);
+    vraw = *reinterpret_cast<const uint4*>(vw + off);
+  }
+#pragma unroll
+  for (int r = 0; r < RP; ++r) {
+    const float4* qp = reinterpret_cast<const float4*>(
+        q + ((int64_t)b * Hq + h0 + (r < nh ? r : nh - 1)) * D + col * 8);
+    const float4 x0 = qp[0], x1 = qp[1];
+    qv[r][0] = x0.x; qv[r][1] = x0.y; qv[r][2] = x0.z; qv[r][3] = x0.w;
+    qv[r][4] = x1.x; qv[r][5] = x1.y; qv[r][6] = x1.z; qv[r][7] = x1.w;
+  }
+  return act;
+}
+
+template <int RP, int D>
+__device__ __forceinline__ void win_slice_scores(float (&sw)[RP], uint4 kraw,
+                                                 const float (&qv)[RP][8], bool act,
+                                                 float scale) {
+  constexpr int L = D / 8;
+  const uint32_t kr[4] = {kraw.x, kraw.y, kraw.z, kraw.w};
+  float kx[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    kx[2 * i] = f16_bits_to_f32(kr[i]);
+    kx[2 * i + 1] = f16_bits_to_f32(kr[i] >> 16);
+  }
+#pragma unroll
+  for (int r = 0; r < RP; ++r) {
+    float dot = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dot = __builtin_fmaf(qv[r][e], kx[e], dot);
+    dot = row_sum<L>(dot) * scale;
+    sw[r] = act ? dot : -__builtin_inff();
+  }
+}
+
+// SGC: compile-time S*G (multiple of 16), or 0 = runtime bytes.
+// wslice > 0: block ci also owns window tokens [ci*wslice, (ci+1)*wslice),
+// record n_chunks + ci; otherwise blocks x >= n_chunks are window blocks.
+template <int RP, int SGC, int D>
 __global__ __launch_bounds__(CH_THREADS, 1) void attn_chunk_kernel(
     const uint8_t* __restrict__ kcodes, const uint8_t* __restrict__ vcodes,
     const float* __restrict__ vcb, const float* __restrict__ lut, float* __restrict__ part,
-    int Hq, int Hkv, int D, int S, int G, int C, int Tc, int n_chunks, int chunk, int n_hsplit,
+    int Hq, int Hkv, int S, int G, int C, int Tc, int n_chunks, int chunk, int n_hsplit,
     int pstride, int fbits, int cparts, size_t lut_slice, const float* __restrict__ q,
-    const uint16_t* __restrict__ kw, const uint16_t* __restrict__ vw, int W, int n_wblocks,
-    float scale) {
+    const uint16_t* __restrict__ kw, const uint16_t* __restrict__ vw, int W, int wslice,
+    int nslots, float scale) {
+  constexpr int L = D / 8;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  if ((int)blockIdx.x >= n_chunks) {                    // window block (uniform per block)
-    const int kv = blockIdx.y / n_hsplit, hs = blockIdx.y - kv * n_hsplit;
-    const int R = Hq / Hkv;
-    const int nh = (R - hs * RP) < RP ? (R - hs * RP) : RP;
-    const int wb = blockIdx.x - n_chunks;
-    const int w0 = wb * ATTN_WIN_BLOCK;
-    const int w1 = (w0 + ATTN_WIN_BLOCK) < W ? (w0 + ATTN_WIN_BLOCK) : W;
-    const int h0 = kv * R + hs * RP;
-#define KVQ_WIN(DD) window_partial<RP, DD>(q, kw, vw, part, smem, blockIdx.z, kv, h0, nh, Hq, Hkv, \
-                                          W, w0, w1, n_chunks + wb, n_chunks + n_wblocks, pstride, scale)
-    if (D == 64) KVQ_WIN(64);
-    else if (D == 128) KVQ_WIN(128);
-    else KVQ_WIN(256);
-#undef KVQ_WIN
-    return;
-  }
-  const int SG = SGC ? SGC : S * G;
-  const int tabn = SG * C * RP;                         // entries in the table region
-  float* tabf = reinterpret_cast<float*>(smem);         // LUT during pass 1
-  uint32_t* tabu = reinterpret_cast<uint32_t*>(smem);   // histogram during pass 2
-  float* cpart = reinterpret_cast<float*>(smem + (((size_t)tabn * 4 + 15) & ~(size_t)15));
-  __shared__ float red_f[8][RP];
-  __shared__ uint32_t red_u[8][RP];
-  __shared__ float mx[RP];
-  __shared__ uint32_t lt[RP];
-
   const int ci = blockIdx.x;
   const int unit = blockIdx.y;                          // kv * n_hsplit + hs
   const int b = blockIdx.z;
@@ -376,10 +428,37 @@ __global__ __launch_bounds__(CH_THREADS, 1) void attn_chunk_kernel(
   const int R = Hq / Hkv;
   const int h0 = kv * R + hs * RP;
   const int nh = (R - hs * RP) < RP ? (R - hs * RP) : RP;
+  if (ci >= n_chunks) {                                 // window block (uniform per block)
+    const int w0 = (ci - n_chunks) * ATTN_WIN_BLOCK;
+    const int w1 = (w0 + ATTN_WIN_BLOCK) < W ? (w0 + ATTN_WIN_BLOCK) : W;
+    window_partial<RP, D>(q, kw, vw, part, smem, b, kv, h0, nh, Hq, Hkv, W, w0, w1, ci, nslots,
+                          pstride, scale);
+    return;
+  }
+  const int SG = SGC ? SGC : S * G;
+  const int tabn = SG * C * RP;                         // entries in the table region
+  float* tabf = reinterpret_cast<float*>(smem);         // LUT during pass 1
+  uint32_t* tabu = reinterpret_cast<uint32_t*>(smem);   // histogram during pass 2
+  float* cpart = reinterpret_cast<float*>(smem + (((size_t)tabn * 4 + 15) & ~(size_t)15));
+  __shared__ float red_f[8][RP], red_wf[8][RP], red_wl[8][RP];
+  __shared__ uint32_t red_u[8][RP];
+  __shared__ float mx[RP], mxw[RP], ltw[RP];
+  __shared__ uint32_t lt[RP];
+
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int t0 = ci * chunk;
   const int t1 = (t0 + chunk) < Tc ? (t0 + chunk) : Tc;
+
+  uint4 wkraw, wvraw;
+  float wq[RP][8], wsc[RP];
+  bool wact = false;
+  if (wslice > 0) {
+    const int wa = ci * wslice < W ? ci * wslice : W;
+    const int wb = (wa + wslice) < W ? (wa + wslice) : W;
+    wact = win_slice_load<RP, D>(wkraw, wvraw, wq, q, kw, vw, b, kv, h0, nh, Hq, Hkv, W, wa, wb,
+                                 tid);
+  }
 
   // ---- stage this unit's LUT: whole 1 KiB pieces straight into LDS, tail by hand
   {
@@ -395,6 +474,7 @@ __global__ __launch_bounds__(CH_THREADS, 1) void attn_chunk_kernel(
       tabu[i] = reinterpret_cast<const uint32_t*>(src)[i];
     __builtin_amdgcn_s_waitcnt(0x0f70);                  // vmcnt(0)
   }
+  if (wslice > 0) win_slice_scores<RP, D>(wsc, wkraw, wq, wact, scale);
   __syncthreads();
 
   const int64_t rowbase = ((int64_t)b * Hkv + kv) * (int64_t)Tc;
@@ -423,12 +503,20 @@ __global__ __launch_bounds__(CH_THREADS, 1) void attn_chunk_kernel(
     for (int k = 0; k < CH_TPT; ++k) v = fmaxf(v, sc[k][r]);
     v = wave_max(v);
     if (lane == 0) red_f[wave][r] = v;
+    if (wslice > 0) {
+      const float vw = wave_max(wsc[r]);
+      if (lane == 0) red_wf[wave][r] = vw;
+    }
   }
   __syncthreads();                                      // also: every LUT read is done
   if (tid < RP) {
-    float v = red_f[0][tid];
-    for (int w = 1; w < CH_THREADS / 64; ++w) v = fmaxf(v, red_f[w][tid]);
+    float v = red_f[0][tid], vw = red_wf[0][tid];
+    for (int w = 1; w < CH_THREADS / 64; ++w) {
+      v = fmaxf(v, red_f[w][tid]);
+      vw = fmaxf(vw, red_wf[w][tid]);
+    }
     mx[tid] = v;
+    mxw[tid] = vw;
   }
   for (int i = tid; i < tabn / 4; i += CH_THREADS)
     reinterpret_cast<uint4*>(tabu)[i] = make_uint4(0u, 0u, 0u, 0u);
@@ -438,11 +526,40 @@ __global__ __launch_bounds__(CH_THREADS, 1) void attn_chunk_kernel(
 #pragma unroll
   for (int r = 0; r < RP; ++r) m[r] = mx[r];
 
-  // ---- pass 2: fixed-point weights into the V histogram
   const float fscale = (float)(1u << fbits);
   uint32_t ls[RP];
 #pragma unroll
   for (int r = 0; r < RP; ++r) ls[r] = 0u;
+
+  // ---- window slice: p = exp(s - m_w), p * v summed over the rows of each
+  // wave into LDS slot [wave][r][D] (the contraction's region, free until
+  // pass 2 ends), sum p over the rows into red_wl
+  if (wslice > 0) {
+    const uint32_t vr[4] = {wvraw.x, wvraw.y, wvraw.z, wvraw.w};
+    float vx[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      vx[2 * i] = f16_bits_to_f32(vr[i]);
+      vx[2 * i + 1] = f16_bits_to_f32(vr[i] >> 16);
+    }
+    const int col = tid % L;
+#pragma unroll
+    for (int r = 0; r < RP; ++r) {
+      const float pf = wact ? __expf(wsc[r] - mxw[r]) : 0.0f;
+      const float lw = wave_sum(col == 0 ? pf : 0.0f);
+      if (lane == 0) red_wl[wave][r] = lw;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float a = pf * vx[e];
+        if constexpr (L <= 8) a += xor_lane<8>(a);    // rows of the wave: xor L .. 32
+        if constexpr (L <= 16) a += xor_lane<16>(a);
+        a += xor_lane<32>(a);
+        if (lane < L) cpart[(wave * RP + r) * D + col * 8 + e] = a;
+      }
+    }
+  }
+
+  // ---- pass 2: fixed-point weights into the V histogram
 #pragma unroll
   for (int k = 0; k < CH_TPT; ++k) {
     const int t = t0 + tid + CH_THREADS * k;
@@ -467,15 +584,33 @@ __global__ __launch_bounds__(CH_THREADS, 1) void attn_chunk_kernel(
   __syncthreads();
   if (tid < RP) {
     uint32_t v = 0u;
-    for (int w = 0; w < CH_THREADS / 64; ++w) v += red_u[w][tid];
+    float vw = 0.0f;
+    for (int w = 0; w < CH_THREADS / 64; ++w) {
+      v += red_u[w][tid];
+      vw += red_wl[w][tid];
+    }
     lt[tid] = v;
+    ltw[tid] = vw;
+  }
+  constexpr int NO = (RP * D + CH_THREADS - 1) / CH_THREADS;   // outputs per thread
+  float wsum[NO];
+#pragma unroll
+  for (int j = 0; j < NO; ++j) wsum[j] = 0.0f;
+  if (wslice > 0) {                                     // window rows, summed over waves
+#pragma unroll
+    for (int j = 0; j < NO; ++j) {
+      const int o = tid + CH_THREADS * j;
+      if (o < RP * D)
+        for (int w = 0; w < CH_THREADS / 64; ++w) wsum[j] += cpart[w * RP * D + o];
+    }
+    __syncthreads();                                    // before the contraction reuses it
   }
 
   // ---- o_rot[r][g*dsub + j] = 2^-F sum_s sum_c W[s][g][c][r] * C^V_sg[c][j].
   // Item (s, codeword part, 4 consecutive dims): float4 codebook loads,
   // histogram entries broadcast to the lanes sharing a codeword.
   const int dsub = D / G;
-  const int D4 = D / 4;
+  constexpr int D4 = D / 4;
   const int P = cparts;
   const int cper = (C + P - 1) / P;
   for (int it = tid; it < S * P * D4; it += CH_THREADS) {
@@ -512,14 +647,21 @@ __global__ __launch_bounds__(CH_THREADS, 1) void attn_chunk_kernel(
   }
   __syncthreads();
   const float inv = 1.0f / fscale;
-  for (int o = tid; o < RP * D; o += CH_THREADS) {
+#pragma unroll
+  for (int j = 0; j < NO; ++j) {
+    const int o = tid + CH_THREADS * j;
     const int r = o / D, d = o - r * D;
-    if (r >= nh) continue;
+    if (o >= RP * D || r >= nh) continue;
     float v = 0.0f;
     for (int sp = 0; sp < S * P; ++sp) v += cpart[(sp * RP + r) * D + d];
-    float* pp = part + ((int64_t)(b * Hq + h0 + r) * (n_chunks + n_wblocks) + ci) * pstride;
+    float* pp = part + ((int64_t)(b * Hq + h0 + r) * nslots + ci) * pstride;
     pp[4 + d] = v * inv;
     if (d == 0) { pp[0] = mx[r]; pp[1] = (float)lt[r] * inv; }
+    if (wslice > 0) {
+      float* pw = pp + (int64_t)n_chunks * pstride;
+      pw[4 + d] = wsum[j];
+      if (d == 0) { pw[0] = mxw[r]; pw[1] = ltw[r]; }
+    }
   }
 }
 
@@ -633,23 +775,28 @@ static hipError_t launch_rp(const AttnPlan& p, int SG, const float* q, const flo
     const size_t wl = ((size_t)ATTN_WIN_BLOCK * RP + (size_t)8 * RP * D) * 4;
     if (wl > lds) lds = wl;
   }
+  if (p.wslice > 0 && S * p.cparts < 8)               // window row sums need 8 slots
+    lds = ((((size_t)SG * C * RP * 4) + 15) & ~(size_t)15) + (size_t)8 * RP * D * 4;
   dim3 grid(p.n_chunks + p.n_wblocks, Hkv * p.n_hsplit, B);
-#define KVQ_CH(SGV)                                                                            \
+  const int nslots = p.n_chunks + (p.wslice > 0 ? p.n_chunks : p.n_wblocks);
+#define KVQ_CH(SGV, DV)                                                                        \
   {                                                                                            \
-    auto kern = attn_chunk_kernel<RP, SGV>;                                                    \
+    auto kern = attn_chunk_kernel<RP, SGV, DV>;                                                \
     e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,     \
                             (int)lds);                                                         \
     if (e != hipSuccess) return e;                                                             \
-    kern<<<grid, CH_THREADS, lds, st>>>(kc, vc, vcb, lut, part, Hq, Hkv, D, S, G, C, Tc,       \
+    kern<<<grid, CH_THREADS, lds, st>>>(kc, vc, vcb, lut, part, Hq, Hkv, S, G, C, Tc,          \
                                         p.n_chunks, p.chunk, p.n_hsplit, p.pstride, p.fbits,   \
-                                        p.cparts, p.lut_slice, q, kw, vw, W, p.n_wblocks,      \
+                                        p.cparts, p.lut_slice, q, kw, vw, W, p.wslice, nslots, \
                                         scale);                                                \
     return hipGetLastError();                                                                  \
   }
-  if (SG == 16) KVQ_CH(16)
-  if (SG == 32) KVQ_CH(32)
-  if (SG == 64) KVQ_CH(64)
-  KVQ_CH(0)
+  if (D == 64) KVQ_CH(0, 64)
+  if (D == 256) KVQ_CH(0, 256)
+  if (SG == 16) KVQ_CH(16, 128)
+  if (SG == 32) KVQ_CH(32, 128)
+  if (SG == 64) KVQ_CH(64, 128)
+  KVQ_CH(0, 128)
 #undef KVQ_CH
 }
 
@@ -667,7 +814,7 @@ hipError_t launch_attend(const AttnPlan& p, int B, int Hq, int Hkv, int D, int S
   else if (p.rp == 2) e = launch_rp<2>(p, SG, q, kcb, kc, vc, vcb, lut, part, kw, vw, B, Hq, Hkv, D, S, G, C, Tc, W, scale, st);
   else e = launch_rp<1>(p, SG, q, kcb, kc, vc, vcb, lut, part, kw, vw, B, Hq, Hkv, D, S, G, C, Tc, W, scale, st);
   if (e != hipSuccess) return e;
-  const int nslots = p.n_chunks + p.n_wblocks;
+  const int nslots = p.n_chunks + (p.wslice > 0 ? p.n_chunks : p.n_wblocks);
   if (D == 64) attn_merge_kernel<64><<<dim3(B * Hq), 256, 0, st>>>(part, out, p.n_chunks, nslots, p.pstride);
   else if (D == 128) attn_merge_kernel<128><<<dim3(B * Hq), 256, 0, st>>>(part, out, p.n_chunks, nslots, p.pstride);
   else attn_merge_kernel<256><<<dim3(B * Hq), 256, 0, st>>>(part, out, p.n_chunks, nslots, p.pstride);

@@ -21,7 +21,8 @@ struct AttnPlan {
   int chunk;       // tokens per chunk
   int fbits;       // fixed-point fraction bits of the softmax-weight histogram
   int cparts;      // codeword ranges per (stage, dims) item in the V contraction
-  int n_wblocks;   // window blocks (partial records after the chunks' ones)
+  int wslice;      // window tokens joining each chunk block (0: window blocks)
+  int n_wblocks;   // window blocks of ATTN_WIN_BLOCK tokens, records after the chunks' ones
   int pstride;     // floats per partial record (m, l, pad, pad, o[D])
   size_t lut_slice;  // bytes of one (sequence, KV head, head split) LUT slice
   size_t lut_bytes, part_bytes, ws_bytes;
