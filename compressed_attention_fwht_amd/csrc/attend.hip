@@ -11,16 +11,18 @@
 //     of softmax weights, W_sg[c] = sum_t p_t [z_tsg == c], and contracted
 //     once per chunk: o_rot = sum_sg sum_c W_sg[c] C^V_sg[c].
 //   * The token axis is split into chunks (split-K); each chunk emits an
-//     fp32 partial (m, l, o_rot).  The dense fp16 window is split the same way
-//     into blocks of the same grid, whose partials stay in the original
-//     domain.  The merge kernel combines all partials by log-sum-exp in fp32,
-//     unrotating the coded part once ("Differential-KV" README, Flash-Style LSE Combine; "VQKV"
-//     summary, 3. Inference Integration, local sliding window of recent
-//     tokens kept uncompressed).
+//     fp32 partial (m, l, o_rot).  The dense fp16 window enters the same
+//     partials with its V rows rotated like the codebooks (H v / sqrt(D)): a
+//     short window as one slice per chunk block, folded into the chunk's
+//     record; a long one as blocks of its own in the same grid.  The merge
+//     kernel combines the partials by log-sum-exp in fp32 and unrotates once
+//     ("Differential-KV" README, Flash-Style LSE Combine; "VQKV" summary,
+//     3. Inference Integration, local sliding window of recent tokens kept
+//     uncompressed).
 //
 // Kernels: attn_lut (q rotation slices, LUT) -> attn_chunk (code streaming,
-// K scores, V histogram, contraction; window blocks) -> attn_merge (LSE
-// merge, unrotation).
+// K scores, V histogram, contraction, window) -> attn_merge (LSE merge,
+// unrotation).
 //
 // The histogram accumulates the weights p = exp(s - m_chunk) in [0, 1] as
 // fixed-point integers round(p * 2^F) with LDS integer atomics (ds_add_u32,
@@ -94,8 +96,7 @@ AttnPlan attn_plan(int B, int Hq, int Hkv, int D, int S, int G, int C, int Tc, i
   p.pstride = D + 4;                                    // m, l, pad, pad, o[D]
   p.lut_slice = ((size_t)SG * C * (p.rp ? p.rp : 1) * 4 + 255) & ~(size_t)255;
   p.lut_bytes = p.n_chunks ? (size_t)B * Hkv * p.n_hsplit * p.lut_slice : 0;
-  const int wrec = p.wslice > 0 ? p.n_chunks : p.n_wblocks;   // window records
-  p.part_bytes = (size_t)B * Hq * (p.n_chunks + wrec) * p.pstride * sizeof(float);
+  p.part_bytes = (size_t)B * Hq * (p.n_chunks + p.n_wblocks) * p.pstride * sizeof(float);
   p.ws_bytes = ((p.lut_bytes + 255) & ~(size_t)255) + p.part_bytes;
   return p;
 }
@@ -223,8 +224,34 @@ __device__ __forceinline__ void for_codes(const uint8_t* row, int SG, int C, Fn&
   }
 }
 
+// Register-staged code rows (compile-time S*G only): load_codes issues the
+// 16-byte loads of one token row, visit_codes walks the bytes like for_codes.
+template <int SGC>
+__device__ __forceinline__ void load_codes(const uint8_t* row, uint4 (&w)[SGC / 16]) {
+#pragma unroll
+  for (int i = 0; i < SGC / 16; ++i) w[i] = reinterpret_cast<const uint4*>(row)[i];
+}
+
+template <int SGC, typename Fn>
+__device__ __forceinline__ void visit_codes(const uint4 (&w)[SGC / 16], int C, Fn&& f) {
+#pragma unroll
+  for (int w4 = 0; w4 < SGC / 16; ++w4) {
+    const uint32_t ws[4] = {w[w4].x, w[w4].y, w[w4].z, w[w4].w};
+#pragma unroll
+    for (int qd = 0; qd < 4; ++qd) {
+#pragma unroll
+      for (int by = 0; by < 4; ++by) {
+        int z = (ws[qd] >> (8 * by)) & 255;
+        if (C < 256) z = z < C ? z : C - 1;
+        f(w4 * 16 + qd * 4 + by, z);
+      }
+    }
+  }
+}
+
 // Window block: softmax partial (m, l, o) of up to ATTN_WIN_BLOCK fp16 window
-// tokens [w0, w1) for the RP query heads of a unit, in the original domain.
+// tokens [w0, w1) for the RP query heads of a unit, o rotated like the coded
+// tokens' (H v / sqrt(D)) so the merge treats every record alike.
 // L = D/8 lanes per token row (8 dims per lane, 16-byte loads); pass A
 // stores the scores in LDS, pass B accumulates p * v per row, rows are summed
 // within each wave by lane exchanges and across waves through LDS.
@@ -311,14 +338,23 @@ __device__ __forceinline__ void window_partial(const float* __restrict__ q,
       }
     }
   }
+  // into the coded (rotated) domain, H sum p v = sum p H v: the L lanes of a
+  // row group hold sums over the same rows
+  constexpr float rs = rsqrt_pow2(D);
+#pragma unroll
+  for (int r = 0; r < RP; ++r) {
+    hadamard_row<8, L>(acc[r], lane);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[r][e] *= rs;
+  }
   // rows of a wave -> one row (lanes L apart), then waves through LDS
 #pragma unroll
   for (int r = 0; r < RP; ++r) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {                     // lanes of one column: xor L, 2L, .. 32
+    for (int e = 0; e < 8; ++e) {                     // lanes of one column: L .. 32 apart
       if constexpr (L <= 8) acc[r][e] += xor_lane<8>(acc[r][e]);
-      if constexpr (L <= 16) acc[r][e] += xor_lane<16>(acc[r][e]);
-      acc[r][e] += xor_lane<32>(acc[r][e]);
+      if constexpr (L <= 16) acc[r][e] = pair_sum<16>(acc[r][e]);
+      acc[r][e] = pair_sum<32>(acc[r][e]);
     }
     ls[r] = wave_sum(col == 0 ? ls[r] : 0.0f);
   }
@@ -353,9 +389,10 @@ __device__ __forceinline__ void window_partial(const float* __restrict__ q,
 // row of L = D/8 lanes.  The K row, the V row and q are loaded when the block
 // starts (their latency overlaps the LUT staging) and the scores are formed
 // once they have landed.  The slice keeps a softmax partial of its own (own
-// max, float weights, original domain) whose reductions share the chunk's
-// barriers; a common fixed-point scale would round every chunk token against
-// a window maximum that may dwarf it.  Returns whether this row holds a token.
+// max, float weights, V rotated like the codebooks) whose reductions share
+// the chunk's barriers, and is folded into the chunk's record at the end; a
+// common fixed-point scale would round every chunk token against a window
+// maximum that may dwarf it.  Returns whether this row holds a token.
 template <int RP, int D>
 __device__ __forceinline__ bool win_slice_load(uint4& kraw, uint4& vraw, float (&qv)[RP][8],
                                                const float* __restrict__ q,
@@ -410,7 +447,7 @@ __device__ __forceinline__ void win_slice_scores(float (&sw)[RP], uint4 kraw,
 
 // SGC: compile-time S*G (multiple of 16), or 0 = runtime bytes.
 // wslice > 0: block ci also owns window tokens [ci*wslice, (ci+1)*wslice),
-// record n_chunks + ci; otherwise blocks x >= n_chunks are window blocks.
+// folded into its record; otherwise blocks x >= n_chunks are window blocks.
 template <int RP, int SGC, int D>
 __global__ __launch_bounds__(CH_THREADS, 1) void attn_chunk_kernel(
     const uint8_t* __restrict__ kcodes, const uint8_t* __restrict__ vcodes,
@@ -450,14 +487,20 @@ __global__ __launch_bounds__(CH_THREADS, 1) void attn_chunk_kernel(
   const int t0 = ci * chunk;
   const int t1 = (t0 + chunk) < Tc ? (t0 + chunk) : Tc;
 
-  uint4 wkraw, wvraw;
-  float wq[RP][8], wsc[RP];
-  bool wact = false;
-  if (wslice > 0) {
-    const int wa = ci * wslice < W ? ci * wslice : W;
-    const int wb = (wa + wslice) < W ? (wa + wslice) : W;
-    wact = win_slice_load<RP, D>(wkraw, wvraw, wq, q, kw, vw, b, kv, h0, nh, Hq, Hkv, W, wa, wb,
-                                 tid);
+  const int64_t rowbase = ((int64_t)b * Hkv + kv) * (int64_t)Tc;
+  // first KP token rows of K codes (and later of V codes) staged in registers
+  // (32 VGPRs) so their HBM latency overlaps the LUT staging (the max
+  // reduction for V)
+  constexpr int SGW = SGC ? SGC / 16 : 1;
+  constexpr int KP = SGC ? (128 / SGC < CH_TPT ? 128 / SGC : CH_TPT) : 0;
+  constexpr int KPA = KP ? KP : 1;
+  uint4 cpre[KPA][SGW];
+  if constexpr (KP > 0) {
+#pragma unroll
+    for (int k = 0; k < KP; ++k) {
+      const int t = t0 + tid + CH_THREADS * k;
+      if (t < t1) load_codes<SGC>(kcodes + (rowbase + t) * SG, cpre[k]);
+    }
   }
 
   // ---- stage this unit's LUT: whole 1 KiB pieces straight into LDS, tail by hand
@@ -474,10 +517,18 @@ __global__ __launch_bounds__(CH_THREADS, 1) void attn_chunk_kernel(
       tabu[i] = reinterpret_cast<const uint32_t*>(src)[i];
     __builtin_amdgcn_s_waitcnt(0x0f70);                  // vmcnt(0)
   }
-  if (wslice > 0) win_slice_scores<RP, D>(wsc, wkraw, wq, wact, scale);
+  // window slice rows: in flight during pass 1, used after it
+  uint4 wkraw, wvraw;
+  float wq[RP][8], wsc[RP];
+  bool wact = false;
+  if (wslice > 0) {
+    const int wa = ci * wslice < W ? ci * wslice : W;
+    const int wb = (wa + wslice) < W ? (wa + wslice) : W;
+    wact = win_slice_load<RP, D>(wkraw, wvraw, wq, q, kw, vw, b, kv, h0, nh, Hq, Hkv, W, wa, wb,
+                                 tid);
+  }
   __syncthreads();
 
-  const int64_t rowbase = ((int64_t)b * Hkv + kv) * (int64_t)Tc;
   float sc[CH_TPT][RP];
   // ---- pass 1: K scores (LUT gathers, RP heads per read)
 #pragma unroll
@@ -489,12 +540,31 @@ __global__ __launch_bounds__(CH_THREADS, 1) void attn_chunk_kernel(
       float acc[RP];
 #pragma unroll
       for (int r = 0; r < RP; ++r) acc[r] = 0.0f;
-      for_codes<SGC>(kcodes + (rowbase + t) * SG, SG, C,
-                     [&](int sg, int z) { lut_add<RP>(tabf, (sg * C + z) * RP, acc); });
+      auto gather = [&](int sg, int z) { lut_add<RP>(tabf, (sg * C + z) * RP, acc); };
+      if constexpr (SGC != 0) {
+        uint4 w[SGW];
+        if (k < KP) {
+#pragma unroll
+          for (int i = 0; i < SGW; ++i) w[i] = cpre[k < KP ? k : 0][i];
+        } else {
+          load_codes<SGC>(kcodes + (rowbase + t) * SG, w);
+        }
+        visit_codes<SGC>(w, C, gather);
+      } else {
+        for_codes<SGC>(kcodes + (rowbase + t) * SG, SG, C, gather);
+      }
 #pragma unroll
       for (int r = 0; r < RP; ++r) sc[k][r] = acc[r];
     }
   }
+  if constexpr (KP > 0) {                               // V code rows, as for K
+#pragma unroll
+    for (int k = 0; k < KP; ++k) {
+      const int t = t0 + tid + CH_THREADS * k;
+      if (t < t1) load_codes<SGC>(vcodes + (rowbase + t) * SG, cpre[k]);
+    }
+  }
+  if (wslice > 0) win_slice_scores<RP, D>(wsc, wkraw, wq, wact, scale);
   // ---- chunk max per head
 #pragma unroll
   for (int r = 0; r < RP; ++r) {
@@ -531,9 +601,9 @@ __global__ __launch_bounds__(CH_THREADS, 1) void attn_chunk_kernel(
 #pragma unroll
   for (int r = 0; r < RP; ++r) ls[r] = 0u;
 
-  // ---- window slice: p = exp(s - m_w), p * v summed over the rows of each
-  // wave into LDS slot [wave][r][D] (the contraction's region, free until
-  // pass 2 ends), sum p over the rows into red_wl
+  // ---- window slice: p = exp(s - m_w), p * H v / sqrt(D) summed over the
+  // rows of each wave into LDS slot [wave][r][D] (the contraction's region,
+  // free until pass 2 ends), sum p over the rows into red_wl
   if (wslice > 0) {
     const uint32_t vr[4] = {wvraw.x, wvraw.y, wvraw.z, wvraw.w};
     float vx[8];
@@ -542,6 +612,10 @@ __global__ __launch_bounds__(CH_THREADS, 1) void attn_chunk_kernel(
       vx[2 * i] = f16_bits_to_f32(vr[i]);
       vx[2 * i + 1] = f16_bits_to_f32(vr[i] >> 16);
     }
+    hadamard_row<8, L>(vx, lane);
+    constexpr float rs = rsqrt_pow2(D);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) vx[e] *= rs;
     const int col = tid % L;
 #pragma unroll
     for (int r = 0; r < RP; ++r) {
@@ -551,9 +625,9 @@ __global__ __launch_bounds__(CH_THREADS, 1) void attn_chunk_kernel(
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         float a = pf * vx[e];
-        if constexpr (L <= 8) a += xor_lane<8>(a);    // rows of the wave: xor L .. 32
-        if constexpr (L <= 16) a += xor_lane<16>(a);
-        a += xor_lane<32>(a);
+        if constexpr (L <= 8) a += xor_lane<8>(a);    // rows of the wave: lanes L .. 32 apart
+        if constexpr (L <= 16) a = pair_sum<16>(a);
+        a = pair_sum<32>(a);
         if (lane < L) cpart[(wave * RP + r) * D + col * 8 + e] = a;
       }
     }
@@ -570,15 +644,24 @@ __global__ __launch_bounds__(CH_THREADS, 1) void attn_chunk_kernel(
         pw[r] = (uint32_t)__builtin_rintf(__expf(sc[k][r] - m[r]) * fscale);
         ls[r] += pw[r];
       }
-      for_codes<SGC>(vcodes + (rowbase + t) * SG, SG, C,
-                     [&](int sg, int z) { hist_add<RP>(tabu, (sg * C + z) * RP, pw); });
+      auto scatter = [&](int sg, int z) { hist_add<RP>(tabu, (sg * C + z) * RP, pw); };
+      if constexpr (SGC != 0) {
+        uint4 w[SGW];
+        if (k < KP) {
+#pragma unroll
+          for (int i = 0; i < SGW; ++i) w[i] = cpre[k < KP ? k : 0][i];
+        } else {
+          load_codes<SGC>(vcodes + (rowbase + t) * SG, w);
+        }
+        visit_codes<SGC>(w, C, scatter);
+      } else {
+        for_codes<SGC>(vcodes + (rowbase + t) * SG, SG, C, scatter);
+      }
     }
   }
 #pragma unroll
   for (int r = 0; r < RP; ++r) {
-    uint32_t v = ls[r];
-#pragma unroll
-    for (int msk = 32; msk >= 1; msk >>= 1) v += (uint32_t)__shfl_xor((int)v, msk);
+    const uint32_t v = wave_sum_u32(ls[r]);
     if (lane == 0) red_u[wave][r] = v;
   }
   __syncthreads();
@@ -654,30 +737,34 @@ __global__ __launch_bounds__(CH_THREADS, 1) void attn_chunk_kernel(
     if (o >= RP * D || r >= nh) continue;
     float v = 0.0f;
     for (int sp = 0; sp < S * P; ++sp) v += cpart[(sp * RP + r) * D + d];
-    float* pp = part + ((int64_t)(b * Hq + h0 + r) * nslots + ci) * pstride;
-    pp[4 + d] = v * inv;
-    if (d == 0) { pp[0] = mx[r]; pp[1] = (float)lt[r] * inv; }
-    if (wslice > 0) {
-      float* pw = pp + (int64_t)n_chunks * pstride;
-      pw[4 + d] = wsum[j];
-      if (d == 0) { pw[0] = mxw[r]; pw[1] = ltw[r]; }
+    v *= inv;
+    float m = mx[r], l = (float)lt[r] * inv;
+    if (wslice > 0) {                                   // fold the window slice in
+      const float mw = mxw[r];
+      const float mm = fmaxf(m, mw);
+      const float a = __expf(m - mm);
+      const float aw = mw == -__builtin_inff() ? 0.0f : __expf(mw - mm);
+      v = v * a + wsum[j] * aw;
+      l = l * a + ltw[r] * aw;
+      m = mm;
     }
+    float* pp = part + ((int64_t)(b * Hq + h0 + r) * nslots + ci) * pstride;
+    pp[4 + d] = v;
+    if (d == 0) { pp[0] = m; pp[1] = l; }
   }
 }
 
 // ------------------------------------------------------------- attn_merge
-// grid (B*Hq), block 256.  Records [0, n_chunks) are coded-token partials
-// (o in the rotated domain), records [n_chunks, nslots) window partials (o in
-// the original domain).  out = (H * sum_coded w_i o_i + sum_window w_i o_i) /
-// sum_i w_i l_i with w_i = exp(m_i - max_j m_j); the two block halves take
-// alternate records.
+// grid (B*Hq), block 256.  Every record holds a softmax partial (m, l, o)
+// with o in the rotated domain (coded chunks, window slices folded in, window
+// blocks).  out = H (sum_i w_i o_i) / (sqrt(D) sum_i w_i l_i) with
+// w_i = exp(m_i - max_j m_j); the two block halves take alternate records.
 template <int D>
 __global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict__ part,
-                                                         float* __restrict__ out, int n_chunks,
-                                                         int nslots, int pstride) {
+                                                         float* __restrict__ out, int nslots,
+                                                         int pstride) {
   constexpr int L = D / 8;
-  __shared__ float crot[2][D];             // coded part, rotated domain
-  __shared__ float corg[2][D];             // window part, original domain
+  __shared__ float crot[2][D];
   __shared__ float wts[256];
   __shared__ float red[8];
   const int bh = blockIdx.x;
@@ -692,7 +779,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict
   const float ms = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   float den = 0.0f;
   const int half = tid >> 7, d = tid & 127;
-  float oc0 = 0.0f, oc1 = 0.0f, ow0 = 0.0f, ow1 = 0.0f;   // dims d and d + 128
+  float o0 = 0.0f, o1 = 0.0f;                           // dims d and d + 128
   for (int i0 = 0; i0 < nslots; i0 += 256) {
     const int i = i0 + tid;
     float wgt = 0.0f, lv = 0.0f;
@@ -705,44 +792,33 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict
     den += wgt * lv;
     __syncthreads();
     const int n = (nslots - i0) < 256 ? (nslots - i0) : 256;
-    int nc = n_chunks - i0;
-    nc = nc < 0 ? 0 : nc > n ? n : nc;
     if (d < D) {
 #pragma unroll 8
-      for (int k = half; k < nc; k += 2) {
+      for (int k = half; k < n; k += 2) {
         const float* rec = pb + (int64_t)(i0 + k) * pstride + 4;
-        oc0 = __builtin_fmaf(wts[k], rec[d], oc0);
-        if (D > 128) oc1 = __builtin_fmaf(wts[k], rec[d + 128], oc1);
-      }
-      for (int k = nc + half; k < n; k += 2) {
-        const float* rec = pb + (int64_t)(i0 + k) * pstride + 4;
-        ow0 = __builtin_fmaf(wts[k], rec[d], ow0);
-        if (D > 128) ow1 = __builtin_fmaf(wts[k], rec[d + 128], ow1);
+        o0 = __builtin_fmaf(wts[k], rec[d], o0);
+        if (D > 128) o1 = __builtin_fmaf(wts[k], rec[d + 128], o1);
       }
     }
     __syncthreads();
   }
   den = wave_sum(den);
   if (lane == 0) red[4 + wave] = den;
-  if (d < D) { crot[half][d] = oc0; corg[half][d] = ow0; }
-  if (D > 128) { crot[half][d + 128] = oc1; corg[half][d + 128] = ow1; }
+  if (d < D) crot[half][d] = o0;
+  if (D > 128) crot[half][d + 128] = o1;
   __syncthreads();
   const float total = red[4] + red[5] + red[6] + red[7];
-  if (tid < 64) {                                        // one wave unrotates the coded part
+  if (tid < 64) {                                        // one wave unrotates
     float v[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = crot[0][col * 8 + e] + crot[1][col * 8 + e];
     hadamard_row<8, L>(v, lane);
     if (lane < L) {
       constexpr float sc = rsqrt_pow2(D);
-      const float inv = 1.0f / total;
-      float r[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        r[e] = (v[e] * sc + corg[0][col * 8 + e] + corg[1][col * 8 + e]) * inv;
+      const float inv = sc / total;
       float4* op = reinterpret_cast<float4*>(out + (int64_t)bh * D + col * 8);
-      op[0] = make_float4(r[0], r[1], r[2], r[3]);
-      op[1] = make_float4(r[4], r[5], r[6], r[7]);
+      op[0] = make_float4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+      op[1] = make_float4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
     }
   }
 }
@@ -778,7 +854,7 @@ static hipError_t launch_rp(const AttnPlan& p, int SG, const float* q, const flo
   if (p.wslice > 0 && S * p.cparts < 8)               // window row sums need 8 slots
     lds = ((((size_t)SG * C * RP * 4) + 15) & ~(size_t)15) + (size_t)8 * RP * D * 4;
   dim3 grid(p.n_chunks + p.n_wblocks, Hkv * p.n_hsplit, B);
-  const int nslots = p.n_chunks + (p.wslice > 0 ? p.n_chunks : p.n_wblocks);
+  const int nslots = p.n_chunks + p.n_wblocks;
 #define KVQ_CH(SGV, DV)                                                                        \
   {                                                                                            \
     auto kern = attn_chunk_kernel<RP, SGV, DV>;                                                \
@@ -814,10 +890,10 @@ hipError_t launch_attend(const AttnPlan& p, int B, int Hq, int Hkv, int D, int S
   else if (p.rp == 2) e = launch_rp<2>(p, SG, q, kcb, kc, vc, vcb, lut, part, kw, vw, B, Hq, Hkv, D, S, G, C, Tc, W, scale, st);
   else e = launch_rp<1>(p, SG, q, kcb, kc, vc, vcb, lut, part, kw, vw, B, Hq, Hkv, D, S, G, C, Tc, W, scale, st);
   if (e != hipSuccess) return e;
-  const int nslots = p.n_chunks + (p.wslice > 0 ? p.n_chunks : p.n_wblocks);
-  if (D == 64) attn_merge_kernel<64><<<dim3(B * Hq), 256, 0, st>>>(part, out, p.n_chunks, nslots, p.pstride);
-  else if (D == 128) attn_merge_kernel<128><<<dim3(B * Hq), 256, 0, st>>>(part, out, p.n_chunks, nslots, p.pstride);
-  else attn_merge_kernel<256><<<dim3(B * Hq), 256, 0, st>>>(part, out, p.n_chunks, nslots, p.pstride);
+  const int nslots = p.n_chunks + p.n_wblocks;
+  if (D == 64) attn_merge_kernel<64><<<dim3(B * Hq), 256, 0, st>>>(part, out, nslots, p.pstride);
+  else if (D == 128) attn_merge_kernel<128><<<dim3(B * Hq), 256, 0, st>>>(part, out, nslots, p.pstride);
+  else attn_merge_kernel<256><<<dim3(B * Hq), 256, 0, st>>>(part, out, nslots, p.pstride);
   return hipGetLastError();
 }
 

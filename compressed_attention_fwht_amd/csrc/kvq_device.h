@@ -66,7 +66,8 @@ __device__ __forceinline__ void load8(const void* p, float (&v)[8]) {
 
 // ------------------------------------------------------- lane exchanges
 // Value of lane (lane ^ M) within the wavefront, for M in {1,2,4,8,16,32}.
-// DPP where one instruction does it, ds_swizzle (32-lane groups) otherwise.
+// DPP or a permlane swap (VALU) where one instruction does it, ds_swizzle
+// for M = 4.
 template <int M>
 __device__ __forceinline__ float xor_lane(float x) {
   int v = __float_as_int(x);
@@ -80,12 +81,73 @@ __device__ __forceinline__ float xor_lane(float x) {
   } else if constexpr (M == 8) {
     r = __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, true);     // row_ror:8 == xor 8 in a row
   } else if constexpr (M == 16) {
-    r = __builtin_amdgcn_ds_swizzle(v, 0x401F);                 // xor 16 (bitmask mode)
+    const auto p = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
+    r = (int)((__lane_id() & 16) ? p[0] : p[1]);
   } else {
     static_assert(M == 32, "xor_lane: unsupported mask");
-    r = __shfl_xor(v, 32);
+    const auto p = __builtin_amdgcn_permlane32_swap((uint32_t)v, (uint32_t)v, false, false);
+    r = (int)((__lane_id() & 32) ? p[0] : p[1]);
   }
   return __int_as_float(r);
+}
+
+// x + (x of lane ^ M) for the reductions: any pairing works once the lower
+// levels are summed, so M = 4 and 8 use the DPP mirrors and 16, 32 add the
+// two halves of a permlane swap (no lane select).
+template <int M>
+__device__ __forceinline__ float pair_sum(float x) {
+  const int v = __float_as_int(x);
+  if constexpr (M == 1 || M == 2) {
+    return x + xor_lane<M>(x);
+  } else if constexpr (M == 4) {
+    return x + __int_as_float(__builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, true));  // half mirror
+  } else if constexpr (M == 8) {
+    return x + __int_as_float(__builtin_amdgcn_mov_dpp(v, 0x140, 0xF, 0xF, true));  // row mirror
+  } else if constexpr (M == 16) {
+    const auto p = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  } else {
+    static_assert(M == 32, "pair_sum: unsupported mask");
+    const auto p = __builtin_amdgcn_permlane32_swap((uint32_t)v, (uint32_t)v, false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  }
+}
+template <int M>
+__device__ __forceinline__ float pair_max(float x) {
+  const int v = __float_as_int(x);
+  if constexpr (M == 1 || M == 2) {
+    return fmaxf(x, xor_lane<M>(x));
+  } else if constexpr (M == 4) {
+    return fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, true)));
+  } else if constexpr (M == 8) {
+    return fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(v, 0x140, 0xF, 0xF, true)));
+  } else if constexpr (M == 16) {
+    const auto p = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
+    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+  } else {
+    static_assert(M == 32, "pair_max: unsupported mask");
+    const auto p = __builtin_amdgcn_permlane32_swap((uint32_t)v, (uint32_t)v, false, false);
+    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+  }
+}
+template <int M>
+__device__ __forceinline__ uint32_t pair_sum_u32(uint32_t v) {
+  if constexpr (M == 1) {
+    return v + (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true);
+  } else if constexpr (M == 2) {
+    return v + (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true);
+  } else if constexpr (M == 4) {
+    return v + (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, true);
+  } else if constexpr (M == 8) {
+    return v + (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, true);
+  } else if constexpr (M == 16) {
+    const auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return p[0] + p[1];
+  } else {
+    static_assert(M == 32, "pair_sum_u32: unsupported mask");
+    const auto p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return p[0] + p[1];
+  }
 }
 
 // Walsh-Hadamard butterfly over one row of D = E*L elements held by L
@@ -125,24 +187,39 @@ __device__ __forceinline__ void hadamard_row(float (&v)[E], int lane) {
 // lane of the row receives the sum.  All lanes of the wavefront execute this.
 template <int L>
 __device__ __forceinline__ float row_sum(float x) {
-  if constexpr (L > 1) x += xor_lane<1>(x);
-  if constexpr (L > 2) x += xor_lane<2>(x);
-  if constexpr (L > 4) x += xor_lane<4>(x);
-  if constexpr (L > 8) x += xor_lane<8>(x);
-  if constexpr (L > 16) x += xor_lane<16>(x);
+  if constexpr (L > 1) x = pair_sum<1>(x);
+  if constexpr (L > 2) x = pair_sum<2>(x);
+  if constexpr (L > 4) x = pair_sum<4>(x);
+  if constexpr (L > 8) x = pair_sum<8>(x);
+  if constexpr (L > 16) x = pair_sum<16>(x);
   return x;
 }
 
-// Wavefront reductions (all 64 lanes participate).
+// Wavefront reductions (all 64 lanes participate), VALU only: DPP within
+// rows, permlane swaps across them.
 __device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m));
-  return x;
+  x = pair_max<1>(x);
+  x = pair_max<2>(x);
+  x = pair_max<4>(x);
+  x = pair_max<8>(x);
+  x = pair_max<16>(x);
+  return pair_max<32>(x);
 }
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
-  return x;
+  x = pair_sum<1>(x);
+  x = pair_sum<2>(x);
+  x = pair_sum<4>(x);
+  x = pair_sum<8>(x);
+  x = pair_sum<16>(x);
+  return pair_sum<32>(x);
+}
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+  v = pair_sum_u32<1>(v);
+  v = pair_sum_u32<2>(v);
+  v = pair_sum_u32<4>(v);
+  v = pair_sum_u32<8>(v);
+  v = pair_sum_u32<16>(v);
+  return pair_sum_u32<32>(v);
 }
 
 __device__ __forceinline__ constexpr float rsqrt_pow2(int d) {
