@@ -20,9 +20,9 @@
 //     3. Inference Integration, local sliding window of recent tokens kept
 //     uncompressed).
 //
-// Kernels: attn_lut (q rotation slices, LUT) -> attn_chunk (code streaming,
-// K scores, V histogram, contraction, window) -> attn_merge (LSE merge,
-// unrotation).
+// Kernels: [attn_lut (q rotation slices, LUT)] -> attn_chunk (LUT when not
+// staged from attn_lut, code streaming, K scores, V histogram, contraction,
+// window) -> attn_merge (LSE merge, unrotation).
 //
 // The histogram accumulates the weights p = exp(s - m_chunk) in [0, 1] as
 // fixed-point integers round(p * 2^F) with LDS integer atomics (ds_add_u32,
@@ -93,9 +93,13 @@ AttnPlan attn_plan(int B, int Hq, int Hkv, int D, int S, int G, int C, int Tc, i
   }
   // fixed-point weights: every bin and every chunk sum below 2^31
   if (p.n_chunks > 0) p.fbits = 31 - ceil_log2(p.chunk);
+  // LUT built by the chunk blocks themselves unless the K codebook re-reads
+  // (S*C*D floats per block, from L2) outweigh one LUT pass
+  p.fuse_lut = p.n_chunks > 0 &&
+               (size_t)B * Hkv * p.n_hsplit * p.n_chunks * S * C * D * 4 <= ((size_t)96 << 20);
   p.pstride = D + 4;                                    // m, l, pad, pad, o[D]
   p.lut_slice = ((size_t)SG * C * (p.rp ? p.rp : 1) * 4 + 255) & ~(size_t)255;
-  p.lut_bytes = p.n_chunks ? (size_t)B * Hkv * p.n_hsplit * p.lut_slice : 0;
+  p.lut_bytes = p.n_chunks && !p.fuse_lut ? (size_t)B * Hkv * p.n_hsplit * p.lut_slice : 0;
   p.part_bytes = (size_t)B * Hq * (p.n_chunks + p.n_wblocks) * p.pstride * sizeof(float);
   p.ws_bytes = ((p.lut_bytes + 255) & ~(size_t)255) + p.part_bytes;
   return p;
@@ -453,7 +457,8 @@ __global__ __launch_bounds__(CH_THREADS, 1) void attn_chunk_kernel(
     const uint8_t* __restrict__ kcodes, const uint8_t* __restrict__ vcodes,
     const float* __restrict__ vcb, const float* __restrict__ lut, float* __restrict__ part,
     int Hq, int Hkv, int S, int G, int C, int Tc, int n_chunks, int chunk, int n_hsplit,
-    int pstride, int fbits, int cparts, size_t lut_slice, const float* __restrict__ q,
+    int pstride, int fbits, int cparts, size_t lut_slice, const float* __restrict__ kcb,
+    int fuse_lut, const float* __restrict__ q,
     const uint16_t* __restrict__ kw, const uint16_t* __restrict__ vw, int W, int wslice,
     int nslots, float scale) {
   constexpr int L = D / 8;
@@ -503,8 +508,92 @@ __global__ __launch_bounds__(CH_THREADS, 1) void attn_chunk_kernel(
     }
   }
 
-  // ---- stage this unit's LUT: whole 1 KiB pieces straight into LDS, tail by hand
-  {
+  if (fuse_lut) {
+    // ---- build this unit's LUT in LDS: scale * H q / sqrt(D) for the RP
+    // heads (wave 0), then entry (sg, c) = q_rot_g . C^K_sg[c], summed in the
+    // order attn_lut_kernel uses.  For dsub = 8 the codebook rows come in
+    // batches of 4 per thread, the first batch in flight across the q
+    // rotation and each next one across the current one's arithmetic.
+    __shared__ float qs[RP][D];
+    const int dsub = D / G;
+    const int nit = SG * C;
+    float4 cb0[4][2], cb1[4][2];
+    auto load_batch = [&](float4 (&cb)[4][2], int base) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int it = base + tid + CH_THREADS * i;
+        if (it < nit) {
+          const float4* cp = reinterpret_cast<const float4*>(kcb + (int64_t)it * 8);
+          cb[i][0] = cp[0];
+          cb[i][1] = cp[1];
+        }
+      }
+    };
+    auto lut_entry = [&](int it, auto&& cv, int n) {     // cv(j): entry j of row it
+      const int g = (it / C) % G;
+      float acc[RP];
+#pragma unroll
+      for (int r = 0; r < RP; ++r) acc[r] = 0.0f;
+      for (int j = 0; j < n; ++j) {
+        const float c = cv(j);
+#pragma unroll
+        for (int r = 0; r < RP; ++r) acc[r] = __builtin_fmaf(qs[r][g * n + j], c, acc[r]);
+      }
+      if constexpr (RP == 4) {
+        *reinterpret_cast<float4*>(tabf + it * 4) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      } else if constexpr (RP == 2) {
+        *reinterpret_cast<float2*>(tabf + it * 2) = make_float2(acc[0], acc[1]);
+      } else {
+        tabf[it] = acc[0];
+      }
+    };
+    if (dsub == 8) load_batch(cb0, 0);
+    if (tid < 64) {
+      constexpr int ROWS = 64 / L;
+#pragma unroll
+      for (int r0 = 0; r0 < RP; r0 += ROWS) {
+        const int r = r0 + lane / L;
+        const int rr = r < RP ? r : RP - 1;
+        const float* qp = q + ((int64_t)b * Hq + h0 + (rr < nh ? rr : nh - 1)) * D + (lane % L) * 8;
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = qp[e];
+        hadamard_row<8, L>(v, lane);
+        const float rs = scale * rsqrt_pow2(D);
+        if (r < RP) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) qs[r][(lane % L) * 8 + e] = v[e] * rs;
+        }
+      }
+    }
+    __syncthreads();
+    if (dsub == 8) {
+      for (int base = 0; base < nit; base += 8 * CH_THREADS) {
+        if (base + 4 * CH_THREADS < nit) load_batch(cb1, base + 4 * CH_THREADS);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int it = base + tid + CH_THREADS * i;
+          const float cv[8] = {cb0[i][0].x, cb0[i][0].y, cb0[i][0].z, cb0[i][0].w,
+                               cb0[i][1].x, cb0[i][1].y, cb0[i][1].z, cb0[i][1].w};
+          if (it < nit) lut_entry(it, [&](int j) { return cv[j]; }, 8);
+        }
+        if (base + 8 * CH_THREADS < nit) load_batch(cb0, base + 8 * CH_THREADS);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int it = base + 4 * CH_THREADS + tid + CH_THREADS * i;
+          const float cv[8] = {cb1[i][0].x, cb1[i][0].y, cb1[i][0].z, cb1[i][0].w,
+                               cb1[i][1].x, cb1[i][1].y, cb1[i][1].z, cb1[i][1].w};
+          if (it < nit) lut_entry(it, [&](int j) { return cv[j]; }, 8);
+        }
+      }
+    } else {
+      for (int it = tid; it < nit; it += CH_THREADS) {
+        const float* cp = kcb + (int64_t)it * dsub;
+        lut_entry(it, [&](int j) { return cp[j]; }, dsub);
+      }
+    }
+  } else {
+    // ---- stage this unit's LUT: whole 1 KiB pieces straight into LDS, tail by hand
     const uint8_t* src = reinterpret_cast<const uint8_t*>(lut) +
                          ((size_t)b * Hkv * n_hsplit + unit) * lut_slice;
     const int bytes = tabn * 4;
@@ -832,7 +921,7 @@ static hipError_t launch_rp(const AttnPlan& p, int SG, const float* q, const flo
                             hipStream_t st) {
   hipError_t e = hipSuccess;
   size_t lds = 0;
-  if (p.n_chunks > 0) {
+  if (p.n_chunks > 0 && !p.fuse_lut) {
     if (D == 64)
       attn_lut_kernel<RP, 64><<<dim3(B * Hkv * p.n_hsplit, SG), 256, 0, st>>>(
           q, kcb, lut, Hq, Hkv, p.n_hsplit, G, C, p.lut_slice, scale);
@@ -844,6 +933,8 @@ static hipError_t launch_rp(const AttnPlan& p, int SG, const float* q, const flo
           q, kcb, lut, Hq, Hkv, p.n_hsplit, G, C, p.lut_slice, scale);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
+  }
+  if (p.n_chunks > 0) {
     const size_t tab = (((size_t)SG * C * RP * 4) + 15) & ~(size_t)15;
     lds = tab + (size_t)S * p.cparts * RP * D * 4;
   }
@@ -863,7 +954,8 @@ static hipError_t launch_rp(const AttnPlan& p, int SG, const float* q, const flo
     if (e != hipSuccess) return e;                                                             \
     kern<<<grid, CH_THREADS, lds, st>>>(kc, vc, vcb, lut, part, Hq, Hkv, S, G, C, Tc,          \
                                         p.n_chunks, p.chunk, p.n_hsplit, p.pstride, p.fbits,   \
-                                        p.cparts, p.lut_slice, q, kw, vw, W, p.wslice, nslots, \
+                                        p.cparts, p.lut_slice, kcb, p.fuse_lut, q, kw, vw, W,  \
+                                        p.wslice, nslots,                                      \
                                         scale);                                                \
     return hipGetLastError();                                                                  \
   }

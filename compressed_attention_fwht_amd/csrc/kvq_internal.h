@@ -23,6 +23,7 @@ struct AttnPlan {
   int cparts;      // codeword ranges per (stage, dims) item in the V contraction
   int wslice;      // window tokens joining each chunk block (0: window blocks)
   int n_wblocks;   // window blocks of ATTN_WIN_BLOCK tokens, records after the chunks' ones
+  int fuse_lut;    // 1: chunk blocks build their LUT (no attn_lut pass, no LUT bytes)
   int pstride;     // floats per partial record (m, l, pad, pad, o[D])
   size_t lut_slice;  // bytes of one (sequence, KV head, head split) LUT slice
   size_t lut_bytes, part_bytes, ws_bytes;

@@ -142,9 +142,12 @@ def test_attend_argument_errors():
 
 
 def test_attend_workspace_sizes():
-    # LUT B*Hq*S*G*C floats, then per (b, h) (chunks + window blocks) records of D + 4 floats
+    # [LUT of B*Hq*S*G*C floats, when a separate pass builds it], then per
+    # (b, h) one record of D + 4 floats per chunk and per window block
     sz = kvq.attend_workspace_size(1, 32, 8, 128, 32640, 128, 1, 16, 256)
-    lut = 32 * 16 * 256 * 4
-    assert sz > lut and (sz - lut) % (32 * 132 * 4) == 0
+    assert sz % (32 * 132 * 4) == 0 and 8 <= sz // (32 * 132 * 4) <= 64   # LUT built in blocks
+    big = kvq.attend_workspace_size(1, 32, 8, 128, 130816, 256, 4, 16, 256)
+    lut = 32 * 64 * 256 * 4                                              # LUT pass: K codebook
+    assert big > lut and (big - lut) % (32 * 132 * 4) == 0               # re-reads would be big
     sz_w = kvq.attend_workspace_size(2, 4, 2, 64, 0, 50, 2, 1, 256)   # window only
     assert sz_w == 2 * 4 * 1 * 68 * 4                                  # no LUT, one window block
