@@ -3,22 +3,31 @@
 One step = the whole path on one batch of the Llama-3-8B-shaped layer
 (8 KV / 32 query heads, head_dim 128, 32768 tokens, 128-token fp16 window,
 16 groups x 8 dims, 1 stage, C = 256):
-  encode    K and V of the 32640 coded tokens (rotation, distance GEMM on
-            MFMA, argmin, residual update, code store),
+  encode       K and V of the 32640 coded tokens (rotation, distance GEMM on
+               MFMA, argmin, residual update, code store),
   reconstruct  every coded vector from its codes (sum of codewords, unrotated),
-  decode    single-token attention for the 32 query heads over the codes and
-            the fp16 window (q rotation, LUT, code streaming, split-K, LSE merge).
-Inputs are resident in HBM before timing; a 512 MB write between the
-producer kernels and the decode evicts the 256 MB Infinity Cache so the decode
-reads its codes from HBM.
+  decode       single-token attention for the 32 query heads over the codes
+               and the fp16 window (q rotation, LUT, code streaming, split-K,
+               LSE merge).
+Inputs are resident in HBM before timing.  The codebooks are packed into the
+encode workspace once at set-up (they are constants of the layer, like
+weights); each step's encode reads the packed copy.  A 512 MB write before the
+encode and before the decode evicts the 256 MB Infinity Cache, so both read
+HBM.
 
 Prints ONE JSON line.  ``value`` is the decode effective bandwidth (code +
-window + LUT bytes over the decode kernels' time); the encode throughput and
-its fraction of the bf16 MFMA peak are reported beside it.
+window + LUT bytes over the decode call's time); the encode throughput and
+its fraction of the bf16 MFMA peak are reported beside it, and again for the
+32-layer bulk prefill encode.  ``roofline`` is for the kernel that takes the
+most time in the step; its HBM ``traffic`` comes from the rocprofv3 counter
+summary committed for that kernel, and is null when the kernel's source has
+changed since those counters were taken.
 """
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -28,8 +37,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-BF16_PEAK_TFLOPS = 2516.6     # dense MFMA, 256 CU x 2.4 GHz x 4096 flop/clk/CU
+BF16_PEAK_TFLOPS = 2516.6         # dense MFMA: 256 CU x 2.4 GHz x 4096 flop/clk/CU
 VALU_LANE_OPS = 256 * 2.4e9 * 64  # non-packed 32-bit VALU lane-ops per second
+CSRC = os.path.join(ROOT, "compressed_attention_fwht_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
 
 
 def parse():
@@ -39,8 +50,39 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", type=int, default=2)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-prefill", action="store_true",
+                   help="skip the 32-layer bulk prefill encode measurement")
     p.add_argument("--no-flush", action="store_true")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="run a plain 256 MiB device copy 3x first (scale for HBM counters)")
     return p.parse_args()
+
+
+def source_sha(name):
+    with open(os.path.join(CSRC, name), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def profiled_traffic(kernel, source):
+    """HBM bytes per launch of ``kernel`` from its committed counter summary
+    (profiles/<kernel>_<workload>.md holds a JSON block), or None when there is
+    none or the kernel's source changed since it was taken."""
+    if not os.path.isdir(PROFILES):
+        return None, None
+    for fn in sorted(os.listdir(PROFILES)):
+        if not (fn.startswith(kernel) and fn.endswith(".md")):
+            continue
+        txt = open(os.path.join(PROFILES, fn)).read()
+        m = re.search(r"```json\n(.*?)\n```", txt, re.S)
+        if not m:
+            continue
+        d = json.loads(m.group(1))
+        if "traffic_bytes_per_launch" not in d:
+            continue
+        if d.get("source_sha256") != source_sha(source):
+            return None, fn
+        return d["traffic_bytes_per_launch"], fn
+    return None, None
 
 
 def main():
@@ -81,6 +123,18 @@ def main():
     kc = codes[0].view(B, Hkv, Tc, S, G)
     vc = codes[1].view(B, Hkv, Tc, S, G)
 
+    if args.calibrate_copy:                 # a copy kernel of known size for the counters
+        src = torch.empty(256 * 1024 * 1024 // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    # set-up: pack the codebooks into the encode workspace (layer constants)
+    kvq.encode(x, cb, n_rows=Tc, codes=codes, workspace=enc_ws)
+    torch.cuda.synchronize()
+
     def flush(i):
         if not args.no_flush:
             flush_buf.fill_(float(i))
@@ -91,7 +145,7 @@ def main():
         e = [torch.cuda.Event(enable_timing=True) for _ in range(5)] if timed else None
         flush(i)
         if timed: e[0].record()
-        kvq.encode(x, cb, n_rows=Tc, codes=codes, workspace=enc_ws)
+        kvq.encode(x, cb, n_rows=Tc, codes=codes, workspace=enc_ws, packed=True)
         if timed: e[1].record()
         kvq.decode_reconstruct(codes, cb, unrotate=True, out=recon)
         if timed: e[2].record()
@@ -129,21 +183,36 @@ def main():
     dec_gbs = eff_b / att_s / 1e9
     enc_tflops = enc_flops / enc_s / 1e12
     cand_per_s = n_vec * S * G * C / enc_s
-    times = {"encode": enc_s, "reconstruct": rec_s, "decode": att_s}
-    dominant = max(times, key=times.get)
+
+    # roofline of the kernel that takes the most time, on its mean launch time
+    means = {"encode": float(np.mean(enc_ms)) * 1e-3, "reconstruct": float(np.mean(rec_ms)) * 1e-3,
+             "decode": float(np.mean(att_ms)) * 1e-3}
+    dominant = max(means, key=means.get)
     if dominant == "encode":
-        roof = {"kernel": "encode (kvq_encode: codebook pack + encode_mfma_kernel)", "bound": "mfma",
-                "achieved": round(enc_tflops, 3), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(enc_tflops / BF16_PEAK_TFLOPS, 4), "traffic": None}
+        ach = enc_flops / means["encode"] / 1e12
+        traffic, prof = profiled_traffic("encode_mfma_kernel", "encode.hip")
+        roof = {"bound": "mfma", "achieved": round(ach, 3), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": traffic,
+                "kernel": "encode_mfma_kernel (kvq_encode, codebooks packed)",
+                "per_launch": {"flops": enc_flops, "vectors": n_vec,
+                               "mean_ms": round(means["encode"] * 1e3, 5)},
+                "counters": prof}
     elif dominant == "reconstruct":
-        gbs = rec_b / rec_s / 1e9
-        roof = {"kernel": "reconstruct_kernel", "bound": "hbm", "achieved": round(gbs, 1),
-                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                "traffic": None}
+        ach = rec_b / means["reconstruct"] / 1e9
+        traffic, prof = profiled_traffic("reconstruct_kernel", "reconstruct.hip")
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": "reconstruct_kernel (kvq_decode_reconstruct)",
+                "per_launch": {"bytes": rec_b, "mean_ms": round(means["reconstruct"] * 1e3, 5)},
+                "counters": prof}
     else:
-        roof = {"kernel": "decode (attn_prep + attn_chunk + attn_merge)", "bound": "hbm",
-                "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": None}
+        ach = eff_b / means["decode"] / 1e9
+        traffic, prof = profiled_traffic("attn_chunk_kernel", "attend.hip")
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": "kvq_attend_decode (attn_chunk + attn_merge)",
+                "per_launch": {"bytes": eff_b, "mean_ms": round(means["decode"] * 1e3, 5)},
+                "counters": prof}
 
     res = {
         "metric": "decode-attn effective HBM GB/s (% peak) + encode Mvec/s (% MFMA peak)",
@@ -178,45 +247,103 @@ def main():
                               "decode": [round(float(np.percentile(att_ms, p)), 5) for p in (10, 90)]},
         "roofline": roof,
     }
-
+    del x, recon, flush_buf
+    torch.cuda.empty_cache()
+    if not args.no_prefill:
+        res["encode_prefill"] = prefill_encode(torch, kvq, synth, dev)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, inp, codes, eff_b, dec_gbs)
     print(json.dumps(res), flush=True)
 
 
-def cpu_baseline(w, inp, codes, eff_b, dec_gbs):
-    """The float64 oracle on a bounded sample of the same workload: decode
-    attention for 2 of the KV heads (all their query heads, every coded token
-    plus the window), and encode of 8192 vectors."""
+def prefill_encode(torch, kvq, synth, dev, reps=5):
+    """Encode throughput of the 32-layer bulk prefill workload (32 layers x
+    K|V x 8 KV heads x 32768 tokens, 16x8 groups, 2 stages): one kvq_encode
+    call over all 64 books.  K/V are drawn on the GPU with the workload's law
+    (N(0,1), rotate-half RoPE theta 5e5 on K, bf16); codebooks are the
+    workload's own."""
+    w = synth.workload(5)
+    L, H, T, D = w.layers, w.n_kv_heads, w.tokens, w.head_dim
+    S, G, C = w.n_stages, w.n_groups, w.n_codewords
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(w.seed)
+    x = torch.empty((2 * L, H, T, D), dtype=torch.bfloat16, device=dev)
+    half = D // 2
+    inv = w.rope_theta ** (-2.0 * torch.arange(half, dtype=torch.float64, device=dev) / D)
+    ang = torch.arange(T, dtype=torch.float64, device=dev)[:, None] * inv[None, :]
+    cs, sn = torch.cos(ang).float(), torch.sin(ang).float()
+    for b in range(2 * L):
+        v = torch.randn((H, T, D), generator=gen, device=dev, dtype=torch.float32)
+        if b % 2 == 0:                                  # K carries RoPE
+            x1, x2 = v[..., :half].clone(), v[..., half:].clone()
+            v[..., :half] = x1 * cs - x2 * sn
+            v[..., half:] = x2 * cs + x1 * sn
+        x[b] = v.to(torch.bfloat16)
+    cb = torch.from_numpy(synth.make_codebooks(w)).to(dev)
+    codes = torch.empty((2 * L, H, T, S, G), dtype=torch.uint8, device=dev)
+    ws = torch.empty(kvq.encode_workspace_size(D, G, S, C, 2 * L), dtype=torch.uint8, device=dev)
+    kvq.encode(x, cb, codes=codes, workspace=ws)       # packs the codebooks, warms up
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        kvq.encode(x, cb, codes=codes, workspace=ws, packed=True)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    n_vec = 2 * L * H * T
+    t = float(np.median(ts)) * 1e-3
+    flops = 2.0 * D * C * S * n_vec
+    del x, codes, ws
+    torch.cuda.empty_cache()
+    return {"workload": f"{w.name}: {L} layers x K|V x Hkv={H} x T={T}, D={D}, "
+                        f"G={G}x{D // G} S={S} C={C}",
+            "value": round(n_vec / t / 1e6, 2), "unit": "Mvec/s", "ms": round(t * 1e3, 4),
+            "vectors": n_vec, "pct_bf16_mfma_peak": round(100 * flops / t / 1e12 / BF16_PEAK_TFLOPS, 3),
+            "reps": reps}
+
+
+def cpu_baseline(w, inp, codes, eff_b, dec_gbs, budget_s=10.0):
+    """The float64 oracle, as it stands, on a bounded sample of the same
+    workload: whole decode calls (all sequences, KV heads and query heads,
+    every coded token plus the window) repeated for about ``budget_s``
+    seconds, then encode of growing batches of the layer's vectors for about
+    ``budget_s`` seconds."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
         blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         blas = os.cpu_count()
-    B, Hkv, Hq, Tc, S, G = w.batch, w.n_kv_heads, w.n_q_heads, w.code_tokens, w.n_stages, w.n_groups
-    rep = Hq // Hkv
-    kvs = 2
+    B, Hkv, Tc, S, G = w.batch, w.n_kv_heads, w.code_tokens, w.n_stages, w.n_groups
     c = codes.cpu().numpy()
-    kc = c[0].reshape(B, Hkv, Tc, S, G)[:1, :kvs]
-    vc = c[1].reshape(B, Hkv, Tc, S, G)[:1, :kvs]
-    t0 = time.perf_counter()
-    oracle.attend(inp["q"][:1, :kvs * rep], kc, vc, inp["cb"][0], inp["cb"][1],
-                  inp["k_win"][:1, :kvs] if w.window else None,
-                  inp["v_win"][:1, :kvs] if w.window else None)
-    t_dec = time.perf_counter() - t0
-    frac = kvs / (B * Hkv)
-    gbs = eff_b * frac / t_dec / 1e9
-    xs = inp["x_f32"][0].reshape(-1, w.head_dim)[:8192].astype(np.float64)
-    t0 = time.perf_counter()
-    oracle.rvq_encode(xs, inp["cb"][0])
-    t_enc = time.perf_counter() - t0
+    kc = c[0].reshape(B, Hkv, Tc, S, G)
+    vc = c[1].reshape(B, Hkv, Tc, S, G)
+    reps, t_dec = 0, 0.0
+    while t_dec < budget_s:
+        t0 = time.perf_counter()
+        oracle.attend(inp["q"], kc, vc, inp["cb"][0], inp["cb"][1],
+                      inp["k_win"] if w.window else None, inp["v_win"] if w.window else None)
+        t_dec += time.perf_counter() - t0
+        reps += 1
+    gbs = eff_b * reps / t_dec / 1e9
+    xs_all = inp["x_f32"][0].reshape(-1, w.head_dim)
+    n_enc, t_enc, n = 0, 0.0, 4096
+    while t_enc < budget_s and n_enc < xs_all.shape[0]:
+        xs = xs_all[n_enc:n_enc + n].astype(np.float64)
+        t0 = time.perf_counter()
+        oracle.rvq_encode(xs, inp["cb"][0])
+        t_enc += time.perf_counter() - t0
+        n_enc += xs.shape[0]
+        n *= 2
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": int(blas), "kind": "oracle",
-            "sample": f"decode: {kvs} of {B * Hkv} (sequence, KV head) pairs with all {rep} query "
-                      f"heads each, {Tc} coded + {w.window} window tokens ({t_dec:.1f} s); encode: "
-                      f"8192 vectors ({t_enc:.1f} s). float64 NumPy; elementwise work on one core, "
-                      f"matrix products on {blas} BLAS threads",
-            "encode_mvec_per_s": round(8192 / t_enc / 1e6, 6),
+            "sample": f"decode: {reps} whole decode calls of the workload ({B * Hkv} (sequence, "
+                      f"KV head) pairs, {w.n_q_heads} query heads, {Tc} coded + {w.window} window "
+                      f"tokens) in {t_dec:.1f} s; encode: the first {n_enc} K vectors in "
+                      f"{t_enc:.1f} s. float64 NumPy; elementwise work on one core, matrix "
+                      f"products on {blas} BLAS threads",
+            "encode_mvec_per_s": round(n_enc / t_enc / 1e6, 6),
             "gpu_over_cpu_decode": round(dec_gbs / gbs, 1)}
 
 

@@ -29,6 +29,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvq.so")
 KVQ_INPUT_PRE_ROTATED = 0x1
 KVQ_UNROTATE = 0x2
 KVQ_ENCODE_GENERIC = 0x4
+KVQ_CODEBOOKS_PACKED = 0x8
 F32, BF16, F16 = 0, 1, 2
 
 EXPORTS = ("kvq_rotate", "kvq_encode_workspace_size", "kvq_encode", "kvq_decode_reconstruct",
@@ -152,11 +153,13 @@ def encode_workspace_size(head_dim, n_groups, n_stages, n_codewords, n_books) ->
 
 
 def encode(x, codebooks, *, n_rows=None, pre_rotated=False, generic=False, codes=None,
-           workspace=None):
+           workspace=None, packed=False):
     """Encode rows [0, n_rows) of every sequence.
 
     x: [n_books][n_seq][seq_stride][D] (f32/bf16/f16); codebooks:
-    [n_books][S][G][C][dsub] f32.  Returns codes [n_books][n_seq][n_rows][S][G] u8."""
+    [n_books][S][G][C][dsub] f32.  Returns codes [n_books][n_seq][n_rows][S][G] u8.
+    ``packed``: ``workspace`` already holds these codebooks packed by an
+    earlier call (KVQ_CODEBOOKS_PACKED)."""
     torch = _torch()
     _need_contig(x, codebooks)
     nb, ns, stride, D = x.shape
@@ -169,7 +172,10 @@ def encode(x, codebooks, *, n_rows=None, pre_rotated=False, generic=False, codes
     need = encode_workspace_size(D, G, S, C, nb)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
-    flags = (KVQ_INPUT_PRE_ROTATED if pre_rotated else 0) | (KVQ_ENCODE_GENERIC if generic else 0)
+    if packed and workspace is None:
+        raise ValueError("packed=True needs the workspace holding the packed codebooks")
+    flags = ((KVQ_INPUT_PRE_ROTATED if pre_rotated else 0) | (KVQ_ENCODE_GENERIC if generic else 0)
+             | (KVQ_CODEBOOKS_PACKED if packed else 0))
     ws_bytes = workspace.numel() if workspace is not None else 0
     _check(_lib().kvq_encode(_ptr(x), _dtype_code(x), ctypes.byref(vq), nb, ns, stride, n_rows,
                           _ptr(codebooks), _ptr(codes), flags, _ptr(workspace), ws_bytes,

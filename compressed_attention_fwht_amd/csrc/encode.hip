@@ -442,17 +442,20 @@ static hipError_t launch_generic_t(const void* x, int xt, const float* cb, uint8
 
 hipError_t launch_encode(const void* x, int xt, int D, int G, int S, int C, int64_t n_books,
                          int64_t n_seq, int64_t seq_stride, int64_t n_rows, const float* cb,
-                         uint8_t* codes, int pre_rotated, int force_generic, void* ws,
-                         hipStream_t st) {
+                         uint8_t* codes, int pre_rotated, int force_generic, int packed_in_ws,
+                         void* ws, hipStream_t st) {
   if (n_books == 0 || n_seq == 0 || n_rows == 0) return hipSuccess;
   if (!force_generic && encode_mfma_eligible(D, G, S, C, xt)) {
     uint8_t* packed = reinterpret_cast<uint8_t*>(ws);
-    const int64_t n_pack = n_books * S * G * 256;
-    int64_t pblocks = (n_pack + 255) / 256;
-    if (pblocks > 4096) pblocks = 4096;
-    pack_codebooks_kernel<<<dim3((unsigned)pblocks), dim3(256), 0, st>>>(cb, packed, n_books, S, G);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (!packed_in_ws) {
+      const int64_t n_pack = n_books * S * G * 256;
+      int64_t pblocks = (n_pack + 255) / 256;
+      if (pblocks > 4096) pblocks = 4096;
+      pack_codebooks_kernel<<<dim3((unsigned)pblocks), dim3(256), 0, st>>>(cb, packed, n_books, S,
+                                                                         G);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
 #define KVQ_MF(SS)                                                                          \
   if (S == SS) {                                                                           \
     if (xt == 1) return launch_mfma_t<SS, 1>(x, packed, codes, n_books, n_seq, seq_stride,  \

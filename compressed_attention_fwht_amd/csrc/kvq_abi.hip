@@ -110,7 +110,8 @@ kvq_status kvq_encode(const void* x, kvq_dtype xt, const kvq_vq_desc* vq, int64_
   if (!valid_dtype(xt)) return KVQ_ERR_DTYPE;
   kvq_status st = check_vq(vq);
   if (st != KVQ_OK) return st;
-  if (flags & ~(KVQ_INPUT_PRE_ROTATED | KVQ_ENCODE_GENERIC)) return KVQ_ERR_SHAPE;
+  if (flags & ~(KVQ_INPUT_PRE_ROTATED | KVQ_ENCODE_GENERIC | KVQ_CODEBOOKS_PACKED))
+    return KVQ_ERR_SHAPE;
   if (n_books < 0 || n_seq < 0 || seq_stride < 0 || n_rows < 0) return KVQ_ERR_SHAPE;
   if (n_rows > seq_stride) return KVQ_ERR_SHAPE;
   if (n_books == 0 || n_seq == 0 || n_rows == 0) return KVQ_OK;
@@ -130,7 +131,8 @@ kvq_status kvq_encode(const void* x, kvq_dtype xt, const kvq_vq_desc* vq, int64_
   }
   return hip_status(kvq::launch_encode(x, (int)xt, D, G, S, C, n_books, n_seq, seq_stride, n_rows,
                                        codebooks, codes, (flags & KVQ_INPUT_PRE_ROTATED) ? 1 : 0,
-                                       generic ? 1 : 0, workspace, stream));
+                                       generic ? 1 : 0, (flags & KVQ_CODEBOOKS_PACKED) ? 1 : 0,
+                                       workspace, stream));
 }
 
 kvq_status kvq_decode_reconstruct(const uint8_t* codes, const kvq_vq_desc* vq, int64_t n_books,

@@ -37,8 +37,8 @@ size_t encode_workspace_bytes(int D, int G, int S, int C, int64_t n_books);
 bool encode_mfma_eligible(int D, int G, int S, int C, int xt);
 hipError_t launch_encode(const void* x, int xt, int D, int G, int S, int C, int64_t n_books,
                          int64_t n_seq, int64_t seq_stride, int64_t n_rows, const float* cb,
-                         uint8_t* codes, int pre_rotated, int force_generic, void* ws,
-                         hipStream_t st);
+                         uint8_t* codes, int pre_rotated, int force_generic, int packed,
+                         void* ws, hipStream_t st);
 
 hipError_t launch_reconstruct(const uint8_t* codes, const float* cb, float* out, int64_t n_books,
                               int64_t n_per_book, int D, int G, int S, int C, int unrotate,

@@ -1,0 +1,132 @@
+"""Short text summaries of rocprofv3 output (CSV), for the profiles folder.
+
+  python -m compressed_attention_fwht_amd.profsummary stats KERNEL_STATS_CSV \\
+      --title T --cmd "the rocprofv3 command" --out FILE.md
+      per-kernel calls / average / min / max duration and share of GPU time.
+
+  python -m compressed_attention_fwht_amd.profsummary traffic \\
+      --fetch FETCH_COUNTER_CSV --write WRITE_COUNTER_CSV --kernel NAME \\
+      --source FILE.hip --copy-bytes N --cmd-fetch "..." --cmd-write "..." \\
+      --out FILE.md
+      FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of kernel NAME, each scaled
+      by what the same counter reads for a plain device copy of N bytes (the
+      largest __amd_rocclr_copyBuffer dispatches of the run), giving HBM bytes
+      per launch; the result goes into a JSON block with the SHA-256 of the
+      kernel's source so a reader can tell whether it still applies.
+
+Host-side text processing only; nothing here touches the GPU.
+"""
+import argparse
+import collections
+import csv
+import hashlib
+import json
+import os
+import sys
+
+CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
+
+
+def _short(name, n=90):
+    return name if len(name) <= n else name[: n - 3] + "..."
+
+
+def stats(args):
+    rows = list(csv.DictReader(open(args.csv)))
+    total = sum(float(r["TotalDurationNs"]) for r in rows) or 1.0
+    lines = [f"# {args.title}", "", "Command:", "", "```", args.cmd, "```", "",
+             "| kernel | calls | avg us | min us | max us | share of GPU time |",
+             "|---|---|---|---|---|---|"]
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        lines.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                     f"{100 * float(r['TotalDurationNs']) / total:.1f} % |")
+    open(args.out, "w").write("\n".join(lines) + "\n")
+
+
+def _per_dispatch(path, counter):
+    vals = collections.defaultdict(dict)   # kernel -> dispatch -> value
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        vals[r["Kernel_Name"]][r["Dispatch_Id"]] = float(r["Counter_Value"])
+    return vals
+
+
+def _kernel_mean(vals, key):
+    hits = [v for name, d in vals.items() if key in name for v in d.values()]
+    if not hits:
+        raise SystemExit(f"no dispatch of a kernel named like {key!r}")
+    return sum(hits) / len(hits), len(hits)
+
+
+def _copy_kib(vals):
+    copies = [v for name, d in vals.items() if "copyBuffer" in name for v in d.values()]
+    if not copies:
+        raise SystemExit("no __amd_rocclr_copyBuffer dispatch (run with the calibration copy)")
+    top = max(copies)
+    big = [v for v in copies if v >= 0.5 * top]
+    return sum(big) / len(big), len(big)
+
+
+def traffic(args):
+    fv = _per_dispatch(args.fetch, "FETCH_SIZE")
+    wv = _per_dispatch(args.write, "WRITE_SIZE")
+    f_k, nf = _kernel_mean(fv, args.kernel)
+    w_k, nw = _kernel_mean(wv, args.kernel)
+    f_c, ncf = _copy_kib(fv)
+    w_c, ncw = _copy_kib(wv)
+    ff = args.copy_bytes / (f_c * 1024.0)
+    fw = args.copy_bytes / (w_c * 1024.0)
+    fetch_b = f_k * 1024.0 * ff
+    write_b = w_k * 1024.0 * fw
+    sha = hashlib.sha256(open(os.path.join(CSRC, args.source), "rb").read()).hexdigest()
+    d = {"kernel": args.kernel, "source": args.source, "source_sha256": sha,
+         "fetch_kib_per_dispatch": round(f_k, 1), "write_kib_per_dispatch": round(w_k, 1),
+         "dispatches": {"fetch_run": nf, "write_run": nw},
+         "copy_bytes": args.copy_bytes,
+         "copy_fetch_kib": round(f_c, 1), "copy_write_kib": round(w_c, 1),
+         "fetch_scale": round(ff, 4), "write_scale": round(fw, 4),
+         "fetch_bytes_per_launch": round(fetch_b), "write_bytes_per_launch": round(write_b),
+         "traffic_bytes_per_launch": round(fetch_b + write_b)}
+    if args.algorithmic_bytes:
+        d["algorithmic_bytes_per_launch"] = args.algorithmic_bytes
+        d["traffic_over_algorithmic"] = round((fetch_b + write_b) / args.algorithmic_bytes, 3)
+    lines = [f"# {args.title}", "",
+             "HBM traffic per launch from two counter passes, each scaled by the same counter",
+             f"read for a plain device copy of {args.copy_bytes} bytes in the same run.", "",
+             "FETCH_SIZE pass:", "", "```", args.cmd_fetch, "```", "",
+             "WRITE_SIZE pass:", "", "```", args.cmd_write, "```", "",
+             "| | kernel KiB/dispatch | copy KiB/dispatch | scale | bytes/launch |",
+             "|---|---|---|---|---|",
+             f"| FETCH_SIZE | {f_k:.1f} | {f_c:.1f} | {ff:.4f} | {fetch_b:.0f} |",
+             f"| WRITE_SIZE | {w_k:.1f} | {w_c:.1f} | {fw:.4f} | {write_b:.0f} |", "",
+             "```json", json.dumps(d, indent=1), "```"]
+    open(args.out, "w").write("\n".join(lines) + "\n")
+
+
+def main(argv=None):
+    p = argparse.ArgumentParser(prog="profsummary")
+    sub = p.add_subparsers(dest="cmd_name", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("csv")
+    s.add_argument("--title", required=True)
+    s.add_argument("--cmd", required=True)
+    s.add_argument("--out", required=True)
+    t = sub.add_parser("traffic")
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--kernel", required=True)
+    t.add_argument("--source", required=True)
+    t.add_argument("--copy-bytes", type=int, required=True)
+    t.add_argument("--algorithmic-bytes", type=int, default=0)
+    t.add_argument("--title", required=True)
+    t.add_argument("--cmd-fetch", required=True)
+    t.add_argument("--cmd-write", required=True)
+    t.add_argument("--out", required=True)
+    a = p.parse_args(argv)
+    (stats if a.cmd_name == "stats" else traffic)(a)
+
+
+if __name__ == "__main__":
+    main(sys.argv[1:])

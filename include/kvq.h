@@ -102,6 +102,8 @@ typedef struct {
 #define KVQ_INPUT_PRE_ROTATED 0x1u /* kvq_encode: x is already H_D x          */
 #define KVQ_UNROTATE          0x2u /* kvq_decode_reconstruct: output H_D x_rot */
 #define KVQ_ENCODE_GENERIC    0x4u /* kvq_encode: force the plain fp32 kernel  */
+#define KVQ_CODEBOOKS_PACKED  0x8u /* kvq_encode: workspace already holds these
+                                      codebooks packed (skip the packing pass) */
 
 /* y = H_D x for n_rows rows of length dim (dim in {64, 128, 256}).
  * x: [n_rows][dim] of type xt; y: [n_rows][dim] float32.  H_D is symmetric
@@ -122,7 +124,12 @@ KVQ_API kvq_status kvq_encode_workspace_size(const kvq_vq_desc* vq, int64_t n_bo
  *            x[b];
  * codes:     [n_books][n_seq][n_rows][S][G] uint8 (output).
  * Requires n_rows <= seq_stride.  Any of n_books, n_seq, n_rows may be 0
- * (no-op).  Codes equal the float64 greedy search except where the best two
+ * (no-op).  On the MFMA path the codebooks are first packed into the
+ * workspace (bf16 operand pieces and norms); the codebooks of a layer are
+ * constants, so a caller may pack once and pass KVQ_CODEBOOKS_PACKED on later
+ * calls with the same codebooks and the same workspace, which skips that
+ * pass.  codebooks is still required (the generic kernel reads it and
+ * ignores the flag).  Codes equal the float64 greedy search except where the best two
  * squared distances of a stage are within a relative 1e-4 of each other,
  * where either choice may be returned. */
 KVQ_API kvq_status kvq_encode(const void* x, kvq_dtype xt, const kvq_vq_desc* vq,

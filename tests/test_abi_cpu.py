@@ -70,6 +70,8 @@ def test_encode_argument_errors():
     assert _enc(rows=65) == SHAPE                        # rows beyond the sequence stride
     assert _enc(nb=-1) == SHAPE
     assert _enc(flags=0x80) == SHAPE
+    assert _enc(flags=0x10) == SHAPE
+    assert _enc(flags=0x8, x=0) == NULL                   # KVQ_CODEBOOKS_PACKED is a known flag
     assert _enc(vq=_vq(D=96, G=12)) == SHAPE             # head_dim not 64/128/256
     assert _enc(vq=_vq(G=15)) == SHAPE                   # G does not divide D
     assert _enc(vq=_vq(G=32)) == SHAPE                   # dsub 4 < 8

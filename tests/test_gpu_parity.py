@@ -158,6 +158,22 @@ def test_encode_pre_rotated_and_f16():
         assert tot["hard"] == 0 and tot["exact"] >= 0.999 * tot["total"]
 
 
+def test_encode_packed_codebooks_reused():
+    say("encode with codebooks packed by an earlier call")
+    w = synth.workload(3, batch=1, tokens=1500, window=0)
+    inp = synth.make_inputs(w)
+    x = to_dev(inp["x"], w)
+    cb = cuda(inp["cb"])
+    ws = torch.empty(kvq.encode_workspace_size(128, 16, 2, 256, 2), dtype=torch.uint8,
+                     device="cuda")
+    first = kvq.encode(x, cb, workspace=ws)
+    again = kvq.encode(x, cb, workspace=ws, packed=True)
+    assert torch.equal(first, again)
+    # the packed copy, not the float codebooks, is what the packed call reads
+    garbage = torch.full_like(cb, float("nan"))
+    assert torch.equal(kvq.encode(x, garbage, workspace=ws, packed=True), first)
+
+
 def test_encode_deterministic():
     say("encode determinism")
     w = synth.workload(2, tokens=2000, window=0)
