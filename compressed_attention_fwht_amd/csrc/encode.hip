@@ -75,9 +75,15 @@ __global__ void pack_codebooks_kernel(const float* __restrict__ cb, uint8_t* __r
 }
 
 // ================================================================ MFMA path
-constexpr int MF_WAVES = 8;                 // 512 threads, 64 vectors per wave
-constexpr int MF_TILE = MF_WAVES * 64;      // vectors per tile
 constexpr int MF_SCRATCH = 4096;            // per-wave transpose scratch (bytes)
+
+// Waves per block (64 vectors each) and LDS bytes of one group's codebook
+// buffer (the last stage's fp32 copy is never read: no residual update
+// follows it).  Up to two stages, blocks of 4 waves with two codebook buffers
+// fit twice per CU, so one block's row loads, rotation and barrier waits
+// overlap the other's argmin; four stages need the whole LDS for one block.
+template <int S> constexpr int mf_waves() { return S <= 2 ? 4 : 8; }
+template <int S> constexpr int mf_buf() { return (S - 1) * 20480 + 12288; }
 
 // Row address (in elements) of vector n of a book.
 __device__ __forceinline__ int64_t row_elem(int64_t book, int64_t n, int64_t n_rows, int64_t n_seq,
@@ -92,12 +98,12 @@ __device__ __forceinline__ int64_t row_elem(int64_t book, int64_t n, int64_t n_r
 // base.  Completion is awaited with wait_vmem().
 template <int S>
 __device__ __forceinline__ void stage_group(const uint8_t* src, uint8_t* dst, int wave, int lane) {
-  // 20 KiB per stage, except 12 KiB for the last one: no residual update
-  // follows it, so its fp32 copy is never read.
+  // 20 KiB per stage, except 12 KiB for the last one (mf_buf)
   constexpr int PIECES = 20 * (S - 1) + 12;
+  constexpr int W = mf_waves<S>();
 #pragma unroll
-  for (int k = 0; k < (PIECES + MF_WAVES - 1) / MF_WAVES; ++k) {
-    const int piece = k * MF_WAVES + wave;               // wave-uniform
+  for (int k = 0; k < (PIECES + W - 1) / W; ++k) {
+    const int piece = k * W + wave;                      // wave-uniform
     if (piece < PIECES) {
       const int st = piece / 20 < S - 1 ? piece / 20 : S - 1;
       const int off = st * PACK_BYTES + (piece - 20 * st) * 1024;
@@ -113,7 +119,7 @@ __device__ __forceinline__ void wait_vmem() {
 }
 
 template <int S, int XT>
-__global__ __launch_bounds__(512, 1) void encode_mfma_kernel(
+__global__ __launch_bounds__(64 * mf_waves<S>(), 8 / mf_waves<S>()) void encode_mfma_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ packed, uint8_t* __restrict__ codes,
     int64_t n_seq, int64_t seq_stride, int64_t n_rows, int64_t tiles_per_book, int pre_rotated) {
   constexpr int G = 16;
@@ -130,7 +136,9 @@ __global__ __launch_bounds__(512, 1) void encode_mfma_kernel(
   const int64_t book = blockIdx.x / tiles_per_book;
   const int64_t tile = blockIdx.x - book * tiles_per_book;
   const int64_t n_per_book = n_seq * n_rows;
-  const int64_t v_own = tile * MF_TILE + wave * 64 + lane;           // vector this lane owns
+  constexpr int TILE = 64 * mf_waves<S>();
+  constexpr int BUF = mf_buf<S>();
+  const int64_t v_own = tile * TILE + wave * 64 + lane;              // vector this lane owns
   const bool live = v_own < n_per_book;
   const int64_t v_ld = live ? v_own : (n_per_book - 1);
   const int64_t my_row = row_elem(book, v_ld, n_rows, n_seq, seq_stride);
@@ -207,10 +215,10 @@ __global__ __launch_bounds__(512, 1) void encode_mfma_kernel(
 
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    const uint8_t* cbs = smem + (g & 1) * (S * PACK_BYTES);
+    const uint8_t* cbs = smem + (g & 1) * BUF;
     // ---- the next group's codebooks stream into the other buffer meanwhile
     if (g + 1 < G) stage_group<S>(pk_book + (int64_t)(g + 1) * S * PACK_BYTES,
-                                  smem + ((g + 1) & 1) * (S * PACK_BYTES), wave, lane);
+                                  smem + ((g + 1) & 1) * BUF, wave, lane);
 
     float r[8];
 #pragma unroll
@@ -410,14 +418,15 @@ static hipError_t launch_mfma_t(const void* x, const uint8_t* packed, uint8_t* c
                                 int64_t n_books, int64_t n_seq, int64_t seq_stride, int64_t n_rows,
                                 int pre_rotated, hipStream_t st) {
   const int64_t n_per_book = n_seq * n_rows;
-  const int64_t tiles = (n_per_book + MF_TILE - 1) / MF_TILE;
-  size_t lds = (size_t)2 * S * PACK_BYTES;                 // two codebook buffers
-  if (lds < (size_t)MF_WAVES * MF_SCRATCH) lds = (size_t)MF_WAVES * MF_SCRATCH;
+  constexpr int TILE = 64 * mf_waves<S>();
+  const int64_t tiles = (n_per_book + TILE - 1) / TILE;
+  size_t lds = (size_t)2 * mf_buf<S>();                    // two codebook buffers
+  if (lds < (size_t)mf_waves<S>() * MF_SCRATCH) lds = (size_t)mf_waves<S>() * MF_SCRATCH;
   auto kern = encode_mfma_kernel<S, XT>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)lds);
   if (e != hipSuccess) return e;
-  kern<<<dim3((unsigned)(tiles * n_books)), dim3(512), lds, st>>>(
+  kern<<<dim3((unsigned)(tiles * n_books)), dim3(64 * mf_waves<S>()), lds, st>>>(
       reinterpret_cast<const uint16_t*>(x), packed, codes, n_seq, seq_stride, n_rows, tiles,
       pre_rotated);
   return hipGetLastError();
