@@ -258,39 +258,62 @@ __global__ __launch_bounds__(64 * mf_waves<S>(), 8 / mf_waves<S>()) void encode_
       __builtin_memcpy(&B2T0, b2t0, 16); __builtin_memcpy(&B2T1, b2t1, 16);
 
       int best0 = 0x7fffffff, best1 = 0x7fffffff;
-      // One codeword tile of 32 x (2 x 32 vectors): four MFMAs, then the argmin.
-      auto issue = [&](int t, f32x16_t& c0, f32x16_t& c1) {
+      // One codeword tile = 32 codewords x (2 x 32 vectors): two MFMAs per
+      // 32-vector half (A1.B1 then A2.B2 accumulated), then the argmin.
+      auto load_a = [&](int t, bf16x8_t& A1, bf16x8_t& A2) {
         const int m = 32 * t + m_lane;
         const uint4 a1 = *reinterpret_cast<const uint4*>(cbs_s + h * 4096 + m * 16);
         const uint4 a2 = *reinterpret_cast<const uint4*>(cbs_s + h * 8192 + m * 16);
-        bf16x8_t A1, A2;
         __builtin_memcpy(&A1, &a1, 16);
         __builtin_memcpy(&A2, &a2, 16);
+      };
+      auto issue = [&](const bf16x8_t& A1, const bf16x8_t& A2, const bf16x8_t& B1,
+                       const bf16x8_t& B2, f32x16_t& c) {
         const f32x16_t z = {0};
-        c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A1, B1T0, z, 0, 0, 0);
-        c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A1, B1T1, z, 0, 0, 0);
-        c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A2, B2T0, c0, 0, 0, 0);
-        c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A2, B2T1, c1, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A1, B1, z, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A2, B2, c, 0, 0, 0);
       };
       // The packed index (32t | row) comes from a scalar register, so each
       // candidate costs one v_and_or_b32; accumulator register i holds codeword
       // row 8*(i/4) + 4*h + (i%4) of the tile (h is or-ed in after the loop).
-      auto reduce = [&](int t, const f32x16_t& c0, const f32x16_t& c1) {
+      auto reduce = [&](int t, const f32x16_t& c, int& best) {
         const uint32_t tb = (uint32_t)__builtin_amdgcn_readfirstlane(t << 5);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const uint32_t idx = tb | (uint32_t)(8 * (i >> 2) + (i & 3));
-          const int k0 = (int)((__float_as_uint(c0[i]) & keep_hi) | idx);
-          const int k1 = (int)((__float_as_uint(c1[i]) & keep_hi) | idx);
-          best0 = min(best0, k0);
-          best1 = min(best1, k1);
+          best = min(best, (int)((__float_as_uint(c[i]) & keep_hi) | idx));
         }
       };
-#pragma nounroll
-      for (int t = 0; t < 8; ++t) {
+      if constexpr (S == 1) {
+        // the halves staggered: one half's MFMAs run while the other half's
+        // previous results are reduced (fits the registers for one stage)
+        bf16x8_t A1, A2;
         f32x16_t acc0, acc1;
-        issue(t, acc0, acc1);
-        reduce(t, acc0, acc1);
+        load_a(0, A1, A2);
+        issue(A1, A2, B1T0, B2T0, acc0);
+        issue(A1, A2, B1T1, B2T1, acc1);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const bool more = t + 1 < 8;
+          if (more) load_a(t + 1, A1, A2);
+          reduce(t, acc0, best0);
+          if (more) issue(A1, A2, B1T0, B2T0, acc0);
+          reduce(t, acc1, best1);
+          if (more) issue(A1, A2, B1T1, B2T1, acc1);
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          bf16x8_t P1, P2;
+          load_a(t, P1, P2);
+          const f32x16_t z = {0};
+          f32x16_t c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(P1, B1T0, z, 0, 0, 0);
+          f32x16_t c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(P1, B1T1, z, 0, 0, 0);
+          c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(P2, B2T0, c0, 0, 0, 0);
+          c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(P2, B2T1, c1, 0, 0, 0);
+          reduce(t, c0, best0);
+          reduce(t, c1, best1);
+        }
       }
       best0 |= h << 2;
       best1 |= h << 2;
