@@ -283,6 +283,34 @@ def test_decode_long_window(key, over):
     assert res["ok"], res
 
 
+def test_decode_reused_workspace_and_smaller_call():
+    say("decode twice on one workspace, then a smaller batch on it")
+    w = synth.workload(3, batch=2, tokens=2600, window=40)
+    inp = synth.make_inputs(w)
+    Tc = w.code_tokens
+    codes = [oracle.rvq_encode(inp["x_f32"][b][:, :Tc].reshape(-1, w.head_dim), inp["cb"][b])
+             for b in range(2)]
+    shp = (w.batch, w.n_kv_heads, Tc, w.n_stages, w.n_groups)
+    args = (cuda(inp["q"]), cuda(codes[0].reshape(shp)), cuda(codes[1].reshape(shp)),
+            cuda(inp["cb"][0]), cuda(inp["cb"][1]), cuda(inp["k_win"]), cuda(inp["v_win"]))
+    sz = kvq.attend_workspace_size(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, Tc, w.window,
+                                   w.n_stages, w.n_groups, w.n_codewords)
+    ws = torch.full((sz,), 0xAB, dtype=torch.uint8, device="cuda")      # no zeroing needed
+    first = kvq.attend_decode(*args, workspace=ws).cpu().numpy()
+    second = kvq.attend_decode(*args, workspace=ws).cpu().numpy()
+    assert np.array_equal(first, second)
+    ref = oracle.attend(inp["q"], codes[0].reshape(shp), codes[1].reshape(shp), inp["cb"][0],
+                        inp["cb"][1], inp["k_win"], inp["v_win"])
+    res = oracle.check_attn(second, ref)
+    assert res["ok"], res
+    small = kvq.attend_decode(args[0][:1].contiguous(), args[1][:1].contiguous(),
+                              args[2][:1].contiguous(), args[3], args[4],
+                              args[5][:1].contiguous(), args[6][:1].contiguous(),
+                              workspace=ws).cpu().numpy()
+    res = oracle.check_attn(small, ref[:1])
+    assert res["ok"], res
+
+
 def test_decode_codes_only_short():
     say("decode codes only, short cache")
     w = synth.workload(4, tokens=37, window=0)
