@@ -4,6 +4,10 @@
       --title T --cmd "the rocprofv3 command" --out FILE.md
       per-kernel calls / average / min / max duration and share of GPU time.
 
+  python -m compressed_attention_fwht_amd.profsummary counters COUNTER_CSV \\
+      --kernels NAME[,NAME...] --title T --cmd "..." --out FILE.md
+      mean per-dispatch value of every counter of the run for each kernel.
+
   python -m compressed_attention_fwht_amd.profsummary traffic \\
       --fetch FETCH_COUNTER_CSV --write WRITE_COUNTER_CSV --kernel NAME \\
       --source FILE.hip --copy-bytes N --cmd-fetch "..." --cmd-write "..." \\
@@ -105,6 +109,29 @@ def traffic(args):
     open(args.out, "w").write("\n".join(lines) + "\n")
 
 
+def counters(args):
+    keys = args.kernels.split(",")
+    vals = collections.defaultdict(lambda: collections.defaultdict(list))
+    names = {}
+    for r in csv.DictReader(open(args.csv)):
+        for k in keys:
+            if k in r["Kernel_Name"]:
+                vals[k][r["Counter_Name"]].append(float(r["Counter_Value"]))
+                names[k] = r["Kernel_Name"]
+    cnames = sorted({c for k in keys for c in vals[k]})
+    lines = [f"# {args.title}", "", "Command:", "", "```", args.cmd, "```", "",
+             "Mean per dispatch (dispatches in parentheses).", "",
+             "| counter | " + " | ".join(f"`{_short(names.get(k, k), 40)}`" for k in keys) + " |",
+             "|---|" + "---|" * len(keys)]
+    for c in cnames:
+        cells = []
+        for k in keys:
+            v = vals[k].get(c, [])
+            cells.append(f"{sum(v) / len(v):.4g} ({len(v)})" if v else "-")
+        lines.append(f"| {c} | " + " | ".join(cells) + " |")
+    open(args.out, "w").write("\n".join(lines) + "\n")
+
+
 def main(argv=None):
     p = argparse.ArgumentParser(prog="profsummary")
     sub = p.add_subparsers(dest="cmd_name", required=True)
@@ -113,6 +140,12 @@ def main(argv=None):
     s.add_argument("--title", required=True)
     s.add_argument("--cmd", required=True)
     s.add_argument("--out", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("csv")
+    c.add_argument("--kernels", required=True)
+    c.add_argument("--title", required=True)
+    c.add_argument("--cmd", required=True)
+    c.add_argument("--out", required=True)
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
@@ -125,7 +158,7 @@ def main(argv=None):
     t.add_argument("--cmd-write", required=True)
     t.add_argument("--out", required=True)
     a = p.parse_args(argv)
-    (stats if a.cmd_name == "stats" else traffic)(a)
+    {"stats": stats, "counters": counters, "traffic": traffic}[a.cmd_name](a)
 
 
 if __name__ == "__main__":
