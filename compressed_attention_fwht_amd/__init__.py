@@ -20,8 +20,9 @@ import ctypes
 import os
 
 __all__ = ["KvqError", "LIB_PATH", "lib", "rotate", "encode", "encode_workspace_size",
-           "decode_reconstruct", "attend_decode", "attend_workspace_size", "EXPORTS",
-           "KVQ_INPUT_PRE_ROTATED", "KVQ_UNROTATE", "KVQ_ENCODE_GENERIC", "VqDesc", "AttnDesc",
+           "decode_reconstruct", "attend_decode", "attend_workspace_size", "window_append",
+           "window_flush", "window_flush_workspace_size", "EXPORTS", "KVQ_INPUT_PRE_ROTATED",
+           "KVQ_UNROTATE", "KVQ_ENCODE_GENERIC", "KVQ_CODEBOOKS_PACKED", "VqDesc", "AttnDesc",
            "status_string"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvq.so")
@@ -33,7 +34,8 @@ KVQ_CODEBOOKS_PACKED = 0x8
 F32, BF16, F16 = 0, 1, 2
 
 EXPORTS = ("kvq_rotate", "kvq_encode_workspace_size", "kvq_encode", "kvq_decode_reconstruct",
-           "kvq_attend_workspace_size", "kvq_attend_decode", "kvq_status_string",
+           "kvq_attend_workspace_size", "kvq_attend_decode", "kvq_window_append",
+           "kvq_window_flush_workspace_size", "kvq_window_flush", "kvq_status_string",
            "kvq_last_hip_error")
 
 
@@ -45,7 +47,8 @@ class VqDesc(ctypes.Structure):
 class AttnDesc(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
                 ("n_kv_heads", ctypes.c_int32), ("n_code_tokens", ctypes.c_int32),
-                ("n_window", ctypes.c_int32), ("vq", VqDesc), ("softmax_scale", ctypes.c_float)]
+                ("n_window", ctypes.c_int32), ("vq", VqDesc), ("softmax_scale", ctypes.c_float),
+                ("code_stride", ctypes.c_int32), ("window_stride", ctypes.c_int32)]
 
 
 def _load():
@@ -59,6 +62,10 @@ def _load():
     L.kvq_decode_reconstruct.argtypes = [P, ctypes.POINTER(VqDesc), I64, I64, P, P, U32, P]
     L.kvq_attend_workspace_size.argtypes = [ctypes.POINTER(AttnDesc), ctypes.POINTER(SZ)]
     L.kvq_attend_decode.argtypes = [ctypes.POINTER(AttnDesc), P, P, P, P, P, P, P, P, P, SZ, P]
+    L.kvq_window_append.argtypes = [I32, I32, I32, I32, I32, P, P, P, P, P]
+    L.kvq_window_flush_workspace_size.argtypes = [ctypes.POINTER(VqDesc), ctypes.POINTER(SZ)]
+    L.kvq_window_flush.argtypes = [ctypes.POINTER(VqDesc), I32, I32, I32, I32, I32, P, P, I32, I32,
+                                   P, P, P, P, P, SZ, P]
     L.kvq_status_string.argtypes = [I32]
     L.kvq_status_string.restype = ctypes.c_char_p
     L.kvq_last_hip_error.argtypes = []
@@ -202,8 +209,9 @@ def decode_reconstruct(codes, codebooks, *, unrotate=False, out=None):
     return out
 
 
-def _attn_desc(B, Hq, Hkv, D, Tc, W, S, G, C, scale):
-    return AttnDesc(B, Hq, Hkv, Tc, W, VqDesc(D, G, S, C), 0.0 if scale is None else float(scale))
+def _attn_desc(B, Hq, Hkv, D, Tc, W, S, G, C, scale, code_stride=0, window_stride=0):
+    return AttnDesc(B, Hq, Hkv, Tc, W, VqDesc(D, G, S, C), 0.0 if scale is None else float(scale),
+                    code_stride, window_stride)
 
 
 def attend_workspace_size(B, Hq, Hkv, D, Tc, W, S, G, C, scale=None) -> int:
@@ -215,16 +223,20 @@ def attend_workspace_size(B, Hq, Hkv, D, Tc, W, S, G, C, scale=None) -> int:
 
 
 def attend_decode(q, k_codes, v_codes, k_cb, v_cb, k_win=None, v_win=None, *, scale=None,
-                  out=None, workspace=None):
-    """q [B][Hq][D] f32; k/v_codes [B][Hkv][Tc][S][G] u8; k/v_cb [S][G][C][dsub]
-    f32; k/v_win [B][Hkv][W][D] f16 (or None).  Returns f32 [B][Hq][D]."""
+                  out=None, workspace=None, n_code=None, n_window=None):
+    """q [B][Hq][D] f32; k/v_codes [B][Hkv][Tcap][S][G] u8; k/v_cb [S][G][C][dsub]
+    f32; k/v_win [B][Hkv][Wcap][D] f16 (or None).  Rows [0, n_code) of the
+    codes and [0, n_window) of the window are attended (default: all rows).
+    Returns f32 [B][Hq][D]."""
     torch = _torch()
     _need_contig(q, k_codes, v_codes, k_cb, v_cb, k_win, v_win)
     B, Hq, D = q.shape
-    _, Hkv, Tc, S, G = k_codes.shape
+    _, Hkv, Tcap, S, G = k_codes.shape
     C = k_cb.shape[2]
-    W = 0 if k_win is None else k_win.shape[2]
-    a = _attn_desc(B, Hq, Hkv, D, Tc, W, S, G, C, scale)
+    Wcap = 0 if k_win is None else k_win.shape[2]
+    Tc = Tcap if n_code is None else int(n_code)
+    W = Wcap if n_window is None else int(n_window)
+    a = _attn_desc(B, Hq, Hkv, D, Tc, W, S, G, C, scale, Tcap, Wcap)
     sz = ctypes.c_size_t(0)
     _check(_lib().kvq_attend_workspace_size(ctypes.byref(a), ctypes.byref(sz)),
            "kvq_attend_workspace_size")
@@ -241,3 +253,51 @@ def attend_decode(q, k_codes, v_codes, k_cb, v_cb, k_win=None, v_win=None, *, sc
                                  _ptr(workspace), workspace.numel(), _stream(q)),
            "kvq_attend_decode")
     return out
+
+
+def window_append(k_new, v_new, k_win, v_win, n_window):
+    """Write one token per (sequence, KV head), k/v_new [B][Hkv][D] f16, into
+    row n_window of the window buffers k/v_win [B][Hkv][Wcap][D] f16."""
+    torch = _torch()
+    _need_contig(k_new, v_new, k_win, v_win)
+    for t in (k_new, v_new, k_win, v_win):
+        if t.dtype != torch.float16:
+            raise TypeError("window tensors must be float16")
+    B, Hkv, Wcap, D = k_win.shape
+    _check(_lib().kvq_window_append(B, Hkv, D, Wcap, int(n_window), _ptr(k_new), _ptr(v_new),
+                                    _ptr(k_win), _ptr(v_win), _stream(k_win)),
+           "kvq_window_append")
+
+
+def window_flush_workspace_size(head_dim, n_groups, n_stages, n_codewords) -> int:
+    vq = VqDesc(head_dim, n_groups, n_stages, n_codewords)
+    sz = ctypes.c_size_t(0)
+    _check(_lib().kvq_window_flush_workspace_size(ctypes.byref(vq), ctypes.byref(sz)),
+           "kvq_window_flush_workspace_size")
+    return sz.value
+
+
+def window_flush(k_win, v_win, n_window, n_flush, k_codes, v_codes, n_code, k_cb, v_cb, *,
+                 workspace=None):
+    """Encode window rows [0, n_flush) into code rows [n_code, n_code + n_flush)
+    (K with k_cb, V with v_cb), then move window rows [n_flush, n_window) to
+    the front.  k/v_win [B][Hkv][Wcap][D] f16; k/v_codes [B][Hkv][Tcap][S][G] u8;
+    k/v_cb [S][G][C][dsub] f32."""
+    torch = _torch()
+    _need_contig(k_win, v_win, k_codes, v_codes, k_cb, v_cb)
+    for t in (k_win, v_win):
+        if t.dtype != torch.float16:
+            raise TypeError("window tensors must be float16")
+    B, Hkv, Wcap, D = k_win.shape
+    _, _, Tcap, S, G = k_codes.shape
+    C = k_cb.shape[2]
+    vq = VqDesc(D, G, S, C)
+    need = window_flush_workspace_size(D, G, S, C)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=k_win.device)
+    ws_bytes = workspace.numel() if workspace is not None else 0
+    _check(_lib().kvq_window_flush(ctypes.byref(vq), B, Hkv, Wcap, int(n_window), int(n_flush),
+                                   _ptr(k_win), _ptr(v_win), Tcap, int(n_code), _ptr(k_codes),
+                                   _ptr(v_codes), _ptr(k_cb), _ptr(v_cb), _ptr(workspace),
+                                   ws_bytes, _stream(k_win)),
+           "kvq_window_flush")

@@ -265,8 +265,8 @@ __device__ __forceinline__ void window_partial(const float* __restrict__ q,
                                                const uint16_t* __restrict__ vw,
                                                float* __restrict__ part, uint8_t* smem, int b,
                                                int kv, int h0, int nh, int Hq, int Hkv, int W,
-                                               int w0, int w1, int slot, int nslots, int pstride,
-                                               float scale) {
+                                               int wstride, int w0, int w1, int slot, int nslots,
+                                               int pstride, float scale) {
   constexpr int L = D / 8;
   constexpr int ROWS = 512 / L;
   float* ssc = reinterpret_cast<float*>(smem);                  // [ATTN_WIN_BLOCK][RP]
@@ -275,8 +275,8 @@ __device__ __forceinline__ void window_partial(const float* __restrict__ q,
   __shared__ float wm[RP];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int row = tid / L, col = tid % L;
-  const uint16_t* kwp = kw + ((int64_t)b * Hkv + kv) * W * D + col * 8;
-  const uint16_t* vwp = vw + ((int64_t)b * Hkv + kv) * W * D + col * 8;
+  const uint16_t* kwp = kw + ((int64_t)b * Hkv + kv) * wstride * D + col * 8;
+  const uint16_t* vwp = vw + ((int64_t)b * Hkv + kv) * wstride * D + col * 8;
   float qv[RP][8];
 #pragma unroll
   for (int r = 0; r < RP; ++r) {
@@ -402,14 +402,14 @@ __device__ __forceinline__ bool win_slice_load(uint4& kraw, uint4& vraw, float (
                                                const float* __restrict__ q,
                                                const uint16_t* __restrict__ kw,
                                                const uint16_t* __restrict__ vw, int b, int kv,
-                                               int h0, int nh, int Hq, int Hkv, int W, int wa,
-                                               int wb, int tid) {
+                                               int h0, int nh, int Hq, int Hkv, int wstride,
+                                               int wa, int wb, int tid) {
   constexpr int L = D / 8;
   const int row = tid / L, col = tid % L;
   const int t = wa + row;
   const bool act = t < wb;
   const int tl = act ? t : (wb > 0 ? wb - 1 : 0);
-  const int64_t off = (((int64_t)b * Hkv + kv) * W + tl) * D + col * 8;
+  const int64_t off = (((int64_t)b * Hkv + kv) * wstride + tl) * D + col * 8;
   kraw = make_uint4(0u, 0u, 0u, 0u);
   vraw = kraw;
   if (wb > wa) {
@@ -460,7 +460,7 @@ __global__ __launch_bounds__(CH_THREADS, 1) void attn_chunk_kernel(
     int pstride, int fbits, int cparts, size_t lut_slice, const float* __restrict__ kcb,
     int fuse_lut, const float* __restrict__ q,
     const uint16_t* __restrict__ kw, const uint16_t* __restrict__ vw, int W, int wslice,
-    int nslots, float scale) {
+    int nslots, float scale, int cstride, int wstride) {
   constexpr int L = D / 8;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int ci = blockIdx.x;
@@ -473,8 +473,8 @@ __global__ __launch_bounds__(CH_THREADS, 1) void attn_chunk_kernel(
   if (ci >= n_chunks) {                                 // window block (uniform per block)
     const int w0 = (ci - n_chunks) * ATTN_WIN_BLOCK;
     const int w1 = (w0 + ATTN_WIN_BLOCK) < W ? (w0 + ATTN_WIN_BLOCK) : W;
-    window_partial<RP, D>(q, kw, vw, part, smem, b, kv, h0, nh, Hq, Hkv, W, w0, w1, ci, nslots,
-                          pstride, scale);
+    window_partial<RP, D>(q, kw, vw, part, smem, b, kv, h0, nh, Hq, Hkv, W, wstride, w0, w1, ci,
+                          nslots, pstride, scale);
     return;
   }
   const int SG = SGC ? SGC : S * G;
@@ -492,7 +492,7 @@ __global__ __launch_bounds__(CH_THREADS, 1) void attn_chunk_kernel(
   const int t0 = ci * chunk;
   const int t1 = (t0 + chunk) < Tc ? (t0 + chunk) : Tc;
 
-  const int64_t rowbase = ((int64_t)b * Hkv + kv) * (int64_t)Tc;
+  const int64_t rowbase = ((int64_t)b * Hkv + kv) * (int64_t)cstride;
   // first KP token rows of K codes (and later of V codes) staged in registers
   // (32 VGPRs) so their HBM latency overlaps the LUT staging (the max
   // reduction for V)
@@ -613,8 +613,8 @@ __global__ __launch_bounds__(CH_THREADS, 1) void attn_chunk_kernel(
   if (wslice > 0) {
     const int wa = ci * wslice < W ? ci * wslice : W;
     const int wb = (wa + wslice) < W ? (wa + wslice) : W;
-    wact = win_slice_load<RP, D>(wkraw, wvraw, wq, q, kw, vw, b, kv, h0, nh, Hq, Hkv, W, wa, wb,
-                                 tid);
+    wact = win_slice_load<RP, D>(wkraw, wvraw, wq, q, kw, vw, b, kv, h0, nh, Hq, Hkv, wstride, wa,
+                                 wb, tid);
   }
   __syncthreads();
 
@@ -917,8 +917,8 @@ template <int RP>
 static hipError_t launch_rp(const AttnPlan& p, int SG, const float* q, const float* kcb,
                             const uint8_t* kc, const uint8_t* vc, const float* vcb, float* lut,
                             float* part, const uint16_t* kw, const uint16_t* vw, int B, int Hq,
-                            int Hkv, int D, int S, int G, int C, int Tc, int W, float scale,
-                            hipStream_t st) {
+                            int Hkv, int D, int S, int G, int C, int Tc, int W, int cstride,
+                            int wstride, float scale, hipStream_t st) {
   hipError_t e = hipSuccess;
   size_t lds = 0;
   if (p.n_chunks > 0 && !p.fuse_lut) {
@@ -955,8 +955,7 @@ static hipError_t launch_rp(const AttnPlan& p, int SG, const float* q, const flo
     kern<<<grid, CH_THREADS, lds, st>>>(kc, vc, vcb, lut, part, Hq, Hkv, S, G, C, Tc,          \
                                         p.n_chunks, p.chunk, p.n_hsplit, p.pstride, p.fbits,   \
                                         p.cparts, p.lut_slice, kcb, p.fuse_lut, q, kw, vw, W,  \
-                                        p.wslice, nslots,                                      \
-                                        scale);                                                \
+                                        p.wslice, nslots, scale, cstride, wstride);            \
     return hipGetLastError();                                                                  \
   }
   if (D == 64) KVQ_CH(0, 64)
@@ -969,7 +968,8 @@ static hipError_t launch_rp(const AttnPlan& p, int SG, const float* q, const flo
 }
 
 hipError_t launch_attend(const AttnPlan& p, int B, int Hq, int Hkv, int D, int S, int G, int C,
-                         int Tc, int W, float scale, const float* q, const uint8_t* kc,
+                         int Tc, int W, int cstride, int wstride, float scale, const float* q,
+                         const uint8_t* kc,
                          const uint8_t* vc, const float* kcb, const float* vcb,
                          const uint16_t* kw, const uint16_t* vw, float* out, void* ws,
                          hipStream_t st) {
@@ -978,9 +978,9 @@ hipError_t launch_attend(const AttnPlan& p, int B, int Hq, int Hkv, int D, int S
                                          ((p.lut_bytes + 255) & ~(size_t)255));
   const int SG = S * G;
   hipError_t e;
-  if (p.rp == 4) e = launch_rp<4>(p, SG, q, kcb, kc, vc, vcb, lut, part, kw, vw, B, Hq, Hkv, D, S, G, C, Tc, W, scale, st);
-  else if (p.rp == 2) e = launch_rp<2>(p, SG, q, kcb, kc, vc, vcb, lut, part, kw, vw, B, Hq, Hkv, D, S, G, C, Tc, W, scale, st);
-  else e = launch_rp<1>(p, SG, q, kcb, kc, vc, vcb, lut, part, kw, vw, B, Hq, Hkv, D, S, G, C, Tc, W, scale, st);
+  if (p.rp == 4) e = launch_rp<4>(p, SG, q, kcb, kc, vc, vcb, lut, part, kw, vw, B, Hq, Hkv, D, S, G, C, Tc, W, cstride, wstride, scale, st);
+  else if (p.rp == 2) e = launch_rp<2>(p, SG, q, kcb, kc, vc, vcb, lut, part, kw, vw, B, Hq, Hkv, D, S, G, C, Tc, W, cstride, wstride, scale, st);
+  else e = launch_rp<1>(p, SG, q, kcb, kc, vc, vcb, lut, part, kw, vw, B, Hq, Hkv, D, S, G, C, Tc, W, cstride, wstride, scale, st);
   if (e != hipSuccess) return e;
   const int nslots = p.n_chunks + p.n_wblocks;
   if (D == 64) attn_merge_kernel<64><<<dim3(B * Hq), 256, 0, st>>>(part, out, nslots, p.pstride);

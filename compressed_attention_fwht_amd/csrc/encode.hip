@@ -92,6 +92,14 @@ __device__ __forceinline__ int64_t row_elem(int64_t book, int64_t n, int64_t n_r
   return ((book * n_seq + seq) * seq_stride + row) * 128;
 }
 
+// Code row of vector n of a book: rows [code_row0, code_row0 + n_rows) of a
+// sequence whose code rows are code_stride apart.
+__device__ __forceinline__ int64_t code_row(int64_t book, int64_t n, int64_t n_rows, int64_t n_seq,
+                                            int64_t code_stride, int64_t code_row0) {
+  const int64_t seq = n / n_rows, row = n - seq * n_rows;
+  return (book * n_seq + seq) * code_stride + code_row0 + row;
+}
+
 // Copy one group's S packed stage blocks (S * 20480 contiguous bytes) from
 // global memory straight into LDS with global_load_lds_dwordx4: each
 // instruction moves 64 lanes x 16 bytes into 1 KiB of LDS at a wave-uniform
@@ -121,7 +129,8 @@ __device__ __forceinline__ void wait_vmem() {
 template <int S, int XT>
 __global__ __launch_bounds__(64 * mf_waves<S>(), 8 / mf_waves<S>()) void encode_mfma_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ packed, uint8_t* __restrict__ codes,
-    int64_t n_seq, int64_t seq_stride, int64_t n_rows, int64_t tiles_per_book, int pre_rotated) {
+    int64_t n_seq, int64_t seq_stride, int64_t n_rows, int64_t code_stride, int64_t code_row0,
+    int64_t tiles_per_book, int pre_rotated) {
   constexpr int G = 16;
   constexpr int SG = S * G;
   // LDS: two buffers of one group's S stage blocks (double buffering); the
@@ -338,7 +347,8 @@ __global__ __launch_bounds__(64 * mf_waves<S>(), 8 / mf_waves<S>()) void encode_
   }
 
   if (live) {
-    uint4* dst = reinterpret_cast<uint4*>(codes + (book * n_per_book + v_own) * SG);
+    uint4* dst = reinterpret_cast<uint4*>(
+        codes + code_row(book, v_own, n_rows, n_seq, code_stride, code_row0) * SG);
 #pragma unroll
     for (int i = 0; i < SG / 16; ++i)
       dst[i] = make_uint4(cw[4 * i], cw[4 * i + 1], cw[4 * i + 2], cw[4 * i + 3]);
@@ -351,8 +361,8 @@ constexpr int GEN_TILE = 64;       // vectors per block
 template <int D, int DSUB>
 __global__ __launch_bounds__(256) void encode_generic_kernel(
     const void* __restrict__ x, int xt, const float* __restrict__ cb, uint8_t* __restrict__ codes,
-    int64_t n_seq, int64_t seq_stride, int64_t n_rows, int64_t tiles_per_book, int S, int C,
-    int pre_rotated) {
+    int64_t n_seq, int64_t seq_stride, int64_t n_rows, int64_t code_stride, int64_t code_row0,
+    int64_t tiles_per_book, int S, int C, int pre_rotated) {
   constexpr int G = D / DSUB;
   constexpr int L = D / 8;
   constexpr int ROWS_PER_WAVE = 64 / L;
@@ -420,10 +430,12 @@ __global__ __launch_bounds__(256) void encode_generic_kernel(
   }
   __syncthreads();
 
-  // ---- write the tile's code rows (contiguous)
+  // ---- write the tile's code rows
   const int64_t nv = (n_per_book - v0) < GEN_TILE ? (n_per_book - v0) : GEN_TILE;
-  uint8_t* dst = codes + (book * n_per_book + v0) * SG;
-  for (int i = threadIdx.x; i < nv * SG; i += 256) dst[i] = cs[i];
+  for (int i = threadIdx.x; i < nv * SG; i += 256) {
+    const int vl = i / SG;
+    codes[code_row(book, v0 + vl, n_rows, n_seq, code_stride, code_row0) * SG + (i - vl * SG)] = cs[i];
+  }
 }
 
 // ================================================================ launchers
@@ -439,7 +451,8 @@ bool encode_mfma_eligible(int D, int G, int S, int C, int xt) {
 template <int S, int XT>
 static hipError_t launch_mfma_t(const void* x, const uint8_t* packed, uint8_t* codes,
                                 int64_t n_books, int64_t n_seq, int64_t seq_stride, int64_t n_rows,
-                                int pre_rotated, hipStream_t st) {
+                                int64_t code_stride, int64_t code_row0, int pre_rotated,
+                                hipStream_t st) {
   const int64_t n_per_book = n_seq * n_rows;
   constexpr int TILE = 64 * mf_waves<S>();
   const int64_t tiles = (n_per_book + TILE - 1) / TILE;
@@ -450,15 +463,16 @@ static hipError_t launch_mfma_t(const void* x, const uint8_t* packed, uint8_t* c
                                      (int)lds);
   if (e != hipSuccess) return e;
   kern<<<dim3((unsigned)(tiles * n_books)), dim3(64 * mf_waves<S>()), lds, st>>>(
-      reinterpret_cast<const uint16_t*>(x), packed, codes, n_seq, seq_stride, n_rows, tiles,
-      pre_rotated);
+      reinterpret_cast<const uint16_t*>(x), packed, codes, n_seq, seq_stride, n_rows, code_stride,
+      code_row0, tiles, pre_rotated);
   return hipGetLastError();
 }
 
 template <int D, int DSUB>
 static hipError_t launch_generic_t(const void* x, int xt, const float* cb, uint8_t* codes,
                                    int64_t n_books, int64_t n_seq, int64_t seq_stride,
-                                   int64_t n_rows, int S, int C, int pre_rotated, hipStream_t st) {
+                                   int64_t n_rows, int64_t code_stride, int64_t code_row0, int S,
+                                   int C, int pre_rotated, hipStream_t st) {
   const int64_t n_per_book = n_seq * n_rows;
   const int64_t tiles = (n_per_book + GEN_TILE - 1) / GEN_TILE;
   const int G = D / DSUB;
@@ -468,14 +482,15 @@ static hipError_t launch_generic_t(const void* x, int xt, const float* cb, uint8
                                      (int)lds);
   if (e != hipSuccess) return e;
   kern<<<dim3((unsigned)(tiles * n_books)), dim3(256), lds, st>>>(
-      x, xt, cb, codes, n_seq, seq_stride, n_rows, tiles, S, C, pre_rotated);
+      x, xt, cb, codes, n_seq, seq_stride, n_rows, code_stride, code_row0, tiles, S, C,
+      pre_rotated);
   return hipGetLastError();
 }
 
 hipError_t launch_encode(const void* x, int xt, int D, int G, int S, int C, int64_t n_books,
                          int64_t n_seq, int64_t seq_stride, int64_t n_rows, const float* cb,
-                         uint8_t* codes, int pre_rotated, int force_generic, int packed_in_ws,
-                         void* ws, hipStream_t st) {
+                         uint8_t* codes, int64_t code_stride, int64_t code_row0, int pre_rotated,
+                         int force_generic, int packed_in_ws, void* ws, hipStream_t st) {
   if (n_books == 0 || n_seq == 0 || n_rows == 0) return hipSuccess;
   if (!force_generic && encode_mfma_eligible(D, G, S, C, xt)) {
     uint8_t* packed = reinterpret_cast<uint8_t*>(ws);
@@ -491,9 +506,10 @@ hipError_t launch_encode(const void* x, int xt, int D, int G, int S, int C, int6
 #define KVQ_MF(SS)                                                                          \
   if (S == SS) {                                                                           \
     if (xt == 1) return launch_mfma_t<SS, 1>(x, packed, codes, n_books, n_seq, seq_stride,  \
-                                             n_rows, pre_rotated, st);                      \
+                                             n_rows, code_stride, code_row0, pre_rotated,   \
+                                             st);                                           \
     return launch_mfma_t<SS, 2>(x, packed, codes, n_books, n_seq, seq_stride, n_rows,       \
-                                pre_rotated, st);                                           \
+                                code_stride, code_row0, pre_rotated, st);                   \
   }
     KVQ_MF(1) KVQ_MF(2) KVQ_MF(3) KVQ_MF(4)
 #undef KVQ_MF
@@ -501,8 +517,8 @@ hipError_t launch_encode(const void* x, int xt, int D, int G, int S, int C, int6
   const int dsub = D / G;
 #define KVQ_GEN(DD, DS) \
   if (D == DD && dsub == DS) \
-    return launch_generic_t<DD, DS>(x, xt, cb, codes, n_books, n_seq, seq_stride, n_rows, S, C, \
-                                    pre_rotated, st);
+    return launch_generic_t<DD, DS>(x, xt, cb, codes, n_books, n_seq, seq_stride, n_rows,      \
+                                    code_stride, code_row0, S, C, pre_rotated, st);
   KVQ_GEN(64, 8) KVQ_GEN(64, 16) KVQ_GEN(64, 32) KVQ_GEN(64, 64)
   KVQ_GEN(128, 8) KVQ_GEN(128, 16) KVQ_GEN(128, 32) KVQ_GEN(128, 64) KVQ_GEN(128, 128)
   KVQ_GEN(256, 8) KVQ_GEN(256, 16) KVQ_GEN(256, 32) KVQ_GEN(256, 64) KVQ_GEN(256, 128)

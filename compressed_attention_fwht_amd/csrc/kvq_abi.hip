@@ -40,6 +40,8 @@ kvq_status check_attn(const kvq_attn_desc* a, kvq::AttnPlan* plan) {
   if (a->n_q_heads % a->n_kv_heads != 0) return KVQ_ERR_SHAPE;
   if (a->n_code_tokens < 0 || a->n_window < 0) return KVQ_ERR_SHAPE;
   if ((int64_t)a->n_code_tokens + a->n_window == 0) return KVQ_ERR_SHAPE;
+  if (a->code_stride != 0 && a->code_stride < a->n_code_tokens) return KVQ_ERR_SHAPE;
+  if (a->window_stride != 0 && a->window_stride < a->n_window) return KVQ_ERR_SHAPE;
   if ((int64_t)a->batch * a->n_q_heads > 0x7fffffff) return KVQ_ERR_SHAPE;
   if (a->batch > 65535) return KVQ_ERR_UNSUPPORTED;
   if (!(a->softmax_scale == a->softmax_scale)) return KVQ_ERR_SHAPE;   // NaN
@@ -130,7 +132,8 @@ kvq_status kvq_encode(const void* x, kvq_dtype xt, const kvq_vq_desc* vq, int64_
     if (need > 0 && !aligned16(workspace)) return KVQ_ERR_ALIGN;
   }
   return hip_status(kvq::launch_encode(x, (int)xt, D, G, S, C, n_books, n_seq, seq_stride, n_rows,
-                                       codebooks, codes, (flags & KVQ_INPUT_PRE_ROTATED) ? 1 : 0,
+                                       codebooks, codes, n_rows, 0,
+                                       (flags & KVQ_INPUT_PRE_ROTATED) ? 1 : 0,
                                        generic ? 1 : 0, (flags & KVQ_CODEBOOKS_PACKED) ? 1 : 0,
                                        workspace, stream));
 }
@@ -150,6 +153,72 @@ kvq_status kvq_decode_reconstruct(const uint8_t* codes, const kvq_vq_desc* vq, i
                                             vq->head_dim, vq->n_groups, vq->n_stages,
                                             vq->n_codewords, (flags & KVQ_UNROTATE) ? 1 : 0,
                                             stream));
+}
+
+kvq_status kvq_window_append(int32_t batch, int32_t n_kv_heads, int32_t head_dim,
+                             int32_t window_cap, int32_t n_window, const uint16_t* k_new,
+                             const uint16_t* v_new, uint16_t* k_win, uint16_t* v_win,
+                             hipStream_t stream) {
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256) return KVQ_ERR_SHAPE;
+  if (batch < 1 || n_kv_heads < 1 || window_cap < 1) return KVQ_ERR_SHAPE;
+  if (n_window < 0 || n_window >= window_cap) return KVQ_ERR_SHAPE;
+  if ((int64_t)batch * n_kv_heads > 0x7fffffff) return KVQ_ERR_SHAPE;
+  if (!k_new || !v_new || !k_win || !v_win) return KVQ_ERR_NULL;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_win) || !aligned16(v_win))
+    return KVQ_ERR_ALIGN;
+  return hip_status(kvq::launch_window_append(k_new, v_new, k_win, v_win,
+                                              (int64_t)batch * n_kv_heads, head_dim, window_cap,
+                                              n_window, stream));
+}
+
+kvq_status kvq_window_flush_workspace_size(const kvq_vq_desc* vq, size_t* bytes) {
+  kvq_status st = check_vq(vq);
+  if (st != KVQ_OK) return st;
+  if (!bytes) return KVQ_ERR_NULL;
+  const size_t one = kvq::encode_workspace_bytes(vq->head_dim, vq->n_groups, vq->n_stages,
+                                                 vq->n_codewords, 1);
+  *bytes = 2 * ((one + 255) & ~(size_t)255);            // K books, then V books
+  return KVQ_OK;
+}
+
+kvq_status kvq_window_flush(const kvq_vq_desc* vq, int32_t batch, int32_t n_kv_heads,
+                            int32_t window_cap, int32_t n_window, int32_t n_flush,
+                            uint16_t* k_win, uint16_t* v_win, int32_t code_cap, int32_t n_code,
+                            uint8_t* k_codes, uint8_t* v_codes, const float* k_cb,
+                            const float* v_cb, void* workspace, size_t ws_bytes,
+                            hipStream_t stream) {
+  kvq_status st = check_vq(vq);
+  if (st != KVQ_OK) return st;
+  if (batch < 1 || n_kv_heads < 1 || window_cap < 1 || code_cap < 0) return KVQ_ERR_SHAPE;
+  if (n_window < 0 || n_window > window_cap) return KVQ_ERR_SHAPE;
+  if (n_flush < 0 || n_flush > n_window) return KVQ_ERR_SHAPE;
+  if (n_code < 0 || (int64_t)n_code + n_flush > code_cap) return KVQ_ERR_SHAPE;
+  if ((int64_t)batch * n_kv_heads > 0x7fffffff) return KVQ_ERR_SHAPE;
+  if (n_flush == 0) return KVQ_OK;
+  if (!k_win || !v_win || !k_codes || !v_codes || !k_cb || !v_cb) return KVQ_ERR_NULL;
+  if (!aligned16(k_win) || !aligned16(v_win) || !aligned16(k_codes) || !aligned16(v_codes) ||
+      !aligned16(k_cb) || !aligned16(v_cb))
+    return KVQ_ERR_ALIGN;
+  const int D = vq->head_dim, G = vq->n_groups, S = vq->n_stages, C = vq->n_codewords;
+  const int64_t units = (int64_t)batch * n_kv_heads;
+  if (((int64_t)n_flush * units + 63) / 64 > 0x7fffffffLL) return KVQ_ERR_UNSUPPORTED;
+  size_t need = 0;
+  kvq_window_flush_workspace_size(vq, &need);
+  const size_t half = need / 2;
+  const bool mfma = kvq::encode_mfma_eligible(D, G, S, C, (int)KVQ_F16);
+  if (mfma) {
+    if (!workspace || ws_bytes < need) return KVQ_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return KVQ_ERR_ALIGN;
+  }
+  uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
+  hipError_t e = kvq::launch_encode(k_win, (int)KVQ_F16, D, G, S, C, 1, units, window_cap, n_flush,
+                                    k_cb, k_codes, code_cap, n_code, 0, 0, 0, ws, stream);
+  if (e == hipSuccess)
+    e = kvq::launch_encode(v_win, (int)KVQ_F16, D, G, S, C, 1, units, window_cap, n_flush, v_cb,
+                           v_codes, code_cap, n_code, 0, 0, 0, mfma ? ws + half : nullptr, stream);
+  if (e == hipSuccess)
+    e = kvq::launch_window_compact(k_win, v_win, units, D, window_cap, n_window, n_flush, stream);
+  return hip_status(e);
 }
 
 kvq_status kvq_attend_workspace_size(const kvq_attn_desc* a, size_t* bytes) {
@@ -185,7 +254,10 @@ kvq_status kvq_attend_decode(const kvq_attn_desc* a, const float* q, const uint8
                                               : (float)(1.0 / sqrt((double)v.head_dim));
   return hip_status(kvq::launch_attend(plan, a->batch, a->n_q_heads, a->n_kv_heads, v.head_dim,
                                        v.n_stages, v.n_groups, v.n_codewords, a->n_code_tokens,
-                                       a->n_window, scale, q, k_codes, v_codes, k_cb, v_cb, k_win,
+                                       a->n_window,
+                                       a->code_stride ? a->code_stride : a->n_code_tokens,
+                                       a->window_stride ? a->window_stride : a->n_window,
+                                       scale, q, k_codes, v_codes, k_cb, v_cb, k_win,
                                        v_win, out, workspace, stream));
 }
 

@@ -37,17 +37,24 @@ size_t encode_workspace_bytes(int D, int G, int S, int C, int64_t n_books);
 bool encode_mfma_eligible(int D, int G, int S, int C, int xt);
 hipError_t launch_encode(const void* x, int xt, int D, int G, int S, int C, int64_t n_books,
                          int64_t n_seq, int64_t seq_stride, int64_t n_rows, const float* cb,
-                         uint8_t* codes, int pre_rotated, int force_generic, int packed,
-                         void* ws, hipStream_t st);
+                         uint8_t* codes, int64_t code_stride, int64_t code_row0, int pre_rotated,
+                         int force_generic, int packed, void* ws, hipStream_t st);
 
 hipError_t launch_reconstruct(const uint8_t* codes, const float* cb, float* out, int64_t n_books,
                               int64_t n_per_book, int D, int G, int S, int C, int unrotate,
                               hipStream_t s);
 
 hipError_t launch_attend(const AttnPlan& p, int B, int Hq, int Hkv, int D, int S, int G, int C,
-                         int Tc, int W, float scale, const float* q, const uint8_t* kc,
+                         int Tc, int W, int cstride, int wstride, float scale, const float* q,
+                         const uint8_t* kc,
                          const uint8_t* vc, const float* kcb, const float* vcb,
                          const uint16_t* kw, const uint16_t* vw, float* out, void* ws,
                          hipStream_t st);
+
+hipError_t launch_window_append(const uint16_t* kn, const uint16_t* vn, uint16_t* kw,
+                                uint16_t* vw, int64_t units, int D, int wcap, int row,
+                                hipStream_t st);
+hipError_t launch_window_compact(uint16_t* kw, uint16_t* vw, int64_t units, int D, int wcap, int n,
+                                 int shift, hipStream_t st);
 
 }  // namespace kvq

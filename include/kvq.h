@@ -87,7 +87,9 @@ typedef struct {
  * Query head h reads KV head h / (n_q_heads / n_kv_heads).  The cache of a
  * (sequence, KV head) holds n_code_tokens coded tokens followed by n_window
  * fp16 tokens on one position axis; either count may be 0, not both.
- * softmax_scale <= 0 selects 1/sqrt(head_dim). */
+ * softmax_scale <= 0 selects 1/sqrt(head_dim).  code_stride / window_stride:
+ * token rows allocated per (sequence, KV head) in the code / window buffers
+ * (a cache grown in place by kvq_window_flush); 0 means dense (= the count). */
 typedef struct {
   int32_t batch;
   int32_t n_q_heads;
@@ -96,6 +98,8 @@ typedef struct {
   int32_t n_window;
   kvq_vq_desc vq;          /* vq.head_dim is the attention head_dim */
   float softmax_scale;
+  int32_t code_stride;     /* 0 or >= n_code_tokens */
+  int32_t window_stride;   /* 0 or >= n_window */
 } kvq_attn_desc;
 
 /* Flags */
@@ -153,9 +157,11 @@ KVQ_API kvq_status kvq_attend_workspace_size(const kvq_attn_desc* a, size_t* byt
 
 /* Single-token decode attention.
  * q:       [B][Hq][D] float32, original domain;
- * k_codes, v_codes: [B][Hkv][Tc][S][G] uint8 (Tc = n_code_tokens);
+ * k_codes, v_codes: [B][Hkv][code_stride][S][G] uint8, rows [0, Tc) read
+ *          (Tc = n_code_tokens);
  * k_cb, v_cb: [S][G][C][dsub] float32 (one codebook set for K, one for V);
- * k_win, v_win: [B][Hkv][W][D] IEEE fp16 bit patterns (W = n_window; may be
+ * k_win, v_win: [B][Hkv][window_stride][D] IEEE fp16 bit patterns, rows
+ *          [0, W) read (W = n_window; may be
  *          NULL when W == 0);
  * out:     [B][Hq][D] float32 = softmax(scale * K q) V over the Tc coded
  *          tokens (K, V = H_D reconstruction) followed by the W window tokens;
@@ -167,6 +173,44 @@ KVQ_API kvq_status kvq_attend_decode(const kvq_attn_desc* a, const float* q,
                              const uint16_t* k_win, const uint16_t* v_win,
                              float* out, void* workspace, size_t ws_bytes,
                              hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Streaming window ("VeloxQuant-MLX 0.5.1", Quick start: a cache grown one
+ * token at a time by append; "ZeroKV-Neo 4.0.0", profiling output: periodic
+ * flush_quantize; "VQKV" summary, 3. Inference Integration: a local window of
+ * recent tokens kept uncompressed, older ones compressed).  The caller keeps
+ * the counts (n_window, n_code); buffers have fixed capacities:
+ *   k_win, v_win:     [B][Hkv][window_cap][D] fp16 bit patterns;
+ *   k_codes, v_codes: [B][Hkv][code_cap][S][G] uint8.
+ * kvq_attend_decode reads such a cache with code_stride = code_cap and
+ * window_stride = window_cap.
+ * ------------------------------------------------------------------------ */
+
+/* Writes k_new / v_new ([B][Hkv][D] fp16) into row n_window of every
+ * (sequence, KV head) window.  Requires 0 <= n_window < window_cap and
+ * head_dim in {64, 128, 256}. */
+KVQ_API kvq_status kvq_window_append(int32_t batch, int32_t n_kv_heads, int32_t head_dim,
+                             int32_t window_cap, int32_t n_window,
+                             const uint16_t* k_new, const uint16_t* v_new,
+                             uint16_t* k_win, uint16_t* v_win, hipStream_t stream);
+
+/* Workspace bytes kvq_window_flush needs (packed K and V codebooks; may be 0). */
+KVQ_API kvq_status kvq_window_flush_workspace_size(const kvq_vq_desc* vq, size_t* bytes);
+
+/* Flush: the oldest n_flush window tokens of every (sequence, KV head),
+ * rows [0, n_flush), are encoded exactly as kvq_encode would (rotation, then
+ * the greedy residual stages; K with k_cb, V with v_cb, each [S][G][C][dsub]
+ * float32) and their codes written to rows [n_code, n_code + n_flush); the
+ * remaining window rows [n_flush, n_window) then move to rows
+ * [0, n_window - n_flush).  Requires 0 <= n_flush <= n_window <= window_cap
+ * and n_code + n_flush <= code_cap; n_flush == 0 is a no-op.  The caller's
+ * counts become n_window - n_flush and n_code + n_flush. */
+KVQ_API kvq_status kvq_window_flush(const kvq_vq_desc* vq, int32_t batch, int32_t n_kv_heads,
+                            int32_t window_cap, int32_t n_window, int32_t n_flush,
+                            uint16_t* k_win, uint16_t* v_win, int32_t code_cap,
+                            int32_t n_code, uint8_t* k_codes, uint8_t* v_codes,
+                            const float* k_cb, const float* v_cb, void* workspace,
+                            size_t ws_bytes, hipStream_t stream);
 
 /* Static description of a status code. */
 KVQ_API const char* kvq_status_string(kvq_status status);

@@ -27,6 +27,10 @@ Sources (page title -- section):
   [DKV]  "Differential-KV" README -- Decode & Prefill Innovations: scoring the
          query in the compressed domain without materialising K; merging with
          the dense recency window by an fp32 log-sum-exp combine.
+  Streaming window: [VI] Quick start (a cache grown one token at a time by
+         append, read by attend); [ZK] profiling output (periodic
+         flush_quantize calls); [VQKV] 3. Inference Integration (recent tokens
+         uncompressed in a local window, older ones compressed).
 
 Parity status of each function is stated in its docstring; every function is
 pinned by ``tests/test_oracle_pins.py`` against closed forms, library routines
@@ -37,8 +41,8 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = ["hadamard_matrix", "fwht", "nearest", "rvq_encode", "reconstruct_rot",
-           "reconstruct", "attend", "attend_dense", "lse_merge",
-           "code_bytes_per_vector", "compression_ratio_vs_fp16"]
+           "reconstruct", "attend", "attend_dense", "lse_merge", "window_append",
+           "window_flush", "code_bytes_per_vector", "compression_ratio_vs_fp16"]
 
 
 # ----------------------------------------------------------------------------
@@ -197,6 +201,47 @@ def attend(q, k_codes, v_codes, k_cb, v_cb, k_win=None, v_win=None, scale=None):
         v = np.concatenate(parts_v, axis=1)
         out[b] = attend_dense(q[b], k, v, scale)
     return out
+
+
+# ----------------------------------------------------------------------------
+# Streaming window  [VI Quick start append/attend], [ZK flush_quantize],
+#                   [VQKV 3. local window]
+# ----------------------------------------------------------------------------
+def window_append(k_win, v_win, n_window, k_new, v_new):
+    """Returns copies of the window buffers [B][Hkv][Wcap][D] fp16 with the
+    tokens k_new, v_new [B][Hkv][D] written at row n_window (n_window < Wcap).
+    """
+    k_win = np.array(k_win, copy=True)
+    v_win = np.array(v_win, copy=True)
+    if not 0 <= n_window < k_win.shape[2]:
+        raise ValueError("window is full")
+    k_win[:, :, n_window] = k_new
+    v_win[:, :, n_window] = v_new
+    return k_win, v_win
+
+
+def window_flush(k_win, v_win, n_window, n_flush, k_codes, v_codes, n_code, k_cb, v_cb):
+    """The oldest n_flush window tokens (rows [0, n_flush) of every
+    (sequence, KV head)) become codes at rows [n_code, n_code + n_flush) --
+    rvq_encode of the fp16 values, K with k_cb, V with v_cb -- and the rows
+    [n_flush, n_window) that stay uncompressed move to the front.  Buffers:
+    windows [B][Hkv][Wcap][D] fp16, codes [B][Hkv][Tcap][S][G] uint8.
+    Returns new (k_win, v_win, k_codes, v_codes); rows past the new counts
+    keep what they held."""
+    if not 0 <= n_flush <= n_window <= k_win.shape[2]:
+        raise ValueError("bad window counts")
+    if n_code + n_flush > k_codes.shape[2]:
+        raise ValueError("code buffer too small")
+    k_win, v_win = np.array(k_win, copy=True), np.array(v_win, copy=True)
+    k_codes, v_codes = np.array(k_codes, copy=True), np.array(v_codes, copy=True)
+    B, H, _, D = k_win.shape
+    S, G = k_codes.shape[3], k_codes.shape[4]
+    for win, codes, cb in ((k_win, k_codes, k_cb), (v_win, v_codes, v_cb)):
+        x = win[:, :, :n_flush].astype(np.float64).reshape(-1, D)
+        codes[:, :, n_code:n_code + n_flush] = rvq_encode(x, cb).reshape(B, H, n_flush, S, G)
+        keep = win[:, :, n_flush:n_window].copy()
+        win[:, :, :n_window - n_flush] = keep
+    return k_win, v_win, k_codes, v_codes
 
 
 def lse_merge(parts):

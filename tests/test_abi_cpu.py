@@ -153,3 +153,34 @@ def test_attend_workspace_sizes():
     assert big > lut and (big - lut) % (32 * 132 * 4) == 0               # re-reads would be big
     sz_w = kvq.attend_workspace_size(2, 4, 2, 64, 0, 50, 2, 1, 256)   # window only
     assert sz_w == 2 * 4 * 1 * 68 * 4                                  # no LUT, one window block
+
+
+def test_window_append_argument_errors():
+    L = kvq.lib
+    assert L.kvq_window_append(1, 2, 100, 8, 0, FAKE, FAKE, FAKE, FAKE, None) == SHAPE   # head_dim
+    assert L.kvq_window_append(1, 2, 128, 8, 8, FAKE, FAKE, FAKE, FAKE, None) == SHAPE   # full
+    assert L.kvq_window_append(1, 2, 128, 8, -1, FAKE, FAKE, FAKE, FAKE, None) == SHAPE
+    assert L.kvq_window_append(0, 2, 128, 8, 0, FAKE, FAKE, FAKE, FAKE, None) == SHAPE
+    assert L.kvq_window_append(1, 2, 128, 8, 0, 0, FAKE, FAKE, FAKE, None) == NULL
+    assert L.kvq_window_append(1, 2, 128, 8, 0, FAKE, FAKE, FAKE + 8, FAKE, None) == ALIGN
+
+
+def _flush(vq=None, B=1, H=2, wcap=32, nw=32, nf=16, ccap=100, nc=0, kw=FAKE, ws=FAKE,
+           wsb=1 << 30):
+    vq = _vq() if vq is None else vq
+    return kvq.lib.kvq_window_flush(ctypes.byref(vq), B, H, wcap, nw, nf, kw, FAKE, ccap, nc, FAKE,
+                                    FAKE, FAKE, FAKE, ws, wsb, None)
+
+
+def test_window_flush_argument_errors():
+    assert _flush(nf=33) == SHAPE                       # more than the window holds
+    assert _flush(nw=33) == SHAPE                       # more than its capacity
+    assert _flush(nc=90) == SHAPE                       # codes past their capacity
+    assert _flush(vq=_vq(D=96, G=12)) == SHAPE
+    assert _flush(B=0) == SHAPE
+    assert _flush(kw=0) == NULL
+    assert _flush(kw=FAKE + 2) == ALIGN
+    assert _flush(ws=0, wsb=0) == WS                    # MFMA path needs packed books
+    assert _flush(nf=0, kw=0, ws=0, wsb=0) == OK        # nothing to flush: no-op
+    assert kvq.window_flush_workspace_size(128, 16, 2, 256) == 2 * 16 * 2 * 20480
+    assert kvq.window_flush_workspace_size(64, 1, 2, 256) == 0   # generic kernel

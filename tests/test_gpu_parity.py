@@ -311,6 +311,66 @@ def test_decode_reused_workspace_and_smaller_call():
     assert res["ok"], res
 
 
+@pytest.mark.parametrize("key,over,wcap,nflush", [
+    (3, dict(batch=2, tokens=300, window=0), 96, 64),     # MFMA encode, S = 2, GQA 7
+    (1, dict(tokens=150, window=0), 40, 24),              # generic encode, D = 64
+])
+def test_streaming_window_parity(key, over, wcap, nflush):
+    """Tokens appended one at a time, the oldest nflush flushed into codes
+    whenever the window is full: window buffers bit-exact with the oracle's
+    stream, codes within the near-tie rule, then decode over the grown cache
+    (capacity strides) against the oracle on the same codes."""
+    say(f"streaming window workload {key} {over} cap {wcap} flush {nflush}")
+    w = synth.workload(key, **over)
+    inp = synth.make_inputs(w)
+    B, H, T, D = w.batch, w.n_kv_heads, w.tokens, w.head_dim
+    S, G = w.n_stages, w.n_groups
+    tk = inp["x_f32"][0].reshape(B, H, T, D).astype(np.float16)
+    tv = inp["x_f32"][1].reshape(B, H, T, D).astype(np.float16)
+    kcb, vcb = inp["cb"][0], inp["cb"][1]
+    ccap = T
+    kw = torch.zeros((B, H, wcap, D), dtype=torch.float16, device="cuda")
+    vw = torch.zeros_like(kw)
+    kc = torch.zeros((B, H, ccap, S, G), dtype=torch.uint8, device="cuda")
+    vc = torch.zeros_like(kc)
+    kcb_d, vcb_d = cuda(kcb), cuda(vcb)
+    tk_d, tv_d = cuda(tk), cuda(tv)
+    okw = np.zeros((B, H, wcap, D), np.float16); ovw = np.zeros_like(okw)
+    nw = nc = 0
+    flushed = []
+    for t in range(T):
+        if nw == wcap:
+            kvq.window_flush(kw, vw, nw, nflush, kc, vc, nc, kcb_d, vcb_d)
+            okw[:, :, :nw - nflush] = okw[:, :, nflush:nw].copy()
+            ovw[:, :, :nw - nflush] = ovw[:, :, nflush:nw].copy()
+            flushed.append((nc, nflush))
+            nw, nc = nw - nflush, nc + nflush
+        kvq.window_append(tk_d[:, :, t].contiguous(), tv_d[:, :, t].contiguous(), kw, vw, nw)
+        okw[:, :, nw] = tk[:, :, t]
+        ovw[:, :, nw] = tv[:, :, t]
+        nw += 1
+    torch.cuda.synchronize()
+    assert nc > 0 and len(flushed) >= 2
+    assert np.array_equal(kw.cpu().numpy()[:, :, :nw], tk[:, :, nc:])
+    assert np.array_equal(vw.cpu().numpy()[:, :, :nw], tv[:, :, nc:])
+    assert np.array_equal(kw.cpu().numpy(), okw) and np.array_equal(vw.cpu().numpy(), ovw)
+    kcn, vcn = kc.cpu().numpy(), vc.cpu().numpy()
+    assert not kcn[:, :, nc:].any()                      # rows past the count untouched
+    for codes, toks, cb in ((kcn, tk, kcb), (vcn, tv, vcb)):
+        res = oracle.check_codes(toks[:, :, :nc].astype(np.float64).reshape(-1, D), cb,
+                                 codes[:, :, :nc].reshape(-1, S, G))
+        say("   codes", {k: res[k] for k in ("total", "exact", "near_tie", "hard")})
+        assert res["hard"] == 0
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((B, w.n_q_heads, D)).astype(np.float32)
+    got = kvq.attend_decode(cuda(q), kc, vc, kcb_d, vcb_d, kw, vw, n_code=nc,
+                            n_window=nw).cpu().numpy()
+    ref = oracle.attend(q, kcn[:, :, :nc], vcn[:, :, :nc], kcb, vcb, tk[:, :, nc:], tv[:, :, nc:])
+    res = oracle.check_attn(got, ref)
+    say("   decode", res)
+    assert res["ok"], res
+
+
 def test_decode_codes_only_short():
     say("decode codes only, short cache")
     w = synth.workload(4, tokens=37, window=0)

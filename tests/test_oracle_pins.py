@@ -367,3 +367,67 @@ def test_pins_catch_planted_slips():
     bad = np.stack([attend_dense(q[h:h + 1], k[h % 2:h % 2 + 1], v[h % 2:h % 2 + 1], 0.25)[0]
                     for h in range(8)])
     assert np.max(np.abs(good - bad)) > 1e-3
+
+
+# ------------------------------------------------------------ streaming window
+def _stream(oracle_mod, tokens_k, tokens_v, wcap, n_flush, k_cb, v_cb, code_cap):
+    """Append tokens one at a time; flush the oldest n_flush when the window is
+    full before an append (the cache protocol of the streaming calls)."""
+    B, H, T, D = tokens_k.shape
+    S, G = k_cb.shape[0], k_cb.shape[1]
+    kw = np.zeros((B, H, wcap, D), np.float16); vw = np.zeros_like(kw)
+    kc = np.zeros((B, H, code_cap, S, G), np.uint8); vc = np.zeros_like(kc)
+    nw = nc = 0
+    for t in range(T):
+        if nw == wcap:
+            kw, vw, kc, vc = oracle_mod.window_flush(kw, vw, nw, n_flush, kc, vc, nc, k_cb, v_cb)
+            nw, nc = nw - n_flush, nc + n_flush
+        kw, vw = oracle_mod.window_append(kw, vw, nw, tokens_k[:, :, t], tokens_v[:, :, t])
+        nw += 1
+    return kw, vw, kc, vc, nw, nc
+
+
+def test_streaming_window_equals_one_shot_encode():
+    """Encoding is per vector, so a cache built by appends and flushes holds
+    exactly the one-shot codes of its oldest tokens and the newest tokens
+    uncompressed, in order."""
+    rng = np.random.default_rng(7)
+    B, H, T, D, S, G = 2, 2, 70, 128, 2, 16
+    tk = rng.standard_normal((B, H, T, D)).astype(np.float16)
+    tv = rng.standard_normal((B, H, T, D)).astype(np.float16)
+    k_cb = (rng.standard_normal((S, G, 256, 8)) / np.sqrt(8) * np.array([1, .5])[:, None, None, None])
+    v_cb = (rng.standard_normal((S, G, 256, 8)) / np.sqrt(8) * np.array([1, .5])[:, None, None, None])
+    kw, vw, kc, vc, nw, nc = _stream(oracle, tk, tv, 24, 16, k_cb, v_cb, 64)
+    assert nc == 48 and nw == 22                      # 70 = 48 coded + 22 in the window
+    assert np.array_equal(kw[:, :, :nw], tk[:, :, nc:]) and np.array_equal(vw[:, :, :nw], tv[:, :, nc:])
+    k_once = oracle.rvq_encode(tk[:, :, :nc].astype(np.float64).reshape(-1, D), k_cb)
+    v_once = oracle.rvq_encode(tv[:, :, :nc].astype(np.float64).reshape(-1, D), v_cb)
+    assert np.array_equal(kc[:, :, :nc].reshape(-1, S, G), k_once)
+    assert np.array_equal(vc[:, :, :nc].reshape(-1, S, G), v_once)
+    # the streamed cache attends like the whole sequence with those codes
+    q = rng.standard_normal((B, 4, D))
+    a = oracle.attend(q, kc[:, :, :nc], vc[:, :, :nc], k_cb, v_cb, kw[:, :, :nw], vw[:, :, :nw])
+    kk = np.concatenate([np.stack([oracle.reconstruct(kc[b, :, :nc].reshape(-1, S, G), k_cb)
+                                   .reshape(H, nc, D) for b in range(B)]),
+                         tk[:, :, nc:].astype(np.float64)], axis=2)
+    vv = np.concatenate([np.stack([oracle.reconstruct(vc[b, :, :nc].reshape(-1, S, G), v_cb)
+                                   .reshape(H, nc, D) for b in range(B)]),
+                         tv[:, :, nc:].astype(np.float64)], axis=2)
+    ref = np.stack([oracle.attend_dense(q[b], kk[b], vv[b], 1 / np.sqrt(D)) for b in range(B)])
+    assert np.allclose(a, ref, rtol=0, atol=1e-12)
+
+
+def test_window_flush_moves_rows_and_keeps_the_tail():
+    rng = np.random.default_rng(3)
+    kw = rng.standard_normal((1, 1, 10, 64)).astype(np.float16)
+    vw = rng.standard_normal((1, 1, 10, 64)).astype(np.float16)
+    cb = rng.standard_normal((1, 1, 256, 64)) / 8
+    kc = np.zeros((1, 1, 8, 1, 1), np.uint8)
+    k2, v2, kc2, vc2 = oracle.window_flush(kw, vw, 9, 3, kc, kc.copy(), 5, cb, cb)
+    assert np.array_equal(k2[0, 0, :6], kw[0, 0, 3:9])       # moved to the front
+    assert np.array_equal(k2[0, 0, 6:], kw[0, 0, 6:])        # rows past the count untouched
+    assert np.array_equal(kc2[0, 0, :5], kc[0, 0, :5])       # earlier codes untouched
+    assert np.array_equal(kc2[0, 0, 5:8, 0, 0],
+                          oracle.rvq_encode(kw[0, 0, :3].astype(np.float64), cb)[:, 0, 0])
+    with pytest.raises(ValueError):
+        oracle.window_flush(kw, vw, 9, 3, kc, kc, 6, cb, cb)  # code buffer too small
