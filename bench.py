@@ -251,6 +251,7 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_prefill:
         res["encode_prefill"] = prefill_encode(torch, kvq, synth, dev)
+    res["stream"] = stream_calls(torch, kvq, inp, w, dev)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, inp, codes, eff_b, dec_gbs)
     print(json.dumps(res), flush=True)
@@ -302,6 +303,46 @@ def prefill_encode(torch, kvq, synth, dev, reps=5):
             "value": round(n_vec / t / 1e6, 2), "unit": "Mvec/s", "ms": round(t * 1e3, 4),
             "vectors": n_vec, "pct_bf16_mfma_peak": round(100 * flops / t / 1e12 / BF16_PEAK_TFLOPS, 3),
             "reps": reps}
+
+
+def stream_calls(torch, kvq, inp, w, dev, reps=20, wcap=192, n_flush=64):
+    """Latency of the streaming calls on the same layer: one window append
+    (a token per KV head) and one flush of the oldest 64 window tokens of
+    every KV head (K and V encoded into codes, the window compacted).  Each
+    timed call starts from a full window of wcap tokens."""
+    B, H, D = w.batch, w.n_kv_heads, w.head_dim
+    S, G, C = w.n_stages, w.n_groups, w.n_codewords
+    g = torch.Generator(device=dev)
+    g.manual_seed(11)
+    kw = torch.randn((B, H, wcap, D), generator=g, device=dev).to(torch.float16)
+    vw = torch.randn((B, H, wcap, D), generator=g, device=dev).to(torch.float16)
+    kc = torch.zeros((B, H, w.tokens, S, G), dtype=torch.uint8, device=dev)
+    vc = torch.zeros_like(kc)
+    kcb = torch.from_numpy(inp["cb"][0]).to(dev)
+    vcb = torch.from_numpy(inp["cb"][1]).to(dev)
+    ws = torch.empty(max(kvq.window_flush_workspace_size(D, G, S, C), 16), dtype=torch.uint8,
+                     device=dev)
+    kn = torch.randn((B, H, D), generator=g, device=dev).to(torch.float16)
+    vn = torch.randn((B, H, D), generator=g, device=dev).to(torch.float16)
+    tf, ta = [], []
+    kvq.window_flush(kw, vw, wcap, n_flush, kc, vc, 0, kcb, vcb, workspace=ws)   # packs the books
+    for i in range(reps + 3):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record()
+        kvq.window_flush(kw, vw, wcap, n_flush, kc, vc, (i % 8) * n_flush, kcb, vcb, workspace=ws,
+                         packed=True)
+        e[1].record()
+        kvq.window_append(kn, vn, kw, vw, wcap - n_flush)
+        e[2].record()
+        torch.cuda.synchronize()
+        if i >= 3:
+            tf.append(e[0].elapsed_time(e[1]))
+            ta.append(e[1].elapsed_time(e[2]))
+    return {"flush_us": round(float(np.median(tf)) * 1e3, 2),
+            "append_us": round(float(np.median(ta)) * 1e3, 2),
+            "flush_vectors": 2 * B * H * n_flush, "window_cap": wcap,
+            "note": "flush = K and V encode of the oldest tokens (codebooks packed once) + "
+                    "window compaction"}
 
 
 def cpu_baseline(w, inp, codes, eff_b, dec_gbs, budget_s=10.0):

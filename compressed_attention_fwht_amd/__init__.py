@@ -65,7 +65,7 @@ def _load():
     L.kvq_window_append.argtypes = [I32, I32, I32, I32, I32, P, P, P, P, P]
     L.kvq_window_flush_workspace_size.argtypes = [ctypes.POINTER(VqDesc), ctypes.POINTER(SZ)]
     L.kvq_window_flush.argtypes = [ctypes.POINTER(VqDesc), I32, I32, I32, I32, I32, P, P, I32, I32,
-                                   P, P, P, P, P, SZ, P]
+                                   P, P, P, P, U32, P, SZ, P]
     L.kvq_status_string.argtypes = [I32]
     L.kvq_status_string.restype = ctypes.c_char_p
     L.kvq_last_hip_error.argtypes = []
@@ -278,11 +278,12 @@ def window_flush_workspace_size(head_dim, n_groups, n_stages, n_codewords) -> in
 
 
 def window_flush(k_win, v_win, n_window, n_flush, k_codes, v_codes, n_code, k_cb, v_cb, *,
-                 workspace=None):
+                 workspace=None, packed=False):
     """Encode window rows [0, n_flush) into code rows [n_code, n_code + n_flush)
     (K with k_cb, V with v_cb), then move window rows [n_flush, n_window) to
     the front.  k/v_win [B][Hkv][Wcap][D] f16; k/v_codes [B][Hkv][Tcap][S][G] u8;
-    k/v_cb [S][G][C][dsub] f32."""
+    k/v_cb [S][G][C][dsub] f32.  ``packed``: ``workspace`` still holds these
+    codebooks packed by an earlier flush (KVQ_CODEBOOKS_PACKED)."""
     torch = _torch()
     _need_contig(k_win, v_win, k_codes, v_codes, k_cb, v_cb)
     for t in (k_win, v_win):
@@ -293,11 +294,14 @@ def window_flush(k_win, v_win, n_window, n_flush, k_codes, v_codes, n_code, k_cb
     C = k_cb.shape[2]
     vq = VqDesc(D, G, S, C)
     need = window_flush_workspace_size(D, G, S, C)
+    if packed and workspace is None:
+        raise ValueError("packed=True needs the workspace holding the packed codebooks")
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=k_win.device)
     ws_bytes = workspace.numel() if workspace is not None else 0
     _check(_lib().kvq_window_flush(ctypes.byref(vq), B, Hkv, Wcap, int(n_window), int(n_flush),
                                    _ptr(k_win), _ptr(v_win), Tcap, int(n_code), _ptr(k_codes),
-                                   _ptr(v_codes), _ptr(k_cb), _ptr(v_cb), _ptr(workspace),
+                                   _ptr(v_codes), _ptr(k_cb), _ptr(v_cb),
+                                   KVQ_CODEBOOKS_PACKED if packed else 0, _ptr(workspace),
                                    ws_bytes, _stream(k_win)),
            "kvq_window_flush")

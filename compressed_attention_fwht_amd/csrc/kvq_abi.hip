@@ -185,10 +185,11 @@ kvq_status kvq_window_flush(const kvq_vq_desc* vq, int32_t batch, int32_t n_kv_h
                             int32_t window_cap, int32_t n_window, int32_t n_flush,
                             uint16_t* k_win, uint16_t* v_win, int32_t code_cap, int32_t n_code,
                             uint8_t* k_codes, uint8_t* v_codes, const float* k_cb,
-                            const float* v_cb, void* workspace, size_t ws_bytes,
+                            const float* v_cb, uint32_t flags, void* workspace, size_t ws_bytes,
                             hipStream_t stream) {
   kvq_status st = check_vq(vq);
   if (st != KVQ_OK) return st;
+  if (flags & ~KVQ_CODEBOOKS_PACKED) return KVQ_ERR_SHAPE;
   if (batch < 1 || n_kv_heads < 1 || window_cap < 1 || code_cap < 0) return KVQ_ERR_SHAPE;
   if (n_window < 0 || n_window > window_cap) return KVQ_ERR_SHAPE;
   if (n_flush < 0 || n_flush > n_window) return KVQ_ERR_SHAPE;
@@ -211,11 +212,13 @@ kvq_status kvq_window_flush(const kvq_vq_desc* vq, int32_t batch, int32_t n_kv_h
     if (!aligned16(workspace)) return KVQ_ERR_ALIGN;
   }
   uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
+  const int packed = (flags & KVQ_CODEBOOKS_PACKED) ? 1 : 0;
   hipError_t e = kvq::launch_encode(k_win, (int)KVQ_F16, D, G, S, C, 1, units, window_cap, n_flush,
-                                    k_cb, k_codes, code_cap, n_code, 0, 0, 0, ws, stream);
+                                    k_cb, k_codes, code_cap, n_code, 0, 0, packed, ws, stream);
   if (e == hipSuccess)
     e = kvq::launch_encode(v_win, (int)KVQ_F16, D, G, S, C, 1, units, window_cap, n_flush, v_cb,
-                           v_codes, code_cap, n_code, 0, 0, 0, mfma ? ws + half : nullptr, stream);
+                           v_codes, code_cap, n_code, 0, 0, packed, mfma ? ws + half : nullptr,
+                           stream);
   if (e == hipSuccess)
     e = kvq::launch_window_compact(k_win, v_win, units, D, window_cap, n_window, n_flush, stream);
   return hip_status(e);

@@ -204,13 +204,15 @@ KVQ_API kvq_status kvq_window_flush_workspace_size(const kvq_vq_desc* vq, size_t
  * remaining window rows [n_flush, n_window) then move to rows
  * [0, n_window - n_flush).  Requires 0 <= n_flush <= n_window <= window_cap
  * and n_code + n_flush <= code_cap; n_flush == 0 is a no-op.  The caller's
- * counts become n_window - n_flush and n_code + n_flush. */
+ * counts become n_window - n_flush and n_code + n_flush.  flags: 0 or
+ * KVQ_CODEBOOKS_PACKED (the workspace still holds the K and V codebooks
+ * packed by an earlier flush with the same codebooks). */
 KVQ_API kvq_status kvq_window_flush(const kvq_vq_desc* vq, int32_t batch, int32_t n_kv_heads,
                             int32_t window_cap, int32_t n_window, int32_t n_flush,
                             uint16_t* k_win, uint16_t* v_win, int32_t code_cap,
                             int32_t n_code, uint8_t* k_codes, uint8_t* v_codes,
-                            const float* k_cb, const float* v_cb, void* workspace,
-                            size_t ws_bytes, hipStream_t stream);
+                            const float* k_cb, const float* v_cb, uint32_t flags,
+                            void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /* Static description of a status code. */
 KVQ_API const char* kvq_status_string(kvq_status status);

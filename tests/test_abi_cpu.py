@@ -166,10 +166,10 @@ def test_window_append_argument_errors():
 
 
 def _flush(vq=None, B=1, H=2, wcap=32, nw=32, nf=16, ccap=100, nc=0, kw=FAKE, ws=FAKE,
-           wsb=1 << 30):
+           wsb=1 << 30, flags=0):
     vq = _vq() if vq is None else vq
     return kvq.lib.kvq_window_flush(ctypes.byref(vq), B, H, wcap, nw, nf, kw, FAKE, ccap, nc, FAKE,
-                                    FAKE, FAKE, FAKE, ws, wsb, None)
+                                    FAKE, FAKE, FAKE, flags, ws, wsb, None)
 
 
 def test_window_flush_argument_errors():
@@ -182,5 +182,7 @@ def test_window_flush_argument_errors():
     assert _flush(kw=FAKE + 2) == ALIGN
     assert _flush(ws=0, wsb=0) == WS                    # MFMA path needs packed books
     assert _flush(nf=0, kw=0, ws=0, wsb=0) == OK        # nothing to flush: no-op
+    assert _flush(flags=0x1) == SHAPE                   # only KVQ_CODEBOOKS_PACKED is known
+    assert _flush(flags=0x8, kw=0) == NULL
     assert kvq.window_flush_workspace_size(128, 16, 2, 256) == 2 * 16 * 2 * 20480
     assert kvq.window_flush_workspace_size(64, 1, 2, 256) == 0   # generic kernel

@@ -338,9 +338,12 @@ def test_streaming_window_parity(key, over, wcap, nflush):
     okw = np.zeros((B, H, wcap, D), np.float16); ovw = np.zeros_like(okw)
     nw = nc = 0
     flushed = []
+    ws = torch.empty(max(kvq.window_flush_workspace_size(D, G, S, w.n_codewords), 16),
+                     dtype=torch.uint8, device="cuda")
     for t in range(T):
-        if nw == wcap:
-            kvq.window_flush(kw, vw, nw, nflush, kc, vc, nc, kcb_d, vcb_d)
+        if nw == wcap:                                   # the first flush packs the books
+            kvq.window_flush(kw, vw, nw, nflush, kc, vc, nc, kcb_d, vcb_d, workspace=ws,
+                             packed=bool(flushed))
             okw[:, :, :nw - nflush] = okw[:, :, nflush:nw].copy()
             ovw[:, :, :nw - nflush] = ovw[:, :, nflush:nw].copy()
             flushed.append((nc, nflush))
