@@ -126,13 +126,16 @@ __device__ __forceinline__ void wait_vmem() {
   __builtin_amdgcn_s_waitcnt(0x0f70);                    // vmcnt(0)
 }
 
-template <int S, int XT>
+template <int S, int XT, int GS>   // GS: blocks sharing a tile's 16 groups (1 or 16)
 __global__ __launch_bounds__(64 * mf_waves<S>(), 8 / mf_waves<S>()) void encode_mfma_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ packed, uint8_t* __restrict__ codes,
     int64_t n_seq, int64_t seq_stride, int64_t n_rows, int64_t code_stride, int64_t code_row0,
     int64_t tiles_per_book, int pre_rotated) {
   constexpr int G = 16;
   constexpr int SG = S * G;
+  // GS = 16 (small batches): one block per (tile, group), each rotating the
+  // tile itself and coding group g0 -- more blocks in flight for a batch too
+  // small to fill the CUs.
   // LDS: two buffers of one group's S stage blocks (double buffering); the
   // per-wave transpose scratch of the tile's input rows aliases them, since
   // it is dead before the first codebook load is issued.
@@ -142,8 +145,10 @@ __global__ __launch_bounds__(64 * mf_waves<S>(), 8 / mf_waves<S>()) void encode_
   const int h = lane >> 5;                                // lane half
   uint8_t* scratch = smem + wave * MF_SCRATCH;
 
-  const int64_t book = blockIdx.x / tiles_per_book;
-  const int64_t tile = blockIdx.x - book * tiles_per_book;
+  const int g0 = GS > 1 ? (int)(blockIdx.x % GS) : 0;
+  const int64_t bt = blockIdx.x / GS;
+  const int64_t book = bt / tiles_per_book;
+  const int64_t tile = bt - book * tiles_per_book;
   const int64_t n_per_book = n_seq * n_rows;
   constexpr int TILE = 64 * mf_waves<S>();
   constexpr int BUF = mf_buf<S>();
@@ -178,8 +183,9 @@ __global__ __launch_bounds__(64 * mf_waves<S>(), 8 / mf_waves<S>()) void encode_
   }
 
   const uint8_t* pk_book = packed + book * (int64_t)G * S * PACK_BYTES;
-  // group 0's codebooks load while the rotation runs
-  stage_group<S>(pk_book, smem, wave, lane);
+  // the first group's codebooks load while the rotation runs
+  stage_group<S>(pk_book + (int64_t)g0 * S * PACK_BYTES, smem + (g0 & 1) * mf_buf<S>(), wave,
+                 lane);
 
   // ---- y = H x (or x itself when pre-rotated), float32 in registers
   float y[128];
@@ -224,10 +230,13 @@ __global__ __launch_bounds__(64 * mf_waves<S>(), 8 / mf_waves<S>()) void encode_
 
 #pragma unroll
   for (int g = 0; g < G; ++g) {
+    if constexpr (GS > 1) {
+      if (g != g0) continue;                             // block-uniform
+    }
     const uint8_t* cbs = smem + (g & 1) * BUF;
     // ---- the next group's codebooks stream into the other buffer meanwhile
-    if (g + 1 < G) stage_group<S>(pk_book + (int64_t)(g + 1) * S * PACK_BYTES,
-                                  smem + ((g + 1) & 1) * BUF, wave, lane);
+    if (GS == 1 && g + 1 < G) stage_group<S>(pk_book + (int64_t)(g + 1) * S * PACK_BYTES,
+                                             smem + ((g + 1) & 1) * BUF, wave, lane);
 
     float r[8];
 #pragma unroll
@@ -347,11 +356,21 @@ __global__ __launch_bounds__(64 * mf_waves<S>(), 8 / mf_waves<S>()) void encode_
   }
 
   if (live) {
-    uint4* dst = reinterpret_cast<uint4*>(
-        codes + code_row(book, v_own, n_rows, n_seq, code_stride, code_row0) * SG);
+    uint8_t* row = codes + code_row(book, v_own, n_rows, n_seq, code_stride, code_row0) * SG;
+    if constexpr (GS == 1) {
+      uint4* dst = reinterpret_cast<uint4*>(row);
 #pragma unroll
-    for (int i = 0; i < SG / 16; ++i)
-      dst[i] = make_uint4(cw[4 * i], cw[4 * i + 1], cw[4 * i + 2], cw[4 * i + 3]);
+      for (int i = 0; i < SG / 16; ++i)
+        dst[i] = make_uint4(cw[4 * i], cw[4 * i + 1], cw[4 * i + 2], cw[4 * i + 3]);
+    } else {                                             // this block's code bytes only
+#pragma unroll
+      for (int s = 0; s < S; ++s)
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const int pos = s * G + g;
+          if (g == g0) row[pos] = (uint8_t)(cw[pos >> 2] >> (8 * (pos & 3)));
+        }
+    }
   }
 }
 
@@ -456,13 +475,20 @@ static hipError_t launch_mfma_t(const void* x, const uint8_t* packed, uint8_t* c
   const int64_t n_per_book = n_seq * n_rows;
   constexpr int TILE = 64 * mf_waves<S>();
   const int64_t tiles = (n_per_book + TILE - 1) / TILE;
+  // a small fp16 batch (a window flush) shares each tile's groups out over 16
+  // blocks, so the batch is spread over the CUs
+  const int64_t blocks = tiles * n_books;
+  const int gs = (XT == 2 && blocks <= 64) ? 16 : 1;
   size_t lds = (size_t)2 * mf_buf<S>();                    // two codebook buffers
   if (lds < (size_t)mf_waves<S>() * MF_SCRATCH) lds = (size_t)mf_waves<S>() * MF_SCRATCH;
-  auto kern = encode_mfma_kernel<S, XT>;
+  auto kern = encode_mfma_kernel<S, XT, 1>;
+  if constexpr (XT == 2) {
+    if (gs == 16) kern = encode_mfma_kernel<S, XT, 16>;
+  }
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)lds);
   if (e != hipSuccess) return e;
-  kern<<<dim3((unsigned)(tiles * n_books)), dim3(64 * mf_waves<S>()), lds, st>>>(
+  kern<<<dim3((unsigned)(blocks * gs)), dim3(64 * mf_waves<S>()), lds, st>>>(
       reinterpret_cast<const uint16_t*>(x), packed, codes, n_seq, seq_stride, n_rows, code_stride,
       code_row0, tiles, pre_rotated);
   return hipGetLastError();
