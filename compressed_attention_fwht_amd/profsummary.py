@@ -5,7 +5,7 @@
       per-kernel calls / average / min / max duration and share of GPU time.
 
   python -m compressed_attention_fwht_amd.profsummary counters COUNTER_CSV \\
-      --kernels NAME[,NAME...] --title T --cmd "..." --out FILE.md
+      --kernels "NAME[;NAME...]" --title T --cmd "..." --out FILE.md
       mean per-dispatch value of every counter of the run for each kernel.
 
   python -m compressed_attention_fwht_amd.profsummary traffic \\
@@ -110,7 +110,7 @@ def traffic(args):
 
 
 def counters(args):
-    keys = args.kernels.split(",")
+    keys = args.kernels.split(";")   # kernel names hold commas
     vals = collections.defaultdict(lambda: collections.defaultdict(list))
     names = {}
     for r in csv.DictReader(open(args.csv)):
