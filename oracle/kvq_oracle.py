@@ -31,6 +31,10 @@ Sources (page title -- section):
          append, read by attend); [ZK] profiling output (periodic
          flush_quantize calls); [VQKV] 3. Inference Integration (recent tokens
          uncompressed in a local window, older ones compressed).
+  Dual transform: [VI] VecInfer section (each key channel divided by the
+         square root of its largest magnitude before the Walsh-Hadamard
+         rotation; the inverse folded into the query so the scores are
+         unchanged).
 
 Parity status of each function is stated in its docstring; every function is
 pinned by ``tests/test_oracle_pins.py`` against closed forms, library routines
@@ -42,7 +46,9 @@ import numpy as np
 
 __all__ = ["hadamard_matrix", "fwht", "nearest", "rvq_encode", "reconstruct_rot",
            "reconstruct", "attend", "attend_dense", "lse_merge", "window_append",
-           "window_flush", "code_bytes_per_vector", "compression_ratio_vs_fp16"]
+           "window_flush", "smooth_factors", "smooth_keys", "smooth_query", "smooth_encode",
+           "reconstruct_smooth", "smooth_rows", "code_bytes_per_vector",
+           "compression_ratio_vs_fp16"]
 
 
 # ----------------------------------------------------------------------------
@@ -176,14 +182,19 @@ def attend_dense(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float) -> n
     return out
 
 
-def attend(q, k_codes, v_codes, k_cb, v_cb, k_win=None, v_win=None, scale=None):
+def attend(q, k_codes, v_codes, k_cb, v_cb, k_win=None, v_win=None, scale=None,
+           k_smooth=None):
     """Decode attention for a batch.
 
     q: [B][Hq][D] (original domain); k_codes, v_codes: [B][Hkv][Tc][S][G];
     k_cb, v_cb: [S][G][C][dsub]; k_win, v_win: fp16 [B][Hkv][W][D] or None.
     Keys/values of the coded part are the reconstructions H (sum of entries);
     the window tokens follow them on the same axis.  scale defaults to
-    1/sqrt(D).  Returns float64 [B][Hq][D].
+    1/sqrt(D).  k_smooth: smoothing factors [n_scale][D] the coded keys were
+    divided by before encoding (dual transform); the coded keys are then
+    reconstruct_smooth of their codes, KV head kv of sequence b using row
+    (b * Hkv + kv) % n_scale.  The window keeps the original keys.  Returns
+    float64 [B][Hq][D].
     """
     q = np.asarray(q, dtype=np.float64)
     B, Hq, D = q.shape
@@ -192,7 +203,11 @@ def attend(q, k_codes, v_codes, k_cb, v_cb, k_win=None, v_win=None, scale=None):
     for b in range(B):
         parts_k, parts_v = [], []
         if k_codes is not None and k_codes.shape[2] > 0:
-            parts_k.append(reconstruct(k_codes[b], k_cb))
+            kk = reconstruct(k_codes[b], k_cb)
+            if k_smooth is not None:
+                Hkv = kk.shape[0]
+                kk = kk * smooth_rows(k_smooth, b * Hkv + np.arange(Hkv))[:, None, :]
+            parts_k.append(kk)
             parts_v.append(reconstruct(v_codes[b], v_cb))
         if k_win is not None and k_win.shape[2] > 0:
             parts_k.append(np.asarray(k_win[b], dtype=np.float64))
@@ -220,14 +235,17 @@ def window_append(k_win, v_win, n_window, k_new, v_new):
     return k_win, v_win
 
 
-def window_flush(k_win, v_win, n_window, n_flush, k_codes, v_codes, n_code, k_cb, v_cb):
+def window_flush(k_win, v_win, n_window, n_flush, k_codes, v_codes, n_code, k_cb, v_cb,
+                 k_smooth=None):
     """The oldest n_flush window tokens (rows [0, n_flush) of every
     (sequence, KV head)) become codes at rows [n_code, n_code + n_flush) --
-    rvq_encode of the fp16 values, K with k_cb, V with v_cb -- and the rows
-    [n_flush, n_window) that stay uncompressed move to the front.  Buffers:
-    windows [B][Hkv][Wcap][D] fp16, codes [B][Hkv][Tcap][S][G] uint8.
-    Returns new (k_win, v_win, k_codes, v_codes); rows past the new counts
-    keep what they held."""
+    rvq_encode of the fp16 values, K with k_cb, V with v_cb; with k_smooth
+    ([n_scale][D]) the keys of (sequence b, KV head kv) are smooth_encode'd
+    with row (b * Hkv + kv) % n_scale -- and the rows [n_flush, n_window)
+    that stay uncompressed move to the front.  Buffers: windows
+    [B][Hkv][Wcap][D] fp16, codes [B][Hkv][Tcap][S][G] uint8.  Returns new
+    (k_win, v_win, k_codes, v_codes); rows past the new counts keep what they
+    held."""
     if not 0 <= n_flush <= n_window <= k_win.shape[2]:
         raise ValueError("bad window counts")
     if n_code + n_flush > k_codes.shape[2]:
@@ -236,12 +254,75 @@ def window_flush(k_win, v_win, n_window, n_flush, k_codes, v_codes, n_code, k_cb
     k_codes, v_codes = np.array(k_codes, copy=True), np.array(v_codes, copy=True)
     B, H, _, D = k_win.shape
     S, G = k_codes.shape[3], k_codes.shape[4]
-    for win, codes, cb in ((k_win, k_codes, k_cb), (v_win, v_codes, v_cb)):
-        x = win[:, :, :n_flush].astype(np.float64).reshape(-1, D)
-        codes[:, :, n_code:n_code + n_flush] = rvq_encode(x, cb).reshape(B, H, n_flush, S, G)
+    for win, codes, cb, sm in ((k_win, k_codes, k_cb, k_smooth), (v_win, v_codes, v_cb, None)):
+        x = win[:, :, :n_flush].astype(np.float64)
+        if sm is None:
+            z = rvq_encode(x.reshape(-1, D), cb)
+        else:
+            lam = smooth_rows(sm, np.arange(B * H)).reshape(B, H, 1, D)
+            z = smooth_encode(x, np.broadcast_to(lam, x.shape), cb)
+        codes[:, :, n_code:n_code + n_flush] = z.reshape(B, H, n_flush, S, G)
         keep = win[:, :, n_flush:n_window].copy()
         win[:, :, :n_window - n_flush] = keep
     return k_win, v_win, k_codes, v_codes
+
+
+# ----------------------------------------------------------------------------
+# Dual transform  [VI VecInfer: per-channel smooth scaling lambda_i =
+#       sqrt(max |K_i|) followed by the Walsh-Hadamard rotation; the inverse
+#       transform is absorbed into the queries]
+# ----------------------------------------------------------------------------
+def smooth_factors(k, n_scale: int = 1) -> np.ndarray:
+    """Smoothing factors of keys k [n_seq][T][D] (original domain).
+
+    lam[j][i] = sqrt(max |k[n][t][i]|) over every token t of every sequence n
+    with n % n_scale == j.  A channel whose maximum is 0 -- or a row j that no
+    sequence maps to -- gets 1: any positive factor leaves an all-zero channel
+    at zero, and 1 leaves the query untouched too.  Returns float64
+    [n_scale][D]."""
+    k = np.abs(np.asarray(k, dtype=np.float64))
+    n_seq, _, D = k.shape
+    lam = np.ones((n_scale, D), dtype=np.float64)
+    for j in range(n_scale):
+        rows = k[j::n_scale].reshape(-1, D)
+        if rows.shape[0] == 0:
+            continue
+        m = rows.max(axis=0)
+        lam[j] = np.where(m > 0.0, np.sqrt(m), 1.0)
+    return lam
+
+
+def smooth_rows(lam, seq_index) -> np.ndarray:
+    """The factor rows that sequences seq_index use: lam[n % n_scale]."""
+    lam = np.asarray(lam, dtype=np.float64)
+    return lam[np.asarray(seq_index) % lam.shape[0]]
+
+
+def smooth_keys(k, lam) -> np.ndarray:
+    """Keys with every channel divided by its factor (lam broadcasts over
+    the leading axes of k)."""
+    return np.asarray(k, dtype=np.float64) / np.asarray(lam, dtype=np.float64)
+
+
+def smooth_query(q, lam) -> np.ndarray:
+    """The query with the inverse of the key smoothing folded in: channel i
+    multiplied by lam_i, so smooth_query(q) . smooth_keys(k) = q . k."""
+    return np.asarray(q, dtype=np.float64) * np.asarray(lam, dtype=np.float64)
+
+
+def smooth_encode(x, lam, codebooks, **kw):
+    """Codes of the smoothed vectors: rvq_encode(x / lam) (rotation
+    included).  x: [..., D]; lam broadcasts to x.  Returns [N][S][G] for the
+    rows of x flattened."""
+    y = smooth_keys(x, lam)
+    return rvq_encode(y.reshape(-1, y.shape[-1]), codebooks, **kw)
+
+
+def reconstruct_smooth(codes, codebooks, lam) -> np.ndarray:
+    """Original-domain keys from codes of smoothed keys: the factors times
+    the unrotated reconstruction (the rotation is undone first, then the
+    division).  lam broadcasts to the output [..., D]."""
+    return reconstruct(codes, codebooks) * np.asarray(lam, dtype=np.float64)
 
 
 def lse_merge(parts):

@@ -431,3 +431,129 @@ def test_window_flush_moves_rows_and_keeps_the_tail():
                           oracle.rvq_encode(kw[0, 0, :3].astype(np.float64), cb)[:, 0, 0])
     with pytest.raises(ValueError):
         oracle.window_flush(kw, vw, 9, 3, kc, kc, 6, cb, cb)  # code buffer too small
+
+
+# ------------------------------------------------------------- dual transform
+# "VeloxQuant-MLX 0.5.1", VecInfer section: each key channel is divided by
+# sqrt(max |K_i|) before the Walsh-Hadamard rotation, and the inverse is folded
+# into the query, leaving the scores unchanged.
+def test_smooth_factors_hand_values():
+    """Channel maxima worked by hand: sequences 0 and 2 share row 0 at two
+    rows, every sequence row 0 at one row, row 3 of four has no sequence."""
+    k = np.array([[[-4.0, 0.0, 0.25], [1.0, 0.0, -9.0]],      # |max| 4, 0, 9
+                  [[2.0, 0.0, 0.0], [0.0, 0.0, 0.0]],         # |max| 2, 0, 0
+                  [[0.0, 1.0, 0.0], [0.0, -16.0, 0.0]]])      # |max| 0, 16, 0
+    assert np.array_equal(oracle.smooth_factors(k, 1), [[2.0, 4.0, 3.0]])
+    assert np.array_equal(oracle.smooth_factors(k, 2), [[2.0, 4.0, 3.0], [np.sqrt(2.0), 1.0, 1.0]])
+    lam4 = oracle.smooth_factors(k, 4)
+    assert np.array_equal(lam4[0], [2.0, 1.0, 3.0]) and np.array_equal(lam4[3], [1.0, 1.0, 1.0])
+    assert np.array_equal(lam4[2], [1.0, 4.0, 1.0])
+    assert np.array_equal(oracle.smooth_rows(lam4, [0, 5, 7]), lam4[[0, 1, 3]])
+
+
+def test_smoothing_square_roots_the_channel_maxima():
+    """After division by sqrt(max |K_i|) the largest magnitude of channel i
+    is sqrt(max |K_i|): the spread between channels is square-rooted."""
+    rng = np.random.default_rng(11)
+    k = rng.standard_normal((3, 200, 64)) * np.exp(rng.uniform(-2, 3, size=64))
+    lam = oracle.smooth_factors(k, 1)
+    ks = oracle.smooth_keys(k, lam[0])
+    mx, mxs = np.abs(k).max(axis=(0, 1)), np.abs(ks).max(axis=(0, 1))
+    assert np.allclose(mxs, np.sqrt(mx), rtol=1e-14)
+    assert np.isclose(mxs.max() / mxs.min(), np.sqrt(mx.max() / mx.min()), rtol=1e-12)
+
+
+def test_smooth_absorption_leaves_scores_unchanged():
+    """(H (lam * q)) . (H (k / lam)) = q . k for every key: H is orthonormal."""
+    rng = np.random.default_rng(12)
+    k = rng.standard_normal((1, 300, 128)) * np.r_[np.full(124, 1.0), np.full(4, 10.0)]
+    q = rng.standard_normal((5, 128))
+    lam = oracle.smooth_factors(k, 1)[0]
+    lhs = fwht(oracle.smooth_query(q, lam)) @ fwht(oracle.smooth_keys(k[0], lam)).T
+    assert np.allclose(lhs, q @ k[0].T, rtol=0, atol=1e-11 * np.abs(q @ k[0].T).max())
+    # the wrong direction (dividing the query) does not cancel
+    bad = fwht(q / lam) @ fwht(oracle.smooth_keys(k[0], lam)).T
+    assert np.max(np.abs(bad - q @ k[0].T)) > 1e-2
+
+
+def test_smooth_encode_special_cases():
+    """Factors of 1 change nothing; with a uniform power-of-two factor c,
+    |x/c - e|^2 = |x - c e|^2 / c^2 exactly, so coding x/c equals coding x
+    with the codebooks multiplied by c (and differs from dividing them)."""
+    rng = np.random.default_rng(13)
+    x = rng.standard_normal((400, 128))
+    cb = rng.standard_normal((2, 16, 256, 8)) / np.sqrt(8) * np.array([1, .5])[:, None, None, None]
+    assert np.array_equal(oracle.smooth_encode(x, np.ones(128), cb), rvq_encode(x, cb))
+    assert np.array_equal(oracle.smooth_encode(x, np.full(128, 4.0), cb), rvq_encode(x, cb * 4.0))
+    assert not np.array_equal(oracle.smooth_encode(x, np.full(128, 4.0), cb), rvq_encode(x, cb / 4.0))
+
+
+def test_smooth_attention_with_representable_codebooks_is_exact():
+    """Codebooks whose entries are exactly the smoothed, rotated key groups
+    (and the rotated value groups) reproduce every coded token, so smoothed
+    decode attention equals textbook softmax attention over the original keys
+    and values; the fp16 window keeps its original keys."""
+    rng = np.random.default_rng(14)
+    B, Hkv, Hq, T, W, D, G = 2, 2, 4, 150, 9, 64, 8
+    dsub = D // G
+    k = rng.standard_normal((B, Hkv, T, D)) * np.exp(rng.uniform(-1, 2, size=(1, Hkv, 1, D)))
+    v = rng.standard_normal((B, Hkv, T, D))
+    kw = rng.standard_normal((B, Hkv, W, D)).astype(np.float16)
+    vw = rng.standard_normal((B, Hkv, W, D)).astype(np.float16)
+    lam = oracle.smooth_factors(k.reshape(B * Hkv, T, D), Hkv)          # one row per KV head
+    q = rng.standard_normal((B, Hq, D))
+    kc = np.empty((B, Hkv, T, 1, G), np.uint8); vc = np.empty_like(kc)
+    out = np.empty((B, Hq, D))
+    for b in range(B):
+        for h in range(Hkv):
+            # one codebook set per (sequence, KV head): entry t = token t's group
+            kt = fwht(oracle.smooth_keys(k[b, h], lam[h]))
+            vt = fwht(v[b, h])
+            far = 1e3 * (1 + np.arange(256 - T))[:, None]
+            kcb = np.stack([np.concatenate([kt[:, g * dsub:(g + 1) * dsub], far + 0 * kt[:1, :dsub]])
+                            for g in range(G)])[None]
+            vcb = np.stack([np.concatenate([vt[:, g * dsub:(g + 1) * dsub], far + 0 * vt[:1, :dsub]])
+                            for g in range(G)])[None]
+            zk = oracle.smooth_encode(k[b, h], lam[h], kcb)
+            assert np.array_equal(zk[:, 0, :], np.repeat(np.arange(T)[:, None], G, 1))
+            one = oracle.attend(q[b:b + 1, 2 * h:2 * h + 2], zk[None, None], rvq_encode(v[b, h], vcb)[None, None],
+                                kcb, vcb, kw[b:b + 1, h:h + 1], vw[b:b + 1, h:h + 1],
+                                k_smooth=lam[h:h + 1])
+            ref = attend_dense(q[b, 2 * h:2 * h + 2],
+                               np.concatenate([k[b, h:h + 1], kw[b, h:h + 1].astype(np.float64)], 1),
+                               np.concatenate([v[b, h:h + 1], vw[b, h:h + 1].astype(np.float64)], 1),
+                               1 / np.sqrt(D))
+            assert np.allclose(one[0], ref, rtol=0, atol=1e-10)
+            # the factor row is chosen by (b * Hkv + kv) % n_scale
+            two = oracle.attend(q[b:b + 1, 2 * h:2 * h + 2], zk[None, None], rvq_encode(v[b, h], vcb)[None, None],
+                                kcb, vcb, kw[b:b + 1, h:h + 1], vw[b:b + 1, h:h + 1],
+                                k_smooth=np.stack([lam[h]] * (b + 1)))
+            assert np.allclose(two, one, rtol=0, atol=1e-12)
+
+
+def test_streaming_with_smoothing_equals_one_shot_smooth_encode():
+    """Flushed keys are smoothed with their (sequence, KV head) row; values
+    are not smoothed."""
+    rng = np.random.default_rng(15)
+    B, H, T, D, S, G = 2, 3, 40, 64, 1, 8
+    tk = (rng.standard_normal((B, H, T, D)) * np.exp(rng.uniform(-1, 2, size=D))).astype(np.float16)
+    tv = rng.standard_normal((B, H, T, D)).astype(np.float16)
+    cb = rng.standard_normal((S, G, 256, 8)) / np.sqrt(8)
+    lam = oracle.smooth_factors(tk.reshape(B * H, T, D).astype(np.float64), H)
+    kw = np.zeros((B, H, 16, D), np.float16); vw = np.zeros_like(kw)
+    kc = np.zeros((B, H, 32, S, G), np.uint8); vc = np.zeros_like(kc)
+    nw = nc = 0
+    for t in range(T):
+        if nw == 16:
+            kw, vw, kc, vc = oracle.window_flush(kw, vw, nw, 8, kc, vc, nc, cb, cb, k_smooth=lam)
+            nw, nc = nw - 8, nc + 8
+        kw, vw = oracle.window_append(kw, vw, nw, tk[:, :, t], tv[:, :, t])
+        nw += 1
+    assert nc == 24
+    xk = tk[:, :, :nc].astype(np.float64)
+    lam_rows = oracle.smooth_rows(lam, np.arange(B * H)).reshape(B, H, 1, D)
+    k_once = oracle.smooth_encode(xk, np.broadcast_to(lam_rows, xk.shape), cb)
+    assert np.array_equal(kc[:, :, :nc].reshape(-1, S, G), k_once)
+    v_once = rvq_encode(tv[:, :, :nc].astype(np.float64).reshape(-1, D), cb)
+    assert np.array_equal(vc[:, :, :nc].reshape(-1, S, G), v_once)
+    assert not np.array_equal(k_once, rvq_encode(xk.reshape(-1, D), cb))
