@@ -13,6 +13,10 @@ Calls (same names as the C ABI):
   encode(x, codebooks, n_rows=...)           codes uint8 [books][seq][rows][S][G]
   decode_reconstruct(codes, codebooks)       sum of codewords     -> f32 [..., D]
   attend_decode(q, k_codes, v_codes, k_cb, v_cb, k_win, v_win) -> f32 [B][Hq][D]
+  window_append / window_flush               streaming fp16 window -> codes
+  smooth_calibrate(k, n_scale)               dual-transform factors f32 [books][n_scale][D]
+  (encode, decode_reconstruct, attend_decode and window_flush take the factors
+  as ``smooth=`` / ``k_smooth=`` and then call the *_smooth entry points)
 """
 from __future__ import annotations
 
@@ -21,7 +25,8 @@ import os
 
 __all__ = ["KvqError", "LIB_PATH", "lib", "rotate", "encode", "encode_workspace_size",
            "decode_reconstruct", "attend_decode", "attend_workspace_size", "window_append",
-           "window_flush", "window_flush_workspace_size", "EXPORTS", "KVQ_INPUT_PRE_ROTATED",
+           "window_flush", "window_flush_workspace_size", "smooth_calibrate", "EXPORTS",
+           "KVQ_INPUT_PRE_ROTATED", "SmoothDesc",
            "KVQ_UNROTATE", "KVQ_ENCODE_GENERIC", "KVQ_CODEBOOKS_PACKED", "VqDesc", "AttnDesc",
            "status_string"]
 
@@ -35,8 +40,9 @@ F32, BF16, F16 = 0, 1, 2
 
 EXPORTS = ("kvq_rotate", "kvq_encode_workspace_size", "kvq_encode", "kvq_decode_reconstruct",
            "kvq_attend_workspace_size", "kvq_attend_decode", "kvq_window_append",
-           "kvq_window_flush_workspace_size", "kvq_window_flush", "kvq_status_string",
-           "kvq_last_hip_error")
+           "kvq_window_flush_workspace_size", "kvq_window_flush", "kvq_smooth_calibrate",
+           "kvq_encode_smooth", "kvq_decode_reconstruct_smooth", "kvq_attend_decode_smooth",
+           "kvq_window_flush_smooth", "kvq_status_string", "kvq_last_hip_error")
 
 
 class VqDesc(ctypes.Structure):
@@ -49,6 +55,10 @@ class AttnDesc(ctypes.Structure):
                 ("n_kv_heads", ctypes.c_int32), ("n_code_tokens", ctypes.c_int32),
                 ("n_window", ctypes.c_int32), ("vq", VqDesc), ("softmax_scale", ctypes.c_float),
                 ("code_stride", ctypes.c_int32), ("window_stride", ctypes.c_int32)]
+
+
+class SmoothDesc(ctypes.Structure):
+    _fields_ = [("factors", ctypes.c_void_p), ("n_scale", ctypes.c_int32)]
 
 
 def _load():
@@ -66,6 +76,16 @@ def _load():
     L.kvq_window_flush_workspace_size.argtypes = [ctypes.POINTER(VqDesc), ctypes.POINTER(SZ)]
     L.kvq_window_flush.argtypes = [ctypes.POINTER(VqDesc), I32, I32, I32, I32, I32, P, P, I32, I32,
                                    P, P, P, P, U32, P, SZ, P]
+    SD = ctypes.POINTER(SmoothDesc)
+    L.kvq_smooth_calibrate.argtypes = [P, I32, I32, I64, I64, I64, I64, I32, P, P]
+    L.kvq_encode_smooth.argtypes = [P, I32, ctypes.POINTER(VqDesc), I64, I64, I64, I64, SD, P, P,
+                                    U32, P, SZ, P]
+    L.kvq_decode_reconstruct_smooth.argtypes = [P, ctypes.POINTER(VqDesc), I64, I64, I64, P, SD,
+                                                P, P]
+    L.kvq_attend_decode_smooth.argtypes = [ctypes.POINTER(AttnDesc), P, P, P, P, P, SD, P, P, P,
+                                           P, SZ, P]
+    L.kvq_window_flush_smooth.argtypes = [ctypes.POINTER(VqDesc), I32, I32, I32, I32, I32, P, P,
+                                          I32, I32, P, P, P, P, SD, U32, P, SZ, P]
     L.kvq_status_string.argtypes = [I32]
     L.kvq_status_string.restype = ctypes.c_char_p
     L.kvq_last_hip_error.argtypes = []
@@ -138,6 +158,38 @@ def _need_contig(*ts):
             raise ValueError("tensors must be contiguous")
 
 
+def _smooth_desc(factors, n_books, D):
+    """SmoothDesc of a float32 factor tensor [n_books][n_scale][D] (or
+    [n_scale][D] when n_books == 1)."""
+    _need_contig(factors)
+    if factors.dtype != _torch().float32:
+        raise TypeError("smoothing factors must be float32")
+    if factors.dim() == 2:
+        factors = factors.unsqueeze(0)
+    if factors.dim() != 3 or factors.shape[0] != n_books or factors.shape[2] != D:
+        raise ValueError(f"smoothing factors must be [{n_books}][n_scale][{D}], got "
+                         f"{tuple(factors.shape)}")
+    return SmoothDesc(_ptr(factors), factors.shape[1])
+
+
+def smooth_calibrate(x, n_scale=1, *, n_rows=None, out=None):
+    """Dual-transform factors of x [n_books][n_seq][seq_stride][D]
+    (f32/bf16/f16): f[b][j][i] = sqrt(max |x[b][n][t][i]|) over sequences n
+    with n % n_scale == j and rows t < n_rows (1 where the maximum is 0).
+    Returns f32 [n_books][n_scale][D]."""
+    torch = _torch()
+    _need_contig(x)
+    nb, ns, stride, D = x.shape
+    n_rows = stride if n_rows is None else n_rows
+    if out is None:
+        out = torch.empty((nb, n_scale, D), dtype=torch.float32, device=x.device)
+    _need_contig(out)
+    _check(_lib().kvq_smooth_calibrate(_ptr(x), _dtype_code(x), D, nb, ns, stride, n_rows,
+                                       int(n_scale), _ptr(out), _stream(x)),
+           "kvq_smooth_calibrate")
+    return out
+
+
 def rotate(x, out=None):
     """y = H_D x over the last axis.  x: cuda tensor f32/bf16/f16 [..., D]."""
     torch = _torch()
@@ -160,13 +212,15 @@ def encode_workspace_size(head_dim, n_groups, n_stages, n_codewords, n_books) ->
 
 
 def encode(x, codebooks, *, n_rows=None, pre_rotated=False, generic=False, codes=None,
-           workspace=None, packed=False):
+           workspace=None, packed=False, smooth=None):
     """Encode rows [0, n_rows) of every sequence.
 
     x: [n_books][n_seq][seq_stride][D] (f32/bf16/f16); codebooks:
     [n_books][S][G][C][dsub] f32.  Returns codes [n_books][n_seq][n_rows][S][G] u8.
     ``packed``: ``workspace`` already holds these codebooks packed by an
-    earlier call (KVQ_CODEBOOKS_PACKED)."""
+    earlier call (KVQ_CODEBOOKS_PACKED).  ``smooth``: dual-transform factors
+    f32 [n_books][n_scale][D]; x is divided by them before the rotation
+    (kvq_encode_smooth)."""
     torch = _torch()
     _need_contig(x, codebooks)
     nb, ns, stride, D = x.shape
@@ -184,19 +238,43 @@ def encode(x, codebooks, *, n_rows=None, pre_rotated=False, generic=False, codes
     flags = ((KVQ_INPUT_PRE_ROTATED if pre_rotated else 0) | (KVQ_ENCODE_GENERIC if generic else 0)
              | (KVQ_CODEBOOKS_PACKED if packed else 0))
     ws_bytes = workspace.numel() if workspace is not None else 0
+    if smooth is not None:
+        sd = _smooth_desc(smooth, nb, D)
+        _check(_lib().kvq_encode_smooth(_ptr(x), _dtype_code(x), ctypes.byref(vq), nb, ns, stride,
+                                        n_rows, ctypes.byref(sd), _ptr(codebooks), _ptr(codes),
+                                        flags, _ptr(workspace), ws_bytes, _stream(x)),
+               "kvq_encode_smooth")
+        return codes
     _check(_lib().kvq_encode(_ptr(x), _dtype_code(x), ctypes.byref(vq), nb, ns, stride, n_rows,
                           _ptr(codebooks), _ptr(codes), flags, _ptr(workspace), ws_bytes,
                           _stream(x)), "kvq_encode")
     return codes
 
 
-def decode_reconstruct(codes, codebooks, *, unrotate=False, out=None):
+def decode_reconstruct(codes, codebooks, *, unrotate=False, out=None, smooth=None):
     """codes [n_books][...][S][G] u8, codebooks [n_books][S][G][C][dsub] f32 ->
-    f32 [n_books][...][D] (rotated domain unless ``unrotate``)."""
+    f32 [n_books][...][D] (rotated domain unless ``unrotate``).  ``smooth``:
+    the factors the codes' vectors were divided by (codes then
+    [n_books][n_seq][n_rows][S][G]); the output is the original domain,
+    factors times the unrotated sum (kvq_decode_reconstruct_smooth)."""
     torch = _torch()
     _need_contig(codes, codebooks)
     nb, S, G, C, dsub = codebooks.shape
     D = G * dsub
+    if smooth is not None:
+        if codes.dim() != 5:
+            raise ValueError("smooth=: codes must be [n_books][n_seq][n_rows][S][G]")
+        _, ns, nr = codes.shape[:3]
+        if out is None:
+            out = torch.empty((nb, ns, nr, D), dtype=torch.float32, device=codes.device)
+        _need_contig(out)
+        sd = _smooth_desc(smooth, nb, D)
+        vq = VqDesc(D, G, S, C)
+        _check(_lib().kvq_decode_reconstruct_smooth(_ptr(codes), ctypes.byref(vq), nb, ns, nr,
+                                                    _ptr(codebooks), ctypes.byref(sd), _ptr(out),
+                                                    _stream(codes)),
+               "kvq_decode_reconstruct_smooth")
+        return out
     per_book = codes.numel() // (nb * S * G) if codes.numel() else 0
     if out is None:
         out = torch.empty(codes.shape[:-2] + (D,), dtype=torch.float32, device=codes.device)
@@ -223,11 +301,12 @@ def attend_workspace_size(B, Hq, Hkv, D, Tc, W, S, G, C, scale=None) -> int:
 
 
 def attend_decode(q, k_codes, v_codes, k_cb, v_cb, k_win=None, v_win=None, *, scale=None,
-                  out=None, workspace=None, n_code=None, n_window=None):
+                  out=None, workspace=None, n_code=None, n_window=None, k_smooth=None):
     """q [B][Hq][D] f32; k/v_codes [B][Hkv][Tcap][S][G] u8; k/v_cb [S][G][C][dsub]
     f32; k/v_win [B][Hkv][Wcap][D] f16 (or None).  Rows [0, n_code) of the
     codes and [0, n_window) of the window are attended (default: all rows).
-    Returns f32 [B][Hq][D]."""
+    ``k_smooth``: f32 [n_scale][D] factors the coded keys were divided by
+    (kvq_attend_decode_smooth).  Returns f32 [B][Hq][D]."""
     torch = _torch()
     _need_contig(q, k_codes, v_codes, k_cb, v_cb, k_win, v_win)
     B, Hq, D = q.shape
@@ -248,6 +327,15 @@ def attend_decode(q, k_codes, v_codes, k_cb, v_cb, k_win=None, v_win=None, *, sc
     for w in (k_win, v_win):
         if w is not None and w.dtype != torch.float16:
             raise TypeError("window tensors must be float16")
+    if k_smooth is not None:
+        sd = _smooth_desc(k_smooth, 1, D)
+        _check(_lib().kvq_attend_decode_smooth(ctypes.byref(a), _ptr(q), _ptr(k_codes),
+                                               _ptr(v_codes), _ptr(k_cb), _ptr(v_cb),
+                                               ctypes.byref(sd), _ptr(k_win), _ptr(v_win),
+                                               _ptr(out), _ptr(workspace), workspace.numel(),
+                                               _stream(q)),
+               "kvq_attend_decode_smooth")
+        return out
     _check(_lib().kvq_attend_decode(ctypes.byref(a), _ptr(q), _ptr(k_codes), _ptr(v_codes),
                                  _ptr(k_cb), _ptr(v_cb), _ptr(k_win), _ptr(v_win), _ptr(out),
                                  _ptr(workspace), workspace.numel(), _stream(q)),
@@ -278,12 +366,14 @@ def window_flush_workspace_size(head_dim, n_groups, n_stages, n_codewords) -> in
 
 
 def window_flush(k_win, v_win, n_window, n_flush, k_codes, v_codes, n_code, k_cb, v_cb, *,
-                 workspace=None, packed=False):
+                 workspace=None, packed=False, k_smooth=None):
     """Encode window rows [0, n_flush) into code rows [n_code, n_code + n_flush)
     (K with k_cb, V with v_cb), then move window rows [n_flush, n_window) to
     the front.  k/v_win [B][Hkv][Wcap][D] f16; k/v_codes [B][Hkv][Tcap][S][G] u8;
     k/v_cb [S][G][C][dsub] f32.  ``packed``: ``workspace`` still holds these
-    codebooks packed by an earlier flush (KVQ_CODEBOOKS_PACKED)."""
+    codebooks packed by an earlier flush (KVQ_CODEBOOKS_PACKED).  ``k_smooth``:
+    f32 [n_scale][D] factors the flushed keys are divided by
+    (kvq_window_flush_smooth)."""
     torch = _torch()
     _need_contig(k_win, v_win, k_codes, v_codes, k_cb, v_cb)
     for t in (k_win, v_win):
@@ -299,9 +389,18 @@ def window_flush(k_win, v_win, n_window, n_flush, k_codes, v_codes, n_code, k_cb
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=k_win.device)
     ws_bytes = workspace.numel() if workspace is not None else 0
+    flags = KVQ_CODEBOOKS_PACKED if packed else 0
+    if k_smooth is not None:
+        sd = _smooth_desc(k_smooth, 1, D)
+        _check(_lib().kvq_window_flush_smooth(ctypes.byref(vq), B, Hkv, Wcap, int(n_window),
+                                              int(n_flush), _ptr(k_win), _ptr(v_win), Tcap,
+                                              int(n_code), _ptr(k_codes), _ptr(v_codes),
+                                              _ptr(k_cb), _ptr(v_cb), ctypes.byref(sd), flags,
+                                              _ptr(workspace), ws_bytes, _stream(k_win)),
+               "kvq_window_flush_smooth")
+        return
     _check(_lib().kvq_window_flush(ctypes.byref(vq), B, Hkv, Wcap, int(n_window), int(n_flush),
                                    _ptr(k_win), _ptr(v_win), Tcap, int(n_code), _ptr(k_codes),
-                                   _ptr(v_codes), _ptr(k_cb), _ptr(v_cb),
-                                   KVQ_CODEBOOKS_PACKED if packed else 0, _ptr(workspace),
+                                   _ptr(v_codes), _ptr(k_cb), _ptr(v_cb), flags, _ptr(workspace),
                                    ws_bytes, _stream(k_win)),
            "kvq_window_flush")

@@ -105,6 +105,20 @@ AttnPlan attn_plan(int B, int Hq, int Hkv, int D, int S, int G, int C, int Tc, i
   return p;
 }
 
+// Dual transform: the keys were coded divided channel-wise by the factor row
+// of their (sequence, KV head); multiplying the query's channels by the same
+// row before the rotation leaves every score unchanged.  v: the 8 channels
+// at col*8 of one query row.
+template <int D>
+__device__ __forceinline__ void smooth_query(float (&v)[8], const float* __restrict__ ksm, int b,
+                                             int kv, int Hkv, int64_t rows, int col) {
+  const float4* lp = reinterpret_cast<const float4*>(
+      ksm + (((int64_t)b * Hkv + kv) % rows) * D + col * 8);
+  const float4 a = lp[0], c = lp[1];
+  v[0] *= a.x; v[1] *= a.y; v[2] *= a.z; v[3] *= a.w;
+  v[4] *= c.x; v[5] *= c.y; v[6] *= c.z; v[7] *= c.w;
+}
+
 // --------------------------------------------------------------- attn_lut
 // grid (B*Hkv*n_hsplit, S*G), block 256.  Block (unit, sg) writes the LUT
 // entries of one (s, g) table for the RP query heads of its unit, laid out
@@ -115,7 +129,9 @@ __global__ __launch_bounds__(256) void attn_lut_kernel(const float* __restrict__
                                                        const float* __restrict__ kcb,
                                                        float* __restrict__ lut, int Hq, int Hkv,
                                                        int n_hsplit, int G, int C,
-                                                       size_t lut_slice, float scale) {
+                                                       size_t lut_slice, float scale,
+                                                       const float* __restrict__ ksm,
+                                                       int64_t ksm_rows) {
   constexpr int L = D / 8;                 // lanes per query row in the butterfly
   constexpr int ROWS = 64 / L;             // query rows per wave
   __shared__ float qs[RP][D];
@@ -138,6 +154,7 @@ __global__ __launch_bounds__(256) void attn_lut_kernel(const float* __restrict__
       float v[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[e] = qp[e];
+      if (ksm != nullptr) smooth_query<D>(v, ksm, b, kv, Hkv, ksm_rows, lane % L);
       hadamard_row<8, L>(v, lane);
       const float rs = scale * rsqrt_pow2(D);
       if (r < RP) {
@@ -460,7 +477,8 @@ __global__ __launch_bounds__(CH_THREADS, 1) void attn_chunk_kernel(
     int pstride, int fbits, int cparts, size_t lut_slice, const float* __restrict__ kcb,
     int fuse_lut, const float* __restrict__ q,
     const uint16_t* __restrict__ kw, const uint16_t* __restrict__ vw, int W, int wslice,
-    int nslots, float scale, int cstride, int wstride) {
+    int nslots, float scale, int cstride, int wstride, const float* __restrict__ ksm,
+    int64_t ksm_rows) {
   constexpr int L = D / 8;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int ci = blockIdx.x;
@@ -558,6 +576,7 @@ __global__ __launch_bounds__(CH_THREADS, 1) void attn_chunk_kernel(
         float v[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = qp[e];
+        if (ksm != nullptr) smooth_query<D>(v, ksm, b, kv, Hkv, ksm_rows, lane % L);
         hadamard_row<8, L>(v, lane);
         const float rs = scale * rsqrt_pow2(D);
         if (r < RP) {
@@ -918,19 +937,19 @@ static hipError_t launch_rp(const AttnPlan& p, int SG, const float* q, const flo
                             const uint8_t* kc, const uint8_t* vc, const float* vcb, float* lut,
                             float* part, const uint16_t* kw, const uint16_t* vw, int B, int Hq,
                             int Hkv, int D, int S, int G, int C, int Tc, int W, int cstride,
-                            int wstride, float scale, hipStream_t st) {
+                            int wstride, float scale, Smooth ksm, hipStream_t st) {
   hipError_t e = hipSuccess;
   size_t lds = 0;
   if (p.n_chunks > 0 && !p.fuse_lut) {
     if (D == 64)
       attn_lut_kernel<RP, 64><<<dim3(B * Hkv * p.n_hsplit, SG), 256, 0, st>>>(
-          q, kcb, lut, Hq, Hkv, p.n_hsplit, G, C, p.lut_slice, scale);
+          q, kcb, lut, Hq, Hkv, p.n_hsplit, G, C, p.lut_slice, scale, ksm.f, ksm.n_scale);
     else if (D == 128)
       attn_lut_kernel<RP, 128><<<dim3(B * Hkv * p.n_hsplit, SG), 256, 0, st>>>(
-          q, kcb, lut, Hq, Hkv, p.n_hsplit, G, C, p.lut_slice, scale);
+          q, kcb, lut, Hq, Hkv, p.n_hsplit, G, C, p.lut_slice, scale, ksm.f, ksm.n_scale);
     else
       attn_lut_kernel<RP, 256><<<dim3(B * Hkv * p.n_hsplit, SG), 256, 0, st>>>(
-          q, kcb, lut, Hq, Hkv, p.n_hsplit, G, C, p.lut_slice, scale);
+          q, kcb, lut, Hq, Hkv, p.n_hsplit, G, C, p.lut_slice, scale, ksm.f, ksm.n_scale);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -955,7 +974,8 @@ static hipError_t launch_rp(const AttnPlan& p, int SG, const float* q, const flo
     kern<<<grid, CH_THREADS, lds, st>>>(kc, vc, vcb, lut, part, Hq, Hkv, S, G, C, Tc,          \
                                         p.n_chunks, p.chunk, p.n_hsplit, p.pstride, p.fbits,   \
                                         p.cparts, p.lut_slice, kcb, p.fuse_lut, q, kw, vw, W,  \
-                                        p.wslice, nslots, scale, cstride, wstride);            \
+                                        p.wslice, nslots, scale, cstride, wstride, ksm.f,      \
+                                        ksm.n_scale);                                          \
     return hipGetLastError();                                                                  \
   }
   if (D == 64) KVQ_CH(0, 64)
@@ -972,15 +992,15 @@ hipError_t launch_attend(const AttnPlan& p, int B, int Hq, int Hkv, int D, int S
                          const uint8_t* kc,
                          const uint8_t* vc, const float* kcb, const float* vcb,
                          const uint16_t* kw, const uint16_t* vw, float* out, void* ws,
-                         hipStream_t st) {
+                         Smooth ksm, hipStream_t st) {
   float* lut = reinterpret_cast<float*>(ws);
   float* part = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) +
                                          ((p.lut_bytes + 255) & ~(size_t)255));
   const int SG = S * G;
   hipError_t e;
-  if (p.rp == 4) e = launch_rp<4>(p, SG, q, kcb, kc, vc, vcb, lut, part, kw, vw, B, Hq, Hkv, D, S, G, C, Tc, W, cstride, wstride, scale, st);
-  else if (p.rp == 2) e = launch_rp<2>(p, SG, q, kcb, kc, vc, vcb, lut, part, kw, vw, B, Hq, Hkv, D, S, G, C, Tc, W, cstride, wstride, scale, st);
-  else e = launch_rp<1>(p, SG, q, kcb, kc, vc, vcb, lut, part, kw, vw, B, Hq, Hkv, D, S, G, C, Tc, W, cstride, wstride, scale, st);
+  if (p.rp == 4) e = launch_rp<4>(p, SG, q, kcb, kc, vc, vcb, lut, part, kw, vw, B, Hq, Hkv, D, S, G, C, Tc, W, cstride, wstride, scale, ksm, st);
+  else if (p.rp == 2) e = launch_rp<2>(p, SG, q, kcb, kc, vc, vcb, lut, part, kw, vw, B, Hq, Hkv, D, S, G, C, Tc, W, cstride, wstride, scale, ksm, st);
+  else e = launch_rp<1>(p, SG, q, kcb, kc, vc, vcb, lut, part, kw, vw, B, Hq, Hkv, D, S, G, C, Tc, W, cstride, wstride, scale, ksm, st);
   if (e != hipSuccess) return e;
   const int nslots = p.n_chunks + p.n_wblocks;
   if (D == 64) attn_merge_kernel<64><<<dim3(B * Hq), 256, 0, st>>>(part, out, nslots, p.pstride);

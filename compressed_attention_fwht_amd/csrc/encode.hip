@@ -130,7 +130,7 @@ template <int S, int XT, int GS>   // GS: blocks sharing a tile's 16 groups (1 o
 __global__ __launch_bounds__(64 * mf_waves<S>(), 8 / mf_waves<S>()) void encode_mfma_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ packed, uint8_t* __restrict__ codes,
     int64_t n_seq, int64_t seq_stride, int64_t n_rows, int64_t code_stride, int64_t code_row0,
-    int64_t tiles_per_book, int pre_rotated) {
+    int64_t tiles_per_book, int pre_rotated, const float* __restrict__ smooth, int64_t n_scale) {
   constexpr int G = 16;
   constexpr int SG = S * G;
   // GS = 16 (small batches): one block per (tile, group), each rotating the
@@ -197,6 +197,20 @@ __global__ __launch_bounds__(64 * mf_waves<S>(), 8 / mf_waves<S>()) void encode_
     } else {
       y[2 * i] = f16_bits_to_f32(xw[i]);
       y[2 * i + 1] = f16_bits_to_f32(xw[i] >> 16);
+    }
+  }
+  if (smooth != nullptr) {
+    // dual transform: channel i divided by the sequence's factor (times its
+    // reciprocal, within 1 ulp) ahead of the rotation
+    const float4* lp = reinterpret_cast<const float4*>(
+        smooth + (book * n_scale + (v_ld / n_rows) % n_scale) * 128);
+#pragma unroll
+    for (int c = 0; c < 32; ++c) {
+      const float4 l = lp[c];
+      y[4 * c + 0] *= __builtin_amdgcn_rcpf(l.x);
+      y[4 * c + 1] *= __builtin_amdgcn_rcpf(l.y);
+      y[4 * c + 2] *= __builtin_amdgcn_rcpf(l.z);
+      y[4 * c + 3] *= __builtin_amdgcn_rcpf(l.w);
     }
   }
   if (!pre_rotated) {
@@ -381,7 +395,8 @@ template <int D, int DSUB>
 __global__ __launch_bounds__(256) void encode_generic_kernel(
     const void* __restrict__ x, int xt, const float* __restrict__ cb, uint8_t* __restrict__ codes,
     int64_t n_seq, int64_t seq_stride, int64_t n_rows, int64_t code_stride, int64_t code_row0,
-    int64_t tiles_per_book, int S, int C, int pre_rotated) {
+    int64_t tiles_per_book, int S, int C, int pre_rotated, const float* __restrict__ smooth,
+    int64_t n_scale) {
   constexpr int G = D / DSUB;
   constexpr int L = D / 8;
   constexpr int ROWS_PER_WAVE = 64 / L;
@@ -410,6 +425,11 @@ __global__ __launch_bounds__(256) void encode_generic_kernel(
     if (xt == 0) load8<0>(xb + e * esz, val);
     else if (xt == 1) load8<1>(xb + e * esz, val);
     else load8<2>(xb + e * esz, val);
+    if (smooth != nullptr) {            // dual transform: divide by the factor row
+      const float* lp = smooth + (book * n_scale + seq % n_scale) * D + col * 8;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) val[i] *= __builtin_amdgcn_rcpf(lp[i]);
+    }
     if (!pre_rotated) {
       hadamard_row<8, L>(val, lane);
       constexpr float sc = rsqrt_pow2(D);
@@ -471,7 +491,7 @@ template <int S, int XT>
 static hipError_t launch_mfma_t(const void* x, const uint8_t* packed, uint8_t* codes,
                                 int64_t n_books, int64_t n_seq, int64_t seq_stride, int64_t n_rows,
                                 int64_t code_stride, int64_t code_row0, int pre_rotated,
-                                hipStream_t st) {
+                                Smooth sm, hipStream_t st) {
   const int64_t n_per_book = n_seq * n_rows;
   constexpr int TILE = 64 * mf_waves<S>();
   const int64_t tiles = (n_per_book + TILE - 1) / TILE;
@@ -490,7 +510,7 @@ static hipError_t launch_mfma_t(const void* x, const uint8_t* packed, uint8_t* c
   if (e != hipSuccess) return e;
   kern<<<dim3((unsigned)(blocks * gs)), dim3(64 * mf_waves<S>()), lds, st>>>(
       reinterpret_cast<const uint16_t*>(x), packed, codes, n_seq, seq_stride, n_rows, code_stride,
-      code_row0, tiles, pre_rotated);
+      code_row0, tiles, pre_rotated, sm.f, sm.n_scale);
   return hipGetLastError();
 }
 
@@ -498,7 +518,7 @@ template <int D, int DSUB>
 static hipError_t launch_generic_t(const void* x, int xt, const float* cb, uint8_t* codes,
                                    int64_t n_books, int64_t n_seq, int64_t seq_stride,
                                    int64_t n_rows, int64_t code_stride, int64_t code_row0, int S,
-                                   int C, int pre_rotated, hipStream_t st) {
+                                   int C, int pre_rotated, Smooth sm, hipStream_t st) {
   const int64_t n_per_book = n_seq * n_rows;
   const int64_t tiles = (n_per_book + GEN_TILE - 1) / GEN_TILE;
   const int G = D / DSUB;
@@ -509,14 +529,15 @@ static hipError_t launch_generic_t(const void* x, int xt, const float* cb, uint8
   if (e != hipSuccess) return e;
   kern<<<dim3((unsigned)(tiles * n_books)), dim3(256), lds, st>>>(
       x, xt, cb, codes, n_seq, seq_stride, n_rows, code_stride, code_row0, tiles, S, C,
-      pre_rotated);
+      pre_rotated, sm.f, sm.n_scale);
   return hipGetLastError();
 }
 
 hipError_t launch_encode(const void* x, int xt, int D, int G, int S, int C, int64_t n_books,
                          int64_t n_seq, int64_t seq_stride, int64_t n_rows, const float* cb,
                          uint8_t* codes, int64_t code_stride, int64_t code_row0, int pre_rotated,
-                         int force_generic, int packed_in_ws, void* ws, hipStream_t st) {
+                         int force_generic, int packed_in_ws, void* ws, Smooth sm,
+                         hipStream_t st) {
   if (n_books == 0 || n_seq == 0 || n_rows == 0) return hipSuccess;
   if (!force_generic && encode_mfma_eligible(D, G, S, C, xt)) {
     uint8_t* packed = reinterpret_cast<uint8_t*>(ws);
@@ -533,9 +554,9 @@ hipError_t launch_encode(const void* x, int xt, int D, int G, int S, int C, int6
   if (S == SS) {                                                                           \
     if (xt == 1) return launch_mfma_t<SS, 1>(x, packed, codes, n_books, n_seq, seq_stride,  \
                                              n_rows, code_stride, code_row0, pre_rotated,   \
-                                             st);                                           \
+                                             sm, st);                                       \
     return launch_mfma_t<SS, 2>(x, packed, codes, n_books, n_seq, seq_stride, n_rows,       \
-                                code_stride, code_row0, pre_rotated, st);                   \
+                                code_stride, code_row0, pre_rotated, sm, st);               \
   }
     KVQ_MF(1) KVQ_MF(2) KVQ_MF(3) KVQ_MF(4)
 #undef KVQ_MF
@@ -544,7 +565,7 @@ hipError_t launch_encode(const void* x, int xt, int D, int G, int S, int C, int6
 #define KVQ_GEN(DD, DS) \
   if (D == DD && dsub == DS) \
     return launch_generic_t<DD, DS>(x, xt, cb, codes, n_books, n_seq, seq_stride, n_rows,      \
-                                    code_stride, code_row0, S, C, pre_rotated, st);
+                                    code_stride, code_row0, S, C, pre_rotated, sm, st);
   KVQ_GEN(64, 8) KVQ_GEN(64, 16) KVQ_GEN(64, 32) KVQ_GEN(64, 64)
   KVQ_GEN(128, 8) KVQ_GEN(128, 16) KVQ_GEN(128, 32) KVQ_GEN(128, 64) KVQ_GEN(128, 128)
   KVQ_GEN(256, 8) KVQ_GEN(256, 16) KVQ_GEN(256, 32) KVQ_GEN(256, 64) KVQ_GEN(256, 128)

@@ -55,6 +55,61 @@ kvq_status check_attn(const kvq_attn_desc* a, kvq::AttnPlan* plan) {
   return KVQ_OK;
 }
 
+kvq_status check_smooth(const kvq_smooth_desc* sm) {
+  if (!sm || !sm->factors) return KVQ_ERR_NULL;
+  if (sm->n_scale < 1) return KVQ_ERR_SHAPE;
+  if (!aligned16(sm->factors)) return KVQ_ERR_ALIGN;
+  return KVQ_OK;
+}
+
+kvq::Smooth to_smooth(const kvq_smooth_desc* sm) {
+  kvq::Smooth r;
+  if (sm) {
+    r.f = sm->factors;
+    r.n_scale = sm->n_scale;
+  }
+  return r;
+}
+
+// kvq_encode and kvq_encode_smooth (smooth == nullptr: no division)
+kvq_status encode_common(const void* x, kvq_dtype xt, const kvq_vq_desc* vq, int64_t n_books,
+                         int64_t n_seq, int64_t seq_stride, int64_t n_rows,
+                         const kvq_smooth_desc* smooth, const float* codebooks, uint8_t* codes,
+                         uint32_t flags, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  if (!valid_dtype(xt)) return KVQ_ERR_DTYPE;
+  kvq_status st = check_vq(vq);
+  if (st != KVQ_OK) return st;
+  if (flags & ~(KVQ_INPUT_PRE_ROTATED | KVQ_ENCODE_GENERIC | KVQ_CODEBOOKS_PACKED))
+    return KVQ_ERR_SHAPE;
+  if (smooth && (flags & KVQ_INPUT_PRE_ROTATED)) return KVQ_ERR_UNSUPPORTED;
+  if (n_books < 0 || n_seq < 0 || seq_stride < 0 || n_rows < 0) return KVQ_ERR_SHAPE;
+  if (n_rows > seq_stride) return KVQ_ERR_SHAPE;
+  if (smooth) {
+    st = check_smooth(smooth);
+    if (st != KVQ_OK) return st;
+  }
+  if (n_books == 0 || n_seq == 0 || n_rows == 0) return KVQ_OK;
+  if (!x || !codebooks || !codes) return KVQ_ERR_NULL;
+  if (!aligned16(x) || !aligned16(codebooks) || !aligned16(codes)) return KVQ_ERR_ALIGN;
+  const int D = vq->head_dim, G = vq->n_groups, S = vq->n_stages, C = vq->n_codewords;
+  const int64_t n_per_book = n_seq * n_rows;
+  if (n_seq > ((int64_t)1 << 40) / n_rows) return KVQ_ERR_SHAPE;
+  const int64_t tile = 64;   // smallest tile of either kernel
+  if (n_books * ((n_per_book + tile - 1) / tile) > 0x7fffffffLL) return KVQ_ERR_UNSUPPORTED;
+  const bool generic = (flags & KVQ_ENCODE_GENERIC) != 0 ||
+                       !kvq::encode_mfma_eligible(D, G, S, C, (int)xt);
+  if (!generic) {
+    const size_t need = kvq::encode_workspace_bytes(D, G, S, C, n_books);
+    if (ws_bytes < need || (need > 0 && !workspace)) return KVQ_ERR_WORKSPACE;
+    if (need > 0 && !aligned16(workspace)) return KVQ_ERR_ALIGN;
+  }
+  return hip_status(kvq::launch_encode(x, (int)xt, D, G, S, C, n_books, n_seq, seq_stride, n_rows,
+                                       codebooks, codes, n_rows, 0,
+                                       (flags & KVQ_INPUT_PRE_ROTATED) ? 1 : 0,
+                                       generic ? 1 : 0, (flags & KVQ_CODEBOOKS_PACKED) ? 1 : 0,
+                                       workspace, to_smooth(smooth), stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -109,33 +164,47 @@ kvq_status kvq_encode(const void* x, kvq_dtype xt, const kvq_vq_desc* vq, int64_
                       int64_t n_seq, int64_t seq_stride, int64_t n_rows, const float* codebooks,
                       uint8_t* codes, uint32_t flags, void* workspace, size_t ws_bytes,
                       hipStream_t stream) {
+  return encode_common(x, xt, vq, n_books, n_seq, seq_stride, n_rows, nullptr, codebooks, codes,
+                       flags, workspace, ws_bytes, stream);
+}
+
+kvq_status kvq_encode_smooth(const void* x, kvq_dtype xt, const kvq_vq_desc* vq, int64_t n_books,
+                             int64_t n_seq, int64_t seq_stride, int64_t n_rows,
+                             const kvq_smooth_desc* smooth, const float* codebooks,
+                             uint8_t* codes, uint32_t flags, void* workspace, size_t ws_bytes,
+                             hipStream_t stream) {
+  if (!smooth) return KVQ_ERR_NULL;
+  return encode_common(x, xt, vq, n_books, n_seq, seq_stride, n_rows, smooth, codebooks, codes,
+                       flags, workspace, ws_bytes, stream);
+}
+
+kvq_status kvq_smooth_calibrate(const void* x, kvq_dtype xt, int32_t head_dim, int64_t n_books,
+                                int64_t n_seq, int64_t seq_stride, int64_t n_rows,
+                                int32_t n_scale, float* factors, hipStream_t stream) {
   if (!valid_dtype(xt)) return KVQ_ERR_DTYPE;
-  kvq_status st = check_vq(vq);
-  if (st != KVQ_OK) return st;
-  if (flags & ~(KVQ_INPUT_PRE_ROTATED | KVQ_ENCODE_GENERIC | KVQ_CODEBOOKS_PACKED))
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256) return KVQ_ERR_SHAPE;
+  if (n_books < 0 || n_seq < 0 || seq_stride < 0 || n_rows < 0 || n_scale < 1)
     return KVQ_ERR_SHAPE;
-  if (n_books < 0 || n_seq < 0 || seq_stride < 0 || n_rows < 0) return KVQ_ERR_SHAPE;
   if (n_rows > seq_stride) return KVQ_ERR_SHAPE;
-  if (n_books == 0 || n_seq == 0 || n_rows == 0) return KVQ_OK;
-  if (!x || !codebooks || !codes) return KVQ_ERR_NULL;
-  if (!aligned16(x) || !aligned16(codebooks) || !aligned16(codes)) return KVQ_ERR_ALIGN;
-  const int D = vq->head_dim, G = vq->n_groups, S = vq->n_stages, C = vq->n_codewords;
-  const int64_t n_per_book = n_seq * n_rows;
-  if (n_seq > ((int64_t)1 << 40) / n_rows) return KVQ_ERR_SHAPE;
-  const int64_t tile = 64;   // smallest tile of either kernel
-  if (n_books * ((n_per_book + tile - 1) / tile) > 0x7fffffffLL) return KVQ_ERR_UNSUPPORTED;
-  const bool generic = (flags & KVQ_ENCODE_GENERIC) != 0 ||
-                       !kvq::encode_mfma_eligible(D, G, S, C, (int)xt);
-  if (!generic) {
-    const size_t need = kvq::encode_workspace_bytes(D, G, S, C, n_books);
-    if (ws_bytes < need || (need > 0 && !workspace)) return KVQ_ERR_WORKSPACE;
-    if (need > 0 && !aligned16(workspace)) return KVQ_ERR_ALIGN;
+  if (n_books == 0) return KVQ_OK;
+  if (!factors) return KVQ_ERR_NULL;
+  if (!aligned16(factors)) return KVQ_ERR_ALIGN;
+  if (n_books > ((int64_t)1 << 40) / ((int64_t)n_scale * head_dim)) return KVQ_ERR_SHAPE;
+  const bool reads = n_seq > 0 && n_rows > 0;
+  if (reads) {
+    if (!x) return KVQ_ERR_NULL;
+    if (!aligned16(x)) return KVQ_ERR_ALIGN;
+    if (n_seq > ((int64_t)1 << 40) / seq_stride / n_books / head_dim) return KVQ_ERR_SHAPE;
+    const int64_t row_blocks = (n_rows + 511) / 512;
+    if (n_books * n_seq > 0x7fffffffLL / row_blocks) return KVQ_ERR_UNSUPPORTED;
+    const int esz = xt == KVQ_F32 ? 4 : 2;
+    const uintptr_t xa = (uintptr_t)x, fa = (uintptr_t)factors;
+    const uintptr_t xe = xa + (uintptr_t)(n_books * n_seq * seq_stride * head_dim * esz);
+    const uintptr_t fe = fa + (uintptr_t)((int64_t)n_books * n_scale * head_dim * 4);
+    if (xa < fe && fa < xe) return KVQ_ERR_SHAPE;       // output may not overlap the input
   }
-  return hip_status(kvq::launch_encode(x, (int)xt, D, G, S, C, n_books, n_seq, seq_stride, n_rows,
-                                       codebooks, codes, n_rows, 0,
-                                       (flags & KVQ_INPUT_PRE_ROTATED) ? 1 : 0,
-                                       generic ? 1 : 0, (flags & KVQ_CODEBOOKS_PACKED) ? 1 : 0,
-                                       workspace, stream));
+  return hip_status(kvq::launch_smooth_calibrate(x, (int)xt, head_dim, n_books, n_seq, seq_stride,
+                                                 n_rows, n_scale, factors, stream));
 }
 
 kvq_status kvq_decode_reconstruct(const uint8_t* codes, const kvq_vq_desc* vq, int64_t n_books,
@@ -152,6 +221,27 @@ kvq_status kvq_decode_reconstruct(const uint8_t* codes, const kvq_vq_desc* vq, i
   return hip_status(kvq::launch_reconstruct(codes, codebooks, out, n_books, n_per_book,
                                             vq->head_dim, vq->n_groups, vq->n_stages,
                                             vq->n_codewords, (flags & KVQ_UNROTATE) ? 1 : 0,
+                                            n_per_book, kvq::Smooth{}, stream));
+}
+
+kvq_status kvq_decode_reconstruct_smooth(const uint8_t* codes, const kvq_vq_desc* vq,
+                                         int64_t n_books, int64_t n_seq, int64_t n_rows,
+                                         const float* codebooks, const kvq_smooth_desc* smooth,
+                                         float* out, hipStream_t stream) {
+  kvq_status st = check_vq(vq);
+  if (st != KVQ_OK) return st;
+  st = check_smooth(smooth);
+  if (st != KVQ_OK) return st;
+  if (n_books < 0 || n_seq < 0 || n_rows < 0) return KVQ_ERR_SHAPE;
+  if (n_books == 0 || n_seq == 0 || n_rows == 0) return KVQ_OK;
+  if (!codes || !codebooks || !out) return KVQ_ERR_NULL;
+  if (!aligned16(codes) || !aligned16(codebooks) || !aligned16(out)) return KVQ_ERR_ALIGN;
+  if (n_seq > ((int64_t)1 << 40) / n_rows) return KVQ_ERR_SHAPE;
+  const int64_t n_per_book = n_seq * n_rows;
+  if (n_per_book > ((int64_t)1 << 40) / n_books) return KVQ_ERR_SHAPE;
+  return hip_status(kvq::launch_reconstruct(codes, codebooks, out, n_books, n_per_book,
+                                            vq->head_dim, vq->n_groups, vq->n_stages,
+                                            vq->n_codewords, 1, n_rows, to_smooth(smooth),
                                             stream));
 }
 
@@ -181,14 +271,19 @@ kvq_status kvq_window_flush_workspace_size(const kvq_vq_desc* vq, size_t* bytes)
   return KVQ_OK;
 }
 
-kvq_status kvq_window_flush(const kvq_vq_desc* vq, int32_t batch, int32_t n_kv_heads,
-                            int32_t window_cap, int32_t n_window, int32_t n_flush,
-                            uint16_t* k_win, uint16_t* v_win, int32_t code_cap, int32_t n_code,
-                            uint8_t* k_codes, uint8_t* v_codes, const float* k_cb,
-                            const float* v_cb, uint32_t flags, void* workspace, size_t ws_bytes,
-                            hipStream_t stream) {
+static kvq_status window_flush_common(const kvq_vq_desc* vq, int32_t batch, int32_t n_kv_heads,
+                                      int32_t window_cap, int32_t n_window, int32_t n_flush,
+                                      uint16_t* k_win, uint16_t* v_win, int32_t code_cap,
+                                      int32_t n_code, uint8_t* k_codes, uint8_t* v_codes,
+                                      const float* k_cb, const float* v_cb,
+                                      const kvq_smooth_desc* k_smooth, uint32_t flags,
+                                      void* workspace, size_t ws_bytes, hipStream_t stream) {
   kvq_status st = check_vq(vq);
   if (st != KVQ_OK) return st;
+  if (k_smooth) {
+    st = check_smooth(k_smooth);
+    if (st != KVQ_OK) return st;
+  }
   if (flags & ~KVQ_CODEBOOKS_PACKED) return KVQ_ERR_SHAPE;
   if (batch < 1 || n_kv_heads < 1 || window_cap < 1 || code_cap < 0) return KVQ_ERR_SHAPE;
   if (n_window < 0 || n_window > window_cap) return KVQ_ERR_SHAPE;
@@ -214,14 +309,39 @@ kvq_status kvq_window_flush(const kvq_vq_desc* vq, int32_t batch, int32_t n_kv_h
   uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
   const int packed = (flags & KVQ_CODEBOOKS_PACKED) ? 1 : 0;
   hipError_t e = kvq::launch_encode(k_win, (int)KVQ_F16, D, G, S, C, 1, units, window_cap, n_flush,
-                                    k_cb, k_codes, code_cap, n_code, 0, 0, packed, ws, stream);
+                                    k_cb, k_codes, code_cap, n_code, 0, 0, packed, ws,
+                                    to_smooth(k_smooth), stream);
   if (e == hipSuccess)
     e = kvq::launch_encode(v_win, (int)KVQ_F16, D, G, S, C, 1, units, window_cap, n_flush, v_cb,
                            v_codes, code_cap, n_code, 0, 0, packed, mfma ? ws + half : nullptr,
-                           stream);
+                           kvq::Smooth{}, stream);
   if (e == hipSuccess)
     e = kvq::launch_window_compact(k_win, v_win, units, D, window_cap, n_window, n_flush, stream);
   return hip_status(e);
+}
+
+kvq_status kvq_window_flush(const kvq_vq_desc* vq, int32_t batch, int32_t n_kv_heads,
+                            int32_t window_cap, int32_t n_window, int32_t n_flush,
+                            uint16_t* k_win, uint16_t* v_win, int32_t code_cap, int32_t n_code,
+                            uint8_t* k_codes, uint8_t* v_codes, const float* k_cb,
+                            const float* v_cb, uint32_t flags, void* workspace, size_t ws_bytes,
+                            hipStream_t stream) {
+  return window_flush_common(vq, batch, n_kv_heads, window_cap, n_window, n_flush, k_win, v_win,
+                             code_cap, n_code, k_codes, v_codes, k_cb, v_cb, nullptr, flags,
+                             workspace, ws_bytes, stream);
+}
+
+kvq_status kvq_window_flush_smooth(const kvq_vq_desc* vq, int32_t batch, int32_t n_kv_heads,
+                                   int32_t window_cap, int32_t n_window, int32_t n_flush,
+                                   uint16_t* k_win, uint16_t* v_win, int32_t code_cap,
+                                   int32_t n_code, uint8_t* k_codes, uint8_t* v_codes,
+                                   const float* k_cb, const float* v_cb,
+                                   const kvq_smooth_desc* k_smooth, uint32_t flags,
+                                   void* workspace, size_t ws_bytes, hipStream_t stream) {
+  if (!k_smooth) return KVQ_ERR_NULL;
+  return window_flush_common(vq, batch, n_kv_heads, window_cap, n_window, n_flush, k_win, v_win,
+                             code_cap, n_code, k_codes, v_codes, k_cb, v_cb, k_smooth, flags,
+                             workspace, ws_bytes, stream);
 }
 
 kvq_status kvq_attend_workspace_size(const kvq_attn_desc* a, size_t* bytes) {
@@ -233,13 +353,18 @@ kvq_status kvq_attend_workspace_size(const kvq_attn_desc* a, size_t* bytes) {
   return KVQ_OK;
 }
 
-kvq_status kvq_attend_decode(const kvq_attn_desc* a, const float* q, const uint8_t* k_codes,
-                             const uint8_t* v_codes, const float* k_cb, const float* v_cb,
-                             const uint16_t* k_win, const uint16_t* v_win, float* out,
-                             void* workspace, size_t ws_bytes, hipStream_t stream) {
+static kvq_status attend_common(const kvq_attn_desc* a, const float* q, const uint8_t* k_codes,
+                                const uint8_t* v_codes, const float* k_cb, const float* v_cb,
+                                const kvq_smooth_desc* k_smooth, const uint16_t* k_win,
+                                const uint16_t* v_win, float* out, void* workspace,
+                                size_t ws_bytes, hipStream_t stream) {
   kvq::AttnPlan plan;
   kvq_status st = check_attn(a, &plan);
   if (st != KVQ_OK) return st;
+  if (k_smooth) {
+    st = check_smooth(k_smooth);
+    if (st != KVQ_OK) return st;
+  }
   if (!q || !out || !workspace) return KVQ_ERR_NULL;
   if (!aligned16(q) || !aligned16(out) || !aligned16(workspace)) return KVQ_ERR_ALIGN;
   if (a->n_code_tokens > 0) {
@@ -261,7 +386,26 @@ kvq_status kvq_attend_decode(const kvq_attn_desc* a, const float* q, const uint8
                                        a->code_stride ? a->code_stride : a->n_code_tokens,
                                        a->window_stride ? a->window_stride : a->n_window,
                                        scale, q, k_codes, v_codes, k_cb, v_cb, k_win,
-                                       v_win, out, workspace, stream));
+                                       v_win, out, workspace, to_smooth(k_smooth), stream));
+}
+
+kvq_status kvq_attend_decode(const kvq_attn_desc* a, const float* q, const uint8_t* k_codes,
+                             const uint8_t* v_codes, const float* k_cb, const float* v_cb,
+                             const uint16_t* k_win, const uint16_t* v_win, float* out,
+                             void* workspace, size_t ws_bytes, hipStream_t stream) {
+  return attend_common(a, q, k_codes, v_codes, k_cb, v_cb, nullptr, k_win, v_win, out, workspace,
+                       ws_bytes, stream);
+}
+
+kvq_status kvq_attend_decode_smooth(const kvq_attn_desc* a, const float* q,
+                                    const uint8_t* k_codes, const uint8_t* v_codes,
+                                    const float* k_cb, const float* v_cb,
+                                    const kvq_smooth_desc* k_smooth, const uint16_t* k_win,
+                                    const uint16_t* v_win, float* out, void* workspace,
+                                    size_t ws_bytes, hipStream_t stream) {
+  if (!k_smooth) return KVQ_ERR_NULL;
+  return attend_common(a, q, k_codes, v_codes, k_cb, v_cb, k_smooth, k_win, v_win, out,
+                       workspace, ws_bytes, stream);
 }
 
 }  // extern "C"

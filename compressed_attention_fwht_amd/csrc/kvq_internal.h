@@ -29,6 +29,13 @@ struct AttnPlan {
   size_t lut_bytes, part_bytes, ws_bytes;
 };
 
+// Dual-transform smoothing factors [n_books][n_scale][D] (f == nullptr: none);
+// sequence n of a book uses row n % n_scale.
+struct Smooth {
+  const float* f = nullptr;
+  int64_t n_scale = 1;
+};
+
 AttnPlan attn_plan(int B, int Hq, int Hkv, int D, int S, int G, int C, int Tc, int W);
 
 hipError_t launch_rotate(const void* x, int xt, float* y, int64_t n_rows, int dim, hipStream_t s);
@@ -38,18 +45,24 @@ bool encode_mfma_eligible(int D, int G, int S, int C, int xt);
 hipError_t launch_encode(const void* x, int xt, int D, int G, int S, int C, int64_t n_books,
                          int64_t n_seq, int64_t seq_stride, int64_t n_rows, const float* cb,
                          uint8_t* codes, int64_t code_stride, int64_t code_row0, int pre_rotated,
-                         int force_generic, int packed, void* ws, hipStream_t st);
+                         int force_generic, int packed, void* ws, Smooth sm, hipStream_t st);
 
+// With sm.f the output is unrotated and multiplied by the factor row of each
+// vector's sequence (n_rows vectors per sequence).
 hipError_t launch_reconstruct(const uint8_t* codes, const float* cb, float* out, int64_t n_books,
                               int64_t n_per_book, int D, int G, int S, int C, int unrotate,
-                              hipStream_t s);
+                              int64_t n_rows, Smooth sm, hipStream_t s);
 
 hipError_t launch_attend(const AttnPlan& p, int B, int Hq, int Hkv, int D, int S, int G, int C,
                          int Tc, int W, int cstride, int wstride, float scale, const float* q,
                          const uint8_t* kc,
                          const uint8_t* vc, const float* kcb, const float* vcb,
                          const uint16_t* kw, const uint16_t* vw, float* out, void* ws,
-                         hipStream_t st);
+                         Smooth ksm, hipStream_t st);
+
+hipError_t launch_smooth_calibrate(const void* x, int xt, int D, int64_t n_books, int64_t n_seq,
+                                   int64_t seq_stride, int64_t n_rows, int64_t n_scale, float* f,
+                                   hipStream_t st);
 
 hipError_t launch_window_append(const uint16_t* kn, const uint16_t* vn, uint16_t* kw,
                                 uint16_t* vw, int64_t units, int D, int wcap, int row,

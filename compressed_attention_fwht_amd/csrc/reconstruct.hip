@@ -21,7 +21,8 @@ namespace kvq {
 template <int D>
 __global__ __launch_bounds__(256) void reconstruct_kernel(
     const uint8_t* __restrict__ codes, const float* __restrict__ cb, float* __restrict__ out,
-    int64_t n_books, int64_t n_per_book, int G, int S, int C, int dsub, int unrotate) {
+    int64_t n_books, int64_t n_per_book, int G, int S, int C, int dsub, int unrotate,
+    const float* __restrict__ smooth, int64_t n_scale, int64_t n_rows) {
   constexpr int L = D / 8;
   constexpr int ROWS_PER_WAVE = 64 / L;
   constexpr int UNR = 4;
@@ -79,6 +80,15 @@ __global__ __launch_bounds__(256) void reconstruct_kernel(
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] *= sc;
       }
+      if (smooth != nullptr && vec < n_total) {   // dual transform undone: times the factors
+        const int64_t book = vec / n_per_book;
+        const int64_t seq = (vec - book * n_per_book) / n_rows;
+        const float4* lp = reinterpret_cast<const float4*>(
+            smooth + (book * n_scale + seq % n_scale) * D + col * 8);
+        const float4 a = lp[0], c = lp[1];
+        v[0] *= a.x; v[1] *= a.y; v[2] *= a.z; v[3] *= a.w;
+        v[4] *= c.x; v[5] *= c.y; v[6] *= c.z; v[7] *= c.w;
+      }
       if (vec < n_total) {
         float4* o = reinterpret_cast<float4*>(out + vec * D + col * 8);
         o[0] = make_float4(v[0], v[1], v[2], v[3]);
@@ -90,22 +100,17 @@ __global__ __launch_bounds__(256) void reconstruct_kernel(
 
 hipError_t launch_reconstruct(const uint8_t* codes, const float* cb, float* out, int64_t n_books,
                               int64_t n_per_book, int D, int G, int S, int C, int unrotate,
-                              hipStream_t s) {
+                              int64_t n_rows, Smooth sm, hipStream_t s) {
   const int64_t n = n_books * n_per_book;
   if (n == 0) return hipSuccess;
   const int dsub = D / G;
   const int rows_per_block = 4 * (64 / (D / 8)) * 4;      // 4 waves, 4 vectors per lane
   int64_t blocks = (n + rows_per_block - 1) / rows_per_block;
   if (blocks > 16384) blocks = 16384;
-  if (D == 64)
-    reconstruct_kernel<64><<<dim3((unsigned)blocks), 256, 0, s>>>(codes, cb, out, n_books, n_per_book,
-                                                                  G, S, C, dsub, unrotate);
-  else if (D == 128)
-    reconstruct_kernel<128><<<dim3((unsigned)blocks), 256, 0, s>>>(codes, cb, out, n_books, n_per_book,
-                                                                   G, S, C, dsub, unrotate);
-  else
-    reconstruct_kernel<256><<<dim3((unsigned)blocks), 256, 0, s>>>(codes, cb, out, n_books, n_per_book,
-                                                                   G, S, C, dsub, unrotate);
+  auto kern = D == 64 ? reconstruct_kernel<64> : D == 128 ? reconstruct_kernel<128>
+                                                          : reconstruct_kernel<256>;
+  kern<<<dim3((unsigned)blocks), 256, 0, s>>>(codes, cb, out, n_books, n_per_book, G, S, C, dsub,
+                                              unrotate, sm.f, sm.n_scale, n_rows);
   return hipGetLastError();
 }
 

@@ -214,6 +214,86 @@ KVQ_API kvq_status kvq_window_flush(const kvq_vq_desc* vq, int32_t batch, int32_
                             const float* k_cb, const float* v_cb, uint32_t flags,
                             void* workspace, size_t ws_bytes, hipStream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * Dual transform ("VeloxQuant-MLX 0.5.1", VecInfer section: per-channel smooth
+ * scaling by lambda_i = sqrt(max |K_i|) ahead of the Walsh-Hadamard rotation,
+ * its inverse absorbed into the query).  Keys are coded as H_D (k / lambda)
+ * (channel-wise division); decode multiplies the query by lambda before
+ * rotating it, so q . k is unchanged.  Values and the fp16 window keep the
+ * plain path (the window holds the original keys and is scored with the
+ * original query).
+ *
+ * Factors live in a float32 device array [n_books][n_scale][D]: the vectors of
+ * sequence n of book b use row n % n_scale of book b.  For a cache laid out
+ * [B][Hkv][T][D] (sequence n = b * Hkv + kv), n_scale = Hkv gives one row per
+ * KV head shared by the batch, n_scale = B * Hkv one per (sequence, KV head)
+ * and n_scale = 1 one per book.  Factors must be positive and finite; other
+ * values give unspecified codes and outputs (no fault).
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  const float* factors;    /* [n_books][n_scale][D] float32, device, 16-byte aligned */
+  int32_t n_scale;         /* >= 1 */
+} kvq_smooth_desc;
+
+/* Calibrates factors from the rows [0, n_rows) of every sequence of
+ * x [n_books][n_seq][seq_stride][D] (type xt, original domain):
+ * factors[b][j][i] = sqrt(max |x[b][n][t][i]|) over every sequence n with
+ * n % n_scale == j and every row t < n_rows, rounded to float32; a channel
+ * whose maximum is 0, or a row j no sequence maps to, gets 1.  A NaN in x
+ * gives NaN factors in its channel.  factors: [n_books][n_scale][D] float32
+ * (output; also the kernels' reduction target, so it may not overlap x).
+ * Requires head_dim in {64, 128, 256}, n_scale >= 1, n_rows <= seq_stride;
+ * n_books == 0 is a no-op; n_seq == 0 or n_rows == 0 writes ones. */
+KVQ_API kvq_status kvq_smooth_calibrate(const void* x, kvq_dtype xt, int32_t head_dim,
+                                int64_t n_books, int64_t n_seq, int64_t seq_stride,
+                                int64_t n_rows, int32_t n_scale, float* factors,
+                                hipStream_t stream);
+
+/* kvq_encode of x / factors: each vector divided channel-wise by its
+ * sequence's factor row before the rotation and the residual stages.  Same
+ * arguments, layouts, workspace and flags as kvq_encode except that
+ * KVQ_INPUT_PRE_ROTATED is refused (the division acts on the original
+ * channels).  smooth->factors: [n_books][n_scale][D]. */
+KVQ_API kvq_status kvq_encode_smooth(const void* x, kvq_dtype xt, const kvq_vq_desc* vq,
+                             int64_t n_books, int64_t n_seq, int64_t seq_stride,
+                             int64_t n_rows, const kvq_smooth_desc* smooth,
+                             const float* codebooks, uint8_t* codes, uint32_t flags,
+                             void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* Original-domain reconstruction of codes made by kvq_encode_smooth:
+ * out[b][n][t] = factors[b][n % n_scale] * (H_D sum of the chosen entries),
+ * the unrotation first, then the channel-wise product.
+ * codes: [n_books][n_seq][n_rows][S][G] uint8; out: [n_books][n_seq][n_rows][D]
+ * float32.  Codes >= C read entry C-1 (no fault). */
+KVQ_API kvq_status kvq_decode_reconstruct_smooth(const uint8_t* codes, const kvq_vq_desc* vq,
+                                         int64_t n_books, int64_t n_seq, int64_t n_rows,
+                                         const float* codebooks,
+                                         const kvq_smooth_desc* smooth, float* out,
+                                         hipStream_t stream);
+
+/* kvq_attend_decode over a cache whose coded keys were smoothed: the table
+ * of KV head kv of sequence b is built from H_D (factors[(b * Hkv + kv) %
+ * n_scale] * q) (one book: factors [n_scale][D]).  Window keys are original;
+ * everything else as kvq_attend_decode, same workspace size. */
+KVQ_API kvq_status kvq_attend_decode_smooth(const kvq_attn_desc* a, const float* q,
+                                    const uint8_t* k_codes, const uint8_t* v_codes,
+                                    const float* k_cb, const float* v_cb,
+                                    const kvq_smooth_desc* k_smooth,
+                                    const uint16_t* k_win, const uint16_t* v_win,
+                                    float* out, void* workspace, size_t ws_bytes,
+                                    hipStream_t stream);
+
+/* kvq_window_flush whose flushed keys are coded as by kvq_encode_smooth, the
+ * window of (sequence b, KV head kv) using factor row (b * Hkv + kv) %
+ * n_scale (one book: factors [n_scale][D]); values as in kvq_window_flush. */
+KVQ_API kvq_status kvq_window_flush_smooth(const kvq_vq_desc* vq, int32_t batch,
+                                   int32_t n_kv_heads, int32_t window_cap, int32_t n_window,
+                                   int32_t n_flush, uint16_t* k_win, uint16_t* v_win,
+                                   int32_t code_cap, int32_t n_code, uint8_t* k_codes,
+                                   uint8_t* v_codes, const float* k_cb, const float* v_cb,
+                                   const kvq_smooth_desc* k_smooth, uint32_t flags,
+                                   void* workspace, size_t ws_bytes, hipStream_t stream);
+
 /* Static description of a status code. */
 KVQ_API const char* kvq_status_string(kvq_status status);
 

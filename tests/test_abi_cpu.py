@@ -186,3 +186,58 @@ def test_window_flush_argument_errors():
     assert _flush(flags=0x8, kw=0) == NULL
     assert kvq.window_flush_workspace_size(128, 16, 2, 256) == 2 * 16 * 2 * 20480
     assert kvq.window_flush_workspace_size(64, 1, 2, 256) == 0   # generic kernel
+
+
+def _sd(f=FAKE, n=8):
+    return kvq.SmoothDesc(f, n)
+
+
+def test_smooth_calibrate_argument_errors():
+    L = kvq.lib
+    cal = lambda x=FAKE, xt=1, D=128, nb=1, ns=8, st=64, nr=64, nsc=8, f=FAKE: \
+        L.kvq_smooth_calibrate(x, xt, D, nb, ns, st, nr, nsc, f, None)
+    assert cal(xt=7) == DTYPE
+    assert cal(D=96) == SHAPE
+    assert cal(nsc=0) == SHAPE
+    assert cal(nr=65) == SHAPE                           # rows beyond the stride
+    assert cal(nb=-1) == SHAPE
+    assert cal(nb=0, f=0) == OK                          # nothing to write
+    assert cal(f=0) == NULL
+    assert cal(x=0) == NULL
+    assert cal(f=FAKE + 4) == ALIGN
+    assert cal(x=FAKE + 2) == ALIGN
+    assert cal(f=FAKE + 64 * 128) == SHAPE               # output inside the input
+
+
+def test_encode_smooth_argument_errors():
+    L = kvq.lib
+    vq = _vq()
+    enc = lambda sd, flags=0, x=FAKE: L.kvq_encode_smooth(x, 1, ctypes.byref(vq), 1, 1, 64, 64, sd,
+                                                          FAKE, FAKE, flags, FAKE, 1 << 30, None)
+    assert enc(None) == NULL
+    assert enc(ctypes.byref(_sd(f=0))) == NULL
+    assert enc(ctypes.byref(_sd(n=0))) == SHAPE
+    assert enc(ctypes.byref(_sd(f=FAKE + 4))) == ALIGN
+    assert enc(ctypes.byref(_sd()), flags=0x1) == UNSUP   # division needs the original channels
+    assert enc(ctypes.byref(_sd()), x=0) == NULL
+
+
+def test_reconstruct_attend_flush_smooth_argument_errors():
+    L = kvq.lib
+    vq = _vq()
+    rec = lambda sd, nr=64, out=FAKE: L.kvq_decode_reconstruct_smooth(
+        FAKE, ctypes.byref(vq), 1, 2, nr, FAKE, sd, out, None)
+    assert rec(None) == NULL
+    assert rec(ctypes.byref(_sd(n=-1))) == SHAPE
+    assert rec(ctypes.byref(_sd()), nr=-1) == SHAPE
+    assert rec(ctypes.byref(_sd()), out=0) == NULL
+    assert rec(ctypes.byref(_sd()), nr=0, out=0) == OK      # empty: no-op
+    a = kvq.AttnDesc(1, 32, 8, 1024, 16, _vq(), 0.0, 0, 0)
+    att = lambda sd: L.kvq_attend_decode_smooth(ctypes.byref(a), FAKE, FAKE, FAKE, FAKE, FAKE, sd,
+                                                FAKE, FAKE, FAKE, FAKE, 1 << 30, None)
+    assert att(None) == NULL
+    assert att(ctypes.byref(_sd(f=FAKE + 8))) == ALIGN
+    fl = lambda sd: L.kvq_window_flush_smooth(ctypes.byref(vq), 1, 2, 32, 32, 16, FAKE, FAKE, 100,
+                                              0, FAKE, FAKE, FAKE, FAKE, sd, 0, FAKE, 1 << 30, None)
+    assert fl(None) == NULL
+    assert fl(ctypes.byref(_sd(n=0))) == SHAPE
