@@ -18,7 +18,10 @@ HBM.
 Prints ONE JSON line.  ``value`` is the decode effective bandwidth (code +
 window + LUT bytes over the decode call's time); the encode throughput and
 its fraction of the bf16 MFMA peak are reported beside it, and again for the
-32-layer bulk prefill encode.  ``roofline`` is for the kernel that takes the
+32-layer bulk prefill encode; the streaming calls (append, flush) and the
+dual-transform calls (factor calibration, smoothed key encode, decode with
+the factors folded into the query) are timed on the same layer after the
+step.  ``roofline`` is for the kernel that takes the
 most time in the step; its HBM ``traffic`` comes from the rocprofv3 counter
 summary committed for that kernel, and is null when the kernel's source has
 changed since those counters were taken.
@@ -247,6 +250,7 @@ def main():
                               "decode": [round(float(np.percentile(att_ms, p)), 5) for p in (10, 90)]},
         "roofline": roof,
     }
+    res["smooth"] = smooth_calls(torch, kvq, x, cb, q, kc, vc, kw, vw, w, dev, flush)
     del x, recon, flush_buf
     torch.cuda.empty_cache()
     if not args.no_prefill:
@@ -303,6 +307,52 @@ def prefill_encode(torch, kvq, synth, dev, reps=5):
             "value": round(n_vec / t / 1e6, 2), "unit": "Mvec/s", "ms": round(t * 1e3, 4),
             "vectors": n_vec, "pct_bf16_mfma_peak": round(100 * flops / t / 1e12 / BF16_PEAK_TFLOPS, 3),
             "reps": reps}
+
+
+def smooth_calls(torch, kvq, x, cb, q, kc, vc, kw, vw, w, dev, flush, reps=20):
+    """The dual transform on the same layer: calibrating the key factors
+    (one row per KV head) over the coded tokens, encoding the keys with and
+    without the division, and decode with the factors folded into the query.
+    Each timed call follows a cache-evicting write, like the step."""
+    B, Hkv, Hq, D, W = w.batch, w.n_kv_heads, w.n_q_heads, w.head_dim, w.window
+    S, G, C, Tc = w.n_stages, w.n_groups, w.n_codewords, w.code_tokens
+    xk, cbk = x[:1], cb[:1]
+    lam = torch.empty((1, Hkv, D), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(kvq.encode_workspace_size(D, G, S, C, 1), 16), dtype=torch.uint8,
+                     device=dev)
+    codes = torch.empty((1, B * Hkv, Tc, S, G), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    att_ws = torch.empty(max(kvq.attend_workspace_size(B, Hq, Hkv, D, Tc, W, S, G, C), 16),
+                         dtype=torch.uint8, device=dev)
+    kvq.encode(xk, cbk, n_rows=Tc, codes=codes, workspace=ws)          # packs the K books
+    calls = {
+        "calibrate": lambda: kvq.smooth_calibrate(xk, Hkv, n_rows=Tc, out=lam),
+        "encode_k_smooth": lambda: kvq.encode(xk, cbk, n_rows=Tc, codes=codes, workspace=ws,
+                                              packed=True, smooth=lam),
+        "encode_k_plain": lambda: kvq.encode(xk, cbk, n_rows=Tc, codes=codes, workspace=ws,
+                                             packed=True),
+        "decode_smooth": lambda: kvq.attend_decode(q, kc, vc, cb[0], cb[1], kw, vw, out=out,
+                                                   workspace=att_ws, k_smooth=lam[0]),
+    }
+    ms = {k: [] for k in calls}
+    for i in range(reps + 3):
+        for k, f in calls.items():
+            flush(i)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            f()
+            e1.record()
+            torch.cuda.synchronize()
+            if i >= 3:
+                ms[k].append(e0.elapsed_time(e1))
+    med = {k: float(np.median(v)) for k, v in ms.items()}
+    cal_bytes = B * Hkv * Tc * D * 2
+    return {"calibrate_us": round(med["calibrate"] * 1e3, 2),
+            "calibrate_gbs": round(cal_bytes / (med["calibrate"] * 1e-3) / 1e9, 1),
+            "encode_k_smooth_us": round(med["encode_k_smooth"] * 1e3, 2),
+            "encode_k_plain_us": round(med["encode_k_plain"] * 1e3, 2),
+            "decode_smooth_us": round(med["decode_smooth"] * 1e3, 2),
+            "note": f"keys of the layer ({B * Hkv * Tc} vectors), factors one row per KV head"}
 
 
 def stream_calls(torch, kvq, inp, w, dev, reps=20, wcap=192, n_flush=64):

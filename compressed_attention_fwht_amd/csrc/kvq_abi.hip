@@ -195,7 +195,7 @@ kvq_status kvq_smooth_calibrate(const void* x, kvq_dtype xt, int32_t head_dim, i
     if (!x) return KVQ_ERR_NULL;
     if (!aligned16(x)) return KVQ_ERR_ALIGN;
     if (n_seq > ((int64_t)1 << 40) / seq_stride / n_books / head_dim) return KVQ_ERR_SHAPE;
-    const int64_t row_blocks = (n_rows + 511) / 512;
+    const int64_t row_blocks = (n_rows + 63) / 64;     // the smallest block covers 64 rows
     if (n_books * n_seq > 0x7fffffffLL / row_blocks) return KVQ_ERR_UNSUPPORTED;
     const int esz = xt == KVQ_F32 ? 4 : 2;
     const uintptr_t xa = (uintptr_t)x, fa = (uintptr_t)factors;
