@@ -7,7 +7,8 @@ never imports it, and it never imports the product.
 from .kvq_oracle import (hadamard_matrix, fwht, nearest, rvq_encode, reconstruct_rot,
                          reconstruct, attend, attend_dense, lse_merge, window_append,
                          window_flush, smooth_factors, smooth_rows, smooth_keys, smooth_query,
-                         smooth_encode, reconstruct_smooth, code_bytes_per_vector,
+                         smooth_encode, reconstruct_smooth, lloyd_update, fit_codebooks,
+                         code_bytes_per_vector,
                          compression_ratio_vs_fp16)
 from .check import (check_codes, check_recon, check_attn, CODE_REL_TOL, RECON_ATOL,
                     ATTN_ATOL, ATTN_REL_L2)

@@ -35,6 +35,9 @@ Sources (page title -- section):
          square root of its largest magnitude before the Walsh-Hadamard
          rotation; the inverse folded into the query so the scores are
          unchanged).
+  Codebook fitting: [VI] VecInfer section (codebooks are K-means codebooks
+         trained beforehand; the allocator list names train_codebook);
+         [VQKV] 2. Methodology (the residual codebooks are trained).
 
 Parity status of each function is stated in its docstring; every function is
 pinned by ``tests/test_oracle_pins.py`` against closed forms, library routines
@@ -47,7 +50,8 @@ import numpy as np
 __all__ = ["hadamard_matrix", "fwht", "nearest", "rvq_encode", "reconstruct_rot",
            "reconstruct", "attend", "attend_dense", "lse_merge", "window_append",
            "window_flush", "smooth_factors", "smooth_keys", "smooth_query", "smooth_encode",
-           "reconstruct_smooth", "smooth_rows", "code_bytes_per_vector",
+           "reconstruct_smooth", "smooth_rows", "lloyd_update", "fit_codebooks",
+           "code_bytes_per_vector",
            "compression_ratio_vs_fp16"]
 
 
@@ -323,6 +327,54 @@ def reconstruct_smooth(codes, codebooks, lam) -> np.ndarray:
     the unrotated reconstruction (the rotation is undone first, then the
     division).  lam broadcasts to the output [..., D]."""
     return reconstruct(codes, codebooks) * np.asarray(lam, dtype=np.float64)
+
+
+# ----------------------------------------------------------------------------
+# Codebook fitting  [VI VecInfer: K-means codebooks per sub-vector, trained
+#       before use ("train_codebook")], [VQKV 2. Methodology: the stage
+#       codebooks are trained]
+# ----------------------------------------------------------------------------
+def lloyd_update(r, z, cb):
+    """One K-means centroid update: entry c becomes the mean of the vectors
+    r [N][dsub] assigned to it (z [N]); an entry with no vector keeps its
+    value.  cb [C][dsub] is not modified; returns the new float64 entries."""
+    r = np.asarray(r, dtype=np.float64)
+    new = np.array(cb, dtype=np.float64, copy=True)
+    for c in range(new.shape[0]):
+        members = r[np.asarray(z) == c]
+        if members.shape[0] > 0:
+            new[c] = members.mean(axis=0)
+    return new
+
+
+def fit_codebooks(x, init, n_iter: int, *, rotate: bool = True, with_history: bool = False):
+    """Fit residual product codebooks by K-means (Lloyd), stage by stage.
+
+    x: [N][D] sample vectors (original domain, or rotated when ``rotate`` is
+    False); init: [S][G][C][dsub] starting entries.  For each stage s and each
+    group g, on the residuals r that the earlier (already fitted) stages
+    leave: n_iter times {assign every vector to its nearest entry (squared
+    distance, lowest index on ties); replace every entry by the mean of its
+    vectors (entries with none keep theirs)}; then assign once more with the
+    fitted entries and subtract them, giving the next stage's residuals.
+    Returns the fitted float64 codebooks (and, with ``with_history``, the
+    per-iteration distortion sum over vectors of |r - C[z]|^2 per (s, g)
+    measured at each assignment, a list [S][G][n_iter + 1])."""
+    cb = np.array(init, dtype=np.float64, copy=True)
+    S, G, C, dsub = cb.shape
+    y = fwht(x) if rotate else np.asarray(x, dtype=np.float64)
+    hist = [[[] for _ in range(G)] for _ in range(S)]
+    for g in range(G):
+        r = y[:, g * dsub:(g + 1) * dsub].copy()
+        for s in range(S):
+            for _ in range(n_iter):
+                z, d = nearest(r, cb[s, g])
+                hist[s][g].append(float(d[np.arange(len(z)), z].sum()))
+                cb[s, g] = lloyd_update(r, z, cb[s, g])
+            z, d = nearest(r, cb[s, g])
+            hist[s][g].append(float(d[np.arange(len(z)), z].sum()))
+            r = r - cb[s, g][z]
+    return (cb, hist) if with_history else cb
 
 
 def lse_merge(parts):

@@ -557,3 +557,66 @@ def test_streaming_with_smoothing_equals_one_shot_smooth_encode():
     v_once = rvq_encode(tv[:, :, :nc].astype(np.float64).reshape(-1, D), cb)
     assert np.array_equal(vc[:, :, :nc].reshape(-1, S, G), v_once)
     assert not np.array_equal(k_once, rvq_encode(xk.reshape(-1, D), cb))
+
+
+# ---------------------------------------------------------- codebook fitting
+# "VeloxQuant-MLX 0.5.1", VecInfer section: K-means codebooks trained before
+# use; "VQKV" summary, 2. Methodology: trained stage codebooks.
+def test_lloyd_update_hand_values():
+    """Means worked by hand; an entry that attracts no vector keeps its value."""
+    r = np.array([[0.0], [1.0], [10.0], [11.0]])
+    new = oracle.lloyd_update(r, np.array([0, 0, 1, 1]), np.array([[0.0], [10.0], [100.0]]))
+    assert np.array_equal(new, [[0.5], [10.5], [100.0]])
+
+
+@pytest.mark.parametrize("rotate", [False, True])
+def test_fit_single_stage_equals_scipy_kmeans2(rotate):
+    """One stage, one group: Lloyd iterations from a given start equal
+    scipy.cluster.vq.kmeans2 (minit='matrix'), including kept empty entries."""
+    from scipy.cluster.vq import kmeans2
+    rng = np.random.default_rng(31)
+    x = rng.standard_normal((1500, 8)) * np.array([1, 2, 3, 1, 1, .5, 1, 4])
+    init = rng.standard_normal((1, 1, 24, 8))
+    init[0, 0, 5] = 50.0                                   # never nearest: stays put
+    fitted = oracle.fit_codebooks(x, init, 6, rotate=rotate)
+    y = fwht(x) if rotate else x
+    with np.errstate(all="ignore"), __import__("warnings").catch_warnings():
+        __import__("warnings").simplefilter("ignore")
+        ref, _ = kmeans2(y, init[0, 0].copy(), iter=6, minit="matrix", missing="warn")
+    assert np.allclose(fitted[0, 0], ref, rtol=0, atol=1e-12)
+    assert np.array_equal(fitted[0, 0, 5], init[0, 0, 5])
+
+
+def test_fit_groups_independent_and_stages_on_residuals():
+    """Groups fit on their own column slices; stage 1 fits the residuals the
+    fitted stage 0 leaves (assignment with the final stage-0 entries)."""
+    from scipy.cluster.vq import kmeans2, vq
+    import warnings
+    rng = np.random.default_rng(32)
+    x = rng.standard_normal((900, 16))
+    init = rng.standard_normal((2, 2, 12, 8)) * np.array([1.0, 0.5])[:, None, None, None]
+    fitted = oracle.fit_codebooks(x, init, 4, rotate=False)
+    with warnings.catch_warnings():
+        warnings.simplefilter("ignore")
+        for g in range(2):
+            y = x[:, 8 * g:8 * g + 8]
+            c0, _ = kmeans2(y, init[0, g].copy(), iter=4, minit="matrix", missing="warn")
+            z0, _ = vq(y, c0)
+            c1, _ = kmeans2(y - c0[z0], init[1, g].copy(), iter=4, minit="matrix", missing="warn")
+            assert np.allclose(fitted[0, g], c0, atol=1e-12)
+            assert np.allclose(fitted[1, g], c1, atol=1e-12)
+
+
+def test_fit_distortion_never_increases():
+    """Lloyd's property: each assignment's distortion is at most the one
+    before it, per (stage, group)."""
+    rng = np.random.default_rng(33)
+    x = rng.laplace(size=(2000, 32)) * np.exp(rng.uniform(-1, 1, 32))
+    init = rng.standard_normal((2, 4, 32, 8))
+    _, hist = oracle.fit_codebooks(x, init, 8, with_history=True)
+    for s in range(2):
+        for g in range(4):
+            h = np.array(hist[s][g])
+            assert len(h) == 9
+            assert np.all(np.diff(h) <= 1e-9 * h[0]), h
+            assert h[-1] < h[0]
