@@ -15,6 +15,7 @@ Calls (same names as the C ABI):
   attend_decode(q, k_codes, v_codes, k_cb, v_cb, k_win, v_win) -> f32 [B][Hq][D]
   window_append / window_flush               streaming fp16 window -> codes
   smooth_calibrate(k, n_scale)               dual-transform factors f32 [books][n_scale][D]
+  codebook_fit(x, init, n_iter)              K-means codebooks [S][G][C][dsub] f32 on a sample
   (encode, decode_reconstruct, attend_decode and window_flush take the factors
   as ``smooth=`` / ``k_smooth=`` and then call the *_smooth entry points)
 """
@@ -25,7 +26,8 @@ import os
 
 __all__ = ["KvqError", "LIB_PATH", "lib", "rotate", "encode", "encode_workspace_size",
            "decode_reconstruct", "attend_decode", "attend_workspace_size", "window_append",
-           "window_flush", "window_flush_workspace_size", "smooth_calibrate", "EXPORTS",
+           "window_flush", "window_flush_workspace_size", "smooth_calibrate", "codebook_fit",
+           "codebook_fit_workspace_size", "EXPORTS",
            "KVQ_INPUT_PRE_ROTATED", "SmoothDesc",
            "KVQ_UNROTATE", "KVQ_ENCODE_GENERIC", "KVQ_CODEBOOKS_PACKED", "VqDesc", "AttnDesc",
            "status_string"]
@@ -42,7 +44,8 @@ EXPORTS = ("kvq_rotate", "kvq_encode_workspace_size", "kvq_encode", "kvq_decode_
            "kvq_attend_workspace_size", "kvq_attend_decode", "kvq_window_append",
            "kvq_window_flush_workspace_size", "kvq_window_flush", "kvq_smooth_calibrate",
            "kvq_encode_smooth", "kvq_decode_reconstruct_smooth", "kvq_attend_decode_smooth",
-           "kvq_window_flush_smooth", "kvq_status_string", "kvq_last_hip_error")
+           "kvq_window_flush_smooth", "kvq_codebook_fit_workspace_size", "kvq_codebook_fit",
+           "kvq_status_string", "kvq_last_hip_error")
 
 
 class VqDesc(ctypes.Structure):
@@ -86,6 +89,9 @@ def _load():
                                            P, SZ, P]
     L.kvq_window_flush_smooth.argtypes = [ctypes.POINTER(VqDesc), I32, I32, I32, I32, I32, P, P,
                                           I32, I32, P, P, P, P, SD, U32, P, SZ, P]
+    L.kvq_codebook_fit_workspace_size.argtypes = [ctypes.POINTER(VqDesc), I64, ctypes.POINTER(SZ)]
+    L.kvq_codebook_fit.argtypes = [P, I32, ctypes.POINTER(VqDesc), I64, I64, I64, SD, I32, P, P,
+                                   SZ, P]
     L.kvq_status_string.argtypes = [I32]
     L.kvq_status_string.restype = ctypes.c_char_p
     L.kvq_last_hip_error.argtypes = []
@@ -188,6 +194,40 @@ def smooth_calibrate(x, n_scale=1, *, n_rows=None, out=None):
                                        int(n_scale), _ptr(out), _stream(x)),
            "kvq_smooth_calibrate")
     return out
+
+
+def codebook_fit_workspace_size(head_dim, n_groups, n_stages, n_codewords, n_vectors) -> int:
+    vq = VqDesc(head_dim, n_groups, n_stages, n_codewords)
+    sz = ctypes.c_size_t(0)
+    _check(_lib().kvq_codebook_fit_workspace_size(ctypes.byref(vq), n_vectors, ctypes.byref(sz)),
+           "kvq_codebook_fit_workspace_size")
+    return sz.value
+
+
+def codebook_fit(x, init, n_iter, *, n_rows=None, smooth=None, workspace=None, inplace=False):
+    """K-means (Lloyd) codebooks fitted on the sample x ([N][D] or
+    [n_seq][seq_stride][D], f32/bf16/f16, rows [0, n_rows) of each sequence),
+    stage by stage on the residuals, starting from init [S][G][C][dsub] f32.
+    ``smooth``: f32 [n_scale][D] dual-transform factors (sequence n uses row
+    n % n_scale).  Returns the fitted codebooks (init itself when
+    ``inplace``)."""
+    torch = _torch()
+    _need_contig(x, init)
+    if x.dim() == 2:
+        x = x.unsqueeze(0)
+    ns, stride, D = x.shape
+    n_rows = stride if n_rows is None else n_rows
+    S, G, C, dsub = init.shape
+    cb = init if inplace else init.clone()
+    vq = VqDesc(D, G, S, C)
+    need = codebook_fit_workspace_size(D, G, S, C, ns * n_rows)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    sd = None if smooth is None else ctypes.byref(_smooth_desc(smooth, 1, D))
+    _check(_lib().kvq_codebook_fit(_ptr(x), _dtype_code(x), ctypes.byref(vq), ns, stride, n_rows,
+                                   sd, int(n_iter), _ptr(cb), _ptr(workspace), workspace.numel(),
+                                   _stream(x)), "kvq_codebook_fit")
+    return cb
 
 
 def rotate(x, out=None):

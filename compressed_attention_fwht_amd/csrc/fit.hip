@@ -1,0 +1,327 @@
+// K-means (Lloyd) fitting of residual product codebooks on a sample.
+//
+// "VeloxQuant-MLX 0.5.1", VecInfer section: the product-VQ codebooks are
+// K-means codebooks trained before use (its allocator list names
+// train_codebook); "VQKV" summary, 2. Methodology: the residual stage
+// codebooks are trained.  Stage by stage, on the residuals the fitted earlier
+// stages leave: n_iter times {assign every vector of the sample to its
+// nearest entry; move every entry to the mean of its vectors (an entry with
+// none keeps its value)}; then assign once more and subtract, which gives the
+// next stage's residuals.
+//
+// Kernels, all on the caller's stream:
+//   fit_prep_kernel      r = H_D (x / lambda) as float32 (the residual before
+//                        stage 0), and per group the largest |r| (bit pattern,
+//                        atomic max);
+//   assignment           the encode kernels themselves, run with the first
+//                        s + 1 stages (their greedy chain reproduces the
+//                        earlier stages' assignments and picks stage s's);
+//   fit_accum_kernel     per (group, 32-dim slice, chunk of vectors): sums of
+//                        the assigned residuals in LDS as 64-bit fixed point
+//                        (ds_add_u64: integer adds, so the sums are exact and
+//                        independent of the order), then added into global
+//                        accumulators with 64-bit integer atomics;
+//   fit_update_kernel    entry = sum * 2^-F / count in float64, rounded once
+//                        to float32 (entries with no vector keep theirs); the
+//                        accumulators are cleared for the next iteration;
+//   fit_residual_kernel  r -= C_s[z_s] with the final assignment, and the new
+//                        per-group bound for the next stage.
+// Fixed point: F = 62 - ceil(log2 N) - e with max |r| < 2^e, so every term is
+// below 2^(62 - ceil(log2 N)) and any sum of N of them below 2^62.
+#include "kvq_internal.h"
+
+namespace kvq {
+
+constexpr int FIT_CHUNK = 4096;      // vectors per accumulate block
+constexpr int FIT_DS = 32;           // dims per accumulate block (slice of a group)
+
+static inline size_t al256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+FitLayout fit_layout(int D, int G, int S, int C, int64_t n) {
+  FitLayout l{};
+  const int dsub = D / G;
+  size_t off = 0;
+  l.resid = off;  off += al256((size_t)n * D * 4);
+  l.codes = off;  off += al256((size_t)n * S * G);
+  l.pack = off;   off += al256(encode_workspace_bytes(D, G, S, C, 1));
+  l.acc = off;    off += al256((size_t)G * C * dsub * 8);
+  l.cnt = off;    off += al256((size_t)G * C * 4);
+  l.bound = off;  off += al256((size_t)(S + 1) * G * 4);
+  l.total = off;
+  return l;
+}
+
+__device__ __forceinline__ int fit_fbits(uint32_t bound_bits, int log2n) {
+  int e = 0;
+  frexpf(__uint_as_float(bound_bits), &e);      // bound < 2^e (0 -> e = 0)
+  return 62 - log2n - e;
+}
+
+__global__ __launch_bounds__(256) void fit_clear_kernel(uint32_t* __restrict__ p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    p[i] = 0u;
+}
+
+// L = D/8 lanes per row, 8 dims per lane (one group's dims when dsub >= 8).
+template <int D, int XT>
+__global__ __launch_bounds__(256) void fit_prep_kernel(const void* __restrict__ x,
+                                                       float* __restrict__ r,
+                                                       uint32_t* __restrict__ bound, int64_t n_seq,
+                                                       int64_t seq_stride, int64_t n_rows, int dsub,
+                                                       const float* __restrict__ smooth,
+                                                       int64_t n_scale) {
+  constexpr int L = D / 8;
+  constexpr int RPP = 256 / L;
+  constexpr int ESZ = XT == 0 ? 4 : 2;
+  __shared__ uint32_t colmax[L];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int col = tid % L, rsub = tid / L;
+  if (tid < L) colmax[tid] = 0u;
+  __syncthreads();
+  const int64_t n = n_seq * n_rows;
+  uint32_t m = 0u;
+  for (int64_t base = (int64_t)blockIdx.x * RPP; base < n; base += (int64_t)gridDim.x * RPP) {
+    const int64_t v = base + rsub;
+    const int64_t vl = v < n ? v : n - 1;               // every lane joins the butterfly
+    const int64_t seq = vl / n_rows, row = vl - seq * n_rows;
+    float val[8];
+    load8<XT>(reinterpret_cast<const char*>(x) + ((seq * seq_stride + row) * D + col * 8) * ESZ,
+              val);
+    if (smooth != nullptr) {
+      const float* lp = smooth + (seq % n_scale) * D + col * 8;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) val[e] *= __builtin_amdgcn_rcpf(lp[e]);
+    }
+    hadamard_row<8, L>(val, lane);
+    constexpr float sc = rsqrt_pow2(D);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) val[e] *= sc;
+    if (v < n) {
+      float4* o = reinterpret_cast<float4*>(r + v * D + col * 8);
+      o[0] = make_float4(val[0], val[1], val[2], val[3]);
+      o[1] = make_float4(val[4], val[5], val[6], val[7]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t a = __float_as_uint(val[e]) & 0x7fffffffu;
+        m = a > m ? a : m;
+      }
+    }
+  }
+  atomicMax(&colmax[col], m);
+  __syncthreads();
+  const int cpg = dsub / 8;                             // columns per group
+  if (tid < D / dsub) {
+    uint32_t a = 0u;
+    for (int c = tid * cpg; c < (tid + 1) * cpg; ++c) a = colmax[c] > a ? colmax[c] : a;
+    if (a != 0u) atomicMax(bound + tid, a);
+  }
+}
+
+// grid (G * nslice, chunks).  Block: group g, dims [slice*DS, slice*DS + DS)
+// of the group, vectors [chunk*FIT_CHUNK, ...).  One vector per thread per
+// pass; its DS values go to LDS sums[z][j] as fixed point.
+template <int DS>
+__global__ __launch_bounds__(256) void fit_accum_kernel(
+    const float* __restrict__ r, const uint8_t* __restrict__ codes, int row_bytes, int s, int G,
+    int C, int D, int dsub, int64_t n, int log2n, const uint32_t* __restrict__ bound,
+    unsigned long long* __restrict__ acc, uint32_t* __restrict__ cnt) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  unsigned long long* sums = reinterpret_cast<unsigned long long*>(smem);   // [C][DS]
+  uint32_t* counts = reinterpret_cast<uint32_t*>(smem + (size_t)C * DS * 8);
+  const int nslice = dsub / DS;
+  const int g = blockIdx.x / nslice, slice = blockIdx.x - g * nslice;
+  const int tid = threadIdx.x;
+  for (int i = tid; i < C * DS; i += 256) sums[i] = 0ull;
+  for (int i = tid; i < C; i += 256) counts[i] = 0u;
+  __syncthreads();
+  const int F = fit_fbits(bound[g], log2n);
+  const int64_t n0 = (int64_t)blockIdx.y * FIT_CHUNK;
+  const int64_t n1 = (n0 + FIT_CHUNK) < n ? (n0 + FIT_CHUNK) : n;
+  const int d0 = g * dsub + slice * DS;
+  for (int64_t v = n0 + tid; v < n1; v += 256) {
+    int z = codes[v * row_bytes + s * G + g];
+    z = z < C ? z : C - 1;
+    const float4* rp = reinterpret_cast<const float4*>(r + v * D + d0);
+#pragma unroll
+    for (int q = 0; q < DS / 4; ++q) {
+      const float4 a = rp[q];
+      const float e4[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const long long t = __double2ll_rn(ldexp((double)e4[k], F));
+        atomicAdd(&sums[z * DS + q * 4 + k], (unsigned long long)t);
+      }
+    }
+    if (slice == 0) atomicAdd(&counts[z], 1u);
+  }
+  __syncthreads();
+  for (int i = tid; i < C * DS; i += 256) {
+    const unsigned long long v = sums[i];
+    if (v != 0ull) {
+      const int c = i / DS, j = i - c * DS;
+      atomicAdd(acc + ((int64_t)g * C + c) * dsub + slice * DS + j, v);
+    }
+  }
+  if (slice == 0) {
+    for (int c = tid; c < C; c += 256)
+      if (counts[c] != 0u) atomicAdd(cnt + g * C + c, counts[c]);
+  }
+}
+
+// grid G, 256 threads over the group's C * dsub entries.
+__global__ __launch_bounds__(256) void fit_update_kernel(
+    float* __restrict__ cb_s, int C, int dsub, int log2n, const uint32_t* __restrict__ bound,
+    unsigned long long* __restrict__ acc, uint32_t* __restrict__ cnt) {
+  const int g = blockIdx.x, tid = threadIdx.x;
+  const int F = fit_fbits(bound[g], log2n);
+  float* cbg = cb_s + (int64_t)g * C * dsub;
+  unsigned long long* ag = acc + (int64_t)g * C * dsub;
+  uint32_t* cg = cnt + g * C;
+  for (int i = tid; i < C * dsub; i += 256) {
+    const uint32_t k = cg[i / dsub];
+    if (k != 0u) {
+      const double sum = ldexp((double)(long long)ag[i], -F);
+      cbg[i] = (float)(sum / (double)k);
+    }
+    ag[i] = 0ull;
+  }
+  __syncthreads();                                      // every count read before it is cleared
+  for (int c = tid; c < C; c += 256) cg[c] = 0u;
+}
+
+// r -= C_s[z_s] for every (vector, group); per-group bound of the new residual.
+template <int D>
+__global__ __launch_bounds__(256) void fit_residual_kernel(
+    float* __restrict__ r, const uint8_t* __restrict__ codes, int row_bytes, int s, int G, int C,
+    int dsub, const float* __restrict__ cb_s, int64_t n, uint32_t* __restrict__ bound_next) {
+  constexpr int L = D / 8;
+  constexpr int RPP = 256 / L;
+  __shared__ uint32_t colmax[L];
+  const int tid = threadIdx.x;
+  const int col = tid % L, rsub = tid / L;
+  if (tid < L) colmax[tid] = 0u;
+  __syncthreads();
+  const int g = col * 8 / dsub, j0 = col * 8 - g * dsub;
+  uint32_t m = 0u;
+  for (int64_t base = (int64_t)blockIdx.x * RPP; base < n; base += (int64_t)gridDim.x * RPP) {
+    const int64_t v = base + rsub;
+    if (v >= n) continue;
+    int z = codes[v * row_bytes + s * G + g];
+    z = z < C ? z : C - 1;
+    const float4* cp = reinterpret_cast<const float4*>(cb_s + ((int64_t)g * C + z) * dsub + j0);
+    float4* rp = reinterpret_cast<float4*>(r + v * D + col * 8);
+    float4 a = rp[0], b = rp[1];
+    const float4 c0 = cp[0], c1 = cp[1];
+    a.x -= c0.x; a.y -= c0.y; a.z -= c0.z; a.w -= c0.w;
+    b.x -= c1.x; b.y -= c1.y; b.z -= c1.z; b.w -= c1.w;
+    rp[0] = a;
+    rp[1] = b;
+    const float e8[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t t = __float_as_uint(e8[e]) & 0x7fffffffu;
+      m = t > m ? t : m;
+    }
+  }
+  atomicMax(&colmax[col], m);
+  __syncthreads();
+  const int cpg = dsub / 8;
+  if (tid < D / dsub) {
+    uint32_t a = 0u;
+    for (int c = tid * cpg; c < (tid + 1) * cpg; ++c) a = colmax[c] > a ? colmax[c] : a;
+    if (a != 0u) atomicMax(bound_next + tid, a);
+  }
+}
+
+static int ceil_log2_i64(int64_t v) {
+  int k = 0;
+  while (((int64_t)1 << k) < v) ++k;
+  return k;
+}
+
+static int64_t grid_rows(int64_t n, int D) {
+  const int64_t rpp = 256 / (D / 8);
+  int64_t b = (n + rpp - 1) / rpp;
+  return b < 2048 ? (b > 0 ? b : 1) : 2048;
+}
+
+hipError_t launch_codebook_fit(const void* x, int xt, int D, int G, int S, int C, int64_t n_seq,
+                               int64_t seq_stride, int64_t n_rows, Smooth sm, int n_iter,
+                               float* cb, void* ws, hipStream_t st) {
+  const int64_t n = n_seq * n_rows;
+  if (n == 0) return hipSuccess;
+  const int dsub = D / G;
+  const FitLayout lay = fit_layout(D, G, S, C, n);
+  uint8_t* w = reinterpret_cast<uint8_t*>(ws);
+  float* r = reinterpret_cast<float*>(w + lay.resid);
+  uint8_t* codes = w + lay.codes;
+  void* pack = w + lay.pack;
+  unsigned long long* acc = reinterpret_cast<unsigned long long*>(w + lay.acc);
+  uint32_t* cnt = reinterpret_cast<uint32_t*>(w + lay.cnt);
+  uint32_t* bound = reinterpret_cast<uint32_t*>(w + lay.bound);
+  const int log2n = ceil_log2_i64(n);
+
+  // accumulators, counts and bounds start at zero (contiguous from acc)
+  const int64_t nclear = (int64_t)(lay.total - lay.acc) / 4;
+  fit_clear_kernel<<<dim3((unsigned)((nclear + 255) / 256 < 1024 ? (nclear + 255) / 256 : 1024)),
+                     dim3(256), 0, st>>>(reinterpret_cast<uint32_t*>(w + lay.acc), nclear);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  const int64_t rb = grid_rows(n, D);
+#define KVQ_PREP(DD, XX)                                                                    \
+  if (D == DD && xt == XX)                                                                 \
+    fit_prep_kernel<DD, XX><<<dim3((unsigned)rb), dim3(256), 0, st>>>(                      \
+        x, r, bound, n_seq, seq_stride, n_rows, dsub, sm.f, sm.n_scale);
+  KVQ_PREP(64, 0) KVQ_PREP(64, 1) KVQ_PREP(64, 2)
+  KVQ_PREP(128, 0) KVQ_PREP(128, 1) KVQ_PREP(128, 2)
+  KVQ_PREP(256, 0) KVQ_PREP(256, 1) KVQ_PREP(256, 2)
+#undef KVQ_PREP
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  const int ds = dsub < FIT_DS ? dsub : FIT_DS;
+  const int nslice = dsub / ds;
+  const int64_t chunks = (n + FIT_CHUNK - 1) / FIT_CHUNK;
+  const size_t alds = (size_t)C * ds * 8 + (size_t)C * 4;
+  for (int s = 0; s < S; ++s) {
+    const int sp = s + 1;                               // stages run by the assignment
+    const int row_bytes = sp * G;
+    float* cb_s = cb + (size_t)s * G * C * dsub;
+    const uint32_t* bs = bound + (size_t)s * G;
+    const bool last = s == S - 1;
+    for (int it = 0; it < n_iter + (last ? 0 : 1); ++it) {
+      e = launch_encode(x, xt, D, G, sp, C, 1, n_seq, seq_stride, n_rows, cb, codes, n_rows, 0, 0,
+                        0, 0, pack, sm, st);
+      if (e != hipSuccess) return e;
+      if (it == n_iter) break;                          // final assignment of a non-last stage
+#define KVQ_ACC(DSV)                                                                         \
+  if (ds == DSV) {                                                                          \
+    e = hipFuncSetAttribute((const void*)fit_accum_kernel<DSV>,                             \
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)alds);         \
+    if (e != hipSuccess) return e;                                                          \
+    fit_accum_kernel<DSV><<<dim3((unsigned)(G * nslice), (unsigned)chunks), dim3(256), alds, \
+                            st>>>(r, codes, row_bytes, s, G, C, D, dsub, n, log2n, bs, acc,  \
+                                  cnt);                                                     \
+  }
+      KVQ_ACC(8) KVQ_ACC(16) KVQ_ACC(32)
+#undef KVQ_ACC
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      fit_update_kernel<<<dim3(G), dim3(256), 0, st>>>(cb_s, C, dsub, log2n, bs, acc, cnt);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    if (!last) {
+      auto kern = D == 64 ? fit_residual_kernel<64>
+                          : D == 128 ? fit_residual_kernel<128> : fit_residual_kernel<256>;
+      kern<<<dim3((unsigned)rb), dim3(256), 0, st>>>(r, codes, row_bytes, s, G, C, dsub, cb_s, n,
+                                                      bound + (size_t)(s + 1) * G);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
+}
+
+}  // namespace kvq

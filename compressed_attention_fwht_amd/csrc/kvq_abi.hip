@@ -207,6 +207,42 @@ kvq_status kvq_smooth_calibrate(const void* x, kvq_dtype xt, int32_t head_dim, i
                                                  n_rows, n_scale, factors, stream));
 }
 
+kvq_status kvq_codebook_fit_workspace_size(const kvq_vq_desc* vq, int64_t n_vectors,
+                                          size_t* bytes) {
+  if (!bytes) return KVQ_ERR_NULL;
+  kvq_status st = check_vq(vq);
+  if (st != KVQ_OK) return st;
+  if (n_vectors < 0 || n_vectors > KVQ_FIT_MAX_VECTORS) return KVQ_ERR_SHAPE;
+  *bytes = kvq::fit_layout(vq->head_dim, vq->n_groups, vq->n_stages, vq->n_codewords, n_vectors)
+               .total;
+  return KVQ_OK;
+}
+
+kvq_status kvq_codebook_fit(const void* x, kvq_dtype xt, const kvq_vq_desc* vq, int64_t n_seq,
+                            int64_t seq_stride, int64_t n_rows, const kvq_smooth_desc* smooth,
+                            int32_t n_iter, float* codebooks, void* workspace, size_t ws_bytes,
+                            hipStream_t stream) {
+  if (!valid_dtype(xt)) return KVQ_ERR_DTYPE;
+  kvq_status st = check_vq(vq);
+  if (st != KVQ_OK) return st;
+  if (n_seq < 0 || seq_stride < 0 || n_rows < 0 || n_rows > seq_stride) return KVQ_ERR_SHAPE;
+  if (n_iter < 0 || n_iter > 100000) return KVQ_ERR_SHAPE;
+  if (smooth) {
+    st = check_smooth(smooth);
+    if (st != KVQ_OK) return st;
+  }
+  if (n_seq == 0 || n_rows == 0) return KVQ_OK;
+  if (n_seq > KVQ_FIT_MAX_VECTORS / n_rows) return KVQ_ERR_SHAPE;
+  const int64_t n = n_seq * n_rows;
+  if (!x || !codebooks || !workspace) return KVQ_ERR_NULL;
+  if (!aligned16(x) || !aligned16(codebooks) || !aligned16(workspace)) return KVQ_ERR_ALIGN;
+  const int D = vq->head_dim, G = vq->n_groups, S = vq->n_stages, C = vq->n_codewords;
+  if (ws_bytes < kvq::fit_layout(D, G, S, C, n).total) return KVQ_ERR_WORKSPACE;
+  return hip_status(kvq::launch_codebook_fit(x, (int)xt, D, G, S, C, n_seq, seq_stride, n_rows,
+                                             to_smooth(smooth), n_iter, codebooks, workspace,
+                                             stream));
+}
+
 kvq_status kvq_decode_reconstruct(const uint8_t* codes, const kvq_vq_desc* vq, int64_t n_books,
                                   int64_t n_per_book, const float* codebooks, float* out,
                                   uint32_t flags, hipStream_t stream) {

@@ -64,6 +64,17 @@ hipError_t launch_smooth_calibrate(const void* x, int xt, int D, int64_t n_books
                                    int64_t seq_stride, int64_t n_rows, int64_t n_scale, float* f,
                                    hipStream_t st);
 
+// Codebook fitting workspace: residuals f32 [N][D], codes [N][S][G], packed
+// codebooks for the assignment, 64-bit accumulators [G][C][dsub], counts
+// [G][C], per-stage bounds [S+1][G]; byte offsets, each 256-aligned.
+struct FitLayout {
+  size_t resid, codes, pack, acc, cnt, bound, total;
+};
+FitLayout fit_layout(int D, int G, int S, int C, int64_t n);
+hipError_t launch_codebook_fit(const void* x, int xt, int D, int G, int S, int C, int64_t n_seq,
+                               int64_t seq_stride, int64_t n_rows, Smooth sm, int n_iter,
+                               float* cb, void* ws, hipStream_t st);
+
 hipError_t launch_window_append(const uint16_t* kn, const uint16_t* vn, uint16_t* kw,
                                 uint16_t* vw, int64_t units, int D, int wcap, int row,
                                 hipStream_t st);

@@ -294,6 +294,42 @@ KVQ_API kvq_status kvq_window_flush_smooth(const kvq_vq_desc* vq, int32_t batch,
                                    const kvq_smooth_desc* k_smooth, uint32_t flags,
                                    void* workspace, size_t ws_bytes, hipStream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * Codebook fitting ("VeloxQuant-MLX 0.5.1", VecInfer section: the product-VQ
+ * codebooks are K-means codebooks trained before use, its allocator list
+ * naming train_codebook; "VQKV" summary, 2. Methodology: trained residual
+ * stage codebooks).  K-means (Lloyd) on a sample, stage by stage: on the
+ * residuals the already fitted earlier stages leave, n_iter times {assign
+ * every vector to its nearest entry of stage s, group g (as kvq_encode does);
+ * move every entry to the mean of its vectors, an entry with no vector keeping
+ * its value}; then one more assignment with the fitted entries, whose
+ * subtraction gives the next stage's residuals.
+ * ------------------------------------------------------------------------ */
+#define KVQ_FIT_MAX_VECTORS (((int64_t)1) << 24)
+
+/* Workspace bytes kvq_codebook_fit needs for n_vectors sample vectors
+ * (4*D + S*G bytes per vector plus fixed parts).  n_vectors <= 2^24. */
+KVQ_API kvq_status kvq_codebook_fit_workspace_size(const kvq_vq_desc* vq, int64_t n_vectors,
+                                           size_t* bytes);
+
+/* Fits codebooks [S][G][C][dsub] float32 IN PLACE (in: the starting entries,
+ * out: the fitted ones) on the sample rows [0, n_rows) of every sequence of
+ * x [n_seq][seq_stride][D] (type xt, original domain; rotated inside, and
+ * divided by smoothing factors first when smooth is not NULL: one book,
+ * factors [n_scale][D], sequence n using row n % n_scale, as
+ * kvq_encode_smooth).  n_seq * n_rows <= 2^24 vectors; 0 <= n_iter <= 100000
+ * (0: the entries are left as they are).  The entry means are exact sums of
+ * the float32 residuals in 64-bit fixed point (F fraction bits with every term
+ * below 2^(62 - ceil(log2 N))), divided in float64 and rounded once to float32,
+ * so repeated calls give identical codebooks.  Assignments follow kvq_encode's
+ * rule (near ties within a relative 1e-4 may go either way).  Non-finite
+ * inputs give unspecified entries. */
+KVQ_API kvq_status kvq_codebook_fit(const void* x, kvq_dtype xt, const kvq_vq_desc* vq,
+                            int64_t n_seq, int64_t seq_stride, int64_t n_rows,
+                            const kvq_smooth_desc* smooth, int32_t n_iter,
+                            float* codebooks, void* workspace, size_t ws_bytes,
+                            hipStream_t stream);
+
 /* Static description of a status code. */
 KVQ_API const char* kvq_status_string(kvq_status status);
 

@@ -241,3 +241,25 @@ def test_reconstruct_attend_flush_smooth_argument_errors():
                                               0, FAKE, FAKE, FAKE, FAKE, sd, 0, FAKE, 1 << 30, None)
     assert fl(None) == NULL
     assert fl(ctypes.byref(_sd(n=0))) == SHAPE
+
+
+def test_codebook_fit_argument_errors():
+    L = kvq.lib
+    vq = _vq()
+    sz = ctypes.c_size_t(0)
+    assert L.kvq_codebook_fit_workspace_size(ctypes.byref(vq), 1 << 25, ctypes.byref(sz)) == SHAPE
+    assert L.kvq_codebook_fit_workspace_size(ctypes.byref(vq), 1000, None) == NULL
+    assert L.kvq_codebook_fit_workspace_size(ctypes.byref(vq), 1000, ctypes.byref(sz)) == OK
+    assert sz.value >= 1000 * (4 * 128 + 2 * 16)
+    fit = lambda x=FAKE, xt=1, ns=4, st=64, nr=64, sd=None, it=3, cb=FAKE, ws=FAKE, wsb=1 << 30: \
+        L.kvq_codebook_fit(x, xt, ctypes.byref(vq), ns, st, nr, sd, it, cb, ws, wsb, None)
+    assert fit(xt=5) == DTYPE
+    assert fit(nr=65) == SHAPE
+    assert fit(it=-1) == SHAPE
+    assert fit(ns=1 << 20, nr=64) == SHAPE               # more than 2^24 vectors
+    assert fit(cb=0) == NULL
+    assert fit(ws=0) == NULL
+    assert fit(x=FAKE + 2) == ALIGN
+    assert fit(wsb=1000) == WS
+    assert fit(sd=ctypes.byref(_sd(n=0))) == SHAPE
+    assert fit(ns=0, x=0, cb=0, ws=0) == OK               # empty sample: no-op

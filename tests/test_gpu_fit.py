@@ -1,0 +1,177 @@
+"""Parity of kvq_codebook_fit (K-means / Lloyd fitting of the residual product
+codebooks on a sample) with the float64 oracle, through the C ABI.
+
+K-means is iterative, so the element-wise check is one iteration at a time:
+the GPU's assignment (the encode kernels, run with the same entries) follows
+the code rule against the oracle's distances, and every fitted entry equals
+the oracle's mean of the residuals the GPU assigned to it within 1e-6 * the
+largest residual component of its group (float32 residuals against float64;
+the fixed-point sums themselves are exact to 2^-40 of that bound).  Entries
+no vector chose must come back bit-identical.  Over several iterations the
+checks are Lloyd's properties: the distortion of the fitted codebooks never
+increases, and ends within 1 % of the oracle's own fit from the same start.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import compressed_attention_fwht_amd as kvq
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    torch.cuda.set_device(0)
+    yield
+    torch.cuda.synchronize()
+
+
+def cuda(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def sample(key, n_rows, **over):
+    """Keys of a workload as the fitting sample: x [n_seq][T][D] on the GPU
+    (bf16 or fp32), their float64 values, the K codebooks as start."""
+    w = synth.workload(key, **over)
+    inp = synth.make_inputs(w)
+    if w.x_dtype == "bf16":
+        x = torch.from_numpy(inp["x"][0].view(np.int16)).view(torch.bfloat16).cuda()
+    else:
+        x = torch.from_numpy(inp["x"][0]).cuda()
+    xf = inp["x_f32"][0][:, :n_rows].astype(np.float64)
+    return w, x, xf, inp["cb"][0]
+
+
+def check_step(r, z, init, fitted, dsub):
+    """One Lloyd update per group: the fitted entries against the oracle's
+    means of r over the GPU's assignment z; unchosen entries unchanged."""
+    G = init.shape[0]
+    for g in range(G):
+        rg = r[:, g * dsub:(g + 1) * dsub]
+        ref = oracle.lloyd_update(rg, z[:, g], init[g])
+        tol = 1e-6 * np.abs(rg).max()
+        err = np.abs(fitted[g].astype(np.float64) - ref)
+        assert err.max() <= tol, (g, err.max(), tol)
+        unused = np.setdiff1d(np.arange(init.shape[1]), z[:, g])
+        assert np.array_equal(fitted[g][unused], init[g][unused])
+
+
+@pytest.mark.parametrize("key,over,n_rows", [
+    (2, dict(tokens=2100, window=0), 2000),     # S = 1, outlier channels, MFMA assignment
+    (1, dict(), 1024),                          # D = 64, one 64-dim group, S = 2, generic kernel
+])
+def test_fit_one_iteration_parity(key, over, n_rows):
+    say(f"codebook fit, one iteration, workload {key} {over} rows {n_rows}")
+    w, x, xf, init = sample(key, n_rows, **over)
+    S, G, C, dsub = init.shape
+    fitted = kvq.codebook_fit(x, cuda(init), 1, n_rows=n_rows).cpu().numpy()
+    y = oracle.fwht(xf.reshape(-1, w.head_dim))
+    # stage 0: the GPU's assignment with the starting entries
+    z0 = kvq.encode(x[None], cuda(init[None, :1]), n_rows=n_rows).cpu().numpy()
+    z0 = z0.reshape(-1, 1, G)
+    res = oracle.check_codes(y, init[:1], z0, rotate=False)
+    say("   stage 0 assignment", {k: res[k] for k in ("total", "exact", "near_tie", "hard")})
+    assert res["hard"] == 0
+    check_step(y, z0[:, 0], init[0], fitted[0], dsub)
+    if S > 1:
+        # stage 1 starts from the residuals of the fitted stage 0 (final assignment)
+        zf = kvq.encode(x[None], cuda(fitted[None, :1]), n_rows=n_rows).cpu().numpy()
+        zf = zf.reshape(-1, G)
+        r1 = y - np.concatenate([fitted[0, g][zf[:, g]] for g in range(G)], axis=1)
+        both = np.concatenate([fitted[:1], init[1:2]])
+        z1 = kvq.encode(x[None], cuda(both[None]), n_rows=n_rows).cpu().numpy()
+        z1 = z1.reshape(-1, 2, G)[:, 1]
+        res = oracle.check_codes(r1, init[1:2], z1[:, None, :], rotate=False)
+        say("   stage 1 assignment", {k: res[k] for k in ("total", "exact", "near_tie", "hard")})
+        assert res["hard"] == 0
+        check_step(r1, z1, init[1], fitted[1], dsub)
+
+
+def test_fit_one_iteration_two_stages_mfma():
+    """Stage chaining on the MFMA assignment (Qwen-shaped keys, S = 2)."""
+    say("codebook fit, one iteration, two stages, MFMA assignment")
+    w, x, xf, init = sample(3, 1500, batch=1, tokens=1500, window=0)
+    S, G, C, dsub = init.shape
+    fitted = kvq.codebook_fit(x, cuda(init), 1).cpu().numpy()
+    y = oracle.fwht(xf.reshape(-1, 128))
+    z0 = kvq.encode(x[None], cuda(init[None, :1])).cpu().numpy().reshape(-1, G)
+    check_step(y, z0, init[0], fitted[0], dsub)
+    zf = kvq.encode(x[None], cuda(fitted[None, :1])).cpu().numpy().reshape(-1, G)
+    r1 = y - np.concatenate([fitted[0, g][zf[:, g]] for g in range(G)], axis=1)
+    both = np.concatenate([fitted[:1], init[1:2]])
+    z1 = kvq.encode(x[None], cuda(both[None])).cpu().numpy().reshape(-1, 2, G)[:, 1]
+    res = oracle.check_codes(r1, init[1:2], z1[:, None, :], rotate=False)
+    assert res["hard"] == 0
+    check_step(r1, z1, init[1], fitted[1], dsub)
+
+
+def test_fit_smoothed_keys_one_iteration():
+    say("codebook fit on smoothed keys, one iteration")
+    w, x, xf, init = sample(2, 1500, tokens=1500, window=0)
+    G, dsub = init.shape[1], init.shape[3]
+    lam = oracle.smooth_factors(xf, w.n_kv_heads).astype(np.float32)
+    init = (init * np.float32(0.25)).astype(np.float32)
+    fitted = kvq.codebook_fit(x, cuda(init), 1, smooth=cuda(lam)).cpu().numpy()
+    rows = oracle.smooth_rows(lam.astype(np.float64), np.arange(w.n_seq))[:, None, :]
+    y = oracle.fwht(oracle.smooth_keys(xf, rows).reshape(-1, 128))
+    z0 = kvq.encode(x[None], cuda(init[None]), smooth=cuda(lam[None])).cpu().numpy()
+    z0 = z0.reshape(-1, G)
+    res = oracle.check_codes(y, init, z0[:, None, :], rotate=False)
+    assert res["hard"] == 0
+    check_step(y, z0, init[0], fitted[0], dsub)
+
+
+def test_fit_deterministic_and_zero_iterations():
+    say("codebook fit: repeatable, n_iter = 0 leaves the entries")
+    w, x, xf, init = sample(3, 1000, batch=1, tokens=1000, window=0)
+    cb = cuda(init)
+    a = kvq.codebook_fit(x, cb, 3)
+    b = kvq.codebook_fit(x, cb, 3)
+    assert torch.equal(a, b)
+    assert not torch.equal(a, cb)
+    assert torch.equal(kvq.codebook_fit(x, cb, 0), cb)
+    ws = torch.empty(kvq.codebook_fit_workspace_size(128, 16, 2, 256, 4 * 1000), dtype=torch.uint8,
+                     device="cuda")
+    c = kvq.codebook_fit(x, cb, 3, workspace=ws)         # a workspace passed in, then reused
+    d = kvq.codebook_fit(x, cb, 3, workspace=ws)
+    assert torch.equal(a, c) and torch.equal(c, d)
+
+
+def test_fit_distortion_never_increases_and_matches_oracle_fit():
+    """Lloyd's property on the GPU fits with 0, 1, 2, 4, 8 iterations (the
+    oracle measures each fitted codebook's distortion exactly), and the
+    8-iteration distortion is within 1 % of the oracle's own 8-iteration fit
+    from the same start."""
+    say("codebook fit: distortion over iterations")
+    w, x, xf, init = sample(2, 512, tokens=512, window=0)
+    G, dsub = init.shape[1], init.shape[3]
+    y = oracle.fwht(xf.reshape(-1, 128))
+
+    def distortion(cb):
+        tot = 0.0
+        for g in range(G):
+            z, d = oracle.nearest(y[:, g * dsub:(g + 1) * dsub], cb[0, g])
+            tot += d[np.arange(len(z)), z].sum()
+        return tot
+
+    cb0 = cuda(init)
+    ds = [distortion(kvq.codebook_fit(x, cb0, k).cpu().numpy().astype(np.float64))
+          for k in (0, 1, 2, 4, 8)]
+    say("   distortion", [f"{d:.6g}" for d in ds])
+    assert all(b <= a * (1 + 1e-6) for a, b in zip(ds, ds[1:])), ds
+    assert ds[-1] < 0.9 * ds[0]
+    ref = distortion(oracle.fit_codebooks(xf.reshape(-1, 128), init, 8))
+    say("   oracle fit", f"{ref:.6g}")
+    assert abs(ds[-1] - ref) <= 0.01 * ref
