@@ -126,16 +126,18 @@ __device__ __forceinline__ void wait_vmem() {
   __builtin_amdgcn_s_waitcnt(0x0f70);                    // vmcnt(0)
 }
 
-template <int S, int XT, int GS>   // GS: blocks sharing a tile's 16 groups (1 or 16)
+template <int S, int XT, int GS>   // GS: 1 = a block codes all 16 groups of its tile;
+                                   // 0 = gsplit blocks share them (runtime)
 __global__ __launch_bounds__(64 * mf_waves<S>(), 8 / mf_waves<S>()) void encode_mfma_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ packed, uint8_t* __restrict__ codes,
     int64_t n_seq, int64_t seq_stride, int64_t n_rows, int64_t code_stride, int64_t code_row0,
-    int64_t tiles_per_book, int pre_rotated, const float* __restrict__ smooth, int64_t n_scale) {
+    int64_t tiles_per_book, int pre_rotated, const float* __restrict__ smooth, int64_t n_scale,
+    int gsplit) {
   constexpr int G = 16;
   constexpr int SG = S * G;
-  // GS = 16 (small batches): one block per (tile, group), each rotating the
-  // tile itself and coding group g0 -- more blocks in flight for a batch too
-  // small to fill the CUs.
+  // GS = 0 (small batches): gsplit blocks per tile, each rotating the tile
+  // itself and coding the groups [g_lo, g_hi) -- more blocks in flight for a
+  // batch too small to give every SIMD two waves.
   // LDS: two buffers of one group's S stage blocks (double buffering); the
   // per-wave transpose scratch of the tile's input rows aliases them, since
   // it is dead before the first codebook load is issued.
@@ -145,8 +147,10 @@ __global__ __launch_bounds__(64 * mf_waves<S>(), 8 / mf_waves<S>()) void encode_
   const int h = lane >> 5;                                // lane half
   uint8_t* scratch = smem + wave * MF_SCRATCH;
 
-  const int g0 = GS > 1 ? (int)(blockIdx.x % GS) : 0;
-  const int64_t bt = blockIdx.x / GS;
+  const int gsp = GS == 1 ? 1 : gsplit;
+  const int g_lo = GS == 1 ? 0 : (int)(blockIdx.x % gsp) * (G / gsp);
+  const int g_hi = GS == 1 ? G : g_lo + G / gsp;
+  const int64_t bt = blockIdx.x / gsp;
   const int64_t book = bt / tiles_per_book;
   const int64_t tile = bt - book * tiles_per_book;
   const int64_t n_per_book = n_seq * n_rows;
@@ -184,7 +188,7 @@ __global__ __launch_bounds__(64 * mf_waves<S>(), 8 / mf_waves<S>()) void encode_
 
   const uint8_t* pk_book = packed + book * (int64_t)G * S * PACK_BYTES;
   // the first group's codebooks load while the rotation runs
-  stage_group<S>(pk_book + (int64_t)g0 * S * PACK_BYTES, smem + (g0 & 1) * mf_buf<S>(), wave,
+  stage_group<S>(pk_book + (int64_t)g_lo * S * PACK_BYTES, smem + (g_lo & 1) * mf_buf<S>(), wave,
                  lane);
 
   // ---- y = H x (or x itself when pre-rotated), float32 in registers
@@ -244,13 +248,13 @@ __global__ __launch_bounds__(64 * mf_waves<S>(), 8 / mf_waves<S>()) void encode_
 
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    if constexpr (GS > 1) {
-      if (g != g0) continue;                             // block-uniform
+    if constexpr (GS != 1) {
+      if (g < g_lo || g >= g_hi) continue;               // block-uniform
     }
     const uint8_t* cbs = smem + (g & 1) * BUF;
     // ---- the next group's codebooks stream into the other buffer meanwhile
-    if (GS == 1 && g + 1 < G) stage_group<S>(pk_book + (int64_t)(g + 1) * S * PACK_BYTES,
-                                             smem + ((g + 1) & 1) * BUF, wave, lane);
+    if (g + 1 < g_hi) stage_group<S>(pk_book + (int64_t)(g + 1) * S * PACK_BYTES,
+                                     smem + ((g + 1) & 1) * BUF, wave, lane);
 
     float r[8];
 #pragma unroll
@@ -382,7 +386,7 @@ __global__ __launch_bounds__(64 * mf_waves<S>(), 8 / mf_waves<S>()) void encode_
 #pragma unroll
         for (int g = 0; g < G; ++g) {
           const int pos = s * G + g;
-          if (g == g0) row[pos] = (uint8_t)(cw[pos >> 2] >> (8 * (pos & 3)));
+          if (g >= g_lo && g < g_hi) row[pos] = (uint8_t)(cw[pos >> 2] >> (8 * (pos & 3)));
         }
     }
   }
@@ -495,22 +499,21 @@ static hipError_t launch_mfma_t(const void* x, const uint8_t* packed, uint8_t* c
   const int64_t n_per_book = n_seq * n_rows;
   constexpr int TILE = 64 * mf_waves<S>();
   const int64_t tiles = (n_per_book + TILE - 1) / TILE;
-  // a small fp16 batch (a window flush) shares each tile's groups out over 16
-  // blocks, so the batch is spread over the CUs
+  // a small batch (a window flush, a codebook-fitting sample) shares each
+  // tile's 16 groups out over gsplit blocks: the fewest that give the CUs'
+  // SIMDs two waves each (512 blocks), at most 16
   const int64_t blocks = tiles * n_books;
-  const int gs = (XT == 2 && blocks <= 64) ? 16 : 1;
+  int gs = 1;
+  while (gs < 16 && blocks * gs < 512) gs *= 2;
   size_t lds = (size_t)2 * mf_buf<S>();                    // two codebook buffers
   if (lds < (size_t)mf_waves<S>() * MF_SCRATCH) lds = (size_t)mf_waves<S>() * MF_SCRATCH;
-  auto kern = encode_mfma_kernel<S, XT, 1>;
-  if constexpr (XT == 2) {
-    if (gs == 16) kern = encode_mfma_kernel<S, XT, 16>;
-  }
+  auto kern = gs > 1 ? encode_mfma_kernel<S, XT, 0> : encode_mfma_kernel<S, XT, 1>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)lds);
   if (e != hipSuccess) return e;
   kern<<<dim3((unsigned)(blocks * gs)), dim3(64 * mf_waves<S>()), lds, st>>>(
       reinterpret_cast<const uint16_t*>(x), packed, codes, n_seq, seq_stride, n_rows, code_stride,
-      code_row0, tiles, pre_rotated, sm.f, sm.n_scale);
+      code_row0, tiles, pre_rotated, sm.f, sm.n_scale, gs);
   return hipGetLastError();
 }
 

@@ -19,23 +19,42 @@
 //   fit_accum_kernel     per (group, 32-dim slice, chunk of vectors): sums of
 //                        the assigned residuals in LDS as 64-bit fixed point
 //                        (ds_add_u64: integer adds, so the sums are exact and
-//                        independent of the order), then added into global
-//                        accumulators with 64-bit integer atomics;
-//   fit_update_kernel    entry = sum * 2^-F / count in float64, rounded once
-//                        to float32 (entries with no vector keep theirs); the
-//                        accumulators are cleared for the next iteration;
+//                        independent of the order), stored as the chunk's
+//                        partial sums (plain stores, no global atomics);
+//   fit_update_kernel    entry = (sum over chunks) * 2^-F / count in float64,
+//                        rounded once to float32 (entries with no vector keep
+//                        theirs);
 //   fit_residual_kernel  r -= C_s[z_s] with the final assignment, and the new
 //                        per-group bound for the next stage.
+// The kernels reading a stage's bound take the max over FIT_BCOPIES copies.
 // Fixed point: F = 62 - ceil(log2 N) - e with max |r| < 2^e, so every term is
-// below 2^(62 - ceil(log2 N)) and any sum of N of them below 2^62.
+// below 2^(62 - ceil(log2 N)) and any sum of N of them below 2^62; a residual
+// becomes a multiple of 2^-F exactly when |r| >= 2^(23-F), and is truncated
+// toward zero (an error below 2^-F) otherwise.
 #include "kvq_internal.h"
 
 namespace kvq {
 
-constexpr int FIT_CHUNK = 4096;      // vectors per accumulate block
+constexpr int FIT_CHUNK = 4096;      // vectors per accumulate block, at least
+constexpr int FIT_MAX_CHUNKS = 64;   // chunks of the sample, at most
 constexpr int FIT_DS = 32;           // dims per accumulate block (slice of a group)
+// The per-group bounds are kept in this many copies, block b folding into
+// copy b % FIT_BCOPIES (readers take the max over them): atomics on one
+// address serialise, so spreading them keeps the bound off the critical path.
+constexpr int FIT_BCOPIES = 32;
 
 static inline size_t al256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// vectors per accumulate chunk: FIT_CHUNK, or more so at most FIT_MAX_CHUNKS
+static int64_t fit_chunk_len(int64_t n) {
+  int64_t c = (n + FIT_MAX_CHUNKS - 1) / FIT_MAX_CHUNKS;
+  c = (c + FIT_CHUNK - 1) / FIT_CHUNK * FIT_CHUNK;
+  return c > FIT_CHUNK ? c : FIT_CHUNK;
+}
+static int64_t fit_chunks(int64_t n) {
+  const int64_t c = fit_chunk_len(n);
+  return n > 0 ? (n + c - 1) / c : 1;
+}
 
 FitLayout fit_layout(int D, int G, int S, int C, int64_t n) {
   FitLayout l{};
@@ -44,17 +63,36 @@ FitLayout fit_layout(int D, int G, int S, int C, int64_t n) {
   l.resid = off;  off += al256((size_t)n * D * 4);
   l.codes = off;  off += al256((size_t)n * S * G);
   l.pack = off;   off += al256(encode_workspace_bytes(D, G, S, C, 1));
-  l.acc = off;    off += al256((size_t)G * C * dsub * 8);
-  l.cnt = off;    off += al256((size_t)G * C * 4);
-  l.bound = off;  off += al256((size_t)(S + 1) * G * 4);
+  const int64_t nch = fit_chunks(n);
+  l.acc = off;    off += al256((size_t)nch * G * C * dsub * 8);
+  l.cnt = off;    off += al256((size_t)nch * G * C * 4);
+  l.bound = off;  off += al256((size_t)(S + 1) * FIT_BCOPIES * G * 4);
   l.total = off;
   return l;
 }
 
-__device__ __forceinline__ int fit_fbits(uint32_t bound_bits, int log2n) {
+// bound: the stage's [FIT_BCOPIES][G] copies
+__device__ __forceinline__ int fit_fbits(const uint32_t* __restrict__ bound, int g, int G,
+                                         int log2n) {
+  uint32_t b = 0u;
+  for (int i = 0; i < FIT_BCOPIES; ++i) b = bound[i * G + g] > b ? bound[i * G + g] : b;
   int e = 0;
-  frexpf(__uint_as_float(bound_bits), &e);      // bound < 2^e (0 -> e = 0)
+  frexpf(__uint_as_float(b), &e);               // bound < 2^e (0 -> e = 0)
   return 62 - log2n - e;
+}
+
+// x * 2^F as a 64-bit integer from the float's bits (integer ALU only): the
+// mantissa shifted by exponent + F; exact when the result is a whole number
+// (|x| >= 2^(23-F)), truncated toward zero below that.  F keeps every value
+// of the stage below 2^62, so the left shift never overflows.
+__device__ __forceinline__ long long fit_fixed(float x, int F) {
+  const uint32_t u = __float_as_uint(x);
+  const int ex = (int)((u >> 23) & 0xffu);
+  const uint32_t man = (u & 0x7fffffu) | (ex ? 0x800000u : 0u);
+  const int sh = (ex ? ex : 1) - 150 + F;               // x = man * 2^(ex - 150)
+  long long t = sh >= 0 ? (long long)((unsigned long long)man << sh)
+                        : (sh > -32 ? (long long)(man >> -sh) : 0ll);
+  return (u >> 31) ? -t : t;
 }
 
 __global__ __launch_bounds__(256) void fit_clear_kernel(uint32_t* __restrict__ p, int64_t n) {
@@ -113,20 +151,24 @@ __global__ __launch_bounds__(256) void fit_prep_kernel(const void* __restrict__ 
   if (tid < D / dsub) {
     uint32_t a = 0u;
     for (int c = tid * cpg; c < (tid + 1) * cpg; ++c) a = colmax[c] > a ? colmax[c] : a;
-    if (a != 0u) atomicMax(bound + tid, a);
+    if (a != 0u) atomicMax(bound + (blockIdx.x % FIT_BCOPIES) * (D / dsub) + tid, a);
   }
 }
 
 // grid (G * nslice, chunks).  Block: group g, dims [slice*DS, slice*DS + DS)
-// of the group, vectors [chunk*FIT_CHUNK, ...).  One vector per thread per
-// pass; its DS values go to LDS sums[z][j] as fixed point.
+// of the group, vectors [chunk*len, (chunk+1)*len); each vector's DS values go
+// to LDS sums[j][z] as fixed point, then the block stores its partial sums to
+// part[chunk][g][j][c] (and counts to pcnt[chunk][g][c]).
 template <int DS>
 __global__ __launch_bounds__(256) void fit_accum_kernel(
     const float* __restrict__ r, const uint8_t* __restrict__ codes, int row_bytes, int s, int G,
-    int C, int D, int dsub, int64_t n, int log2n, const uint32_t* __restrict__ bound,
-    unsigned long long* __restrict__ acc, uint32_t* __restrict__ cnt) {
+    int C, int D, int dsub, int64_t n, int64_t len, int log2n,
+    const uint32_t* __restrict__ bound, unsigned long long* __restrict__ part,
+    uint32_t* __restrict__ pcnt) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  unsigned long long* sums = reinterpret_cast<unsigned long long*>(smem);   // [C][DS]
+  // [DS][C]: the lanes of one atomic instruction (same j, random entries z)
+  // spread over the banks; [C][DS] would put them all DS * 8 bytes apart
+  unsigned long long* sums = reinterpret_cast<unsigned long long*>(smem);
   uint32_t* counts = reinterpret_cast<uint32_t*>(smem + (size_t)C * DS * 8);
   const int nslice = dsub / DS;
   const int g = blockIdx.x / nslice, slice = blockIdx.x - g * nslice;
@@ -134,59 +176,66 @@ __global__ __launch_bounds__(256) void fit_accum_kernel(
   for (int i = tid; i < C * DS; i += 256) sums[i] = 0ull;
   for (int i = tid; i < C; i += 256) counts[i] = 0u;
   __syncthreads();
-  const int F = fit_fbits(bound[g], log2n);
-  const int64_t n0 = (int64_t)blockIdx.y * FIT_CHUNK;
-  const int64_t n1 = (n0 + FIT_CHUNK) < n ? (n0 + FIT_CHUNK) : n;
+  const int F = fit_fbits(bound, g, G, log2n);
+  const int64_t n0 = (int64_t)blockIdx.y * len;
+  const int64_t n1 = (n0 + len) < n ? (n0 + len) : n;
   const int d0 = g * dsub + slice * DS;
-  for (int64_t v = n0 + tid; v < n1; v += 256) {
-    int z = codes[v * row_bytes + s * G + g];
-    z = z < C ? z : C - 1;
-    const float4* rp = reinterpret_cast<const float4*>(r + v * D + d0);
+  // VB vectors per thread per pass, all their loads issued before any atomic
+  // (indices past the end repeat the last vector; their atomics are skipped)
+  constexpr int VB = DS == 32 ? 2 : 4;
+  for (int64_t b = n0 + tid; b < n1; b += VB * 256) {
+    int zz[VB];
+    float4 a[VB][DS / 4];
 #pragma unroll
-    for (int q = 0; q < DS / 4; ++q) {
-      const float4 a = rp[q];
-      const float e4[4] = {a.x, a.y, a.z, a.w};
+    for (int k = 0; k < VB; ++k) {
+      const int64_t v = b + 256 * k < n1 ? b + 256 * k : n1 - 1;
+      zz[k] = codes[v * row_bytes + s * G + g];
+      const float4* rp = reinterpret_cast<const float4*>(r + v * D + d0);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const long long t = __double2ll_rn(ldexp((double)e4[k], F));
-        atomicAdd(&sums[z * DS + q * 4 + k], (unsigned long long)t);
-      }
+      for (int q = 0; q < DS / 4; ++q) a[k][q] = rp[q];
     }
-    if (slice == 0) atomicAdd(&counts[z], 1u);
+#pragma unroll
+    for (int k = 0; k < VB; ++k) {
+      if (b + 256 * k >= n1) continue;
+      const int z = zz[k] < C ? zz[k] : C - 1;
+#pragma unroll
+      for (int q = 0; q < DS / 4; ++q) {
+        const float e4[4] = {a[k][q].x, a[k][q].y, a[k][q].z, a[k][q].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const long long t = fit_fixed(e4[j], F);
+          atomicAdd(&sums[(q * 4 + j) * C + z], (unsigned long long)t);
+        }
+      }
+      if (slice == 0) atomicAdd(&counts[z], 1u);
+    }
   }
   __syncthreads();
-  for (int i = tid; i < C * DS; i += 256) {
-    const unsigned long long v = sums[i];
-    if (v != 0ull) {
-      const int c = i / DS, j = i - c * DS;
-      atomicAdd(acc + ((int64_t)g * C + c) * dsub + slice * DS + j, v);
-    }
-  }
+  unsigned long long* pp = part + (((int64_t)blockIdx.y * G + g) * dsub + slice * DS) * C;
+  for (int i = tid; i < C * DS; i += 256) pp[i] = sums[i];
   if (slice == 0) {
-    for (int c = tid; c < C; c += 256)
-      if (counts[c] != 0u) atomicAdd(cnt + g * C + c, counts[c]);
+    uint32_t* pc = pcnt + ((int64_t)blockIdx.y * G + g) * C;
+    for (int c = tid; c < C; c += 256) pc[c] = counts[c];
   }
 }
 
-// grid G, 256 threads over the group's C * dsub entries.
+// grid (G, dsub), one entry c per thread (C <= 256): the chunks' partial sums
+// and counts added in chunk order (integers: exact).
 __global__ __launch_bounds__(256) void fit_update_kernel(
-    float* __restrict__ cb_s, int C, int dsub, int log2n, const uint32_t* __restrict__ bound,
-    unsigned long long* __restrict__ acc, uint32_t* __restrict__ cnt) {
-  const int g = blockIdx.x, tid = threadIdx.x;
-  const int F = fit_fbits(bound[g], log2n);
-  float* cbg = cb_s + (int64_t)g * C * dsub;
-  unsigned long long* ag = acc + (int64_t)g * C * dsub;
-  uint32_t* cg = cnt + g * C;
-  for (int i = tid; i < C * dsub; i += 256) {
-    const uint32_t k = cg[i / dsub];
-    if (k != 0u) {
-      const double sum = ldexp((double)(long long)ag[i], -F);
-      cbg[i] = (float)(sum / (double)k);
-    }
-    ag[i] = 0ull;
+    float* __restrict__ cb_s, int G, int C, int dsub, int log2n, int64_t nch,
+    const uint32_t* __restrict__ bound, const unsigned long long* __restrict__ part,
+    const uint32_t* __restrict__ pcnt) {
+  const int g = blockIdx.x, j = blockIdx.y, c = threadIdx.x;
+  if (c >= C) return;
+  const int F = fit_fbits(bound, g, G, log2n);
+  unsigned long long sum = 0ull;
+  uint32_t k = 0u;
+  for (int64_t h = 0; h < nch; ++h) {
+    sum += part[((h * G + g) * dsub + j) * C + c];
+    k += pcnt[(h * G + g) * C + c];
   }
-  __syncthreads();                                      // every count read before it is cleared
-  for (int c = tid; c < C; c += 256) cg[c] = 0u;
+  if (k != 0u)
+    cb_s[((int64_t)g * C + c) * dsub + j] = (float)(ldexp((double)(long long)sum, -F) / (double)k);
 }
 
 // r -= C_s[z_s] for every (vector, group); per-group bound of the new residual.
@@ -229,7 +278,7 @@ __global__ __launch_bounds__(256) void fit_residual_kernel(
   if (tid < D / dsub) {
     uint32_t a = 0u;
     for (int c = tid * cpg; c < (tid + 1) * cpg; ++c) a = colmax[c] > a ? colmax[c] : a;
-    if (a != 0u) atomicMax(bound_next + tid, a);
+    if (a != 0u) atomicMax(bound_next + (blockIdx.x % FIT_BCOPIES) * (D / dsub) + tid, a);
   }
 }
 
@@ -261,10 +310,10 @@ hipError_t launch_codebook_fit(const void* x, int xt, int D, int G, int S, int C
   uint32_t* bound = reinterpret_cast<uint32_t*>(w + lay.bound);
   const int log2n = ceil_log2_i64(n);
 
-  // accumulators, counts and bounds start at zero (contiguous from acc)
-  const int64_t nclear = (int64_t)(lay.total - lay.acc) / 4;
+  // the bounds start at zero (the partial sums are overwritten by every pass)
+  const int64_t nclear = (int64_t)(lay.total - lay.bound) / 4;
   fit_clear_kernel<<<dim3((unsigned)((nclear + 255) / 256 < 1024 ? (nclear + 255) / 256 : 1024)),
-                     dim3(256), 0, st>>>(reinterpret_cast<uint32_t*>(w + lay.acc), nclear);
+                     dim3(256), 0, st>>>(bound, nclear);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
@@ -282,13 +331,14 @@ hipError_t launch_codebook_fit(const void* x, int xt, int D, int G, int S, int C
 
   const int ds = dsub < FIT_DS ? dsub : FIT_DS;
   const int nslice = dsub / ds;
-  const int64_t chunks = (n + FIT_CHUNK - 1) / FIT_CHUNK;
+  const int64_t clen = fit_chunk_len(n);
+  const int64_t chunks = fit_chunks(n);
   const size_t alds = (size_t)C * ds * 8 + (size_t)C * 4;
   for (int s = 0; s < S; ++s) {
     const int sp = s + 1;                               // stages run by the assignment
     const int row_bytes = sp * G;
     float* cb_s = cb + (size_t)s * G * C * dsub;
-    const uint32_t* bs = bound + (size_t)s * G;
+    const uint32_t* bs = bound + (size_t)s * FIT_BCOPIES * G;
     const bool last = s == S - 1;
     for (int it = 0; it < n_iter + (last ? 0 : 1); ++it) {
       e = launch_encode(x, xt, D, G, sp, C, 1, n_seq, seq_stride, n_rows, cb, codes, n_rows, 0, 0,
@@ -301,14 +351,15 @@ hipError_t launch_codebook_fit(const void* x, int xt, int D, int G, int S, int C
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)alds);         \
     if (e != hipSuccess) return e;                                                          \
     fit_accum_kernel<DSV><<<dim3((unsigned)(G * nslice), (unsigned)chunks), dim3(256), alds, \
-                            st>>>(r, codes, row_bytes, s, G, C, D, dsub, n, log2n, bs, acc,  \
-                                  cnt);                                                     \
+                            st>>>(r, codes, row_bytes, s, G, C, D, dsub, n, clen, log2n, bs, \
+                                  acc, cnt);                                                \
   }
       KVQ_ACC(8) KVQ_ACC(16) KVQ_ACC(32)
 #undef KVQ_ACC
       e = hipGetLastError();
       if (e != hipSuccess) return e;
-      fit_update_kernel<<<dim3(G), dim3(256), 0, st>>>(cb_s, C, dsub, log2n, bs, acc, cnt);
+      fit_update_kernel<<<dim3(G, dsub), dim3(256), 0, st>>>(cb_s, G, C, dsub, log2n, chunks, bs,
+                                                             acc, cnt);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
@@ -316,7 +367,7 @@ hipError_t launch_codebook_fit(const void* x, int xt, int D, int G, int S, int C
       auto kern = D == 64 ? fit_residual_kernel<64>
                           : D == 128 ? fit_residual_kernel<128> : fit_residual_kernel<256>;
       kern<<<dim3((unsigned)rb), dim3(256), 0, st>>>(r, codes, row_bytes, s, G, C, dsub, cb_s, n,
-                                                      bound + (size_t)(s + 1) * G);
+                                                      bound + (size_t)(s + 1) * FIT_BCOPIES * G);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
     }

@@ -65,8 +65,9 @@ hipError_t launch_smooth_calibrate(const void* x, int xt, int D, int64_t n_books
                                    hipStream_t st);
 
 // Codebook fitting workspace: residuals f32 [N][D], codes [N][S][G], packed
-// codebooks for the assignment, 64-bit accumulators [G][C][dsub], counts
-// [G][C], per-stage bounds [S+1][G]; byte offsets, each 256-aligned.
+// codebooks for the assignment, 64-bit partial sums [chunks][G][dsub][C],
+// partial counts [chunks][G][C], per-stage bounds [S+1][copies][G]; byte
+// offsets, each 256-aligned.
 struct FitLayout {
   size_t resid, codes, pack, acc, cnt, bound, total;
 };

@@ -318,10 +318,12 @@ KVQ_API kvq_status kvq_codebook_fit_workspace_size(const kvq_vq_desc* vq, int64_
  * divided by smoothing factors first when smooth is not NULL: one book,
  * factors [n_scale][D], sequence n using row n % n_scale, as
  * kvq_encode_smooth).  n_seq * n_rows <= 2^24 vectors; 0 <= n_iter <= 100000
- * (0: the entries are left as they are).  The entry means are exact sums of
- * the float32 residuals in 64-bit fixed point (F fraction bits with every term
- * below 2^(62 - ceil(log2 N))), divided in float64 and rounded once to float32,
- * so repeated calls give identical codebooks.  Assignments follow kvq_encode's
+ * (0: the entries are left as they are).  The entry means are sums of the
+ * float32 residuals in 64-bit fixed point (F fraction bits with every term
+ * below 2^(62 - ceil(log2 N)); a residual is taken exactly when it is a
+ * multiple of 2^-F, else truncated toward zero), divided in float64 and
+ * rounded once to float32; integer sums do not depend on the order, so
+ * repeated calls give identical codebooks.  Assignments follow kvq_encode's
  * rule (near ties within a relative 1e-4 may go either way).  Non-finite
  * inputs give unspecified entries. */
 KVQ_API kvq_status kvq_codebook_fit(const void* x, kvq_dtype xt, const kvq_vq_desc* vq,
