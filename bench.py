@@ -20,7 +20,8 @@ window + LUT bytes over the decode call's time); the encode throughput and
 its fraction of the bf16 MFMA peak are reported beside it, and again for the
 32-layer bulk prefill encode; the streaming calls (append, flush) and the
 dual-transform calls (factor calibration, smoothed key encode, decode with
-the factors folded into the query) are timed on the same layer after the
+the factors folded into the query) and the K-means fitting of the key
+codebooks on a 65,536-vector sample are timed on the same layer after the
 step.  ``roofline`` is for the kernel that takes the
 most time in the step; its HBM ``traffic`` comes from the rocprofv3 counter
 summary committed for that kernel, and is null when the kernel's source has
@@ -56,6 +57,9 @@ def parse():
     p.add_argument("--no-prefill", action="store_true",
                    help="skip the 32-layer bulk prefill encode measurement")
     p.add_argument("--no-flush", action="store_true")
+    p.add_argument("--step-only", action="store_true",
+                   help="time the step only (no prefill, streaming, dual-transform or fitting "
+                        "legs), so a profiler sees only the step's kernels")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="run a plain 256 MiB device copy 3x first (scale for HBM counters)")
     return p.parse_args()
@@ -250,12 +254,15 @@ def main():
                               "decode": [round(float(np.percentile(att_ms, p)), 5) for p in (10, 90)]},
         "roofline": roof,
     }
-    res["smooth"] = smooth_calls(torch, kvq, x, cb, q, kc, vc, kw, vw, w, dev, flush)
+    if not args.step_only:
+        res["smooth"] = smooth_calls(torch, kvq, x, cb, q, kc, vc, kw, vw, w, dev, flush)
+        res["fit"] = fit_calls(torch, kvq, x, cb, w, dev)
     del x, recon, flush_buf
     torch.cuda.empty_cache()
-    if not args.no_prefill:
+    if not args.no_prefill and not args.step_only:
         res["encode_prefill"] = prefill_encode(torch, kvq, synth, dev)
-    res["stream"] = stream_calls(torch, kvq, inp, w, dev)
+    if not args.step_only:
+        res["stream"] = stream_calls(torch, kvq, inp, w, dev)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, inp, codes, eff_b, dec_gbs)
     print(json.dumps(res), flush=True)
@@ -353,6 +360,33 @@ def smooth_calls(torch, kvq, x, cb, q, kc, vc, kw, vw, w, dev, flush, reps=20):
             "encode_k_plain_us": round(med["encode_k_plain"] * 1e3, 2),
             "decode_smooth_us": round(med["decode_smooth"] * 1e3, 2),
             "note": f"keys of the layer ({B * Hkv * Tc} vectors), factors one row per KV head"}
+
+
+def fit_calls(torch, kvq, x, cb, w, dev, rows=8192, n_iter=10, reps=5):
+    """K-means fitting of the layer's key codebooks on a sample: the first
+    ``rows`` coded tokens of every KV head (65,536 vectors), ``n_iter``
+    Lloyd iterations from the layer's codebooks."""
+    H, D, S, G, C = w.n_kv_heads, w.head_dim, w.n_stages, w.n_groups, w.n_codewords
+    xk = x[0]                                           # [Hkv][T][D] keys, rows [0, rows) used
+    ws = torch.empty(kvq.codebook_fit_workspace_size(D, G, S, C, H * rows), dtype=torch.uint8,
+                     device=dev)
+    cb0 = cb[0].clone()
+    out = cb0.clone()
+    ms = []
+    for i in range(reps + 1):
+        out.copy_(cb0)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        kvq.codebook_fit(xk, out, n_iter, n_rows=rows, workspace=ws, inplace=True)
+        e1.record()
+        torch.cuda.synchronize()
+        if i >= 1:
+            ms.append(e0.elapsed_time(e1))
+    t = float(np.median(ms))
+    return {"ms": round(t, 4), "ms_per_iteration": round(t / n_iter, 4), "vectors": H * rows,
+            "n_iter": n_iter, "stages": S,
+            "note": "per iteration: assignment (codebook packing + encode of the sample) + "
+                    "fixed-point centroid sums + update; the sample is L2/Infinity-Cache resident"}
 
 
 def stream_calls(torch, kvq, inp, w, dev, reps=20, wcap=192, n_flush=64):
