@@ -8,6 +8,9 @@ from .kvq_oracle import (hadamard_matrix, fwht, nearest, rvq_encode, reconstruct
                          reconstruct, attend, attend_dense, lse_merge, window_append,
                          window_flush, smooth_factors, smooth_rows, smooth_keys, smooth_query,
                          smooth_encode, reconstruct_smooth, lloyd_update, fit_codebooks,
+                         lloyd_max_levels, lloyd_max_distortion, scalar_nearest, boundary_sum,
+                         scalar_rvq_encode, pack_bits, unpack_bits, scalar_reconstruct,
+                         scalar_product_codebook, attend_scalar,
                          code_bytes_per_vector,
                          compression_ratio_vs_fp16)
 from .check import (check_codes, check_recon, check_attn, CODE_REL_TOL, RECON_ATOL,

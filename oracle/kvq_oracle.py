@@ -38,6 +38,12 @@ Sources (page title -- section):
   Codebook fitting: [VI] VecInfer section (codebooks are K-means codebooks
          trained beforehand; the allocator list names train_codebook);
          [VQKV] 2. Methodology (the residual codebooks are trained).
+  Scalar residual variant: [VI] Architecture, TurboQuantRVQ pipeline (rotate,
+         stage-1 Gaussian Lloyd-Max scalar quantiser, residual, stage-2
+         Laplacian Lloyd-Max, indices only, decode by summing then
+         unrotating); module table (turboquant_rvq, Lloyd-Max codebooks,
+         dsa.bit_pack sub-byte index packing); throughput journey
+         (boundary-sum quantise in place of the argmin, same indices).
 
 Parity status of each function is stated in its docstring; every function is
 pinned by ``tests/test_oracle_pins.py`` against closed forms, library routines
@@ -51,6 +57,9 @@ __all__ = ["hadamard_matrix", "fwht", "nearest", "rvq_encode", "reconstruct_rot"
            "reconstruct", "attend", "attend_dense", "lse_merge", "window_append",
            "window_flush", "smooth_factors", "smooth_keys", "smooth_query", "smooth_encode",
            "reconstruct_smooth", "smooth_rows", "lloyd_update", "fit_codebooks",
+           "lloyd_max_levels", "lloyd_max_distortion", "scalar_nearest", "boundary_sum",
+           "scalar_rvq_encode", "pack_bits", "unpack_bits", "scalar_reconstruct",
+           "scalar_product_codebook", "attend_scalar",
            "code_bytes_per_vector",
            "compression_ratio_vs_fp16"]
 
@@ -375,6 +384,155 @@ def fit_codebooks(x, init, n_iter: int, *, rotate: bool = True, with_history: bo
             hist[s][g].append(float(d[np.arange(len(z)), z].sum()))
             r = r - cb[s, g][z]
     return (cb, hist) if with_history else cb
+
+
+# ----------------------------------------------------------------------------
+# Scalar residual variant  [VI Architecture: TurboQuantRVQ pipeline; module
+#       table: turboquant_rvq, Lloyd-Max codebooks, dsa.bit_pack; throughput
+#       journey: boundary-sum quantise]
+# ----------------------------------------------------------------------------
+def _unit_pdf(kind: str):
+    if kind == "gaussian":
+        return lambda t: np.exp(-0.5 * t * t) / np.sqrt(2.0 * np.pi)
+    if kind == "laplacian":
+        s = 1.0 / np.sqrt(2.0)                      # unit variance: scale 1/sqrt(2)
+        return lambda t: np.exp(-np.abs(t) / s) / (2.0 * s)
+    raise ValueError(kind)
+
+
+def lloyd_max_levels(kind: str, bits: int, tol: float = 1e-13, max_iter: int = 10000):
+    """Lloyd-Max quantiser of 2^bits levels for the unit-variance density
+    ``kind`` ("gaussian" or "laplacian"): alternate {thresholds = midpoints of
+    neighbouring levels; level = centroid of the density over its cell}, each
+    integral by adaptive quadrature, until the levels move less than tol.
+    Returns the sorted float64 levels."""
+    from scipy import integrate
+    pdf = _unit_pdf(kind)
+    n = 2 ** bits
+    lv = np.linspace(-2.0, 2.0, n)
+    for _ in range(max_iter):
+        t = (lv[1:] + lv[:-1]) / 2.0
+        edges = np.concatenate([[-np.inf], t, [np.inf]])
+        new = np.empty(n)
+        for k in range(n):
+            a, b = edges[k], edges[k + 1]
+            mass = integrate.quad(pdf, a, b, limit=200)[0]
+            first = integrate.quad(lambda u: u * pdf(u), a, b, limit=200)[0]
+            new[k] = first / mass
+        done = np.max(np.abs(new - lv)) < tol
+        lv = new
+        if done:
+            break
+    return lv
+
+
+def lloyd_max_distortion(kind: str, levels) -> float:
+    """Mean squared error of nearest-level quantisation of the unit-variance
+    density by these levels (by quadrature)."""
+    from scipy import integrate
+    pdf = _unit_pdf(kind)
+    lv = np.asarray(levels, dtype=np.float64)
+    t = (lv[1:] + lv[:-1]) / 2.0
+    edges = np.concatenate([[-np.inf], t, [np.inf]])
+    return float(sum(integrate.quad(lambda u, c=c: (u - c) ** 2 * pdf(u), a, b, limit=200)[0]
+                     for a, b, c in zip(edges[:-1], edges[1:], lv)))
+
+
+def scalar_nearest(y, levels):
+    """Index of the nearest level for every element (lowest index on exact
+    ties), the plain definition."""
+    y = np.asarray(y, dtype=np.float64)
+    lv = np.asarray(levels, dtype=np.float64)
+    return np.argmin((y[..., None] - lv) ** 2, axis=-1).astype(np.uint8)
+
+
+def boundary_sum(y, levels):
+    """The index as the number of decision thresholds (midpoints of sorted
+    neighbouring levels) strictly below the element."""
+    y = np.asarray(y, dtype=np.float64)
+    lv = np.asarray(levels, dtype=np.float64)
+    t = (lv[1:] + lv[:-1]) / 2.0
+    return (y[..., None] > t).sum(axis=-1).astype(np.uint8)
+
+
+def scalar_rvq_encode(x, levels1, levels2, *, rotate: bool = True):
+    """Two-pass scalar residual quantisation of every element of the rotated
+    vectors: z1 = nearest of levels1 to y, r = y - levels1[z1], z2 = nearest
+    of levels2 to r.  x: [N][D].  Returns (z1, z2), uint8 [N][D] each."""
+    y = fwht(x) if rotate else np.asarray(x, dtype=np.float64)
+    l1 = np.asarray(levels1, dtype=np.float64)
+    l2 = np.asarray(levels2, dtype=np.float64)
+    z1 = scalar_nearest(y, l1)
+    z2 = scalar_nearest(y - l1[z1], l2)
+    return z1, z2
+
+
+def pack_bits(z, bits: int):
+    """Sub-byte packing of indices z [..., D] (values < 2^bits, bits in
+    {1, 2, 4}): element i goes to bits [(i mod k)*bits, ...) of byte i // k,
+    k = 8 / bits (least significant first).  Returns uint8 [..., D*bits/8]."""
+    z = np.asarray(z, dtype=np.uint32)
+    k = 8 // bits
+    zz = z.reshape(z.shape[:-1] + (z.shape[-1] // k, k))
+    shifts = (np.arange(k) * bits).astype(np.uint32)
+    return (zz << shifts).sum(axis=-1).astype(np.uint8)
+
+
+def unpack_bits(codes, bits: int):
+    """Inverse of pack_bits: uint8 [..., B] -> indices [..., B*8/bits]."""
+    c = np.asarray(codes, dtype=np.uint32)
+    k = 8 // bits
+    shifts = (np.arange(k) * bits).astype(np.uint32)
+    z = (c[..., None] >> shifts) & ((1 << bits) - 1)
+    return z.reshape(c.shape[:-1] + (c.shape[-1] * k,)).astype(np.uint8)
+
+
+def scalar_reconstruct(z1, z2, levels1, levels2, *, unrotate: bool = True):
+    """y_hat = levels1[z1] + levels2[z2] per element, then H (the decode)."""
+    l1 = np.asarray(levels1, dtype=np.float64)
+    l2 = np.asarray(levels2, dtype=np.float64)
+    y = l1[np.asarray(z1)] + l2[np.asarray(z2)]
+    return fwht(y) if unrotate else y
+
+
+def scalar_product_codebook(levels1, levels2, bits: int, head_dim: int):
+    """The product codebook [2][G][256][k] (k = 8/bits, G = head_dim / k)
+    under which a packed byte of stage s is an ordinary code: entry c holds
+    levels_s[(c >> (j*bits)) & (2^bits - 1)] for j < k, the same for every
+    group.  With it the packed scalar codes decode by reconstruct_rot."""
+    k = 8 // bits
+    G = head_dim // k
+    c = np.arange(256)[:, None]
+    idx = (c >> (np.arange(k)[None, :] * bits)) & ((1 << bits) - 1)
+    out = np.empty((2, G, 256, k))
+    for s, lv in enumerate((levels1, levels2)):
+        out[s] = np.asarray(lv, dtype=np.float64)[idx][None]
+    return out
+
+
+def attend_scalar(q, k_codes, v_codes, k_levels, v_levels, bits, k_win=None, v_win=None,
+                  scale=None):
+    """Decode attention over packed scalar codes: k_codes, v_codes
+    [B][Hkv][Tc][2][D*bits/8] uint8 (stage-1 bytes, then stage-2 bytes);
+    k_levels, v_levels: (levels1, levels2) pairs.  Keys and values of the
+    coded part are scalar_reconstruct of the unpacked indices; the rest as
+    attend."""
+    q = np.asarray(q, dtype=np.float64)
+    B, Hq, D = q.shape
+    scale = 1.0 / np.sqrt(D) if scale is None else float(scale)
+    out = np.empty((B, Hq, D))
+    for b in range(B):
+        parts_k, parts_v = [], []
+        if k_codes is not None and k_codes.shape[2] > 0:
+            for codes, lv, parts in ((k_codes, k_levels, parts_k), (v_codes, v_levels, parts_v)):
+                z = unpack_bits(codes[b], bits)                 # [Hkv][Tc][2][D]
+                parts.append(scalar_reconstruct(z[:, :, 0], z[:, :, 1], lv[0], lv[1]))
+        if k_win is not None and k_win.shape[2] > 0:
+            parts_k.append(np.asarray(k_win[b], dtype=np.float64))
+            parts_v.append(np.asarray(v_win[b], dtype=np.float64))
+        out[b] = attend_dense(q[b], np.concatenate(parts_k, axis=1),
+                              np.concatenate(parts_v, axis=1), scale)
+    return out
 
 
 def lse_merge(parts):

@@ -620,3 +620,99 @@ def test_fit_distortion_never_increases():
             assert len(h) == 9
             assert np.all(np.diff(h) <= 1e-9 * h[0]), h
             assert h[-1] < h[0]
+
+
+# -------------------------------------------------- scalar residual variant
+# "VeloxQuant-MLX 0.5.1": Architecture, TurboQuantRVQ pipeline (Gaussian then
+# Laplacian Lloyd-Max stages on the rotated vector, decode by summing and
+# unrotating); throughput journey (boundary-sum quantise, same indices as the
+# argmin); module table (dsa.bit_pack sub-byte index packing).
+# Lloyd-Max reference values: J. Max, "Quantizing for minimum distortion" (1960),
+# unit-variance Gaussian; M. D. Paez and T. H. Glisson, "Minimum mean-squared-
+# error quantization in speech PCM and DPCM systems" (1972), unit-variance
+# Laplacian.  Positive half of each symmetric level set.
+MAX_GAUSS = {1: [0.7979], 2: [0.4528, 1.510], 3: [0.2451, 0.7560, 1.344, 2.152],
+             4: [0.1284, 0.3881, 0.6568, 0.9424, 1.256, 1.618, 2.069, 2.733]}
+PG_LAPLACE = {1: [0.7071], 2: [0.4198, 1.834], 3: [0.2334, 0.8330, 1.6725, 3.0867]}
+
+
+@pytest.mark.parametrize("kind,table", [("gaussian", MAX_GAUSS), ("laplacian", PG_LAPLACE)])
+def test_lloyd_max_levels_match_published_tables(kind, table):
+    for bits, half in table.items():
+        lv = oracle.lloyd_max_levels(kind, bits)
+        assert np.allclose(lv, -lv[::-1], atol=1e-12)                 # symmetric
+        assert np.allclose(lv[len(lv) // 2:], half, rtol=0, atol=1.5e-3), (kind, bits, lv)
+    one = oracle.lloyd_max_levels(kind, 1)[1]
+    assert np.isclose(one, np.sqrt(2 / np.pi) if kind == "gaussian" else 1 / np.sqrt(2),
+                      rtol=0, atol=1e-10)                            # E|X| in closed form
+
+
+def test_lloyd_max_distortion_closed_form_and_table():
+    g1 = oracle.lloyd_max_distortion("gaussian", oracle.lloyd_max_levels("gaussian", 1))
+    assert np.isclose(g1, 1 - 2 / np.pi, rtol=0, atol=1e-9)
+    for bits, mse in ((2, 0.1175), (3, 0.03454), (4, 0.009497)):      # Max (1960)
+        d = oracle.lloyd_max_distortion("gaussian", oracle.lloyd_max_levels("gaussian", bits))
+        assert np.isclose(d, mse, rtol=2e-3), (bits, d)
+
+
+def test_boundary_sum_equals_nearest_level():
+    """The pages report 100 % index match of boundary-sum against argmin."""
+    rng = np.random.default_rng(41)
+    for bits in (1, 2, 3, 4):
+        for kind in ("gaussian", "laplacian"):
+            lv = oracle.lloyd_max_levels(kind, bits) * rng.uniform(0.3, 3.0)
+            y = rng.standard_normal(50000) * 2
+            assert np.array_equal(oracle.boundary_sum(y, lv), oracle.scalar_nearest(y, lv))
+
+
+def test_pack_bits_hand_fixture_and_roundtrip():
+    assert oracle.pack_bits(np.array([[1, 0, 1, 1, 0, 0, 0, 1]]), 1)[0, 0] == 0x8D
+    assert oracle.pack_bits(np.array([[3, 0, 1, 2]]), 2)[0, 0] == 0x93
+    assert oracle.pack_bits(np.array([[0xA, 0x5]]), 4)[0, 0] == 0x5A
+    rng = np.random.default_rng(42)
+    for bits in (1, 2, 4):
+        z = rng.integers(0, 2 ** bits, size=(7, 128))
+        p = oracle.pack_bits(z, bits)
+        assert p.shape == (7, 128 * bits // 8)
+        assert np.array_equal(oracle.unpack_bits(p, bits), z)
+
+
+@pytest.mark.parametrize("bits", [1, 2, 4])
+def test_product_codebook_decodes_packed_scalar_codes(bits):
+    """A packed byte of stage s is an ordinary code of the product codebook:
+    the VQ reconstruction of the packed codes equals the scalar one."""
+    rng = np.random.default_rng(43)
+    D = 64
+    l1 = oracle.lloyd_max_levels("gaussian", bits) * 1.7
+    l2 = oracle.lloyd_max_levels("laplacian", bits) * 0.4
+    x = rng.standard_normal((300, D)) * 1.7
+    z1, z2 = oracle.scalar_rvq_encode(x, l1, l2)
+    codes = np.stack([oracle.pack_bits(z1, bits), oracle.pack_bits(z2, bits)], axis=1)
+    cb = oracle.scalar_product_codebook(l1, l2, bits, D)
+    assert cb.shape == (2, D * bits // 8, 256, 8 // bits)
+    assert np.array_equal(reconstruct_rot(codes, cb),
+                          oracle.scalar_reconstruct(z1, z2, l1, l2, unrotate=False))
+    # and decode attention over either form agrees
+    q = rng.standard_normal((1, 2, D))
+    kc = codes.reshape(1, 1, 300, 2, -1)
+    a = oracle.attend_scalar(q, kc, kc, (l1, l2), (l1, l2), bits)
+    b = oracle.attend(q, kc, kc, cb, cb)
+    assert np.allclose(a, b, rtol=0, atol=1e-12)
+
+
+def test_scalar_rvq_stage_errors_follow_lloyd_max():
+    """On Gaussian vectors (still Gaussian after the orthonormal rotation) the
+    first stage's mean squared error per element is the Lloyd-Max distortion;
+    the Laplacian second stage, scaled to the residual's deviation, lowers it."""
+    rng = np.random.default_rng(44)
+    x = rng.standard_normal((20000, 64)) * 2.0
+    for bits in (1, 2):
+        d1 = oracle.lloyd_max_distortion("gaussian", oracle.lloyd_max_levels("gaussian", bits))
+        l1 = oracle.lloyd_max_levels("gaussian", bits) * 2.0
+        l2 = oracle.lloyd_max_levels("laplacian", bits) * 2.0 * np.sqrt(d1)
+        z1, z2 = oracle.scalar_rvq_encode(x, l1, l2)
+        y = oracle.fwht(x)
+        e1 = np.mean((y - l1[z1]) ** 2) / 4.0
+        e2 = np.mean((y - oracle.scalar_reconstruct(z1, z2, l1, l2, unrotate=False)) ** 2) / 4.0
+        assert abs(e1 - d1) < 0.02 * d1, (bits, e1, d1)
+        assert e2 < 0.5 * e1
