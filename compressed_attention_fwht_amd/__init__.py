@@ -16,6 +16,8 @@ Calls (same names as the C ABI):
   window_append / window_flush               streaming fp16 window -> codes
   smooth_calibrate(k, n_scale)               dual-transform factors f32 [books][n_scale][D]
   codebook_fit(x, init, n_iter)              K-means codebooks [S][G][C][dsub] f32 on a sample
+  lloyd_max / scalar_encode / scalar_decode_reconstruct / scalar_product_codebook
+                                             two-pass scalar residual variant, packed codes
   (encode, decode_reconstruct, attend_decode and window_flush take the factors
   as ``smooth=`` / ``k_smooth=`` and then call the *_smooth entry points)
 """
@@ -27,7 +29,8 @@ import os
 __all__ = ["KvqError", "LIB_PATH", "lib", "rotate", "encode", "encode_workspace_size",
            "decode_reconstruct", "attend_decode", "attend_workspace_size", "window_append",
            "window_flush", "window_flush_workspace_size", "smooth_calibrate", "codebook_fit",
-           "codebook_fit_workspace_size", "EXPORTS",
+           "codebook_fit_workspace_size", "lloyd_max", "scalar_encode",
+           "scalar_decode_reconstruct", "scalar_product_codebook", "EXPORTS",
            "KVQ_INPUT_PRE_ROTATED", "SmoothDesc",
            "KVQ_UNROTATE", "KVQ_ENCODE_GENERIC", "KVQ_CODEBOOKS_PACKED", "VqDesc", "AttnDesc",
            "status_string"]
@@ -45,6 +48,8 @@ EXPORTS = ("kvq_rotate", "kvq_encode_workspace_size", "kvq_encode", "kvq_decode_
            "kvq_window_flush_workspace_size", "kvq_window_flush", "kvq_smooth_calibrate",
            "kvq_encode_smooth", "kvq_decode_reconstruct_smooth", "kvq_attend_decode_smooth",
            "kvq_window_flush_smooth", "kvq_codebook_fit_workspace_size", "kvq_codebook_fit",
+           "kvq_lloyd_max", "kvq_scalar_encode", "kvq_scalar_decode_reconstruct",
+           "kvq_scalar_product_codebook",
            "kvq_status_string", "kvq_last_hip_error")
 
 
@@ -92,6 +97,11 @@ def _load():
     L.kvq_codebook_fit_workspace_size.argtypes = [ctypes.POINTER(VqDesc), I64, ctypes.POINTER(SZ)]
     L.kvq_codebook_fit.argtypes = [P, I32, ctypes.POINTER(VqDesc), I64, I64, I64, SD, I32, P, P,
                                    SZ, P]
+    DP = ctypes.POINTER(ctypes.c_double)
+    L.kvq_lloyd_max.argtypes = [I32, I32, DP, DP]
+    L.kvq_scalar_encode.argtypes = [P, I32, I32, I32, I64, I64, I64, I64, P, P, U32, P]
+    L.kvq_scalar_decode_reconstruct.argtypes = [P, I32, I32, I64, I64, P, P, U32, P]
+    L.kvq_scalar_product_codebook.argtypes = [I32, I32, P, P, P]
     L.kvq_status_string.argtypes = [I32]
     L.kvq_status_string.restype = ctypes.c_char_p
     L.kvq_last_hip_error.argtypes = []
@@ -228,6 +238,71 @@ def codebook_fit(x, init, n_iter, *, n_rows=None, smooth=None, workspace=None, i
                                    sd, int(n_iter), _ptr(cb), _ptr(workspace), workspace.numel(),
                                    _stream(x)), "kvq_codebook_fit")
     return cb
+
+
+KVQ_LEVELS_GAUSSIAN, KVQ_LEVELS_LAPLACIAN = 0, 1
+
+
+def lloyd_max(kind, bits):
+    """Levels (ascending, float64 list) and mean squared error of the
+    Lloyd-Max quantiser with 2^bits levels for the unit-variance density
+    ``kind`` ("gaussian" or "laplacian"); computed by the library on the host."""
+    k = {"gaussian": KVQ_LEVELS_GAUSSIAN, "laplacian": KVQ_LEVELS_LAPLACIAN}[kind]
+    lv = (ctypes.c_double * (1 << bits))()
+    d = ctypes.c_double(0.0)
+    _check(_lib().kvq_lloyd_max(k, bits, lv, ctypes.byref(d)), "kvq_lloyd_max")
+    return list(lv), d.value
+
+
+def scalar_encode(x, levels, bits, *, n_rows=None, pre_rotated=False, codes=None):
+    """Two-pass scalar codes of rows [0, n_rows) of every sequence of x
+    [n_books][n_seq][seq_stride][D] (f32/bf16/f16); levels f32
+    [n_books][2][2^bits].  Returns u8 [n_books][n_seq][n_rows][2][D*bits/8]."""
+    torch = _torch()
+    _need_contig(x, levels)
+    nb, ns, stride, D = x.shape
+    n_rows = stride if n_rows is None else n_rows
+    if codes is None:
+        codes = torch.empty((nb, ns, n_rows, 2, D * bits // 8), dtype=torch.uint8,
+                            device=x.device)
+    _need_contig(codes)
+    _check(_lib().kvq_scalar_encode(_ptr(x), _dtype_code(x), D, bits, nb, ns, stride, n_rows,
+                                    _ptr(levels), _ptr(codes),
+                                    KVQ_INPUT_PRE_ROTATED if pre_rotated else 0, _stream(x)),
+           "kvq_scalar_encode")
+    return codes
+
+
+def scalar_decode_reconstruct(codes, levels, bits, *, unrotate=False, out=None):
+    """codes u8 [n_books][...][2][D*bits/8], levels f32 [n_books][2][2^bits] ->
+    f32 [n_books][...][D]: levels1[z1] + levels2[z2] (then H_D if unrotate)."""
+    torch = _torch()
+    _need_contig(codes, levels)
+    nb = levels.shape[0]
+    D = codes.shape[-1] * 8 // bits
+    per_book = codes.numel() // (nb * 2 * codes.shape[-1]) if codes.numel() else 0
+    if out is None:
+        out = torch.empty(codes.shape[:-2] + (D,), dtype=torch.float32, device=codes.device)
+    _need_contig(out)
+    _check(_lib().kvq_scalar_decode_reconstruct(_ptr(codes), D, bits, nb, per_book, _ptr(levels),
+                                                _ptr(out), KVQ_UNROTATE if unrotate else 0,
+                                                _stream(codes)),
+           "kvq_scalar_decode_reconstruct")
+    return out
+
+
+def scalar_product_codebook(levels, bits, head_dim, out=None):
+    """The product codebook f32 [2][D*bits/8][256][8/bits] of one book's levels
+    [2][2^bits]; with it kvq_attend_decode reads packed scalar codes."""
+    torch = _torch()
+    _need_contig(levels)
+    G, k = head_dim * bits // 8, 8 // bits
+    if out is None:
+        out = torch.empty((2, G, 256, k), dtype=torch.float32, device=levels.device)
+    _need_contig(out)
+    _check(_lib().kvq_scalar_product_codebook(head_dim, bits, _ptr(levels), _ptr(out),
+                                              _stream(levels)), "kvq_scalar_product_codebook")
+    return out
 
 
 def rotate(x, out=None):

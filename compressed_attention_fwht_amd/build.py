@@ -20,7 +20,7 @@ LIB = os.path.join(PKG, "libkvq.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["kvq_abi.hip", "rotate.hip", "encode.hip", "reconstruct.hip", "attend.hip",
-           "window.hip", "smooth.hip", "fit.hip"]
+           "window.hip", "smooth.hip", "fit.hip", "scalar.hip"]
 
 COMMON = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",

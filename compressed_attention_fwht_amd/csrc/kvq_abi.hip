@@ -12,13 +12,15 @@ thread_local int g_last_hip_error = 0;
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 inline bool pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
 
-kvq_status check_vq(const kvq_vq_desc* vq) {
+// min_dsub: 8 for the encode, reconstruction and fitting kernels, 4 for decode
+// attention (its V contraction works on 4 dims at a time).
+kvq_status check_vq(const kvq_vq_desc* vq, int min_dsub = 8) {
   if (!vq) return KVQ_ERR_NULL;
   const int D = vq->head_dim, G = vq->n_groups, S = vq->n_stages, C = vq->n_codewords;
   if (D != 64 && D != 128 && D != 256) return KVQ_ERR_SHAPE;
   if (G < 1 || G > D || D % G != 0) return KVQ_ERR_SHAPE;
   const int dsub = D / G;
-  if (!pow2(dsub) || dsub < 8 || dsub > 128) return KVQ_ERR_SHAPE;
+  if (!pow2(dsub) || dsub < min_dsub || dsub > 128) return KVQ_ERR_SHAPE;
   if (S < 1 || S > 8) return KVQ_ERR_SHAPE;
   if (C < 1 || C > 256) return KVQ_ERR_SHAPE;
   return KVQ_OK;
@@ -34,7 +36,7 @@ kvq_status hip_status(hipError_t e) {
 
 kvq_status check_attn(const kvq_attn_desc* a, kvq::AttnPlan* plan) {
   if (!a) return KVQ_ERR_NULL;
-  kvq_status st = check_vq(&a->vq);
+  kvq_status st = check_vq(&a->vq, 4);
   if (st != KVQ_OK) return st;
   if (a->batch < 1 || a->n_q_heads < 1 || a->n_kv_heads < 1) return KVQ_ERR_SHAPE;
   if (a->n_q_heads % a->n_kv_heads != 0) return KVQ_ERR_SHAPE;
@@ -241,6 +243,64 @@ kvq_status kvq_codebook_fit(const void* x, kvq_dtype xt, const kvq_vq_desc* vq, 
   return hip_status(kvq::launch_codebook_fit(x, (int)xt, D, G, S, C, n_seq, seq_stride, n_rows,
                                              to_smooth(smooth), n_iter, codebooks, workspace,
                                              stream));
+}
+
+kvq_status kvq_lloyd_max(kvq_levels_kind kind, int32_t bits, double* levels,
+                         double* distortion) {
+  if (kind != KVQ_LEVELS_GAUSSIAN && kind != KVQ_LEVELS_LAPLACIAN) return KVQ_ERR_SHAPE;
+  if (bits < 1 || bits > 4) return KVQ_ERR_SHAPE;
+  if (!levels) return KVQ_ERR_NULL;
+  kvq::lloyd_max((int)kind, bits, levels, distortion);
+  return KVQ_OK;
+}
+
+static bool scalar_bits_ok(int bits) { return bits == 1 || bits == 2 || bits == 4; }
+
+kvq_status kvq_scalar_encode(const void* x, kvq_dtype xt, int32_t head_dim, int32_t bits,
+                             int64_t n_books, int64_t n_seq, int64_t seq_stride, int64_t n_rows,
+                             const float* levels, uint8_t* codes, uint32_t flags,
+                             hipStream_t stream) {
+  if (!valid_dtype(xt)) return KVQ_ERR_DTYPE;
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256) return KVQ_ERR_SHAPE;
+  if (!scalar_bits_ok(bits)) return KVQ_ERR_SHAPE;
+  if (flags & ~KVQ_INPUT_PRE_ROTATED) return KVQ_ERR_SHAPE;
+  if (n_books < 0 || n_seq < 0 || seq_stride < 0 || n_rows < 0 || n_rows > seq_stride)
+    return KVQ_ERR_SHAPE;
+  if (n_books == 0 || n_seq == 0 || n_rows == 0) return KVQ_OK;
+  if (n_books > 65535) return KVQ_ERR_UNSUPPORTED;
+  if (n_seq > ((int64_t)1 << 40) / n_rows) return KVQ_ERR_SHAPE;
+  if (!x || !levels || !codes) return KVQ_ERR_NULL;
+  if (!aligned16(x) || !aligned16(levels) || !aligned16(codes)) return KVQ_ERR_ALIGN;
+  return hip_status(kvq::launch_scalar_encode(x, (int)xt, head_dim, bits, n_books, n_seq,
+                                              seq_stride, n_rows, levels, codes,
+                                              (flags & KVQ_INPUT_PRE_ROTATED) ? 1 : 0, stream));
+}
+
+kvq_status kvq_scalar_decode_reconstruct(const uint8_t* codes, int32_t head_dim, int32_t bits,
+                                         int64_t n_books, int64_t n_per_book,
+                                         const float* levels, float* out, uint32_t flags,
+                                         hipStream_t stream) {
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256) return KVQ_ERR_SHAPE;
+  if (!scalar_bits_ok(bits)) return KVQ_ERR_SHAPE;
+  if (flags & ~KVQ_UNROTATE) return KVQ_ERR_SHAPE;
+  if (n_books < 0 || n_per_book < 0) return KVQ_ERR_SHAPE;
+  if (n_books == 0 || n_per_book == 0) return KVQ_OK;
+  if (n_books > 65535) return KVQ_ERR_UNSUPPORTED;
+  if (n_per_book > ((int64_t)1 << 40) / n_books) return KVQ_ERR_SHAPE;
+  if (!codes || !levels || !out) return KVQ_ERR_NULL;
+  if (!aligned16(codes) || !aligned16(levels) || !aligned16(out)) return KVQ_ERR_ALIGN;
+  return hip_status(kvq::launch_scalar_reconstruct(codes, head_dim, bits, n_books, n_per_book,
+                                                   levels, out,
+                                                   (flags & KVQ_UNROTATE) ? 1 : 0, stream));
+}
+
+kvq_status kvq_scalar_product_codebook(int32_t head_dim, int32_t bits, const float* levels,
+                                       float* codebooks, hipStream_t stream) {
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256) return KVQ_ERR_SHAPE;
+  if (!scalar_bits_ok(bits)) return KVQ_ERR_SHAPE;
+  if (!levels || !codebooks) return KVQ_ERR_NULL;
+  if (!aligned16(levels) || !aligned16(codebooks)) return KVQ_ERR_ALIGN;
+  return hip_status(kvq::launch_scalar_product_cb(levels, head_dim, bits, codebooks, stream));
 }
 
 kvq_status kvq_decode_reconstruct(const uint8_t* codes, const kvq_vq_desc* vq, int64_t n_books,

@@ -76,6 +76,18 @@ hipError_t launch_codebook_fit(const void* x, int xt, int D, int G, int S, int C
                                int64_t seq_stride, int64_t n_rows, Smooth sm, int n_iter,
                                float* cb, void* ws, hipStream_t st);
 
+// Scalar residual variant (bits in {1, 2, 4}); lloyd_max runs on the host.
+int lloyd_max(int kind, int bits, double* levels, double* distortion);
+hipError_t launch_scalar_encode(const void* x, int xt, int D, int bits, int64_t n_books,
+                                int64_t n_seq, int64_t seq_stride, int64_t n_rows,
+                                const float* levels, uint8_t* codes, int pre_rotated,
+                                hipStream_t st);
+hipError_t launch_scalar_reconstruct(const uint8_t* codes, int D, int bits, int64_t n_books,
+                                     int64_t n, const float* levels, float* out, int unrotate,
+                                     hipStream_t st);
+hipError_t launch_scalar_product_cb(const float* levels, int D, int bits, float* cb,
+                                    hipStream_t st);
+
 hipError_t launch_window_append(const uint16_t* kn, const uint16_t* vn, uint16_t* kw,
                                 uint16_t* vw, int64_t units, int D, int wcap, int row,
                                 hipStream_t st);

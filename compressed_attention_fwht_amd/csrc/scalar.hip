@@ -1,0 +1,304 @@
+// Scalar residual variant: two-pass scalar quantisation of the rotated vector
+// with sub-byte index packing.
+//
+// "VeloxQuant-MLX 0.5.1": Architecture, TurboQuantRVQ pipeline -- rotate,
+// stage-1 Gaussian Lloyd-Max scalar quantiser, residual, stage-2 Laplacian
+// Lloyd-Max, the indices only, decode by summing the two levels and
+// unrotating; throughput journey -- the index as a sum over decision
+// boundaries instead of an argmin (same indices); module table --
+// dsa.bit_pack sub-byte packing.
+//
+// Codes: a vector's row is [stage-1 bytes][stage-2 bytes], D*b/8 bytes each;
+// element i of a stage sits in bits [(i mod k)*b, ...) of byte i / k (k = 8/b,
+// least significant first).  A byte of stage s therefore is a code of the
+// product codebook whose entry c lists levels_s[(c >> j*b) & (2^b - 1)] for
+// j < k -- scalar_product_cb_kernel writes it, so the decode-attention kernels
+// read packed scalar codes as ordinary product codes (G = D*b/8 groups of k
+// dims, C = 256).
+//
+// Layout per lane as elsewhere: L = D/8 lanes per row, 8 consecutive elements
+// per lane, so a lane's indices fill b whole bytes per stage.  HBM-bound:
+// 2 (or 4) bytes in and b/4 bytes out per element.
+#include <math.h>
+
+#include "kvq_internal.h"
+
+namespace kvq {
+
+// -------------------------------------------------------------- Lloyd-Max
+// Moments of a unit-variance density over [a, b] (a < b, either may be
+// infinite): mass, first and second moments, in closed form.
+namespace {
+struct Moments {
+  double m0, m1, m2;
+};
+
+constexpr double kPi = 3.14159265358979323846;
+inline double phi(double t) { return isinf(t) ? 0.0 : exp(-0.5 * t * t) / sqrt(2.0 * kPi); }
+inline double Phi(double t) { return 0.5 * erfc(-t / sqrt(2.0)); }
+
+Moments gauss_moments(double a, double b) {
+  // int phi = Phi(b) - Phi(a); int t phi = phi(a) - phi(b);
+  // int t^2 phi = Phi(b) - Phi(a) - (b phi(b) - a phi(a))
+  const double ta = isinf(a) ? 0.0 : a * phi(a), tb = isinf(b) ? 0.0 : b * phi(b);
+  const double m0 = Phi(b) - Phi(a);
+  return {m0, phi(a) - phi(b), m0 - (tb - ta)};
+}
+
+// Laplace with scale beta = 1/sqrt(2) (unit variance), on [a, b] with a >= 0:
+// int_a^b e^(-x/beta) / (2 beta) x^n dx through the antiderivatives.
+Moments laplace_pos(double a, double b) {
+  const double be = 1.0 / sqrt(2.0);
+  auto F = [&](double x, int n) -> double {          // value of -0.5 e^(-x/be) P_n(x)
+    if (isinf(x)) return 0.0;
+    const double e = exp(-x / be);
+    if (n == 0) return -0.5 * e;
+    if (n == 1) return -0.5 * e * (x + be);
+    return -0.5 * e * (x * x + 2.0 * be * x + 2.0 * be * be);
+  };
+  return {F(b, 0) - F(a, 0), F(b, 1) - F(a, 1), F(b, 2) - F(a, 2)};
+}
+
+Moments laplace_moments(double a, double b) {
+  if (a >= 0.0) return laplace_pos(a, b);
+  if (b <= 0.0) {                                     // mirror: x -> -x
+    const Moments m = laplace_pos(-b, -a);
+    return {m.m0, -m.m1, m.m2};
+  }
+  const Moments l = laplace_pos(0.0, -a), r = laplace_pos(0.0, b);
+  return {l.m0 + r.m0, r.m1 - l.m1, l.m2 + r.m2};
+}
+}  // namespace
+
+int lloyd_max(int kind, int bits, double* levels, double* distortion) {
+  const int n = 1 << bits;
+  auto mom = [&](double a, double b) {
+    return kind == 0 ? gauss_moments(a, b) : laplace_moments(a, b);
+  };
+  for (int k = 0; k < n; ++k) levels[k] = n > 1 ? -2.0 + 4.0 * k / (n - 1) : 0.0;
+  double edges[17];
+  for (int it = 0; it < 100000; ++it) {
+    edges[0] = -INFINITY;
+    edges[n] = INFINITY;
+    for (int k = 1; k < n; ++k) edges[k] = 0.5 * (levels[k - 1] + levels[k]);
+    double moved = 0.0;
+    for (int k = 0; k < n; ++k) {
+      const Moments m = mom(edges[k], edges[k + 1]);
+      const double c = m.m1 / m.m0;
+      moved = fmax(moved, fabs(c - levels[k]));
+      levels[k] = c;
+    }
+    if (moved < 1e-15) break;
+  }
+  if (distortion) {
+    edges[0] = -INFINITY;
+    edges[n] = INFINITY;
+    for (int k = 1; k < n; ++k) edges[k] = 0.5 * (levels[k - 1] + levels[k]);
+    double d = 0.0;
+    for (int k = 0; k < n; ++k) {                     // int (t - c)^2 = m2 - 2 c m1 + c^2 m0
+      const Moments m = mom(edges[k], edges[k + 1]);
+      d += m.m2 - 2.0 * levels[k] * m.m1 + levels[k] * levels[k] * m.m0;
+    }
+    *distortion = d;
+  }
+  return 0;
+}
+
+// ---------------------------------------------------------------- kernels
+// Levels of the block's book staged in LDS with the decision thresholds
+// (midpoints of neighbouring levels, float32).
+template <int B>
+__device__ __forceinline__ void stage_levels(const float* __restrict__ levels, int64_t book,
+                                             float (&lv)[2][1 << B], float (&th)[2][1 << B]) {
+  constexpr int NL = 1 << B;
+  const int tid = threadIdx.x;
+  if (tid < 2 * NL) lv[tid / NL][tid % NL] = levels[book * 2 * NL + tid];
+  __syncthreads();
+  if (tid < 2 * NL && tid % NL < NL - 1)
+    th[tid / NL][tid % NL] = 0.5f * (lv[tid / NL][tid % NL] + lv[tid / NL][tid % NL + 1]);
+  __syncthreads();
+}
+
+template <int B>
+__device__ __forceinline__ int bsum(float v, const float* th) {
+  int z = 0;
+#pragma unroll
+  for (int k = 0; k < (1 << B) - 1; ++k) z += v > th[k] ? 1 : 0;
+  return z;
+}
+
+// grid (row blocks, n_books), 256 threads; grid-stride over the book's rows.
+template <int D, int XT, int B>
+__global__ __launch_bounds__(256) void scalar_encode_kernel(
+    const void* __restrict__ x, const float* __restrict__ levels, uint8_t* __restrict__ codes,
+    int64_t n_seq, int64_t seq_stride, int64_t n_rows, int pre_rotated) {
+  constexpr int L = D / 8;
+  constexpr int RPB = 256 / L;                          // rows per block pass
+  constexpr int ESZ = XT == 0 ? 4 : 2;
+  constexpr int SB = D * B / 8;                         // bytes per stage
+  __shared__ float lv[2][1 << B], th[2][1 << B];
+  const int64_t book = blockIdx.y;
+  stage_levels<B>(levels, book, lv, th);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int col = tid % L, rsub = tid / L;
+  const int64_t n = n_seq * n_rows;
+  for (int64_t base = (int64_t)blockIdx.x * RPB; base < n; base += (int64_t)gridDim.x * RPB) {
+    const int64_t v = base + rsub;
+    const int64_t vl = v < n ? v : n - 1;               // every lane joins the butterfly
+    const int64_t seq = vl / n_rows, row = vl - seq * n_rows;
+    float y[8];
+    load8<XT>(reinterpret_cast<const char*>(x) +
+                  (((book * n_seq + seq) * seq_stride + row) * D + col * 8) * ESZ,
+              y);
+    if (!pre_rotated) {
+      hadamard_row<8, L>(y, lane);
+      constexpr float sc = rsqrt_pow2(D);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] *= sc;
+    }
+    uint32_t p1 = 0u, p2 = 0u;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int z1 = bsum<B>(y[e], th[0]);
+      const int z2 = bsum<B>(y[e] - lv[0][z1], th[1]);
+      p1 |= (uint32_t)z1 << (e * B);
+      p2 |= (uint32_t)z2 << (e * B);
+    }
+    if (v < n) {
+      uint8_t* rowp = codes + (book * n + v) * (2 * SB) + col * B;
+      if constexpr (B == 1) {
+        rowp[0] = (uint8_t)p1;
+        rowp[SB] = (uint8_t)p2;
+      } else if constexpr (B == 2) {
+        *reinterpret_cast<uint16_t*>(rowp) = (uint16_t)p1;
+        *reinterpret_cast<uint16_t*>(rowp + SB) = (uint16_t)p2;
+      } else {
+        *reinterpret_cast<uint32_t*>(rowp) = p1;
+        *reinterpret_cast<uint32_t*>(rowp + SB) = p2;
+      }
+    }
+  }
+}
+
+// grid (row blocks, n_books); out = levels1[z1] + levels2[z2] (one float32
+// rounding of the sum), then H_D when unrotate.
+template <int D, int B>
+__global__ __launch_bounds__(256) void scalar_reconstruct_kernel(
+    const uint8_t* __restrict__ codes, const float* __restrict__ levels, float* __restrict__ out,
+    int64_t n, int unrotate) {
+  constexpr int L = D / 8;
+  constexpr int RPB = 256 / L;
+  constexpr int SB = D * B / 8;
+  constexpr uint32_t MASK = (1u << B) - 1u;
+  __shared__ float lv[2][1 << B], th[2][1 << B];
+  const int64_t book = blockIdx.y;
+  stage_levels<B>(levels, book, lv, th);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int col = tid % L, rsub = tid / L;
+  for (int64_t base = (int64_t)blockIdx.x * RPB; base < n; base += (int64_t)gridDim.x * RPB) {
+    const int64_t v = base + rsub;
+    const int64_t vl = v < n ? v : n - 1;
+    const uint8_t* rowp = codes + (book * n + vl) * (2 * SB) + col * B;
+    uint32_t p1, p2;
+    if constexpr (B == 1) {
+      p1 = rowp[0];
+      p2 = rowp[SB];
+    } else if constexpr (B == 2) {
+      p1 = *reinterpret_cast<const uint16_t*>(rowp);
+      p2 = *reinterpret_cast<const uint16_t*>(rowp + SB);
+    } else {
+      p1 = *reinterpret_cast<const uint32_t*>(rowp);
+      p2 = *reinterpret_cast<const uint32_t*>(rowp + SB);
+    }
+    float y[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      y[e] = lv[0][(p1 >> (e * B)) & MASK] + lv[1][(p2 >> (e * B)) & MASK];
+    if (unrotate) {
+      hadamard_row<8, L>(y, lane);
+      constexpr float sc = rsqrt_pow2(D);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] *= sc;
+    }
+    if (v < n) {
+      float4* o = reinterpret_cast<float4*>(out + (book * n + v) * D + col * 8);
+      o[0] = make_float4(y[0], y[1], y[2], y[3]);
+      o[1] = make_float4(y[4], y[5], y[6], y[7]);
+    }
+  }
+}
+
+// cb[s][g][c][j] = levels_s[(c >> j*B) & MASK], j < 8/B, the same for every g.
+template <int B>
+__global__ __launch_bounds__(256) void scalar_product_cb_kernel(const float* __restrict__ levels,
+                                                                float* __restrict__ cb, int G) {
+  constexpr int K = 8 / B;
+  constexpr uint32_t MASK = (1u << B) - 1u;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;    // (s, g, c)
+  if (i >= (int64_t)2 * G * 256) return;
+  const int c = (int)(i % 256);
+  const int s = (int)(i / ((int64_t)G * 256));
+  float* dst = cb + i * K;
+#pragma unroll
+  for (int j = 0; j < K; ++j) dst[j] = levels[s * (1 << B) + ((c >> (j * B)) & MASK)];
+}
+
+// ---------------------------------------------------------------- launchers
+static unsigned row_grid(int64_t n, int D) {
+  const int64_t rpb = 256 / (D / 8);
+  int64_t b = (n + rpb - 1) / rpb;
+  if (b > 4096) b = 4096;
+  return (unsigned)(b > 0 ? b : 1);
+}
+
+hipError_t launch_scalar_encode(const void* x, int xt, int D, int bits, int64_t n_books,
+                                int64_t n_seq, int64_t seq_stride, int64_t n_rows,
+                                const float* levels, uint8_t* codes, int pre_rotated,
+                                hipStream_t st) {
+  const int64_t n = n_seq * n_rows;
+  if (n == 0 || n_books == 0) return hipSuccess;
+  const dim3 grid(row_grid(n, D), (unsigned)n_books);
+#define KVQ_SE(DD, XX, BB)                                                                 \
+  if (D == DD && xt == XX && bits == BB) {                                                \
+    scalar_encode_kernel<DD, XX, BB><<<grid, dim3(256), 0, st>>>(x, levels, codes, n_seq,  \
+                                                                 seq_stride, n_rows,       \
+                                                                 pre_rotated);             \
+    return hipGetLastError();                                                              \
+  }
+#define KVQ_SE_D(DD)                                                                      \
+  KVQ_SE(DD, 0, 1) KVQ_SE(DD, 0, 2) KVQ_SE(DD, 0, 4) KVQ_SE(DD, 1, 1) KVQ_SE(DD, 1, 2)     \
+  KVQ_SE(DD, 1, 4) KVQ_SE(DD, 2, 1) KVQ_SE(DD, 2, 2) KVQ_SE(DD, 2, 4)
+  KVQ_SE_D(64) KVQ_SE_D(128) KVQ_SE_D(256)
+#undef KVQ_SE_D
+#undef KVQ_SE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_scalar_reconstruct(const uint8_t* codes, int D, int bits, int64_t n_books,
+                                     int64_t n, const float* levels, float* out, int unrotate,
+                                     hipStream_t st) {
+  if (n == 0 || n_books == 0) return hipSuccess;
+  const dim3 grid(row_grid(n, D), (unsigned)n_books);
+#define KVQ_SR(DD, BB)                                                                     \
+  if (D == DD && bits == BB) {                                                             \
+    scalar_reconstruct_kernel<DD, BB><<<grid, dim3(256), 0, st>>>(codes, levels, out, n,    \
+                                                                  unrotate);               \
+    return hipGetLastError();                                                              \
+  }
+  KVQ_SR(64, 1) KVQ_SR(64, 2) KVQ_SR(64, 4) KVQ_SR(128, 1) KVQ_SR(128, 2) KVQ_SR(128, 4)
+  KVQ_SR(256, 1) KVQ_SR(256, 2) KVQ_SR(256, 4)
+#undef KVQ_SR
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_scalar_product_cb(const float* levels, int D, int bits, float* cb,
+                                    hipStream_t st) {
+  const int G = D * bits / 8;
+  const unsigned blocks = (unsigned)((2 * G * 256 + 255) / 256);
+  if (bits == 1) scalar_product_cb_kernel<1><<<blocks, 256, 0, st>>>(levels, cb, G);
+  else if (bits == 2) scalar_product_cb_kernel<2><<<blocks, 256, 0, st>>>(levels, cb, G);
+  else scalar_product_cb_kernel<4><<<blocks, 256, 0, st>>>(levels, cb, G);
+  return hipGetLastError();
+}
+
+}  // namespace kvq

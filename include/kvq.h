@@ -332,6 +332,59 @@ KVQ_API kvq_status kvq_codebook_fit(const void* x, kvq_dtype xt, const kvq_vq_de
                             float* codebooks, void* workspace, size_t ws_bytes,
                             hipStream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * Scalar residual variant ("VeloxQuant-MLX 0.5.1": Architecture, TurboQuantRVQ
+ * pipeline -- rotate, stage-1 Gaussian Lloyd-Max scalar quantiser, residual,
+ * stage-2 Laplacian Lloyd-Max, the indices only, decode by summing the two
+ * levels and unrotating; throughput journey -- the index counted over decision
+ * boundaries instead of an argmin; module table -- dsa.bit_pack sub-byte
+ * index packing).  bits b in {1, 2, 4}: 2^b levels per stage.
+ *
+ * Codes: a vector's row is [stage-1 bytes][stage-2 bytes], D*b/8 bytes each;
+ * element i of a stage occupies bits [(i mod k)*b, (i mod k)*b + b) of byte
+ * i / k, k = 8/b, least significant first.  Levels: float32
+ * [n_books][2][2^b], each stage's levels strictly increasing (stage 1 for the
+ * rotated element, stage 2 for its residual); other orders give unspecified
+ * codes (no fault).  A byte of stage s is also a code of the product codebook
+ * kvq_scalar_product_codebook writes, so kvq_attend_decode reads scalar codes
+ * with vq = {D, G = D*b/8, S = 2, C = 256} (b in {1, 2}: the decode needs at
+ * least 4 dims per group).
+ * ------------------------------------------------------------------------ */
+typedef enum { KVQ_LEVELS_GAUSSIAN = 0, KVQ_LEVELS_LAPLACIAN = 1 } kvq_levels_kind;
+
+/* Host call (no GPU): the 2^bits levels (ascending) of the Lloyd-Max
+ * quantiser for the unit-variance Gaussian or Laplacian density, iterated to a
+ * fixed point with the cell moments in closed form; *distortion (if not NULL)
+ * receives its mean squared error.  bits in 1..4; levels: host [2^bits]. */
+KVQ_API kvq_status kvq_lloyd_max(kvq_levels_kind kind, int32_t bits, double* levels,
+                         double* distortion);
+
+/* y = H_D x (unless KVQ_INPUT_PRE_ROTATED); per element z1 = number of
+ * stage-1 thresholds (float32 midpoints of neighbouring levels) strictly below
+ * y, r = y - levels1[z1], z2 likewise on r with the stage-2 levels; packed as
+ * above.  x: [n_books][n_seq][seq_stride][D] of type xt, rows [0, n_rows);
+ * levels: [n_books][2][2^b]; codes: [n_books][n_seq][n_rows][2][D*b/8].
+ * Equals the nearest level per stage except where an element lies within
+ * float32 rounding of a threshold. */
+KVQ_API kvq_status kvq_scalar_encode(const void* x, kvq_dtype xt, int32_t head_dim, int32_t bits,
+                             int64_t n_books, int64_t n_seq, int64_t seq_stride,
+                             int64_t n_rows, const float* levels, uint8_t* codes,
+                             uint32_t flags, hipStream_t stream);
+
+/* out[b][n] = levels1[z1] + levels2[z2] per element (float32), then H_D with
+ * KVQ_UNROTATE.  codes: [n_books][n_per_book][2][D*b/8]; out:
+ * [n_books][n_per_book][D] float32. */
+KVQ_API kvq_status kvq_scalar_decode_reconstruct(const uint8_t* codes, int32_t head_dim,
+                                         int32_t bits, int64_t n_books, int64_t n_per_book,
+                                         const float* levels, float* out, uint32_t flags,
+                                         hipStream_t stream);
+
+/* codebooks[s][g][c][j] = levels[s][(c >> j*b) & (2^b - 1)] for s < 2,
+ * g < D*b/8, c < 256, j < 8/b (one book's levels [2][2^b]). */
+KVQ_API kvq_status kvq_scalar_product_codebook(int32_t head_dim, int32_t bits,
+                                       const float* levels, float* codebooks,
+                                       hipStream_t stream);
+
 /* Static description of a status code. */
 KVQ_API const char* kvq_status_string(kvq_status status);
 

@@ -13,5 +13,5 @@ from .kvq_oracle import (hadamard_matrix, fwht, nearest, rvq_encode, reconstruct
                          scalar_product_codebook, attend_scalar,
                          code_bytes_per_vector,
                          compression_ratio_vs_fp16)
-from .check import (check_codes, check_recon, check_attn, CODE_REL_TOL, RECON_ATOL,
-                    ATTN_ATOL, ATTN_REL_L2)
+from .check import (check_codes, check_scalar_codes, check_recon, check_attn, CODE_REL_TOL,
+                    RECON_ATOL, ATTN_ATOL, ATTN_REL_L2, SCALAR_REL_TOL)

@@ -7,6 +7,11 @@ tolerances:
     tie, where several codes are correct).  After any accepted choice the
     oracle continues the residual chain from that choice (teacher forcing), so
     one near tie does not make later stages look wrong;
+  * scalar codes: equal to the oracle's nearest level, except where the
+    element lies within SCALAR_REL_TOL * rms(row) of the decision threshold
+    between the two levels (float32 rotation error is below a quarter of that
+    at head_dim 128); stage 2 is checked on the residual of the candidate's
+    stage-1 choice;
   * reconstructed vectors: within 1e-6 absolute;
   * attention outputs: within 2e-3 max-abs and 1e-3 relative L2.
 """
@@ -14,12 +19,13 @@ from __future__ import annotations
 
 import numpy as np
 
-from .kvq_oracle import fwht, nearest
+from .kvq_oracle import fwht, nearest, scalar_nearest
 
 CODE_REL_TOL = 1e-4
 RECON_ATOL = 1e-6
 ATTN_ATOL = 2e-3
 ATTN_REL_L2 = 1e-3
+SCALAR_REL_TOL = 2e-5
 
 
 def check_codes(x, codebooks, codes, *, rotate=True, rel_tol=CODE_REL_TOL, block=4096):
@@ -65,6 +71,31 @@ def check_codes(x, codebooks, codes, *, rotate=True, rel_tol=CODE_REL_TOL, block
     total = x.shape[0] * S * G
     return {"total": total, "exact": n_exact, "near_tie": n_tie, "hard": n_hard,
             "worst_rel_excess": worst, "hard_examples": hard_at}
+
+
+def check_scalar_codes(y, levels1, levels2, z1, z2, *, rel_tol=SCALAR_REL_TOL):
+    """Teacher-forced check of candidate scalar indices z1, z2 [N][D] against
+    the nearest levels of the rotated vectors y [N][D] (float64).  A
+    non-matching index is accepted when its distance exceeds the best one by
+    at most 2 * rel_tol * rms(row) (the element within rel_tol * rms(row) of
+    the threshold)."""
+    y = np.asarray(y, dtype=np.float64)
+    l1 = np.asarray(levels1, dtype=np.float64)
+    l2 = np.asarray(levels2, dtype=np.float64)
+    tol = 2.0 * rel_tol * np.sqrt(np.mean(y * y, axis=-1, keepdims=True))
+    out = {"total": 2 * y.size, "exact": 0, "near_tie": 0, "hard": 0}
+    r = y
+    for lv, zc in ((l1, np.asarray(z1)), (l2, np.asarray(z2))):
+        zo = scalar_nearest(r, lv)
+        dc = np.abs(r - lv[zc])
+        do = np.abs(r - lv[zo])
+        exact = zc == zo
+        ok = dc <= do + tol
+        out["exact"] += int(exact.sum())
+        out["near_tie"] += int((~exact & ok).sum())
+        out["hard"] += int((~exact & ~ok).sum())
+        r = r - lv[zc]
+    return out
 
 
 def check_recon(got, ref, atol=RECON_ATOL):

@@ -263,3 +263,52 @@ def test_codebook_fit_argument_errors():
     assert fit(wsb=1000) == WS
     assert fit(sd=ctypes.byref(_sd(n=0))) == SHAPE
     assert fit(ns=0, x=0, cb=0, ws=0) == OK               # empty sample: no-op
+
+
+def test_lloyd_max_host_call_matches_the_oracle():
+    """kvq_lloyd_max runs on the host (no GPU): its closed-form moments agree
+    with the oracle's quadrature."""
+    import oracle
+    for kind in ("gaussian", "laplacian"):
+        for bits in (1, 2, 3, 4):
+            lv, d = kvq.lloyd_max(kind, bits)
+            ref = oracle.lloyd_max_levels(kind, bits)
+            assert max(abs(a - b) for a, b in zip(lv, ref)) < 1e-9, (kind, bits)
+            assert abs(d - oracle.lloyd_max_distortion(kind, ref)) < 1e-9
+    L = kvq.lib
+    buf = (ctypes.c_double * 16)()
+    assert L.kvq_lloyd_max(2, 2, buf, None) == SHAPE
+    assert L.kvq_lloyd_max(0, 5, buf, None) == SHAPE
+    assert L.kvq_lloyd_max(0, 2, None, None) == NULL
+
+
+def test_scalar_argument_errors():
+    L = kvq.lib
+    enc = lambda x=FAKE, xt=1, D=128, b=2, nb=1, ns=2, st=64, nr=64, lv=FAKE, c=FAKE, fl=0: \
+        L.kvq_scalar_encode(x, xt, D, b, nb, ns, st, nr, lv, c, fl, None)
+    assert enc(xt=4) == DTYPE
+    assert enc(D=96) == SHAPE
+    assert enc(b=3) == SHAPE                           # packing covers 1, 2, 4 bits
+    assert enc(nr=65) == SHAPE
+    assert enc(fl=0x2) == SHAPE
+    assert enc(lv=0) == NULL
+    assert enc(c=FAKE + 1) == ALIGN
+    assert enc(ns=0, x=0, lv=0, c=0) == OK
+    rec = lambda b=2, nb=1, n=10, lv=FAKE, o=FAKE, fl=0: \
+        L.kvq_scalar_decode_reconstruct(FAKE, 128, b, nb, n, lv, o, fl, None)
+    assert rec(b=8) == SHAPE
+    assert rec(fl=0x1) == SHAPE
+    assert rec(o=0) == NULL
+    assert rec(n=0, o=0) == OK
+    assert L.kvq_scalar_product_codebook(128, 3, FAKE, FAKE, None) == SHAPE
+    assert L.kvq_scalar_product_codebook(128, 2, FAKE, 0, None) == NULL
+    # decode attention accepts 4-dim groups (2-bit scalar codes), not 2-dim ones
+    sz = ctypes.c_size_t(0)
+    a4 = kvq.AttnDesc(1, 4, 1, 100, 0, kvq.VqDesc(128, 32, 2, 256), 0.0, 0, 0)
+    assert L.kvq_attend_workspace_size(ctypes.byref(a4), ctypes.byref(sz)) == OK
+    a2 = kvq.AttnDesc(1, 4, 1, 100, 0, kvq.VqDesc(128, 64, 2, 256), 0.0, 0, 0)
+    assert L.kvq_attend_workspace_size(ctypes.byref(a2), ctypes.byref(sz)) == SHAPE
+    # the encode still needs 8 dims per group
+    vq4 = kvq.VqDesc(128, 32, 2, 256)
+    assert L.kvq_encode(FAKE, 1, ctypes.byref(vq4), 1, 1, 64, 64, FAKE, FAKE, 0, FAKE, 1 << 30,
+                        None) == SHAPE

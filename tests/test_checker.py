@@ -1,6 +1,7 @@
 """Unit tests of the tolerance checker with constructed near ties.  CPU only."""
 import numpy as np
 
+import oracle
 from oracle import check_codes, check_recon, check_attn, rvq_encode
 
 
@@ -59,3 +60,24 @@ def test_recon_and_attn_rules():
     small = np.full((2, 3, 64), 1e-3)
     r = check_attn(small * 1.5, small)                    # relative L2 rule
     assert r["max_abs"] < 2e-3 and not r["ok"]
+
+
+def test_scalar_checker_rules():
+    """Exact indices pass; an index on the wrong side of a threshold by a hair
+    is a near tie; a far one is hard; stage 2 follows the candidate's stage 1."""
+    lv1 = np.array([-1.5, -0.5, 0.5, 1.5])
+    lv2 = np.array([-0.3, -0.1, 0.1, 0.3])
+    y = np.array([[0.2, -0.9, 1.0 + 1e-7, 1.4] * 4])            # rms ~ 1
+    z1 = oracle.scalar_nearest(y, lv1)
+    z2 = oracle.scalar_nearest(y - lv1[z1], lv2)
+    res = oracle.check_scalar_codes(y, lv1, lv2, z1, z2)
+    assert res["exact"] == res["total"] == 32 and res["hard"] == 0
+    zt = z1.copy()
+    zt[0, 2] = 2                                                 # 1.0 + 1e-7: threshold by a hair
+    z2t = oracle.scalar_nearest(y - lv1[zt], lv2)                # stage 2 on the candidate's residual
+    res = oracle.check_scalar_codes(y, lv1, lv2, zt, z2t)
+    assert res["near_tie"] == 1 and res["hard"] == 0
+    zf = z1.copy()
+    zf[0, 0] = 0                                                 # 0.2 coded as -1.5: hard
+    res = oracle.check_scalar_codes(y, lv1, lv2, zf, z2)
+    assert res["hard"] >= 1
