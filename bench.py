@@ -20,9 +20,11 @@ window + LUT bytes over the decode call's time); the encode throughput and
 its fraction of the bf16 MFMA peak are reported beside it, and again for the
 32-layer bulk prefill encode; the streaming calls (append, flush) and the
 dual-transform calls (factor calibration, smoothed key encode, decode with
-the factors folded into the query) and the K-means fitting of the key
-codebooks on a 65,536-vector sample are timed on the same layer after the
-step.  ``roofline`` is for the kernel that takes the
+the factors folded into the query), the K-means fitting of the key
+codebooks on a 65,536-vector sample and the scalar residual variant (2 bits
+per stage: encode, reconstruction, decode through the product codebook) are
+timed on the same layer after the step; the prefill leg also times the scalar
+encode of its 64 books.  ``roofline`` is for the kernel that takes the
 most time in the step; its HBM ``traffic`` comes from the rocprofv3 counter
 summary committed for that kernel, and is null when the kernel's source has
 changed since those counters were taken.
@@ -257,6 +259,7 @@ def main():
     if not args.step_only:
         res["smooth"] = smooth_calls(torch, kvq, x, cb, q, kc, vc, kw, vw, w, dev, flush)
         res["fit"] = fit_calls(torch, kvq, x, cb, w, dev)
+        res["scalar"] = scalar_calls(torch, kvq, x, q, kw, vw, w, dev, flush)
     del x, recon, flush_buf
     torch.cuda.empty_cache()
     if not args.no_prefill and not args.step_only:
@@ -307,13 +310,97 @@ def prefill_encode(torch, kvq, synth, dev, reps=5):
     n_vec = 2 * L * H * T
     t = float(np.median(ts)) * 1e-3
     flops = 2.0 * D * C * S * n_vec
-    del x, codes, ws
+    del codes, ws
+    # the scalar residual variant on the same 64 books, 2 bits per stage (levels
+    # for the unit-variance source)
+    bits = 2
+    lv = scalar_levels(torch, kvq, [1.0] * (2 * L), bits, dev)
+    sc = torch.empty((2 * L, H, T, 2, D * bits // 8), dtype=torch.uint8, device=dev)
+    kvq.scalar_encode(x, lv, bits, codes=sc)
+    torch.cuda.synchronize()
+    ts2 = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        kvq.scalar_encode(x, lv, bits, codes=sc)
+        e1.record()
+        torch.cuda.synchronize()
+        ts2.append(e0.elapsed_time(e1))
+    t2 = float(np.median(ts2)) * 1e-3
+    sb = n_vec * (2 * D + 2 * D * bits // 8)
+    del x, sc
     torch.cuda.empty_cache()
     return {"workload": f"{w.name}: {L} layers x K|V x Hkv={H} x T={T}, D={D}, "
                         f"G={G}x{D // G} S={S} C={C}",
             "value": round(n_vec / t / 1e6, 2), "unit": "Mvec/s", "ms": round(t * 1e3, 4),
             "vectors": n_vec, "pct_bf16_mfma_peak": round(100 * flops / t / 1e12 / BF16_PEAK_TFLOPS, 3),
-            "reps": reps}
+            "reps": reps,
+            "scalar_2bit": {"ms": round(t2 * 1e3, 4), "bytes": sb,
+                            "gbs": round(sb / t2 / 1e9, 1),
+                            "pct_hbm_peak": round(100 * sb / t2 / 1e9 / HBM_PEAK_GBS, 2),
+                            "note": "kvq_scalar_encode of the same bf16 books, 2 bits per stage: "
+                                    "bf16 in + packed codes out"}}
+
+
+def scalar_levels(torch, kvq, sigmas, bits, dev):
+    """Levels [books][2][2^bits] of the scalar variant: stage 1 = sigma x the
+    unit Gaussian Lloyd-Max levels, stage 2 = sigma x sqrt(stage-1 error) x the
+    unit Laplacian ones (both from the library's kvq_lloyd_max)."""
+    g, dg = kvq.lloyd_max("gaussian", bits)
+    lap, _ = kvq.lloyd_max("laplacian", bits)
+    rows = [[[v * s for v in g], [v * s * float(np.sqrt(dg)) for v in lap]] for s in sigmas]
+    return torch.tensor(rows, dtype=torch.float32, device=dev)
+
+
+def scalar_calls(torch, kvq, x, q, kw, vw, w, dev, flush, bits=2, reps=20):
+    """The scalar residual variant on the same layer (2 bits per stage): encode
+    of K and V, reconstruction (unrotated float32), and decode attention over
+    the packed codes through the product codebook.  Levels from each book's
+    per-element deviation (measured once at set-up)."""
+    B, Hkv, Hq, D, W, Tc = w.batch, w.n_kv_heads, w.n_q_heads, w.head_dim, w.window, w.code_tokens
+    sig = [float(torch.sqrt(torch.mean(x[b, :, :Tc].float() ** 2))) for b in range(2)]
+    lv = scalar_levels(torch, kvq, sig, bits, dev)
+    G = D * bits // 8
+    codes = torch.empty((2, B * Hkv, Tc, 2, G), dtype=torch.uint8, device=dev)
+    recon = torch.empty((2, B * Hkv, Tc, D), dtype=torch.float32, device=dev)
+    kcb = kvq.scalar_product_codebook(lv[0], bits, D)
+    vcb = kvq.scalar_product_codebook(lv[1], bits, D)
+    kc = codes[0].view(B, Hkv, Tc, 2, G)
+    vc = codes[1].view(B, Hkv, Tc, 2, G)
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    att_ws = torch.empty(max(kvq.attend_workspace_size(B, Hq, Hkv, D, Tc, W, 2, G, 256), 16),
+                         dtype=torch.uint8, device=dev)
+    calls = {
+        "encode": lambda: kvq.scalar_encode(x, lv, bits, n_rows=Tc, codes=codes),
+        "reconstruct": lambda: kvq.scalar_decode_reconstruct(codes, lv, bits, unrotate=True,
+                                                            out=recon),
+        "decode": lambda: kvq.attend_decode(q, kc, vc, kcb, vcb, kw, vw, out=out,
+                                            workspace=att_ws),
+    }
+    ms = {k: [] for k in calls}
+    for i in range(reps + 3):
+        for k, f in calls.items():
+            flush(i)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            f()
+            e1.record()
+            torch.cuda.synchronize()
+            if i >= 3:
+                ms[k].append(e0.elapsed_time(e1))
+    med = {k: float(np.median(v)) * 1e-3 for k, v in ms.items()}
+    n_vec = 2 * B * Hkv * Tc
+    sbytes = 2 * D * bits // 8
+    enc_b = n_vec * (2 * D + sbytes)
+    rec_b = n_vec * (sbytes + 4 * D)
+    dec_b = n_vec * sbytes + 2 * B * Hkv * W * D * 2 + B * Hq * 2 * G * 256 * 4
+    res = {"bits": bits, "code_bytes_per_vector": sbytes}
+    for k, b in (("encode", enc_b), ("reconstruct", rec_b), ("decode", dec_b)):
+        res[k] = {"us": round(med[k] * 1e6, 2), "bytes": b, "gbs": round(b / med[k] / 1e9, 1),
+                  "pct_hbm_peak": round(100 * b / med[k] / 1e9 / HBM_PEAK_GBS, 2)}
+    res["note"] = ("decode bytes = packed codes + fp16 window + LUT (2 x G x 256 floats per query "
+                   "head); the product codebook makes the packed bytes ordinary decode codes")
+    return res
 
 
 def smooth_calls(torch, kvq, x, cb, q, kc, vc, kw, vw, w, dev, flush, reps=20):

@@ -119,21 +119,29 @@ __device__ __forceinline__ void stage_levels(const float* __restrict__ levels, i
   __syncthreads();
 }
 
+// Number of thresholds strictly below v: the test v > t is the sign bit of
+// t - v (t - v is +0 when they are equal, so equality counts as "not above",
+// like the strict comparison) -- integer work, no comparison mask.
 template <int B>
-__device__ __forceinline__ int bsum(float v, const float* th) {
-  int z = 0;
+__device__ __forceinline__ uint32_t bsum(float v, const float (&th)[1 << B]) {
+  uint32_t z = 0u;
 #pragma unroll
-  for (int k = 0; k < (1 << B) - 1; ++k) z += v > th[k] ? 1 : 0;
+  for (int k = 0; k < (1 << B) - 1; ++k) z += __float_as_uint(th[k] - v) >> 31;
   return z;
 }
+
+// rows per lane per pass: their loads are all issued before any of them is
+// used, so each wave keeps SC_U loads in flight (a streaming kernel is bound by
+// the bytes in flight, not by its arithmetic)
+constexpr int SC_U = 4;
 
 // grid (row blocks, n_books), 256 threads; grid-stride over the book's rows.
 template <int D, int XT, int B>
 __global__ __launch_bounds__(256) void scalar_encode_kernel(
     const void* __restrict__ x, const float* __restrict__ levels, uint8_t* __restrict__ codes,
-    int64_t n_seq, int64_t seq_stride, int64_t n_rows, int pre_rotated) {
+    int64_t n_seq, int64_t seq_stride, int64_t n_rows, int pre_rotated, uint64_t dm, int dsh) {
   constexpr int L = D / 8;
-  constexpr int RPB = 256 / L;                          // rows per block pass
+  constexpr int RPB = 256 / L;                          // rows per block and unroll step
   constexpr int ESZ = XT == 0 ? 4 : 2;
   constexpr int SB = D * B / 8;                         // bytes per stage
   __shared__ float lv[2][1 << B], th[2][1 << B];
@@ -142,39 +150,73 @@ __global__ __launch_bounds__(256) void scalar_encode_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   const int col = tid % L, rsub = tid / L;
   const int64_t n = n_seq * n_rows;
-  for (int64_t base = (int64_t)blockIdx.x * RPB; base < n; base += (int64_t)gridDim.x * RPB) {
-    const int64_t v = base + rsub;
-    const int64_t vl = v < n ? v : n - 1;               // every lane joins the butterfly
-    const int64_t seq = vl / n_rows, row = vl - seq * n_rows;
-    float y[8];
-    load8<XT>(reinterpret_cast<const char*>(x) +
-                  (((book * n_seq + seq) * seq_stride + row) * D + col * 8) * ESZ,
-              y);
+  float t0[1 << B], t1[1 << B];                         // the thresholds, in registers
+#pragma unroll
+  for (int k = 0; k < (1 << B); ++k) {
+    t0[k] = th[0][k];
+    t1[k] = th[1][k];
+  }
+  for (int64_t base = (int64_t)blockIdx.x * RPB * SC_U; base < n;
+       base += (int64_t)gridDim.x * RPB * SC_U) {
+    float y[SC_U][8];
+#pragma unroll
+    for (int u = 0; u < SC_U; ++u) {
+      const int64_t v = base + u * RPB + rsub;
+      const int64_t vl = v < n ? v : n - 1;             // every lane joins the butterfly
+      // vl / n_rows by multiply and shift when both fit 31 bits (dsh != 0)
+      const int64_t seq = dsh ? (int64_t)(((uint64_t)vl * dm) >> dsh) : vl / n_rows;
+      const int64_t row = vl - seq * n_rows;
+      load8<XT>(reinterpret_cast<const char*>(x) +
+                    (((book * n_seq + seq) * seq_stride + row) * D + col * 8) * ESZ,
+                y[u]);
+    }
+    // phases over all SC_U * 8 elements of the lane, so that independent work
+    // (butterflies, index sums, level reads from LDS) overlaps
     if (!pre_rotated) {
-      hadamard_row<8, L>(y, lane);
-      constexpr float sc = rsqrt_pow2(D);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) y[e] *= sc;
-    }
-    uint32_t p1 = 0u, p2 = 0u;
+      for (int u = 0; u < SC_U; ++u) {
+        hadamard_row<8, L>(y[u], lane);
+        constexpr float sc = rsqrt_pow2(D);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int z1 = bsum<B>(y[e], th[0]);
-      const int z2 = bsum<B>(y[e] - lv[0][z1], th[1]);
-      p1 |= (uint32_t)z1 << (e * B);
-      p2 |= (uint32_t)z2 << (e * B);
+        for (int e = 0; e < 8; ++e) y[u][e] *= sc;
+      }
     }
-    if (v < n) {
-      uint8_t* rowp = codes + (book * n + v) * (2 * SB) + col * B;
-      if constexpr (B == 1) {
-        rowp[0] = (uint8_t)p1;
-        rowp[SB] = (uint8_t)p2;
-      } else if constexpr (B == 2) {
-        *reinterpret_cast<uint16_t*>(rowp) = (uint16_t)p1;
-        *reinterpret_cast<uint16_t*>(rowp + SB) = (uint16_t)p2;
-      } else {
-        *reinterpret_cast<uint32_t*>(rowp) = p1;
-        *reinterpret_cast<uint32_t*>(rowp + SB) = p2;
+    uint32_t z1[SC_U][8];
+#pragma unroll
+    for (int u = 0; u < SC_U; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) z1[u][e] = bsum<B>(y[u][e], t0);
+    float q1[SC_U][8];
+#pragma unroll
+    for (int u = 0; u < SC_U; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) q1[u][e] = lv[0][z1[u][e]];
+    uint32_t p1[SC_U], p2[SC_U];
+#pragma unroll
+    for (int u = 0; u < SC_U; ++u) {
+      p1[u] = 0u;
+      p2[u] = 0u;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        p1[u] |= z1[u][e] << (e * B);
+        p2[u] |= bsum<B>(y[u][e] - q1[u][e], t1) << (e * B);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < SC_U; ++u) {
+      const int64_t v = base + u * RPB + rsub;
+      if (v < n) {
+        uint8_t* rowp = codes + (book * n + v) * (2 * SB) + col * B;
+        if constexpr (B == 1) {
+          rowp[0] = (uint8_t)p1[u];
+          rowp[SB] = (uint8_t)p2[u];
+        } else if constexpr (B == 2) {
+          *reinterpret_cast<uint16_t*>(rowp) = (uint16_t)p1[u];
+          *reinterpret_cast<uint16_t*>(rowp + SB) = (uint16_t)p2[u];
+        } else {
+          *reinterpret_cast<uint32_t*>(rowp) = p1[u];
+          *reinterpret_cast<uint32_t*>(rowp + SB) = p2[u];
+        }
       }
     }
   }
@@ -195,35 +237,43 @@ __global__ __launch_bounds__(256) void scalar_reconstruct_kernel(
   stage_levels<B>(levels, book, lv, th);
   const int tid = threadIdx.x, lane = tid & 63;
   const int col = tid % L, rsub = tid / L;
-  for (int64_t base = (int64_t)blockIdx.x * RPB; base < n; base += (int64_t)gridDim.x * RPB) {
-    const int64_t v = base + rsub;
-    const int64_t vl = v < n ? v : n - 1;
-    const uint8_t* rowp = codes + (book * n + vl) * (2 * SB) + col * B;
-    uint32_t p1, p2;
-    if constexpr (B == 1) {
-      p1 = rowp[0];
-      p2 = rowp[SB];
-    } else if constexpr (B == 2) {
-      p1 = *reinterpret_cast<const uint16_t*>(rowp);
-      p2 = *reinterpret_cast<const uint16_t*>(rowp + SB);
-    } else {
-      p1 = *reinterpret_cast<const uint32_t*>(rowp);
-      p2 = *reinterpret_cast<const uint32_t*>(rowp + SB);
-    }
-    float y[8];
+  for (int64_t base = (int64_t)blockIdx.x * RPB * SC_U; base < n;
+       base += (int64_t)gridDim.x * RPB * SC_U) {
+    uint32_t p1[SC_U], p2[SC_U];
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      y[e] = lv[0][(p1 >> (e * B)) & MASK] + lv[1][(p2 >> (e * B)) & MASK];
-    if (unrotate) {
-      hadamard_row<8, L>(y, lane);
-      constexpr float sc = rsqrt_pow2(D);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) y[e] *= sc;
+    for (int u = 0; u < SC_U; ++u) {
+      const int64_t v = base + u * RPB + rsub;
+      const int64_t vl = v < n ? v : n - 1;
+      const uint8_t* rowp = codes + (book * n + vl) * (2 * SB) + col * B;
+      if constexpr (B == 1) {
+        p1[u] = rowp[0];
+        p2[u] = rowp[SB];
+      } else if constexpr (B == 2) {
+        p1[u] = *reinterpret_cast<const uint16_t*>(rowp);
+        p2[u] = *reinterpret_cast<const uint16_t*>(rowp + SB);
+      } else {
+        p1[u] = *reinterpret_cast<const uint32_t*>(rowp);
+        p2[u] = *reinterpret_cast<const uint32_t*>(rowp + SB);
+      }
     }
-    if (v < n) {
-      float4* o = reinterpret_cast<float4*>(out + (book * n + v) * D + col * 8);
-      o[0] = make_float4(y[0], y[1], y[2], y[3]);
-      o[1] = make_float4(y[4], y[5], y[6], y[7]);
+#pragma unroll
+    for (int u = 0; u < SC_U; ++u) {
+      const int64_t v = base + u * RPB + rsub;
+      float y[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        y[e] = lv[0][(p1[u] >> (e * B)) & MASK] + lv[1][(p2[u] >> (e * B)) & MASK];
+      if (unrotate) {
+        hadamard_row<8, L>(y, lane);
+        constexpr float sc = rsqrt_pow2(D);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] *= sc;
+      }
+      if (v < n) {
+        float4* o = reinterpret_cast<float4*>(out + (book * n + v) * D + col * 8);
+        o[0] = make_float4(y[0], y[1], y[2], y[3]);
+        o[1] = make_float4(y[4], y[5], y[6], y[7]);
+      }
     }
   }
 }
@@ -245,7 +295,7 @@ __global__ __launch_bounds__(256) void scalar_product_cb_kernel(const float* __r
 
 // ---------------------------------------------------------------- launchers
 static unsigned row_grid(int64_t n, int D) {
-  const int64_t rpb = 256 / (D / 8);
+  const int64_t rpb = 256 / (D / 8) * SC_U;
   int64_t b = (n + rpb - 1) / rpb;
   if (b > 4096) b = 4096;
   return (unsigned)(b > 0 ? b : 1);
@@ -258,11 +308,22 @@ hipError_t launch_scalar_encode(const void* x, int xt, int D, int bits, int64_t 
   const int64_t n = n_seq * n_rows;
   if (n == 0 || n_books == 0) return hipSuccess;
   const dim3 grid(row_grid(n, D), (unsigned)n_books);
+  // q = floor(v / n_rows) = (v * m) >> (31 + l) for every v < 2^31, with
+  // l = ceil(log2 n_rows) and m = ceil(2^(31+l) / n_rows) (Granlund and
+  // Montgomery, "Division by invariant integers using multiplication", 1994)
+  uint64_t dm = 0;
+  int dsh = 0;
+  if (n < ((int64_t)1 << 31)) {
+    int l = 0;
+    while (((int64_t)1 << l) < n_rows) ++l;
+    dm = (((uint64_t)1 << (31 + l)) + (uint64_t)n_rows - 1) / (uint64_t)n_rows;
+    dsh = 31 + l;
+  }
 #define KVQ_SE(DD, XX, BB)                                                                 \
   if (D == DD && xt == XX && bits == BB) {                                                \
     scalar_encode_kernel<DD, XX, BB><<<grid, dim3(256), 0, st>>>(x, levels, codes, n_seq,  \
                                                                  seq_stride, n_rows,       \
-                                                                 pre_rotated);             \
+                                                                 pre_rotated, dm, dsh);    \
     return hipGetLastError();                                                              \
   }
 #define KVQ_SE_D(DD)                                                                      \
