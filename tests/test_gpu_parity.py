@@ -419,3 +419,22 @@ def test_full_size_prefill_layers_sampled():
         idx = np.arange(0, flat.shape[0], 131)
         res = oracle.check_codes(xs[idx].astype(np.float64), inp["cb"][b], flat[idx])
         assert res["hard"] == 0, res
+
+
+@pytest.mark.parametrize("first", [0, 8, 16, 24])
+def test_prefill_every_layer_sampled(first):
+    """The prefill workload's sample check: for every one of its 32 layers
+    (8 per test), K and V of all 8 KV heads, every 64th token, coded at full
+    per-layer size on the GPU and checked against the oracle."""
+    w = synth.workload(5)
+    for layer in range(first, first + 8):
+        say(f"prefill layer {layer}: encode K and V (8 heads x 32768 tokens), check every 64th token")
+        inp = synth.make_inputs(w, layers=[layer])
+        x = to_dev(inp["x"], w)
+        codes = kvq.encode(x, cuda(inp["cb"]))[:, :, ::64].cpu().numpy()
+        del x
+        for b in range(2):
+            xs = inp["x_f32"][b][:, ::64].reshape(-1, 128).astype(np.float64)
+            res = oracle.check_codes(xs, inp["cb"][b], codes[b].reshape(-1, 2, 16))
+            assert res["hard"] == 0, (layer, b, res)
+            assert res["exact"] >= 0.999 * res["total"], (layer, b, res)
