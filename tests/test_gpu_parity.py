@@ -438,3 +438,30 @@ def test_prefill_every_layer_sampled(first):
             res = oracle.check_codes(xs, inp["cb"][b], codes[b].reshape(-1, 2, 16))
             assert res["hard"] == 0, (layer, b, res)
             assert res["exact"] >= 0.999 * res["total"], (layer, b, res)
+
+
+def test_decode_independent_of_chunk_count():
+    """Split-K invariance on the GPU: one sequence decoded alone (20 chunks of
+    1000 tokens) and inside a batch of four copies (8 chunks of 2500 tokens, a
+    different fixed-point scale and merge) agree to the fixed-point rounding;
+    the batch rows, which share a plan, agree bit for bit."""
+    say("decode: chunk-count invariance")
+    w = synth.workload(2, tokens=20128, window=128)
+    inp = synth.make_inputs(w)
+    Tc = w.code_tokens
+    rng = np.random.default_rng(8)
+    ck = rng.integers(0, 256, size=(1, 8, Tc, 1, 16), dtype=np.uint8)
+    cv = rng.integers(0, 256, size=(1, 8, Tc, 1, 16), dtype=np.uint8)
+    args = (cuda(inp["cb"][0]), cuda(inp["cb"][1]))
+    one = kvq.attend_decode(cuda(inp["q"]), cuda(ck), cuda(cv), *args, cuda(inp["k_win"]),
+                            cuda(inp["v_win"])).cpu().numpy()
+    rep = lambda a: np.ascontiguousarray(np.repeat(a, 4, axis=0))
+    four = kvq.attend_decode(cuda(rep(inp["q"])), cuda(rep(ck)), cuda(rep(cv)), *args,
+                             cuda(rep(inp["k_win"])), cuda(rep(inp["v_win"]))).cpu().numpy()
+    # plans differ: chunk length 1000 vs 2500 (8 vs 32 units over 256 blocks)
+    for b in range(1, 4):
+        assert np.array_equal(four[b], four[0])
+    scale = np.abs(one).max()
+    assert np.max(np.abs(four[0] - one[0])) <= 2e-5 * scale, np.max(np.abs(four[0] - one[0]))
+    ref = oracle.attend(inp["q"], ck, cv, inp["cb"][0], inp["cb"][1], inp["k_win"], inp["v_win"])
+    assert oracle.check_attn(one, ref)["ok"] and oracle.check_attn(four[:1], ref)["ok"]
