@@ -10,27 +10,35 @@
 // next stage's residuals.
 //
 // Kernels, all on the caller's stream:
-//   fit_prep_kernel      r = H_D (x / lambda) as float32 (the residual before
-//                        stage 0), and per group the largest |r| (bit pattern,
+//   fit_prep_kernel      y = H_D (x / lambda) as float32 (kept for the whole
+//                        call) and per group the largest |y| (bit pattern,
 //                        atomic max);
 //   assignment           the encode kernels themselves, run with the first
-//                        s + 1 stages (their greedy chain reproduces the
-//                        earlier stages' assignments and picks stage s's);
-//   fit_accum_kernel     per (group, 32-dim slice, chunk of vectors): sums of
-//                        the assigned residuals in LDS as 64-bit fixed point
-//                        (ds_add_u64: integer adds, so the sums are exact and
-//                        independent of the order), stored as the chunk's
-//                        partial sums (plain stores, no global atomics);
+//                        s + 1 stages (their greedy chain runs the earlier,
+//                        fitted stages and picks stage s's entry);
+//   fit_accum_kernel     per (group, 32-dim slice, chunk of vectors): the
+//                        stage-s residual y - sum_{t<s} C_t[z_t] rebuilt from
+//                        the codes of that same assignment call (so the sums
+//                        follow exactly the chain that chose z_s), summed per
+//                        entry in LDS as 64-bit fixed point (ds_add_u64:
+//                        integer adds, exact and independent of the order),
+//                        stored as the chunk's partial sums;
 //   fit_update_kernel    entry = (sum over chunks) * 2^-F / count in float64,
 //                        rounded once to float32 (entries with no vector keep
 //                        theirs);
-//   fit_residual_kernel  r -= C_s[z_s] with the final assignment, and the new
-//                        per-group bound for the next stage.
+//   fit_bound_kernel     after a stage's last assignment: per group the
+//                        largest residual component, the next stage's bound.
 // The kernels reading a stage's bound take the max over FIT_BCOPIES copies.
-// Fixed point: F = 62 - ceil(log2 N) - e with max |r| < 2^e, so every term is
-// below 2^(62 - ceil(log2 N)) and any sum of N of them below 2^62; a residual
-// becomes a multiple of 2^-F exactly when |r| >= 2^(23-F), and is truncated
-// toward zero (an error below 2^-F) otherwise.
+// Fixed point: F = 62 - ceil(log2 N) - e - m with the measured bound below 2^e
+// and a margin m = 1 + ceil(log2 sqrt(dsub)).  The bound is measured on the
+// chain of the stage's previous assignment call; a later call's chain can
+// differ at a near tie (the assignment changes kernels between 4 and 5
+// stages), and the margin covers any residual whose group norm stays within
+// twice sqrt(dsub) times the bound, which such a chain gives.  Every term is
+// below 2^(62 - ceil(log2 N)) (conversion clamps the shift there, so even a
+// residual past the margin cannot overflow) and any sum of N of them below
+// 2^62; a residual becomes a multiple of 2^-F exactly when |r| >= 2^(23-F),
+// and is truncated toward zero (an error below 2^-F) otherwise.
 #include "kvq_internal.h"
 
 namespace kvq {
@@ -62,7 +70,9 @@ FitLayout fit_layout(int D, int G, int S, int C, int64_t n) {
   size_t off = 0;
   l.resid = off;  off += al256((size_t)n * D * 4);
   l.codes = off;  off += al256((size_t)n * S * G);
-  l.pack = off;   off += al256(encode_workspace_bytes(D, G, S, C, 1));
+  // the assignment of stage s runs the encode with s + 1 stages, on the MFMA
+  // path (packed codebooks) whenever s + 1 <= 4: room for the longest such prefix
+  l.pack = off;   off += al256(encode_workspace_bytes(D, G, S < 4 ? S : 4, C, 1));
   const int64_t nch = fit_chunks(n);
   l.acc = off;    off += al256((size_t)nch * G * C * dsub * 8);
   l.cnt = off;    off += al256((size_t)nch * G * C * 4);
@@ -71,25 +81,26 @@ FitLayout fit_layout(int D, int G, int S, int C, int64_t n) {
   return l;
 }
 
-// bound: the stage's [FIT_BCOPIES][G] copies
+// bound: the stage's [FIT_BCOPIES][G] copies; margin: see the header
 __device__ __forceinline__ int fit_fbits(const uint32_t* __restrict__ bound, int g, int G,
-                                         int log2n) {
+                                         int log2n, int margin) {
   uint32_t b = 0u;
   for (int i = 0; i < FIT_BCOPIES; ++i) b = bound[i * G + g] > b ? bound[i * G + g] : b;
   int e = 0;
   frexpf(__uint_as_float(b), &e);               // bound < 2^e (0 -> e = 0)
-  return 62 - log2n - e;
+  return 62 - log2n - e - margin;
 }
 
 // x * 2^F as a 64-bit integer from the float's bits (integer ALU only): the
 // mantissa shifted by exponent + F; exact when the result is a whole number
-// (|x| >= 2^(23-F)), truncated toward zero below that.  F keeps every value
-// of the stage below 2^62, so the left shift never overflows.
-__device__ __forceinline__ long long fit_fixed(float x, int F) {
+// (|x| >= 2^(23-F)), truncated toward zero below that.  The shift is clamped
+// to shmax = 38 - ceil(log2 N), so every term is below 2^(62 - ceil(log2 N)).
+__device__ __forceinline__ long long fit_fixed(float x, int F, int shmax) {
   const uint32_t u = __float_as_uint(x);
   const int ex = (int)((u >> 23) & 0xffu);
   const uint32_t man = (u & 0x7fffffu) | (ex ? 0x800000u : 0u);
-  const int sh = (ex ? ex : 1) - 150 + F;               // x = man * 2^(ex - 150)
+  int sh = (ex ? ex : 1) - 150 + F;                     // x = man * 2^(ex - 150)
+  sh = sh < shmax ? sh : shmax;
   long long t = sh >= 0 ? (long long)((unsigned long long)man << sh)
                         : (sh > -32 ? (long long)(man >> -sh) : 0ll);
   return (u >> 31) ? -t : t;
@@ -156,14 +167,16 @@ __global__ __launch_bounds__(256) void fit_prep_kernel(const void* __restrict__ 
 }
 
 // grid (G * nslice, chunks).  Block: group g, dims [slice*DS, slice*DS + DS)
-// of the group, vectors [chunk*len, (chunk+1)*len); each vector's DS values go
-// to LDS sums[j][z] as fixed point, then the block stores its partial sums to
+// of the group, vectors [chunk*len, (chunk+1)*len); each vector's stage-s
+// residual over those dims (y minus the entries its earlier-stage codes
+// chose, subtracted stage by stage in float32 as the encode does) goes to
+// LDS sums[j][z] as fixed point, then the block stores its partial sums to
 // part[chunk][g][j][c] (and counts to pcnt[chunk][g][c]).
 template <int DS>
 __global__ __launch_bounds__(256) void fit_accum_kernel(
-    const float* __restrict__ r, const uint8_t* __restrict__ codes, int row_bytes, int s, int G,
-    int C, int D, int dsub, int64_t n, int64_t len, int log2n,
-    const uint32_t* __restrict__ bound, unsigned long long* __restrict__ part,
+    const float* __restrict__ y, const uint8_t* __restrict__ codes, int row_bytes, int s, int G,
+    int C, int D, int dsub, const float* __restrict__ cb, int64_t n, int64_t len, int log2n,
+    int margin, const uint32_t* __restrict__ bound, unsigned long long* __restrict__ part,
     uint32_t* __restrict__ pcnt) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   // [DS][C]: the lanes of one atomic instruction (same j, random entries z)
@@ -176,7 +189,7 @@ __global__ __launch_bounds__(256) void fit_accum_kernel(
   for (int i = tid; i < C * DS; i += 256) sums[i] = 0ull;
   for (int i = tid; i < C; i += 256) counts[i] = 0u;
   __syncthreads();
-  const int F = fit_fbits(bound, g, G, log2n);
+  const int F = fit_fbits(bound, g, G, log2n, margin);
   const int64_t n0 = (int64_t)blockIdx.y * len;
   const int64_t n1 = (n0 + len) < n ? (n0 + len) : n;
   const int d0 = g * dsub + slice * DS;
@@ -184,15 +197,30 @@ __global__ __launch_bounds__(256) void fit_accum_kernel(
   // (indices past the end repeat the last vector; their atomics are skipped)
   constexpr int VB = DS == 32 ? 2 : 4;
   for (int64_t b = n0 + tid; b < n1; b += VB * 256) {
+    int64_t vv[VB];
     int zz[VB];
     float4 a[VB][DS / 4];
 #pragma unroll
     for (int k = 0; k < VB; ++k) {
-      const int64_t v = b + 256 * k < n1 ? b + 256 * k : n1 - 1;
-      zz[k] = codes[v * row_bytes + s * G + g];
-      const float4* rp = reinterpret_cast<const float4*>(r + v * D + d0);
+      vv[k] = b + 256 * k < n1 ? b + 256 * k : n1 - 1;
+      zz[k] = codes[vv[k] * row_bytes + s * G + g];
+      const float4* rp = reinterpret_cast<const float4*>(y + vv[k] * D + d0);
 #pragma unroll
       for (int q = 0; q < DS / 4; ++q) a[k][q] = rp[q];
+    }
+    for (int t = 0; t < s; ++t) {                       // the earlier stages' entries
+      const float* cbt = cb + ((int64_t)t * G + g) * C * dsub + slice * DS;
+#pragma unroll
+      for (int k = 0; k < VB; ++k) {
+        int zt = codes[vv[k] * row_bytes + t * G + g];
+        zt = zt < C ? zt : C - 1;
+        const float4* cp = reinterpret_cast<const float4*>(cbt + (int64_t)zt * dsub);
+#pragma unroll
+        for (int q = 0; q < DS / 4; ++q) {
+          const float4 c4 = cp[q];
+          a[k][q].x -= c4.x; a[k][q].y -= c4.y; a[k][q].z -= c4.z; a[k][q].w -= c4.w;
+        }
+      }
     }
 #pragma unroll
     for (int k = 0; k < VB; ++k) {
@@ -203,7 +231,7 @@ __global__ __launch_bounds__(256) void fit_accum_kernel(
         const float e4[4] = {a[k][q].x, a[k][q].y, a[k][q].z, a[k][q].w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const long long t = fit_fixed(e4[j], F);
+          const long long t = fit_fixed(e4[j], F, 38 - log2n);
           atomicAdd(&sums[(q * 4 + j) * C + z], (unsigned long long)t);
         }
       }
@@ -222,12 +250,12 @@ __global__ __launch_bounds__(256) void fit_accum_kernel(
 // grid (G, dsub), one entry c per thread (C <= 256): the chunks' partial sums
 // and counts added in chunk order (integers: exact).
 __global__ __launch_bounds__(256) void fit_update_kernel(
-    float* __restrict__ cb_s, int G, int C, int dsub, int log2n, int64_t nch,
+    float* __restrict__ cb_s, int G, int C, int dsub, int log2n, int margin, int64_t nch,
     const uint32_t* __restrict__ bound, const unsigned long long* __restrict__ part,
     const uint32_t* __restrict__ pcnt) {
   const int g = blockIdx.x, j = blockIdx.y, c = threadIdx.x;
   if (c >= C) return;
-  const int F = fit_fbits(bound, g, G, log2n);
+  const int F = fit_fbits(bound, g, G, log2n, margin);
   unsigned long long sum = 0ull;
   uint32_t k = 0u;
   for (int64_t h = 0; h < nch; ++h) {
@@ -238,11 +266,13 @@ __global__ __launch_bounds__(256) void fit_update_kernel(
     cb_s[((int64_t)g * C + c) * dsub + j] = (float)(ldexp((double)(long long)sum, -F) / (double)k);
 }
 
-// r -= C_s[z_s] for every (vector, group); per-group bound of the new residual.
+// Per group, the largest component of y - sum_{t<=s} C_t[z_t] over the
+// vectors (the residual stage s + 1 starts from), from the codes of stage s's
+// last assignment (stages 0..s in each row).
 template <int D>
-__global__ __launch_bounds__(256) void fit_residual_kernel(
-    float* __restrict__ r, const uint8_t* __restrict__ codes, int row_bytes, int s, int G, int C,
-    int dsub, const float* __restrict__ cb_s, int64_t n, uint32_t* __restrict__ bound_next) {
+__global__ __launch_bounds__(256) void fit_bound_kernel(
+    const float* __restrict__ y, const uint8_t* __restrict__ codes, int row_bytes, int s, int G,
+    int C, int dsub, const float* __restrict__ cb, int64_t n, uint32_t* __restrict__ bound_next) {
   constexpr int L = D / 8;
   constexpr int RPP = 256 / L;
   __shared__ uint32_t colmax[L];
@@ -255,16 +285,17 @@ __global__ __launch_bounds__(256) void fit_residual_kernel(
   for (int64_t base = (int64_t)blockIdx.x * RPP; base < n; base += (int64_t)gridDim.x * RPP) {
     const int64_t v = base + rsub;
     if (v >= n) continue;
-    int z = codes[v * row_bytes + s * G + g];
-    z = z < C ? z : C - 1;
-    const float4* cp = reinterpret_cast<const float4*>(cb_s + ((int64_t)g * C + z) * dsub + j0);
-    float4* rp = reinterpret_cast<float4*>(r + v * D + col * 8);
+    const float4* rp = reinterpret_cast<const float4*>(y + v * D + col * 8);
     float4 a = rp[0], b = rp[1];
-    const float4 c0 = cp[0], c1 = cp[1];
-    a.x -= c0.x; a.y -= c0.y; a.z -= c0.z; a.w -= c0.w;
-    b.x -= c1.x; b.y -= c1.y; b.z -= c1.z; b.w -= c1.w;
-    rp[0] = a;
-    rp[1] = b;
+    for (int t = 0; t <= s; ++t) {
+      int z = codes[v * row_bytes + t * G + g];
+      z = z < C ? z : C - 1;
+      const float4* cp =
+          reinterpret_cast<const float4*>(cb + (((int64_t)t * G + g) * C + z) * dsub + j0);
+      const float4 c0 = cp[0], c1 = cp[1];
+      a.x -= c0.x; a.y -= c0.y; a.z -= c0.z; a.w -= c0.w;
+      b.x -= c1.x; b.y -= c1.y; b.z -= c1.z; b.w -= c1.w;
+    }
     const float e8[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -330,6 +361,7 @@ hipError_t launch_codebook_fit(const void* x, int xt, int D, int G, int S, int C
   if (e != hipSuccess) return e;
 
   const int ds = dsub < FIT_DS ? dsub : FIT_DS;
+  const int margin = 1 + (ceil_log2_i64(dsub) + 1) / 2;  // 1 + ceil(log2 sqrt(dsub))
   const int nslice = dsub / ds;
   const int64_t clen = fit_chunk_len(n);
   const int64_t chunks = fit_chunks(n);
@@ -351,22 +383,22 @@ hipError_t launch_codebook_fit(const void* x, int xt, int D, int G, int S, int C
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)alds);         \
     if (e != hipSuccess) return e;                                                          \
     fit_accum_kernel<DSV><<<dim3((unsigned)(G * nslice), (unsigned)chunks), dim3(256), alds, \
-                            st>>>(r, codes, row_bytes, s, G, C, D, dsub, n, clen, log2n, bs, \
-                                  acc, cnt);                                                \
+                            st>>>(r, codes, row_bytes, s, G, C, D, dsub, cb, n, clen, log2n, \
+                                  margin, bs, acc, cnt);                                    \
   }
       KVQ_ACC(8) KVQ_ACC(16) KVQ_ACC(32)
 #undef KVQ_ACC
       e = hipGetLastError();
       if (e != hipSuccess) return e;
-      fit_update_kernel<<<dim3(G, dsub), dim3(256), 0, st>>>(cb_s, G, C, dsub, log2n, chunks, bs,
-                                                             acc, cnt);
+      fit_update_kernel<<<dim3(G, dsub), dim3(256), 0, st>>>(cb_s, G, C, dsub, log2n, margin,
+                                                             chunks, bs, acc, cnt);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
     if (!last) {
-      auto kern = D == 64 ? fit_residual_kernel<64>
-                          : D == 128 ? fit_residual_kernel<128> : fit_residual_kernel<256>;
-      kern<<<dim3((unsigned)rb), dim3(256), 0, st>>>(r, codes, row_bytes, s, G, C, dsub, cb_s, n,
+      auto kern = D == 64 ? fit_bound_kernel<64>
+                          : D == 128 ? fit_bound_kernel<128> : fit_bound_kernel<256>;
+      kern<<<dim3((unsigned)rb), dim3(256), 0, st>>>(r, codes, row_bytes, s, G, C, dsub, cb, n,
                                                       bound + (size_t)(s + 1) * FIT_BCOPIES * G);
       e = hipGetLastError();
       if (e != hipSuccess) return e;

@@ -2,11 +2,12 @@
 codebooks on a sample) with the float64 oracle, through the C ABI.
 
 K-means is iterative, so the element-wise check is one iteration at a time:
-the GPU's assignment (the encode kernels, run with the same entries) follows
-the code rule against the oracle's distances, and every fitted entry equals
-the oracle's mean of the residuals the GPU assigned to it within 1e-6 * the
-largest residual component of its group (float32 residuals against float64;
-the fixed-point sums themselves are exact to 2^-40 of that bound).  Entries
+the GPU's assignment (the encode kernels, run with the same entries and the
+earlier stages' fitted ones) follows the code rule against the oracle's
+distances, and every fitted entry equals the oracle's mean of the residuals
+(y minus the earlier-stage entries that same assignment chose) the GPU
+assigned to it within 1e-6 * the largest residual component of its group
+(the fixed-point sums themselves are exact to 2^-30 of that bound).  Entries
 no vector chose must come back bit-identical.  Over several iterations the
 checks are Lloyd's properties: the distortion of the fitted codebooks never
 increases, and ends within 1 % of the oracle's own fit from the same start.
@@ -54,6 +55,16 @@ def sample(key, n_rows, **over):
     return w, x, xf, inp["cb"][0]
 
 
+def residual(y, cb, codes, s):
+    """y minus the entries of stages 0..s-1 that codes [n][>=s][G] chose,
+    subtracted stage by stage in float32 (as the assignment's chain does)."""
+    G = cb.shape[1]
+    r = y.astype(np.float32)
+    for t in range(s):
+        r = r - np.concatenate([cb[t, g][codes[:, t, g]] for g in range(G)], axis=1)
+    return r.astype(np.float64)
+
+
 def check_step(r, z, init, fitted, dsub):
     """One Lloyd update per group: the fitted entries against the oracle's
     means of r over the GPU's assignment z; unchosen entries unchanged."""
@@ -86,13 +97,12 @@ def test_fit_one_iteration_parity(key, over, n_rows):
     assert res["hard"] == 0
     check_step(y, z0[:, 0], init[0], fitted[0], dsub)
     if S > 1:
-        # stage 1 starts from the residuals of the fitted stage 0 (final assignment)
-        zf = kvq.encode(x[None], cuda(fitted[None, :1]), n_rows=n_rows).cpu().numpy()
-        zf = zf.reshape(-1, G)
-        r1 = y - np.concatenate([fitted[0, g][zf[:, g]] for g in range(G)], axis=1)
+        # stage 1's assignment runs the fitted stage 0 and then stage 1; its
+        # residuals are y minus the stage-0 entries that same call chose
         both = np.concatenate([fitted[:1], init[1:2]])
-        z1 = kvq.encode(x[None], cuda(both[None]), n_rows=n_rows).cpu().numpy()
-        z1 = z1.reshape(-1, 2, G)[:, 1]
+        zz = kvq.encode(x[None], cuda(both[None]), n_rows=n_rows).cpu().numpy().reshape(-1, 2, G)
+        r1 = residual(y, fitted, zz, 1)
+        z1 = zz[:, 1]
         res = oracle.check_codes(r1, init[1:2], z1[:, None, :], rotate=False)
         say("   stage 1 assignment", {k: res[k] for k in ("total", "exact", "near_tie", "hard")})
         assert res["hard"] == 0
@@ -108,10 +118,10 @@ def test_fit_one_iteration_two_stages_mfma():
     y = oracle.fwht(xf.reshape(-1, 128))
     z0 = kvq.encode(x[None], cuda(init[None, :1])).cpu().numpy().reshape(-1, G)
     check_step(y, z0, init[0], fitted[0], dsub)
-    zf = kvq.encode(x[None], cuda(fitted[None, :1])).cpu().numpy().reshape(-1, G)
-    r1 = y - np.concatenate([fitted[0, g][zf[:, g]] for g in range(G)], axis=1)
     both = np.concatenate([fitted[:1], init[1:2]])
-    z1 = kvq.encode(x[None], cuda(both[None])).cpu().numpy().reshape(-1, 2, G)[:, 1]
+    zz = kvq.encode(x[None], cuda(both[None])).cpu().numpy().reshape(-1, 2, G)
+    r1 = residual(y, fitted, zz, 1)
+    z1 = zz[:, 1]
     res = oracle.check_codes(r1, init[1:2], z1[:, None, :], rotate=False)
     assert res["hard"] == 0
     check_step(r1, z1, init[1], fitted[1], dsub)
@@ -175,3 +185,30 @@ def test_fit_distortion_never_increases_and_matches_oracle_fit():
     ref = distortion(oracle.fit_codebooks(xf.reshape(-1, 128), init, 8))
     say("   oracle fit", f"{ref:.6g}")
     assert abs(ds[-1] - ref) <= 0.01 * ref
+
+
+def test_fit_five_stages_mfma_then_generic():
+    """Five stages: the assignments of stages 0-3 run on the MFMA path (packed
+    codebooks in the workspace), stage 4's on the generic kernel.  Stage 0 and
+    stage 4 each follow one Lloyd update of the GPU's own assignment."""
+    say("codebook fit, five stages")
+    w, x, xf, init3 = sample(3, 1200, batch=1, tokens=1200, window=0)
+    rng = np.random.default_rng(51)
+    G, C, dsub = 16, 256, 8
+    init = (rng.standard_normal((5, G, C, dsub)) / np.sqrt(8)
+            * (0.5 ** np.arange(5))[:, None, None, None]).astype(np.float32)
+    fitted = kvq.codebook_fit(x, cuda(init), 1).cpu().numpy()
+    assert np.all(np.isfinite(fitted))
+    y = oracle.fwht(xf.reshape(-1, 128))
+    z0 = kvq.encode(x[None], cuda(init[None, :1])).cpu().numpy().reshape(-1, G)
+    check_step(y, z0, init[0], fitted[0], dsub)
+    # stage 4's assignment (generic kernel) runs the four fitted stages itself;
+    # its residuals follow that call's own stage 0-3 codes
+    both = np.concatenate([fitted[:4], init[4:5]])
+    zz = kvq.encode(x[None], cuda(both[None])).cpu().numpy().reshape(-1, 5, G)
+    r4 = residual(y, fitted, zz, 4)
+    z4 = zz[:, 4]
+    res = oracle.check_codes(r4, init[4:5], z4[:, None, :], rotate=False)
+    assert res["hard"] == 0
+    check_step(r4, z4, init[4], fitted[4], dsub)
+    assert torch.equal(kvq.codebook_fit(x, cuda(init), 1), cuda(fitted))
