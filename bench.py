@@ -476,12 +476,15 @@ def smooth_calls(torch, kvq, x, cb, q, kc, vc, kw, vw, w, dev, flush, reps=20):
             "note": f"keys of the layer ({B * Hkv * Tc} vectors), factors one row per KV head"}
 
 
-def fit_calls(torch, kvq, x, cb, w, dev, rows=8192, n_iter=10, reps=5):
-    """K-means fitting of the layer's key codebooks on a sample: the first
-    ``rows`` coded tokens of every KV head (65,536 vectors), ``n_iter``
-    Lloyd iterations from the layer's codebooks."""
-    H, D, S, G, C = w.n_kv_heads, w.head_dim, w.n_stages, w.n_groups, w.n_codewords
-    xk = x[0]                                           # [Hkv][T][D] keys, rows [0, rows) used
+def fit_calls(torch, kvq, x, cb, w, dev, sample=65536, n_iter=10, reps=5):
+    """K-means fitting of the layer's key codebooks on a sample of ``sample``
+    vectors: the first sample / (sequences x KV heads) tokens of every
+    (sequence, KV head) (8,192 of each of the 8 KV heads for the Llama-shaped
+    layer), ``n_iter`` Lloyd iterations from the layer's codebooks."""
+    D, S, G, C = w.head_dim, w.n_stages, w.n_groups, w.n_codewords
+    xk = x[0]                                           # [B*Hkv][T][D] keys, rows [0, rows) used
+    H = xk.shape[0]
+    rows = min(sample // H, xk.shape[1])
     ws = torch.empty(kvq.codebook_fit_workspace_size(D, G, S, C, H * rows), dtype=torch.uint8,
                      device=dev)
     cb0 = cb[0].clone()

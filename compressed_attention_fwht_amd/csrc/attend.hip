@@ -43,6 +43,10 @@ static int ceil_log2(int64_t v) {
 }
 
 // ----------------------------------------------------------- workspace plan
+// V histogram: per sg a block of C * RP 32-bit words plus a 4-word pad
+constexpr int HIST_PAD = 4;
+__host__ __device__ constexpr int hist_stride(int C, int RP) { return C * RP + HIST_PAD; }
+
 AttnPlan attn_plan(int B, int Hq, int Hkv, int D, int S, int G, int C, int Tc, int W) {
   AttnPlan p{};
   const int SG = S * G;
@@ -56,7 +60,7 @@ AttnPlan attn_plan(int B, int Hq, int Hkv, int D, int S, int G, int C, int Tc, i
   p.rp = 0;
   for (int rp = 4; rp >= 1 && !p.rp; rp >>= 1) {
     if (rp > R && rp > 1) continue;
-    const size_t tab = (size_t)SG * C * rp * 4;
+    const size_t tab = (size_t)SG * hist_stride(C, rp) * 4;
     for (int P = P0; P >= 1; P >>= 1) {
       if (tab + (size_t)S * P * rp * D * 4 <= ATTN_LDS_TABLES) { p.rp = rp; p.cparts = P; break; }
     }
@@ -86,7 +90,7 @@ AttnPlan attn_plan(int B, int Hq, int Hkv, int D, int S, int G, int C, int Tc, i
     const int per = p.n_chunks > 0 ? (W + p.n_chunks - 1) / p.n_chunks : 0;
     const int sp = S * p.cparts > 8 ? S * p.cparts : 8;
     if (p.n_chunks > 0 && per <= 4096 / D &&
-        (size_t)SG * C * p.rp * 4 + (size_t)sp * p.rp * D * 4 <= ATTN_LDS_TABLES)
+        (size_t)SG * hist_stride(C, p.rp) * 4 + (size_t)sp * p.rp * D * 4 <= ATTN_LDS_TABLES)
       p.wslice = per;
     else
       p.n_wblocks = (W + ATTN_WIN_BLOCK - 1) / ATTN_WIN_BLOCK;
@@ -193,16 +197,34 @@ __global__ __launch_bounds__(256) void attn_lut_kernel(const float* __restrict__
 constexpr int CH_THREADS = 512;
 constexpr int CH_TPT = ATTN_MAX_CHUNK / CH_THREADS;
 
+// Histogram layout: per sg a block of HIST_PAD + C * RP 32-bit words holding
+// [RP/2][C] 64-bit bins (the two 32-bit weights of a head pair in one bin),
+// or [C] 32-bit ones for RP = 1.  Pair-major keeps the bins of one atomic
+// instruction (same sg and pair, random z) 8 bytes apart, so they spread over
+// twice the LDS banks a [C][RP] layout reaches; the 4-word pad per block
+// puts the blocks of different sg on different banks, which the contraction
+// (lanes of one wave on different groups, same codeword) reads together.
+
 template <int RP>
-__device__ __forceinline__ void hist_add(uint32_t* tab, int e, const uint32_t (&pw)[RP]) {
+__device__ __forceinline__ void hist_add(uint32_t* tab, int sg, int z, int C,
+                                         const uint32_t (&pw)[RP]) {
+  uint32_t* blk = tab + sg * hist_stride(C, RP);
   if constexpr (RP == 1) {
-    atomicAdd(tab + e, pw[0]);
+    atomicAdd(blk + z, pw[0]);
   } else {
-    unsigned long long* t64 = reinterpret_cast<unsigned long long*>(tab + e);
+    unsigned long long* t64 = reinterpret_cast<unsigned long long*>(blk);
 #pragma unroll
     for (int r = 0; r < RP; r += 2)
-      atomicAdd(t64 + r / 2, (unsigned long long)pw[r] | ((unsigned long long)pw[r + 1] << 32));
+      atomicAdd(t64 + (r / 2) * C + z,
+                (unsigned long long)pw[r] | ((unsigned long long)pw[r + 1] << 32));
   }
+}
+
+// bin of head r, codeword c inside one sg's block
+template <int RP>
+__device__ __forceinline__ int hist_bin(int c, int r, int C) {
+  if constexpr (RP == 1) return c;
+  else return ((r >> 1) * C + c) * 2 + (r & 1);
 }
 
 template <int RP>
@@ -414,25 +436,34 @@ __device__ __forceinline__ void window_partial(const float* __restrict__ q,
 // the chunk's barriers, and is folded into the chunk's record at the end; a
 // common fixed-point scale would round every chunk token against a window
 // maximum that may dwarf it.  Returns whether this row holds a token.
+// The loads are issued whatever the slice holds (rows past it read the last
+// window row, or, with no window at all, the first bytes of q) so the number
+// of loads in flight is fixed and later waits count exactly; rows without a
+// token come back as zeros.
 template <int RP, int D>
 __device__ __forceinline__ bool win_slice_load(uint4& kraw, uint4& vraw, float (&qv)[RP][8],
                                                const float* __restrict__ q,
                                                const uint16_t* __restrict__ kw,
-                                               const uint16_t* __restrict__ vw, int b, int kv,
-                                               int h0, int nh, int Hq, int Hkv, int wstride,
-                                               int wa, int wb, int tid) {
+                                               const uint16_t* __restrict__ vw, bool have,
+                                               int b, int kv, int h0, int nh, int Hq, int Hkv,
+                                               int wstride, int wa, int wb, int tid) {
   constexpr int L = D / 8;
   const int row = tid / L, col = tid % L;
   const int t = wa + row;
-  const bool act = t < wb;
-  const int tl = act ? t : (wb > 0 ? wb - 1 : 0);
-  const int64_t off = (((int64_t)b * Hkv + kv) * wstride + tl) * D + col * 8;
-  kraw = make_uint4(0u, 0u, 0u, 0u);
-  vraw = kraw;
-  if (wb > wa) {
-    kraw = *reinterpret_cast<const uint4*>(kw + off);
-    vraw = *reinterpret_cast<const uint4*>(vw + off);
+  const bool act = have && t < wb;
+  const int tl = t < wb ? t : (wb > 0 ? wb - 1 : 0);
+  const uint16_t* kp = reinterpret_cast<const uint16_t*>(q) + col * 8;
+  const uint16_t* vp = kp;
+  if (have) {
+    const int64_t off = (((int64_t)b * Hkv + kv) * wstride + tl) * D + col * 8;
+    kp = kw + off;
+    vp = vw + off;
   }
+  const uint4 kl = *reinterpret_cast<const uint4*>(kp);
+  const uint4 vl = *reinterpret_cast<const uint4*>(vp);
+  const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+  kraw = act ? kl : z;
+  vraw = act ? vl : z;
 #pragma unroll
   for (int r = 0; r < RP; ++r) {
     const float4* qp = reinterpret_cast<const float4*>(
@@ -466,16 +497,18 @@ __device__ __forceinline__ void win_slice_scores(float (&sw)[RP], uint4 kraw,
   }
 }
 
-// SGC: compile-time S*G (multiple of 16), or 0 = runtime bytes.
+// SGC: compile-time S*G (multiple of 16), or 0 = runtime bytes.  FUSE: the
+// block builds its unit's LUT itself (else it stages the one attn_lut_kernel
+// wrote); separate instances keep each path's memory waits exact.
 // wslice > 0: block ci also owns window tokens [ci*wslice, (ci+1)*wslice),
 // folded into its record; otherwise blocks x >= n_chunks are window blocks.
-template <int RP, int SGC, int D>
+template <int RP, int SGC, int D, bool FUSE>
 __global__ __launch_bounds__(CH_THREADS, 1) void attn_chunk_kernel(
     const uint8_t* __restrict__ kcodes, const uint8_t* __restrict__ vcodes,
     const float* __restrict__ vcb, const float* __restrict__ lut, float* __restrict__ part,
     int Hq, int Hkv, int S, int G, int C, int Tc, int n_chunks, int chunk, int n_hsplit,
     int pstride, int fbits, int cparts, size_t lut_slice, const float* __restrict__ kcb,
-    int fuse_lut, const float* __restrict__ q,
+    const float* __restrict__ q,
     const uint16_t* __restrict__ kw, const uint16_t* __restrict__ vw, int W, int wslice,
     int nslots, float scale, int cstride, int wstride, const float* __restrict__ ksm,
     int64_t ksm_rows) {
@@ -496,10 +529,11 @@ __global__ __launch_bounds__(CH_THREADS, 1) void attn_chunk_kernel(
     return;
   }
   const int SG = SGC ? SGC : S * G;
-  const int tabn = SG * C * RP;                         // entries in the table region
+  const int tabn = SG * C * RP;                         // LUT entries
+  const int tabh = SG * hist_stride(C, RP);             // histogram words (the region's size)
   float* tabf = reinterpret_cast<float*>(smem);         // LUT during pass 1
   uint32_t* tabu = reinterpret_cast<uint32_t*>(smem);   // histogram during pass 2
-  float* cpart = reinterpret_cast<float*>(smem + (((size_t)tabn * 4 + 15) & ~(size_t)15));
+  float* cpart = reinterpret_cast<float*>(smem + (((size_t)tabh * 4 + 15) & ~(size_t)15));
   __shared__ float red_f[8][RP], red_wf[8][RP], red_wl[8][RP];
   __shared__ uint32_t red_u[8][RP];
   __shared__ float mx[RP], mxw[RP], ltw[RP];
@@ -511,104 +545,152 @@ __global__ __launch_bounds__(CH_THREADS, 1) void attn_chunk_kernel(
   const int t1 = (t0 + chunk) < Tc ? (t0 + chunk) : Tc;
 
   const int64_t rowbase = ((int64_t)b * Hkv + kv) * (int64_t)cstride;
-  // first KP token rows of K codes (and later of V codes) staged in registers
-  // (32 VGPRs) so their HBM latency overlaps the LUT staging (the max
-  // reduction for V)
+  // The first KP token rows of K codes (and of V codes) are staged in
+  // registers (32 VGPRs each) so their HBM latency overlaps the LUT work.
+  // Prefetches are issued unconditionally, rows past the chunk clamped to its
+  // last one: vector loads complete in order, and a load that may or may not
+  // have been issued makes later waits drain everything in flight.  A block
+  // that builds its LUT loads its V rows at the start too; one that stages a
+  // prepared LUT waits for all its loads once (the LDS copy), so its V rows
+  // follow pass 1 instead.
   constexpr int SGW = SGC ? SGC / 16 : 1;
   constexpr int KP = SGC ? (128 / SGC < CH_TPT ? 128 / SGC : CH_TPT) : 0;
   constexpr int KPA = KP ? KP : 1;
-  uint4 cpre[KPA][SGW];
-  if constexpr (KP > 0) {
+  uint4 cpre[KPA][SGW], vpre[KPA][SGW];
+  auto prefetch_rows = [&](const uint8_t* __restrict__ codes_, uint4 (&dst)[KPA][SGW]) {
+    if constexpr (KP > 0) {
 #pragma unroll
-    for (int k = 0; k < KP; ++k) {
-      const int t = t0 + tid + CH_THREADS * k;
-      if (t < t1) load_codes<SGC>(kcodes + (rowbase + t) * SG, cpre[k]);
+      for (int k = 0; k < KP; ++k) {
+        const int t = t0 + tid + CH_THREADS * k;
+        load_codes<SGC>(codes_ + (rowbase + (t < t1 ? t : t1 - 1)) * SG, dst[k]);
+      }
     }
-  }
+  };
+  prefetch_rows(kcodes, cpre);
 
-  if (fuse_lut) {
+  if constexpr (FUSE) {
     // ---- build this unit's LUT in LDS: scale * H q / sqrt(D) for the RP
-    // heads (wave 0), then entry (sg, c) = q_rot_g . C^K_sg[c], summed in the
-    // order attn_lut_kernel uses.  For dsub = 8 the codebook rows come in
-    // batches of 4 per thread, the first batch in flight across the q
-    // rotation and each next one across the current one's arithmetic.
+    // heads, then entry (sg, c) = q_rot_g . C^K_sg[c], summed in the order
+    // attn_lut_kernel uses.  For dsub = 8 and C = 256 a thread owns one sg
+    // per pass (16 * pass + tid / 32) and the codewords c = tid % 32 + 32 k,
+    // k < 8: its slice of q_rot is read from LDS once per pass, and a wave's
+    // row loads stay two contiguous 1 KiB runs.  The pass's rows come in two
+    // halves of 4 (both in flight across the q rotation), each half of the
+    // next pass issued across the arithmetic of the current one.
     __shared__ float qs[RP][D];
+    prefetch_rows(vcodes, vpre);
+    constexpr int QROWS = 64 / L;                       // q rows per wave-wide load
+    constexpr int QIT = (RP + QROWS - 1) / QROWS;
+    float qraw[QIT][8];
+#pragma unroll
+    for (int i = 0; i < QIT; ++i) {
+      const int r = i * QROWS + lane / L;
+      const int rr = r < RP ? r : RP - 1;
+      const float4* qp = reinterpret_cast<const float4*>(
+          q + ((int64_t)b * Hq + h0 + (rr < nh ? rr : nh - 1)) * D + (lane % L) * 8);
+      const float4 x0 = qp[0], x1 = qp[1];
+      qraw[i][0] = x0.x; qraw[i][1] = x0.y; qraw[i][2] = x0.z; qraw[i][3] = x0.w;
+      qraw[i][4] = x1.x; qraw[i][5] = x1.y; qraw[i][6] = x1.z; qraw[i][7] = x1.w;
+    }
     const int dsub = D / G;
     const int nit = SG * C;
+    const bool fast = dsub == 8 && C == 256;
+    const int npass = (SG + 15) / 16;
     float4 cb0[4][2], cb1[4][2];
-    auto load_batch = [&](float4 (&cb)[4][2], int base) {
+    auto load_half = [&](float4 (&cb)[4][2], int pass, int half) {   // rows past nit: the last
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int it = base + tid + CH_THREADS * i;
-        if (it < nit) {
-          const float4* cp = reinterpret_cast<const float4*>(kcb + (int64_t)it * 8);
-          cb[i][0] = cp[0];
-          cb[i][1] = cp[1];
-        }
+        const int it = (16 * pass + tid / 32) * 256 + tid % 32 + 32 * (half * 4 + i);
+        const float4* cp = reinterpret_cast<const float4*>(kcb + (int64_t)(it < nit ? it : nit - 1) * 8);
+        cb[i][0] = cp[0];
+        cb[i][1] = cp[1];
       }
     };
-    auto lut_entry = [&](int it, auto&& cv, int n) {     // cv(j): entry j of row it
-      const int g = (it / C) % G;
-      float acc[RP];
+    if (fast) {
+      load_half(cb0, 0, 0);
+      load_half(cb1, 0, 1);
+    }
+    // the smoothing row is read whatever ksm holds (q when there is none) so
+    // the loads in flight stay countable; every wave rotates, wave 0 stores
+    float fac[QIT][8];
 #pragma unroll
-      for (int r = 0; r < RP; ++r) acc[r] = 0.0f;
-      for (int j = 0; j < n; ++j) {
-        const float c = cv(j);
+    for (int i = 0; i < QIT; ++i) {
+      const float4* fp = reinterpret_cast<const float4*>(
+          ksm != nullptr ? ksm + (((int64_t)b * Hkv + kv) % ksm_rows) * D + (lane % L) * 8
+                         : q + (lane % L) * 8);
+      const float4 f0 = fp[0], f1 = fp[1];
+      fac[i][0] = f0.x; fac[i][1] = f0.y; fac[i][2] = f0.z; fac[i][3] = f0.w;
+      fac[i][4] = f1.x; fac[i][5] = f1.y; fac[i][6] = f1.z; fac[i][7] = f1.w;
+    }
 #pragma unroll
-        for (int r = 0; r < RP; ++r) acc[r] = __builtin_fmaf(qs[r][g * n + j], c, acc[r]);
-      }
-      if constexpr (RP == 4) {
-        *reinterpret_cast<float4*>(tabf + it * 4) = make_float4(acc[0], acc[1], acc[2], acc[3]);
-      } else if constexpr (RP == 2) {
-        *reinterpret_cast<float2*>(tabf + it * 2) = make_float2(acc[0], acc[1]);
-      } else {
-        tabf[it] = acc[0];
-      }
-    };
-    if (dsub == 8) load_batch(cb0, 0);
-    if (tid < 64) {
-      constexpr int ROWS = 64 / L;
+    for (int i = 0; i < QIT; ++i) {
+      const int r = i * QROWS + lane / L;
+      float v[8];
 #pragma unroll
-      for (int r0 = 0; r0 < RP; r0 += ROWS) {
-        const int r = r0 + lane / L;
-        const int rr = r < RP ? r : RP - 1;
-        const float* qp = q + ((int64_t)b * Hq + h0 + (rr < nh ? rr : nh - 1)) * D + (lane % L) * 8;
-        float v[8];
+      for (int e = 0; e < 8; ++e) v[e] = ksm != nullptr ? qraw[i][e] * fac[i][e] : qraw[i][e];
+      hadamard_row<8, L>(v, lane);
+      const float rs = scale * rsqrt_pow2(D);
+      if (wave == 0 && r < RP) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = qp[e];
-        if (ksm != nullptr) smooth_query<D>(v, ksm, b, kv, Hkv, ksm_rows, lane % L);
-        hadamard_row<8, L>(v, lane);
-        const float rs = scale * rsqrt_pow2(D);
-        if (r < RP) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) qs[r][(lane % L) * 8 + e] = v[e] * rs;
-        }
+        for (int e = 0; e < 8; ++e) qs[r][(lane % L) * 8 + e] = v[e] * rs;
       }
     }
     __syncthreads();
-    if (dsub == 8) {
-      for (int base = 0; base < nit; base += 8 * CH_THREADS) {
-        if (base + 4 * CH_THREADS < nit) load_batch(cb1, base + 4 * CH_THREADS);
+    if (fast) {
+      const int gsub = tid / 32, cl = tid % 32;
+      auto half_entries = [&](const float4 (&cb)[4][2], int sg, int half, const float (&qv)[RP][8]) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int it = base + tid + CH_THREADS * i;
-          const float cv[8] = {cb0[i][0].x, cb0[i][0].y, cb0[i][0].z, cb0[i][0].w,
-                               cb0[i][1].x, cb0[i][1].y, cb0[i][1].z, cb0[i][1].w};
-          if (it < nit) lut_entry(it, [&](int j) { return cv[j]; }, 8);
-        }
-        if (base + 8 * CH_THREADS < nit) load_batch(cb0, base + 8 * CH_THREADS);
+          const float cv[8] = {cb[i][0].x, cb[i][0].y, cb[i][0].z, cb[i][0].w,
+                               cb[i][1].x, cb[i][1].y, cb[i][1].z, cb[i][1].w};
+          float acc[RP];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int it = base + 4 * CH_THREADS + tid + CH_THREADS * i;
-          const float cv[8] = {cb1[i][0].x, cb1[i][0].y, cb1[i][0].z, cb1[i][0].w,
-                               cb1[i][1].x, cb1[i][1].y, cb1[i][1].z, cb1[i][1].w};
-          if (it < nit) lut_entry(it, [&](int j) { return cv[j]; }, 8);
+          for (int r = 0; r < RP; ++r) {
+            acc[r] = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[r] = __builtin_fmaf(qv[r][j], cv[j], acc[r]);
+          }
+          const int it = sg * 256 + cl + 32 * (half * 4 + i);
+          if constexpr (RP == 4) {
+            *reinterpret_cast<float4*>(tabf + it * 4) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+          } else if constexpr (RP == 2) {
+            *reinterpret_cast<float2*>(tabf + it * 2) = make_float2(acc[0], acc[1]);
+          } else {
+            tabf[it] = acc[0];
+          }
         }
+      };
+      for (int pass = 0; pass < npass; ++pass) {
+        const int sg = 16 * pass + gsub;
+        const bool own = sg < SG;
+        const int g = (own ? sg : 0) % G;
+        float qv[RP][8];
+#pragma unroll
+        for (int r = 0; r < RP; ++r) {
+          const float4* qp = reinterpret_cast<const float4*>(&qs[r][g * 8]);
+          const float4 x0 = qp[0], x1 = qp[1];
+          qv[r][0] = x0.x; qv[r][1] = x0.y; qv[r][2] = x0.z; qv[r][3] = x0.w;
+          qv[r][4] = x1.x; qv[r][5] = x1.y; qv[r][6] = x1.z; qv[r][7] = x1.w;
+        }
+        if (own) half_entries(cb0, sg, 0, qv);
+        if (pass + 1 < npass) load_half(cb0, pass + 1, 0);
+        if (own) half_entries(cb1, sg, 1, qv);
+        if (pass + 1 < npass) load_half(cb1, pass + 1, 1);
       }
     } else {
       for (int it = tid; it < nit; it += CH_THREADS) {
+        const int g = (it / C) % G;
         const float* cp = kcb + (int64_t)it * dsub;
-        lut_entry(it, [&](int j) { return cp[j]; }, dsub);
+        float acc[RP];
+#pragma unroll
+        for (int r = 0; r < RP; ++r) acc[r] = 0.0f;
+        for (int j = 0; j < dsub; ++j) {
+          const float c = cp[j];
+#pragma unroll
+          for (int r = 0; r < RP; ++r) acc[r] = __builtin_fmaf(qs[r][g * dsub + j], c, acc[r]);
+        }
+#pragma unroll
+        for (int r = 0; r < RP; ++r) tabf[it * RP + r] = acc[r];
       }
     }
   } else {
@@ -628,12 +710,12 @@ __global__ __launch_bounds__(CH_THREADS, 1) void attn_chunk_kernel(
   // window slice rows: in flight during pass 1, used after it
   uint4 wkraw, wvraw;
   float wq[RP][8], wsc[RP];
-  bool wact = false;
-  if (wslice > 0) {
+  bool wact;
+  {
     const int wa = ci * wslice < W ? ci * wslice : W;
     const int wb = (wa + wslice) < W ? (wa + wslice) : W;
-    wact = win_slice_load<RP, D>(wkraw, wvraw, wq, q, kw, vw, b, kv, h0, nh, Hq, Hkv, wstride, wa,
-                                 wb, tid);
+    wact = win_slice_load<RP, D>(wkraw, wvraw, wq, q, kw, vw, wslice > 0, b, kv, h0, nh, Hq, Hkv,
+                                 wstride, wa, wb, tid);
   }
   __syncthreads();
 
@@ -665,14 +747,8 @@ __global__ __launch_bounds__(CH_THREADS, 1) void attn_chunk_kernel(
       for (int r = 0; r < RP; ++r) sc[k][r] = acc[r];
     }
   }
-  if constexpr (KP > 0) {                               // V code rows, as for K
-#pragma unroll
-    for (int k = 0; k < KP; ++k) {
-      const int t = t0 + tid + CH_THREADS * k;
-      if (t < t1) load_codes<SGC>(vcodes + (rowbase + t) * SG, cpre[k]);
-    }
-  }
   if (wslice > 0) win_slice_scores<RP, D>(wsc, wkraw, wq, wact, scale);
+  if constexpr (!FUSE) prefetch_rows(vcodes, vpre);   // after the window row's wait
   // ---- chunk max per head
 #pragma unroll
   for (int r = 0; r < RP; ++r) {
@@ -696,9 +772,9 @@ __global__ __launch_bounds__(CH_THREADS, 1) void attn_chunk_kernel(
     mx[tid] = v;
     mxw[tid] = vw;
   }
-  for (int i = tid; i < tabn / 4; i += CH_THREADS)
+  for (int i = tid; i < tabh / 4; i += CH_THREADS)
     reinterpret_cast<uint4*>(tabu)[i] = make_uint4(0u, 0u, 0u, 0u);
-  for (int i = (tabn / 4) * 4 + tid; i < tabn; i += CH_THREADS) tabu[i] = 0u;
+  for (int i = (tabh / 4) * 4 + tid; i < tabh; i += CH_THREADS) tabu[i] = 0u;
   __syncthreads();
   float m[RP];
 #pragma unroll
@@ -752,12 +828,12 @@ __global__ __launch_bounds__(CH_THREADS, 1) void attn_chunk_kernel(
         pw[r] = (uint32_t)__builtin_rintf(__expf(sc[k][r] - m[r]) * fscale);
         ls[r] += pw[r];
       }
-      auto scatter = [&](int sg, int z) { hist_add<RP>(tabu, (sg * C + z) * RP, pw); };
+      auto scatter = [&](int sg, int z) { hist_add<RP>(tabu, sg, z, C, pw); };
       if constexpr (SGC != 0) {
         uint4 w[SGW];
         if (k < KP) {
 #pragma unroll
-          for (int i = 0; i < SGW; ++i) w[i] = cpre[k < KP ? k : 0][i];
+          for (int i = 0; i < SGW; ++i) w[i] = vpre[k < KP ? k : 0][i];
         } else {
           load_codes<SGC>(vcodes + (rowbase + t) * SG, w);
         }
@@ -818,13 +894,13 @@ __global__ __launch_bounds__(CH_THREADS, 1) void attn_chunk_kernel(
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc[r][e] = 0.0f;
     const float* cvp = vcb + (int64_t)sg * C * dsub + j0;
-    const uint32_t* hp = tabu + sg * C * RP;
+    const uint32_t* hp = tabu + sg * hist_stride(C, RP);
 #pragma unroll 16
     for (int c = c0; c < c1; ++c) {
       const float4 cv = *reinterpret_cast<const float4*>(cvp + (int64_t)c * dsub);
 #pragma unroll
       for (int r = 0; r < RP; ++r) {
-        const float w = (float)hp[c * RP + r];
+        const float w = (float)hp[hist_bin<RP>(c, r, C)];
         acc[r][0] = __builtin_fmaf(w, cv.x, acc[r][0]);
         acc[r][1] = __builtin_fmaf(w, cv.y, acc[r][1]);
         acc[r][2] = __builtin_fmaf(w, cv.z, acc[r][2]);
@@ -954,7 +1030,7 @@ static hipError_t launch_rp(const AttnPlan& p, int SG, const float* q, const flo
     if (e != hipSuccess) return e;
   }
   if (p.n_chunks > 0) {
-    const size_t tab = (((size_t)SG * C * RP * 4) + 15) & ~(size_t)15;
+    const size_t tab = (((size_t)SG * hist_stride(C, RP) * 4) + 15) & ~(size_t)15;
     lds = tab + (size_t)S * p.cparts * RP * D * 4;
   }
   if (p.n_wblocks > 0) {
@@ -962,18 +1038,19 @@ static hipError_t launch_rp(const AttnPlan& p, int SG, const float* q, const flo
     if (wl > lds) lds = wl;
   }
   if (p.wslice > 0 && S * p.cparts < 8)               // window row sums need 8 slots
-    lds = ((((size_t)SG * C * RP * 4) + 15) & ~(size_t)15) + (size_t)8 * RP * D * 4;
+    lds = ((((size_t)SG * hist_stride(C, RP) * 4) + 15) & ~(size_t)15) + (size_t)8 * RP * D * 4;
   dim3 grid(p.n_chunks + p.n_wblocks, Hkv * p.n_hsplit, B);
   const int nslots = p.n_chunks + p.n_wblocks;
 #define KVQ_CH(SGV, DV)                                                                        \
   {                                                                                            \
-    auto kern = attn_chunk_kernel<RP, SGV, DV>;                                                \
+    auto kern = p.fuse_lut ? attn_chunk_kernel<RP, SGV, DV, true>                              \
+                           : attn_chunk_kernel<RP, SGV, DV, false>;                            \
     e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,     \
                             (int)lds);                                                         \
     if (e != hipSuccess) return e;                                                             \
     kern<<<grid, CH_THREADS, lds, st>>>(kc, vc, vcb, lut, part, Hq, Hkv, S, G, C, Tc,          \
                                         p.n_chunks, p.chunk, p.n_hsplit, p.pstride, p.fbits,   \
-                                        p.cparts, p.lut_slice, kcb, p.fuse_lut, q, kw, vw, W,  \
+                                        p.cparts, p.lut_slice, kcb, q, kw, vw, W,              \
                                         p.wslice, nslots, scale, cstride, wstride, ksm.f,      \
                                         ksm.n_scale);                                          \
     return hipGetLastError();                                                                  \
