@@ -6,95 +6,229 @@
 // stage outputs, then unrotate).
 //
 // The stage sum is accumulated in float64 and rounded once to float32, so the
-// result is the correctly rounded sum whatever the stage order.  Layout as in
-// K1: L = D/8 lanes per row, 8 output dims per lane (coalesced 32-byte
-// stores), which is also the layout the optional unrotation needs.
-// HBM-bound by the 4*D-byte float32 output per vector.
+// result is the correctly rounded sum whatever the stage order.  HBM-bound by
+// the 4*D-byte float32 output per vector.
+//
+// Lane layout: L = D/8 lanes per row; lane c of a row holds the dims
+// [4c, 4c+4) (elements 0..3) and [D/2 + 4c, D/2 + 4c + 4) (elements 4..7).
+// Each of the two 16-byte stores of a lane then lands next to its
+// neighbours' (a row's lanes write two contiguous D*2-byte halves).  The
+// layout is a permutation of the bits of the dim index (the top bit becomes
+// the element's bit 2), and the Walsh-Hadamard matrix is unchanged by
+// permuting the index bits of rows and columns alike, so the butterfly over
+// (lane, element) computes the same transform.
+//
+// Two variants: with one stage whose codebooks fit in LDS (G*C*dsub*4 bytes
+// up to RC_LDS_MAX), each block copies them into LDS once and codes a range
+// of that book's vectors, so the codeword gathers are LDS reads; otherwise
+// the gathers go through the caches (a grid-stride loop over all vectors).
 #include "kvq_internal.h"
 
 namespace kvq {
 
-// Each lane handles UNR independent vectors per iteration, stage-outer so
-// that the code bytes and codeword rows of all UNR vectors are in flight
-// together (memory-level parallelism).  dsub >= 8: a lane's 8 output dims lie
-// in one group.
+constexpr int RC_THREADS = 512;              // cache variant
+constexpr int RC_LDS_THREADS = 1024;         // LDS variant: one block per CU at 128 KiB
+constexpr int RC_UNR = 4;                    // vectors per lane per iteration
+constexpr size_t RC_LDS_MAX = 128 * 1024;
+
+// Code bytes of RC_UNR vectors for a lane: stages s < SS, groups ga and gb.
+template <int SS>
+struct RcCodes {
+  int za[RC_UNR][SS], zb[RC_UNR][SS];
+};
+
+template <int SS>
+__device__ __forceinline__ void rc_load_codes(RcCodes<SS>& k, const uint8_t* __restrict__ codes,
+                                              const int64_t (&vec)[RC_UNR], int G, int ga,
+                                              int gb) {
+#pragma unroll
+  for (int u = 0; u < RC_UNR; ++u)
+#pragma unroll
+    for (int s = 0; s < SS; ++s) {
+      const uint8_t* row = codes + vec[u] * (SS * G) + s * G;
+      k.za[u][s] = row[ga];
+      k.zb[u][s] = row[gb];
+    }
+}
+
+// Finish RC_UNR vectors of a lane (their float32 sums): optional unrotation
+// and smoothing, the two 16-byte stores.
 template <int D>
-__global__ __launch_bounds__(256) void reconstruct_kernel(
+__device__ __forceinline__ void rc_finish(float (&sum)[RC_UNR][8], float* __restrict__ out,
+                                          const int64_t (&vec)[RC_UNR],
+                                          const bool (&live)[RC_UNR], int64_t n_per_book,
+                                          int unrotate, const float* __restrict__ smooth,
+                                          int64_t n_scale, int64_t n_rows, int lane, int da,
+                                          int db) {
+  constexpr int L = D / 8;
+#pragma unroll
+  for (int u = 0; u < RC_UNR; ++u) {
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = sum[u][e];
+    if (unrotate) {                         // uniform branch: all lanes take it
+      hadamard_row<8, L>(v, lane);
+      constexpr float sc = rsqrt_pow2(D);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] *= sc;
+    }
+    if (smooth != nullptr && live[u]) {     // dual transform undone: times the factors
+      const int64_t book = vec[u] / n_per_book;
+      const int64_t seq = (vec[u] - book * n_per_book) / n_rows;
+      const float* lp = smooth + (book * n_scale + seq % n_scale) * D;
+      const float4 a = *reinterpret_cast<const float4*>(lp + da);
+      const float4 b = *reinterpret_cast<const float4*>(lp + db);
+      v[0] *= a.x; v[1] *= a.y; v[2] *= a.z; v[3] *= a.w;
+      v[4] *= b.x; v[5] *= b.y; v[6] *= b.z; v[7] *= b.w;
+    }
+    if (live[u]) {
+      float* o = out + vec[u] * D;
+      *reinterpret_cast<float4*>(o + da) = make_float4(v[0], v[1], v[2], v[3]);
+      *reinterpret_cast<float4*>(o + db) = make_float4(v[4], v[5], v[6], v[7]);
+    }
+  }
+}
+
+// LDS variant (SS = S stages; instantiated for one stage): grid (blocks per
+// book, n_books);
+// block (x, book) copies the book's codebooks into LDS and codes its vectors
+// [x*per, (x+1)*per).  The code bytes of a wave's next RC_UNR x ROWS vectors
+// are loaded while the current ones are summed and stored.
+template <int D, int SS>
+__global__ __launch_bounds__(RC_LDS_THREADS) void reconstruct_lds_kernel(
+    const uint8_t* __restrict__ codes, const float* __restrict__ cb, float* __restrict__ out,
+    int64_t n_per_book, int64_t per_block, int G, int C, int dsub, int unrotate,
+    const float* __restrict__ smooth, int64_t n_scale, int64_t n_rows) {
+  constexpr int L = D / 8;
+  constexpr int ROWS = 64 / L;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const float* cbl = reinterpret_cast<const float*>(smem);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane % L;
+  const int da = 4 * col, db = D / 2 + 4 * col;
+  const int ga = da / dsub, ja = da - ga * dsub;
+  const int gb = db / dsub, jb = db - gb * dsub;
+  const int64_t book = blockIdx.y;
+  const int64_t book_stride = (int64_t)SS * G * C * dsub;
+  const int64_t v0 = (int64_t)blockIdx.x * per_block;
+  const int64_t v1 = (v0 + per_block) < n_per_book ? (v0 + per_block) : n_per_book;
+  const int64_t first = book * n_per_book;              // global index of the book's vector 0
+  constexpr int64_t STEP = (int64_t)ROWS * (RC_LDS_THREADS / 64);
+  auto rows_of = [&](int64_t wbase, int64_t (&vec)[RC_UNR], bool (&live)[RC_UNR]) {
+#pragma unroll
+    for (int u = 0; u < RC_UNR; ++u) {
+      const int64_t v = wbase + lane / L + u * STEP;
+      live[u] = v < v1;
+      vec[u] = first + (live[u] ? v : v1 - 1);
+    }
+  };
+  // the first codes are in flight across the codebook copy
+  int64_t wbase = v0 + wave * ROWS;
+  int64_t vec[RC_UNR];
+  bool live[RC_UNR];
+  rows_of(wbase, vec, live);
+  RcCodes<SS> cur;
+  rc_load_codes<SS>(cur, codes, vec, G, ga, gb);
+  const float4* src = reinterpret_cast<const float4*>(cb + book * book_stride);
+  for (int64_t i = threadIdx.x; i < book_stride / 4; i += RC_LDS_THREADS)
+    reinterpret_cast<float4*>(smem)[i] = src[i];
+  __syncthreads();
+  // the loop bound is wave-uniform: every lane joins the butterfly
+  for (; wbase < v1; wbase += STEP * RC_UNR) {
+    int64_t nvec[RC_UNR];
+    bool nlive[RC_UNR];
+    rows_of(wbase + STEP * RC_UNR, nvec, nlive);
+    RcCodes<SS> nxt;
+    rc_load_codes<SS>(nxt, codes, nvec, G, ga, gb);
+    // one or two stages: the float32 sum is already the correctly rounded
+    // one (a single entry, or one rounding of the sum of two floats)
+    float sum[RC_UNR][8];
+#pragma unroll
+    for (int u = 0; u < RC_UNR; ++u) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sum[u][e] = 0.0f;
+#pragma unroll
+      for (int s = 0; s < SS; ++s) {
+        const int za = cur.za[u][s] < C ? cur.za[u][s] : C - 1;
+        const int zb = cur.zb[u][s] < C ? cur.zb[u][s] : C - 1;
+        const float4 a = *reinterpret_cast<const float4*>(cbl + ((s * G + ga) * C + za) * dsub + ja);
+        const float4 b = *reinterpret_cast<const float4*>(cbl + ((s * G + gb) * C + zb) * dsub + jb);
+        sum[u][0] += a.x; sum[u][1] += a.y; sum[u][2] += a.z; sum[u][3] += a.w;
+        sum[u][4] += b.x; sum[u][5] += b.y; sum[u][6] += b.z; sum[u][7] += b.w;
+      }
+    }
+    rc_finish<D>(sum, out, vec, live, n_per_book, unrotate, smooth, n_scale, n_rows, lane, da,
+                 db);
+    cur = nxt;
+#pragma unroll
+    for (int u = 0; u < RC_UNR; ++u) {
+      vec[u] = nvec[u];
+      live[u] = nlive[u];
+    }
+  }
+}
+
+// Cache variant: grid-stride over every vector of every book, any S.
+template <int D>
+__global__ __launch_bounds__(RC_THREADS) void reconstruct_kernel(
     const uint8_t* __restrict__ codes, const float* __restrict__ cb, float* __restrict__ out,
     int64_t n_books, int64_t n_per_book, int G, int S, int C, int dsub, int unrotate,
     const float* __restrict__ smooth, int64_t n_scale, int64_t n_rows) {
   constexpr int L = D / 8;
-  constexpr int ROWS_PER_WAVE = 64 / L;
-  constexpr int UNR = 4;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int64_t n_total = n_books * n_per_book;
-  const int64_t waves_total = (int64_t)gridDim.x * (blockDim.x >> 6);
-  const int sub = lane / L;
+  constexpr int ROWS = 64 / L;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane % L;
+  const int da = 4 * col, db = D / 2 + 4 * col;
+  const int ga = da / dsub, ja = da - ga * dsub;
+  const int gb = db / dsub, jb = db - gb * dsub;
   const int SG = S * G;
-  const int64_t book_stride = (int64_t)S * G * C * dsub;   // floats per book
-  const int64_t step = waves_total * ROWS_PER_WAVE;
-  const int d0 = col * 8;
-  const int g = d0 / dsub, j0 = d0 % dsub;
-  for (int64_t base = ((int64_t)blockIdx.x * (blockDim.x >> 6) + wave) * ROWS_PER_WAVE;
-       base < n_total; base += step * UNR) {
-    const uint8_t* crow[UNR];
-    const float* bk[UNR];
+  const int64_t n_total = n_books * n_per_book;
+  const int64_t book_stride = (int64_t)S * G * C * dsub;
+  const int64_t step = (int64_t)gridDim.x * (RC_THREADS / 64) * ROWS;
+  // the loop bound is wave-uniform: every lane joins the butterfly
+  for (int64_t wbase = ((int64_t)blockIdx.x * (RC_THREADS / 64) + wave) * ROWS; wbase < n_total;
+       wbase += step * RC_UNR) {
+    int64_t vec[RC_UNR];
+    bool live[RC_UNR];
 #pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      int64_t vec = base + u * step + sub;
-      if (vec >= n_total) vec = n_total - 1;              // keep every lane in the butterfly
-      crow[u] = codes + vec * SG + g;
-      bk[u] = cb + (vec / n_per_book) * book_stride + (int64_t)g * C * dsub + j0;
+    for (int u = 0; u < RC_UNR; ++u) {
+      const int64_t v = wbase + lane / L + u * step;
+      live[u] = v < n_total;
+      vec[u] = live[u] ? v : n_total - 1;
     }
-    double acc[UNR][8];
+    double acc[RC_UNR][8];
 #pragma unroll
-    for (int u = 0; u < UNR; ++u)
+    for (int u = 0; u < RC_UNR; ++u)
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[u][e] = 0.0;
     for (int s = 0; s < S; ++s) {
-      int z[UNR];
+      int za[RC_UNR], zb[RC_UNR];
 #pragma unroll
-      for (int u = 0; u < UNR; ++u) {
-        z[u] = crow[u][s * G];
-        z[u] = z[u] < C ? z[u] : C - 1;
+      for (int u = 0; u < RC_UNR; ++u) {
+        const uint8_t* row = codes + vec[u] * SG + s * G;
+        za[u] = row[ga];
+        zb[u] = row[gb];
+        za[u] = za[u] < C ? za[u] : C - 1;
+        zb[u] = zb[u] < C ? zb[u] : C - 1;
       }
 #pragma unroll
-      for (int u = 0; u < UNR; ++u) {
-        const float4* p = reinterpret_cast<const float4*>(bk[u] + ((int64_t)s * G * C + z[u]) * dsub);
-        const float4 a = p[0], c = p[1];
+      for (int u = 0; u < RC_UNR; ++u) {
+        const float* base = cb + (vec[u] / n_per_book) * book_stride;
+        const float4 a = *reinterpret_cast<const float4*>(
+            base + (((int64_t)s * G + ga) * C + za[u]) * dsub + ja);
+        const float4 b = *reinterpret_cast<const float4*>(
+            base + (((int64_t)s * G + gb) * C + zb[u]) * dsub + jb);
         acc[u][0] += a.x; acc[u][1] += a.y; acc[u][2] += a.z; acc[u][3] += a.w;
-        acc[u][4] += c.x; acc[u][5] += c.y; acc[u][6] += c.z; acc[u][7] += c.w;
+        acc[u][4] += b.x; acc[u][5] += b.y; acc[u][6] += b.z; acc[u][7] += b.w;
       }
     }
+    float sum[RC_UNR][8];
 #pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      const int64_t vec = base + u * step + sub;
-      float v[8];
+    for (int u = 0; u < RC_UNR; ++u)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = (float)acc[u][e];
-      if (unrotate) {                       // uniform branch: all lanes take it
-        hadamard_row<8, L>(v, lane);
-        constexpr float sc = rsqrt_pow2(D);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] *= sc;
-      }
-      if (smooth != nullptr && vec < n_total) {   // dual transform undone: times the factors
-        const int64_t book = vec / n_per_book;
-        const int64_t seq = (vec - book * n_per_book) / n_rows;
-        const float4* lp = reinterpret_cast<const float4*>(
-            smooth + (book * n_scale + seq % n_scale) * D + col * 8);
-        const float4 a = lp[0], c = lp[1];
-        v[0] *= a.x; v[1] *= a.y; v[2] *= a.z; v[3] *= a.w;
-        v[4] *= c.x; v[5] *= c.y; v[6] *= c.z; v[7] *= c.w;
-      }
-      if (vec < n_total) {
-        float4* o = reinterpret_cast<float4*>(out + vec * D + col * 8);
-        o[0] = make_float4(v[0], v[1], v[2], v[3]);
-        o[1] = make_float4(v[4], v[5], v[6], v[7]);
-      }
-    }
+      for (int e = 0; e < 8; ++e) sum[u][e] = (float)acc[u][e];
+    rc_finish<D>(sum, out, vec, live, n_per_book, unrotate, smooth, n_scale, n_rows, lane, da,
+                 db);
   }
 }
 
@@ -104,13 +238,36 @@ hipError_t launch_reconstruct(const uint8_t* codes, const float* cb, float* out,
   const int64_t n = n_books * n_per_book;
   if (n == 0) return hipSuccess;
   const int dsub = D / G;
-  const int rows_per_block = 4 * (64 / (D / 8)) * 4;      // 4 waves, 4 vectors per lane
-  int64_t blocks = (n + rows_per_block - 1) / rows_per_block;
-  if (blocks > 16384) blocks = 16384;
+  const size_t cbytes = (size_t)S * G * C * dsub * sizeof(float);
+  const int64_t vec_per_iter = (int64_t)(RC_THREADS / 64) * (64 / (D / 8)) * RC_UNR;
+  if (cbytes <= RC_LDS_MAX && S == 1) {
+    // blocks per CU that fit the LDS, about 256 CUs' worth of blocks over the books
+    const int per_cu = cbytes * 2 <= 160 * 1024 ? 2 : 1;
+    const int64_t lvec = (int64_t)(RC_LDS_THREADS / 64) * (64 / (D / 8)) * RC_UNR;
+    int64_t nx = (256 * per_cu + n_books - 1) / n_books;
+    int64_t per = (n_per_book + nx - 1) / nx;
+    per = (per + lvec - 1) / lvec * lvec;
+    nx = (n_per_book + per - 1) / per;
+#define KVQ_RL(DD, SSV)                                                                       \
+    if (D == DD && S == SSV) {                                                               \
+      auto kern = reconstruct_lds_kernel<DD, SSV>;                                           \
+      hipError_t e = hipFuncSetAttribute((const void*)kern,                                  \
+                                         hipFuncAttributeMaxDynamicSharedMemorySize,         \
+                                         (int)cbytes);                                       \
+      if (e != hipSuccess) return e;                                                         \
+      kern<<<dim3((unsigned)nx, (unsigned)n_books), RC_LDS_THREADS, cbytes, s>>>(            \
+          codes, cb, out, n_per_book, per, G, C, dsub, unrotate, sm.f, sm.n_scale, n_rows);  \
+      return hipGetLastError();                                                              \
+    }
+    KVQ_RL(64, 1) KVQ_RL(128, 1) KVQ_RL(256, 1)
+#undef KVQ_RL
+  }
+  int64_t blocks = (n + vec_per_iter - 1) / vec_per_iter;
+  if (blocks > 4096) blocks = 4096;
   auto kern = D == 64 ? reconstruct_kernel<64> : D == 128 ? reconstruct_kernel<128>
                                                           : reconstruct_kernel<256>;
-  kern<<<dim3((unsigned)blocks), 256, 0, s>>>(codes, cb, out, n_books, n_per_book, G, S, C, dsub,
-                                              unrotate, sm.f, sm.n_scale, n_rows);
+  kern<<<dim3((unsigned)blocks), RC_THREADS, 0, s>>>(codes, cb, out, n_books, n_per_book, G, S, C,
+                                                     dsub, unrotate, sm.f, sm.n_scale, n_rows);
   return hipGetLastError();
 }
 
