@@ -208,10 +208,10 @@ def main():
                 "counters": prof}
     elif dominant == "reconstruct":
         ach = rec_b / means["reconstruct"] / 1e9
-        traffic, prof = profiled_traffic("reconstruct_kernel", "reconstruct.hip")
+        traffic, prof = profiled_traffic("reconstruct_lds_kernel", "reconstruct.hip")
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "reconstruct_kernel (kvq_decode_reconstruct)",
+                "kernel": "reconstruct_lds_kernel (kvq_decode_reconstruct)",
                 "per_launch": {"bytes": rec_b, "mean_ms": round(means["reconstruct"] * 1e3, 5)},
                 "counters": prof}
     else:
