@@ -104,6 +104,49 @@ def test_reconstruct_out_of_range_codes_clamp():
     assert np.array_equal(got[0], ref)
 
 
+@pytest.mark.parametrize("D,G,C,n", [
+    (128, 16, 256, 1),          # one vector: a single partial row group
+    (128, 16, 256, 5),
+    (128, 16, 100, 777),        # C < 256 with out-of-range codes (clamped)
+    (64, 8, 256, 3001),         # 64 KiB of codebooks: two blocks per CU
+    (256, 32, 64, 1234),        # D = 256 in LDS (C = 64)
+])
+def test_reconstruct_one_stage_lds_shapes(D, G, C, n):
+    """One-stage books small enough for the LDS kernel, at ragged and tiny
+    sizes; rotated output bit-exact, unrotated within 1e-6 * |x_hat|."""
+    say(f"reconstruct, one stage in LDS: D {D} G {G} C {C} n {n}")
+    rng = np.random.default_rng(D + C + n)
+    dsub = D // G
+    cb = rng.standard_normal((2, 1, G, C, dsub)).astype(np.float32)
+    codes = rng.integers(0, 256, size=(2, n, 1, G), dtype=np.uint8)
+    clamped = np.minimum(codes, C - 1)
+    got = kvq.decode_reconstruct(cuda(codes), cuda(cb)).cpu().numpy()
+    got_u = kvq.decode_reconstruct(cuda(codes), cuda(cb), unrotate=True).cpu().numpy()
+    for b in range(2):
+        ref = oracle.reconstruct_rot(clamped[b], cb[b])
+        assert np.array_equal(got[b], ref.astype(np.float32))
+        ref_u = oracle.reconstruct(clamped[b], cb[b])
+        nrm = np.linalg.norm(ref_u, axis=1, keepdims=True)
+        assert np.max(np.abs(got_u[b] - ref_u) / nrm) <= 1e-6
+
+
+def test_reconstruct_full_size_llama_layer_sampled():
+    """The Llama-shaped layer's K and V books at full size (261,120 vectors each,
+    the bench's launch), every 97th vector against the oracle."""
+    say("reconstruct, full-size Llama-shaped layer, sampled")
+    w = synth.workload(2)
+    cb = synth.make_codebooks(w)[:2]
+    rng = np.random.default_rng(11)
+    n = w.n_kv_heads * w.code_tokens
+    codes = rng.integers(0, 256, size=(2, n, 1, w.n_groups), dtype=np.uint8)
+    got_u = kvq.decode_reconstruct(cuda(codes), cuda(cb), unrotate=True).cpu().numpy()
+    idx = np.arange(0, n, 97)
+    for b in range(2):
+        ref = oracle.reconstruct(codes[b][idx], cb[b])
+        nrm = np.linalg.norm(ref, axis=1, keepdims=True)
+        assert np.max(np.abs(got_u[b][idx] - ref) / nrm) <= 1e-6
+
+
 # ------------------------------------------------------------------ encode
 SMALL_ENCODE = [
     (1, dict()),                                              # tiny, full size
