@@ -223,7 +223,19 @@ __global__ __launch_bounds__(256) void scalar_encode_kernel(
 }
 
 // grid (row blocks, n_books); out = levels1[z1] + levels2[z2] (one float32
-// rounding of the sum), then H_D when unrotate.
+// rounding of the sum), then H_D when unrotate.  Lane c of a row holds dims
+// [4c, 4c+4) and [D/2 + 4c, D/2 + 4c + 4): a permutation of the dim index
+// bits, under which the same butterfly computes the transform, and which puts
+// each 16-byte store next to its neighbours'.  The 4 indices of a half sit
+// in 4*B consecutive bits of the packed row.
+template <int B>
+__device__ __forceinline__ uint32_t scalar_bits4(const uint8_t* __restrict__ rowp, int d0) {
+  const int bit = d0 * B;                               // 4*B bits from here, 4*B | 8 or = 4
+  if constexpr (B == 1) return (uint32_t)(rowp[bit >> 3] >> (bit & 7)) & 15u;
+  else if constexpr (B == 2) return rowp[bit >> 3];
+  else return *reinterpret_cast<const uint16_t*>(rowp + (bit >> 3));
+}
+
 template <int D, int B>
 __global__ __launch_bounds__(256) void scalar_reconstruct_kernel(
     const uint8_t* __restrict__ codes, const float* __restrict__ levels, float* __restrict__ out,
@@ -237,32 +249,29 @@ __global__ __launch_bounds__(256) void scalar_reconstruct_kernel(
   stage_levels<B>(levels, book, lv, th);
   const int tid = threadIdx.x, lane = tid & 63;
   const int col = tid % L, rsub = tid / L;
+  const int da = 4 * col, db = D / 2 + 4 * col;
   for (int64_t base = (int64_t)blockIdx.x * RPB * SC_U; base < n;
        base += (int64_t)gridDim.x * RPB * SC_U) {
-    uint32_t p1[SC_U], p2[SC_U];
+    uint32_t p1a[SC_U], p1b[SC_U], p2a[SC_U], p2b[SC_U];
 #pragma unroll
     for (int u = 0; u < SC_U; ++u) {
       const int64_t v = base + u * RPB + rsub;
       const int64_t vl = v < n ? v : n - 1;
-      const uint8_t* rowp = codes + (book * n + vl) * (2 * SB) + col * B;
-      if constexpr (B == 1) {
-        p1[u] = rowp[0];
-        p2[u] = rowp[SB];
-      } else if constexpr (B == 2) {
-        p1[u] = *reinterpret_cast<const uint16_t*>(rowp);
-        p2[u] = *reinterpret_cast<const uint16_t*>(rowp + SB);
-      } else {
-        p1[u] = *reinterpret_cast<const uint32_t*>(rowp);
-        p2[u] = *reinterpret_cast<const uint32_t*>(rowp + SB);
-      }
+      const uint8_t* rowp = codes + (book * n + vl) * (2 * SB);
+      p1a[u] = scalar_bits4<B>(rowp, da);
+      p1b[u] = scalar_bits4<B>(rowp, db);
+      p2a[u] = scalar_bits4<B>(rowp + SB, da);
+      p2b[u] = scalar_bits4<B>(rowp + SB, db);
     }
 #pragma unroll
     for (int u = 0; u < SC_U; ++u) {
       const int64_t v = base + u * RPB + rsub;
       float y[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        y[e] = lv[0][(p1[u] >> (e * B)) & MASK] + lv[1][(p2[u] >> (e * B)) & MASK];
+      for (int e = 0; e < 4; ++e) {
+        y[e] = lv[0][(p1a[u] >> (e * B)) & MASK] + lv[1][(p2a[u] >> (e * B)) & MASK];
+        y[4 + e] = lv[0][(p1b[u] >> (e * B)) & MASK] + lv[1][(p2b[u] >> (e * B)) & MASK];
+      }
       if (unrotate) {
         hadamard_row<8, L>(y, lane);
         constexpr float sc = rsqrt_pow2(D);
@@ -270,9 +279,9 @@ __global__ __launch_bounds__(256) void scalar_reconstruct_kernel(
         for (int e = 0; e < 8; ++e) y[e] *= sc;
       }
       if (v < n) {
-        float4* o = reinterpret_cast<float4*>(out + (book * n + v) * D + col * 8);
-        o[0] = make_float4(y[0], y[1], y[2], y[3]);
-        o[1] = make_float4(y[4], y[5], y[6], y[7]);
+        float* o = out + (book * n + v) * D;
+        *reinterpret_cast<float4*>(o + da) = make_float4(y[0], y[1], y[2], y[3]);
+        *reinterpret_cast<float4*>(o + db) = make_float4(y[4], y[5], y[6], y[7]);
       }
     }
   }
