@@ -303,7 +303,7 @@ __device__ __forceinline__ void window_partial(const float* __restrict__ q,
                                                const uint16_t* __restrict__ kw,
                                                const uint16_t* __restrict__ vw,
                                                float* __restrict__ part, uint8_t* smem, int b,
-                                               int kv, int h0, int nh, int Hq, int Hkv, int W,
+                                               int kv, int h0, int nh, int Hq, int Hkv,
                                                int wstride, int w0, int w1, int slot, int nslots,
                                                int pstride, float scale) {
   constexpr int L = D / 8;
@@ -324,8 +324,7 @@ __device__ __forceinline__ void window_partial(const float* __restrict__ q,
     for (int e = 0; e < 8; ++e) qv[r][e] = qp[e] * scale;
   }
   const int n = w1 - w0;
-  // pass A: scores
-#pragma unroll 4
+  // pass A: scores (the row sums' lane exchanges keep this loop rolled)
   for (int i = 0; i < n; i += ROWS) {                 // uniform trip count
     const int w = i + row;
     const int wl = w < n ? w : n - 1;
@@ -524,7 +523,7 @@ __global__ __launch_bounds__(CH_THREADS, 1) void attn_chunk_kernel(
   if (ci >= n_chunks) {                                 // window block (uniform per block)
     const int w0 = (ci - n_chunks) * ATTN_WIN_BLOCK;
     const int w1 = (w0 + ATTN_WIN_BLOCK) < W ? (w0 + ATTN_WIN_BLOCK) : W;
-    window_partial<RP, D>(q, kw, vw, part, smem, b, kv, h0, nh, Hq, Hkv, W, wstride, w0, w1, ci,
+    window_partial<RP, D>(q, kw, vw, part, smem, b, kv, h0, nh, Hq, Hkv, wstride, w0, w1, ci,
                           nslots, pstride, scale);
     return;
   }
