@@ -64,6 +64,29 @@ __device__ __forceinline__ void load8(const void* p, float (&v)[8]) {
   }
 }
 
+// Four consecutive elements (16-byte aligned for f32, 8-byte for 2-byte types)
+// as float32 into v[o..o+3].
+template <int XT>
+__device__ __forceinline__ void load4(const void* p, float (&v)[8], int o) {
+  if constexpr (XT == 0) {
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    v[o] = a.x; v[o + 1] = a.y; v[o + 2] = a.z; v[o + 3] = a.w;
+  } else {
+    const uint2 w = *reinterpret_cast<const uint2*>(p);
+    const uint32_t ws[2] = {w.x, w.y};
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      if constexpr (XT == 1) {
+        v[o + 2 * i] = bf16_lo(ws[i]);
+        v[o + 2 * i + 1] = bf16_hi(ws[i]);
+      } else {
+        v[o + 2 * i] = f16_bits_to_f32(ws[i]);
+        v[o + 2 * i + 1] = f16_bits_to_f32(ws[i] >> 16);
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------- lane exchanges
 // Value of lane (lane ^ M) within the wavefront, for M in {1,2,4,8,16,32}.
 // DPP or a permlane swap (VALU) where one instruction does it, ds_swizzle

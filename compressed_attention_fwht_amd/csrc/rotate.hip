@@ -5,10 +5,14 @@
 // Walsh-Hadamard rotation).  HBM-bound: each row is read once (2 or 4 bytes
 // per element) and written once as float32.
 //
-// Layout: one row is held by L = D/8 consecutive lanes, 8 elements per lane,
-// so a wavefront covers 64/L rows and each lane moves one 16-byte (bf16/f16)
-// or 32-byte (f32) contiguous piece: fully coalesced.  Butterflies on the 3
-// in-lane bits are register adds; the cross-lane bits use DPP / ds_swizzle.
+// Layout: one row is held by L = D/8 consecutive lanes, 8 elements per lane:
+// lane c holds elements [4c, 4c+4) and [D/2 + 4c, D/2 + 4c + 4), so each of
+// its two loads and two 16-byte stores lands next to its neighbours'.  That
+// layout permutes the bits of the element index (the top bit becomes the
+// in-lane bit 2); the Walsh-Hadamard matrix is unchanged by the same bit
+// permutation of rows and columns, so the butterfly over (lane, element)
+// computes the transform.  Butterflies on the 3 in-lane bits are register
+// adds; the cross-lane bits use DPP / ds_swizzle.
 #include "kvq_internal.h"
 
 namespace kvq {
@@ -23,21 +27,22 @@ __global__ __launch_bounds__(256) void rotate_kernel(const void* x,
   const int wave = threadIdx.x >> 6;
   const int64_t waves_total = (int64_t)gridDim.x * (blockDim.x >> 6);
   const int sub = lane / L;        // row within the wave's group
-  const int col = lane % L;        // 8-element piece within the row
+  const int col = lane % L;        // the lane's place within the row
   const char* xb = reinterpret_cast<const char*>(x);
   for (int64_t base = ((int64_t)blockIdx.x * (blockDim.x >> 6) + wave) * ROWS_PER_WAVE;
        base < n_rows; base += waves_total * ROWS_PER_WAVE) {
     const int64_t row = base + sub;
     const bool live = row < n_rows;
     const int64_t r_ld = live ? row : (n_rows - 1);  // keep every lane in the exchanges
+    const int da = 4 * col, db = D / 2 + 4 * col;
     float v[8];
-    load8<XT>(xb + (r_ld * D + (int64_t)col * 8) * ESZ, v);
+    load4<XT>(xb + (r_ld * D + da) * ESZ, v, 0);
+    load4<XT>(xb + (r_ld * D + db) * ESZ, v, 4);
     hadamard_row<8, L>(v, lane);
     constexpr float sc = rsqrt_pow2(D);
     if (live) {
-      float4* o = reinterpret_cast<float4*>(y + row * D + col * 8);
-      o[0] = make_float4(v[0] * sc, v[1] * sc, v[2] * sc, v[3] * sc);
-      o[1] = make_float4(v[4] * sc, v[5] * sc, v[6] * sc, v[7] * sc);
+      *reinterpret_cast<float4*>(y + row * D + da) = make_float4(v[0] * sc, v[1] * sc, v[2] * sc, v[3] * sc);
+      *reinterpret_cast<float4*>(y + row * D + db) = make_float4(v[4] * sc, v[5] * sc, v[6] * sc, v[7] * sc);
     }
   }
 }
