@@ -287,6 +287,7 @@ def main():
         res["smooth"] = smooth_calls(torch, kvq, x, cb, q, kc, vc, kw, vw, w, dev, flush)
         res["fit"] = fit_calls(torch, kvq, x, cb, w, dev)
         res["scalar"] = scalar_calls(torch, kvq, x, q, kw, vw, w, dev, flush)
+        res["rotate"] = rotate_calls(torch, kvq, x, w, dev, flush)
     del x, recon, flush_buf
     torch.cuda.empty_cache()
     if not args.no_prefill and not args.step_only:
@@ -377,6 +378,29 @@ def scalar_levels(torch, kvq, sigmas, bits, dev):
     lap, _ = kvq.lloyd_max("laplacian", bits)
     rows = [[[v * s for v in g], [v * s * float(np.sqrt(dg)) for v in lap]] for s in sigmas]
     return torch.tensor(rows, dtype=torch.float32, device=dev)
+
+
+def rotate_calls(torch, kvq, x, w, dev, flush, reps=20):
+    """kvq_rotate alone: the layer's K and V rows (input dtype) -> float32
+    rotated rows, flushed caches; HBM-bound (input bytes + 4 bytes per element
+    out)."""
+    rows = x.reshape(-1, w.head_dim)
+    out = torch.empty(rows.shape, dtype=torch.float32, device=dev)
+    ms = []
+    for i in range(reps + 3):
+        flush(i)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        kvq.rotate(rows, out=out)
+        e1.record()
+        torch.cuda.synchronize()
+        if i >= 3:
+            ms.append(e0.elapsed_time(e1))
+    t = float(np.median(ms)) * 1e-3
+    nbytes = rows.numel() * (rows.element_size() + 4)
+    return {"us": round(t * 1e6, 2), "rows": rows.shape[0], "bytes": nbytes,
+            "gbs": round(nbytes / t / 1e9, 1), "pct_hbm_peak": round(100 * nbytes / t / 1e9 / HBM_PEAK_GBS, 2),
+            "note": "all of the layer's K and V rows, input dtype in, float32 out"}
 
 
 def scalar_calls(torch, kvq, x, q, kw, vw, w, dev, flush, bits=2, reps=20):
