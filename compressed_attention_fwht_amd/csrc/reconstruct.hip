@@ -18,17 +18,20 @@
 // permuting the index bits of rows and columns alike, so the butterfly over
 // (lane, element) computes the same transform.
 //
-// Two variants: with one stage whose codebooks fit in LDS (G*C*dsub*4 bytes
-// up to RC_LDS_MAX), each block copies them into LDS once and codes a range
-// of that book's vectors, so the codeword gathers are LDS reads; otherwise
-// the gathers go through the caches (a grid-stride loop over all vectors).
+// Two variants.  With 1, 2 or 4 stages whose per-stage codebooks fit in LDS
+// (G*C*dsub*4 bytes up to RC_LDS_MAX), each block copies its book's stage-0
+// codebooks into LDS once and codes a range of that book's vectors: the
+// stage-0 gathers are LDS reads, later stages' go through the caches.
+// Otherwise every gather goes through the caches (a grid-stride loop over
+// all vectors).
 #include "kvq_internal.h"
+#include <type_traits>
 
 namespace kvq {
 
 constexpr int RC_THREADS = 512;              // cache variant
 constexpr int RC_LDS_THREADS = 1024;         // LDS variant: one block per CU at 128 KiB
-constexpr int RC_UNR = 4;                    // vectors per lane per iteration
+constexpr int RC_UNR = 2;                    // vectors per lane per iteration
 constexpr size_t RC_LDS_MAX = 128 * 1024;
 
 // Code bytes of RC_UNR vectors for a lane: stages s < SS, groups ga and gb.
@@ -89,9 +92,9 @@ __device__ __forceinline__ void rc_finish(float (&sum)[RC_UNR][8], float* __rest
   }
 }
 
-// LDS variant (SS = S stages; instantiated for one stage): grid (blocks per
+// LDS variant (SS = S stages: 1, 2 or 4; stage 0 in LDS): grid (blocks per
 // book, n_books);
-// block (x, book) copies the book's codebooks into LDS and codes its vectors
+// block (x, book) copies the book's stage-0 codebooks into LDS and codes its vectors
 // [x*per, (x+1)*per).  The code bytes of a wave's next RC_UNR x ROWS vectors
 // are loaded while the current ones are summed and stored.
 template <int D, int SS>
@@ -110,6 +113,8 @@ __global__ __launch_bounds__(RC_LDS_THREADS) void reconstruct_lds_kernel(
   const int gb = db / dsub, jb = db - gb * dsub;
   const int64_t book = blockIdx.y;
   const int64_t book_stride = (int64_t)SS * G * C * dsub;
+  const int64_t stage_stride = (int64_t)G * C * dsub;
+  const float* cbg = cb + book * book_stride;
   const int64_t v0 = (int64_t)blockIdx.x * per_block;
   const int64_t v1 = (v0 + per_block) < n_per_book ? (v0 + per_block) : n_per_book;
   const int64_t first = book * n_per_book;              // global index of the book's vector 0
@@ -129,8 +134,8 @@ __global__ __launch_bounds__(RC_LDS_THREADS) void reconstruct_lds_kernel(
   rows_of(wbase, vec, live);
   RcCodes<SS> cur;
   rc_load_codes<SS>(cur, codes, vec, G, ga, gb);
-  const float4* src = reinterpret_cast<const float4*>(cb + book * book_stride);
-  for (int64_t i = threadIdx.x; i < book_stride / 4; i += RC_LDS_THREADS)
+  const float4* src = reinterpret_cast<const float4*>(cbg);
+  for (int64_t i = threadIdx.x; i < stage_stride / 4; i += RC_LDS_THREADS)
     reinterpret_cast<float4*>(smem)[i] = src[i];
   __syncthreads();
   // the loop bound is wave-uniform: every lane joins the butterfly
@@ -141,22 +146,30 @@ __global__ __launch_bounds__(RC_LDS_THREADS) void reconstruct_lds_kernel(
     RcCodes<SS> nxt;
     rc_load_codes<SS>(nxt, codes, nvec, G, ga, gb);
     // one or two stages: the float32 sum is already the correctly rounded
-    // one (a single entry, or one rounding of the sum of two floats)
-    float sum[RC_UNR][8];
+    // one (a single entry, or one rounding of the sum of two floats); four:
+    // float64, rounded once
+    using Acc = typename std::conditional<(SS <= 2), float, double>::type;
+    Acc acc[RC_UNR][8];
 #pragma unroll
     for (int u = 0; u < RC_UNR; ++u) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sum[u][e] = 0.0f;
+      for (int e = 0; e < 8; ++e) acc[u][e] = 0;
 #pragma unroll
       for (int s = 0; s < SS; ++s) {
         const int za = cur.za[u][s] < C ? cur.za[u][s] : C - 1;
         const int zb = cur.zb[u][s] < C ? cur.zb[u][s] : C - 1;
-        const float4 a = *reinterpret_cast<const float4*>(cbl + ((s * G + ga) * C + za) * dsub + ja);
-        const float4 b = *reinterpret_cast<const float4*>(cbl + ((s * G + gb) * C + zb) * dsub + jb);
-        sum[u][0] += a.x; sum[u][1] += a.y; sum[u][2] += a.z; sum[u][3] += a.w;
-        sum[u][4] += b.x; sum[u][5] += b.y; sum[u][6] += b.z; sum[u][7] += b.w;
+        const float* base = s == 0 ? cbl : cbg + s * stage_stride;
+        const float4 a = *reinterpret_cast<const float4*>(base + ((int64_t)ga * C + za) * dsub + ja);
+        const float4 b = *reinterpret_cast<const float4*>(base + ((int64_t)gb * C + zb) * dsub + jb);
+        acc[u][0] += a.x; acc[u][1] += a.y; acc[u][2] += a.z; acc[u][3] += a.w;
+        acc[u][4] += b.x; acc[u][5] += b.y; acc[u][6] += b.z; acc[u][7] += b.w;
       }
     }
+    float sum[RC_UNR][8];
+#pragma unroll
+    for (int u = 0; u < RC_UNR; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sum[u][e] = (float)acc[u][e];
     rc_finish<D>(sum, out, vec, live, n_per_book, unrotate, smooth, n_scale, n_rows, lane, da,
                  db);
     cur = nxt;
@@ -238,9 +251,9 @@ hipError_t launch_reconstruct(const uint8_t* codes, const float* cb, float* out,
   const int64_t n = n_books * n_per_book;
   if (n == 0) return hipSuccess;
   const int dsub = D / G;
-  const size_t cbytes = (size_t)S * G * C * dsub * sizeof(float);
+  const size_t cbytes = (size_t)G * C * dsub * sizeof(float);
   const int64_t vec_per_iter = (int64_t)(RC_THREADS / 64) * (64 / (D / 8)) * RC_UNR;
-  if (cbytes <= RC_LDS_MAX && S == 1) {
+  if (cbytes <= RC_LDS_MAX && (S == 1 || S == 2 || S == 4)) {
     // blocks per CU that fit the LDS, about 256 CUs' worth of blocks over the books
     const int per_cu = cbytes * 2 <= 160 * 1024 ? 2 : 1;
     const int64_t lvec = (int64_t)(RC_LDS_THREADS / 64) * (64 / (D / 8)) * RC_UNR;
@@ -259,7 +272,8 @@ hipError_t launch_reconstruct(const uint8_t* codes, const float* cb, float* out,
           codes, cb, out, n_per_book, per, G, C, dsub, unrotate, sm.f, sm.n_scale, n_rows);  \
       return hipGetLastError();                                                              \
     }
-    KVQ_RL(64, 1) KVQ_RL(128, 1) KVQ_RL(256, 1)
+    KVQ_RL(64, 1) KVQ_RL(128, 1) KVQ_RL(256, 1) KVQ_RL(64, 2) KVQ_RL(128, 2) KVQ_RL(256, 2)
+    KVQ_RL(64, 4) KVQ_RL(128, 4) KVQ_RL(256, 4)
 #undef KVQ_RL
   }
   int64_t blocks = (n + vec_per_iter - 1) / vec_per_iter;

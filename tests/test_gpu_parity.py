@@ -111,14 +111,16 @@ def test_reconstruct_out_of_range_codes_clamp():
     (64, 8, 256, 3001),         # 64 KiB of codebooks: two blocks per CU
     (256, 32, 64, 1234),        # D = 256 in LDS (C = 64)
 ])
-def test_reconstruct_one_stage_lds_shapes(D, G, C, n):
-    """One-stage books small enough for the LDS kernel, at ragged and tiny
-    sizes; rotated output bit-exact, unrotated within 1e-6 * |x_hat|."""
-    say(f"reconstruct, one stage in LDS: D {D} G {G} C {C} n {n}")
-    rng = np.random.default_rng(D + C + n)
+@pytest.mark.parametrize("S", [1, 2, 4])
+def test_reconstruct_lds_shapes(D, G, C, n, S):
+    """Books whose per-stage codebooks fit the LDS kernel (stage 0 in LDS, later
+    stages through the caches), at ragged and tiny sizes; rotated output
+    bit-exact, unrotated within 1e-6 * |x_hat|."""
+    say(f"reconstruct, LDS kernel: D {D} G {G} C {C} n {n} S {S}")
+    rng = np.random.default_rng(D + C + n + S)
     dsub = D // G
-    cb = rng.standard_normal((2, 1, G, C, dsub)).astype(np.float32)
-    codes = rng.integers(0, 256, size=(2, n, 1, G), dtype=np.uint8)
+    cb = rng.standard_normal((2, S, G, C, dsub)).astype(np.float32)
+    codes = rng.integers(0, 256, size=(2, n, S, G), dtype=np.uint8)
     clamped = np.minimum(codes, C - 1)
     got = kvq.decode_reconstruct(cuda(codes), cuda(cb)).cpu().numpy()
     got_u = kvq.decode_reconstruct(cuda(codes), cuda(cb), unrotate=True).cpu().numpy()
