@@ -226,6 +226,7 @@ def main():
     # the same decode call replayed from a HIP graph (captured once): the launch
     # gaps between its kernels leave the measured latency
     graph_us = None
+    layers = None
     if not args.step_only:
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
@@ -248,6 +249,8 @@ def main():
                 gts.append(e0.elapsed_time(e1))
         graph_us = round(float(np.median(gts)) * 1e3, 2)
         del graph
+        layers = decode_layers_graph(torch, kvq, q, kc, vc, cb, kw, vw, out, att_ws, flush,
+                                     eff_b, args.steps)
 
     res = {
         "metric": "decode-attn effective HBM GB/s (% peak) + encode Mvec/s (% MFMA peak)",
@@ -270,7 +273,8 @@ def main():
                    "ms": round(att_s * 1e3, 5), "effective_bytes": eff_b,
                    "bytes": {"codes": code_b, "window": win_b, "lut": lut_b},
                    "cache_flushed": not args.no_flush,
-                   "graph_replay_us": graph_us},
+                   "graph_replay_us": graph_us,
+                   "layers_graph": layers},
         "encode": {"value": round(n_vec / enc_s / 1e6, 2), "unit": "Mvec/s",
                    "pct_bf16_mfma_peak": round(100 * enc_tflops / BF16_PEAK_TFLOPS, 3),
                    "ms": round(enc_s * 1e3, 5), "vectors": n_vec, "algorithmic_flops": enc_flops,
@@ -378,6 +382,52 @@ def scalar_levels(torch, kvq, sigmas, bits, dev):
     lap, _ = kvq.lloyd_max("laplacian", bits)
     rows = [[[v * s for v in g], [v * s * float(np.sqrt(dg)) for v in lap]] for s in sigmas]
     return torch.tensor(rows, dtype=torch.float32, device=dev)
+
+
+def decode_layers_graph(torch, kvq, q, kc, vc, cb, kw, vw, out, ws, flush, eff_b, reps,
+                        n_layers=32):
+    """One decode token through n_layers layers: n_layers decode calls, each on
+    a layer of its own (codes, codebooks, query and window of the layer's
+    shape; codes drawn at random), captured in one HIP graph and replayed after
+    a cache-evicting fill; reported per layer.  The launch gaps between calls
+    are the graph's, as a decode loop over the layers would have them."""
+    g = torch.Generator(device=kc.device).manual_seed(7)
+    per = []
+    for _ in range(n_layers):
+        per.append((torch.randn(q.shape, generator=g, device=q.device),
+                    torch.randint(0, 256, kc.shape, generator=g, device=kc.device,
+                                  dtype=torch.uint8),
+                    torch.randint(0, 256, vc.shape, generator=g, device=vc.device,
+                                  dtype=torch.uint8),
+                    cb * 1.0, kw.clone() if kw is not None else None,
+                    vw.clone() if vw is not None else None))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for (ql, kl, vl, cbl, kwl, vwl) in per:
+            kvq.attend_decode(ql, kl, vl, cbl[0], cbl[1], kwl, vwl, out=out, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for (ql, kl, vl, cbl, kwl, vwl) in per:
+            kvq.attend_decode(ql, kl, vl, cbl[0], cbl[1], kwl, vwl, out=out, workspace=ws)
+    ts = []
+    for i in range(reps + 3):
+        flush(i)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        if i >= 3:
+            ts.append(e0.elapsed_time(e1))
+    del graph, per
+    t = float(np.median(ts)) * 1e-3 / n_layers
+    return {"layers": n_layers, "us_per_layer": round(t * 1e6, 2),
+            "gbs": round(eff_b / t / 1e9, 1),
+            "note": "decode of one token over n layers of the workload's shape (random codes, "
+                    "layers of their own), one HIP graph, caches evicted before the token"}
 
 
 def rotate_calls(torch, kvq, x, w, dev, flush, reps=20):
