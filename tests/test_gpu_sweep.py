@@ -1,0 +1,110 @@
+"""Seeded sweep of decode and reconstruction shapes against the float64 oracle,
+through the C ABI: batch, KV heads, GQA ratio, head size, groups, stages,
+codebook size, coded and window lengths drawn at random (small enough for the
+oracle), so the plan's choices (heads per block, head splits, chunking, window
+slices or window blocks, LUT built per block or in its own pass) and the
+kernels' ragged edges meet many combinations.  Bars as elsewhere: attention
+within 2e-3 max-abs and 1e-3 relative L2; rotated reconstruction bit-exact,
+unrotated within 1e-6 * |x_hat|.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import compressed_attention_fwht_amd as kvq
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    torch.cuda.set_device(0)
+    yield
+    torch.cuda.synchronize()
+
+
+def cuda(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _shape(rng):
+    # redraw until one query head's tables fit the chunk kernel's LDS (the
+    # library reports larger ones as unsupported)
+    while True:
+        D = int(rng.choice([64, 128, 256]))
+        dsub = int(rng.choice([d for d in (4, 8, 16, 32) if D // d <= 64]))
+        G = D // dsub
+        S = int(rng.integers(1, 5))
+        C = int(rng.choice([16, 100, 256]))
+        if S * G * (C + 4) * 4 + 8 * D * 4 <= 140 * 1024:
+            break
+    B = int(rng.integers(1, 4))
+    Hkv = int(rng.choice([1, 2, 4]))
+    R = int(rng.choice([1, 2, 3, 4, 5, 7, 8]))
+    Tc = int(rng.choice([0, int(rng.integers(1, 300)), int(rng.integers(300, 5000))]))
+    W = int(rng.choice([0, int(rng.integers(1, 80)), int(rng.integers(80, 300))]))
+    if Tc + W == 0:
+        Tc = 17
+    return dict(D=D, dsub=dsub, G=G, S=S, C=C, B=B, Hkv=Hkv, R=R, Tc=Tc, W=W)
+
+
+CASES = list(range(40))
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_decode_sweep(case):
+    rng = np.random.default_rng(1000 + case)
+    p = _shape(rng)
+    D, G, S, C, B, Hkv, R, Tc, W = (p[k] for k in ("D", "G", "S", "C", "B", "Hkv", "R", "Tc", "W"))
+    dsub = D // G
+    say(f"decode sweep case {case}: {p}")
+    Hq = Hkv * R
+    q = rng.standard_normal((B, Hq, D)).astype(np.float32)
+    kcb = (rng.standard_normal((S, G, C, dsub)) / np.sqrt(dsub)
+           * (0.5 ** np.arange(S))[:, None, None, None]).astype(np.float32)
+    vcb = (rng.standard_normal((S, G, C, dsub)) / np.sqrt(dsub)
+           * (0.5 ** np.arange(S))[:, None, None, None]).astype(np.float32)
+    kc = rng.integers(0, C, size=(B, Hkv, Tc, S, G), dtype=np.uint8)
+    vc = rng.integers(0, C, size=(B, Hkv, Tc, S, G), dtype=np.uint8)
+    kw = rng.standard_normal((B, Hkv, W, D)).astype(np.float16) if W else None
+    vw = rng.standard_normal((B, Hkv, W, D)).astype(np.float16) if W else None
+    got = kvq.attend_decode(cuda(q), cuda(kc), cuda(vc), cuda(kcb), cuda(vcb),
+                            None if kw is None else cuda(kw),
+                            None if vw is None else cuda(vw)).cpu().numpy()
+    ref = oracle.attend(q, kc, vc, kcb, vcb, kw, vw)
+    res = oracle.check_attn(got, ref)
+    say("   ", {k: res[k] for k in ("ok", "max_abs", "rel_l2")})
+    assert res["ok"], res
+
+
+@pytest.mark.parametrize("case", list(range(20)))
+def test_reconstruct_sweep(case):
+    rng = np.random.default_rng(2000 + case)
+    D = int(rng.choice([64, 128, 256]))
+    dsub = int(rng.choice([8, 16, 32]))
+    G = D // dsub
+    S = int(rng.integers(1, 6))
+    C = int(rng.choice([16, 100, 256]))
+    nb = int(rng.integers(1, 4))
+    n = int(rng.choice([1, int(rng.integers(2, 200)), int(rng.integers(200, 3000))]))
+    say(f"reconstruct sweep case {case}: D {D} G {G} S {S} C {C} books {nb} n {n}")
+    cb = rng.standard_normal((nb, S, G, C, dsub)).astype(np.float32)
+    codes = rng.integers(0, 256, size=(nb, n, S, G), dtype=np.uint8)
+    clamped = np.minimum(codes, C - 1)
+    got = kvq.decode_reconstruct(cuda(codes), cuda(cb)).cpu().numpy()
+    got_u = kvq.decode_reconstruct(cuda(codes), cuda(cb), unrotate=True).cpu().numpy()
+    for b in range(nb):
+        ref = oracle.reconstruct_rot(clamped[b], cb[b])
+        assert np.array_equal(got[b], ref.astype(np.float32))
+        ref_u = oracle.reconstruct(clamped[b], cb[b])
+        nrm = np.linalg.norm(ref_u, axis=1, keepdims=True)
+        assert np.max(np.abs(got_u[b] - ref_u) / nrm) <= 1e-6
