@@ -108,3 +108,39 @@ def test_reconstruct_sweep(case):
         ref_u = oracle.reconstruct(clamped[b], cb[b])
         nrm = np.linalg.norm(ref_u, axis=1, keepdims=True)
         assert np.max(np.abs(got_u[b] - ref_u) / nrm) <= 1e-6
+
+
+@pytest.mark.parametrize("case", list(range(24)))
+def test_encode_sweep(case):
+    """Encode shapes: every other case is an MFMA-eligible one (D = 128,
+    dsub = 8, C = 256, 2-byte input; 1-4 stages, small batches that split
+    the groups over blocks), the rest random for the generic kernel (D, dsub,
+    C, stages, dtype, rotation done by the caller or not).  Every code follows
+    the oracle's rule (exact, or within the 1e-4 near-tie band)."""
+    rng = np.random.default_rng(3000 + case)
+    mfma = case % 2 == 0
+    if mfma:
+        D, dsub, C = 128, 8, 256
+        dt = [torch.bfloat16, torch.float16][int(rng.integers(0, 2))]
+    else:
+        D = int(rng.choice([64, 128, 256]))
+        dsub = int(rng.choice([d for d in (8, 16, 32, 64, 128) if d <= D]))
+        C = int(rng.choice([16, 100, 256]))
+        dt = [torch.float32, torch.bfloat16, torch.float16][int(rng.integers(0, 3))]
+    G = D // dsub
+    S = int(rng.integers(1, 5))
+    nb = int(rng.integers(1, 3))
+    n = int(rng.choice([1, int(rng.integers(2, 300)), int(rng.integers(300, 3000))]))
+    pre = bool(rng.integers(0, 2)) and not mfma
+    say(f"encode sweep case {case}: D {D} dsub {dsub} C {C} S {S} books {nb} n {n} {dt} "
+        f"pre_rotated={pre}")
+    cb = (rng.standard_normal((nb, S, G, C, dsub)) / np.sqrt(dsub)
+          * (0.5 ** np.arange(S))[None, :, None, None, None]).astype(np.float32)
+    x = torch.from_numpy(rng.standard_normal((nb, 1, n, D)).astype(np.float32)).to(dt).cuda()
+    xf = x.double().cpu().numpy()
+    codes = kvq.encode(x, cuda(cb), pre_rotated=pre).cpu().numpy()
+    assert codes.shape == (nb, 1, n, S, G)
+    for b in range(nb):
+        res = oracle.check_codes(xf[b, 0], cb[b], codes[b, 0], rotate=not pre)
+        assert res["hard"] == 0, (case, b, {k: res[k] for k in ("total", "exact", "near_tie",
+                                                                  "hard")})
