@@ -144,3 +144,81 @@ def test_encode_sweep(case):
         res = oracle.check_codes(xf[b, 0], cb[b], codes[b, 0], rotate=not pre)
         assert res["hard"] == 0, (case, b, {k: res[k] for k in ("total", "exact", "near_tie",
                                                                   "hard")})
+
+
+@pytest.mark.parametrize("case", list(range(16)))
+def test_scalar_sweep(case):
+    """Scalar variant shapes: D 64-256, b = 1, 2, 4, 1-3 books, ragged row
+    counts, f32/bf16/f16 input; encode under the threshold rule and the
+    reconstruction bit-exact (rotated) / within 1e-6 * |x_hat| (unrotated)."""
+    rng = np.random.default_rng(4000 + case)
+    D = int(rng.choice([64, 128, 256]))
+    bits = int(rng.choice([1, 2, 4]))
+    nb = int(rng.integers(1, 4))
+    n = int(rng.choice([1, int(rng.integers(2, 300)), int(rng.integers(300, 3000))]))
+    dt = [torch.float32, torch.bfloat16, torch.float16][int(rng.integers(0, 3))]
+    say(f"scalar sweep case {case}: D {D} bits {bits} books {nb} n {n} {dt}")
+    g = oracle.lloyd_max_levels("gaussian", bits)
+    lap = oracle.lloyd_max_levels("laplacian", bits)
+    dg = oracle.lloyd_max_distortion("gaussian", g)
+    sd = rng.uniform(0.5, 2.0, size=nb)
+    lv = np.stack([[g * s, lap * s * np.sqrt(dg)] for s in sd]).astype(np.float32)
+    x = torch.from_numpy((rng.standard_normal((nb, 1, n, D)) * sd[:, None, None, None])
+                         .astype(np.float32)).to(dt).cuda()
+    codes = kvq.scalar_encode(x, cuda(lv), bits).cpu().numpy()
+    nbytes = D * bits // 8
+    assert codes.shape == (nb, 1, n, 2, nbytes)
+    xf = x.double().cpu().numpy()
+    rot = kvq.scalar_decode_reconstruct(cuda(codes), cuda(lv), bits).cpu().numpy()
+    unr = kvq.scalar_decode_reconstruct(cuda(codes), cuda(lv), bits, unrotate=True).cpu().numpy()
+    for b in range(nb):
+        z = oracle.unpack_bits(codes[b, 0], bits)
+        y = oracle.fwht(xf[b, 0])
+        res = oracle.check_scalar_codes(y, lv[b, 0], lv[b, 1], z[:, 0], z[:, 1])
+        assert res["hard"] == 0, (case, b, res)
+        ref = oracle.scalar_reconstruct(z[:, 0], z[:, 1], lv[b, 0], lv[b, 1], unrotate=False)
+        assert np.array_equal(rot[b, 0], ref.astype(np.float32))
+        ref_u = oracle.fwht(ref)
+        nrm = np.linalg.norm(ref, axis=1, keepdims=True)
+        assert np.all(np.abs(unr[b, 0] - ref_u) <= 1e-6 * nrm)
+
+
+@pytest.mark.parametrize("case", list(range(12)))
+def test_smoothed_decode_sweep(case):
+    """Dual transform on random shapes: factors from the GPU calibration equal
+    the oracle's, the keys' codes follow the code rule on the smoothed, rotated
+    keys, and decode with the factors folded into the query matches the
+    oracle's attention over the smoothed reconstruction."""
+    rng = np.random.default_rng(5000 + case)
+    D = 128
+    G, dsub, S, C = 16, 8, int(rng.integers(1, 3)), 256
+    B = int(rng.integers(1, 3))
+    Hkv = int(rng.choice([1, 2, 4]))
+    R = int(rng.choice([1, 3, 4]))
+    Tc = int(rng.integers(1, 1500))
+    W = int(rng.choice([0, int(rng.integers(1, 100))]))
+    say(f"smoothed decode sweep case {case}: S {S} B {B} Hkv {Hkv} R {R} Tc {Tc} W {W}")
+    scale_ch = np.exp(rng.uniform(np.log(0.3), np.log(8.0), size=(B * Hkv, 1, D)))
+    k = (rng.standard_normal((B * Hkv, Tc, D)) * scale_ch).astype(np.float32)
+    kt = torch.from_numpy(k).cuda()[None]                       # [1][B*Hkv][Tc][D]
+    lam = kvq.smooth_calibrate(kt, B * Hkv).cpu().numpy()[0]    # one row per (sequence, KV head)
+    ref_lam = oracle.smooth_factors(k.astype(np.float64), B * Hkv)
+    assert np.array_equal(lam, ref_lam.astype(np.float32))
+    cb = (rng.standard_normal((2, S, G, C, dsub)) / np.sqrt(dsub) * 0.5
+          * (0.5 ** np.arange(S))[None, :, None, None, None]).astype(np.float32)
+    kc = kvq.encode(kt, cuda(cb[:1]), smooth=cuda(lam[None])).cpu().numpy()[0]
+    rows = oracle.smooth_rows(lam.astype(np.float64), np.arange(B * Hkv))
+    ys = oracle.fwht(oracle.smooth_keys(k.astype(np.float64), rows[:, None, :]).reshape(-1, D))
+    res = oracle.check_codes(ys, cb[0], kc.reshape(-1, S, G), rotate=False)
+    assert res["hard"] == 0, res
+    vc = rng.integers(0, C, size=(B, Hkv, Tc, S, G), dtype=np.uint8)
+    kcs = kc.reshape(B, Hkv, Tc, S, G)
+    q = rng.standard_normal((B, Hkv * R, D)).astype(np.float32)
+    kw = rng.standard_normal((B, Hkv, W, D)).astype(np.float16) if W else None
+    vw = rng.standard_normal((B, Hkv, W, D)).astype(np.float16) if W else None
+    got = kvq.attend_decode(cuda(q), cuda(kcs), cuda(vc), cuda(cb[0]), cuda(cb[1]),
+                            None if kw is None else cuda(kw), None if vw is None else cuda(vw),
+                            k_smooth=cuda(lam)).cpu().numpy()
+    ref = oracle.attend(q, kcs, vc, cb[0], cb[1], kw, vw, k_smooth=lam.astype(np.float64))
+    r = oracle.check_attn(got, ref)
+    assert r["ok"], r
