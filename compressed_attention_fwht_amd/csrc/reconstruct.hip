@@ -18,10 +18,11 @@
 // permuting the index bits of rows and columns alike, so the butterfly over
 // (lane, element) computes the same transform.
 //
-// Two variants.  With 1, 2 or 4 stages whose per-stage codebooks fit in LDS
-// (G*C*dsub*4 bytes up to RC_LDS_MAX), each block copies its book's stage-0
-// codebooks into LDS once and codes a range of that book's vectors: the
-// stage-0 gathers are LDS reads, later stages' go through the caches.
+// Two variants.  With 1, 2 or 4 stages (4 only below D = 256) whose
+// per-stage codebooks fit in LDS (G*C*dsub*4 bytes up to RC_LDS_MAX), each
+// block copies its book's stage-0 codebooks into LDS once (and its code rows
+// too, when they fit beside them) and codes a range of that book's vectors:
+// the stage-0 gathers are LDS reads, later stages' go through the caches.
 // Otherwise every gather goes through the caches (a grid-stride loop over
 // all vectors).
 #include "kvq_internal.h"
@@ -32,27 +33,14 @@ namespace kvq {
 constexpr int RC_THREADS = 512;              // cache variant
 constexpr int RC_LDS_THREADS = 1024;         // LDS variant: one block per CU at 128 KiB
 constexpr int RC_UNR = 2;                    // vectors per lane per iteration
-constexpr size_t RC_LDS_MAX = 128 * 1024;
+constexpr size_t RC_LDS_MAX = 128 * 1024;    // stage-0 codebooks in LDS, at most
+constexpr size_t RC_LDS_BLOCK = 160 * 1024;  // LDS of one CU
 
 // Code bytes of RC_UNR vectors for a lane: stages s < SS, groups ga and gb.
 template <int SS>
 struct RcCodes {
   int za[RC_UNR][SS], zb[RC_UNR][SS];
 };
-
-template <int SS>
-__device__ __forceinline__ void rc_load_codes(RcCodes<SS>& k, const uint8_t* __restrict__ codes,
-                                              const int64_t (&vec)[RC_UNR], int G, int ga,
-                                              int gb) {
-#pragma unroll
-  for (int u = 0; u < RC_UNR; ++u)
-#pragma unroll
-    for (int s = 0; s < SS; ++s) {
-      const uint8_t* row = codes + vec[u] * (SS * G) + s * G;
-      k.za[u][s] = row[ga];
-      k.zb[u][s] = row[gb];
-    }
-}
 
 // Finish RC_UNR vectors of a lane (their float32 sums): optional unrotation
 // and smoothing, the two 16-byte stores.
@@ -95,9 +83,12 @@ __device__ __forceinline__ void rc_finish(float (&sum)[RC_UNR][8], float* __rest
 // LDS variant (SS = S stages: 1, 2 or 4; stage 0 in LDS): grid (blocks per
 // book, n_books);
 // block (x, book) copies the book's stage-0 codebooks into LDS and codes its vectors
-// [x*per, (x+1)*per).  The code bytes of a wave's next RC_UNR x ROWS vectors
-// are loaded while the current ones are summed and stored.
-template <int D, int SS>
+// [x*per, (x+1)*per).  PRE: the block's code rows are copied into LDS beside
+// the codebooks up front, so the stream that follows only writes to HBM
+// (reads between the writes cost measurable bandwidth); otherwise the code
+// bytes of a wave's next RC_UNR x ROWS vectors are loaded while the current
+// ones are summed and stored.
+template <int D, int SS, bool PRE>
 __global__ __launch_bounds__(RC_LDS_THREADS) void reconstruct_lds_kernel(
     const uint8_t* __restrict__ codes, const float* __restrict__ cb, float* __restrict__ out,
     int64_t n_per_book, int64_t per_block, int G, int C, int dsub, int unrotate,
@@ -127,24 +118,58 @@ __global__ __launch_bounds__(RC_LDS_THREADS) void reconstruct_lds_kernel(
       vec[u] = first + (live[u] ? v : v1 - 1);
     }
   };
-  // the first codes are in flight across the codebook copy
+  // PRE: the code rows sit in LDS after the codebooks at the same offset
+  // modulo 16 as in global memory (whole 16-byte pieces copied as such, the
+  // partial first and last pieces byte by byte)
+  const int SG = SS * G;
+  uint8_t* lcodes = smem + stage_stride * 4;
+  const int64_t a0 = (first + v0) * SG;
+  const int lo = (int)(a0 & 15);
+  auto code_row = [&](int64_t v) -> const uint8_t* {    // v: global vector index
+    if constexpr (PRE) return lcodes + lo + (v - first - v0) * SG;
+    else return codes + v * SG;
+  };
+  auto load_codes_of = [&](RcCodes<SS>& k, const int64_t (&vv)[RC_UNR]) {
+#pragma unroll
+    for (int u = 0; u < RC_UNR; ++u)
+#pragma unroll
+      for (int s = 0; s < SS; ++s) {
+        const uint8_t* row = code_row(vv[u]) + s * G;
+        k.za[u][s] = row[ga];
+        k.zb[u][s] = row[gb];
+      }
+  };
   int64_t wbase = v0 + wave * ROWS;
   int64_t vec[RC_UNR];
   bool live[RC_UNR];
   rows_of(wbase, vec, live);
   RcCodes<SS> cur;
-  rc_load_codes<SS>(cur, codes, vec, G, ga, gb);
+  if constexpr (!PRE) load_codes_of(cur, vec);          // in flight across the codebook copy
   const float4* src = reinterpret_cast<const float4*>(cbg);
   for (int64_t i = threadIdx.x; i < stage_stride / 4; i += RC_LDS_THREADS)
     reinterpret_cast<float4*>(smem)[i] = src[i];
+  if constexpr (PRE) {
+    const int64_t nbytes = (v1 - v0) * SG;
+    const int64_t nchunk = (lo + nbytes + 15) / 16;
+    for (int64_t i = threadIdx.x; i < nchunk; i += RC_LDS_THREADS) {
+      const int64_t g0 = a0 - lo + 16 * i;
+      if (g0 >= a0 && g0 + 16 <= a0 + nbytes) {
+        reinterpret_cast<uint4*>(lcodes)[i] = *reinterpret_cast<const uint4*>(codes + g0);
+      } else {
+        for (int b = 0; b < 16; ++b)
+          if (g0 + b >= a0 && g0 + b < a0 + nbytes) lcodes[16 * i + b] = codes[g0 + b];
+      }
+    }
+  }
   __syncthreads();
+  if constexpr (PRE) load_codes_of(cur, vec);
   // the loop bound is wave-uniform: every lane joins the butterfly
   for (; wbase < v1; wbase += STEP * RC_UNR) {
     int64_t nvec[RC_UNR];
     bool nlive[RC_UNR];
     rows_of(wbase + STEP * RC_UNR, nvec, nlive);
     RcCodes<SS> nxt;
-    rc_load_codes<SS>(nxt, codes, nvec, G, ga, gb);
+    load_codes_of(nxt, nvec);
     // one or two stages: the float32 sum is already the correctly rounded
     // one (a single entry, or one rounding of the sum of two floats); four:
     // float64, rounded once
@@ -253,27 +278,35 @@ hipError_t launch_reconstruct(const uint8_t* codes, const float* cb, float* out,
   const int dsub = D / G;
   const size_t cbytes = (size_t)G * C * dsub * sizeof(float);
   const int64_t vec_per_iter = (int64_t)(RC_THREADS / 64) * (64 / (D / 8)) * RC_UNR;
-  if (cbytes <= RC_LDS_MAX && (S == 1 || S == 2 || S == 4)) {
+  if (cbytes <= RC_LDS_MAX && (S == 1 || S == 2 || (S == 4 && D < 256))) {
     // blocks per CU that fit the LDS, about 256 CUs' worth of blocks over the books
-    const int per_cu = cbytes * 2 <= 160 * 1024 ? 2 : 1;
+    const int per_cu = cbytes * 2 <= RC_LDS_BLOCK ? 2 : 1;
     const int64_t lvec = (int64_t)(RC_LDS_THREADS / 64) * (64 / (D / 8)) * RC_UNR;
     int64_t nx = (256 * per_cu + n_books - 1) / n_books;
     int64_t per = (n_per_book + nx - 1) / nx;
     per = (per + lvec - 1) / lvec * lvec;
     nx = (n_per_book + per - 1) / per;
+    // the blocks' code rows go to LDS too when they fit beside the codebooks
+    // (a 16-byte slack when a block's rows may start off a 16-byte boundary)
+    const int64_t SG = (int64_t)S * G;
+    const size_t slack = (n_per_book * SG) % 16 == 0 && (per * SG) % 16 == 0 ? 0 : 16;
+    const size_t with_codes = cbytes + (size_t)per * SG + slack;
+    const bool pre = with_codes <= RC_LDS_BLOCK / per_cu;
+    const size_t ldsb = pre ? with_codes : cbytes;
 #define KVQ_RL(DD, SSV)                                                                       \
     if (D == DD && S == SSV) {                                                               \
-      auto kern = reconstruct_lds_kernel<DD, SSV>;                                           \
+      auto kern = pre ? reconstruct_lds_kernel<DD, SSV, true>                                \
+                      : reconstruct_lds_kernel<DD, SSV, false>;                              \
       hipError_t e = hipFuncSetAttribute((const void*)kern,                                  \
                                          hipFuncAttributeMaxDynamicSharedMemorySize,         \
-                                         (int)cbytes);                                       \
+                                         (int)ldsb);                                         \
       if (e != hipSuccess) return e;                                                         \
-      kern<<<dim3((unsigned)nx, (unsigned)n_books), RC_LDS_THREADS, cbytes, s>>>(            \
+      kern<<<dim3((unsigned)nx, (unsigned)n_books), RC_LDS_THREADS, ldsb, s>>>(              \
           codes, cb, out, n_per_book, per, G, C, dsub, unrotate, sm.f, sm.n_scale, n_rows);  \
       return hipGetLastError();                                                              \
     }
     KVQ_RL(64, 1) KVQ_RL(128, 1) KVQ_RL(256, 1) KVQ_RL(64, 2) KVQ_RL(128, 2) KVQ_RL(256, 2)
-    KVQ_RL(64, 4) KVQ_RL(128, 4) KVQ_RL(256, 4)
+    KVQ_RL(64, 4) KVQ_RL(128, 4)                       // D = 256 with 4 stages: cache kernel
 #undef KVQ_RL
   }
   int64_t blocks = (n + vec_per_iter - 1) / vec_per_iter;
