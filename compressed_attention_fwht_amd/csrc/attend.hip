@@ -188,9 +188,9 @@ __global__ __launch_bounds__(256) void attn_lut_kernel(const float* __restrict__
 // ------------------------------------------------------------- attn_chunk
 // grid (n_chunks + n_wblocks, Hkv * n_hsplit, B), block 512.  A short
 // window rides on the chunk blocks (a slice each, win_slice_*); a long one gets
-// blocks x >= n_chunks of its own (window_partial).  LDS: one table region of
-// [S*G][C][RP] 4-byte entries that holds the LUT (floats) during pass 1 and
-// the weight histogram (integers) during pass 2, plus the contraction's
+// blocks x >= n_chunks of its own (window_partial).  LDS: one table region
+// that holds the LUT ([S*G][C][RP] floats) during pass 1 and the weight
+// histogram (integers, layout below) during pass 2, plus the contraction's
 // partial sums.  Each thread owns up to CH_TPT tokens of the chunk
 // (token = t0 + tid + 512*k) and keeps their RP scores in registers across
 // the two passes.
