@@ -13,6 +13,7 @@ Calls (same names as the C ABI):
   encode(x, codebooks, n_rows=...)           codes uint8 [books][seq][rows][S][G]
   decode_reconstruct(codes, codebooks)       sum of codewords     -> f32 [..., D]
   attend_decode(q, k_codes, v_codes, k_cb, v_cb, k_win, v_win) -> f32 [B][Hq][D]
+  cache_bytes(B, Hq, Hkv, D, Tc, W, S, G, C) bytes a layer's compressed cache holds
   window_append / window_flush               streaming fp16 window -> codes
   smooth_calibrate(k, n_scale)               dual-transform factors f32 [books][n_scale][D]
   codebook_fit(x, init, n_iter)              K-means codebooks [S][G][C][dsub] f32 on a sample
@@ -27,7 +28,8 @@ import ctypes
 import os
 
 __all__ = ["KvqError", "LIB_PATH", "lib", "rotate", "encode", "encode_workspace_size",
-           "decode_reconstruct", "attend_decode", "attend_workspace_size", "window_append",
+           "decode_reconstruct", "attend_decode", "attend_workspace_size", "cache_bytes",
+           "window_append",
            "window_flush", "window_flush_workspace_size", "smooth_calibrate", "codebook_fit",
            "codebook_fit_workspace_size", "lloyd_max", "scalar_encode",
            "scalar_decode_reconstruct", "scalar_product_codebook", "EXPORTS",
@@ -44,7 +46,8 @@ KVQ_CODEBOOKS_PACKED = 0x8
 F32, BF16, F16 = 0, 1, 2
 
 EXPORTS = ("kvq_rotate", "kvq_encode_workspace_size", "kvq_encode", "kvq_decode_reconstruct",
-           "kvq_attend_workspace_size", "kvq_attend_decode", "kvq_window_append",
+           "kvq_attend_workspace_size", "kvq_attend_decode", "kvq_cache_bytes",
+           "kvq_window_append",
            "kvq_window_flush_workspace_size", "kvq_window_flush", "kvq_smooth_calibrate",
            "kvq_encode_smooth", "kvq_decode_reconstruct_smooth", "kvq_attend_decode_smooth",
            "kvq_window_flush_smooth", "kvq_codebook_fit_workspace_size", "kvq_codebook_fit",
@@ -80,6 +83,8 @@ def _load():
     L.kvq_decode_reconstruct.argtypes = [P, ctypes.POINTER(VqDesc), I64, I64, P, P, U32, P]
     L.kvq_attend_workspace_size.argtypes = [ctypes.POINTER(AttnDesc), ctypes.POINTER(SZ)]
     L.kvq_attend_decode.argtypes = [ctypes.POINTER(AttnDesc), P, P, P, P, P, P, P, P, P, SZ, P]
+    U64P = ctypes.POINTER(ctypes.c_uint64)
+    L.kvq_cache_bytes.argtypes = [ctypes.POINTER(AttnDesc), U64P, U64P, U64P, U64P]
     L.kvq_window_append.argtypes = [I32, I32, I32, I32, I32, P, P, P, P, P]
     L.kvq_window_flush_workspace_size.argtypes = [ctypes.POINTER(VqDesc), ctypes.POINTER(SZ)]
     L.kvq_window_flush.argtypes = [ctypes.POINTER(VqDesc), I32, I32, I32, I32, I32, P, P, I32, I32,
@@ -413,6 +418,18 @@ def attend_workspace_size(B, Hq, Hkv, D, Tc, W, S, G, C, scale=None) -> int:
     _check(_lib().kvq_attend_workspace_size(ctypes.byref(a), ctypes.byref(sz)),
            "kvq_attend_workspace_size")
     return sz.value
+
+
+def cache_bytes(B, Hq, Hkv, D, Tc, W, S, G, C) -> dict:
+    """Bytes one layer's compressed cache holds (K and V): ``code``, ``window``
+    (fp16), ``codebooks`` (float32) and ``dense`` (the same tokens as a dense
+    fp16 cache), from kvq_cache_bytes (host arithmetic, no GPU)."""
+    a = _attn_desc(B, Hq, Hkv, D, Tc, W, S, G, C, None)
+    v = [ctypes.c_uint64(0) for _ in range(4)]
+    _check(_lib().kvq_cache_bytes(ctypes.byref(a), *[ctypes.byref(x) for x in v]),
+           "kvq_cache_bytes")
+    return {"code": v[0].value, "window": v[1].value, "codebooks": v[2].value,
+            "dense": v[3].value}
 
 
 def attend_decode(q, k_codes, v_codes, k_cb, v_cb, k_win=None, v_win=None, *, scale=None,

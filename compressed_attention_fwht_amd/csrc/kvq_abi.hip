@@ -440,6 +440,30 @@ kvq_status kvq_window_flush_smooth(const kvq_vq_desc* vq, int32_t batch, int32_t
                              workspace, ws_bytes, stream);
 }
 
+kvq_status kvq_cache_bytes(const kvq_attn_desc* a, uint64_t* code_bytes, uint64_t* window_bytes,
+                           uint64_t* codebook_bytes, uint64_t* dense_bytes) {
+  if (!a || !code_bytes || !window_bytes || !codebook_bytes || !dense_bytes) return KVQ_ERR_NULL;
+  const kvq_status st = check_vq(&a->vq, 4);
+  if (st != KVQ_OK) return st;
+  if (a->batch < 1 || a->n_q_heads < 1 || a->n_kv_heads < 1) return KVQ_ERR_SHAPE;
+  if (a->n_q_heads % a->n_kv_heads != 0) return KVQ_ERR_SHAPE;
+  if (a->n_code_tokens < 0 || a->n_window < 0) return KVQ_ERR_SHAPE;
+  const kvq_vq_desc& v = a->vq;
+  using u128 = unsigned __int128;
+  const u128 heads = (u128)2 * (u128)a->batch * (u128)a->n_kv_heads;   // K and V rows
+  const u128 code = heads * (u128)a->n_code_tokens * (u128)(v.n_stages * v.n_groups);
+  const u128 win = heads * (u128)a->n_window * (u128)v.head_dim * 2;
+  const u128 books = (u128)2 * v.n_stages * v.n_groups * v.n_codewords * (v.head_dim / v.n_groups) * 4;
+  const u128 dense = heads * ((u128)a->n_code_tokens + (u128)a->n_window) * (u128)v.head_dim * 2;
+  const u128 lim = (u128)1 << 63;
+  if (code > lim || win > lim || dense > lim) return KVQ_ERR_SHAPE;
+  *code_bytes = (uint64_t)code;
+  *window_bytes = (uint64_t)win;
+  *codebook_bytes = (uint64_t)books;
+  *dense_bytes = (uint64_t)dense;
+  return KVQ_OK;
+}
+
 kvq_status kvq_attend_workspace_size(const kvq_attn_desc* a, size_t* bytes) {
   if (!bytes) return KVQ_ERR_NULL;
   kvq::AttnPlan plan;

@@ -174,6 +174,24 @@ KVQ_API kvq_status kvq_attend_decode(const kvq_attn_desc* a, const float* q,
                              float* out, void* workspace, size_t ws_bytes,
                              hipStream_t stream);
 
+/* Bytes one layer's compressed cache of shape *a holds ("VeloxQuant-MLX
+ * 0.5.1", Quick start: the cache reports its memory use; its results count
+ * compression as code bytes against fp16 K and V).  K and V together, over
+ * the n_code_tokens coded and n_window window tokens of every (sequence, KV
+ * head):
+ *   code_bytes     = 2 * B * Hkv * n_code_tokens * S * G   (one byte per code)
+ *   window_bytes   = 2 * B * Hkv * n_window * D * 2        (fp16 rows)
+ *   codebook_bytes = 2 * S * G * C * dsub * 4              (float32 K and V sets)
+ *   dense_bytes    = 2 * B * Hkv * (n_code_tokens + n_window) * D * 2
+ *                    (the same tokens held as a dense fp16 cache).
+ * Rows allocated beyond the counts (code_stride, window_stride) are not
+ * counted.  Host arithmetic only: no HIP call.  Every output pointer is
+ * required.  Shape checks are those of kvq_attend_workspace_size, except that
+ * both counts may be 0; a total past 2^63 is KVQ_ERR_SHAPE. */
+KVQ_API kvq_status kvq_cache_bytes(const kvq_attn_desc* a, uint64_t* code_bytes,
+                                   uint64_t* window_bytes, uint64_t* codebook_bytes,
+                                   uint64_t* dense_bytes);
+
 /* ---------------------------------------------------------------------------
  * Streaming window ("VeloxQuant-MLX 0.5.1", Quick start: a cache grown one
  * token at a time by append; "ZeroKV-Neo 4.0.0", profiling output: periodic

@@ -155,6 +155,48 @@ def test_attend_workspace_sizes():
     assert sz_w == 2 * 4 * 1 * 68 * 4                                  # no LUT, one window block
 
 
+def test_cache_bytes_match_the_closed_form_and_the_workload_tables():
+    """kvq_cache_bytes: codes = tokens x the oracle's code bytes per vector
+    (pinned there to the pages' 16x / 8x ratios), the window and codebooks in
+    fp16 / float32, and the code and window byte counts of the decode workloads'
+    table (Llama-, Qwen-shaped and long-context caches)."""
+    import oracle
+    for (B, Hq, Hkv, T, W, S, code, win) in [
+            (1, 32, 8, 32768, 128, 1, 8_355_840, 524_288),
+            (16, 28, 4, 8192, 64, 2, 33_292_288, 2_097_152),
+            (1, 32, 8, 131072, 256, 4, 133_955_584, 1_048_576)]:
+        r = kvq.cache_bytes(B, Hq, Hkv, 128, T - W, W, S, 16, 256)
+        assert r["code"] == code and r["window"] == win
+        assert r["code"] == 2 * B * Hkv * (T - W) * oracle.code_bytes_per_vector(S, 16)
+        assert r["codebooks"] == 2 * S * 16 * 256 * 8 * 4
+        assert r["dense"] == 2 * B * Hkv * T * 128 * 2
+        # codes alone against the same tokens in fp16: the oracle's ratio
+        assert r["dense"] * (T - W) / T / r["code"] == pytest.approx(
+            oracle.compression_ratio_vs_fp16(128, S, 16))
+    tiny = kvq.cache_bytes(1, 1, 1, 64, 1024, 0, 2, 1, 256)
+    assert tiny == {"code": 4096, "window": 0, "codebooks": 2 * 2 * 256 * 64 * 4,
+                    "dense": 2 * 1024 * 64 * 2}
+    assert kvq.cache_bytes(2, 4, 2, 64, 0, 0, 1, 8, 256)["dense"] == 0   # empty cache
+
+
+def test_cache_bytes_argument_errors():
+    u = [ctypes.c_uint64(7) for _ in range(4)]
+    refs = [ctypes.byref(x) for x in u]
+
+    def call(a, *ptrs):
+        return kvq.lib.kvq_cache_bytes(ctypes.byref(a), *(ptrs or refs))
+    assert call(_attn(Hq=30)) == SHAPE
+    assert call(_attn(Tc=-1)) == SHAPE
+    assert call(_attn(B=0)) == SHAPE
+    assert call(_attn(G=3)) == SHAPE
+    assert call(_attn(B=1 << 30, Hkv=1 << 30, Hq=1 << 30, Tc=1 << 30)) == SHAPE   # past 2^63
+    assert call(_attn(), refs[0], None, refs[2], refs[3]) == NULL
+    assert kvq.lib.kvq_cache_bytes(None, *refs) == NULL
+    assert [x.value for x in u] == [7, 7, 7, 7]          # nothing written on error
+    with pytest.raises(kvq.KvqError):
+        kvq.cache_bytes(1, 30, 8, 128, 10, 0, 1, 16, 256)
+
+
 def test_window_append_argument_errors():
     L = kvq.lib
     assert L.kvq_window_append(1, 2, 100, 8, 0, FAKE, FAKE, FAKE, FAKE, None) == SHAPE   # head_dim
