@@ -183,6 +183,10 @@ def main():
     code_b = 2 * B * Hkv * Tc * S * G
     win_b = 2 * B * Hkv * W * D * 2
     lut_b = B * Hq * S * G * C * 4
+    # the layer's cache as the library counts it (kvq_cache_bytes), and its
+    # size against the same tokens held as dense fp16
+    cache = kvq.cache_bytes(B, Hq, Hkv, D, Tc, W, S, G, C)
+    cache["vs_dense_fp16"] = round(cache["dense"] / (cache["code"] + cache["window"]), 2)
     eff_b = code_b + win_b + lut_b
     rec_b = n_vec * (S * G + 4 * D)
 
@@ -272,6 +276,7 @@ def main():
                    "pct_hbm_peak": round(100 * dec_gbs / HBM_PEAK_GBS, 3),
                    "ms": round(att_s * 1e3, 5), "effective_bytes": eff_b,
                    "bytes": {"codes": code_b, "window": win_b, "lut": lut_b},
+                   "cache": cache,
                    "cache_flushed": not args.no_flush,
                    "graph_replay_us": graph_us,
                    "layers_graph": layers},
