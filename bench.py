@@ -665,7 +665,27 @@ def cpu_baseline(w, inp, codes, eff_b, dec_gbs, budget_s=10.0):
                       f"{t_enc:.1f} s. float64 NumPy; elementwise work on one core, matrix "
                       f"products on {blas} BLAS threads",
             "encode_mvec_per_s": round(n_enc / t_enc / 1e6, 6),
-            "gpu_over_cpu_decode": round(dec_gbs / gbs, 1)}
+            "gpu_over_cpu_decode": round(dec_gbs / gbs, 1),
+            "host": host_cpu()}
+
+
+def host_cpu():
+    """The host the oracle ran on: CPU model, logical CPUs, the CPUs this
+    process may run on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = None
+    return {"cpu_model": model, "os_cpu_count": os.cpu_count(), "affinity": affinity}
 
 
 if __name__ == "__main__":
