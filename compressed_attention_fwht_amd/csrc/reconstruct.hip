@@ -18,13 +18,15 @@
 // permuting the index bits of rows and columns alike, so the butterfly over
 // (lane, element) computes the same transform.
 //
-// Two variants.  With 1, 2 or 4 stages (4 only below D = 256) whose
-// per-stage codebooks fit in LDS (G*C*dsub*4 bytes up to RC_LDS_MAX), each
-// block copies its book's stage-0 codebooks into LDS once (and its code rows
-// too, when they fit beside them) and codes a range of that book's vectors:
-// the stage-0 gathers are LDS reads, later stages' go through the caches.
-// Otherwise every gather goes through the caches (a grid-stride loop over
-// all vectors).
+// Three variants.  With 2 stages whose codebooks for half the dims fit in
+// LDS (2*C*D/2*4 bytes up to RC_LDS_MAX), the half-table kernel holds each
+// half's tables in LDS in turn, so every gather is an LDS read.  Otherwise,
+// with 1, 2 or 4 stages (4 only below D = 256) whose per-stage codebooks fit
+// in LDS (G*C*dsub*4 bytes up to RC_LDS_MAX), each block copies its book's
+// stage-0 codebooks into LDS once (and its code rows too, when they fit
+// beside them) and codes a range of that book's vectors: the stage-0 gathers
+// are LDS reads, later stages' go through the caches.  Otherwise every gather
+// goes through the caches (a grid-stride loop over all vectors).
 #include "kvq_internal.h"
 #include <type_traits>
 
@@ -206,6 +208,165 @@ __global__ __launch_bounds__(RC_LDS_THREADS) void reconstruct_lds_kernel(
   }
 }
 
+// Half-table variant (S stages whose tables for half the dims fit in LDS;
+// launched for S = 2, where it is measured faster -- more stages spill
+// registers at 4 vectors per lane): lane c of a row holds dims [4c, 4c+4) of the first half and
+// [D/2 + 4c, D/2 + 4c + 4) of the second, and the groups of each half are
+// contiguous in every stage's codebook.  A batch of RC_HK vectors per lane
+// is coded in two phases: the block stages every stage's codebooks of one
+// half's groups into LDS (S*C*D/2 floats), every lane sums its dims of that
+// half over the stages and keeps the 4 sums per vector in registers; then the
+// other half's tables replace them and each vector is finished (unrotation,
+// smoothing, stores) as soon as its second half is summed.  Consecutive
+// batches take the halves in opposite orders, so a batch after the first
+// loads one table, not two.  The batch's code rows are copied into LDS
+// behind the table first, so every gather, of codes and of entries, is an
+// LDS read.
+// grid (blocks per book, n_books); block (x, book) codes its book's vectors
+// [x*per, (x+1)*per).
+constexpr int RC_HT_THREADS = 1024;
+constexpr int RC_HK = 4;                     // vectors per lane per batch (8 spills)
+
+template <int D, int S>
+__global__ __launch_bounds__(RC_HT_THREADS) void reconstruct_half_kernel(
+    const uint8_t* __restrict__ codes, const float* __restrict__ cb, float* __restrict__ out,
+    int64_t n_per_book, int64_t per_block, int G, int C, int unrotate,
+    const float* __restrict__ smooth, int64_t n_scale, int64_t n_rows) {
+  static_assert(RC_HK % RC_UNR == 0, "vectors are finished RC_UNR at a time");
+  constexpr int L = D / 8;
+  constexpr int RPASS = RC_HT_THREADS / L;              // rows of one pass of the block
+  constexpr int BATCH = RPASS * RC_HK;
+  using Acc = typename std::conditional<(S <= 2), float, double>::type;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  float* tab = reinterpret_cast<float*>(smem);
+  const int lane = threadIdx.x & 63;
+  const int col = lane % L;
+  const int rloc = threadIdx.x / L;                     // row within a pass
+  const int dsub = D / G;
+  const int GH = G / 2;                                 // groups per half
+  const int da = 4 * col, db = D / 2 + 4 * col;
+  const int64_t book = blockIdx.y;
+  const int SG = S * G;
+  const float* cbb = cb + book * (int64_t)S * G * C * dsub;
+  const int64_t v0 = (int64_t)blockIdx.x * per_block;
+  const int64_t v1 = (v0 + per_block) < n_per_book ? (v0 + per_block) : n_per_book;
+  const int64_t first = book * n_per_book;
+  const int64_t half_floats = (int64_t)GH * C * dsub;   // one stage of one half
+  // code rows of the batch, behind the table, at the same offset modulo 16
+  // as in global memory
+  uint8_t* lcodes = smem + (size_t)S * half_floats * 4;
+  int loaded = -1;                                      // half held in LDS (block-uniform)
+  int lo = 0;                                           // offset of the batch's first code byte
+
+  // the code rows of vectors [vb, min(vb + BATCH, v1)) into lcodes + lo
+  // (whole 16-byte pieces as such, the partial first and last bytewise);
+  // block-uniform call, after a barrier that ends every read of the old rows
+  auto load_codes = [&](int64_t vb) {
+    const int64_t a0 = (first + vb) * SG;
+    const int64_t vend = (vb + BATCH) < v1 ? (vb + BATCH) : v1;
+    const int64_t nbytes = (vend - vb) * SG;
+    lo = (int)(a0 & 15);
+    const int64_t nchunk = (lo + nbytes + 15) / 16;
+    for (int64_t i = threadIdx.x; i < nchunk; i += RC_HT_THREADS) {
+      const int64_t g0 = a0 - lo + 16 * i;
+      if (g0 >= a0 && g0 + 16 <= a0 + nbytes) {
+        reinterpret_cast<uint4*>(lcodes)[i] = *reinterpret_cast<const uint4*>(codes + g0);
+      } else {
+        for (int b = 0; b < 16; ++b)
+          if (g0 + b >= a0 && g0 + b < a0 + nbytes) lcodes[16 * i + b] = codes[g0 + b];
+      }
+    }
+  };
+
+  // one half's tables (and the batch's code rows when vb >= 0); block-uniform call
+  auto load_half = [&](int hh, int64_t vb) {
+    __syncthreads();                                    // every read of the old contents is done
+    if (vb >= 0) load_codes(vb);
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      const float4* src = reinterpret_cast<const float4*>(cbb + ((int64_t)s * G + hh * GH) * C * dsub);
+      float4* dst = reinterpret_cast<float4*>(tab + s * half_floats);
+      for (int64_t i = threadIdx.x; i < half_floats / 4; i += RC_HT_THREADS) dst[i] = src[i];
+    }
+    __syncthreads();
+    loaded = hh;
+  };
+  auto row_of = [&](int64_t vb, int k, int64_t& vec, bool& live) {
+    const int64_t v = vb + (int64_t)k * RPASS + rloc;
+    live = v < v1;
+    vec = first + (live ? v : v1 - 1);
+  };
+  // this lane's 4 sums of half hh for vector vec of the batch at vb
+  auto sum_half = [&](int hh, int64_t vb, int64_t vec, float (&r)[4]) {
+    const int dh = hh ? db : da;
+    const int g = dh / dsub, j = dh - g * dsub;
+    const int gl = g - hh * GH;
+    const uint8_t* row = lcodes + lo + (vec - first - vb) * SG + g;
+    int z[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      z[s] = row[s * G];
+      z[s] = z[s] < C ? z[s] : C - 1;
+    }
+    Acc acc[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      const float4 e = *reinterpret_cast<const float4*>(
+          tab + s * half_floats + ((int64_t)gl * C + z[s]) * dsub + j);
+      acc[0] += e.x; acc[1] += e.y; acc[2] += e.z; acc[3] += e.w;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[e] = (float)acc[e];
+  };
+  // one batch: half h0 first, then half 1 - h0 with the finish
+  auto batch = [&](int64_t vb, int h0) {
+    if (loaded != h0) {
+      load_half(h0, vb);
+    } else {
+      __syncthreads();                                  // every read of the old rows is done
+      load_codes(vb);
+      __syncthreads();
+    }
+    float hold[RC_HK][4];
+#pragma unroll
+    for (int k = 0; k < RC_HK; ++k) {
+      int64_t vec;
+      bool live;
+      row_of(vb, k, vec, live);
+      sum_half(h0, vb, vec, hold[k]);
+      // one vector's LDS reads at a time: hoisting them all would spill
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    load_half(1 - h0, -1);
+#pragma unroll
+    for (int k = 0; k < RC_HK; k += RC_UNR) {
+      int64_t vec[RC_UNR];
+      bool live[RC_UNR];
+      float sum[RC_UNR][8];
+#pragma unroll
+      for (int u = 0; u < RC_UNR; ++u) {
+        row_of(vb, k + u, vec[u], live[u]);
+        float r[4];
+        sum_half(1 - h0, vb, vec[u], r);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sum[u][e] = h0 == 0 ? hold[k + u][e] : r[e];
+          sum[u][4 + e] = h0 == 0 ? r[e] : hold[k + u][e];
+        }
+      }
+      rc_finish<D>(sum, out, vec, live, n_per_book, unrotate, smooth, n_scale, n_rows, lane, da,
+                   db);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // the loop bounds are block-uniform: every thread takes part in the table
+  // loads, barriers and butterflies
+  for (int64_t vb = v0; vb < v1; vb += 2 * BATCH) {
+    batch(vb, 0);
+    if (vb + BATCH < v1) batch(vb + BATCH, 1);
+  }
+}
+
 // Cache variant: grid-stride over every vector of every book, any S.
 template <int D>
 __global__ __launch_bounds__(RC_THREADS) void reconstruct_kernel(
@@ -278,7 +439,33 @@ hipError_t launch_reconstruct(const uint8_t* codes, const float* cb, float* out,
   const int dsub = D / G;
   const size_t cbytes = (size_t)G * C * dsub * sizeof(float);
   const int64_t vec_per_iter = (int64_t)(RC_THREADS / 64) * (64 / (D / 8)) * RC_UNR;
-  if (cbytes <= RC_LDS_MAX && (S == 1 || S == 2 || (S == 4 && D < 256))) {
+  // 2 stages whose half-dim tables fit RC_LDS_MAX: the half-table variant
+  // (the LDS variants put the books on grid.y)
+  const size_t hbytes = (size_t)S * C * (D / 2) * sizeof(float);
+  const int64_t hbatch = (int64_t)(RC_HT_THREADS / (D / 8)) * RC_HK;
+  const size_t hlds = hbytes + (size_t)hbatch * S * G + 16;   // table, a batch's code rows
+  if (S == 2 && G % 2 == 0 && hbytes <= RC_LDS_MAX && hlds <= RC_LDS_BLOCK &&
+      n_books <= 65535) {
+    const int64_t batch = hbatch;
+    int64_t nx = (256 + n_books - 1) / n_books;
+    int64_t per = (n_per_book + nx - 1) / nx;
+    per = (per + batch - 1) / batch * batch;
+    nx = (n_per_book + per - 1) / per;
+#define KVQ_RH(DD, SSV)                                                                       \
+    if (D == DD && S == SSV) {                                                                \
+      auto kern = reconstruct_half_kernel<DD, SSV>;                                           \
+      hipError_t e = hipFuncSetAttribute((const void*)kern,                                   \
+                                         hipFuncAttributeMaxDynamicSharedMemorySize,          \
+                                         (int)hlds);                                          \
+      if (e != hipSuccess) return e;                                                          \
+      kern<<<dim3((unsigned)nx, (unsigned)n_books), RC_HT_THREADS, hlds, s>>>(                \
+          codes, cb, out, n_per_book, per, G, C, unrotate, sm.f, sm.n_scale, n_rows);         \
+      return hipGetLastError();                                                               \
+    }
+    KVQ_RH(64, 2) KVQ_RH(128, 2) KVQ_RH(256, 2)
+#undef KVQ_RH
+  }
+  if (cbytes <= RC_LDS_MAX && (S == 1 || S == 2 || (S == 4 && D < 256)) && n_books <= 65535) {
     // blocks per CU that fit the LDS, about 256 CUs' worth of blocks over the books
     const int per_cu = cbytes * 2 <= RC_LDS_BLOCK ? 2 : 1;
     const int64_t lvec = (int64_t)(RC_LDS_THREADS / 64) * (64 / (D / 8)) * RC_UNR;

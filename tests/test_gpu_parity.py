@@ -132,6 +132,32 @@ def test_reconstruct_lds_shapes(D, G, C, n, S):
         assert np.max(np.abs(got_u[b] - ref_u) / nrm) <= 1e-6
 
 
+@pytest.mark.parametrize("G,n", [
+    (16, 520192),               # the Qwen-shaped layer's K (or V) vectors per book
+    (2, 100001),                # 4 code bytes per row: batches start off 16-byte boundaries
+])
+def test_reconstruct_two_stages_many_batches(G, n):
+    """Two-stage books at sizes where every block of the half-table kernel
+    codes several batches (the halves taken in alternating order, the code
+    rows of each batch copied into LDS): rotated output bit-exact everywhere,
+    unrotated within 1e-6 * |x_hat| on every 97th vector."""
+    say(f"reconstruct, two stages: G {G} n {n} x 2 books")
+    D, S, C = 128, 2, 256
+    rng = np.random.default_rng(G + n)
+    cb = rng.standard_normal((2, S, G, C, D // G)).astype(np.float32)
+    codes = rng.integers(0, 256, size=(2, n, S, G), dtype=np.uint8)
+    dc, dcb = cuda(codes), cuda(cb)
+    got = kvq.decode_reconstruct(dc, dcb).cpu().numpy()
+    got_u = kvq.decode_reconstruct(dc, dcb, unrotate=True).cpu().numpy()
+    idx = np.arange(0, n, 97)
+    for b in range(2):
+        ref = oracle.reconstruct_rot(codes[b], cb[b])
+        assert np.array_equal(got[b], ref.astype(np.float32))
+        ref_u = oracle.reconstruct(codes[b][idx], cb[b])
+        nrm = np.linalg.norm(ref_u, axis=1, keepdims=True)
+        assert np.max(np.abs(got_u[b][idx] - ref_u) / nrm) <= 1e-6
+
+
 def test_reconstruct_full_size_llama_layer_sampled():
     """The Llama-shaped layer's K and V books at full size (261,120 vectors each,
     the bench's launch), every 97th vector against the oracle."""
