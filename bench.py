@@ -276,6 +276,7 @@ def main():
                    "pct_hbm_peak": round(100 * dec_gbs / HBM_PEAK_GBS, 3),
                    "ms": round(att_s * 1e3, 5), "effective_bytes": eff_b,
                    "bytes": {"codes": code_b, "window": win_b, "lut": lut_b},
+                   "codes_window_gbs": round((code_b + win_b) / att_s / 1e9, 2),
                    "cache": cache,
                    "cache_flushed": not args.no_flush,
                    "graph_replay_us": graph_us,
