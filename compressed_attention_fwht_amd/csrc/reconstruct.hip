@@ -18,9 +18,10 @@
 // permuting the index bits of rows and columns alike, so the butterfly over
 // (lane, element) computes the same transform.
 //
-// Three variants.  With 2 stages whose codebooks for half the dims fit in
-// LDS (2*C*D/2*4 bytes up to RC_LDS_MAX), the half-table kernel holds each
-// half's tables in LDS in turn, so every gather is an LDS read.  Otherwise,
+// Three variants.  With 2 to 4 stages whose first two stages' codebooks for
+// half the dims fit in LDS (2*C*D/2*4 bytes up to RC_LDS_MAX), the half-table
+// kernel holds each half's tables of those stages in LDS in turn (later
+// stages are gathered through the caches).  Otherwise,
 // with 1, 2 or 4 stages (4 only below D = 256) whose per-stage codebooks fit
 // in LDS (G*C*dsub*4 bytes up to RC_LDS_MAX), each block copies its book's
 // stage-0 codebooks into LDS once (and its code rows too, when they fit
@@ -208,13 +209,13 @@ __global__ __launch_bounds__(RC_LDS_THREADS) void reconstruct_lds_kernel(
   }
 }
 
-// Half-table variant (S stages whose tables for half the dims fit in LDS;
-// launched for S = 2, where it is measured faster -- more stages spill
-// registers at 4 vectors per lane): lane c of a row holds dims [4c, 4c+4) of the first half and
+// Half-table variant (2 to 4 stages; the first SL = 2 stages' tables for half
+// the dims fit in LDS, later stages are gathered through the caches in the
+// same ascending order): lane c of a row holds dims [4c, 4c+4) of the first half and
 // [D/2 + 4c, D/2 + 4c + 4) of the second, and the groups of each half are
 // contiguous in every stage's codebook.  A batch of RC_HK vectors per lane
 // is coded in two phases: the block stages every stage's codebooks of one
-// half's groups into LDS (S*C*D/2 floats), every lane sums its dims of that
+// half's groups into LDS (SL*C*D/2 floats), every lane sums its dims of that
 // half over the stages and keeps the 4 sums per vector in registers; then the
 // other half's tables replace them and each vector is finished (unrotation,
 // smoothing, stores) as soon as its second half is summed.  Consecutive
@@ -227,7 +228,7 @@ __global__ __launch_bounds__(RC_LDS_THREADS) void reconstruct_lds_kernel(
 constexpr int RC_HT_THREADS = 1024;
 constexpr int RC_HK = 4;                     // vectors per lane per batch (8 spills)
 
-template <int D, int S>
+template <int D, int S, int SL>
 __global__ __launch_bounds__(RC_HT_THREADS) void reconstruct_half_kernel(
     const uint8_t* __restrict__ codes, const float* __restrict__ cb, float* __restrict__ out,
     int64_t n_per_book, int64_t per_block, int G, int C, int unrotate,
@@ -254,7 +255,7 @@ __global__ __launch_bounds__(RC_HT_THREADS) void reconstruct_half_kernel(
   const int64_t half_floats = (int64_t)GH * C * dsub;   // one stage of one half
   // code rows of the batch, behind the table, at the same offset modulo 16
   // as in global memory
-  uint8_t* lcodes = smem + (size_t)S * half_floats * 4;
+  uint8_t* lcodes = smem + (size_t)SL * half_floats * 4;
   int loaded = -1;                                      // half held in LDS (block-uniform)
   int lo = 0;                                           // offset of the batch's first code byte
 
@@ -283,7 +284,7 @@ __global__ __launch_bounds__(RC_HT_THREADS) void reconstruct_half_kernel(
     __syncthreads();                                    // every read of the old contents is done
     if (vb >= 0) load_codes(vb);
 #pragma unroll
-    for (int s = 0; s < S; ++s) {
+    for (int s = 0; s < SL; ++s) {
       const float4* src = reinterpret_cast<const float4*>(cbb + ((int64_t)s * G + hh * GH) * C * dsub);
       float4* dst = reinterpret_cast<float4*>(tab + s * half_floats);
       // four loads in flight per thread before their LDS stores (one at a
@@ -321,9 +322,10 @@ __global__ __launch_bounds__(RC_HT_THREADS) void reconstruct_half_kernel(
     }
     Acc acc[4] = {0, 0, 0, 0};
 #pragma unroll
-    for (int s = 0; s < S; ++s) {
-      const float4 e = *reinterpret_cast<const float4*>(
-          tab + s * half_floats + ((int64_t)gl * C + z[s]) * dsub + j);
+    for (int s = 0; s < S; ++s) {                       // ascending stages
+      const float4 e = s < SL
+          ? *reinterpret_cast<const float4*>(tab + s * half_floats + ((int64_t)gl * C + z[s]) * dsub + j)
+          : *reinterpret_cast<const float4*>(cbb + (((int64_t)s * G + g) * C + z[s]) * dsub + j);
       acc[0] += e.x; acc[1] += e.y; acc[2] += e.z; acc[3] += e.w;
     }
 #pragma unroll
@@ -450,12 +452,14 @@ hipError_t launch_reconstruct(const uint8_t* codes, const float* cb, float* out,
   const int dsub = D / G;
   const size_t cbytes = (size_t)G * C * dsub * sizeof(float);
   const int64_t vec_per_iter = (int64_t)(RC_THREADS / 64) * (64 / (D / 8)) * RC_UNR;
-  // 2 stages whose half-dim tables fit RC_LDS_MAX: the half-table variant
+  // 2 to 4 stages whose first two stages' half-dim tables fit RC_LDS_MAX: the
+  // half-table variant
   // (the LDS variants put the books on grid.y)
-  const size_t hbytes = (size_t)S * C * (D / 2) * sizeof(float);
+  const int SLc = S < 2 ? S : 2;                         // stages whose half tables sit in LDS
+  const size_t hbytes = (size_t)SLc * C * (D / 2) * sizeof(float);
   const int64_t hbatch = (int64_t)(RC_HT_THREADS / (D / 8)) * RC_HK;
   const size_t hlds = hbytes + (size_t)hbatch * S * G + 16;   // table, a batch's code rows
-  if (S == 2 && G % 2 == 0 && hbytes <= RC_LDS_MAX && hlds <= RC_LDS_BLOCK &&
+  if (S >= 2 && S <= 4 && G % 2 == 0 && hbytes <= RC_LDS_MAX && hlds <= RC_LDS_BLOCK &&
       n_books <= 65535) {
     const int64_t batch = hbatch;
     int64_t nx = (256 + n_books - 1) / n_books;
@@ -464,7 +468,7 @@ hipError_t launch_reconstruct(const uint8_t* codes, const float* cb, float* out,
     nx = (n_per_book + per - 1) / per;
 #define KVQ_RH(DD, SSV)                                                                       \
     if (D == DD && S == SSV) {                                                                \
-      auto kern = reconstruct_half_kernel<DD, SSV>;                                           \
+      auto kern = reconstruct_half_kernel<DD, SSV, 2>;                                        \
       hipError_t e = hipFuncSetAttribute((const void*)kern,                                   \
                                          hipFuncAttributeMaxDynamicSharedMemorySize,          \
                                          (int)hlds);                                          \
@@ -473,7 +477,8 @@ hipError_t launch_reconstruct(const uint8_t* codes, const float* cb, float* out,
           codes, cb, out, n_per_book, per, G, C, unrotate, sm.f, sm.n_scale, n_rows);         \
       return hipGetLastError();                                                               \
     }
-    KVQ_RH(64, 2) KVQ_RH(128, 2) KVQ_RH(256, 2)
+    KVQ_RH(64, 2) KVQ_RH(128, 2) KVQ_RH(256, 2) KVQ_RH(64, 3) KVQ_RH(128, 3) KVQ_RH(256, 3)
+    KVQ_RH(64, 4) KVQ_RH(128, 4) KVQ_RH(256, 4)
 #undef KVQ_RH
   }
   if (cbytes <= RC_LDS_MAX && (S == 1 || S == 2 || (S == 4 && D < 256)) && n_books <= 65535) {
