@@ -28,10 +28,12 @@
 // fixed-point integers round(p * 2^F) with LDS integer atomics (ds_add_u32,
 // or ds_add_u64 carrying two heads' 32-bit fields at once): on gfx950 LDS
 // float atomics retire an order of magnitude slower than integer ones.
-// F = 31 - ceil(log2(chunk)) keeps every bin and every field sum below 2^31,
-// so packed fields never carry into each other.  The chunk's l is the sum of
-// the same integers, so the rounding of the weights cancels in o = sum p v /
-// sum p to first order.
+// F = 31 - ceil(log2(l)) per head, l = sum_t p_t of the chunk (at least 1),
+// keeps every bin and every field sum below 2^32, so packed fields never
+// carry into each other, and bounds the weight rounded away per token by
+// l * 2^-32, so the rounding error of the chunk stays below chunk * 2^-32 of
+// l even when one token dominates.  The chunk's l is the sum of the same
+// integers, so numerator and denominator see the same rounded weights.
 #include "kvq_internal.h"
 
 namespace kvq {
@@ -95,8 +97,6 @@ AttnPlan attn_plan(int B, int Hq, int Hkv, int D, int S, int G, int C, int Tc, i
     else
       p.n_wblocks = (W + ATTN_WIN_BLOCK - 1) / ATTN_WIN_BLOCK;
   }
-  // fixed-point weights: every bin and every chunk sum below 2^31
-  if (p.n_chunks > 0) p.fbits = 31 - ceil_log2(p.chunk);
   // LUT built by the chunk blocks themselves unless the K codebook re-reads
   // (S*C*D floats per block, from L2) outweigh one LUT pass
   p.fuse_lut = p.n_chunks > 0 &&
@@ -506,7 +506,7 @@ __global__ __launch_bounds__(CH_THREADS, 1) void attn_chunk_kernel(
     const uint8_t* __restrict__ kcodes, const uint8_t* __restrict__ vcodes,
     const float* __restrict__ vcb, const float* __restrict__ lut, float* __restrict__ part,
     int Hq, int Hkv, int S, int G, int C, int Tc, int n_chunks, int chunk, int n_hsplit,
-    int pstride, int fbits, int cparts, size_t lut_slice, const float* __restrict__ kcb,
+    int pstride, int cparts, size_t lut_slice, const float* __restrict__ kcb,
     const float* __restrict__ q,
     const uint16_t* __restrict__ kw, const uint16_t* __restrict__ vw, int W, int wslice,
     int nslots, float scale, int cstride, int wstride, const float* __restrict__ ksm,
@@ -533,7 +533,7 @@ __global__ __launch_bounds__(CH_THREADS, 1) void attn_chunk_kernel(
   float* tabf = reinterpret_cast<float*>(smem);         // LUT during pass 1
   uint32_t* tabu = reinterpret_cast<uint32_t*>(smem);   // histogram during pass 2
   float* cpart = reinterpret_cast<float*>(smem + (((size_t)tabh * 4 + 15) & ~(size_t)15));
-  __shared__ float red_f[8][RP], red_wf[8][RP], red_wl[8][RP];
+  __shared__ float red_f[8][RP], red_wf[8][RP], red_wl[8][RP], red_l[8][RP];
   __shared__ uint32_t red_u[8][RP];
   __shared__ float mx[RP], mxw[RP], ltw[RP];
   __shared__ uint32_t lt[RP];
@@ -762,6 +762,15 @@ __global__ __launch_bounds__(CH_THREADS, 1) void attn_chunk_kernel(
     }
   }
   __syncthreads();                                      // also: every LUT read is done
+  // chunk max per head (every thread folds the wave maxima itself), then the
+  // weights p = exp(s - m) in place of the scores and their per-head sum
+  float m[RP];
+#pragma unroll
+  for (int r = 0; r < RP; ++r) {
+    float v = red_f[0][r];
+    for (int w = 1; w < CH_THREADS / 64; ++w) v = fmaxf(v, red_f[w][r]);
+    m[r] = v;
+  }
   if (tid < RP) {
     float v = red_f[0][tid], vw = red_wf[0][tid];
     for (int w = 1; w < CH_THREADS / 64; ++w) {
@@ -771,15 +780,36 @@ __global__ __launch_bounds__(CH_THREADS, 1) void attn_chunk_kernel(
     mx[tid] = v;
     mxw[tid] = vw;
   }
+#pragma unroll
+  for (int r = 0; r < RP; ++r) {
+    float sp = 0.0f;
+#pragma unroll
+    for (int k = 0; k < CH_TPT; ++k) {
+      sc[k][r] = __expf(sc[k][r] - m[r]);               // -inf (no token) -> 0
+      sp += sc[k][r];
+    }
+    sp = wave_sum(sp);
+    if (lane == 0) red_l[wave][r] = sp;
+  }
   for (int i = tid; i < tabh / 4; i += CH_THREADS)
     reinterpret_cast<uint4*>(tabu)[i] = make_uint4(0u, 0u, 0u, 0u);
   for (int i = (tabh / 4) * 4 + tid; i < tabh; i += CH_THREADS) tabu[i] = 0u;
   __syncthreads();
-  float m[RP];
+  // fraction bits per head from the chunk's own weight sum l (>= 1, the
+  // maximum's weight): F = 31 - ceil(log2 l) keeps l * 2^F <= 2^31, so every
+  // bin, every 32-bit field and the integer sum of the chunk stay below 2^32,
+  // while a weight dropped by rounding is below 2^-F-1 <= l * 2^-32: the
+  // mass lost to rounding is at most chunk * 2^-32 of l however peaky the
+  // chunk.
+  float fsc[RP], finv[RP];
 #pragma unroll
-  for (int r = 0; r < RP; ++r) m[r] = mx[r];
-
-  const float fscale = (float)(1u << fbits);
+  for (int r = 0; r < RP; ++r) {
+    float l = red_l[0][r];
+    for (int w = 1; w < CH_THREADS / 64; ++w) l += red_l[w][r];
+    const int F = 31 - ceil_log2_f(l);
+    fsc[r] = (float)(1u << F);
+    finv[r] = 1.0f / fsc[r];
+  }
   uint32_t ls[RP];
 #pragma unroll
   for (int r = 0; r < RP; ++r) ls[r] = 0u;
@@ -824,7 +854,7 @@ __global__ __launch_bounds__(CH_THREADS, 1) void attn_chunk_kernel(
       uint32_t pw[RP];
 #pragma unroll
       for (int r = 0; r < RP; ++r) {
-        pw[r] = (uint32_t)__builtin_rintf(__expf(sc[k][r] - m[r]) * fscale);
+        pw[r] = (uint32_t)__builtin_rintf(sc[k][r] * fsc[r]);
         ls[r] += pw[r];
       }
       auto scatter = [&](int sg, int z) { hist_add<RP>(tabu, sg, z, C, pw); };
@@ -912,12 +942,14 @@ __global__ __launch_bounds__(CH_THREADS, 1) void attn_chunk_kernel(
           make_float4(acc[r][0], acc[r][1], acc[r][2], acc[r][3]);
   }
   __syncthreads();
-  const float inv = 1.0f / fscale;
 #pragma unroll
   for (int j = 0; j < NO; ++j) {
     const int o = tid + CH_THREADS * j;
     const int r = o / D, d = o - r * D;
     if (o >= RP * D || r >= nh) continue;
+    float inv = finv[0];
+#pragma unroll
+    for (int rr = 1; rr < RP; ++rr) inv = r == rr ? finv[rr] : inv;
     float v = 0.0f;
     for (int sp = 0; sp < S * P; ++sp) v += cpart[(sp * RP + r) * D + d];
     v *= inv;
@@ -1048,7 +1080,7 @@ static hipError_t launch_rp(const AttnPlan& p, int SG, const float* q, const flo
                             (int)lds);                                                         \
     if (e != hipSuccess) return e;                                                             \
     kern<<<grid, CH_THREADS, lds, st>>>(kc, vc, vcb, lut, part, Hq, Hkv, S, G, C, Tc,          \
-                                        p.n_chunks, p.chunk, p.n_hsplit, p.pstride, p.fbits,   \
+                                        p.n_chunks, p.chunk, p.n_hsplit, p.pstride,            \
                                         p.cparts, p.lut_slice, kcb, q, kw, vw, W,              \
                                         p.wslice, nslots, scale, cstride, wstride, ksm.f,      \
                                         ksm.n_scale);                                          \

@@ -206,6 +206,47 @@ __device__ __forceinline__ void hadamard_row(float (&v)[E], int lane) {
 #undef KVQ_XSTAGE
 }
 
+// The same butterfly in float64 (each exchange moves the two 32-bit halves).
+// With the non-packed float32 rate for float64 adds on gfx950, it costs what
+// the float32 butterfly costs twice; it is exact for 2-byte inputs (their
+// 8- or 11-bit significands summed over at most 256 terms fit 53 bits).
+template <int M>
+__device__ __forceinline__ double xor_lane_f64(double x) {
+  const uint64_t u = __double_as_longlong(x);
+  const float lo = xor_lane<M>(__uint_as_float((uint32_t)u));
+  const float hi = xor_lane<M>(__uint_as_float((uint32_t)(u >> 32)));
+  return __longlong_as_double((long long)(((uint64_t)__float_as_uint(hi) << 32) |
+                                          __float_as_uint(lo)));
+}
+template <int E, int L>
+__device__ __forceinline__ void hadamard_row_f64(double (&v)[E], int lane) {
+#pragma unroll
+  for (int h = 1; h < E; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      if ((i & h) == 0) {
+        const double a = v[i], b = v[i + h];
+        v[i] = a + b;
+        v[i + h] = a - b;
+      }
+    }
+  }
+#define KVQ_XSTAGE_D(MASK)                                            \
+  if constexpr (L > (MASK)) {                                         \
+    const bool up = (lane & (MASK)) != 0;                             \
+    _Pragma("unroll") for (int i = 0; i < E; ++i) {                   \
+      const double p = xor_lane_f64<(MASK)>(v[i]);                    \
+      v[i] = up ? p - v[i] : v[i] + p;                                \
+    }                                                                 \
+  }
+  KVQ_XSTAGE_D(1)
+  KVQ_XSTAGE_D(2)
+  KVQ_XSTAGE_D(4)
+  KVQ_XSTAGE_D(8)
+  KVQ_XSTAGE_D(16)
+#undef KVQ_XSTAGE_D
+}
+
 // Sum over the L consecutive lanes of a row (L a power of two <= 32); every
 // lane of the row receives the sum.  All lanes of the wavefront execute this.
 template <int L>
@@ -243,6 +284,19 @@ __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
   v = pair_sum_u32<8>(v);
   v = pair_sum_u32<16>(v);
   return pair_sum_u32<32>(v);
+}
+
+__device__ __forceinline__ constexpr double rsqrt_pow2_f64(int d) {
+  // 1/sqrt(d) rounded to float64, d in {64, 128, 256}.
+  return d == 64 ? 0.125 : d == 128 ? 0.08838834764831843 : 0.0625;
+}
+
+// ceil(log2 x) for a finite float x >= 1 (exact: from the exponent field,
+// plus one when any mantissa bit is set).
+__device__ __forceinline__ int ceil_log2_f(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const int e = (int)((u >> 23) & 255u) - 127;
+  return e + ((u & 0x7fffffu) != 0u ? 1 : 0);
 }
 
 __device__ __forceinline__ constexpr float rsqrt_pow2(int d) {

@@ -19,7 +19,6 @@ struct AttnPlan {
   int n_hsplit;    // blocks per KV head along the query heads of its group
   int n_chunks;    // split-K chunks along the coded tokens
   int chunk;       // tokens per chunk
-  int fbits;       // fixed-point fraction bits of the softmax-weight histogram
   int cparts;      // codeword ranges per (stage, dims) item in the V contraction
   int wslice;      // window tokens joining each chunk block (0: window blocks)
   int n_wblocks;   // window blocks of ATTN_WIN_BLOCK tokens, records after the chunks' ones

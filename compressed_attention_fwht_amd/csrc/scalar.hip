@@ -170,15 +170,28 @@ __global__ __launch_bounds__(256) void scalar_encode_kernel(
                     (((book * n_seq + seq) * seq_stride + row) * D + col * 8) * ESZ,
                 y[u]);
     }
-    // phases over all SC_U * 8 elements of the lane, so that independent work
-    // (butterflies, index sums, level reads from LDS) overlaps
+    // The rotation runs in float64 (exact for 2-byte inputs), each element is
+    // rounded once to float32 for the stage-1 threshold tests, and the
+    // stage-2 residual y - level is taken in float64 before its own rounding:
+    // a test then errs only when the element lies within about 1e-7 of its
+    // magnitude from a threshold, far inside the 1e-4 near-tie rule for
+    // every level spacing of b <= 4.  Phases run over all SC_U * 8 elements
+    // of the lane, so that independent work overlaps.
+    double yd[SC_U][8];
+#pragma unroll
+    for (int u = 0; u < SC_U; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) yd[u][e] = (double)y[u][e];
     if (!pre_rotated) {
 #pragma unroll
       for (int u = 0; u < SC_U; ++u) {
-        hadamard_row<8, L>(y[u], lane);
-        constexpr float sc = rsqrt_pow2(D);
+        hadamard_row_f64<8, L>(yd[u], lane);
+        constexpr double sc = rsqrt_pow2_f64(D);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) y[u][e] *= sc;
+        for (int e = 0; e < 8; ++e) {
+          yd[u][e] *= sc;
+          y[u][e] = (float)yd[u][e];
+        }
       }
     }
     uint32_t z1[SC_U][8];
@@ -199,7 +212,7 @@ __global__ __launch_bounds__(256) void scalar_encode_kernel(
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         p1[u] |= z1[u][e] << (e * B);
-        p2[u] |= bsum<B>(y[u][e] - q1[u][e], t1) << (e * B);
+        p2[u] |= bsum<B>((float)(yd[u][e] - (double)q1[u][e]), t1) << (e * B);
       }
     }
 #pragma unroll

@@ -7,11 +7,10 @@ tolerances:
     tie, where several codes are correct).  After any accepted choice the
     oracle continues the residual chain from that choice (teacher forcing), so
     one near tie does not make later stages look wrong;
-  * scalar codes: equal to the oracle's nearest level, except where the
-    element lies within SCALAR_REL_TOL * rms(row) of the decision threshold
-    between the two levels (float32 rotation error is below a quarter of that
-    at head_dim 128); stage 2 is checked on the residual of the candidate's
-    stage-1 choice;
+  * scalar codes: the same rule on the scalar distances: equal to the
+    oracle's nearest level, except where the candidate level's squared
+    distance is within a relative 1e-4 of the best one; stage 2 is checked on
+    the residual of the candidate's stage-1 choice;
   * reconstructed vectors: within 1e-6 absolute;
   * attention outputs: within 2e-3 max-abs and 1e-3 relative L2.
 """
@@ -25,7 +24,6 @@ CODE_REL_TOL = 1e-4
 RECON_ATOL = 1e-6
 ATTN_ATOL = 2e-3
 ATTN_REL_L2 = 1e-3
-SCALAR_REL_TOL = 2e-5
 
 
 def check_codes(x, codebooks, codes, *, rotate=True, rel_tol=CODE_REL_TOL, block=4096):
@@ -73,27 +71,30 @@ def check_codes(x, codebooks, codes, *, rotate=True, rel_tol=CODE_REL_TOL, block
             "worst_rel_excess": worst, "hard_examples": hard_at}
 
 
-def check_scalar_codes(y, levels1, levels2, z1, z2, *, rel_tol=SCALAR_REL_TOL):
+def check_scalar_codes(y, levels1, levels2, z1, z2, *, rel_tol=CODE_REL_TOL):
     """Teacher-forced check of candidate scalar indices z1, z2 [N][D] against
-    the nearest levels of the rotated vectors y [N][D] (float64).  A
-    non-matching index is accepted when its distance exceeds the best one by
-    at most 2 * rel_tol * rms(row) (the element within rel_tol * rms(row) of
-    the threshold)."""
+    the nearest levels of the rotated vectors y [N][D] (float64), under the
+    code rule of the vector quantiser: a non-matching index is accepted when
+    its squared distance to the element is at most (1 + rel_tol) times the
+    best level's (the best two distances within rel_tol relative)."""
     y = np.asarray(y, dtype=np.float64)
     l1 = np.asarray(levels1, dtype=np.float64)
     l2 = np.asarray(levels2, dtype=np.float64)
-    tol = 2.0 * rel_tol * np.sqrt(np.mean(y * y, axis=-1, keepdims=True))
-    out = {"total": 2 * y.size, "exact": 0, "near_tie": 0, "hard": 0}
+    out = {"total": 2 * y.size, "exact": 0, "near_tie": 0, "hard": 0, "worst_rel_excess": 0.0}
     r = y
     for lv, zc in ((l1, np.asarray(z1)), (l2, np.asarray(z2))):
         zo = scalar_nearest(r, lv)
-        dc = np.abs(r - lv[zc])
-        do = np.abs(r - lv[zo])
+        dc = (r - lv[zc]) ** 2
+        do = (r - lv[zo]) ** 2
         exact = zc == zo
-        ok = dc <= do + tol
+        ok = dc <= (1.0 + rel_tol) * do
         out["exact"] += int(exact.sum())
         out["near_tie"] += int((~exact & ok).sum())
         out["hard"] += int((~exact & ~ok).sum())
+        if (~exact).any():
+            with np.errstate(divide="ignore", invalid="ignore"):
+                ex = np.where(do > 0, dc / do - 1.0, np.where(dc > 0, np.inf, 0.0))
+            out["worst_rel_excess"] = max(out["worst_rel_excess"], float(ex[~exact].max()))
         r = r - lv[zc]
     return out
 

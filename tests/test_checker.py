@@ -64,7 +64,9 @@ def test_recon_and_attn_rules():
 
 def test_scalar_checker_rules():
     """Exact indices pass; an index on the wrong side of a threshold by a hair
-    is a near tie; a far one is hard; stage 2 follows the candidate's stage 1."""
+    (squared distances within 1e-4 relative) is a near tie; one 1e-4 of the
+    spacing away is hard; a far one is hard; stage 2 follows the candidate's
+    stage 1."""
     lv1 = np.array([-1.5, -0.5, 0.5, 1.5])
     lv2 = np.array([-0.3, -0.1, 0.1, 0.3])
     y = np.array([[0.2, -0.9, 1.0 + 1e-7, 1.4] * 4])            # rms ~ 1
@@ -77,6 +79,14 @@ def test_scalar_checker_rules():
     z2t = oracle.scalar_nearest(y - lv1[zt], lv2)                # stage 2 on the candidate's residual
     res = oracle.check_scalar_codes(y, lv1, lv2, zt, z2t)
     assert res["near_tie"] == 1 and res["hard"] == 0
+    yh = y.copy()
+    yh[0, 2] = 1.0 + 1e-4                                        # (d_c / d_1) - 1 ~ 4e-4: hard
+    z1h = oracle.scalar_nearest(yh, lv1)
+    zh = z1h.copy()
+    zh[0, 2] = 2
+    z2h = oracle.scalar_nearest(yh - lv1[zh], lv2)
+    res = oracle.check_scalar_codes(yh, lv1, lv2, zh, z2h)
+    assert res["hard"] == 1 and res["near_tie"] == 0
     zf = z1.copy()
     zf[0, 0] = 0                                                 # 0.2 coded as -1.5: hard
     res = oracle.check_scalar_codes(y, lv1, lv2, zf, z2)

@@ -454,6 +454,59 @@ def test_decode_codes_only_short():
     assert res["ok"], res
 
 
+
+@pytest.mark.parametrize("key,delta,every", [(2, 15.5, 1024), (4, 14.0, 4096)])
+def test_decode_attention_sink_chunks(key, delta, every):
+    """Peaky softmax inside the split-K chunks, at the workload's full shape:
+    every `every`-th coded token is a sink whose key scores `delta` nats
+    above every other key (all other coded keys share one code row, the
+    window keys equal their reconstruction), and the V rows differ by several
+    units (V codebook x10, random V codes).  On the long-context shape each
+    4088-token chunk holds one sink and 4087 weights of e^-14, 3.4e-3 of its
+    mass: a fixed-point weight step taken from the chunk length alone (2^-19)
+    rounds them all to zero, about 5e-2 off in the output (CPU emulation of
+    that rule).  Query heads are equal so every head sees the same gap.  The
+    fp32 log-sum-exp combine must still meet 2e-3 max-abs / 1e-3 relative L2
+    ("Differential-KV" README, Flash-Style LSE Combine)."""
+    w = synth.workload(key)
+    B, Hkv, Hq, D, W = w.batch, w.n_kv_heads, w.n_q_heads, w.head_dim, w.window
+    S, G, C, Tc = w.n_stages, w.n_groups, w.n_codewords, w.code_tokens
+    say(f"decode attention-sink chunks, {w.name} shape: Tc={Tc} W={W} S={S}")
+    cb = synth.make_codebooks(w)
+    kcb = cb[0]
+    vcb = np.ascontiguousarray(cb[1] * 10.0)
+    rng = np.random.default_rng(20 + key)
+    q0 = rng.standard_normal(D)
+    q = np.broadcast_to(q0.astype(np.float32), (B, Hq, D)).copy()
+    # sink code: per (stage, group) the entry with the largest q_rot . c
+    # (greedy per stage); the other keys: one random code row
+    qr = oracle.fwht(q0[None, :])[0]
+    dsub = D // G
+    sink = np.array([[int(np.argmax(kcb[s, g].astype(np.float64) @ qr[g * dsub:(g + 1) * dsub]))
+                      for g in range(G)] for s in range(S)], dtype=np.uint8)
+    other = rng.integers(0, C, size=(S, G), dtype=np.uint8)
+    k_sink = oracle.reconstruct(sink[None], kcb)[0]
+    k_other = oracle.reconstruct(other[None], kcb)[0]
+    gap = float(q0 @ (k_sink - k_other)) / np.sqrt(D)
+    assert gap > 0.5, gap
+    scale = float(delta / (gap * np.sqrt(D)))          # softmax scale: sink - rest = delta
+    ck = np.broadcast_to(other, (B, Hkv, Tc, S, G)).copy()
+    ck[:, :, ::every] = sink
+    cv = rng.integers(0, C, size=(B, Hkv, Tc, S, G), dtype=np.uint8)
+    kwin = np.broadcast_to(k_other.astype(np.float16), (B, Hkv, W, D)).copy()
+    vwin = (rng.standard_normal((B, Hkv, W, D)) * 5).astype(np.float16)
+    got = kvq.attend_decode(cuda(q), cuda(ck), cuda(cv), cuda(kcb), cuda(vcb), cuda(kwin),
+                            cuda(vwin), scale=scale).cpu().numpy()
+    ref = oracle.attend(q, ck, cv, kcb, vcb, kwin, vwin, scale=scale)
+    # the construction is as described: delta nats between the sink and the rest
+    kr = oracle.reconstruct(ck[0, 0, :every + 1].reshape(-1, S, G), kcb)
+    sc = kr @ q0 * scale
+    assert abs((sc[0] - sc[1]) - delta) < 1e-6 and abs(sc[every] - sc[0]) < 1e-9
+    spread = np.abs(ref - ref.mean(axis=(0, 1), keepdims=True)).max()
+    res = oracle.check_attn(got, ref)
+    say("   ", res, "output spread", round(float(spread), 3))
+    assert res["ok"], res
+
 # ------------------------------------------------- full sizes (sampled encode)
 @pytest.mark.parametrize("key", [2, 3, 4])
 def test_full_size_encode_sampled_and_decode(key):

@@ -2,8 +2,9 @@
 vector, boundary-sum indices, sub-byte packing) with the float64 oracle,
 through the C ABI.
 
-Bars: indices equal the oracle's nearest levels except within 2e-5 * rms(row)
-of a threshold (oracle.check_scalar_codes); reconstruction in the rotated
+Bars: indices equal the oracle's nearest levels except where the candidate's
+squared distance is within a relative 1e-4 of the best level's, the code rule
+of the vector quantiser (oracle.check_scalar_codes); reconstruction in the rotated
 domain within one float32 rounding of the level sum, unrotated within 1e-6 *
 |x_hat|; the product codebook bit-exact; decode attention through it within
 2e-3 max-abs and 1e-3 relative L2 of the oracle's attention over the scalar
