@@ -34,7 +34,7 @@
 // l * 2^-32, so the rounding error of the chunk stays below chunk * 2^-32 of
 // l even when one token dominates.  The chunk's l is the sum of the same
 // integers, so numerator and denominator see the same rounded weights.
-#include "kvq_internal.h"
+#include "attend_common.h"
 
 namespace kvq {
 
@@ -53,6 +53,33 @@ AttnPlan attn_plan(int B, int Hq, int Hkv, int D, int S, int G, int C, int Tc, i
   AttnPlan p{};
   const int SG = S * G;
   const int R = Hq / Hkv;
+  if (attn_rc_eligible(D, G, S, C, Hq, Hkv, Tc)) {
+    // rotated-code kernels: four query heads per block, one chunk of at most
+    // RC_MAX_CHUNK tokens per block, about 256 blocks; the window as a slice
+    // of each chunk block, or in short blocks of the LUT kernel's grid when
+    // the slices would be long
+    p.rc = 1;
+    p.rp = 4;
+    p.n_hsplit = (R + 3) / 4;
+    const int64_t units = (int64_t)B * Hkv * p.n_hsplit;
+    int64_t nc = (256 + units - 1) / units;
+    const int64_t min_nc = (Tc + RC_MAX_CHUNK - 1) / RC_MAX_CHUNK;
+    const int64_t max_nc = (Tc + ATTN_MIN_CHUNK - 1) / ATTN_MIN_CHUNK;
+    if (nc > max_nc) nc = max_nc;
+    if (nc < min_nc) nc = min_nc;
+    if (nc < 1) nc = 1;
+    p.chunk = (int)((Tc + nc - 1) / nc);
+    p.n_chunks = (int)((Tc + p.chunk - 1) / p.chunk);
+    p.wslice = attn_rc_window_slice(W, p.n_chunks);
+    p.n_wblocks = W > 0 && p.wslice == 0 ? attn_rc_window_blocks(W) : 0;
+    p.pstride = D + 4;
+    p.lut_slice = attn_rc_table_bytes(S);
+    // per-unit LUT segments, then the V codebook in the contraction's order
+    p.lut_bytes = (size_t)units * p.lut_slice + (size_t)S * G * C * (D / G) * sizeof(float);
+    p.part_bytes = (size_t)B * Hq * (p.n_chunks + p.n_wblocks) * p.pstride * sizeof(float);
+    p.ws_bytes = ((p.lut_bytes + 255) & ~(size_t)255) + p.part_bytes;
+    return p;
+  }
   // codeword ranges per (stage, 4-dim) item of the V contraction: aim at 512
   // items (at most 16 ranges), fewer when LDS is short; more heads per block
   // win over more ranges
@@ -107,20 +134,6 @@ AttnPlan attn_plan(int B, int Hq, int Hkv, int D, int S, int G, int C, int Tc, i
   p.part_bytes = (size_t)B * Hq * (p.n_chunks + p.n_wblocks) * p.pstride * sizeof(float);
   p.ws_bytes = ((p.lut_bytes + 255) & ~(size_t)255) + p.part_bytes;
   return p;
-}
-
-// Dual transform: the keys were coded divided channel-wise by the factor row
-// of their (sequence, KV head); multiplying the query's channels by the same
-// row before the rotation leaves every score unchanged.  v: the 8 channels
-// at col*8 of one query row.
-template <int D>
-__device__ __forceinline__ void smooth_query(float (&v)[8], const float* __restrict__ ksm, int b,
-                                             int kv, int Hkv, int64_t rows, int col) {
-  const float4* lp = reinterpret_cast<const float4*>(
-      ksm + (((int64_t)b * Hkv + kv) % rows) * D + col * 8);
-  const float4 a = lp[0], c = lp[1];
-  v[0] *= a.x; v[1] *= a.y; v[2] *= a.z; v[3] *= a.w;
-  v[4] *= c.x; v[5] *= c.y; v[6] *= c.z; v[7] *= c.w;
 }
 
 // --------------------------------------------------------------- attn_lut
@@ -288,141 +301,6 @@ __device__ __forceinline__ void visit_codes(const uint4 (&w)[SGC / 16], int C, F
         if (C < 256) z = z < C ? z : C - 1;
         f(w4 * 16 + qd * 4 + by, z);
       }
-    }
-  }
-}
-
-// Window block: softmax partial (m, l, o) of up to ATTN_WIN_BLOCK fp16 window
-// tokens [w0, w1) for the RP query heads of a unit, o rotated like the coded
-// tokens' (H v / sqrt(D)) so the merge treats every record alike.
-// L = D/8 lanes per token row (8 dims per lane, 16-byte loads); pass A
-// stores the scores in LDS, pass B accumulates p * v per row, rows are summed
-// within each wave by lane exchanges and across waves through LDS.
-template <int RP, int D>
-__device__ __forceinline__ void window_partial(const float* __restrict__ q,
-                                               const uint16_t* __restrict__ kw,
-                                               const uint16_t* __restrict__ vw,
-                                               float* __restrict__ part, uint8_t* smem, int b,
-                                               int kv, int h0, int nh, int Hq, int Hkv,
-                                               int wstride, int w0, int w1, int slot, int nslots,
-                                               int pstride, float scale) {
-  constexpr int L = D / 8;
-  constexpr int ROWS = 512 / L;
-  float* ssc = reinterpret_cast<float*>(smem);                  // [ATTN_WIN_BLOCK][RP]
-  float* wacc = ssc + ATTN_WIN_BLOCK * RP;                      // [8 waves][RP][D]
-  __shared__ float wred[8][RP];
-  __shared__ float wm[RP];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int row = tid / L, col = tid % L;
-  const uint16_t* kwp = kw + ((int64_t)b * Hkv + kv) * wstride * D + col * 8;
-  const uint16_t* vwp = vw + ((int64_t)b * Hkv + kv) * wstride * D + col * 8;
-  float qv[RP][8];
-#pragma unroll
-  for (int r = 0; r < RP; ++r) {
-    const float* qp = q + ((int64_t)b * Hq + h0 + (r < nh ? r : nh - 1)) * D + col * 8;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) qv[r][e] = qp[e] * scale;
-  }
-  const int n = w1 - w0;
-  // pass A: scores (the row sums' lane exchanges keep this loop rolled)
-  for (int i = 0; i < n; i += ROWS) {                 // uniform trip count
-    const int w = i + row;
-    const int wl = w < n ? w : n - 1;
-    float kx[8];
-    load8<2>(kwp + (int64_t)(w0 + wl) * D, kx);
-#pragma unroll
-    for (int r = 0; r < RP; ++r) {
-      float dot = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) dot = __builtin_fmaf(qv[r][e], kx[e], dot);
-      dot = row_sum<L>(dot);
-      if (w < n && col == 0) ssc[w * RP + r] = dot;
-    }
-  }
-  __syncthreads();
-  float m[RP];
-#pragma unroll
-  for (int r = 0; r < RP; ++r) {
-    float v = -__builtin_inff();
-    for (int t = tid; t < n; t += 512) v = fmaxf(v, ssc[t * RP + r]);
-    v = wave_max(v);
-    if (lane == 0) wred[wave][r] = v;
-  }
-  __syncthreads();
-  if (tid < RP) {
-    float v = wred[0][tid];
-    for (int w = 1; w < 8; ++w) v = fmaxf(v, wred[w][tid]);
-    wm[tid] = v;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int r = 0; r < RP; ++r) m[r] = wm[r];
-  // pass B: weights and p * v
-  float acc[RP][8], ls[RP];
-#pragma unroll
-  for (int r = 0; r < RP; ++r) {
-    ls[r] = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[r][e] = 0.0f;
-  }
-#pragma unroll 4
-  for (int i = 0; i < n; i += ROWS) {
-    const int w = i + row;
-    if (w < n) {
-      float vx[8];
-      load8<2>(vwp + (int64_t)(w0 + w) * D, vx);
-#pragma unroll
-      for (int r = 0; r < RP; ++r) {
-        const float pw = __expf(ssc[w * RP + r] - m[r]);
-        ls[r] += pw;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[r][e] = __builtin_fmaf(pw, vx[e], acc[r][e]);
-      }
-    }
-  }
-  // into the coded (rotated) domain, H sum p v = sum p H v: the L lanes of a
-  // row group hold sums over the same rows
-  constexpr float rs = rsqrt_pow2(D);
-#pragma unroll
-  for (int r = 0; r < RP; ++r) {
-    hadamard_row<8, L>(acc[r], lane);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[r][e] *= rs;
-  }
-  // rows of a wave -> one row (lanes L apart), then waves through LDS
-#pragma unroll
-  for (int r = 0; r < RP; ++r) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {                     // lanes of one column: L .. 32 apart
-      if constexpr (L <= 8) acc[r][e] += xor_lane<8>(acc[r][e]);
-      if constexpr (L <= 16) acc[r][e] = pair_sum<16>(acc[r][e]);
-      acc[r][e] = pair_sum<32>(acc[r][e]);
-    }
-    ls[r] = wave_sum(col == 0 ? ls[r] : 0.0f);
-  }
-  if (lane < L) {
-#pragma unroll
-    for (int r = 0; r < RP; ++r)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) wacc[(wave * RP + r) * D + col * 8 + e] = acc[r][e];
-  }
-  if (lane == 0) {
-#pragma unroll
-    for (int r = 0; r < RP; ++r) wred[wave][r] = ls[r];
-  }
-  __syncthreads();
-  for (int o = tid; o < RP * D; o += 512) {
-    const int r = o / D, d = o - r * D;
-    if (r >= nh) continue;
-    float v = 0.0f;
-    for (int w = 0; w < 8; ++w) v += wacc[(w * RP + r) * D + d];
-    float* pp = part + ((int64_t)(b * Hq + h0 + r) * nslots + slot) * pstride;
-    pp[4 + d] = v;
-    if (d == 0) {
-      float l = 0.0f;
-      for (int w = 0; w < 8; ++w) l += wred[w][r];
-      pp[0] = m[r];
-      pp[1] = l;
     }
   }
 }
@@ -1106,7 +984,9 @@ hipError_t launch_attend(const AttnPlan& p, int B, int Hq, int Hkv, int D, int S
                                          ((p.lut_bytes + 255) & ~(size_t)255));
   const int SG = S * G;
   hipError_t e;
-  if (p.rp == 4) e = launch_rp<4>(p, SG, q, kcb, kc, vc, vcb, lut, part, kw, vw, B, Hq, Hkv, D, S, G, C, Tc, W, cstride, wstride, scale, ksm, st);
+  if (p.rc) e = launch_attend_rc(p, B, Hq, Hkv, S, Tc, W, cstride, wstride, scale, q, kc, vc, kcb,
+                                 vcb, kw, vw, reinterpret_cast<uint8_t*>(lut), part, ksm, st);
+  else if (p.rp == 4) e = launch_rp<4>(p, SG, q, kcb, kc, vc, vcb, lut, part, kw, vw, B, Hq, Hkv, D, S, G, C, Tc, W, cstride, wstride, scale, ksm, st);
   else if (p.rp == 2) e = launch_rp<2>(p, SG, q, kcb, kc, vc, vcb, lut, part, kw, vw, B, Hq, Hkv, D, S, G, C, Tc, W, cstride, wstride, scale, ksm, st);
   else e = launch_rp<1>(p, SG, q, kcb, kc, vc, vcb, lut, part, kw, vw, B, Hq, Hkv, D, S, G, C, Tc, W, cstride, wstride, scale, ksm, st);
   if (e != hipSuccess) return e;

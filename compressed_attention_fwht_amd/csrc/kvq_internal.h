@@ -13,8 +13,10 @@ constexpr size_t ATTN_LDS_TABLES = 150 * 1024;
 constexpr int ATTN_MAX_CHUNK = 4096;   // tokens per split-K chunk, upper bound
 constexpr int ATTN_MIN_CHUNK = 1024;   // preferred lower bound on chunk length
 constexpr int ATTN_WIN_BLOCK = 2048;   // fp16 window tokens per window block
+constexpr int RC_MAX_CHUNK = 4096;     // tokens per chunk of the rotated-code decode kernel
 
 struct AttnPlan {
+  int rc;          // 1: rotated-code kernels (attend_rc.hip), else the general ones
   int rp;          // query heads per chunk block (0: tables do not fit LDS)
   int n_hsplit;    // blocks per KV head along the query heads of its group
   int n_chunks;    // split-K chunks along the coded tokens
@@ -51,6 +53,19 @@ hipError_t launch_encode(const void* x, int xt, int D, int G, int S, int C, int6
 hipError_t launch_reconstruct(const uint8_t* codes, const float* cb, float* out, int64_t n_books,
                               int64_t n_per_book, int D, int G, int S, int C, int unrotate,
                               int64_t n_rows, Smooth sm, hipStream_t s);
+
+// Rotated-code decode (head_dim 128, 16 x 8-dim groups, C = 256, 1/2/4 stages,
+// GQA >= 2): eligibility, LUT bytes per unit, and the launch of its LUT /
+// window kernel and chunk kernel (records only; the merge follows).
+bool attn_rc_eligible(int D, int G, int S, int C, int Hq, int Hkv, int Tc);
+size_t attn_rc_table_bytes(int S);
+int attn_rc_window_blocks(int W);
+int attn_rc_window_slice(int W, int n_chunks);
+hipError_t launch_attend_rc(const AttnPlan& p, int B, int Hq, int Hkv, int S, int Tc, int W,
+                            int cstride, int wstride, float scale, const float* q,
+                            const uint8_t* kc, const uint8_t* vc, const float* kcb,
+                            const float* vcb, const uint16_t* kw, const uint16_t* vw,
+                            uint8_t* lut, float* part, Smooth ksm, hipStream_t st);
 
 hipError_t launch_attend(const AttnPlan& p, int B, int Hq, int Hkv, int D, int S, int G, int C,
                          int Tc, int W, int cstride, int wstride, float scale, const float* q,

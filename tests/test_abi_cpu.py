@@ -149,8 +149,12 @@ def test_attend_workspace_sizes():
     sz = kvq.attend_workspace_size(1, 32, 8, 128, 32640, 128, 1, 16, 256)
     assert sz % (32 * 132 * 4) == 0 and 8 <= sz // (32 * 132 * 4) <= 64   # LUT built in blocks
     big = kvq.attend_workspace_size(1, 32, 8, 128, 130816, 256, 4, 16, 256)
-    lut = 32 * 64 * 256 * 4                                              # LUT pass: K codebook
-    assert big > lut and (big - lut) % (32 * 132 * 4) == 0               # re-reads would be big
+    # long context: per (sequence, KV head, four query heads) a table of 4 stages
+    # x 16 groups x 256 codewords x 4 heads of floats, then the V codebook in the
+    # contraction's order, then 32 chunk records per head (the window rides on
+    # the chunk blocks)
+    lut = 8 * 64 * 256 * 4 * 4 + 4 * 16 * 256 * 8 * 4
+    assert big == lut + 32 * 32 * 132 * 4
     sz_w = kvq.attend_workspace_size(2, 4, 2, 64, 0, 50, 2, 1, 256)   # window only
     assert sz_w == 2 * 4 * 1 * 68 * 4                                  # no LUT, one window block
 
