@@ -28,7 +28,8 @@ import ctypes
 import os
 
 __all__ = ["KvqError", "LIB_PATH", "lib", "rotate", "encode", "encode_workspace_size",
-           "decode_reconstruct", "attend_decode", "attend_workspace_size", "cache_bytes",
+           "decode_reconstruct", "attend_decode", "attend_decode_noalloc", "NOALLOC_SCRATCH_BYTES",
+           "attend_workspace_size", "cache_bytes",
            "window_append",
            "window_flush", "window_flush_workspace_size", "smooth_calibrate", "codebook_fit",
            "codebook_fit_workspace_size", "lloyd_max", "scalar_encode",
@@ -46,7 +47,8 @@ KVQ_CODEBOOKS_PACKED = 0x8
 F32, BF16, F16 = 0, 1, 2
 
 EXPORTS = ("kvq_rotate", "kvq_encode_workspace_size", "kvq_encode", "kvq_decode_reconstruct",
-           "kvq_attend_workspace_size", "kvq_attend_decode", "kvq_cache_bytes",
+           "kvq_attend_workspace_size", "kvq_attend_decode", "kvq_attend_decode_noalloc",
+           "kvq_cache_bytes",
            "kvq_window_append",
            "kvq_window_flush_workspace_size", "kvq_window_flush", "kvq_smooth_calibrate",
            "kvq_encode_smooth", "kvq_decode_reconstruct_smooth", "kvq_attend_decode_smooth",
@@ -83,6 +85,7 @@ def _load():
     L.kvq_decode_reconstruct.argtypes = [P, ctypes.POINTER(VqDesc), I64, I64, P, P, U32, P]
     L.kvq_attend_workspace_size.argtypes = [ctypes.POINTER(AttnDesc), ctypes.POINTER(SZ)]
     L.kvq_attend_decode.argtypes = [ctypes.POINTER(AttnDesc), P, P, P, P, P, P, P, P, P, SZ, P]
+    L.kvq_attend_decode_noalloc.argtypes = [ctypes.POINTER(AttnDesc), P, P, P, P, P, P, P, P, P]
     U64P = ctypes.POINTER(ctypes.c_uint64)
     L.kvq_cache_bytes.argtypes = [ctypes.POINTER(AttnDesc), U64P, U64P, U64P, U64P]
     L.kvq_window_append.argtypes = [I32, I32, I32, I32, I32, P, P, P, P, P]
@@ -472,6 +475,29 @@ def attend_decode(q, k_codes, v_codes, k_cb, v_cb, k_win=None, v_win=None, *, sc
                                  _ptr(k_cb), _ptr(v_cb), _ptr(k_win), _ptr(v_win), _ptr(out),
                                  _ptr(workspace), workspace.numel(), _stream(q)),
            "kvq_attend_decode")
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20      # KVQ_NOALLOC_SCRATCH_BYTES
+
+
+def attend_decode_noalloc(q, k_codes, v_codes, k_cb, v_cb, k_win=None, v_win=None, *, out,
+                          scale=None, n_code=None, n_window=None):
+    """kvq_attend_decode_noalloc: attend_decode without a workspace (the
+    library's per-GPU array of NOALLOC_SCRATCH_BYTES).  ``out`` [B][Hq][D] f32
+    is required, so this call allocates nothing."""
+    _need_contig(q, k_codes, v_codes, k_cb, v_cb, k_win, v_win, out)
+    B, Hq, D = q.shape
+    _, Hkv, Tcap, S, G = k_codes.shape
+    C = k_cb.shape[2]
+    Wcap = 0 if k_win is None else k_win.shape[2]
+    Tc = Tcap if n_code is None else int(n_code)
+    W = Wcap if n_window is None else int(n_window)
+    a = _attn_desc(B, Hq, Hkv, D, Tc, W, S, G, C, scale, Tcap, Wcap)
+    _check(_lib().kvq_attend_decode_noalloc(ctypes.byref(a), _ptr(q), _ptr(k_codes),
+                                            _ptr(v_codes), _ptr(k_cb), _ptr(v_cb), _ptr(k_win),
+                                            _ptr(v_win), _ptr(out), _stream(q)),
+           "kvq_attend_decode_noalloc")
     return out
 
 

@@ -2,8 +2,15 @@
 // sizing and kernel dispatch.  See include/kvq.h for the contract.
 #include <math.h>
 
+#include <mutex>
+
 #include "kvq.h"
 #include "kvq_internal.h"
+
+// Workspace of kvq_attend_decode_noalloc: one copy per GPU, held until the
+// process ends.  In host code this name is a host-side stand-in, not a device
+// address; the device address comes from hipGetSymbolAddress (scratch_base).
+static __device__ __align__(256) uint8_t scratch[KVQ_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -473,20 +480,19 @@ kvq_status kvq_attend_workspace_size(const kvq_attn_desc* a, size_t* bytes) {
   return KVQ_OK;
 }
 
-static kvq_status attend_common(const kvq_attn_desc* a, const float* q, const uint8_t* k_codes,
-                                const uint8_t* v_codes, const float* k_cb, const float* v_cb,
-                                const kvq_smooth_desc* k_smooth, const uint16_t* k_win,
-                                const uint16_t* v_win, float* out, void* workspace,
-                                size_t ws_bytes, hipStream_t stream) {
-  kvq::AttnPlan plan;
-  kvq_status st = check_attn(a, &plan);
+// Every check of a decode call except the workspace's, before any HIP call.
+static kvq_status attend_check(const kvq_attn_desc* a, const float* q, const uint8_t* k_codes,
+                               const uint8_t* v_codes, const float* k_cb, const float* v_cb,
+                               const kvq_smooth_desc* k_smooth, const uint16_t* k_win,
+                               const uint16_t* v_win, const float* out, kvq::AttnPlan* plan) {
+  kvq_status st = check_attn(a, plan);
   if (st != KVQ_OK) return st;
   if (k_smooth) {
     st = check_smooth(k_smooth);
     if (st != KVQ_OK) return st;
   }
-  if (!q || !out || !workspace) return KVQ_ERR_NULL;
-  if (!aligned16(q) || !aligned16(out) || !aligned16(workspace)) return KVQ_ERR_ALIGN;
+  if (!q || !out) return KVQ_ERR_NULL;
+  if (!aligned16(q) || !aligned16(out)) return KVQ_ERR_ALIGN;
   if (a->n_code_tokens > 0) {
     if (!k_codes || !v_codes || !k_cb || !v_cb) return KVQ_ERR_NULL;
     if (!aligned16(k_codes) || !aligned16(v_codes) || !aligned16(k_cb) || !aligned16(v_cb))
@@ -496,6 +502,20 @@ static kvq_status attend_common(const kvq_attn_desc* a, const float* q, const ui
     if (!k_win || !v_win) return KVQ_ERR_NULL;
     if (!aligned16(k_win) || !aligned16(v_win)) return KVQ_ERR_ALIGN;
   }
+  return KVQ_OK;
+}
+
+static kvq_status attend_common(const kvq_attn_desc* a, const float* q, const uint8_t* k_codes,
+                                const uint8_t* v_codes, const float* k_cb, const float* v_cb,
+                                const kvq_smooth_desc* k_smooth, const uint16_t* k_win,
+                                const uint16_t* v_win, float* out, void* workspace,
+                                size_t ws_bytes, hipStream_t stream) {
+  kvq::AttnPlan plan;
+  kvq_status st = attend_check(a, q, k_codes, v_codes, k_cb, v_cb, k_smooth, k_win, v_win, out,
+                               &plan);
+  if (st != KVQ_OK) return st;
+  if (!workspace) return KVQ_ERR_NULL;
+  if (!aligned16(workspace)) return KVQ_ERR_ALIGN;
   if (ws_bytes < plan.ws_bytes) return KVQ_ERR_WORKSPACE;
   const kvq_vq_desc& v = a->vq;
   const float scale = a->softmax_scale > 0.0f ? a->softmax_scale
@@ -515,6 +535,53 @@ kvq_status kvq_attend_decode(const kvq_attn_desc* a, const float* q, const uint8
                              void* workspace, size_t ws_bytes, hipStream_t stream) {
   return attend_common(a, q, k_codes, v_codes, k_cb, v_cb, nullptr, k_win, v_win, out, workspace,
                        ws_bytes, stream);
+}
+
+// Device address of `scratch` on the current device: looked up with that
+// device current the first time a call runs on it, then kept (one address per
+// device; the lookup is guarded for calls from several host threads).  A
+// stream of another device is refused: its kernels would reach this device's
+// copy.
+static kvq_status scratch_base(hipStream_t stream, void** base) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return KVQ_ERR_UNSUPPORTED;
+  if (stream) {
+    hipDevice_t sdev = -1;
+    e = hipStreamGetDevice(stream, &sdev);
+    if (e != hipSuccess) return hip_status(e);
+    if (sdev != dev) return KVQ_ERR_UNSUPPORTED;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e);
+    addr[dev] = p;
+  }
+  *base = addr[dev];
+  return KVQ_OK;
+}
+
+kvq_status kvq_attend_decode_noalloc(const kvq_attn_desc* a, const float* q,
+                                     const uint8_t* k_codes, const uint8_t* v_codes,
+                                     const float* k_cb, const float* v_cb,
+                                     const uint16_t* k_win, const uint16_t* v_win, float* out,
+                                     hipStream_t stream) {
+  kvq::AttnPlan plan;
+  kvq_status st = attend_check(a, q, k_codes, v_codes, k_cb, v_cb, nullptr, k_win, v_win, out,
+                               &plan);
+  if (st != KVQ_OK) return st;
+  if (plan.ws_bytes > (size_t)KVQ_NOALLOC_SCRATCH_BYTES) return KVQ_ERR_WORKSPACE;
+  void* ws = nullptr;
+  st = scratch_base(stream, &ws);
+  if (st != KVQ_OK) return st;
+  return attend_common(a, q, k_codes, v_codes, k_cb, v_cb, nullptr, k_win, v_win, out, ws,
+                       (size_t)KVQ_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 kvq_status kvq_attend_decode_smooth(const kvq_attn_desc* a, const float* q,

@@ -174,6 +174,27 @@ KVQ_API kvq_status kvq_attend_decode(const kvq_attn_desc* a, const float* q,
                              float* out, void* workspace, size_t ws_bytes,
                              hipStream_t stream);
 
+/* Bytes of the device array kvq_attend_decode_noalloc works in, per GPU. */
+#define KVQ_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/* Decode attention for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Arguments, layouts, results and checks as kvq_attend_decode,
+ * without a workspace: the call works in a device array the library holds,
+ * KVQ_NOALLOC_SCRATCH_BYTES on each GPU it runs on, from the first call on
+ * that GPU until the process ends; it calls no allocator.  A shape whose
+ * kvq_attend_workspace_size exceeds that is KVQ_ERR_WORKSPACE (nothing
+ * launched).  A stream of a device other than the current one is
+ * KVQ_ERR_UNSUPPORTED.  Every call on one GPU uses the same array, which
+ * keeps the last call's contents: calls that overlap on one GPU (other
+ * streams, other host threads) race and must be ordered by the caller.  Each
+ * call writes every byte of it that it reads, so it needs no clearing. */
+KVQ_API kvq_status kvq_attend_decode_noalloc(const kvq_attn_desc* a, const float* q,
+                             const uint8_t* k_codes, const uint8_t* v_codes,
+                             const float* k_cb, const float* v_cb,
+                             const uint16_t* k_win, const uint16_t* v_win,
+                             float* out, hipStream_t stream);
+
 /* Bytes one layer's compressed cache of shape *a holds ("VeloxQuant-MLX
  * 0.5.1", Quick start: the cache reports its memory use; its results count
  * compression as code bytes against fp16 K and V).  K and V together, over

@@ -143,6 +143,33 @@ def test_attend_argument_errors():
                                      None) == NULL
 
 
+def test_attend_noalloc_argument_errors():
+    """The no-allocation entry point runs the same checks as kvq_attend_decode
+    and refuses a shape whose workspace exceeds its device array, all before any
+    HIP call."""
+    L = kvq.lib
+
+    def na(a, q=FAKE, out=FAKE, kw=FAKE):
+        return L.kvq_attend_decode_noalloc(ctypes.byref(a), q, FAKE, FAKE, FAKE, FAKE, kw, FAKE,
+                                           out, None)
+    assert L.kvq_attend_decode_noalloc(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                       None) == NULL
+    assert na(_attn(Hq=30)) == SHAPE
+    assert na(_attn(), q=0) == NULL
+    assert na(_attn(), kw=0) == NULL
+    assert na(_attn(), out=FAKE + 4) == ALIGN
+    assert na(_attn(D=256, S=8, G=32)) == UNSUP
+    big = _attn(B=64, Hq=28, Hkv=4, Tc=8128, W=64, S=2)
+    need = kvq.attend_workspace_size(64, 28, 4, 128, 8128, 64, 2, 16, 256)
+    assert need > kvq.NOALLOC_SCRATCH_BYTES
+    assert na(big) == WS
+    # the decode workloads' shapes fit the array
+    for (B, Hq, Hkv, Tc, W, S) in [(1, 32, 8, 32640, 128, 1), (16, 28, 4, 8128, 64, 2),
+                                   (1, 32, 8, 130816, 256, 4)]:
+        assert kvq.attend_workspace_size(B, Hq, Hkv, 128, Tc, W, S, 16, 256) \
+            <= kvq.NOALLOC_SCRATCH_BYTES
+
+
 def test_attend_workspace_sizes():
     # [LUT of B*Hq*S*G*C floats, when a separate pass builds it], then per
     # (b, h) one record of D + 4 floats per chunk and per window block
