@@ -154,6 +154,10 @@ def _check(st: int, where: str):
 
 
 # --------------------------------------------------------------- torch glue
+# The C ABI sees only pointers and the sizes in its descriptors, so every
+# wrapper checks each tensor's dtype, shape, layout and device against those
+# sizes before the call: a mismatch raises TypeError (dtype) or ValueError
+# (shape, layout, device) and nothing is launched.
 def _torch():
     import torch
     return torch
@@ -182,6 +186,44 @@ def _need_contig(*ts):
             raise ValueError("tensors must be contiguous")
 
 
+def _expect(t, name, dtypes, shape=None, ndim=None):
+    """t has one of ``dtypes`` (a torch dtype or a tuple of them), the given
+    shape (None entries match anything) or number of dimensions, and is
+    contiguous."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not isinstance(dtypes, tuple):
+        dtypes = (dtypes,)
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} must be {' or '.join(str(d) for d in dtypes)}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got shape {tuple(t.shape)}")
+    if shape is not None:
+        shape = tuple(shape)
+        if t.dim() != len(shape) or any(e is not None and int(a) != int(e)
+                                         for a, e in zip(t.shape, shape)):
+            want = "[" + "][".join("*" if e is None else str(e) for e in shape) + "]"
+            raise ValueError(f"{name} must have shape {want}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _same_device(ref, **ts):
+    """Every tensor of ts (None skipped) is a GPU tensor on ref's device."""
+    for name, t in ts.items():
+        if t is None:
+            continue
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be a GPU tensor, got {t.device}")
+        if t.device != ref.device:
+            raise ValueError(f"{name} is on {t.device}, the call runs on {ref.device}")
+
+
+def _workspace(ws, name="workspace"):
+    if ws is not None:
+        _expect(ws, name, _torch().uint8, ndim=1)
+
+
 def _smooth_desc(factors, n_books, D):
     """SmoothDesc of a float32 factor tensor [n_books][n_scale][D] (or
     [n_scale][D] when n_books == 1)."""
@@ -196,18 +238,26 @@ def _smooth_desc(factors, n_books, D):
     return SmoothDesc(_ptr(factors), factors.shape[1])
 
 
+def _dims(x, name, n):
+    if x.dim() != n:
+        raise ValueError(f"{name} must have {n} dimensions, got shape {tuple(x.shape)}")
+    return x.shape
+
+
 def smooth_calibrate(x, n_scale=1, *, n_rows=None, out=None):
     """Dual-transform factors of x [n_books][n_seq][seq_stride][D]
     (f32/bf16/f16): f[b][j][i] = sqrt(max |x[b][n][t][i]|) over sequences n
     with n % n_scale == j and rows t < n_rows (1 where the maximum is 0).
     Returns f32 [n_books][n_scale][D]."""
     torch = _torch()
+    _dtype_code(x)
     _need_contig(x)
-    nb, ns, stride, D = x.shape
+    nb, ns, stride, D = _dims(x, "x", 4)
     n_rows = stride if n_rows is None else n_rows
     if out is None:
         out = torch.empty((nb, n_scale, D), dtype=torch.float32, device=x.device)
-    _need_contig(out)
+    _expect(out, "out", torch.float32, (nb, n_scale, D))
+    _same_device(x, x=x, out=out)
     _check(_lib().kvq_smooth_calibrate(_ptr(x), _dtype_code(x), D, nb, ns, stride, n_rows,
                                        int(n_scale), _ptr(out), _stream(x)),
            "kvq_smooth_calibrate")
@@ -230,12 +280,19 @@ def codebook_fit(x, init, n_iter, *, n_rows=None, smooth=None, workspace=None, i
     n % n_scale).  Returns the fitted codebooks (init itself when
     ``inplace``)."""
     torch = _torch()
-    _need_contig(x, init)
+    _dtype_code(x)
+    _need_contig(x)
     if x.dim() == 2:
         x = x.unsqueeze(0)
-    ns, stride, D = x.shape
+    ns, stride, D = _dims(x, "x", 3)
     n_rows = stride if n_rows is None else n_rows
+    _expect(init, "init", torch.float32, ndim=4)
     S, G, C, dsub = init.shape
+    if G * dsub != D:
+        raise ValueError(f"init [S][G][C][dsub] must have G * dsub = D = {D}, got "
+                         f"{tuple(init.shape)}")
+    _workspace(workspace)
+    _same_device(x, x=x, init=init, smooth=smooth, workspace=workspace)
     cb = init if inplace else init.clone()
     vq = VqDesc(D, G, S, C)
     need = codebook_fit_workspace_size(D, G, S, C, ns * n_rows)
@@ -262,18 +319,27 @@ def lloyd_max(kind, bits):
     return list(lv), d.value
 
 
+def _scalar_bits(bits):
+    if bits not in (1, 2, 4):
+        raise ValueError(f"bits must be 1, 2 or 4, got {bits}")
+
+
 def scalar_encode(x, levels, bits, *, n_rows=None, pre_rotated=False, codes=None):
     """Two-pass scalar codes of rows [0, n_rows) of every sequence of x
     [n_books][n_seq][seq_stride][D] (f32/bf16/f16); levels f32
     [n_books][2][2^bits].  Returns u8 [n_books][n_seq][n_rows][2][D*bits/8]."""
     torch = _torch()
-    _need_contig(x, levels)
-    nb, ns, stride, D = x.shape
+    _scalar_bits(bits)
+    _dtype_code(x)
+    _need_contig(x)
+    nb, ns, stride, D = _dims(x, "x", 4)
     n_rows = stride if n_rows is None else n_rows
+    _expect(levels, "levels", torch.float32, (nb, 2, 1 << bits))
     if codes is None:
         codes = torch.empty((nb, ns, n_rows, 2, D * bits // 8), dtype=torch.uint8,
                             device=x.device)
-    _need_contig(codes)
+    _expect(codes, "codes", torch.uint8, (nb, ns, n_rows, 2, D * bits // 8))
+    _same_device(x, x=x, levels=levels, codes=codes)
     _check(_lib().kvq_scalar_encode(_ptr(x), _dtype_code(x), D, bits, nb, ns, stride, n_rows,
                                     _ptr(levels), _ptr(codes),
                                     KVQ_INPUT_PRE_ROTATED if pre_rotated else 0, _stream(x)),
@@ -285,13 +351,18 @@ def scalar_decode_reconstruct(codes, levels, bits, *, unrotate=False, out=None):
     """codes u8 [n_books][...][2][D*bits/8], levels f32 [n_books][2][2^bits] ->
     f32 [n_books][...][D]: levels1[z1] + levels2[z2] (then H_D if unrotate)."""
     torch = _torch()
-    _need_contig(codes, levels)
-    nb = levels.shape[0]
+    _scalar_bits(bits)
+    _expect(codes, "codes", torch.uint8)
+    if codes.dim() < 3 or codes.shape[-2] != 2:
+        raise ValueError(f"codes must be [n_books][...][2][D*bits/8], got {tuple(codes.shape)}")
+    nb = codes.shape[0]
+    _expect(levels, "levels", torch.float32, (nb, 2, 1 << bits))
     D = codes.shape[-1] * 8 // bits
     per_book = codes.numel() // (nb * 2 * codes.shape[-1]) if codes.numel() else 0
     if out is None:
         out = torch.empty(codes.shape[:-2] + (D,), dtype=torch.float32, device=codes.device)
-    _need_contig(out)
+    _expect(out, "out", torch.float32, tuple(codes.shape[:-2]) + (D,))
+    _same_device(codes, codes=codes, levels=levels, out=out)
     _check(_lib().kvq_scalar_decode_reconstruct(_ptr(codes), D, bits, nb, per_book, _ptr(levels),
                                                 _ptr(out), KVQ_UNROTATE if unrotate else 0,
                                                 _stream(codes)),
@@ -303,11 +374,13 @@ def scalar_product_codebook(levels, bits, head_dim, out=None):
     """The product codebook f32 [2][D*bits/8][256][8/bits] of one book's levels
     [2][2^bits]; with it kvq_attend_decode reads packed scalar codes."""
     torch = _torch()
-    _need_contig(levels)
+    _scalar_bits(bits)
+    _expect(levels, "levels", torch.float32, (2, 1 << bits))
     G, k = head_dim * bits // 8, 8 // bits
     if out is None:
         out = torch.empty((2, G, 256, k), dtype=torch.float32, device=levels.device)
-    _need_contig(out)
+    _expect(out, "out", torch.float32, (2, G, 256, k))
+    _same_device(levels, levels=levels, out=out)
     _check(_lib().kvq_scalar_product_codebook(head_dim, bits, _ptr(levels), _ptr(out),
                                               _stream(levels)), "kvq_scalar_product_codebook")
     return out
@@ -316,12 +389,16 @@ def scalar_product_codebook(levels, bits, head_dim, out=None):
 def rotate(x, out=None):
     """y = H_D x over the last axis.  x: cuda tensor f32/bf16/f16 [..., D]."""
     torch = _torch()
+    _dtype_code(x)
     _need_contig(x)
+    if x.dim() < 1:
+        raise ValueError("x must have a last (head) axis")
     D = x.shape[-1]
     n = x.numel() // D if D else 0
     if out is None:
         out = torch.empty(x.shape, dtype=torch.float32, device=x.device)
-    _need_contig(out)
+    _expect(out, "out", torch.float32, tuple(x.shape))
+    _same_device(x, x=x, out=out)
     _check(_lib().kvq_rotate(_ptr(x), _dtype_code(x), _ptr(out), n, D, _stream(x)), "kvq_rotate")
     return out
 
@@ -345,14 +422,21 @@ def encode(x, codebooks, *, n_rows=None, pre_rotated=False, generic=False, codes
     f32 [n_books][n_scale][D]; x is divided by them before the rotation
     (kvq_encode_smooth)."""
     torch = _torch()
-    _need_contig(x, codebooks)
-    nb, ns, stride, D = x.shape
+    _dtype_code(x)
+    _need_contig(x)
+    nb, ns, stride, D = _dims(x, "x", 4)
+    _expect(codebooks, "codebooks", torch.float32, ndim=5)
     _, S, G, C, dsub = codebooks.shape
+    _expect(codebooks, "codebooks", torch.float32, (nb, S, G, C, D // G if G else 0))
+    if G * dsub != D:
+        raise ValueError(f"codebooks [n_books][S][G][C][dsub] must have G * dsub = D = {D}")
     n_rows = stride if n_rows is None else n_rows
     vq = VqDesc(D, G, S, C)
     if codes is None:
         codes = torch.empty((nb, ns, n_rows, S, G), dtype=torch.uint8, device=x.device)
-    _need_contig(codes)
+    _expect(codes, "codes", torch.uint8, (nb, ns, n_rows, S, G))
+    _workspace(workspace)
+    _same_device(x, x=x, codebooks=codebooks, codes=codes, workspace=workspace, smooth=smooth)
     need = encode_workspace_size(D, G, S, C, nb)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
@@ -381,16 +465,20 @@ def decode_reconstruct(codes, codebooks, *, unrotate=False, out=None, smooth=Non
     [n_books][n_seq][n_rows][S][G]); the output is the original domain,
     factors times the unrotated sum (kvq_decode_reconstruct_smooth)."""
     torch = _torch()
-    _need_contig(codes, codebooks)
+    _expect(codebooks, "codebooks", torch.float32, ndim=5)
     nb, S, G, C, dsub = codebooks.shape
     D = G * dsub
+    _expect(codes, "codes", torch.uint8)
+    if codes.dim() < 3 or codes.shape[0] != nb or tuple(codes.shape[-2:]) != (S, G):
+        raise ValueError(f"codes must be [{nb}][...][{S}][{G}], got {tuple(codes.shape)}")
     if smooth is not None:
         if codes.dim() != 5:
             raise ValueError("smooth=: codes must be [n_books][n_seq][n_rows][S][G]")
         _, ns, nr = codes.shape[:3]
         if out is None:
             out = torch.empty((nb, ns, nr, D), dtype=torch.float32, device=codes.device)
-        _need_contig(out)
+        _expect(out, "out", torch.float32, (nb, ns, nr, D))
+        _same_device(codes, codes=codes, codebooks=codebooks, out=out, smooth=smooth)
         sd = _smooth_desc(smooth, nb, D)
         vq = VqDesc(D, G, S, C)
         _check(_lib().kvq_decode_reconstruct_smooth(_ptr(codes), ctypes.byref(vq), nb, ns, nr,
@@ -401,7 +489,8 @@ def decode_reconstruct(codes, codebooks, *, unrotate=False, out=None, smooth=Non
     per_book = codes.numel() // (nb * S * G) if codes.numel() else 0
     if out is None:
         out = torch.empty(codes.shape[:-2] + (D,), dtype=torch.float32, device=codes.device)
-    _need_contig(out)
+    _expect(out, "out", torch.float32, tuple(codes.shape[:-2]) + (D,))
+    _same_device(codes, codes=codes, codebooks=codebooks, out=out)
     vq = VqDesc(D, G, S, C)
     _check(_lib().kvq_decode_reconstruct(_ptr(codes), ctypes.byref(vq), nb, per_book,
                                       _ptr(codebooks), _ptr(out),
@@ -435,6 +524,41 @@ def cache_bytes(B, Hq, Hkv, D, Tc, W, S, G, C) -> dict:
             "dense": v[3].value}
 
 
+def _attend_args(q, k_codes, v_codes, k_cb, v_cb, k_win, v_win, out, scale, n_code, n_window):
+    """Checks the decode call's tensors against each other and returns its
+    descriptor: q [B][Hq][D] f32, k/v_codes [B][Hkv][Tcap][S][G] u8, k/v_cb
+    [S][G][C][D/G] f32, k/v_win [B][Hkv][Wcap][D] f16 (both or neither),
+    out [B][Hq][D] f32 (None: the caller allocates it)."""
+    torch = _torch()
+    _expect(q, "q", torch.float32, ndim=3)
+    B, Hq, D = q.shape
+    _expect(k_codes, "k_codes", torch.uint8, ndim=5)
+    _, Hkv, Tcap, S, G = k_codes.shape
+    _expect(k_codes, "k_codes", torch.uint8, (B, Hkv, Tcap, S, G))
+    _expect(v_codes, "v_codes", torch.uint8, (B, Hkv, Tcap, S, G))
+    if G <= 0 or D % G:
+        raise ValueError(f"the code groups G = {G} must divide the head dimension D = {D}")
+    _expect(k_cb, "k_cb", torch.float32, ndim=4)
+    C = k_cb.shape[2]
+    _expect(k_cb, "k_cb", torch.float32, (S, G, C, D // G))
+    _expect(v_cb, "v_cb", torch.float32, (S, G, C, D // G))
+    if (k_win is None) != (v_win is None):
+        raise ValueError("k_win and v_win go together")
+    Wcap = 0
+    if k_win is not None:
+        _expect(k_win, "k_win", torch.float16, ndim=4)
+        Wcap = k_win.shape[2]
+        _expect(k_win, "k_win", torch.float16, (B, Hkv, Wcap, D))
+        _expect(v_win, "v_win", torch.float16, (B, Hkv, Wcap, D))
+    if out is not None:
+        _expect(out, "out", torch.float32, (B, Hq, D))
+    _same_device(q, q=q, k_codes=k_codes, v_codes=v_codes, k_cb=k_cb, v_cb=v_cb, k_win=k_win,
+                 v_win=v_win, out=out)
+    Tc = Tcap if n_code is None else int(n_code)
+    W = Wcap if n_window is None else int(n_window)
+    return _attn_desc(B, Hq, Hkv, D, Tc, W, S, G, C, scale, Tcap, Wcap)
+
+
 def attend_decode(q, k_codes, v_codes, k_cb, v_cb, k_win=None, v_win=None, *, scale=None,
                   out=None, workspace=None, n_code=None, n_window=None, k_smooth=None):
     """q [B][Hq][D] f32; k/v_codes [B][Hkv][Tcap][S][G] u8; k/v_cb [S][G][C][dsub]
@@ -443,14 +567,10 @@ def attend_decode(q, k_codes, v_codes, k_cb, v_cb, k_win=None, v_win=None, *, sc
     ``k_smooth``: f32 [n_scale][D] factors the coded keys were divided by
     (kvq_attend_decode_smooth).  Returns f32 [B][Hq][D]."""
     torch = _torch()
-    _need_contig(q, k_codes, v_codes, k_cb, v_cb, k_win, v_win)
+    _workspace(workspace)
+    a = _attend_args(q, k_codes, v_codes, k_cb, v_cb, k_win, v_win, out, scale, n_code, n_window)
+    _same_device(q, workspace=workspace, k_smooth=k_smooth)
     B, Hq, D = q.shape
-    _, Hkv, Tcap, S, G = k_codes.shape
-    C = k_cb.shape[2]
-    Wcap = 0 if k_win is None else k_win.shape[2]
-    Tc = Tcap if n_code is None else int(n_code)
-    W = Wcap if n_window is None else int(n_window)
-    a = _attn_desc(B, Hq, Hkv, D, Tc, W, S, G, C, scale, Tcap, Wcap)
     sz = ctypes.c_size_t(0)
     _check(_lib().kvq_attend_workspace_size(ctypes.byref(a), ctypes.byref(sz)),
            "kvq_attend_workspace_size")
@@ -458,10 +578,6 @@ def attend_decode(q, k_codes, v_codes, k_cb, v_cb, k_win=None, v_win=None, *, sc
         workspace = torch.empty(max(sz.value, 16), dtype=torch.uint8, device=q.device)
     if out is None:
         out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
-    _need_contig(out)
-    for w in (k_win, v_win):
-        if w is not None and w.dtype != torch.float16:
-            raise TypeError("window tensors must be float16")
     if k_smooth is not None:
         sd = _smooth_desc(k_smooth, 1, D)
         _check(_lib().kvq_attend_decode_smooth(ctypes.byref(a), _ptr(q), _ptr(k_codes),
@@ -486,14 +602,9 @@ def attend_decode_noalloc(q, k_codes, v_codes, k_cb, v_cb, k_win=None, v_win=Non
     """kvq_attend_decode_noalloc: attend_decode without a workspace (the
     library's per-GPU array of NOALLOC_SCRATCH_BYTES).  ``out`` [B][Hq][D] f32
     is required, so this call allocates nothing."""
-    _need_contig(q, k_codes, v_codes, k_cb, v_cb, k_win, v_win, out)
-    B, Hq, D = q.shape
-    _, Hkv, Tcap, S, G = k_codes.shape
-    C = k_cb.shape[2]
-    Wcap = 0 if k_win is None else k_win.shape[2]
-    Tc = Tcap if n_code is None else int(n_code)
-    W = Wcap if n_window is None else int(n_window)
-    a = _attn_desc(B, Hq, Hkv, D, Tc, W, S, G, C, scale, Tcap, Wcap)
+    if out is None:
+        raise ValueError("out is required")
+    a = _attend_args(q, k_codes, v_codes, k_cb, v_cb, k_win, v_win, out, scale, n_code, n_window)
     _check(_lib().kvq_attend_decode_noalloc(ctypes.byref(a), _ptr(q), _ptr(k_codes),
                                             _ptr(v_codes), _ptr(k_cb), _ptr(v_cb), _ptr(k_win),
                                             _ptr(v_win), _ptr(out), _stream(q)),
@@ -505,11 +616,12 @@ def window_append(k_new, v_new, k_win, v_win, n_window):
     """Write one token per (sequence, KV head), k/v_new [B][Hkv][D] f16, into
     row n_window of the window buffers k/v_win [B][Hkv][Wcap][D] f16."""
     torch = _torch()
-    _need_contig(k_new, v_new, k_win, v_win)
-    for t in (k_new, v_new, k_win, v_win):
-        if t.dtype != torch.float16:
-            raise TypeError("window tensors must be float16")
+    _expect(k_win, "k_win", torch.float16, ndim=4)
     B, Hkv, Wcap, D = k_win.shape
+    _expect(v_win, "v_win", torch.float16, (B, Hkv, Wcap, D))
+    _expect(k_new, "k_new", torch.float16, (B, Hkv, D))
+    _expect(v_new, "v_new", torch.float16, (B, Hkv, D))
+    _same_device(k_win, k_new=k_new, v_new=v_new, k_win=k_win, v_win=v_win)
     _check(_lib().kvq_window_append(B, Hkv, D, Wcap, int(n_window), _ptr(k_new), _ptr(v_new),
                                     _ptr(k_win), _ptr(v_win), _stream(k_win)),
            "kvq_window_append")
@@ -533,13 +645,22 @@ def window_flush(k_win, v_win, n_window, n_flush, k_codes, v_codes, n_code, k_cb
     f32 [n_scale][D] factors the flushed keys are divided by
     (kvq_window_flush_smooth)."""
     torch = _torch()
-    _need_contig(k_win, v_win, k_codes, v_codes, k_cb, v_cb)
-    for t in (k_win, v_win):
-        if t.dtype != torch.float16:
-            raise TypeError("window tensors must be float16")
+    _expect(k_win, "k_win", torch.float16, ndim=4)
     B, Hkv, Wcap, D = k_win.shape
-    _, _, Tcap, S, G = k_codes.shape
+    _expect(v_win, "v_win", torch.float16, (B, Hkv, Wcap, D))
+    _expect(k_codes, "k_codes", torch.uint8, ndim=5)
+    Tcap, S, G = k_codes.shape[2:]
+    _expect(k_codes, "k_codes", torch.uint8, (B, Hkv, Tcap, S, G))
+    _expect(v_codes, "v_codes", torch.uint8, (B, Hkv, Tcap, S, G))
+    if G <= 0 or D % G:
+        raise ValueError(f"the code groups G = {G} must divide the head dimension D = {D}")
+    _expect(k_cb, "k_cb", torch.float32, ndim=4)
     C = k_cb.shape[2]
+    _expect(k_cb, "k_cb", torch.float32, (S, G, C, D // G))
+    _expect(v_cb, "v_cb", torch.float32, (S, G, C, D // G))
+    _workspace(workspace)
+    _same_device(k_win, k_win=k_win, v_win=v_win, k_codes=k_codes, v_codes=v_codes, k_cb=k_cb,
+                 v_cb=v_cb, workspace=workspace, k_smooth=k_smooth)
     vq = VqDesc(D, G, S, C)
     need = window_flush_workspace_size(D, G, S, C)
     if packed and workspace is None:

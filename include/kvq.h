@@ -60,7 +60,11 @@ extern "C" {
 #define KVQ_API __attribute__((visibility("default")))
 #endif
 
-typedef enum {
+/* Status codes, element types and level kinds are plain 32-bit integers with
+ * named values (not enum types), so any value a caller passes is data that a
+ * call checks and rejects, never an out-of-range enum. */
+typedef int32_t kvq_status;
+enum {
   KVQ_OK = 0,
   KVQ_ERR_NULL = 1,        /* a required pointer is NULL                      */
   KVQ_ERR_SHAPE = 2,       /* sizes inconsistent or out of range              */
@@ -69,9 +73,10 @@ typedef enum {
   KVQ_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required         */
   KVQ_ERR_DTYPE = 6,       /* unknown element type                            */
   KVQ_ERR_HIP = 7          /* a HIP launch failed; see kvq_last_hip_error()   */
-} kvq_status;
+};
 
-typedef enum { KVQ_F32 = 0, KVQ_BF16 = 1, KVQ_F16 = 2 } kvq_dtype;
+typedef int32_t kvq_dtype;
+enum { KVQ_F32 = 0, KVQ_BF16 = 1, KVQ_F16 = 2 };
 
 /* Quantiser shape.  head_dim D in {64, 128, 256}; n_groups G divides D;
  * dsub = D/G a power of two in [8, 128]; 1 <= n_stages S <= 8;
@@ -389,7 +394,8 @@ KVQ_API kvq_status kvq_codebook_fit(const void* x, kvq_dtype xt, const kvq_vq_de
  * with vq = {D, G = D*b/8, S = 2, C = 256} (b in {1, 2}: the decode needs at
  * least 4 dims per group).
  * ------------------------------------------------------------------------ */
-typedef enum { KVQ_LEVELS_GAUSSIAN = 0, KVQ_LEVELS_LAPLACIAN = 1 } kvq_levels_kind;
+typedef int32_t kvq_levels_kind;
+enum { KVQ_LEVELS_GAUSSIAN = 0, KVQ_LEVELS_LAPLACIAN = 1 };
 
 /* Host call (no GPU): the 2^bits levels (ascending) of the Lloyd-Max
  * quantiser for the unit-variance Gaussian or Laplacian density, iterated to a
