@@ -9,14 +9,16 @@
       mean per-dispatch value of every counter of the run for each kernel.
 
   python -m compressed_attention_fwht_amd.profsummary traffic \\
-      --fetch FETCH_COUNTER_CSV --write WRITE_COUNTER_CSV --kernel NAME \\
-      --source FILE.hip --copy-bytes N --cmd-fetch "..." --cmd-write "..." \\
+      --fetch FETCH_COUNTER_CSV --write WRITE_COUNTER_CSV --kernel "NAME[;NAME...]" \\
+      --source "FILE[;FILE...]" --copy-bytes N --cmd-fetch "..." --cmd-write "..." \\
       --out FILE.md
       FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of kernel NAME, each scaled
       by what the same counter reads for a plain device copy of N bytes (the
       largest __amd_rocclr_copyBuffer dispatches of the run), giving HBM bytes
-      per launch; the result goes into a JSON block with the SHA-256 of the
-      kernel's source so a reader can tell whether it still applies.
+      per launch; with several names, the sum of their per-dispatch means (the
+      kernels of one call, each launched once per call).  The result goes into
+      a JSON block with the SHA-256 of every source file the kernels are built
+      from, so a reader can tell whether it still applies.
 
 Host-side text processing only; nothing here touches the GPU.
 """
@@ -76,17 +78,23 @@ def _copy_kib(vals):
 def traffic(args):
     fv = _per_dispatch(args.fetch, "FETCH_SIZE")
     wv = _per_dispatch(args.write, "WRITE_SIZE")
-    f_k, nf = _kernel_mean(fv, args.kernel)
-    w_k, nw = _kernel_mean(wv, args.kernel)
+    keys = args.kernel.split(";")
+    per_f = [_kernel_mean(fv, k) for k in keys]
+    per_w = [_kernel_mean(wv, k) for k in keys]
+    f_k, nf = sum(m for m, _ in per_f), [n for _, n in per_f]
+    w_k, nw = sum(m for m, _ in per_w), [n for _, n in per_w]
     f_c, ncf = _copy_kib(fv)
     w_c, ncw = _copy_kib(wv)
     ff = args.copy_bytes / (f_c * 1024.0)
     fw = args.copy_bytes / (w_c * 1024.0)
     fetch_b = f_k * 1024.0 * ff
     write_b = w_k * 1024.0 * fw
-    sha = hashlib.sha256(open(os.path.join(CSRC, args.source), "rb").read()).hexdigest()
-    d = {"kernel": args.kernel, "source": args.source, "source_sha256": sha,
+    shas = {src: hashlib.sha256(open(os.path.join(CSRC, src), "rb").read()).hexdigest()
+            for src in args.source.split(";")}
+    d = {"kernel": args.kernel, "sources_sha256": shas,
          "fetch_kib_per_dispatch": round(f_k, 1), "write_kib_per_dispatch": round(w_k, 1),
+         "per_kernel_kib": {k: [round(f, 1), round(w, 1)]
+                            for k, (f, _), (w, _) in zip(keys, per_f, per_w)},
          "dispatches": {"fetch_run": nf, "write_run": nw},
          "copy_bytes": args.copy_bytes,
          "copy_fetch_kib": round(f_c, 1), "copy_write_kib": round(w_c, 1),

@@ -61,18 +61,62 @@ def test_traffic_scaling_by_the_copy_calibration(tmp_path):
     assert d["traffic_bytes_per_launch"] == round(1100.0 * 2048 + 500.0 * 1024)
     assert d["traffic_over_algorithmic"] == pytest.approx(
         (1100.0 * 2048 + 500.0 * 1024) / 1_000_000, abs=1e-3)
-    assert len(d["source_sha256"]) == 64
+    assert list(d["sources_sha256"]) == ["rotate.hip"]
+    assert len(d["sources_sha256"]["rotate.hip"]) == 64
 
 
-def test_stale_profile_is_not_used(monkeypatch):
+def test_traffic_sums_the_kernels_of_one_call(tmp_path):
+    """Several kernel names: the per-launch bytes are the sum of each kernel's
+    mean per dispatch (one launch of each per call), every source hashed."""
+    n = 1 << 28
+    fetch = tmp_path / "fetch.csv"
+    write = tmp_path / "write.csv"
+    _counter_csv(fetch, "FETCH_SIZE", [
+        ("__amd_rocclr_copyBuffer", n / 1024), ("void kvq::prep_kernel<16>()", 100.0),
+        ("void kvq::chunk_kernel<16>()", 2000.0), ("void kvq::chunk_kernel<16>()", 2200.0),
+        ("void kvq::merge_kernel()", 10.0)])
+    _counter_csv(write, "WRITE_SIZE", [
+        ("__amd_rocclr_copyBuffer", n / 1024), ("void kvq::prep_kernel<16>()", 50.0),
+        ("void kvq::chunk_kernel<16>()", 30.0), ("void kvq::merge_kernel()", 4.0)])
+    out = tmp_path / "t.md"
+    args = types.SimpleNamespace(fetch=str(fetch), write=str(write),
+                                 kernel="prep_kernel;chunk_kernel;merge_kernel",
+                                 source="attend.hip;attend_rc.hip", copy_bytes=n,
+                                 algorithmic_bytes=0, title="t", cmd_fetch="f", cmd_write="w",
+                                 out=str(out))
+    profsummary.traffic(args)
+    d = json.loads(re.search(r"```json\n(.*?)\n```", out.read_text(), re.S).group(1))
+    assert d["fetch_bytes_per_launch"] == round((100.0 + 2100.0 + 10.0) * 1024)
+    assert d["write_bytes_per_launch"] == round((50.0 + 30.0 + 4.0) * 1024)
+    assert d["dispatches"]["fetch_run"] == [1, 2, 1]
+    assert set(d["sources_sha256"]) == {"attend.hip", "attend_rc.hip"}
+
+
+def test_stale_profile_is_not_used(monkeypatch, tmp_path):
     """bench.profiled_traffic reports no traffic for a summary whose recorded
-    source hash differs from the source as it stands."""
+    hash of any of its sources differs from that source as it stands."""
     sys.path.insert(0, ROOT)
     import bench
-    names = [f for f in os.listdir(bench.PROFILES) if f.startswith("encode_mfma_kernel")]
-    assert names, "the encode kernel's counter summary is committed"
-    monkeypatch.setattr(bench, "source_sha", lambda name: "0" * 64)
-    traffic, fn = bench.profiled_traffic("encode_mfma_kernel", "encode.hip")
-    assert traffic is None and fn == names[0]
-    monkeypatch.setattr(bench, "PROFILES", os.path.join(ROOT, "no-such-folder"))
-    assert bench.profiled_traffic("encode_mfma_kernel", "encode.hip") == (None, None)
+    shas = {s: bench.source_sha(s) for s in bench.DECODE_SOURCES}
+    (tmp_path / "d.md").write_text("# t\n\n```json\n" + json.dumps(
+        {"traffic_bytes_per_launch": 123, "sources_sha256": shas}) + "\n```\n")
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    assert bench.profiled_traffic("d.md", bench.DECODE_SOURCES) == (123, "d.md")
+    real = bench.source_sha
+    monkeypatch.setattr(bench, "source_sha",
+                        lambda name: "0" * 64 if name == "attend_common.h" else real(name))
+    assert bench.profiled_traffic("d.md", bench.DECODE_SOURCES) == (None, "d.md")
+    assert bench.profiled_traffic("missing.md", bench.DECODE_SOURCES) == (None, None)
+
+
+def test_committed_headline_summaries_name_their_sources():
+    """The counter summaries the bench line reads exist and hash the sources
+    the bench checks them against."""
+    import bench
+    for fname, sources in ((bench.DECODE_TRAFFIC, bench.DECODE_SOURCES),
+                           (bench.ENCODE_TRAFFIC, bench.ENCODE_SOURCES)):
+        path = os.path.join(bench.PROFILES, fname)
+        if not os.path.exists(path):
+            pytest.skip(f"{fname} not taken yet")
+        d = json.loads(re.search(r"```json\n(.*?)\n```", open(path).read(), re.S).group(1))
+        assert set(d["sources_sha256"]) == set(sources)

@@ -507,10 +507,16 @@ def test_decode_attention_sink_chunks(key, delta, every):
     say("   ", res, "output spread", round(float(spread), 3))
     assert res["ok"], res
 
-# ------------------------------------------------- full sizes (sampled encode)
+# ------------------------------------------------------------- full sizes
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("key", [2, 3, 4])
-def test_full_size_encode_sampled_and_decode(key):
-    say(f"full-size workload {key}: encode (sampled check) + decode")
+def test_full_size_encode_and_decode(key):
+    """Full-size decode workloads: the K book's codes checked against the
+    oracle for every coded vector of the layer (the check split over worker
+    processes), the V book's on every 97th vector, then decode over the
+    GPU's codes."""
+    from parallel_check import check_codes_all
+    say(f"full-size workload {key}: encode (K book every vector, V book every 97th) + decode")
     w = synth.workload(key)
     inp = synth.make_inputs(w)
     Tc = w.code_tokens
@@ -522,10 +528,14 @@ def test_full_size_encode_sampled_and_decode(key):
     for b in range(2):
         flat = codes_np[b].reshape(-1, w.n_stages, w.n_groups)
         xs = inp["x_f32"][b][:, :Tc].reshape(-1, w.head_dim)
-        idx = np.arange(0, flat.shape[0], 97)
-        res = oracle.check_codes(xs[idx].astype(np.float64), inp["cb"][b], flat[idx])
+        if b == 0:
+            res = check_codes_all(xs, inp["cb"][b], flat)
+            assert res["total"] == xs.shape[0] * w.n_stages * w.n_groups
+        else:
+            idx = np.arange(0, flat.shape[0], 97)
+            res = oracle.check_codes(xs[idx].astype(np.float64), inp["cb"][b], flat[idx])
         say("   book", b, {k: res[k] for k in ("total", "exact", "near_tie", "hard")})
-        assert res["hard"] == 0
+        assert res["hard"] == 0, res["hard_examples"]
     res = _decode_case(w, inp, codes_np[0], codes_np[1])
     say("   decode", res)
     assert res["ok"], res
