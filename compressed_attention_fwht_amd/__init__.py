@@ -319,9 +319,10 @@ def lloyd_max(kind, bits):
     return list(lv), d.value
 
 
-def _scalar_bits(bits):
-    if bits not in (1, 2, 4):
-        raise ValueError(f"bits must be 1, 2 or 4, got {bits}")
+def _scalar_bits(bits, product=False):
+    ok = (1, 2, 4) if product else (1, 2, 3, 4)
+    if bits not in ok:
+        raise ValueError(f"bits must be one of {ok}, got {bits}")
 
 
 def scalar_encode(x, levels, bits, *, n_rows=None, pre_rotated=False, codes=None):
@@ -374,7 +375,7 @@ def scalar_product_codebook(levels, bits, head_dim, out=None):
     """The product codebook f32 [2][D*bits/8][256][8/bits] of one book's levels
     [2][2^bits]; with it kvq_attend_decode reads packed scalar codes."""
     torch = _torch()
-    _scalar_bits(bits)
+    _scalar_bits(bits, product=True)
     _expect(levels, "levels", torch.float32, (2, 1 << bits))
     G, k = head_dim * bits // 8, 8 // bits
     if out is None:

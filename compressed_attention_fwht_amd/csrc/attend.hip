@@ -782,12 +782,43 @@ __global__ __launch_bounds__(CH_THREADS, 1) void attn_chunk_kernel(
 
   // ---- o_rot[r][g*dsub + j] = 2^-F sum_s sum_c W[s][g][c][r] * C^V_sg[c][j].
   // Item (s, codeword part, 4 consecutive dims): float4 codebook loads,
-  // histogram entries broadcast to the lanes sharing a codeword.
+  // histogram entries broadcast to the lanes sharing a codeword.  Groups of
+  // 2 dims (4-bit scalar codes through their product codebook) take items of
+  // one group each, with float2 loads.
   const int dsub = D / G;
   constexpr int D4 = D / 4;
   const int P = cparts;
   const int cper = (C + P - 1) / P;
-  for (int it = tid; it < S * P * D4; it += CH_THREADS) {
+  if (dsub == 2) {
+    constexpr int D2 = D / 2;
+    for (int it = tid; it < S * P * D2; it += CH_THREADS) {
+      const int g = it % D2;
+      const int rest = it / D2;
+      const int pi = rest % P, s = rest / P;
+      const int sg = s * G + g;
+      const int c0 = pi * cper, c1 = (c0 + cper) < C ? (c0 + cper) : C;
+      float acc[RP][2];
+#pragma unroll
+      for (int r = 0; r < RP; ++r) acc[r][0] = acc[r][1] = 0.0f;
+      const float* cvp = vcb + (int64_t)sg * C * 2;
+      const uint32_t* hp = tabu + sg * hist_stride(C, RP);
+#pragma unroll 16
+      for (int c = c0; c < c1; ++c) {
+        const float2 cv = *reinterpret_cast<const float2*>(cvp + (int64_t)c * 2);
+#pragma unroll
+        for (int r = 0; r < RP; ++r) {
+          const float w = (float)hp[hist_bin<RP>(c, r, C)];
+          acc[r][0] = __builtin_fmaf(w, cv.x, acc[r][0]);
+          acc[r][1] = __builtin_fmaf(w, cv.y, acc[r][1]);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < RP; ++r)
+        *reinterpret_cast<float2*>(cpart + ((s * P + pi) * RP + r) * D + 2 * g) =
+            make_float2(acc[r][0], acc[r][1]);
+    }
+  }
+  for (int it = tid; dsub >= 4 && it < S * P * D4; it += CH_THREADS) {
     const int d4 = it % D4;
     const int rest = it / D4;
     const int pi = rest % P, s = rest / P;

@@ -43,7 +43,7 @@ kvq_status hip_status(hipError_t e) {
 
 kvq_status check_attn(const kvq_attn_desc* a, kvq::AttnPlan* plan) {
   if (!a) return KVQ_ERR_NULL;
-  kvq_status st = check_vq(&a->vq, 4);
+  kvq_status st = check_vq(&a->vq, 2);      // 2-dim groups: 4-bit scalar codes
   if (st != KVQ_OK) return st;
   if (a->batch < 1 || a->n_q_heads < 1 || a->n_kv_heads < 1) return KVQ_ERR_SHAPE;
   if (a->n_q_heads % a->n_kv_heads != 0) return KVQ_ERR_SHAPE;
@@ -261,7 +261,9 @@ kvq_status kvq_lloyd_max(kvq_levels_kind kind, int32_t bits, double* levels,
   return KVQ_OK;
 }
 
-static bool scalar_bits_ok(int bits) { return bits == 1 || bits == 2 || bits == 4; }
+// codes of 1..4 bits; the product codebook needs whole elements per byte
+static bool scalar_bits_ok(int bits) { return bits >= 1 && bits <= 4; }
+static bool product_bits_ok(int bits) { return bits == 1 || bits == 2 || bits == 4; }
 
 kvq_status kvq_scalar_encode(const void* x, kvq_dtype xt, int32_t head_dim, int32_t bits,
                              int64_t n_books, int64_t n_seq, int64_t seq_stride, int64_t n_rows,
@@ -304,7 +306,7 @@ kvq_status kvq_scalar_decode_reconstruct(const uint8_t* codes, int32_t head_dim,
 kvq_status kvq_scalar_product_codebook(int32_t head_dim, int32_t bits, const float* levels,
                                        float* codebooks, hipStream_t stream) {
   if (head_dim != 64 && head_dim != 128 && head_dim != 256) return KVQ_ERR_SHAPE;
-  if (!scalar_bits_ok(bits)) return KVQ_ERR_SHAPE;
+  if (!product_bits_ok(bits)) return KVQ_ERR_SHAPE;
   if (!levels || !codebooks) return KVQ_ERR_NULL;
   if (!aligned16(levels) || !aligned16(codebooks)) return KVQ_ERR_ALIGN;
   return hip_status(kvq::launch_scalar_product_cb(levels, head_dim, bits, codebooks, stream));

@@ -9,12 +9,14 @@
 // dsa.bit_pack sub-byte packing.
 //
 // Codes: a vector's row is [stage-1 bytes][stage-2 bytes], D*b/8 bytes each;
-// element i of a stage sits in bits [(i mod k)*b, ...) of byte i / k (k = 8/b,
-// least significant first).  A byte of stage s therefore is a code of the
-// product codebook whose entry c lists levels_s[(c >> j*b) & (2^b - 1)] for
-// j < k -- scalar_product_cb_kernel writes it, so the decode-attention kernels
-// read packed scalar codes as ordinary product codes (G = D*b/8 groups of k
-// dims, C = 256).
+// a stage is one bit string, least significant bit first: bit t of element i
+// is bit i*b + t of the stage's bytes.  For b in {1, 2, 4} element i sits in
+// bits [(i mod k)*b, ...) of byte i / k (k = 8/b), so a byte of stage s is a
+// code of the product codebook whose entry c lists levels_s[(c >> j*b) &
+// (2^b - 1)] for j < k -- scalar_product_cb_kernel writes it, and the
+// decode-attention kernels read packed scalar codes as ordinary product codes
+// (G = D*b/8 groups of k dims, C = 256).  For b = 3 elements straddle bytes:
+// encode and reconstruction only.
 //
 // Layout per lane as elsewhere: L = D/8 lanes per row, 8 consecutive elements
 // per lane, so a lane's indices fill b whole bytes per stage.  HBM-bound:
@@ -226,6 +228,12 @@ __global__ __launch_bounds__(256) void scalar_encode_kernel(
         } else if constexpr (B == 2) {
           *reinterpret_cast<uint16_t*>(rowp) = (uint16_t)p1[u];
           *reinterpret_cast<uint16_t*>(rowp + SB) = (uint16_t)p2[u];
+        } else if constexpr (B == 3) {                // 3 bytes at an odd offset for odd col
+#pragma unroll
+          for (int i = 0; i < 3; ++i) {
+            rowp[i] = (uint8_t)(p1[u] >> (8 * i));
+            rowp[SB + i] = (uint8_t)(p2[u] >> (8 * i));
+          }
         } else {
           *reinterpret_cast<uint32_t*>(rowp) = p1[u];
           *reinterpret_cast<uint32_t*>(rowp + SB) = p2[u];
@@ -243,10 +251,13 @@ __global__ __launch_bounds__(256) void scalar_encode_kernel(
 // in 4*B consecutive bits of the packed row.
 template <int B>
 __device__ __forceinline__ uint32_t scalar_bits4(const uint8_t* __restrict__ rowp, int d0) {
-  const int bit = d0 * B;                               // 4*B bits from here, 4*B | 8 or = 4
+  const int bit = d0 * B;                               // 4*B bits from here (d0 % 4 == 0)
   if constexpr (B == 1) return (uint32_t)(rowp[bit >> 3] >> (bit & 7)) & 15u;
   else if constexpr (B == 2) return rowp[bit >> 3];
-  else return *reinterpret_cast<const uint16_t*>(rowp + (bit >> 3));
+  else if constexpr (B == 3) {                          // 12 bits from bit 0 or 4 of a byte
+    const uint32_t two = (uint32_t)rowp[bit >> 3] | ((uint32_t)rowp[(bit >> 3) + 1] << 8);
+    return (two >> (bit & 7)) & 0xfffu;
+  } else return *reinterpret_cast<const uint16_t*>(rowp + (bit >> 3));
 }
 
 template <int D, int B>
@@ -348,11 +359,12 @@ hipError_t launch_scalar_encode(const void* x, int xt, int D, int bits, int64_t 
                                                                  pre_rotated, dm, dsh);    \
     return hipGetLastError();                                                              \
   }
-#define KVQ_SE_D(DD)                                                                      \
-  KVQ_SE(DD, 0, 1) KVQ_SE(DD, 0, 2) KVQ_SE(DD, 0, 4) KVQ_SE(DD, 1, 1) KVQ_SE(DD, 1, 2)     \
-  KVQ_SE(DD, 1, 4) KVQ_SE(DD, 2, 1) KVQ_SE(DD, 2, 2) KVQ_SE(DD, 2, 4)
+#define KVQ_SE_X(DD, XX)                                                                  \
+  KVQ_SE(DD, XX, 1) KVQ_SE(DD, XX, 2) KVQ_SE(DD, XX, 3) KVQ_SE(DD, XX, 4)
+#define KVQ_SE_D(DD) KVQ_SE_X(DD, 0) KVQ_SE_X(DD, 1) KVQ_SE_X(DD, 2)
   KVQ_SE_D(64) KVQ_SE_D(128) KVQ_SE_D(256)
 #undef KVQ_SE_D
+#undef KVQ_SE_X
 #undef KVQ_SE
   return hipErrorInvalidValue;
 }
@@ -368,8 +380,8 @@ hipError_t launch_scalar_reconstruct(const uint8_t* codes, int D, int bits, int6
                                                                   unrotate);               \
     return hipGetLastError();                                                              \
   }
-  KVQ_SR(64, 1) KVQ_SR(64, 2) KVQ_SR(64, 4) KVQ_SR(128, 1) KVQ_SR(128, 2) KVQ_SR(128, 4)
-  KVQ_SR(256, 1) KVQ_SR(256, 2) KVQ_SR(256, 4)
+  KVQ_SR(64, 1) KVQ_SR(64, 2) KVQ_SR(64, 3) KVQ_SR(64, 4) KVQ_SR(128, 1) KVQ_SR(128, 2)
+  KVQ_SR(128, 3) KVQ_SR(128, 4) KVQ_SR(256, 1) KVQ_SR(256, 2) KVQ_SR(256, 3) KVQ_SR(256, 4)
 #undef KVQ_SR
   return hipErrorInvalidValue;
 }

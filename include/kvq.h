@@ -382,17 +382,20 @@ KVQ_API kvq_status kvq_codebook_fit(const void* x, kvq_dtype xt, const kvq_vq_de
  * stage-2 Laplacian Lloyd-Max, the indices only, decode by summing the two
  * levels and unrotating; throughput journey -- the index counted over decision
  * boundaries instead of an argmin; module table -- dsa.bit_pack sub-byte
- * index packing).  bits b in {1, 2, 4}: 2^b levels per stage.
+ * index packing; the allocator's bit choices include 3 bits).  bits b in
+ * 1..4: 2^b levels per stage.
  *
  * Codes: a vector's row is [stage-1 bytes][stage-2 bytes], D*b/8 bytes each;
- * element i of a stage occupies bits [(i mod k)*b, (i mod k)*b + b) of byte
- * i / k, k = 8/b, least significant first.  Levels: float32
- * [n_books][2][2^b], each stage's levels strictly increasing (stage 1 for the
- * rotated element, stage 2 for its residual); other orders give unspecified
- * codes (no fault).  A byte of stage s is also a code of the product codebook
+ * each stage is one bit string, least significant bit first: bit t of element
+ * i is bit i*b + t of the stage's bytes (for b in {1, 2, 4}: bits
+ * [(i mod k)*b, (i mod k)*b + b) of byte i / k, k = 8/b; for b = 3 an element
+ * may straddle two bytes).  Levels: float32 [n_books][2][2^b], each stage's
+ * levels strictly increasing (stage 1 for the rotated element, stage 2 for
+ * its residual); other orders give unspecified codes (no fault).  For b in
+ * {1, 2, 4} a byte of stage s is also a code of the product codebook
  * kvq_scalar_product_codebook writes, so kvq_attend_decode reads scalar codes
- * with vq = {D, G = D*b/8, S = 2, C = 256} (b in {1, 2}: the decode needs at
- * least 4 dims per group).
+ * with vq = {D, G = D*b/8, S = 2, C = 256}; 3-bit codes have no whole
+ * elements per byte and are encoded and reconstructed only.
  * ------------------------------------------------------------------------ */
 typedef int32_t kvq_levels_kind;
 enum { KVQ_LEVELS_GAUSSIAN = 0, KVQ_LEVELS_LAPLACIAN = 1 };
@@ -425,7 +428,8 @@ KVQ_API kvq_status kvq_scalar_decode_reconstruct(const uint8_t* codes, int32_t h
                                          hipStream_t stream);
 
 /* codebooks[s][g][c][j] = levels[s][(c >> j*b) & (2^b - 1)] for s < 2,
- * g < D*b/8, c < 256, j < 8/b (one book's levels [2][2^b]). */
+ * g < D*b/8, c < 256, j < 8/b (one book's levels [2][2^b]); b in {1, 2, 4}
+ * (b = 3 is KVQ_ERR_SHAPE). */
 KVQ_API kvq_status kvq_scalar_product_codebook(int32_t head_dim, int32_t bits,
                                        const float* levels, float* codebooks,
                                        hipStream_t stream);

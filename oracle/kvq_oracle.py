@@ -468,23 +468,31 @@ def scalar_rvq_encode(x, levels1, levels2, *, rotate: bool = True):
 
 
 def pack_bits(z, bits: int):
-    """Sub-byte packing of indices z [..., D] (values < 2^bits, bits in
-    {1, 2, 4}): element i goes to bits [(i mod k)*bits, ...) of byte i // k,
-    k = 8 / bits (least significant first).  Returns uint8 [..., D*bits/8]."""
-    z = np.asarray(z, dtype=np.uint32)
-    k = 8 // bits
-    zz = z.reshape(z.shape[:-1] + (z.shape[-1] // k, k))
-    shifts = (np.arange(k) * bits).astype(np.uint32)
-    return (zz << shifts).sum(axis=-1).astype(np.uint8)
+    """Sub-byte packing of indices z [..., D] (values < 2^bits, bits 1..4,
+    D * bits a multiple of 8) as one least-significant-first bit string per
+    row: bit t of element i is bit 8 * j + k of the row's bytes, where
+    i * bits + t = 8 * j + k.  For bits 1, 2 and 4 element i fills bits
+    [(i mod k) * bits, ...) of byte i // k (k = 8 / bits); for 3 bits an
+    element can straddle two bytes.  Returns uint8 [..., D*bits/8]."""
+    z = np.asarray(z, dtype=np.uint8)
+    D = z.shape[-1]
+    if (D * bits) % 8:
+        raise ValueError("D * bits must fill whole bytes")
+    t = np.arange(bits, dtype=np.uint8)
+    stream = (z[..., :, None] >> t) & 1                      # [..., D, bits]: bit t of z_i
+    stream = stream.reshape(z.shape[:-1] + (D * bits // 8, 8))
+    weights = (1 << np.arange(8)).astype(np.uint32)
+    return (stream.astype(np.uint32) * weights).sum(axis=-1).astype(np.uint8)
 
 
 def unpack_bits(codes, bits: int):
     """Inverse of pack_bits: uint8 [..., B] -> indices [..., B*8/bits]."""
-    c = np.asarray(codes, dtype=np.uint32)
-    k = 8 // bits
-    shifts = (np.arange(k) * bits).astype(np.uint32)
-    z = (c[..., None] >> shifts) & ((1 << bits) - 1)
-    return z.reshape(c.shape[:-1] + (c.shape[-1] * k,)).astype(np.uint8)
+    c = np.asarray(codes, dtype=np.uint8)
+    nbytes = c.shape[-1]
+    stream = (c[..., :, None] >> np.arange(8, dtype=np.uint8)) & 1     # [..., B, 8]
+    stream = stream.reshape(c.shape[:-1] + (nbytes * 8 // bits, bits))
+    weights = (1 << np.arange(bits)).astype(np.uint32)
+    return (stream.astype(np.uint32) * weights).sum(axis=-1).astype(np.uint8)
 
 
 def scalar_reconstruct(z1, z2, levels1, levels2, *, unrotate: bool = True):

@@ -361,7 +361,8 @@ def test_scalar_argument_errors():
         L.kvq_scalar_encode(x, xt, D, b, nb, ns, st, nr, lv, c, fl, None)
     assert enc(xt=4) == DTYPE
     assert enc(D=96) == SHAPE
-    assert enc(b=3) == SHAPE                           # packing covers 1, 2, 4 bits
+    assert enc(b=5) == SHAPE                           # packing covers 1..4 bits
+    assert enc(b=0) == SHAPE
     assert enc(nr=65) == SHAPE
     assert enc(fl=0x2) == SHAPE
     assert enc(lv=0) == NULL
@@ -375,12 +376,18 @@ def test_scalar_argument_errors():
     assert rec(n=0, o=0) == OK
     assert L.kvq_scalar_product_codebook(128, 3, FAKE, FAKE, None) == SHAPE
     assert L.kvq_scalar_product_codebook(128, 2, FAKE, 0, None) == NULL
-    # decode attention accepts 4-dim groups (2-bit scalar codes), not 2-dim ones
+    # decode attention accepts 4-dim groups (2-bit scalar codes) and 2-dim ones
+    # (4-bit codes: one head per block, the 128-group table fills the LDS), not 1-dim
     sz = ctypes.c_size_t(0)
     a4 = kvq.AttnDesc(1, 4, 1, 100, 0, kvq.VqDesc(128, 32, 2, 256), 0.0, 0, 0)
     assert L.kvq_attend_workspace_size(ctypes.byref(a4), ctypes.byref(sz)) == OK
     a2 = kvq.AttnDesc(1, 4, 1, 100, 0, kvq.VqDesc(128, 64, 2, 256), 0.0, 0, 0)
-    assert L.kvq_attend_workspace_size(ctypes.byref(a2), ctypes.byref(sz)) == SHAPE
+    assert L.kvq_attend_workspace_size(ctypes.byref(a2), ctypes.byref(sz)) == OK
+    a1 = kvq.AttnDesc(1, 4, 1, 100, 0, kvq.VqDesc(128, 128, 2, 256), 0.0, 0, 0)
+    assert L.kvq_attend_workspace_size(ctypes.byref(a1), ctypes.byref(sz)) == SHAPE
+    # 2-dim groups of a 256-dim head need a 256 KiB table: no kernel
+    a3 = kvq.AttnDesc(1, 4, 1, 100, 0, kvq.VqDesc(256, 128, 2, 256), 0.0, 0, 0)
+    assert L.kvq_attend_workspace_size(ctypes.byref(a3), ctypes.byref(sz)) == UNSUP
     # the encode still needs 8 dims per group
     vq4 = kvq.VqDesc(128, 32, 2, 256)
     assert L.kvq_encode(FAKE, 1, ctypes.byref(vq4), 1, 1, 64, 64, FAKE, FAKE, 0, FAKE, 1 << 30,

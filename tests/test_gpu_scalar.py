@@ -74,7 +74,7 @@ def book_levels(xf, bits):
     (3, dict(batch=2, tokens=700, window=64)),
     (1, dict()),                                # fp32, D = 64
 ])
-@pytest.mark.parametrize("bits", [1, 2, 4])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
 def test_scalar_encode_parity(key, over, bits):
     say(f"scalar encode workload {key} {over} bits {bits}")
     w = synth.workload(key, **over)
@@ -116,7 +116,7 @@ def test_scalar_encode_pre_rotated_and_f16():
             assert res["hard"] == 0
 
 
-@pytest.mark.parametrize("bits", [1, 2, 4])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
 @pytest.mark.parametrize("D", [64, 128, 256])
 def test_scalar_reconstruct_parity(bits, D):
     say(f"scalar reconstruct D {D} bits {bits}")
@@ -150,6 +150,9 @@ def test_scalar_product_codebook_exact(bits):
     (2, dict(tokens=3000, window=128), 2),      # 32 groups of 4 dims
     (3, dict(batch=3, tokens=2100, window=64), 2),
     (1, dict(tokens=1500, window=0), 1),        # D = 64
+    (2, dict(tokens=3000, window=128), 4),      # 64 groups of 2 dims: one head per block
+    (3, dict(batch=2, tokens=1800, window=64), 4),
+    (1, dict(tokens=1500, window=0), 4),        # D = 64, 32 groups of 2 dims
 ])
 def test_scalar_decode_through_product_codebook(key, over, bits):
     say(f"scalar decode workload {key} {over} bits {bits}")

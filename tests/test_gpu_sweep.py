@@ -153,7 +153,7 @@ def test_scalar_sweep(case):
     reconstruction bit-exact (rotated) / within 1e-6 * |x_hat| (unrotated)."""
     rng = np.random.default_rng(4000 + case)
     D = int(rng.choice([64, 128, 256]))
-    bits = int(rng.choice([1, 2, 4]))
+    bits = int(rng.choice([1, 2, 3, 4]))
     nb = int(rng.integers(1, 4))
     n = int(rng.choice([1, int(rng.integers(2, 300)), int(rng.integers(300, 3000))]))
     dt = [torch.float32, torch.bfloat16, torch.float16][int(rng.integers(0, 3))]

@@ -669,8 +669,16 @@ def test_pack_bits_hand_fixture_and_roundtrip():
     assert oracle.pack_bits(np.array([[1, 0, 1, 1, 0, 0, 0, 1]]), 1)[0, 0] == 0x8D
     assert oracle.pack_bits(np.array([[3, 0, 1, 2]]), 2)[0, 0] == 0x93
     assert oracle.pack_bits(np.array([[0xA, 0x5]]), 4)[0, 0] == 0x5A
+    # 3 bits: elements 5, 3, 6, 1, 7, 0, 2, 4 give the bit string (each element
+    # least significant bit first) 101 110 011 100 111 000 010 001, i.e. the
+    # bytes (first bit = bit 0) 10111001, 11001110, 00010001 = 0x9D, 0x73, 0x88;
+    # the same as the little-endian bytes of sum z_i * 8^i = 0x88739D
+    z3 = np.array([[5, 3, 6, 1, 7, 0, 2, 4]])
+    assert sum(int(v) << (3 * i) for i, v in enumerate(z3[0])) == 0x88739D
+    assert list(oracle.pack_bits(z3, 3)[0]) == [0x9D, 0x73, 0x88]
+    assert np.array_equal(oracle.unpack_bits(np.array([[0x9D, 0x73, 0x88]], dtype=np.uint8), 3), z3)
     rng = np.random.default_rng(42)
-    for bits in (1, 2, 4):
+    for bits in (1, 2, 3, 4):
         z = rng.integers(0, 2 ** bits, size=(7, 128))
         p = oracle.pack_bits(z, bits)
         assert p.shape == (7, 128 * bits // 8)
