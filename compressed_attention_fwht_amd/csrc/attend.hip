@@ -427,9 +427,10 @@ __global__ __launch_bounds__(CH_THREADS, 1) void attn_chunk_kernel(
   // Prefetches are issued unconditionally, rows past the chunk clamped to its
   // last one: vector loads complete in order, and a load that may or may not
   // have been issued makes later waits drain everything in flight.  A block
-  // that builds its LUT loads its V rows at the start too; one that stages a
-  // prepared LUT waits for all its loads once (the LDS copy), so its V rows
-  // follow pass 1 instead.
+  // that builds its LUT issues its K and V rows right after the query and
+  // codebook loads the table needs; one that stages a prepared LUT issues its
+  // K rows first and waits for all its loads once (the LDS copy), so its V
+  // rows follow pass 1 instead.
   constexpr int SGW = SGC ? SGC / 16 : 1;
   constexpr int KP = SGC ? (128 / SGC < CH_TPT ? 128 / SGC : CH_TPT) : 0;
   constexpr int KPA = KP ? KP : 1;
@@ -443,7 +444,7 @@ __global__ __launch_bounds__(CH_THREADS, 1) void attn_chunk_kernel(
       }
     }
   };
-  prefetch_rows(kcodes, cpre);
+  if constexpr (!FUSE) prefetch_rows(kcodes, cpre);
 
   if constexpr (FUSE) {
     // ---- build this unit's LUT in LDS: scale * H q / sqrt(D) for the RP
@@ -455,7 +456,6 @@ __global__ __launch_bounds__(CH_THREADS, 1) void attn_chunk_kernel(
     // halves of 4 (both in flight across the q rotation), each half of the
     // next pass issued across the arithmetic of the current one.
     __shared__ float qs[RP][D];
-    prefetch_rows(vcodes, vpre);
     constexpr int QROWS = 64 / L;                       // q rows per wave-wide load
     constexpr int QIT = (RP + QROWS - 1) / QROWS;
     float qraw[QIT][8];
@@ -499,6 +499,11 @@ __global__ __launch_bounds__(CH_THREADS, 1) void attn_chunk_kernel(
       fac[i][0] = f0.x; fac[i][1] = f0.y; fac[i][2] = f0.z; fac[i][3] = f0.w;
       fac[i][4] = f1.x; fac[i][5] = f1.y; fac[i][6] = f1.z; fac[i][7] = f1.w;
     }
+    // the code rows go out after the query, codebook and factor loads:
+    // loads complete in order, so the rotation and the table wait for
+    // those alone while the rows stream in
+    prefetch_rows(kcodes, cpre);
+    prefetch_rows(vcodes, vpre);
 #pragma unroll
     for (int i = 0; i < QIT; ++i) {
       const int r = i * QROWS + lane / L;

@@ -303,52 +303,44 @@ __global__ __launch_bounds__(64 * mf_waves<S>(), 8 / mf_waves<S>()) void encode_
         __builtin_memcpy(&A1, &a1, 16);
         __builtin_memcpy(&A2, &a2, 16);
       };
-      auto issue = [&](const bf16x8_t& A1, const bf16x8_t& A2, const bf16x8_t& B1,
-                       const bf16x8_t& B2, f32x16_t& c) {
-        const f32x16_t z = {0};
-        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A1, B1, z, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A2, B2, c, 0, 0, 0);
-      };
       // The packed index (32t | row) comes from a scalar register, so each
       // candidate costs one v_and_or_b32; accumulator register i holds codeword
       // row 8*(i/4) + 4*h + (i%4) of the tile (h is or-ed in after the loop).
-      auto reduce = [&](int t, const f32x16_t& c, int& best) {
+      // One call reduces 8 of a tile's 16 candidates.
+      auto reduce8 = [&](int t, const f32x16_t& c, int& best, int lo) {
         const uint32_t tb = (uint32_t)__builtin_amdgcn_readfirstlane(t << 5);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
+        for (int i = lo; i < lo + 8; ++i) {
           const uint32_t idx = tb | (uint32_t)(8 * (i >> 2) + (i & 3));
           best = min(best, (int)((__float_as_uint(c[i]) & keep_hi) | idx));
         }
       };
-      if constexpr (S == 1) {
-        // the halves staggered: one half's MFMAs run while the other half's
-        // previous results are reduced (fits the registers for one stage)
-        bf16x8_t A1, A2;
-        f32x16_t acc0, acc1;
-        load_a(0, A1, A2);
-        issue(A1, A2, B1T0, B2T0, acc0);
-        issue(A1, A2, B1T1, B2T1, acc1);
+      // The halves staggered: one half's MFMA pair is issued before the other
+      // half's previous tile is reduced, so the reduction never waits for the
+      // MFMAs just issued.
+      bf16x8_t A1, A2;
+      f32x16_t acc0, acc1;
+      const f32x16_t zero = {0};
+      load_a(0, A1, A2);
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A1, B1T0, zero, 0, 0, 0);
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A2, B2T0, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A1, B1T1, zero, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A2, B2T1, acc1, 0, 0, 0);
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const bool more = t + 1 < 8;
-          if (more) load_a(t + 1, A1, A2);
-          reduce(t, acc0, best0);
-          if (more) issue(A1, A2, B1T0, B2T0, acc0);
-          reduce(t, acc1, best1);
-          if (more) issue(A1, A2, B1T1, B2T1, acc1);
+      for (int t = 0; t < 8; ++t) {
+        const bool more = t + 1 < 8;
+        if (more) load_a(t + 1, A1, A2);
+        reduce8(t, acc0, best0, 0);
+        reduce8(t, acc0, best0, 8);
+        if (more) {
+          acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A1, B1T0, zero, 0, 0, 0);
+          acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A2, B2T0, acc0, 0, 0, 0);
         }
-      } else {
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          bf16x8_t P1, P2;
-          load_a(t, P1, P2);
-          const f32x16_t z = {0};
-          f32x16_t c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(P1, B1T0, z, 0, 0, 0);
-          f32x16_t c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(P1, B1T1, z, 0, 0, 0);
-          c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(P2, B2T0, c0, 0, 0, 0);
-          c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(P2, B2T1, c1, 0, 0, 0);
-          reduce(t, c0, best0);
-          reduce(t, c1, best1);
+        reduce8(t, acc1, best1, 0);
+        reduce8(t, acc1, best1, 8);
+        if (more) {
+          acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A1, B1T1, zero, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A2, B2T1, acc1, 0, 0, 0);
         }
       }
       best0 |= h << 2;
