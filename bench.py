@@ -292,7 +292,7 @@ def layer_report(torch, kvq, L, enc_ms, rec_ms, att_ms, flush, reps, graphs=True
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this build runs on one GPU only (no multi-GPU path); use --gpus 1",
+        print("bench.py: the library runs on one GPU only (no multi-GPU path); use --gpus 1",
               file=sys.stderr)
         sys.exit(2)
     import torch

@@ -128,7 +128,7 @@ const char* kvq_status_string(kvq_status s) {
     case KVQ_OK: return "ok";
     case KVQ_ERR_NULL: return "a required pointer is NULL";
     case KVQ_ERR_SHAPE: return "sizes are inconsistent or out of range";
-    case KVQ_ERR_UNSUPPORTED: return "valid request with no kernel in this build";
+    case KVQ_ERR_UNSUPPORTED: return "valid request the library has no kernel for";
     case KVQ_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case KVQ_ERR_WORKSPACE: return "workspace missing or too small";
     case KVQ_ERR_DTYPE: return "unknown element type";

@@ -68,7 +68,7 @@ enum {
   KVQ_OK = 0,
   KVQ_ERR_NULL = 1,        /* a required pointer is NULL                      */
   KVQ_ERR_SHAPE = 2,       /* sizes inconsistent or out of range              */
-  KVQ_ERR_UNSUPPORTED = 3, /* valid request this build has no kernel for      */
+  KVQ_ERR_UNSUPPORTED = 3, /* valid request the library has no kernel for    */
   KVQ_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                */
   KVQ_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required         */
   KVQ_ERR_DTYPE = 6,       /* unknown element type                            */

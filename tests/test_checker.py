@@ -36,7 +36,7 @@ def test_near_tie_is_accepted_and_far_choice_is_hard():
 
 
 def test_teacher_forcing_follows_the_candidate():
-    """After an accepted near tie at stage 0, stage 1 is judged from the
+    """After an accepted near tie at stage 0, stage 1 is checked from the
     candidate's residual, where the candidate's stage-1 code is exact."""
     cb = np.zeros((2, 1, 2, 2))
     cb[0, 0, 0] = [1.0, 0.0]
