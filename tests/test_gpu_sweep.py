@@ -86,6 +86,46 @@ def test_decode_sweep(case):
     assert res["ok"], res
 
 
+@pytest.mark.parametrize("case", list(range(16)))
+def test_rotated_code_decode_sweep(case):
+    """The cache shape of the rotated-code kernels (128-dim heads, 16 groups of
+    8, C = 256, two or four stages, at least two query heads per KV head):
+    head groups of 1-4 heads (GQA 2-8, head splits with a ragged last one),
+    coded lengths from a single token to several chunks with a ragged tail,
+    no window, short windows riding on the chunk blocks and long ones in
+    blocks of their own, the factors of the dual transform on some cases."""
+    rng = np.random.default_rng(3000 + case)
+    D, G, C, dsub = 128, 16, 256, 8
+    S = int(rng.choice([2, 4]))
+    B = int(rng.integers(1, 4))
+    Hkv = int(rng.choice([1, 2, 4]))
+    R = int(rng.choice([2, 3, 4, 5, 7, 8]))
+    Tc = int(rng.choice([1, int(rng.integers(2, 1100)), int(rng.integers(1100, 9000))]))
+    W = int(rng.choice([0, int(rng.integers(1, 64)), int(rng.integers(300, 1200))]))
+    smooth = bool(rng.integers(0, 4) == 0)
+    say(f"rotated-code decode sweep case {case}: S {S} B {B} Hkv {Hkv} GQA {R} Tc {Tc} W {W} "
+        f"smooth {smooth}")
+    Hq = Hkv * R
+    q = rng.standard_normal((B, Hq, D)).astype(np.float32)
+    kcb = (rng.standard_normal((S, G, C, dsub)) / np.sqrt(dsub)
+           * (0.5 ** np.arange(S))[:, None, None, None]).astype(np.float32)
+    vcb = (rng.standard_normal((S, G, C, dsub)) / np.sqrt(dsub)
+           * (0.5 ** np.arange(S))[:, None, None, None]).astype(np.float32)
+    kc = rng.integers(0, C, size=(B, Hkv, Tc, S, G), dtype=np.uint8)
+    vc = rng.integers(0, C, size=(B, Hkv, Tc, S, G), dtype=np.uint8)
+    kw = rng.standard_normal((B, Hkv, W, D)).astype(np.float16) if W else None
+    vw = rng.standard_normal((B, Hkv, W, D)).astype(np.float16) if W else None
+    lam = rng.uniform(0.5, 2.0, size=(1, D)).astype(np.float32) if smooth else None
+    got = kvq.attend_decode(cuda(q), cuda(kc), cuda(vc), cuda(kcb), cuda(vcb),
+                            None if kw is None else cuda(kw), None if vw is None else cuda(vw),
+                            k_smooth=None if lam is None else cuda(lam)).cpu().numpy()
+    ref = oracle.attend(q, kc, vc, kcb, vcb, kw, vw,
+                        k_smooth=None if lam is None else lam.astype(np.float64))
+    res = oracle.check_attn(got, ref)
+    say("   ", {k: res[k] for k in ("ok", "max_abs", "rel_l2")})
+    assert res["ok"], res
+
+
 @pytest.mark.parametrize("case", list(range(20)))
 def test_reconstruct_sweep(case):
     rng = np.random.default_rng(2000 + case)
