@@ -14,8 +14,12 @@ Inputs are resident in HBM before timing.  The codebooks are packed into the
 encode workspace once at set-up (they are constants of the layer, like
 weights); each step's encode reads the packed copy, and the packing pass,
 left out of the step, is timed on its own and reported beside the encode.
-A 512 MB write before the encode and before the decode evicts the 256 MB
-Infinity Cache, so both read HBM.
+Before the encode and before the decode the caches are evicted clean: a
+512 MB write replaces every line of the 256 MB Infinity Cache and the L2s,
+then a 512 MB read of a second buffer writes those dirty lines back and
+leaves clean ones, so each call reads its inputs from HBM and no write-back
+of other data shares HBM with it.  The decode after the write alone (dirty
+lines still cached) is reported beside it as ``dirty_eviction_us``.
 
 Prints ONE JSON line.  ``value`` is the long-context decode's effective
 bandwidth (code + window + LUT bytes over the decode call's time: LUT and
@@ -70,7 +74,8 @@ def parse():
                    help="skip the 32-layer bulk prefill encode measurement")
     p.add_argument("--no-flush", action="store_true")
     p.add_argument("--step-only", action="store_true",
-                   help="time the main step only (no secondary workloads, prefill, streaming, "
+                   help="time the main step only (no graph replays, dirty-eviction decode, "
+                        "secondary workloads, prefill, streaming, "
                         "dual-transform, fitting, scalar or rotation legs), so a profiler sees "
                         "only the step's kernels")
     p.add_argument("--prefill-only", action="store_true",
@@ -249,6 +254,21 @@ def graph_replay_us(torch, L, flush, reps):
     return round(float(np.median(gts)) * 1e3, 2)
 
 
+def decode_after(torch, L, evict, reps):
+    """Median decode call time (us) with ``evict`` run before each call."""
+    ts = []
+    for i in range(reps + 3):
+        evict(i)
+        e0, e1 = cuda_events(torch, 2)
+        e0.record()
+        L.decode()
+        e1.record()
+        torch.cuda.synchronize()
+        if i >= 3:
+            ts.append(e0.elapsed_time(e1))
+    return round(float(np.median(ts)) * 1e3, 2)
+
+
 def layer_report(torch, kvq, L, enc_ms, rec_ms, att_ms, flush, reps, graphs=True):
     w = L.w
     att_s = float(np.median(att_ms)) * 1e-3
@@ -313,8 +333,14 @@ def main():
         return
 
     flush_buf = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+    clean_buf = torch.zeros(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
 
     def flush(i):
+        if not args.no_flush:
+            flush_buf.fill_(float(i))
+            clean_buf.sum()
+
+    def flush_dirty(i):
         if not args.no_flush:
             flush_buf.fill_(float(i))
 
@@ -337,6 +363,8 @@ def main():
 
     main_rep = layer_report(torch, kvq, L, enc_ms, rec_ms, att_ms, flush, args.steps,
                             graphs=not args.step_only)
+    if not args.step_only:
+        main_rep["decode"]["dirty_eviction_us"] = decode_after(torch, L, flush_dirty, args.steps)
     if not args.step_only:
         main_rep["decode"]["layers_graph"] = decode_layers_graph(
             torch, kvq, L.q, L.kc, L.vc, L.cb, L.kw, L.vw, L.out, L.att_ws, flush, L.eff_b,
@@ -397,7 +425,7 @@ def main():
             for k in ("smooth", "fit", "scalar", "rotate", "stream"):
                 res[k]["layer"] = A.name() + tag
             del A, aux
-        del flush_buf
+        del flush_buf, clean_buf
         torch.cuda.empty_cache()
         if not args.no_prefill:
             pre = prefill_encode(torch, kvq, synth, dev)

@@ -256,7 +256,19 @@ __global__ __launch_bounds__(RC_THREADS, 1) void attn_rc_kernel(
   float (*red_l)[4] = reinterpret_cast<float (*)[4]>(smem + Gm::TAB + NW * 16);
   uint32_t (*red_w)[4] = reinterpret_cast<uint32_t (*)[4]>(smem + Gm::TAB + 2 * NW * 16);
 
-  const int ci = blockIdx.x, unit = blockIdx.y, b = blockIdx.z;
+  // Workgroups are handed to the eight XCDs round-robin by linear id; the
+  // ids are renumbered so that each XCD runs whole units (all chunks of a
+  // few (sequence, KV head) pairs), so its L2 holds those units' tables only.
+  int ci, unit, b;
+  {
+    const int nx = gridDim.x, ny = gridDim.y, nb = nx * ny * gridDim.z;
+    int lin = blockIdx.x + nx * (blockIdx.y + ny * blockIdx.z);
+    if ((nb & 7) == 0) lin = (lin & 7) * (nb >> 3) + (lin >> 3);
+    ci = lin % nx;
+    const int rest = lin / nx;
+    unit = rest % ny;
+    b = rest / ny;
+  }
   const int kv = unit / n_hsplit, hs = unit - kv * n_hsplit;
   const int R = Hq / Hkv;
   const int h0 = kv * R + hs * 4;
