@@ -575,6 +575,20 @@ __global__ __launch_bounds__(RC_THREADS, 1) void attn_rc_kernel(
 #pragma unroll
     for (int k = 0; k < RC_TPT; ++k) {
       if (k + PF < RC_TPT) load_seg(vcodes, k + PF, seg, RB[(k + PF) % NB]);
+      // the token's code bytes in visiting order, formed (and marked used)
+      // ahead of the skip test: with its first use inside the branch the
+      // compiler sinks the row's load (a read-only argument, so no barrier
+      // orders it) past the barrier into the branch
+      uint32_t e4s[2][NJ][2];
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj)
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            e4s[kc][jj][q] = codes4(RB[k % NB], kc, jj, q);
+            asm volatile("" ::"v"(e4s[kc][jj][q]));
+          }
       if ((W0[k] | W1[k]) != 0ull) {
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc)
@@ -582,7 +596,7 @@ __global__ __launch_bounds__(RC_THREADS, 1) void attn_rc_kernel(
           for (int jj = 0; jj < NJ; ++jj)
 #pragma unroll
           for (int q = 0; q < 2; ++q) {
-            const uint32_t e4 = codes4(RB[k % NB], kc, jj, q);
+            const uint32_t e4 = e4s[kc][jj][q];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const uint32_t a = __builtin_amdgcn_perm(e4, LV[kc][q][i >> 1], SA[i][jj]);
