@@ -1,5 +1,5 @@
 // Decode attention over uint8 codes for the common cache shape -- head_dim
-// 128, 16 groups of 8 dims, C = 256 codewords, 1, 2 or 4 stages -- with LDS
+// 128, 16 groups of 8 dims, C = 256 codewords, 2 or 4 stages -- with LDS
 // tables laid out so that code-driven gathers and histogram atomics never
 // collide on a bank.
 //
@@ -27,13 +27,13 @@
 // 16 lanes of a quarter sit on 16 different slots, for any codes.
 //
 // Geometry.  A code row (S*G bytes, [stage][group]) is cut into segments of
-// 32 bytes (two stages; the whole 16-byte row for one stage); one segment's
-// table lives in LDS at a time: LUT entries [region][c][slot] of 16 bytes,
-// histogram bins [region][c][pair][slot] of 8 bytes, a region being 64 KiB
-// (c at bits 8-15 of the LDS address).  A segment is two units (16 or 8
-// bytes) of 4 or 2 dwords; the byte e = 16u + 4d + i of a two-stage segment
-// (unit u, dword d, byte i) sits in region d >> 1, slot 8u + 4(d & 1) + i; the
-// byte e = 8u + 4d + i of a one-stage row in region 0, slot e.
+// 32 bytes (two stages); one segment's table lives in LDS at a time: LUT
+// entries [region][c][slot] of 16 bytes, histogram bins [region][c][pair][slot]
+// of 8 bytes, a region being 64 KiB (c at bits 8-15 of the LDS address).  A
+// segment is two units of 16 bytes (4 dwords); the byte e = 16u + 4d + i of a
+// segment (unit u, dword d, byte i) sits in region d >> 1, slot 8u + 4(d & 1)
+// + i.  (One-stage caches, whose 16-byte rows would need one region only, run
+// faster on attend.hip's kernel and are not routed here.)
 //
 // The rotation moves no data.  Lane p loads unit (kc ^ p0) into unit slot kc
 // (p0 = p & 1: the address does it); for step (kc, jj, q) a first
@@ -97,34 +97,19 @@ __device__ __forceinline__ void lds_sync() {
 
 template <int SG>
 struct RcGeom {
-  static constexpr int NSEG = SG == 16 ? 1 : SG / 32;   // table segments per row
-  static constexpr int SEGB = SG == 16 ? 16 : 32;       // code bytes per segment
+  static_assert(SG == 32 || SG == 64, "two or four stages of 16 groups");
+  static constexpr int NSEG = SG / 32;                  // table segments per row
+  static constexpr int SEGB = 32;                       // code bytes per segment
   static constexpr int UNITB = SEGB / 2;                // bytes per unit
   static constexpr int UDW = UNITB / 4;                 // dwords per unit
-  static constexpr int TAB = SG == 16 ? 65536 : 131072; // LDS table bytes per segment
-  static constexpr int NPART = SG == 16 ? 16 : 32;      // contraction partials per group
+  static constexpr int TAB = 131072;                    // LDS table bytes per segment
+  static constexpr int NPART = 32;                      // contraction partials per group
 };
 
 // Region and slot of segment byte e.
-template <int SG>
-__host__ __device__ constexpr int rc_region(int e) {
-  return SG == 16 ? 0 : ((e >> 2) & 3) >> 1;
-}
-template <int SG>
+__host__ __device__ constexpr int rc_region(int e) { return ((e >> 2) & 3) >> 1; }
 __host__ __device__ constexpr int rc_slot(int e) {
-  return SG == 16 ? e : 8 * (e >> 4) + 4 * ((e >> 2) & 1) + (e & 3);
-}
-
-// Table byte offset (within its segment) of entry (segment byte e, codeword c).
-template <int SG>
-__host__ __device__ constexpr uint32_t rc_entry(int e, int c) {
-  if constexpr (SG == 16) {
-    return (uint32_t)c * 256u + (uint32_t)e * 16u;
-  } else {
-    const int u = e >> 4, d = (e >> 2) & 3, i = e & 3;
-    return (uint32_t)(d >> 1) * 65536u + (uint32_t)c * 256u +
-           (uint32_t)(8 * u + 4 * (d & 1) + i) * 16u;
-  }
+  return 8 * (e >> 4) + 4 * ((e >> 2) & 1) + (e & 3);
 }
 
 // --------------------------------------------------------- attn_rc_prep
@@ -148,7 +133,7 @@ __global__ __launch_bounds__(512) void attn_rc_prep_kernel(
     float scale, const float* __restrict__ ksm, int64_t ksm_rows) {
   using Gm = RcGeom<SG>;
   constexpr int D = 128, L = 16;
-  constexpr int NREG = SG == 16 ? 1 : 2;
+  constexpr int NREG = 2;
   constexpr int LB_PER_UNIT = Gm::NSEG * NREG * 4;      // (segment, region, codeword quarter)
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ float qs[4][D];
@@ -160,10 +145,10 @@ __global__ __launch_bounds__(512) void attn_rc_prep_kernel(
   if (bid >= nlb && bid < nlb + SG / 2) {               // V codebook -> contraction order
     const int row = (bid - nlb) * 512 + tid;             // (sg, c), one 8-float row each
     const int sg = row >> 8, c = row & 255;
-    const int seg = SG == 16 ? 0 : sg >> 5, e = SG == 16 ? sg : sg & 31;
+    const int seg = sg >> 5, e = sg & 31;
     const float4* src = reinterpret_cast<const float4*>(vcb + (int64_t)row * 8);
     float4* dst = reinterpret_cast<float4*>(
-        cvt + ((((int64_t)seg * 256 + c) * NREG + rc_region<SG>(e)) * 16 + rc_slot<SG>(e)) * 8);
+        cvt + ((((int64_t)seg * 256 + c) * NREG + rc_region(e)) * 16 + rc_slot(e)) * 8);
     dst[0] = src[0];
     dst[1] = src[1];
     return;
@@ -189,7 +174,7 @@ __global__ __launch_bounds__(512) void attn_rc_prep_kernel(
   const int slot = tid & 15;
   // the segment byte e of (region, slot): inverse of rc_region / rc_slot
   const int u = slot >> 3, i = slot & 3;
-  const int e = SG == 16 ? slot : 16 * u + 4 * (2 * region + ((slot >> 2) & 1)) + i;
+  const int e = 16 * u + 4 * (2 * region + ((slot >> 2) & 1)) + i;
   const int sg = seg * 32 + e;
   const int g = sg & 15;
   // codebook rows first: their loads are in flight across the query rotation
@@ -316,7 +301,7 @@ __global__ __launch_bounds__(RC_THREADS, 1) void attn_rc_kernel(
   // i ^ (p >> 2); LK / LV hold the two slot offsets (16- and 8-byte
   // entries) of the lane's step (unit slot kc, q, i >> 1) and the region
   // bytes 0 and 1; SA[i][jj] picks the slot offset by bit 0 of i ^ (p >> 2),
-  // the code byte i, and region jj (0 for one stage).
+  // the code byte i, and region jj.
   constexpr int NJ = UDW / 2;                           // dword pairs per unit
   uint32_t SE[2], SA[4][NJ];
 #pragma unroll
@@ -330,7 +315,7 @@ __global__ __launch_bounds__(RC_THREADS, 1) void attn_rc_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       SA[i][jj] = (((uint32_t)i & 1u) ^ p2) | ((4u + (uint32_t)i) << 8) |
-                  ((SG == 16 ? 12u : 2u + (uint32_t)jj) << 16) | (12u << 24);
+                  ((2u + (uint32_t)jj) << 16) | (12u << 24);
   // slot-offset constants with entry size ES (16 for the LUT, 8 for the
   // histogram), built where each pass starts
   auto slot_consts = [&](uint32_t (&L)[2][2][2], uint32_t es) {
@@ -360,13 +345,8 @@ __global__ __launch_bounds__(RC_THREADS, 1) void attn_rc_kernel(
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) {
       const uint8_t* src = row + ((uint32_t)kc ^ p0) * Gm::UNITB;
-      if constexpr (UDW == 4) {
-        const uint4 v = *reinterpret_cast<const uint4*>(src);
-        dst[kc][0] = v.x; dst[kc][1] = v.y; dst[kc][2] = v.z; dst[kc][3] = v.w;
-      } else {
-        const uint2 v = *reinterpret_cast<const uint2*>(src);
-        dst[kc][0] = v.x; dst[kc][1] = v.y;
-      }
+      const uint4 v = *reinterpret_cast<const uint4*>(src);
+      dst[kc][0] = v.x; dst[kc][1] = v.y; dst[kc][2] = v.z; dst[kc][3] = v.w;
     }
   };
   // code bytes of (unit slot kc, pair jj, member q) in visiting order
@@ -546,17 +526,11 @@ __global__ __launch_bounds__(RC_THREADS, 1) void attn_rc_kernel(
 
   // ---- V: histogram per segment, then its share of the contraction
   // contraction mapping: quarter Q = tid / 16 reads slot p of region (Q & 1)
-  // (two stages) or 0 (one stage) for its range of codewords; the slot names
-  // the (stage, group), the group is the same in every segment.
+  // for its range of codewords; the slot names the (stage, group), the group
+  // is the same in every segment.
   const int Q = tid >> 4;
-  int creg, c0, cn, ustage, grp;
-  if constexpr (SG == 16) {
-    creg = 0; cn = 4; c0 = Q * 4; ustage = 0; grp = (int)p;
-  } else {
-    creg = Q & 1; cn = 8; c0 = (Q >> 1) * 8;
-    ustage = (int)(p >> 3);
-    grp = 4 * (2 * creg + (int)((p >> 2) & 1)) + (int)(p & 3);
-  }
+  const int creg = Q & 1, cn = 8, c0 = (Q >> 1) * 8;
+  const int grp = 4 * (2 * creg + (int)((p >> 2) & 1)) + (int)(p & 3);
   uint32_t LV[2][2][2];
   slot_consts(LV, 8u);
   float o[4][8];
@@ -611,7 +585,7 @@ __global__ __launch_bounds__(RC_THREADS, 1) void attn_rc_kernel(
     // this lane's rows: histogram bins (region creg, slot p) and codebook
     // rows of its (stage, group), codewords c0 .. c0 + cn - 1, one codeword
     // ahead in flight (a rolled loop, so registers stay bounded)
-    constexpr int NREG = SG == 16 ? 1 : 2;
+    constexpr int NREG = 2;
     const uint8_t* hp = smem + creg * 65536 + c0 * 256 + p * 8;
     const float4* cp = reinterpret_cast<const float4*>(
         cvt + ((((int64_t)seg * 256 + c0) * NREG + creg) * 16 + p) * 8);
@@ -639,17 +613,12 @@ __global__ __launch_bounds__(RC_THREADS, 1) void attn_rc_kernel(
   for (int r = 0; r < 4; ++r)
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      if constexpr (SG == 16) {
-        o[r][j] = pair_sum<16>(o[r][j]);
-        o[r][j] = pair_sum<32>(o[r][j]);
-      } else {
-        o[r][j] += xor_lane<8>(o[r][j]);                // the two stages of the segment pair
-      }
+      o[r][j] += xor_lane<8>(o[r][j]);                  // the two stages of the segment pair
     }
   lds_sync();
   float* buf = reinterpret_cast<float*>(smem);          // [NPART][4][128]
-  const bool writer = SG == 16 ? lane < 16 : (p & 8) == 0;
-  const int pi = SG == 16 ? wave : (Q >> 1);
+  const bool writer = (p & 8) == 0;
+  const int pi = Q >> 1;
   if (writer) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -705,7 +674,7 @@ bool attn_rc_eligible(int D, int G, int S, int C, int Hq, int Hkv, int Tc) {
 }
 
 size_t attn_rc_table_bytes(int S) {
-  return (size_t)(S == 1 ? 65536 : 131072) * (S == 4 ? 2 : 1);
+  return (size_t)131072 * (S == 4 ? 2 : 1);
 }
 
 int attn_rc_window_slice(int W, int n_chunks) {
@@ -725,7 +694,7 @@ static hipError_t launch_rc_sg(const AttnPlan& p, int B, int Hq, int Hkv, int Tc
   const int units = B * Hkv * p.n_hsplit;
   const int nslots = p.n_chunks + p.n_wblocks;
   const size_t wl = p.n_wblocks ? ((size_t)RC_WIN_BLOCK * 4 + (size_t)8 * 4 * 128) * 4 : 0;
-  constexpr int LB_PER_UNIT = Gm::NSEG * (SG == 16 ? 1 : 2) * 4;
+  constexpr int LB_PER_UNIT = Gm::NSEG * 2 * 4;
   float* cvt = reinterpret_cast<float*>(lut + (size_t)units * p.lut_slice);
   hipError_t e;
   if (wl > 0) {
@@ -754,9 +723,7 @@ hipError_t launch_attend_rc(const AttnPlan& p, int B, int Hq, int Hkv, int S, in
                             const uint8_t* kc, const uint8_t* vc, const float* kcb,
                             const float* vcb, const uint16_t* kw, const uint16_t* vw,
                             uint8_t* lut, float* part, Smooth ksm, hipStream_t st) {
-  if (S == 1)
-    return launch_rc_sg<16>(p, B, Hq, Hkv, Tc, W, cstride, wstride, scale, q, kc, vc, kcb, vcb,
-                            kw, vw, lut, part, ksm, st);
+  if (S != 2 && S != 4) return hipErrorInvalidValue;    // the plan routes no other here
   if (S == 2)
     return launch_rc_sg<32>(p, B, Hq, Hkv, Tc, W, cstride, wstride, scale, q, kc, vc, kcb, vcb,
                             kw, vw, lut, part, ksm, st);
