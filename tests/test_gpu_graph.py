@@ -50,7 +50,8 @@ def _capture(fn):
 
 @pytest.mark.parametrize("key,over", [
     (2, dict(tokens=3000, window=128)),                  # LUT built in the chunk blocks
-    (4, dict(tokens=40000, window=256)),                 # separate LUT pass, four stages
+    (2, dict(batch=3, tokens=7000, window=128, n_stages=3)),  # LUT staged from its own pass
+    (4, dict(tokens=40000, window=256)),                 # rotated-code kernels, four stages
 ])
 def test_decode_graph_replays_match_eager(key, over):
     say(f"decode graph workload {key} {over}")

@@ -313,6 +313,36 @@ def test_decode_parity(key, over):
     assert res["ok"], res
 
 
+@pytest.mark.parametrize("B,Hkv,R,Tc,W", [
+    (3, 4, 4, 12000, 200),     # 264 chunk blocks, window slices on them
+    (3, 1, 7, 23000, 2500),    # GQA 7 in head pairs (ragged last), window blocks of their own
+])
+def test_decode_general_lut_pass(B, Hkv, R, Tc, W):
+    """Three-stage caches (outside the rotated-code kernels' shape), long
+    enough that building each unit's LUT in every chunk block would re-read
+    more than 96 MB of K codebook, so the plan stages it from attn_lut_kernel
+    (264 chunk blocks of two heads, 99 MB of re-reads)."""
+    say(f"decode through the separate LUT pass: B {B} Hkv {Hkv} GQA {R} Tc {Tc} W {W}")
+    rng = np.random.default_rng(700 + R)
+    S, D, G, C, dsub = 3, 128, 16, 256, 8
+    Hq = Hkv * R
+    q = rng.standard_normal((B, Hq, D)).astype(np.float32)
+    kcb = (rng.standard_normal((S, G, C, dsub)) / np.sqrt(dsub)
+           * (0.5 ** np.arange(S))[:, None, None, None]).astype(np.float32)
+    vcb = (rng.standard_normal((S, G, C, dsub)) / np.sqrt(dsub)
+           * (0.5 ** np.arange(S))[:, None, None, None]).astype(np.float32)
+    kc = rng.integers(0, C, size=(B, Hkv, Tc, S, G), dtype=np.uint8)
+    vc = rng.integers(0, C, size=(B, Hkv, Tc, S, G), dtype=np.uint8)
+    kw = rng.standard_normal((B, Hkv, W, D)).astype(np.float16)
+    vw = rng.standard_normal((B, Hkv, W, D)).astype(np.float16)
+    got = kvq.attend_decode(cuda(q), cuda(kc), cuda(vc), cuda(kcb), cuda(vcb), cuda(kw),
+                            cuda(vw)).cpu().numpy()
+    ref = oracle.attend(q, kc, vc, kcb, vcb, kw, vw)
+    res = oracle.check_attn(got, ref)
+    say("   ", {k: res[k] for k in ("ok", "max_abs", "rel_l2")})
+    assert res["ok"], res
+
+
 def test_decode_random_codes_and_scale():
     say("decode random codes, explicit scale, GQA 7")
     w = synth.workload(3, batch=2, tokens=1500, window=33)

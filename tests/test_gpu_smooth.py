@@ -196,11 +196,17 @@ def test_decode_smooth_parity(key, over, n_scale):
     assert res["ok"], res
 
 
-def test_decode_smooth_table_pass():
-    """A long single sequence: the tables come from the separate LUT pass
-    (building them in every chunk block would re-read too much codebook)."""
-    say("decode smooth, long context with the LUT pass (random codes)")
-    w = synth.workload(4, tokens=40000, window=256)
+@pytest.mark.parametrize("key,over", [
+    (4, dict(tokens=40000, window=256)),                 # rotated-code kernels' prep tables
+    (2, dict(batch=3, tokens=7000, window=128, n_stages=3)),  # attn_lut_kernel's tables
+])
+def test_decode_smooth_table_pass(key, over):
+    """Long caches whose tables come from a pass of their own, the factors
+    folded into the query there: the rotated-code kernels' prep kernel (four
+    stages) and attn_lut_kernel (three stages, where building the LUT in every
+    chunk block would re-read more than 96 MB of codebook)."""
+    say(f"decode smooth, tables from their own pass: workload {key} {over} (random codes)")
+    w = synth.workload(key, **over)
     inp = synth.make_inputs(w)
     lam, kcb = key_setup(w, inp, 8)
     rng = np.random.default_rng(9)
