@@ -343,6 +343,41 @@ def test_decode_general_lut_pass(B, Hkv, R, Tc, W):
     assert res["ok"], res
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,D,S,G,Tc,W", [
+    (128, 32, 8, 128, 1, 16, 70, 16),   # one stage, GQA 4: 1,024 single-chunk blocks
+    (64, 8, 8, 128, 2, 16, 70, 0),      # two stages, one query head per KV head
+    (64, 8, 8, 128, 4, 16, 40, 24),     # four stages, one query head per KV head
+    (64, 32, 8, 256, 1, 32, 50, 8),     # 256-dim heads, window in a block of its own
+    (128, 16, 8, 64, 2, 8, 60, 20),     # 64-dim heads, GQA 2
+])
+def test_decode_large_batch_lut_pass(B, Hq, Hkv, D, S, G, Tc, W):
+    """Many short sequences (a serving batch): one chunk per (sequence, KV
+    head, head split), 512-1,024 blocks, whose in-block LUT builds would
+    re-read 128-256 MB of K codebook, so the plan stages each unit's LUT from
+    attn_lut_kernel; the heads-per-block, head-size and code-row variants of
+    that path."""
+    say(f"large-batch decode through the LUT pass: B {B} Hq {Hq} Hkv {Hkv} D {D} S {S} G {G} "
+        f"Tc {Tc} W {W}")
+    rng = np.random.default_rng(900 + B + D + S)
+    C, dsub = 256, D // G
+    q = rng.standard_normal((B, Hq, D)).astype(np.float32)
+    kcb = (rng.standard_normal((S, G, C, dsub)) / np.sqrt(dsub)
+           * (0.5 ** np.arange(S))[:, None, None, None]).astype(np.float32)
+    vcb = (rng.standard_normal((S, G, C, dsub)) / np.sqrt(dsub)
+           * (0.5 ** np.arange(S))[:, None, None, None]).astype(np.float32)
+    kc = rng.integers(0, C, size=(B, Hkv, Tc, S, G), dtype=np.uint8)
+    vc = rng.integers(0, C, size=(B, Hkv, Tc, S, G), dtype=np.uint8)
+    kw = rng.standard_normal((B, Hkv, W, D)).astype(np.float16) if W else None
+    vw = rng.standard_normal((B, Hkv, W, D)).astype(np.float16) if W else None
+    got = kvq.attend_decode(cuda(q), cuda(kc), cuda(vc), cuda(kcb), cuda(vcb),
+                            None if kw is None else cuda(kw),
+                            None if vw is None else cuda(vw)).cpu().numpy()
+    ref = oracle.attend(q, kc, vc, kcb, vcb, kw, vw)
+    res = oracle.check_attn(got, ref)
+    say("   ", {k: res[k] for k in ("ok", "max_abs", "rel_l2")})
+    assert res["ok"], res
+
+
 def test_decode_random_codes_and_scale():
     say("decode random codes, explicit scale, GQA 7")
     w = synth.workload(3, batch=2, tokens=1500, window=33)
