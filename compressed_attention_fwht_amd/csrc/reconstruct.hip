@@ -508,8 +508,10 @@ hipError_t launch_reconstruct(const uint8_t* codes, const float* cb, float* out,
           codes, cb, out, n_per_book, per, G, C, dsub, unrotate, sm.f, sm.n_scale, n_rows);  \
       return hipGetLastError();                                                              \
     }
-    KVQ_RL(64, 1) KVQ_RL(128, 1) KVQ_RL(256, 1) KVQ_RL(64, 2) KVQ_RL(128, 2) KVQ_RL(256, 2)
-    KVQ_RL(64, 4) KVQ_RL(128, 4)                       // D = 256 with 4 stages: cache kernel
+    KVQ_RL(64, 1) KVQ_RL(128, 1) KVQ_RL(256, 1) KVQ_RL(64, 2) KVQ_RL(128, 2)
+    KVQ_RL(64, 4) KVQ_RL(128, 4)
+    // (D = 256 has an even group count, so its 2 and 4 stages take the half
+    // tables or, with books over 128 KiB, the cache kernel)
 #undef KVQ_RL
   }
   int64_t blocks = (n + vec_per_iter - 1) / vec_per_iter;

@@ -150,6 +150,51 @@ def test_reconstruct_sweep(case):
         assert np.max(np.abs(got_u[b] - ref_u) / nrm) <= 1e-6
 
 
+@pytest.mark.parametrize("D,dsub,S,C,nb,n", [
+    (128, 8, 3, 256, 2, 3000),        # half tables, three stages
+    (128, 128, 2, 256, 2, 2000),      # one group (odd): stage-0 book in LDS, rows staged
+    (128, 128, 4, 256, 1, 2000),
+    (64, 64, 4, 256, 2, 2000),
+    (128, 8, 5, 256, 2, 2000),        # five stages: the cache kernel
+    (64, 8, 5, 100, 2, 2000),
+    (128, 8, 1, 256, 1, 600000),      # LDS kernels whose blocks' code rows no longer fit
+    (64, 8, 1, 256, 1, 1100000),      # beside the book: rows read from global memory
+    (256, 8, 1, 128, 1, 300000),
+    (64, 64, 2, 256, 1, 4200000),
+    (128, 128, 2, 256, 1, 4300000),
+    (64, 64, 4, 256, 1, 2100000),
+    (128, 128, 4, 256, 1, 2100000),
+])
+def test_reconstruct_dispatch_variants(D, dsub, S, C, nb, n):
+    """Each reconstruction kernel variant the launcher can pick: half tables
+    at three stages, the whole stage-0 book in LDS for a single group (two
+    and four stages) with the blocks' code rows staged beside it or, for large
+    calls, read from global memory, and the cache kernel for five stages.
+    Rotated output bit-exact, unrotated within 1e-6 * |x_hat|; calls over
+    10,000 vectors per book on every 97th vector and the last."""
+    G = D // dsub
+    say(f"reconstruct variant: D {D} G {G} S {S} C {C} books {nb} n {n}")
+    rng = np.random.default_rng(4000 + D + dsub + S + nb)
+    cb = rng.standard_normal((nb, S, G, C, dsub)).astype(np.float32)
+    codes = rng.integers(0, 256, size=(nb, n, S, G), dtype=np.uint8)
+    clamped = np.minimum(codes, C - 1)
+    idx = np.arange(n) if n <= 10000 else np.r_[np.arange(0, n, 97), n - 1]
+    idx_t = torch.from_numpy(idx).cuda()
+    for unrot in (False, True):
+        got = kvq.decode_reconstruct(cuda(codes), cuda(cb), unrotate=unrot)
+        got = got[:, idx_t].cpu().numpy()
+        for b in range(nb):
+            if not unrot:
+                ref = oracle.reconstruct_rot(clamped[b][idx], cb[b])
+                assert np.array_equal(got[b], ref.astype(np.float32)), b
+            else:
+                ref = oracle.reconstruct(clamped[b][idx], cb[b])
+                nrm = np.linalg.norm(ref, axis=1, keepdims=True)
+                assert np.max(np.abs(got[b] - ref) / nrm) <= 1e-6, b
+        del got
+        torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("case", list(range(24)))
 def test_encode_sweep(case):
     """Encode shapes: every other case is an MFMA-eligible one (D = 128,
@@ -184,6 +229,45 @@ def test_encode_sweep(case):
         res = oracle.check_codes(xf[b, 0], cb[b], codes[b, 0], rotate=not pre)
         assert res["hard"] == 0, (case, b, {k: res[k] for k in ("total", "exact", "near_tie",
                                                                   "hard")})
+
+
+@pytest.mark.parametrize("D,dsub,S,C,dt,n", [
+    # MFMA kernel, batches of at least 512 tiles (each block codes all 16 groups)
+    (128, 8, 1, 256, "f16", 140000),
+    (128, 8, 2, 256, "f16", 140000),
+    (128, 8, 3, 256, "bf16", 270000),
+    (128, 8, 3, 256, "f16", 270000),
+    (128, 8, 4, 256, "f16", 270000),
+    # generic kernel, the (D, dsub) pairs not drawn by the sweep above
+    (128, 128, 2, 100, "f32", 700),
+    (128, 32, 3, 256, "bf16", 700),
+    (128, 64, 1, 16, "f16", 700),
+    (256, 16, 2, 256, "f32", 700),
+    (256, 64, 3, 100, "bf16", 700),
+    (64, 32, 2, 256, "f16", 700),
+    (64, 8, 4, 100, "f32", 700),
+])
+def test_encode_dispatch_variants(D, dsub, S, C, dt, n):
+    """Encode kernel variants the sweep's shapes do not reach: the MFMA
+    kernel's full-group instances for 2-byte inputs at 1-4 stages (checked on
+    every 97th vector and the last), and generic-kernel head and group sizes.
+    Every checked code follows the oracle's rule."""
+    G = D // dsub
+    say(f"encode variant: D {D} dsub {dsub} S {S} C {C} {dt} n {n}")
+    rng = np.random.default_rng(5000 + D + dsub + S + n)
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[dt]
+    cb = (rng.standard_normal((1, S, G, C, dsub)) / np.sqrt(dsub)
+          * (0.5 ** np.arange(S))[None, :, None, None, None]).astype(np.float32)
+    x = torch.from_numpy(rng.standard_normal((1, 1, n, D)).astype(np.float32)).to(tdt).cuda()
+    codes = kvq.encode(x, cuda(cb))
+    assert codes.shape == (1, 1, n, S, G)
+    idx = np.arange(n) if n <= 10000 else np.r_[np.arange(0, n, 97), n - 1]
+    idx_t = torch.from_numpy(idx).cuda()
+    xf = x[0, 0, idx_t].double().cpu().numpy()
+    got = codes[0, 0, idx_t].cpu().numpy()
+    res = oracle.check_codes(xf, cb[0], got)
+    say("   ", {k: res[k] for k in ("total", "exact", "near_tie", "hard")})
+    assert res["hard"] == 0, {k: res[k] for k in ("total", "exact", "near_tie", "hard")}
 
 
 @pytest.mark.parametrize("case", list(range(16)))
