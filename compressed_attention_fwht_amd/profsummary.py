@@ -4,6 +4,11 @@
       --title T --cmd "the rocprofv3 command" --out FILE.md
       per-kernel calls / average / min / max duration and share of GPU time.
 
+  python -m compressed_attention_fwht_amd.profsummary coverage KERNEL_STATS_CSV \\
+      --title T --cmd "the rocprofv3 command" --out FILE.md
+      every instance of the library's kernels the run launched (name with its
+      template arguments, the parameter list dropped) and its call count.
+
   python -m compressed_attention_fwht_amd.profsummary counters COUNTER_CSV \\
       --kernels "NAME[;NAME...]" --title T --cmd "..." --out FILE.md
       mean per-dispatch value of every counter of the run for each kernel.
@@ -47,6 +52,38 @@ def stats(args):
         lines.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
                      f"{100 * float(r['TotalDurationNs']) / total:.1f} % |")
+    open(args.out, "w").write("\n".join(lines) + "\n")
+
+
+def _instance(name):
+    """'void kvq::k<1, 2>(int, ...)' -> 'k<1, 2>'; None outside the library."""
+    name = name.replace("void ", "", 1)
+    if not name.startswith("kvq::"):
+        return None
+    name = name[len("kvq::"):]
+    depth = 0
+    for i, ch in enumerate(name):
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0:
+            return name[:i]
+    return name
+
+
+def coverage(args):
+    rows = list(csv.DictReader(open(args.csv)))
+    calls = collections.Counter()
+    for r in rows:
+        inst = _instance(r["Name"])
+        if inst is not None:
+            calls[inst] += int(r["Calls"])
+    lines = [f"# {args.title}", "", "Command:", "", "```", args.cmd, "```", "",
+             f"{len(calls)} kernel instances launched.", "",
+             "| kernel instance | calls |", "|---|---|"]
+    for k in sorted(calls):
+        lines.append(f"| `{k}` | {calls[k]} |")
     open(args.out, "w").write("\n".join(lines) + "\n")
 
 
@@ -148,6 +185,11 @@ def main(argv=None):
     s.add_argument("--title", required=True)
     s.add_argument("--cmd", required=True)
     s.add_argument("--out", required=True)
+    v = sub.add_parser("coverage")
+    v.add_argument("csv")
+    v.add_argument("--title", required=True)
+    v.add_argument("--cmd", required=True)
+    v.add_argument("--out", required=True)
     c = sub.add_parser("counters")
     c.add_argument("csv")
     c.add_argument("--kernels", required=True)
@@ -166,7 +208,7 @@ def main(argv=None):
     t.add_argument("--cmd-write", required=True)
     t.add_argument("--out", required=True)
     a = p.parse_args(argv)
-    {"stats": stats, "counters": counters, "traffic": traffic}[a.cmd_name](a)
+    {"stats": stats, "coverage": coverage, "counters": counters, "traffic": traffic}[a.cmd_name](a)
 
 
 if __name__ == "__main__":

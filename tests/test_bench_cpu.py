@@ -120,3 +120,26 @@ def test_committed_headline_summaries_name_their_sources():
             pytest.skip(f"{fname} not taken yet")
         d = json.loads(re.search(r"```json\n(.*?)\n```", open(path).read(), re.S).group(1))
         assert set(d["sources_sha256"]) == set(sources)
+
+
+def test_coverage_summary_names_instances(tmp_path):
+    """The coverage summary keeps a kernel's template arguments, drops its
+    parameter list and leaves out kernels that are not the library's."""
+    assert profsummary._instance("void kvq::attn_rc_kernel<64>(unsigned char const*, int)") == \
+        "attn_rc_kernel<64>"
+    assert profsummary._instance("kvq::pack_codebooks_kernel(float const*, long)") == \
+        "pack_codebooks_kernel"
+    assert profsummary._instance("void kvq::k<1, std::array<int, 2> >(int)") == \
+        "k<1, std::array<int, 2> >"
+    assert profsummary._instance("void at::native::reduce_kernel<512, 1>(int)") is None
+    csv_path = tmp_path / "s.csv"
+    csv_path.write_text(
+        '"Name","Calls","TotalDurationNs","AverageNs","Percentage","MinNs","MaxNs","StdDev"\n'
+        '"void kvq::a<1>(int)",3,1,1,1,1,1,0\n'
+        '"void kvq::a<1>(int, float)",2,1,1,1,1,1,0\n'
+        '"__amd_rocclr_copyBuffer",9,1,1,1,1,1,0\n')
+    out = tmp_path / "cov.md"
+    profsummary.main(["coverage", str(csv_path), "--title", "t", "--cmd", "c", "--out", str(out)])
+    text = out.read_text()
+    assert "1 kernel instances launched." in text and "| `a<1>` | 5 |" in text
+    assert "rocclr" not in text

@@ -109,6 +109,45 @@ def test_fit_one_iteration_parity(key, over, n_rows):
         check_step(r1, z1, init[1], fitted[1], dsub)
 
 
+@pytest.mark.parametrize("D,dsub,S,C,dt", [
+    (128, 16, 1, 64, "f32"),
+    (128, 8, 2, 256, "f16"),
+    (256, 8, 2, 100, "f32"),
+    (256, 32, 1, 256, "bf16"),
+    (256, 16, 1, 64, "f16"),
+    (64, 16, 2, 64, "bf16"),
+    (64, 8, 1, 100, "f16"),
+])
+def test_fit_kernel_instances(D, dsub, S, C, dt):
+    """The fitting kernels' (head size, input dtype) preparation instances,
+    accumulation slices of 8, 16 and 32 dims and the between-stage bound at
+    each head size, on random samples (two sequences, a ragged row count):
+    one Lloyd iteration per stage against the oracle's update over the GPU's
+    assignment, as in the workload tests above."""
+    G = D // dsub
+    say(f"codebook fit instance D {D} dsub {dsub} S {S} C {C} {dt}")
+    rng = np.random.default_rng(7200 + D + dsub + S + C)
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[dt]
+    n_rows = 590
+    x = torch.from_numpy(rng.standard_normal((2, 600, D)).astype(np.float32)).to(tdt).cuda()
+    xf = x[:, :n_rows].double().cpu().numpy()
+    init = (rng.standard_normal((S, G, C, dsub)) / np.sqrt(dsub)
+            * (0.5 ** np.arange(S))[:, None, None, None]).astype(np.float32)
+    fitted = kvq.codebook_fit(x, cuda(init), 1, n_rows=n_rows).cpu().numpy()
+    y = oracle.fwht(xf.reshape(-1, D))
+    z0 = kvq.encode(x[None], cuda(init[None, :1]), n_rows=n_rows).cpu().numpy().reshape(-1, 1, G)
+    res = oracle.check_codes(y, init[:1], z0, rotate=False)
+    assert res["hard"] == 0
+    check_step(y, z0[:, 0], init[0], fitted[0], dsub)
+    if S > 1:
+        both = np.concatenate([fitted[:1], init[1:2]])
+        zz = kvq.encode(x[None], cuda(both[None]), n_rows=n_rows).cpu().numpy().reshape(-1, 2, G)
+        r1 = residual(y, fitted, zz, 1)
+        res = oracle.check_codes(r1, init[1:2], zz[:, 1][:, None, :], rotate=False)
+        assert res["hard"] == 0
+        check_step(r1, zz[:, 1], init[1], fitted[1], dsub)
+
+
 def test_fit_one_iteration_two_stages_mfma():
     """Stage chaining on the MFMA assignment (Qwen-shaped keys, S = 2)."""
     say("codebook fit, one iteration, two stages, MFMA assignment")

@@ -117,6 +117,28 @@ def test_scalar_encode_pre_rotated_and_f16():
 
 
 @pytest.mark.parametrize("bits", [1, 2, 3, 4])
+@pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_scalar_encode_every_instance(D, dt, bits):
+    """Every (head size, input dtype, bits) instance of the scalar encode
+    kernel on random rows (two books, one ragged row count): the oracle's
+    code rule on every code."""
+    say(f"scalar encode instance D {D} {dt} bits {bits}")
+    rng = np.random.default_rng(7000 + D + bits + len(dt))
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[dt]
+    x = torch.from_numpy(rng.standard_normal((2, 1, 301, D)).astype(np.float32)).to(tdt).cuda()
+    xf = x.double().cpu().numpy()
+    lv = book_levels(xf, bits)
+    codes = kvq.scalar_encode(x, cuda(lv), bits).cpu().numpy()
+    assert codes.shape == (2, 1, 301, 2, D * bits // 8)
+    for b in range(2):
+        z = oracle.unpack_bits(codes[b].reshape(-1, 2, codes.shape[-1]), bits)
+        y = oracle.fwht(xf[b].reshape(-1, D))
+        res = oracle.check_scalar_codes(y, lv[b, 0], lv[b, 1], z[:, 0], z[:, 1])
+        assert res["hard"] == 0, (b, {k: res[k] for k in ("total", "exact", "near_tie", "hard")})
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
 @pytest.mark.parametrize("D", [64, 128, 256])
 def test_scalar_reconstruct_parity(bits, D):
     say(f"scalar reconstruct D {D} bits {bits}")

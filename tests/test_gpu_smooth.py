@@ -77,6 +77,24 @@ def test_smooth_calibrate_bit_exact(key, over, n_scale, n_rows):
         assert np.array_equal(got[b], ref.astype(np.float32)), (b, np.abs(got[b] - ref).max())
 
 
+@pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_smooth_calibrate_every_instance(D, dt):
+    """Every (head size, input dtype) instance of the channel-maximum kernel
+    on random rows (two books, three sequences sharing two factor rows, a
+    ragged row count): bit-exact against the oracle."""
+    say(f"smooth calibrate instance D {D} {dt}")
+    rng = np.random.default_rng(7100 + D + len(dt))
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[dt]
+    x = torch.from_numpy((rng.standard_normal((2, 3, 203, D)) *
+                          rng.uniform(0.1, 8.0, size=(1, 1, 1, D))).astype(np.float32)).to(tdt).cuda()
+    got = kvq.smooth_calibrate(x, 2, n_rows=190).cpu().numpy()
+    xf = x.double().cpu().numpy()
+    for b in range(2):
+        ref = oracle.smooth_factors(xf[b][:, :190], 2)
+        assert np.array_equal(got[b], ref.astype(np.float32)), (b, np.abs(got[b] - ref).max())
+
+
 def test_smooth_calibrate_special_inputs():
     say("smooth calibrate: f16 input, zero channels, empty rows, unmapped rows")
     rng = np.random.default_rng(21)
