@@ -365,7 +365,6 @@ def main():
                             graphs=not args.step_only)
     if not args.step_only:
         main_rep["decode"]["dirty_eviction_us"] = decode_after(torch, L, flush_dirty, args.steps)
-    if not args.step_only:
         main_rep["decode"]["layers_graph"] = decode_layers_graph(
             torch, kvq, L.q, L.kc, L.vc, L.cb, L.kw, L.vw, L.out, L.att_ws, flush, L.eff_b,
             args.steps)
