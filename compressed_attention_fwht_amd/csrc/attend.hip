@@ -73,7 +73,7 @@ AttnPlan attn_plan(int B, int Hq, int Hkv, int D, int S, int G, int C, int Tc, i
     p.wslice = attn_rc_window_slice(W, p.n_chunks);
     p.n_wblocks = W > 0 && p.wslice == 0 ? attn_rc_window_blocks(W) : 0;
     p.pstride = D + 4;
-    p.lut_slice = attn_rc_table_bytes(S);
+    p.lut_slice = attn_rc_table_bytes(S, G);
     // per-unit LUT segments, then the V codebook in the contraction's order
     p.lut_bytes = (size_t)units * p.lut_slice + (size_t)S * G * C * (D / G) * sizeof(float);
     p.part_bytes = (size_t)B * Hq * (p.n_chunks + p.n_wblocks) * p.pstride * sizeof(float);
@@ -1020,7 +1020,7 @@ hipError_t launch_attend(const AttnPlan& p, int B, int Hq, int Hkv, int D, int S
                                          ((p.lut_bytes + 255) & ~(size_t)255));
   const int SG = S * G;
   hipError_t e;
-  if (p.rc) e = launch_attend_rc(p, B, Hq, Hkv, S, Tc, W, cstride, wstride, scale, q, kc, vc, kcb,
+  if (p.rc) e = launch_attend_rc(p, B, Hq, Hkv, S, G, Tc, W, cstride, wstride, scale, q, kc, vc, kcb,
                                  vcb, kw, vw, reinterpret_cast<uint8_t*>(lut), part, ksm, st);
   else if (p.rp == 4) e = launch_rp<4>(p, SG, q, kcb, kc, vc, vcb, lut, part, kw, vw, B, Hq, Hkv, D, S, G, C, Tc, W, cstride, wstride, scale, ksm, st);
   else if (p.rp == 2) e = launch_rp<2>(p, SG, q, kcb, kc, vc, vcb, lut, part, kw, vw, B, Hq, Hkv, D, S, G, C, Tc, W, cstride, wstride, scale, ksm, st);

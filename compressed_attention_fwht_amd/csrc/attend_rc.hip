@@ -1,5 +1,6 @@
-// Decode attention over uint8 codes for the common cache shape -- head_dim
-// 128, 16 groups of 8 dims, C = 256 codewords, 2 or 4 stages -- with LDS
+// Decode attention over uint8 codes for the common cache shapes -- head_dim
+// 128, C = 256 codewords, code rows of 32 or 64 bytes: 2 or 4 stages of 16
+// groups of 8 dims, or 1 or 2 stages of 32 groups of 4 dims -- with LDS
 // tables laid out so that code-driven gathers and histogram atomics never
 // collide on a bank.
 //
@@ -27,13 +28,14 @@
 // 16 lanes of a quarter sit on 16 different slots, for any codes.
 //
 // Geometry.  A code row (S*G bytes, [stage][group]) is cut into segments of
-// 32 bytes (two stages); one segment's table lives in LDS at a time: LUT
-// entries [region][c][slot] of 16 bytes, histogram bins [region][c][pair][slot]
-// of 8 bytes, a region being 64 KiB (c at bits 8-15 of the LDS address).  A
-// segment is two units of 16 bytes (4 dwords); the byte e = 16u + 4d + i of a
-// segment (unit u, dword d, byte i) sits in region d >> 1, slot 8u + 4(d & 1)
-// + i.  (One-stage caches, whose 16-byte rows would need one region only, run
-// faster on attend.hip's kernel and are not routed here.)
+// 32 bytes (two stages of 16 groups, or one of 32); one segment's table lives
+// in LDS at a time: LUT entries [region][c][slot] of 16 bytes, histogram bins
+// [region][c][pair][slot] of 8 bytes, a region being 64 KiB (c at bits 8-15 of
+// the LDS address).  A segment is two units of 16 bytes (4 dwords); the byte
+// e = 16u + 4d + i of a segment (unit u, dword d, byte i) sits in region
+// d >> 1, slot 8u + 4(d & 1) + i.  (One-stage caches of 16 groups, whose
+// 16-byte rows would fill one region only, run faster on attend.hip's kernel
+// and are not routed here.)
 //
 // The rotation moves no data.  Lane p loads unit (kc ^ p0) into unit slot kc
 // (p0 = p & 1: the address does it); for step (kc, jj, q) a first
@@ -55,7 +57,7 @@
 // by rounding); tokens whose four weights round to zero add nothing and are
 // skipped.  V: per segment, the histogram cleared, ds_add_u64 per code and
 // head pair, then the contraction o_rot += 2^-F sum_c W[c] C^V[c] over the
-// segment's stages, each thread keeping one group's 8 dims for 4 heads.
+// segment's stages, each thread keeping one group's 8 (or 4) dims for 4 heads.
 #include "attend_common.h"
 
 namespace kvq {
@@ -124,7 +126,7 @@ __host__ __device__ constexpr int rc_slot(int e) {
 // wave, on the sixteen slots of one region and one codeword, read 512
 // contiguous bytes.  A window block computes the softmax partial of up to
 // RC_WIN_BLOCK window tokens (record n_chunks + block of the unit's heads).
-template <int SG>
+template <int SG, int NG>
 __global__ __launch_bounds__(512) void attn_rc_prep_kernel(
     const float* __restrict__ q, const float* __restrict__ kcb, const float* __restrict__ vcb,
     uint8_t* __restrict__ lut, float* __restrict__ cvt, float* __restrict__ part,
@@ -132,7 +134,7 @@ __global__ __launch_bounds__(512) void attn_rc_prep_kernel(
     int n_hsplit, int n_wb, int W, int wstride, int n_chunks, int nslots, int pstride,
     float scale, const float* __restrict__ ksm, int64_t ksm_rows) {
   using Gm = RcGeom<SG>;
-  constexpr int D = 128, L = 16;
+  constexpr int D = 128, L = 16, DS = D / NG;
   constexpr int NREG = 2;
   constexpr int LB_PER_UNIT = Gm::NSEG * NREG * 4;      // (segment, region, codeword quarter)
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -143,14 +145,14 @@ __global__ __launch_bounds__(512) void attn_rc_prep_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   int bid = blockIdx.x;
   if (bid >= nlb && bid < nlb + SG / 2) {               // V codebook -> contraction order
-    const int row = (bid - nlb) * 512 + tid;             // (sg, c), one 8-float row each
+    const int row = (bid - nlb) * 512 + tid;             // (sg, c), one DS-float row each
     const int sg = row >> 8, c = row & 255;
     const int seg = sg >> 5, e = sg & 31;
-    const float4* src = reinterpret_cast<const float4*>(vcb + (int64_t)row * 8);
+    const float4* src = reinterpret_cast<const float4*>(vcb + (int64_t)row * DS);
     float4* dst = reinterpret_cast<float4*>(
-        cvt + ((((int64_t)seg * 256 + c) * NREG + rc_region(e)) * 16 + rc_slot(e)) * 8);
-    dst[0] = src[0];
-    dst[1] = src[1];
+        cvt + ((((int64_t)seg * 256 + c) * NREG + rc_region(e)) * 16 + rc_slot(e)) * DS);
+#pragma unroll
+    for (int i = 0; i < DS / 4; ++i) dst[i] = src[i];
     return;
   }
   const bool win = bid >= nlb;
@@ -176,16 +178,18 @@ __global__ __launch_bounds__(512) void attn_rc_prep_kernel(
   const int u = slot >> 3, i = slot & 3;
   const int e = 16 * u + 4 * (2 * region + ((slot >> 2) & 1)) + i;
   const int sg = seg * 32 + e;
-  const int g = sg & 15;
+  const int g = sg % NG;
   // codebook rows first: their loads are in flight across the query rotation
-  float cv[2][8];
+  float cv[2][DS];
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     const int c = cq * 64 + (tid >> 4) + 32 * k;
-    const float4* cp = reinterpret_cast<const float4*>(kcb + ((int64_t)sg * 256 + c) * 8);
-    const float4 c0 = cp[0], c1 = cp[1];
-    cv[k][0] = c0.x; cv[k][1] = c0.y; cv[k][2] = c0.z; cv[k][3] = c0.w;
-    cv[k][4] = c1.x; cv[k][5] = c1.y; cv[k][6] = c1.z; cv[k][7] = c1.w;
+    const float4* cp = reinterpret_cast<const float4*>(kcb + ((int64_t)sg * 256 + c) * DS);
+#pragma unroll
+    for (int i = 0; i < DS / 4; ++i) {
+      const float4 c4 = cp[i];
+      cv[k][4 * i] = c4.x; cv[k][4 * i + 1] = c4.y; cv[k][4 * i + 2] = c4.z; cv[k][4 * i + 3] = c4.w;
+    }
   }
   if (tid < 64) {                                       // wave 0: the four query rows
     const int r = lane / L;
@@ -200,11 +204,11 @@ __global__ __launch_bounds__(512) void attn_rc_prep_kernel(
     for (int e2 = 0; e2 < 8; ++e2) qs[r][(lane % L) * 8 + e2] = v[e2] * rs;
   }
   __syncthreads();
-  float qv[4][8];
+  float qv[4][DS];
 #pragma unroll
   for (int r = 0; r < 4; ++r)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) qv[r][j] = qs[r][g * 8 + j];
+    for (int j = 0; j < DS; ++j) qv[r][j] = qs[r][g * DS + j];
   uint8_t* dst = lut + (size_t)unit * (Gm::NSEG * Gm::TAB) + (size_t)seg * Gm::TAB +
                  (size_t)region * 65536 + slot * 16;
 #pragma unroll
@@ -215,7 +219,7 @@ __global__ __launch_bounds__(512) void attn_rc_prep_kernel(
     for (int r = 0; r < 4; ++r) {
       acc[r] = 0.0f;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc[r] = __builtin_fmaf(qv[r][j], cv[k][j], acc[r]);
+      for (int j = 0; j < DS; ++j) acc[r] = __builtin_fmaf(qv[r][j], cv[k][j], acc[r]);
     }
     *reinterpret_cast<float4*>(dst + c * 256) = make_float4(acc[0], acc[1], acc[2], acc[3]);
   }
@@ -225,7 +229,7 @@ __global__ __launch_bounds__(512) void attn_rc_prep_kernel(
 // grid (n_chunks, Hkv * n_hsplit, B), RC_THREADS threads, Gm::TAB bytes of
 // dynamic LDS for one table segment (the contraction's partials reuse it)
 // plus the block reductions.
-template <int SG>
+template <int SG, int NG>
 __global__ __launch_bounds__(RC_THREADS, 1) void attn_rc_kernel(
     const uint8_t* __restrict__ kcodes, const uint8_t* __restrict__ vcodes,
     const float* __restrict__ cvt, const uint8_t* __restrict__ lut, float* __restrict__ part,
@@ -526,18 +530,22 @@ __global__ __launch_bounds__(RC_THREADS, 1) void attn_rc_kernel(
 
   // ---- V: histogram per segment, then its share of the contraction
   // contraction mapping: quarter Q = tid / 16 reads slot p of region (Q & 1)
-  // for its range of codewords; the slot names the (stage, group), the group
-  // is the same in every segment.
+  // for its range of codewords; the slot names the segment byte e and so its
+  // (stage, group): with 16 groups of 8 dims a segment holds two stages (bytes
+  // e and e + 16 are one group, lanes p and p ^ 8), with 32 groups of 4 dims
+  // one stage (byte e is group e).  The group is the same in every segment.
+  constexpr int DS = 128 / NG;
   const int Q = tid >> 4;
   const int creg = Q & 1, cn = 8, c0 = (Q >> 1) * 8;
-  const int grp = 4 * (2 * creg + (int)((p >> 2) & 1)) + (int)(p & 3);
+  const int grp = 4 * (2 * creg + (int)((p >> 2) & 1)) + (int)(p & 3) +
+                  (NG == 16 ? 0 : 16 * (int)(p >> 3));   // the segment byte's group
   uint32_t LV[2][2][2];
   slot_consts(LV, 8u);
-  float o[4][8];
+  float o[4][DS];
 #pragma unroll
   for (int r = 0; r < 4; ++r)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) o[r][j] = 0.0f;
+    for (int j = 0; j < DS; ++j) o[r][j] = 0.0f;
 #pragma unroll
   for (int seg = 0; seg < NSEG; ++seg) {
     if (seg > 0) {
@@ -588,43 +596,57 @@ __global__ __launch_bounds__(RC_THREADS, 1) void attn_rc_kernel(
     constexpr int NREG = 2;
     const uint8_t* hp = smem + creg * 65536 + c0 * 256 + p * 8;
     const float4* cp = reinterpret_cast<const float4*>(
-        cvt + ((((int64_t)seg * 256 + c0) * NREG + creg) * 16 + p) * 8);
-    constexpr int CSTEP = NREG * 16 * 8 / 4;            // float4s from one codeword to the next
+        cvt + ((((int64_t)seg * 256 + c0) * NREG + creg) * 16 + p) * DS);
+    constexpr int CSTEP = NREG * 16 * DS / 4;           // float4s from one codeword to the next
+    constexpr int NX = DS / 4;                          // float4s of one codebook row
     uint2 wa = *reinterpret_cast<const uint2*>(hp), wb = *reinterpret_cast<const uint2*>(hp + 128);
-    float4 x0 = cp[0], x1 = cp[1];
+    float4 x[NX];
+#pragma unroll
+    for (int i = 0; i < NX; ++i) x[i] = cp[i];
 #pragma unroll 1
     for (int cc = 0; cc < cn; ++cc) {
       const uint2 na = *reinterpret_cast<const uint2*>(hp + 256 * (cc + 1 < cn ? cc + 1 : cc));
       const uint2 nb = *reinterpret_cast<const uint2*>(hp + 128 + 256 * (cc + 1 < cn ? cc + 1 : cc));
       const float4* np = cp + CSTEP * (cc + 1 < cn ? cc + 1 : cc);
-      const float4 n0 = np[0], n1 = np[1];
+      float4 nx[NX];
+#pragma unroll
+      for (int i = 0; i < NX; ++i) nx[i] = np[i];
       const float wf[4] = {(float)wa.x, (float)wa.y, (float)wb.x, (float)wb.y};
-      const float cv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+      float cv[DS];
+#pragma unroll
+      for (int i = 0; i < NX; ++i) {
+        cv[4 * i] = x[i].x; cv[4 * i + 1] = x[i].y; cv[4 * i + 2] = x[i].z; cv[4 * i + 3] = x[i].w;
+      }
 #pragma unroll
       for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) o[r][j] = __builtin_fmaf(wf[r], cv[j], o[r][j]);
-      wa = na; wb = nb; x0 = n0; x1 = n1;
+        for (int j = 0; j < DS; ++j) o[r][j] = __builtin_fmaf(wf[r], cv[j], o[r][j]);
+      wa = na; wb = nb;
+#pragma unroll
+      for (int i = 0; i < NX; ++i) x[i] = nx[i];
     }
   }
   // ---- partials of one group: lanes sharing it summed by lane exchanges,
   // then across waves / quarters through LDS (the table is free now)
+  if constexpr (NG == 16) {
 #pragma unroll
-  for (int r = 0; r < 4; ++r)
+    for (int r = 0; r < 4; ++r)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      o[r][j] += xor_lane<8>(o[r][j]);                  // the two stages of the segment pair
-    }
+      for (int j = 0; j < DS; ++j) {
+        o[r][j] += xor_lane<8>(o[r][j]);                // the two stages of the segment pair
+      }
+  }
   lds_sync();
   float* buf = reinterpret_cast<float*>(smem);          // [NPART][4][128]
-  const bool writer = (p & 8) == 0;
+  const bool writer = NG == 16 ? (p & 8) == 0 : true;
   const int pi = Q >> 1;
   if (writer) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      float4* dp = reinterpret_cast<float4*>(buf + (pi * 4 + r) * 128 + grp * 8);
-      dp[0] = make_float4(o[r][0], o[r][1], o[r][2], o[r][3]);
-      dp[1] = make_float4(o[r][4], o[r][5], o[r][6], o[r][7]);
+      float4* dp = reinterpret_cast<float4*>(buf + (pi * 4 + r) * 128 + grp * DS);
+#pragma unroll
+      for (int i = 0; i < DS / 4; ++i)
+        dp[i] = make_float4(o[r][4 * i], o[r][4 * i + 1], o[r][4 * i + 2], o[r][4 * i + 3]);
     }
   }
   lds_sync();
@@ -665,17 +687,18 @@ __global__ __launch_bounds__(RC_THREADS, 1) void attn_rc_kernel(
 }
 
 // ------------------------------------------------------------- launcher
-// One-stage caches are small (16 code bytes per token): their decode is
-// bound by memory round trips and launches, which the general kernel, with
-// its LUT built inside the chunk blocks and no separate LUT pass, keeps
-// fewer of; they stay there.
+// Code rows of 32 or 64 bytes: two or four stages of 16 groups of 8 dims, or
+// one or two stages of 32 groups of 4 dims (the product codebooks of 2-bit
+// scalar codes).  One-stage caches of 16 groups are small (16 code bytes per
+// token): their decode is bound by memory round trips and launches, which the
+// general kernel, with its LUT built inside the chunk blocks and no separate
+// LUT pass, keeps fewer of; they stay there.
 bool attn_rc_eligible(int D, int G, int S, int C, int Hq, int Hkv, int Tc) {
-  return D == 128 && G == 16 && C == 256 && (S == 2 || S == 4) && Tc > 0 && Hq / Hkv >= 2;
+  const bool rows = (G == 16 && (S == 2 || S == 4)) || (G == 32 && (S == 1 || S == 2));
+  return D == 128 && C == 256 && rows && Tc > 0 && Hq / Hkv >= 2;
 }
 
-size_t attn_rc_table_bytes(int S) {
-  return (size_t)131072 * (S == 4 ? 2 : 1);
-}
+size_t attn_rc_table_bytes(int S, int G) { return (size_t)131072 * (S * G / 32); }
 
 int attn_rc_window_slice(int W, int n_chunks) {
   const int per = n_chunks > 0 ? (W + n_chunks - 1) / n_chunks : 0;
@@ -684,7 +707,7 @@ int attn_rc_window_slice(int W, int n_chunks) {
 
 int attn_rc_window_blocks(int W) { return (W + RC_WIN_BLOCK - 1) / RC_WIN_BLOCK; }
 
-template <int SG>
+template <int SG, int NG>
 static hipError_t launch_rc_sg(const AttnPlan& p, int B, int Hq, int Hkv, int Tc, int W,
                                int cstride, int wstride, float scale, const float* q,
                                const uint8_t* kc, const uint8_t* vc, const float* kcb,
@@ -698,37 +721,39 @@ static hipError_t launch_rc_sg(const AttnPlan& p, int B, int Hq, int Hkv, int Tc
   float* cvt = reinterpret_cast<float*>(lut + (size_t)units * p.lut_slice);
   hipError_t e;
   if (wl > 0) {
-    e = hipFuncSetAttribute((const void*)attn_rc_prep_kernel<SG>,
+    e = hipFuncSetAttribute((const void*)attn_rc_prep_kernel<SG, NG>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)wl);
     if (e != hipSuccess) return e;
   }
-  attn_rc_prep_kernel<SG><<<dim3(units * LB_PER_UNIT + SG / 2 + units * p.n_wblocks), 512, wl, st>>>(
+  attn_rc_prep_kernel<SG, NG><<<dim3(units * LB_PER_UNIT + SG / 2 + units * p.n_wblocks), 512, wl,
+                                st>>>(
       q, kcb, vcb, lut, cvt, part, kw, vw, B, Hq, Hkv, p.n_hsplit, p.n_wblocks, W, wstride,
       p.n_chunks, nslots, p.pstride, scale, ksm.f, ksm.n_scale);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   // table, block reductions, window maxima and sums, window partials
   const int lds = Gm::TAB + 5 * (RC_THREADS / 64) * 16 + RC_WIN_SLICE / 4 * 4 * 128 * 4;
-  e = hipFuncSetAttribute((const void*)attn_rc_kernel<SG>,
+  e = hipFuncSetAttribute((const void*)attn_rc_kernel<SG, NG>,
                           hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
-  attn_rc_kernel<SG><<<dim3(p.n_chunks, Hkv * p.n_hsplit, B), RC_THREADS, lds, st>>>(
+  attn_rc_kernel<SG, NG><<<dim3(p.n_chunks, Hkv * p.n_hsplit, B), RC_THREADS, lds, st>>>(
       kc, vc, cvt, lut, part, Hq, Hkv, p.n_hsplit, Tc, p.chunk, nslots, p.pstride, cstride, q, kw,
       vw, W, p.wslice, wstride, scale);
   return hipGetLastError();
 }
 
-hipError_t launch_attend_rc(const AttnPlan& p, int B, int Hq, int Hkv, int S, int Tc, int W,
-                            int cstride, int wstride, float scale, const float* q,
+hipError_t launch_attend_rc(const AttnPlan& p, int B, int Hq, int Hkv, int S, int G, int Tc,
+                            int W, int cstride, int wstride, float scale, const float* q,
                             const uint8_t* kc, const uint8_t* vc, const float* kcb,
                             const float* vcb, const uint16_t* kw, const uint16_t* vw,
                             uint8_t* lut, float* part, Smooth ksm, hipStream_t st) {
-  if (S != 2 && S != 4) return hipErrorInvalidValue;    // the plan routes no other here
-  if (S == 2)
-    return launch_rc_sg<32>(p, B, Hq, Hkv, Tc, W, cstride, wstride, scale, q, kc, vc, kcb, vcb,
-                            kw, vw, lut, part, ksm, st);
-  return launch_rc_sg<64>(p, B, Hq, Hkv, Tc, W, cstride, wstride, scale, q, kc, vc, kcb, vcb, kw,
-                          vw, lut, part, ksm, st);
+#define KVQ_RC(SS, GG)                                                                        \
+  if (S == SS && G == GG)                                                                     \
+    return launch_rc_sg<SS * GG, GG>(p, B, Hq, Hkv, Tc, W, cstride, wstride, scale, q, kc, vc, \
+                                     kcb, vcb, kw, vw, lut, part, ksm, st);
+  KVQ_RC(2, 16) KVQ_RC(4, 16) KVQ_RC(1, 32) KVQ_RC(2, 32)
+#undef KVQ_RC
+  return hipErrorInvalidValue;                          // the plan routes no other here
 }
 
 }  // namespace kvq

@@ -58,11 +58,11 @@ hipError_t launch_reconstruct(const uint8_t* codes, const float* cb, float* out,
 // GQA >= 2): eligibility, LUT bytes per unit, and the launch of its LUT /
 // window kernel and chunk kernel (records only; the merge follows).
 bool attn_rc_eligible(int D, int G, int S, int C, int Hq, int Hkv, int Tc);
-size_t attn_rc_table_bytes(int S);
+size_t attn_rc_table_bytes(int S, int G);
 int attn_rc_window_blocks(int W);
 int attn_rc_window_slice(int W, int n_chunks);
-hipError_t launch_attend_rc(const AttnPlan& p, int B, int Hq, int Hkv, int S, int Tc, int W,
-                            int cstride, int wstride, float scale, const float* q,
+hipError_t launch_attend_rc(const AttnPlan& p, int B, int Hq, int Hkv, int S, int G, int Tc,
+                            int W, int cstride, int wstride, float scale, const float* q,
                             const uint8_t* kc, const uint8_t* vc, const float* kcb,
                             const float* vcb, const uint16_t* kw, const uint16_t* vw,
                             uint8_t* lut, float* part, Smooth ksm, hipStream_t st);

@@ -168,11 +168,11 @@ def test_scalar_product_codebook_exact(bits):
 
 
 @pytest.mark.parametrize("key,over,bits", [
-    (2, dict(tokens=3000, window=128), 1),      # 16 groups of 8 dims: the compiled 2 x 16 path
-    (2, dict(tokens=3000, window=128), 2),      # 32 groups of 4 dims
+    (2, dict(tokens=3000, window=128), 1),      # 16 groups of 8 dims: rotated-code kernels
+    (2, dict(tokens=3000, window=128), 2),      # 32 groups of 4 dims: rotated-code kernels
     (3, dict(batch=3, tokens=2100, window=64), 2),
     (1, dict(tokens=1500, window=0), 1),        # D = 64
-    (2, dict(tokens=3000, window=128), 4),      # 64 groups of 2 dims: one head per block
+    (2, dict(tokens=3000, window=128), 4),      # 64 groups of 2 dims: general kernel
     (3, dict(batch=2, tokens=1800, window=64), 4),
     (1, dict(tokens=1500, window=0), 4),        # D = 64, 32 groups of 2 dims
 ])

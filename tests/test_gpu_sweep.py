@@ -86,25 +86,16 @@ def test_decode_sweep(case):
     assert res["ok"], res
 
 
-@pytest.mark.parametrize("case", list(range(16)))
-def test_rotated_code_decode_sweep(case):
-    """The cache shape of the rotated-code kernels (128-dim heads, 16 groups of
-    8, C = 256, two or four stages, at least two query heads per KV head):
-    head groups of 1-4 heads (GQA 2-8, head splits with a ragged last one),
-    coded lengths from a single token to several chunks with a ragged tail,
-    no window, short windows riding on the chunk blocks and long ones in
-    blocks of their own, the factors of the dual transform on some cases."""
-    rng = np.random.default_rng(3000 + case)
-    D, G, C, dsub = 128, 16, 256, 8
-    S = int(rng.choice([2, 4]))
+def _rotated_code_case(rng, G, stages):
+    D, C, dsub = 128, 256, 128 // G
+    S = int(rng.choice(stages))
     B = int(rng.integers(1, 4))
     Hkv = int(rng.choice([1, 2, 4]))
     R = int(rng.choice([2, 3, 4, 5, 7, 8]))
     Tc = int(rng.choice([1, int(rng.integers(2, 1100)), int(rng.integers(1100, 9000))]))
     W = int(rng.choice([0, int(rng.integers(1, 64)), int(rng.integers(300, 1200))]))
     smooth = bool(rng.integers(0, 4) == 0)
-    say(f"rotated-code decode sweep case {case}: S {S} B {B} Hkv {Hkv} GQA {R} Tc {Tc} W {W} "
-        f"smooth {smooth}")
+    say(f"rotated-code decode: G {G} S {S} B {B} Hkv {Hkv} GQA {R} Tc {Tc} W {W} smooth {smooth}")
     Hq = Hkv * R
     q = rng.standard_normal((B, Hq, D)).astype(np.float32)
     kcb = (rng.standard_normal((S, G, C, dsub)) / np.sqrt(dsub)
@@ -124,6 +115,25 @@ def test_rotated_code_decode_sweep(case):
     res = oracle.check_attn(got, ref)
     say("   ", {k: res[k] for k in ("ok", "max_abs", "rel_l2")})
     assert res["ok"], res
+
+
+@pytest.mark.parametrize("case", list(range(16)))
+def test_rotated_code_decode_sweep(case):
+    """The cache shape of the rotated-code kernels (128-dim heads, 16 groups of
+    8, C = 256, two or four stages, at least two query heads per KV head):
+    head groups of 1-4 heads (GQA 2-8, head splits with a ragged last one),
+    coded lengths from a single token to several chunks with a ragged tail,
+    no window, short windows riding on the chunk blocks and long ones in
+    blocks of their own, the factors of the dual transform on some cases."""
+    _rotated_code_case(np.random.default_rng(3000 + case), 16, [2, 4])
+
+
+@pytest.mark.parametrize("case", list(range(12)))
+def test_rotated_code_decode_sweep_32_groups(case):
+    """The same sweep for the rotated-code kernels' other row shape: 32 groups
+    of 4 dims (the product codebooks of 2-bit scalar codes), one or two
+    stages."""
+    _rotated_code_case(np.random.default_rng(3100 + case), 32, [1, 2])
 
 
 @pytest.mark.parametrize("case", list(range(20)))
