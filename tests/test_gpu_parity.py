@@ -378,32 +378,34 @@ def test_decode_large_batch_lut_pass(B, Hq, Hkv, D, S, G, Tc, W):
     assert res["ok"], res
 
 
-@pytest.mark.parametrize("B,Hq,Hkv,D,S,G,Tc,W", [
+@pytest.mark.parametrize("B,Hq,Hkv,D,S,G,C,Tc,W", [
     # window only: the chunk kernel's window blocks, per heads-per-block and code-row class
-    (2, 4, 4, 128, 3, 16, 0, 300),
-    (2, 4, 4, 64, 1, 8, 0, 300),
-    (2, 4, 4, 128, 1, 16, 0, 300),
-    (2, 8, 4, 256, 1, 32, 0, 300),
-    (2, 8, 4, 128, 1, 16, 0, 300),
-    (2, 8, 4, 128, 2, 16, 0, 300),
-    (2, 8, 4, 128, 4, 16, 0, 300),
-    (2, 16, 4, 128, 3, 16, 0, 300),
-    (2, 16, 4, 128, 4, 16, 0, 300),
+    (2, 4, 4, 128, 3, 16, 256, 0, 300),
+    (2, 4, 4, 64, 1, 8, 256, 0, 300),
+    (2, 4, 4, 128, 1, 16, 256, 0, 300),
+    (2, 8, 4, 256, 1, 32, 256, 0, 300),
+    (2, 8, 4, 128, 1, 16, 256, 0, 300),
+    (2, 8, 4, 128, 2, 16, 256, 0, 300),
+    (2, 8, 4, 128, 4, 16, 256, 0, 300),
+    (2, 16, 4, 128, 3, 16, 256, 0, 300),
+    (2, 16, 4, 128, 4, 16, 256, 0, 300),
     # 256-dim heads two per block, LUT built in the chunk blocks
-    (2, 8, 4, 256, 1, 32, 900, 40),
+    (2, 8, 4, 256, 1, 32, 256, 900, 40),
     # serving batches whose LUTs come from attn_lut_kernel: 1, 2 and 4 heads, 64/256 dims
-    (64, 8, 8, 256, 1, 32, 50, 0),
-    (128, 8, 8, 64, 2, 8, 50, 0),
-    (64, 16, 8, 256, 1, 32, 50, 0),
-    (128, 32, 8, 64, 2, 8, 50, 0),
+    (64, 8, 8, 256, 1, 32, 256, 50, 0),
+    (128, 8, 8, 64, 2, 8, 256, 50, 0),
+    (64, 16, 8, 256, 1, 32, 256, 50, 0),
+    (128, 32, 8, 64, 2, 8, 256, 50, 0),
+    # 64-byte code rows, two heads per block, a book of 128 (outside the rotated-code shape)
+    (2, 8, 4, 128, 2, 32, 128, 900, 40),
 ])
-def test_decode_dispatch_variants(B, Hq, Hkv, D, S, G, Tc, W):
+def test_decode_dispatch_variants(B, Hq, Hkv, D, S, G, C, Tc, W):
     """The remaining (heads per block, head size, code-row size, LUT mode)
     instances of the general decode kernel and of attn_lut_kernel: window-only
     calls, 256-dim heads in pairs, and large batches with staged LUTs."""
-    say(f"decode variant: B {B} Hq {Hq} Hkv {Hkv} D {D} S {S} G {G} Tc {Tc} W {W}")
+    say(f"decode variant: B {B} Hq {Hq} Hkv {Hkv} D {D} S {S} G {G} C {C} Tc {Tc} W {W}")
     rng = np.random.default_rng(6000 + B + Hq + D + S + Tc)
-    C, dsub = 256, D // G
+    dsub = D // G
     q = rng.standard_normal((B, Hq, D)).astype(np.float32)
     kcb = (rng.standard_normal((S, G, C, dsub)) / np.sqrt(dsub)
            * (0.5 ** np.arange(S))[:, None, None, None]).astype(np.float32)
