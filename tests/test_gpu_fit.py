@@ -5,9 +5,11 @@ K-means is iterative, so the element-wise check is one iteration at a time:
 the GPU's assignment (the encode kernels, run with the same entries and the
 earlier stages' fitted ones) follows the code rule against the oracle's
 distances, and every fitted entry equals the oracle's mean of the residuals
-(y minus the earlier-stage entries that same assignment chose) the GPU
-assigned to it within 1e-6 * the largest residual component of its group
-(the fixed-point sums themselves are exact to 2^-30 of that bound).  Entries
+(y minus the earlier-stage entries that same assignment chose, the chain
+taken in float64) the GPU assigned to it within 1e-6 * the largest residual
+component of its group (the fixed-point sums themselves are exact to 2^-30
+of that bound), plus, at stage s > 0, s * 2^-23 * max|y| of the group: the
+kernel forms its residuals in float32, one rounding per subtraction.  Entries
 no vector chose must come back bit-identical.  Over several iterations the
 checks are Lloyd's properties: the distortion of the fitted codebooks never
 increases, and ends within 1 % of the oracle's own fit from the same start.
@@ -56,23 +58,29 @@ def sample(key, n_rows, **over):
 
 
 def residual(y, cb, codes, s):
-    """y minus the entries of stages 0..s-1 that codes [n][>=s][G] chose,
-    subtracted stage by stage in float32 (as the assignment's chain does)."""
+    """The oracle's residual chain in float64: y minus the entries of stages
+    0..s-1 that codes [n][>=s][G] chose (the GPU's codes, teacher-forced)."""
     G = cb.shape[1]
-    r = y.astype(np.float32)
+    r = np.asarray(y, dtype=np.float64).copy()
     for t in range(s):
-        r = r - np.concatenate([cb[t, g][codes[:, t, g]] for g in range(G)], axis=1)
-    return r.astype(np.float64)
+        r -= np.concatenate([cb[t, g][codes[:, t, g]] for g in range(G)], axis=1).astype(np.float64)
+    return r
 
 
-def check_step(r, z, init, fitted, dsub):
+def check_step(r, z, init, fitted, dsub, y=None, s=0):
     """One Lloyd update per group: the fitted entries against the oracle's
-    means of r over the GPU's assignment z; unchosen entries unchanged."""
+    float64 means of r over the GPU's assignment z; unchosen entries
+    unchanged.  The kernel's residuals of stage s are float32 (the rotation
+    rounded once, then s subtractions each rounded once), so beyond the
+    1e-6 * max|r| bound of the sums a stage-s entry may differ from the
+    float64 chain by s * 2^-23 * max|y| of its group."""
     G = init.shape[0]
     for g in range(G):
         rg = r[:, g * dsub:(g + 1) * dsub]
         ref = oracle.lloyd_update(rg, z[:, g], init[g])
         tol = 1e-6 * np.abs(rg).max()
+        if s > 0:
+            tol += s * 2.0 ** -23 * np.abs(y[:, g * dsub:(g + 1) * dsub]).max()
         err = np.abs(fitted[g].astype(np.float64) - ref)
         assert err.max() <= tol, (g, err.max(), tol)
         unused = np.setdiff1d(np.arange(init.shape[1]), z[:, g])
@@ -106,7 +114,7 @@ def test_fit_one_iteration_parity(key, over, n_rows):
         res = oracle.check_codes(r1, init[1:2], z1[:, None, :], rotate=False)
         say("   stage 1 assignment", {k: res[k] for k in ("total", "exact", "near_tie", "hard")})
         assert res["hard"] == 0
-        check_step(r1, z1, init[1], fitted[1], dsub)
+        check_step(r1, z1, init[1], fitted[1], dsub, y, 1)
 
 
 @pytest.mark.parametrize("D,dsub,S,C,dt", [
@@ -145,7 +153,7 @@ def test_fit_kernel_instances(D, dsub, S, C, dt):
         r1 = residual(y, fitted, zz, 1)
         res = oracle.check_codes(r1, init[1:2], zz[:, 1][:, None, :], rotate=False)
         assert res["hard"] == 0
-        check_step(r1, zz[:, 1], init[1], fitted[1], dsub)
+        check_step(r1, zz[:, 1], init[1], fitted[1], dsub, y, 1)
 
 
 def test_fit_one_iteration_two_stages_mfma():
@@ -163,7 +171,7 @@ def test_fit_one_iteration_two_stages_mfma():
     z1 = zz[:, 1]
     res = oracle.check_codes(r1, init[1:2], z1[:, None, :], rotate=False)
     assert res["hard"] == 0
-    check_step(r1, z1, init[1], fitted[1], dsub)
+    check_step(r1, z1, init[1], fitted[1], dsub, y, 1)
 
 
 def test_fit_smoothed_keys_one_iteration():
@@ -249,5 +257,5 @@ def test_fit_five_stages_mfma_then_generic():
     z4 = zz[:, 4]
     res = oracle.check_codes(r4, init[4:5], z4[:, None, :], rotate=False)
     assert res["hard"] == 0
-    check_step(r4, z4, init[4], fitted[4], dsub)
+    check_step(r4, z4, init[4], fitted[4], dsub, y, 4)
     assert torch.equal(kvq.codebook_fit(x, cuda(init), 1), cuda(fitted))

@@ -566,7 +566,7 @@ def test_decode_codes_only_short():
 
 
 
-@pytest.mark.parametrize("key,delta,every", [(2, 15.5, 1024), (4, 14.0, 4096)])
+@pytest.mark.parametrize("key,delta,every", [(2, 15.5, 1024), (3, 14.0, 2048), (4, 14.0, 4096)])
 def test_decode_attention_sink_chunks(key, delta, every):
     """Peaky softmax inside the split-K chunks, at the workload's full shape:
     every `every`-th coded token is a sink whose key scores `delta` nats
@@ -576,7 +576,8 @@ def test_decode_attention_sink_chunks(key, delta, every):
     4088-token chunk holds one sink and 4087 weights of e^-14, 3.4e-3 of its
     mass: a fixed-point weight step taken from the chunk length alone (2^-19)
     rounds them all to zero, about 5e-2 off in the output (CPU emulation of
-    that rule).  Query heads are equal so every head sees the same gap.  The
+    that rule).  The Qwen-shaped batch (16 sequences, two stages, seven query
+    heads per KV head split 4 + 3 over two blocks) has two sinks per chunk.  Query heads are equal so every head sees the same gap.  The
     fp32 log-sum-exp combine must still meet 2e-3 max-abs / 1e-3 relative L2
     ("Differential-KV" README, Flash-Style LSE Combine)."""
     w = synth.workload(key)
