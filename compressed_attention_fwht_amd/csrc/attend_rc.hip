@@ -20,9 +20,9 @@
 // fields each).  Both are picked by a random code byte c.  gfx950 serves
 // ds_read_b128, ds_read_b64 and ds_add_u64 sixteen lanes at a time and runs
 // them at full rate when those sixteen lanes use different slots of a
-// 256-byte bank row, whatever the rows are (measured: 13.6 lanes per cycle
-// per CU for such b128 reads against 5.2 for random addresses; 16.7 against
-// 8.3 for u64 atomics).  So a table row c holds the entries of 16 (stage,
+// 256-byte bank row, whatever the rows are (measured: 13.7 lanes per cycle
+// per CU for such b128 reads against 5.8 for random slots; 9.9 against 6.2
+// for u64 atomics).  So a table row c holds the entries of 16 (stage,
 // group) pairs in 16 slots, and each lane visits the pairs of its own token
 // in an order rotated by its place p in its quarter wave: at every step the
 // 16 lanes of a quarter sit on 16 different slots, for any codes.
