@@ -18,9 +18,10 @@
 // (G = D*b/8 groups of k dims, C = 256).  For b = 3 elements straddle bytes:
 // encode and reconstruction only.
 //
-// Layout per lane as elsewhere: L = D/8 lanes per row, 8 consecutive elements
-// per lane, so a lane's indices fill b whole bytes per stage.  HBM-bound:
-// 2 (or 4) bytes in and b/4 bytes out per element.
+// Encode: 32 consecutive elements per lane (D/32 lanes per row), so a lane's
+// indices fill b whole 32-bit words per stage; reconstruction: D/8 lanes per
+// row.  In principle HBM-bound: 2 (or 4) bytes in and b/4 bytes out per
+// element.
 #include <math.h>
 
 #include "kvq_internal.h"
@@ -137,15 +138,26 @@ __device__ __forceinline__ uint32_t bsum(float v, const float (&th)[1 << B]) {
 // the bytes in flight, not by its arithmetic)
 constexpr int SC_U = 4;
 
+// Encode layout: SE_E consecutive elements per lane (L = D/SE_E lanes per
+// row, 2, 4 or 8), so the 128-point butterfly has five in-register stages
+// and two cross-lane ones (each cross-lane stage moves both 32-bit halves of
+// every float64 element and selects around them, the costly part), and a
+// lane's indices fill SE_E*b/32 whole words per stage.  SE_U rows per lane
+// and pass.
+constexpr int SE_E = 32;
+constexpr int SE_U = 1;
+
 // grid (row blocks, n_books), 256 threads; grid-stride over the book's rows.
 template <int D, int XT, int B>
 __global__ __launch_bounds__(256) void scalar_encode_kernel(
     const void* __restrict__ x, const float* __restrict__ levels, uint8_t* __restrict__ codes,
     int64_t n_seq, int64_t seq_stride, int64_t n_rows, int pre_rotated, uint64_t dm, int dsh) {
-  constexpr int L = D / 8;
+  constexpr int E = SE_E;
+  constexpr int L = D / E;
   constexpr int RPB = 256 / L;                          // rows per block and unroll step
   constexpr int ESZ = XT == 0 ? 4 : 2;
   constexpr int SB = D * B / 8;                         // bytes per stage
+  constexpr int NW = E * B / 32;                        // code words per lane and stage
   __shared__ float lv[2][1 << B], th[2][1 << B];
   const int64_t book = blockIdx.y;
   stage_levels<B>(levels, book, lv, th);
@@ -158,85 +170,77 @@ __global__ __launch_bounds__(256) void scalar_encode_kernel(
     t0[k] = th[0][k];
     t1[k] = th[1][k];
   }
-  for (int64_t base = (int64_t)blockIdx.x * RPB * SC_U; base < n;
-       base += (int64_t)gridDim.x * RPB * SC_U) {
-    float y[SC_U][8];
-#pragma unroll
-    for (int u = 0; u < SC_U; ++u) {
-      const int64_t v = base + u * RPB + rsub;
-      const int64_t vl = v < n ? v : n - 1;             // every lane joins the butterfly
-      // vl / n_rows by multiply and shift when both fit 31 bits (dsh != 0)
-      const int64_t seq = dsh ? (int64_t)(((uint64_t)vl * dm) >> dsh) : vl / n_rows;
-      const int64_t row = vl - seq * n_rows;
-      load8<XT>(reinterpret_cast<const char*>(x) +
-                    (((book * n_seq + seq) * seq_stride + row) * D + col * 8) * ESZ,
-                y[u]);
-    }
+  for (int64_t base = (int64_t)blockIdx.x * RPB * SE_U; base < n;
+       base += (int64_t)gridDim.x * RPB * SE_U) {
     // The rotation runs in float64 (exact for 2-byte inputs), each element is
     // rounded once to float32 for the stage-1 threshold tests, and the
     // stage-2 residual y - level is taken in float64 before its own rounding:
     // a test then errs only when the element lies within about 1e-7 of its
     // magnitude from a threshold, far inside the 1e-4 near-tie rule for
-    // every level spacing of b <= 4.  Phases run over all SC_U * 8 elements
-    // of the lane, so that independent work overlaps.
-    double yd[SC_U][8];
+    // every level spacing of b <= 4.  All SE_U rows' loads go out first.
+    double yd[SE_U][E];
 #pragma unroll
-    for (int u = 0; u < SC_U; ++u)
+    for (int u = 0; u < SE_U; ++u) {
+      const int64_t v = base + u * RPB + rsub;
+      const int64_t vl = v < n ? v : n - 1;             // every lane joins the butterfly
+      // vl / n_rows by multiply and shift when both fit 31 bits (dsh != 0)
+      const int64_t seq = dsh ? (int64_t)(((uint64_t)vl * dm) >> dsh) : vl / n_rows;
+      const int64_t row = vl - seq * n_rows;
+      const char* src = reinterpret_cast<const char*>(x) +
+                        (((book * n_seq + seq) * seq_stride + row) * D + col * E) * ESZ;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) yd[u][e] = (double)y[u][e];
-    if (!pre_rotated) {
+      for (int c = 0; c < E / 8; ++c) {
+        float f[8];
+        load8<XT>(src + c * 8 * ESZ, f);
 #pragma unroll
-      for (int u = 0; u < SC_U; ++u) {
-        hadamard_row_f64<8, L>(yd[u], lane);
-        constexpr double sc = rsqrt_pow2_f64(D);
+        for (int e = 0; e < 8; ++e) yd[u][8 * c + e] = (double)f[e];
+      }
+    }
+    uint32_t p1[SE_U][NW], p2[SE_U][NW];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          yd[u][e] *= sc;
-          y[u][e] = (float)yd[u][e];
+    for (int u = 0; u < SE_U; ++u) {
+      if (!pre_rotated) hadamard_row_f64<E, L>(yd[u], lane);
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        p1[u][w] = 0u;
+        p2[u][w] = 0u;
+      }
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        double y = yd[u][e];
+        if (!pre_rotated) y *= rsqrt_pow2_f64(D);
+        const uint32_t z1 = bsum<B>((float)y, t0);
+        const uint32_t z2 = bsum<B>((float)(y - (double)lv[0][z1]), t1);
+        // bits [e*B, e*B + B) of the lane's stage words (a 3-bit index may
+        // straddle two words)
+        const int bit = e * B, w = bit >> 5, sh = bit & 31;
+        p1[u][w] |= z1 << sh;
+        p2[u][w] |= z2 << sh;
+        if (sh + B > 32) {
+          p1[u][w + 1] |= z1 >> (32 - sh);
+          p2[u][w + 1] |= z2 >> (32 - sh);
         }
       }
     }
-    uint32_t z1[SC_U][8];
 #pragma unroll
-    for (int u = 0; u < SC_U; ++u)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) z1[u][e] = bsum<B>(y[u][e], t0);
-    float q1[SC_U][8];
-#pragma unroll
-    for (int u = 0; u < SC_U; ++u)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) q1[u][e] = lv[0][z1[u][e]];
-    uint32_t p1[SC_U], p2[SC_U];
-#pragma unroll
-    for (int u = 0; u < SC_U; ++u) {
-      p1[u] = 0u;
-      p2[u] = 0u;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        p1[u] |= z1[u][e] << (e * B);
-        p2[u] |= bsum<B>((float)(yd[u][e] - (double)q1[u][e]), t1) << (e * B);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < SC_U; ++u) {
+    for (int u = 0; u < SE_U; ++u) {
       const int64_t v = base + u * RPB + rsub;
       if (v < n) {
-        uint8_t* rowp = codes + (book * n + v) * (2 * SB) + col * B;
-        if constexpr (B == 1) {
-          rowp[0] = (uint8_t)p1[u];
-          rowp[SB] = (uint8_t)p2[u];
-        } else if constexpr (B == 2) {
-          *reinterpret_cast<uint16_t*>(rowp) = (uint16_t)p1[u];
-          *reinterpret_cast<uint16_t*>(rowp + SB) = (uint16_t)p2[u];
-        } else if constexpr (B == 3) {                // 3 bytes at an odd offset for odd col
-#pragma unroll
-          for (int i = 0; i < 3; ++i) {
-            rowp[i] = (uint8_t)(p1[u] >> (8 * i));
-            rowp[SB + i] = (uint8_t)(p2[u] >> (8 * i));
-          }
+        uint8_t* rowp = codes + (book * n + v) * (2 * SB) + col * (E * B / 8);
+        uint32_t* a = reinterpret_cast<uint32_t*>(rowp);      // 4-byte aligned: E*B/8 = 4*NW
+        uint32_t* b = reinterpret_cast<uint32_t*>(rowp + SB);
+        if constexpr (NW == 2) {
+          *reinterpret_cast<uint2*>(a) = make_uint2(p1[u][0], p1[u][1]);
+          *reinterpret_cast<uint2*>(b) = make_uint2(p2[u][0], p2[u][1]);
+        } else if constexpr (NW == 4) {
+          *reinterpret_cast<uint4*>(a) = make_uint4(p1[u][0], p1[u][1], p1[u][2], p1[u][3]);
+          *reinterpret_cast<uint4*>(b) = make_uint4(p2[u][0], p2[u][1], p2[u][2], p2[u][3]);
         } else {
-          *reinterpret_cast<uint32_t*>(rowp) = p1[u];
-          *reinterpret_cast<uint32_t*>(rowp + SB) = p2[u];
+#pragma unroll
+          for (int w = 0; w < NW; ++w) {
+            a[w] = p1[u][w];
+            b[w] = p2[u][w];
+          }
         }
       }
     }
@@ -327,8 +331,8 @@ __global__ __launch_bounds__(256) void scalar_product_cb_kernel(const float* __r
 }
 
 // ---------------------------------------------------------------- launchers
-static unsigned row_grid(int64_t n, int D) {
-  const int64_t rpb = 256 / (D / 8) * SC_U;
+static unsigned row_grid(int64_t n, int D, int per_lane = 8, int rows_per_lane = SC_U) {
+  const int64_t rpb = 256 / (D / per_lane) * rows_per_lane;
   int64_t b = (n + rpb - 1) / rpb;
   if (b > 4096) b = 4096;
   return (unsigned)(b > 0 ? b : 1);
@@ -340,7 +344,7 @@ hipError_t launch_scalar_encode(const void* x, int xt, int D, int bits, int64_t 
                                 hipStream_t st) {
   const int64_t n = n_seq * n_rows;
   if (n == 0 || n_books == 0) return hipSuccess;
-  const dim3 grid(row_grid(n, D), (unsigned)n_books);
+  const dim3 grid(row_grid(n, D, SE_E, SE_U), (unsigned)n_books);
   // q = floor(v / n_rows) = (v * m) >> (31 + l) for every v < 2^31, with
   // l = ceil(log2 n_rows) and m = ceil(2^(31+l) / n_rows) (Granlund and
   // Montgomery, "Division by invariant integers using multiplication", 1994)
